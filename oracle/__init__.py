@@ -1,0 +1,31 @@
+"""CPU oracle of the DeepSeekMoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously correct NumPy (fp64) implementation of what the
+layer computes, written from the DeepSeek-V3 pages:
+
+* "DeepSeek_V3_Report: Annotation", section "DeepSeekMoE with
+  Auxiliary-Loss-Free Load Balancing", eq. (12)-(16); sections "Node-Limited
+  Routing" and "No Token-Dropping"; section "Fine-Grained Quantization",
+  "Increasing Accumulation Precision", "Mantissa over Exponents" and "Online
+  Quantization" of the FP8 framework; the SwiGLU paragraph.
+* "DeepSeek V3 / V4 Infra" (blog digest), section on V3 FP8 (1x128 activation
+  tiles, 128x128 weight blocks, promotion every 128 elements) and the 6hd
+  FLOP count per token-expert pair.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The GPU library never calls it, links
+it or shares code with it; the two meet only through the seeded inputs of
+``moe_inputs``.
+
+Parity pins: every function here is pinned by a CPU test in
+``tests/test_oracle_*.py`` against something other than itself (brute force,
+closed forms, invariants, or a library routine). The absolute output values of
+the full layer have no worked example on the pages: beyond those pins they
+are "parity unpinned".
+"""
+from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode  # noqa: F401
+from .moe import (  # noqa: F401
+    affinity, route, permute, swiglu_ffn, quantize_tiles, quantize_blocks,
+    dequantize_tiles, dequantize_blocks, ffn_fp8, combine, bias_update,
+    expert_ffn, layer_forward,
+)
