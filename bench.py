@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""MoE-layer forward throughput on one MI355X.
+
+One step = one pass of the whole layer on one batch: moe_route, moe_permute,
+the routed grouped FFN (moe_ffn_gate_up + moe_ffn_down), the shared-expert
+FFN, moe_combine and the step-end moe_bias_update. Inputs (seeded synthetic
+tokens and random-init weights of the workload's shape) are resident in HBM
+before the timed region. The default workload is the DeepSeek-V3-shaped layer
+(T=8192, d=7168, 256 routed experts in 8 groups, top-8 of 4 groups, 1 shared
+expert, I=2048) in bf16; ``--config c4`` runs the same shape with fp8 GEMMs.
+
+Prints one JSON line with the throughput, the roofline of the dominant kernel
+(measured with HIP events on the launch stream), per-call times and the CPU
+oracle timed on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12               # bytes/s, MI355X published
+MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}
+METRIC = "MoE-layer fwd tokens/s at V3 shape + % of MFMA peak (bf16, fp8)"
+CALLS = ["route", "permute", "ffn_gate_up", "ffn_down", "ffn_shared", "combine", "bias_update"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--cpu-sample", type=int, default=32, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing (HBM counter calibration)")
+    return ap.parse_args()
+
+
+FFN_SOURCES = ["ffn_bf16.hip", "gemm_bf16.h", "sched.h", "common.h"]
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if the kernel is unchanged since."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "mixture_experts_layer_gate_amd", "csrc")
+    h = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in FFN_SOURCES)).hexdigest()[:16]
+    for name in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        for line in open(os.path.join(ROOT, "profiles", name)):
+            m = re.match(r"traffic-record: (\{.*\})", line.strip())
+            if m:
+                rec = json.loads(m.group(1))
+                if rec["kernel"] == kernel and rec["workload"] == workload and rec["sources_sha256_16"] == h:
+                    return rec["fetch_bytes"] + rec["write_bytes"]
+    return None
+
+
+def touched_experts(load):
+    return int((load > 0).sum())
+
+
+def cpu_baseline(cfg, inp, layer, n_tok):
+    """The oracle, as it stands, on the first n_tok tokens of the same batch (host cores)."""
+    import numpy as np
+    import torch
+    import oracle
+
+    u = inp["u"][:n_tok].cpu()
+    cent, bias = inp["centroids"].cpu(), inp["bias"].cpu()
+    r0 = oracle.route(u, cent, bias, cfg.n_groups, cfg.topk_groups, cfg.group_topn, cfg.topk)
+    need = sorted(set(int(e) for e in r0["idx"].ravel()))
+    wg = {e: inp["w_gate_up"][e].cpu() for e in need}          # host copies fetched before timing
+    wd = {e: inp["w_down"][e].cpu() for e in need}
+    sg = [inp["s_gate_up"][s].cpu() for s in range(cfg.n_shared)]
+    sd = [inp["s_down"][s].cpu() for s in range(cfg.n_shared)]
+    t0 = time.perf_counter()
+    r = oracle.route(u, cent, bias, cfg.n_groups, cfg.topk_groups, cfg.group_topn, cfg.topk)
+    off, perm, row_of = oracle.permute(r["idx"], cfg.n_routed)
+    u64 = u.double().numpy()
+    y = np.zeros((n_tok * cfg.topk, cfg.d))
+    for e in range(cfg.n_routed):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            y[lo:hi] = oracle.expert_ffn(u64[perm[lo:hi]], wg[e], wd[e], cfg.gemm)
+    ysh = np.stack([oracle.expert_ffn(u64, sg[s], sd[s], cfg.gemm) for s in range(cfg.n_shared)])
+    oracle.combine(u64, y, row_of, r["gate"], ysh)
+    oracle.bias_update(bias.numpy(), r["load"], n_tok, cfg.topk, cfg.gamma)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        blas = 1
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"first {n_tok} tokens of the same {cfg.name} batch: full routing against all "
+                      f"{cfg.n_routed} centroids, permutation, {len(need)} routed experts + {cfg.n_shared} shared "
+                      f"FFN in fp64 (NumPy), combine, bias update; {dt:.1f} s wall",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the layer runs on a single MI355X with no collectives; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from moe_inputs import get_config, generate
+    from mixture_experts_layer_gate_amd import MoELayer
+
+    cfg = get_config(args.config)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    inp = generate(cfg, dev)
+    layer = MoELayer(cfg, inp, dev)
+    u = inp["u"]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
+        layer.route(u)
+        rec(1)
+        layer.permute(u)
+        rec(2)
+        layer.ffn_routed_phases(u, between=lambda: rec(3))
+        rec(4)
+        layer.ffn_shared(u)
+        rec(5)
+        layer.combine(u)
+        rec(6)
+        layer.bias_update()
+        rec(7)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    per_call = {c: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
+                for j, c in enumerate(CALLS)}
+
+    load = layer.expert_load.cpu().numpy()
+    n_touch = touched_experts(load)
+    T, d, I, K, N, Ns = cfg.T, cfg.d, cfg.inter, cfg.topk, cfg.n_routed, cfg.n_shared
+    wb = 1 if cfg.gemm == "fp8" else 2          # weight bytes per element
+    ab = 2                                      # u / out bytes per element (bf16)
+    # dominant kernel: routed gate/up projection
+    gu_bytes = n_touch * 2 * I * d * wb + T * d * ab
+    gu_flops = 2.0 * T * K * d * 2 * I
+    gu_s = per_call["ffn_gate_up"] / 1e3
+    gu_bound = "hbm" if gu_bytes / HBM_PEAK >= gu_flops / MFMA_PEAK[cfg.gemm] else "mfma"
+    if gu_bound == "hbm":
+        roof = {"bound": "hbm", "achieved": gu_bytes / gu_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": MFMA_PEAK[cfg.gemm] / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = recorded_traffic(f"ffn_gate_up_{cfg.gemm} routed", cfg.name)
+    roof["kernel"] = "ffn_gate_up (routed experts)"
+    roof["mfma_frac"] = gu_flops / gu_s / MFMA_PEAK[cfg.gemm]
+
+    ffn_flops = cfg.ffn_flops()
+    ffn_s = (per_call["ffn_gate_up"] + per_call["ffn_down"] + per_call["ffn_shared"]) / 1e3
+    layer_bytes = (n_touch * 3 * I * d * wb + Ns * 3 * I * d * wb + 2 * T * d * ab + N * d * ab)
+    calls = {c: {"ms": round(per_call[c], 4)} for c in CALLS}
+    calls["route"]["GB/s"] = round((T * d * ab + N * d * ab) / (per_call["route"] / 1e3) / 1e9, 1)
+    calls["combine"]["GB/s"] = round((T * d * ab * 2 + (T * K + T * Ns) * d * ab) / (per_call["combine"] / 1e3) / 1e9, 1)
+    calls["ffn_down"]["GB/s_weights"] = round(n_touch * I * d * wb / (per_call["ffn_down"] / 1e3) / 1e9, 1)
+    calls["ffn_shared"]["TFLOP/s"] = round(6.0 * T * Ns * d * I / (per_call["ffn_shared"] / 1e3) / 1e12, 1)
+
+    res = {
+        "metric": METRIC,
+        "value": T / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.gemm,
+        "data": "synthetic: seeded N(0,1) tokens, random-init N(0,0.02^2) weights of the workload's shape",
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "T": T, "d": d, "n_routed": N,
+                   "groups": cfg.n_groups, "topk_groups": cfg.topk_groups, "topk": K, "n_shared": Ns, "inter": I,
+                   "gemm": cfg.gemm},
+        "roofline": roof,
+        "ffn": {"TFLOP/s": ffn_flops / ffn_s / 1e12, "mfma_frac": ffn_flops / ffn_s / MFMA_PEAK[cfg.gemm],
+                "hbm_frac_weights": (n_touch + Ns) * 3 * I * d * wb / ffn_s / HBM_PEAK},
+        "layer": {"algorithmic_GB": layer_bytes / 1e9, "roofline_ms": max(layer_bytes / HBM_PEAK,
+                  (ffn_flops + cfg.router_flops()) / MFMA_PEAK[cfg.gemm]) * 1e3,
+                  "experts_touched": n_touch, "max_load": int(load.max()), "min_load": int(load.min())},
+        "calls": calls,
+    }
+    res["layer"]["frac_of_roofline"] = res["layer"]["roofline_ms"] / ms_step
+    if args.cpu_sample > 0:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, layer, args.cpu_sample)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

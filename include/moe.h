@@ -1,0 +1,217 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward.
+ *
+ * The layer is the DeepSeekMoE FFN of the DeepSeek-V3 report ("DeepSeek_V3_Report:
+ * Annotation", section "DeepSeekMoE with Auxiliary-Loss-Free Load Balancing",
+ * eq. (12)-(16)): sigmoid affinities, an expert bias used only to select the
+ * top-K experts inside the M best expert groups, gates normalised over the
+ * selected raw affinities, SwiGLU experts, a gate-weighted combine with the
+ * shared experts and the residual, and the step-end bias update.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless stated; arrays are dense and
+ *    row-major. The caller owns every buffer; the library never allocates,
+ *    frees or keeps a pointer after a call returns. Scratch memory comes in
+ *    through `workspace` (size from moe_workspace_bytes).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Each
+ *    call only enqueues work on it and returns; no call synchronises the host,
+ *    except when the environment variable MOE_SYNC_DEBUG=1 is set (then every
+ *    call waits for its stream and reports kernel errors).
+ *  - Arguments are validated on the host before anything is launched:
+ *    MOE_E_INVALID for a null required pointer, a non-positive size or an
+ *    inconsistent shape; MOE_E_UNSUPPORTED for shapes or dtypes this build
+ *    does not handle; MOE_E_WORKSPACE when ws_bytes is too small; MOE_E_HIP
+ *    when a launch fails. The message of the last non-OK status of the calling
+ *    thread is returned by moe_last_error(). No exception crosses the ABI.
+ *  - Device-side integer inputs (expert ids, offsets, row indices) are range
+ *    checked by the kernels: an out-of-range entry is skipped or read as a
+ *    zero row, never dereferenced.
+ *  - Calls are re-entrant; calls on different streams may run concurrently
+ *    if they do not share output or workspace buffers.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_INVALID = 1,
+  MOE_E_UNSUPPORTED = 2,
+  MOE_E_WORKSPACE = 3,
+  MOE_E_HIP = 4
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,     /* IEEE binary32 */
+  MOE_BF16 = 1,    /* bfloat16 */
+  MOE_F8E4M3 = 2   /* OCP E4M3FN: bias 7, max 448, no infinities */
+} moe_dtype;
+
+/* How moe_grouped_ffn finds the input row of output row r of expert e. */
+typedef enum {
+  MOE_ROWS_DIRECT = 0,   /* a[r]                       (a already permuted)      */
+  MOE_ROWS_GATHER = 1,   /* a[row_src[r]]              (gather fused in the GEMM) */
+  MOE_ROWS_SEGMENT = 2   /* a[r - expert_offsets[e]]   (shared experts: all tokens) */
+} moe_row_mode;
+
+/* Host struct. N_r = n_routed experts in n_groups contiguous groups of
+ * S = N_r / n_groups; each token keeps the topk_groups (M) groups with the
+ * highest group score (sum of the group_topn largest biased affinities of the
+ * group) and selects topk (K) experts inside them. */
+typedef struct {
+  int32_t T;            /* tokens                                  */
+  int32_t d;            /* hidden size, multiple of 128            */
+  int32_t n_routed;     /* N_r <= 1024                             */
+  int32_t n_groups;     /* G, divides N_r, <= 64                   */
+  int32_t topk_groups;  /* M <= G                                  */
+  int32_t group_topn;   /* 1..4, <= S                              */
+  int32_t topk;         /* K <= 16, K <= M * S                     */
+  int32_t n_shared;     /* N_s >= 0                                */
+  int32_t inter;        /* I, SwiGLU width, multiple of 128        */
+} moe_shape;
+
+/*
+ * moe_route -- affinities, biased group-limited top-K, gates and load histogram.
+ * Defined by eq. (15) (s = Sigmoid(u . e_i)), eq. (16) (selection on s + b),
+ * eq. (13)-(14) (gates = selected s / their sum) of "DeepSeek_V3_Report:
+ * Annotation", section "DeepSeekMoE with Auxiliary-Loss-Free Load Balancing",
+ * and its section "Node-Limited Routing" (at most M groups per token).
+ *   act        MOE_F32 or MOE_BF16: dtype of u and centroids.
+ *   u          [T, d] token inputs.
+ *   centroids  [N_r, d] expert centroid vectors e_i.
+ *   bias       [N_r] fp32 expert biases b_i (selection only).
+ *   topk_idx   out [T, K] int32, selected experts of each token in ascending id order.
+ *   topk_gate  out [T, K] fp32, gate of each selected expert (sums to 1 per token).
+ *   expert_load out [N_r] int32, number of tokens per expert (overwritten, not accumulated).
+ *   scores     out [T, N_r] fp32 sigmoid affinities, or NULL (then kept in the workspace).
+ * Selection compares fp32 values s + b; ties go to the lower group / expert id.
+ */
+moe_status moe_route(const moe_shape* shape, moe_dtype act, const void* u, const void* centroids,
+                     const float* bias, int32_t* topk_idx, float* topk_gate, int32_t* expert_load,
+                     float* scores, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute -- stable permutation of the T*K token-expert pairs to their experts
+ * (the one-GPU form of the dispatch; no pair is dropped, per the section
+ * "No Token-Dropping" of "DeepSeek_V3_Report: Annotation"), optionally with the
+ * row gather and the online fp8 quantisation of the activations (1x128 tiles,
+ * section "Fine-Grained Quantization"; scale from the current max-abs, section
+ * "Online Quantization").
+ *   topk_idx       [T, K] int32 from moe_route.
+ *   expert_offsets out [N_r + 1] int32: rows of expert e are [off[e], off[e+1]).
+ *   perm_token     out [T*K] int32: token of each row (rows ordered by expert, then token).
+ *   row_of         out [T*K] int32: row of pair (t, k) at index t*K + k.
+ *   a              out or NULL. gather=1: [T*K, d] rows a[r] = u[perm_token[r]];
+ *                  gather=0: [T, d] in token order (only with a_dtype = MOE_F8E4M3:
+ *                  the quantised u, to be gathered inside moe_grouped_ffn).
+ *   a_dtype        dtype of a: act (plain copy) or MOE_F8E4M3 (quantised).
+ *   a_scale        out [rows of a, d/128] fp32 scales when a_dtype = MOE_F8E4M3, else NULL.
+ *                  Quantisation of a tile x: amax = max|x|; amax = 0 gives scale 1
+ *                  and zero codes; else q = E4M3_rne_sat(x * fl32(448/amax)),
+ *                  scale = fl32(amax/448).
+ * Deterministic: the result does not depend on the order atomics complete in.
+ */
+moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* topk_idx, const void* u,
+                       int32_t* expert_offsets, int32_t* perm_token, int32_t* row_of,
+                       void* a, moe_dtype a_dtype, float* a_scale, int32_t gather,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn -- per-expert SwiGLU FFN as one grouped GEMM pass over all experts:
+ * y[r] = (SiLU(x W_g^T) * (x W_u^T)) W_d^T for every row r of every expert
+ * (SwiGLU paragraph of "DeepSeek_V3_Report: Annotation", beta = 1; the three
+ * projections cost 6*d*I FLOPs per row, "DeepSeek V3 / V4 Infra", V4 EP section).
+ *   w            weight dtype: MOE_F32 (a f32), MOE_BF16 (a bf16) or MOE_F8E4M3
+ *                (a is fp8 with a_scale; weights fp8 with 128x128 block scales;
+ *                fp32 accumulation with the scales applied per 128-wide K chunk,
+ *                section "Increasing Accumulation Precision"; the SwiGLU output
+ *                is re-quantised per 1x128 tile along I before the down projection).
+ *   n_experts    experts in this call (routed N_r, or N_s for the shared experts).
+ *   n_rows       total rows = expert_offsets[n_experts] (T*K routed, N_s*T shared).
+ *   expert_offsets [n_experts + 1] int32 device array.
+ *   mode, row_src  see moe_row_mode; row_src [n_rows] int32 for MOE_ROWS_GATHER, else NULL.
+ *   a            input rows [a_rows, d]; a_scale [a_rows, d/128] fp32 for fp8, else NULL.
+ *   w_gate_up    [n_experts, 2I, d]: gate rows [0, I) then up rows [I, 2I), K-contiguous.
+ *   w_gu_scale   [n_experts, 2I/128, d/128] fp32 block scales (fp8 only, else NULL).
+ *   w_down       [n_experts, d, I], K-contiguous.
+ *   w_d_scale    [n_experts, d/128, I/128] fp32 block scales (fp8 only, else NULL).
+ *   y_dtype      MOE_F32 (only with w = MOE_F32) or MOE_BF16.
+ *   y            out [n_rows, d].
+ */
+moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                           const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
+                           const void* a, const float* a_scale, int32_t a_rows,
+                           const void* w_gate_up, const float* w_gu_scale,
+                           const void* w_down, const float* w_d_scale,
+                           moe_dtype y_dtype, void* y, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_ffn_gate_up / moe_ffn_down -- the two GEMM phases of moe_grouped_ffn as
+ * separate calls, for callers that schedule or time them apart:
+ * moe_grouped_ffn(...) == moe_ffn_gate_up(...) into its workspace, then moe_ffn_down(...).
+ * Arguments as in moe_grouped_ffn, plus the SwiGLU output
+ *   h        [n_rows, I]: fp32 (w = MOE_F32), bf16 (w = MOE_BF16) or E4M3 codes
+ *            (w = MOE_F8E4M3, quantised per 1x128 tile along I with h_scale).
+ *   h_scale  [n_rows, I/128] fp32 for fp8, else NULL.
+ */
+moe_status moe_ffn_gate_up(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                           const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
+                           const void* a, const float* a_scale, int32_t a_rows,
+                           const void* w_gate_up, const float* w_gu_scale,
+                           void* h, float* h_scale, void* stream);
+moe_status moe_ffn_down(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                        const int32_t* expert_offsets, const void* h, const float* h_scale,
+                        const void* w_down, const float* w_d_scale, moe_dtype y_dtype, void* y, void* stream);
+
+/*
+ * moe_combine -- eq. (12): out[t] = u[t] + sum_s y_shared[s*T + t] + sum_k gate[t,k] * y_routed[row_of[t*K+k]].
+ * fp32 accumulation in that fixed order, one rounding to the output dtype.
+ *   io        MOE_F32 or MOE_BF16: dtype of u, y_routed, y_shared and out.
+ *   y_shared  [N_s*T, d], NULL iff N_s = 0.
+ */
+moe_status moe_combine(const moe_shape* shape, moe_dtype io, const void* u, const void* y_routed,
+                       const int32_t* row_of, const float* topk_gate, const void* y_shared,
+                       void* out, void* stream);
+
+/*
+ * moe_bias_update -- step-end update of the aux-loss-free bias ("DeepSeek_V3_Report:
+ * Annotation", section "DeepSeekMoE with Auxiliary-Loss-Free Load Balancing"):
+ * bias[i] -= gamma if expert i received more than the mean T*K/N_r pairs,
+ * bias[i] += gamma if fewer, unchanged at the mean. fp32 arithmetic, in place.
+ *   expert_load [N_r] int32 from moe_route.
+ */
+moe_status moe_bias_update(const moe_shape* shape, const int32_t* expert_load, float gamma,
+                           float* bias, void* stream);
+
+/*
+ * moe_quantize_weights -- 128x128 block quantisation of expert weights to E4M3
+ * ("DeepSeek_V3_Report: Annotation", section "Fine-Grained Quantization"): for
+ * n_mats matrices [rows, cols] of bf16 (rows, cols multiples of 128), writes
+ * codes [n_mats, rows, cols] and scales [n_mats, rows/128, cols/128] fp32 with
+ * the same tile rule as moe_permute. Weight preparation, not part of a forward.
+ */
+moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, const void* w_bf16,
+                                void* w_codes, float* w_scale, void* stream);
+
+/* Host: bytes of workspace that any single call above needs for this shape
+ * (with the routed FFN sized for T*K rows and the shared FFN for N_s*T rows).
+ * One workspace can serve all calls issued in order on one stream. */
+size_t moe_workspace_bytes(const moe_shape* shape, moe_dtype gemm);
+
+/* Host: message of the calling thread's last non-OK status ("" if none). */
+const char* moe_last_error(void);
+
+/* Host: library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,220 @@
+"""ctypes binding of libmoe.so (include/moe.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors are passed as device pointers, the
+stream is torch's current stream, and tensor sizes are checked against the
+shape before the call (the C side cannot see sizes). Every step runs in the
+HIP library; if it is not built this module raises at import of the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_F8E4M3 = 0, 1, 2
+MOE_ROWS_DIRECT, MOE_ROWS_GATHER, MOE_ROWS_SEGMENT = 0, 1, 2
+
+_STATUS = {1: "MOE_E_INVALID", 2: "MOE_E_UNSUPPORTED", 3: "MOE_E_WORKSPACE", 4: "MOE_E_HIP"}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "d", "n_routed", "n_groups", "topk_groups", "group_topn", "topk", "n_shared", "inter")]
+
+    @classmethod
+    def of(cls, cfg) -> "moe_shape":
+        return cls(cfg.T, cfg.d, cfg.n_routed, cfg.n_groups, cfg.topk_groups, cfg.group_topn, cfg.topk,
+                   cfg.n_shared, cfg.inter)
+
+
+_lib = None
+_lock = threading.Lock()
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_S = ctypes.POINTER(moe_shape)
+
+_SIGS = {
+    "moe_route": [_S, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_permute": [_S, _I, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, ctypes.c_size_t, _P],
+    "moe_grouped_ffn": [_S, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
+    "moe_ffn_gate_up": [_S, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P],
+    "moe_ffn_down": [_S, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P],
+    "moe_combine": [_S, _I, _P, _P, _P, _P, _P, _P, _P],
+    "moe_bias_update": [_S, _P, ctypes.c_float, _P, _P],
+    "moe_quantize_weights": [_I, _I, _I, _P, _P, _P, _P],
+    "moe_workspace_bytes": [_S, _I],
+    "moe_last_error": [],
+    "moe_version": [],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (once). Raises if the library has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_gate_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, args in _SIGS.items():
+                f = getattr(L, name)
+                f.argtypes = args
+                f.restype = ctypes.c_int
+            L.moe_workspace_bytes.restype = ctypes.c_size_t
+            L.moe_last_error.restype = ctypes.c_char_p
+            L.moe_version.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoEError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return MOE_F8E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: Optional[torch.Tensor], numel: int, name: str):
+    if t is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def moe_workspace_bytes(shape: moe_shape, gemm: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(shape), gemm))
+
+
+def moe_route(shape: moe_shape, u, centroids, bias, topk_idx, topk_gate, expert_load, scores=None,
+              workspace=None, stream=None):
+    T, d, N, K = shape.T, shape.d, shape.n_routed, shape.topk
+    _need(u, T * d, "u"); _need(centroids, N * d, "centroids"); _need(bias, N, "bias")
+    _need(topk_idx, T * K, "topk_idx"); _need(topk_gate, T * K, "topk_gate"); _need(expert_load, N, "expert_load")
+    _need(scores, T * N, "scores")
+    _check(lib().moe_route(ctypes.byref(shape), _dt(u), _ptr(u), _ptr(centroids), _ptr(bias), _ptr(topk_idx),
+                           _ptr(topk_gate), _ptr(expert_load), _ptr(scores), _ptr(workspace), _nbytes(workspace),
+                           _stream(stream)))
+
+
+def moe_permute(shape: moe_shape, topk_idx, u, expert_offsets, perm_token, row_of, a=None, a_dtype=None,
+                a_scale=None, gather=1, workspace=None, stream=None):
+    T, d, N, K = shape.T, shape.d, shape.n_routed, shape.topk
+    _need(topk_idx, T * K, "topk_idx"); _need(expert_offsets, N + 1, "expert_offsets")
+    _need(perm_token, T * K, "perm_token"); _need(row_of, T * K, "row_of")
+    act = _dt(u) if u is not None else MOE_BF16
+    if a is not None:
+        rows = T * K if gather else T
+        _need(u, T * d, "u"); _need(a, rows * d, "a")
+        if a_dtype is None:
+            a_dtype = _dt(a)
+        if a_dtype == MOE_F8E4M3:
+            _need(a_scale, rows * (d // 128), "a_scale")
+    _check(lib().moe_permute(ctypes.byref(shape), act, _ptr(topk_idx), _ptr(u), _ptr(expert_offsets),
+                             _ptr(perm_token), _ptr(row_of), _ptr(a), a_dtype if a_dtype is not None else act,
+                             _ptr(a_scale), int(gather), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_grouped_ffn(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_offsets, mode: int, row_src,
+                    a, a_scale, a_rows: int, w_gate_up, w_gu_scale, w_down, w_d_scale, y, workspace=None,
+                    stream=None):
+    d, I = shape.d, shape.inter
+    _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a, a_rows * d, "a")
+    _need(w_gate_up, n_experts * 2 * I * d, "w_gate_up"); _need(w_down, n_experts * d * I, "w_down")
+    _need(y, n_rows * d, "y")
+    if mode == MOE_ROWS_GATHER:
+        _need(row_src, n_rows, "row_src")
+    if w == MOE_F8E4M3:
+        _need(a_scale, a_rows * (d // 128), "a_scale")
+        _need(w_gu_scale, n_experts * (2 * I // 128) * (d // 128), "w_gu_scale")
+        _need(w_d_scale, n_experts * (d // 128) * (I // 128), "w_d_scale")
+    _check(lib().moe_grouped_ffn(ctypes.byref(shape), w, n_experts, n_rows, _ptr(expert_offsets), mode,
+                                 _ptr(row_src), _ptr(a), _ptr(a_scale), a_rows, _ptr(w_gate_up), _ptr(w_gu_scale),
+                                 _ptr(w_down), _ptr(w_d_scale), _dt(y), _ptr(y), _ptr(workspace),
+                                 _nbytes(workspace), _stream(stream)))
+
+
+def moe_ffn_gate_up(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_offsets, mode: int, row_src,
+                    a, a_scale, a_rows: int, w_gate_up, w_gu_scale, h, h_scale=None, stream=None):
+    d, I = shape.d, shape.inter
+    _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a, a_rows * d, "a")
+    _need(w_gate_up, n_experts * 2 * I * d, "w_gate_up"); _need(h, n_rows * I, "h")
+    if mode == MOE_ROWS_GATHER:
+        _need(row_src, n_rows, "row_src")
+    if w == MOE_F8E4M3:
+        _need(a_scale, a_rows * (d // 128), "a_scale")
+        _need(w_gu_scale, n_experts * (2 * I // 128) * (d // 128), "w_gu_scale")
+        _need(h_scale, n_rows * (I // 128), "h_scale")
+    _check(lib().moe_ffn_gate_up(ctypes.byref(shape), w, n_experts, n_rows, _ptr(expert_offsets), mode,
+                                 _ptr(row_src), _ptr(a), _ptr(a_scale), a_rows, _ptr(w_gate_up), _ptr(w_gu_scale),
+                                 _ptr(h), _ptr(h_scale), _stream(stream)))
+
+
+def moe_ffn_down(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_offsets, h, h_scale, w_down,
+                 w_d_scale, y, stream=None):
+    d, I = shape.d, shape.inter
+    _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(h, n_rows * I, "h")
+    _need(w_down, n_experts * d * I, "w_down"); _need(y, n_rows * d, "y")
+    if w == MOE_F8E4M3:
+        _need(h_scale, n_rows * (I // 128), "h_scale")
+        _need(w_d_scale, n_experts * (d // 128) * (I // 128), "w_d_scale")
+    _check(lib().moe_ffn_down(ctypes.byref(shape), w, n_experts, n_rows, _ptr(expert_offsets), _ptr(h),
+                              _ptr(h_scale), _ptr(w_down), _ptr(w_d_scale), _dt(y), _ptr(y), _stream(stream)))
+
+
+def moe_combine(shape: moe_shape, u, y_routed, row_of, topk_gate, y_shared, out, stream=None):
+    T, d, K, Ns = shape.T, shape.d, shape.topk, shape.n_shared
+    _need(u, T * d, "u"); _need(y_routed, T * K * d, "y_routed"); _need(row_of, T * K, "row_of")
+    _need(topk_gate, T * K, "topk_gate"); _need(out, T * d, "out")
+    if Ns:
+        _need(y_shared, Ns * T * d, "y_shared")
+    _check(lib().moe_combine(ctypes.byref(shape), _dt(u), _ptr(u), _ptr(y_routed), _ptr(row_of), _ptr(topk_gate),
+                             _ptr(y_shared), _ptr(out), _stream(stream)))
+
+
+def moe_bias_update(shape: moe_shape, expert_load, gamma: float, bias, stream=None):
+    _need(expert_load, shape.n_routed, "expert_load"); _need(bias, shape.n_routed, "bias")
+    _check(lib().moe_bias_update(ctypes.byref(shape), _ptr(expert_load), float(gamma), _ptr(bias),
+                                 _stream(stream)))
+
+
+def moe_quantize_weights(w, codes, scale, stream=None):
+    """w [n, rows, cols] bf16 -> codes [n, rows, cols] uint8, scale [n, rows/128, cols/128] fp32."""
+    n, rows, cols = w.shape
+    _need(codes, n * rows * cols, "codes"); _need(scale, n * (rows // 128) * (cols // 128), "scale")
+    _check(lib().moe_quantize_weights(n, rows, cols, _ptr(w), _ptr(codes), _ptr(scale), _stream(stream)))

@@ -1,0 +1,317 @@
+// The C ABI of include/moe.h: argument validation on the host (before any
+// HIP call), workspace sizing, dispatch to the launchers, error reporting.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+bool sync_debug() {
+  static const bool on = [] {
+    const char* v = std::getenv("MOE_SYNC_DEBUG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+moe_status finish(hipError_t e, const char* what, hipStream_t st) {
+  if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(MOE_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+#define REQUIRE(cond, ...)                          \
+  do {                                              \
+    if (!(cond)) return fail(MOE_E_INVALID, __VA_ARGS__); \
+  } while (0)
+#define SUPPORT(cond, ...)                              \
+  do {                                                  \
+    if (!(cond)) return fail(MOE_E_UNSUPPORTED, __VA_ARGS__); \
+  } while (0)
+
+moe_status check_shape(const moe_shape* s) {
+  REQUIRE(s != nullptr, "shape is NULL");
+  REQUIRE(s->T > 0 && s->d > 0 && s->n_routed > 0 && s->n_groups > 0 && s->topk_groups > 0 &&
+              s->group_topn > 0 && s->topk > 0 && s->inter > 0 && s->n_shared >= 0,
+          "non-positive size in shape (T=%d d=%d N_r=%d G=%d M=%d topn=%d K=%d N_s=%d I=%d)", s->T, s->d,
+          s->n_routed, s->n_groups, s->topk_groups, s->group_topn, s->topk, s->n_shared, s->inter);
+  REQUIRE(s->n_routed % s->n_groups == 0, "n_routed (%d) is not a multiple of n_groups (%d)", s->n_routed,
+          s->n_groups);
+  REQUIRE(s->topk_groups <= s->n_groups, "topk_groups (%d) > n_groups (%d)", s->topk_groups, s->n_groups);
+  const int S = s->n_routed / s->n_groups;
+  REQUIRE(s->group_topn <= S, "group_topn (%d) > group size (%d)", s->group_topn, S);
+  REQUIRE(s->topk <= s->topk_groups * S, "topk (%d) > topk_groups * group size (%d)", s->topk,
+          s->topk_groups * S);
+  SUPPORT(s->d % 128 == 0, "d (%d) must be a multiple of 128", s->d);
+  SUPPORT(s->inter % 128 == 0, "inter (%d) must be a multiple of 128", s->inter);
+  SUPPORT(s->topk <= 16, "topk (%d) > 16", s->topk);
+  SUPPORT(s->n_routed <= 1024, "n_routed (%d) > 1024", s->n_routed);
+  SUPPORT(s->n_groups <= 64, "n_groups (%d) > 64", s->n_groups);
+  SUPPORT(s->group_topn <= 4, "group_topn (%d) > 4", s->group_topn);
+  SUPPORT(static_cast<long long>(s->T) * s->topk < (1LL << 31) && static_cast<long long>(s->T) * s->n_shared < (1LL << 31),
+          "T*K or T*N_s does not fit int32");
+  return MOE_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+std::mutex g_cu_mutex;
+int g_cu[64];
+
+}  // namespace
+
+namespace moe {
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(g_cu_mutex);
+  if (g_cu[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu[dev] = n;
+  }
+  return g_cu[dev];
+}
+
+size_t ffn_ws_bytes(moe_dtype w, int n_rows, int I) {
+  const size_t n = static_cast<size_t>(n_rows) * I;
+  if (w == MOE_F32) return align256(n * 4);
+  if (w == MOE_BF16) return align256(n * 2);
+  return align256(n) + align256(static_cast<size_t>(n_rows) * (I / 128) * 4);
+}
+
+}  // namespace moe
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "moe-gfx950 0.1"; }
+
+size_t moe_workspace_bytes(const moe_shape* shape, moe_dtype gemm) {
+  if (!shape || check_shape(shape) != MOE_OK) return 0;
+  const moe::Shape s = moe::to_shape(*shape);
+  const size_t route = align256(static_cast<size_t>(s.T) * s.N * sizeof(float));
+  const size_t perm = align256(moe::permute_ws_bytes(s));
+  const int rows = s.T * (s.K > s.Ns ? s.K : s.Ns);
+  const size_t ffn = moe::ffn_ws_bytes(gemm, rows, s.I);
+  size_t m = route > perm ? route : perm;
+  return m > ffn ? m : ffn;
+}
+
+moe_status moe_route(const moe_shape* shape, moe_dtype act, const void* u, const void* centroids,
+                     const float* bias, int32_t* topk_idx, float* topk_gate, int32_t* expert_load, float* scores,
+                     void* workspace, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (moe_status st = check_shape(shape); st != MOE_OK) return st;
+  REQUIRE(act == MOE_F32 || act == MOE_BF16, "route: act must be MOE_F32 or MOE_BF16 (got %d)", static_cast<int>(act));
+  REQUIRE(u && centroids && bias && topk_idx && topk_gate && expert_load, "route: a required pointer is NULL");
+  const moe::Shape s = moe::to_shape(*shape);
+  if (!scores) {
+    const size_t need = static_cast<size_t>(s.T) * s.N * sizeof(float);
+    if (!workspace || ws_bytes < need)
+      return fail(MOE_E_WORKSPACE, "route: workspace of %zu bytes < %zu needed for the scores", ws_bytes, need);
+    scores = static_cast<float*>(workspace);
+  }
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_route(s, act, u, centroids, bias, topk_idx, topk_gate, expert_load, scores, st),
+                "moe_route", st);
+}
+
+moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* topk_idx, const void* u,
+                       int32_t* expert_offsets, int32_t* perm_token, int32_t* row_of, void* a, moe_dtype a_dtype,
+                       float* a_scale, int32_t gather, void* workspace, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (moe_status st = check_shape(shape); st != MOE_OK) return st;
+  REQUIRE(topk_idx && expert_offsets && perm_token && row_of, "permute: a required pointer is NULL");
+  const moe::Shape s = moe::to_shape(*shape);
+  if (a) {
+    REQUIRE(u != nullptr, "permute: u is NULL but an output a is requested");
+    REQUIRE(act == MOE_F32 || act == MOE_BF16, "permute: act must be MOE_F32 or MOE_BF16");
+    REQUIRE(a_dtype == act || a_dtype == MOE_F8E4M3, "permute: a_dtype must equal act or be MOE_F8E4M3");
+    REQUIRE(a_dtype != MOE_F8E4M3 || a_scale != nullptr, "permute: fp8 output needs a_scale");
+    REQUIRE(gather == 0 || gather == 1, "permute: gather must be 0 or 1");
+    REQUIRE(gather == 1 || a_dtype == MOE_F8E4M3, "permute: gather=0 is only meaningful for fp8 quantisation");
+  }
+  const size_t need = moe::permute_ws_bytes(s);
+  if (!workspace || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "permute: workspace of %zu bytes < %zu needed", ws_bytes, need);
+  auto st = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_permute_maps(s, topk_idx, expert_offsets, perm_token, row_of, workspace, st);
+  if (e == hipSuccess && a) {
+    const int rows = gather ? s.T * s.K : s.T;
+    e = moe::launch_rows_copy(rows, s.d, act, u, s.T, gather ? perm_token : nullptr, a_dtype, a, a_scale, st);
+  }
+  return finish(e, "moe_permute", st);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the grouped FFN calls (phase: 0 both, 1 gate/up, 2 down).
+moe_status check_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                     const int32_t* offsets, int phase) {
+  REQUIRE(shape != nullptr, "shape is NULL");
+  const int d = shape->d, I = shape->inter;
+  REQUIRE(d > 0 && I > 0, "grouped_ffn: d and inter must be positive");
+  SUPPORT(d % 128 == 0 && I % 128 == 0, "grouped_ffn: d (%d) and inter (%d) must be multiples of 128", d, I);
+  REQUIRE(n_experts > 0 && n_rows > 0, "grouped_ffn: n_experts and n_rows must be positive");
+  SUPPORT(n_experts <= 4096, "grouped_ffn: n_experts (%d) > 4096", n_experts);
+  SUPPORT(static_cast<long long>(n_rows) * (d > I ? d : I) < (1LL << 40), "grouped_ffn: too many rows");
+  REQUIRE(offsets != nullptr, "grouped_ffn: expert_offsets is NULL");
+  REQUIRE(w == MOE_F32 || w == MOE_BF16 || w == MOE_F8E4M3, "grouped_ffn: bad weight dtype %d", static_cast<int>(w));
+  (void)phase;
+  return MOE_OK;
+}
+
+moe_status check_gate_up(moe_dtype w, moe_row_mode mode, const int32_t* row_src, const void* a,
+                         const float* a_scale, int32_t a_rows, const void* w_gate_up, const float* w_gu_scale) {
+  REQUIRE(a && w_gate_up, "grouped_ffn: a or w_gate_up is NULL");
+  REQUIRE(a_rows > 0, "grouped_ffn: a_rows must be positive");
+  REQUIRE(mode == MOE_ROWS_DIRECT || mode == MOE_ROWS_GATHER || mode == MOE_ROWS_SEGMENT,
+          "grouped_ffn: bad row mode %d", static_cast<int>(mode));
+  REQUIRE(mode != MOE_ROWS_GATHER || row_src != nullptr, "grouped_ffn: MOE_ROWS_GATHER needs row_src");
+  if (w == MOE_F8E4M3) REQUIRE(a_scale && w_gu_scale, "grouped_ffn: fp8 needs a_scale and w_gu_scale");
+  return MOE_OK;
+}
+
+moe_status check_down(moe_dtype w, const void* w_down, const float* w_d_scale, moe_dtype y_dtype, const void* y) {
+  REQUIRE(w_down && y, "grouped_ffn: w_down or y is NULL");
+  REQUIRE(y_dtype == MOE_BF16 || (y_dtype == MOE_F32 && w == MOE_F32),
+          "grouped_ffn: y_dtype must be MOE_BF16 (or MOE_F32 with MOE_F32 weights)");
+  if (w == MOE_F8E4M3) REQUIRE(w_d_scale != nullptr, "grouped_ffn: fp8 needs w_d_scale");
+  return MOE_OK;
+}
+
+hipError_t run_gate_up(moe_dtype w, const moe::FfnArgs& p, hipStream_t st) {
+  if (w == MOE_F32) return moe::launch_ffn_f32_gate_up(p, st);
+  if (w == MOE_BF16) return moe::launch_ffn_bf16_gate_up(p, st);
+  return moe::launch_ffn_fp8_gate_up(p, st);
+}
+
+hipError_t run_down(moe_dtype w, const moe::FfnArgs& p, hipStream_t st) {
+  if (w == MOE_F32) return moe::launch_ffn_f32_down(p, st);
+  if (w == MOE_BF16) return moe::launch_ffn_bf16_down(p, st);
+  return moe::launch_ffn_fp8_down(p, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                           const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src, const void* a,
+                           const float* a_scale, int32_t a_rows, const void* w_gate_up, const float* w_gu_scale,
+                           const void* w_down, const float* w_d_scale, moe_dtype y_dtype, void* y, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 0); r != MOE_OK) return r;
+  if (moe_status r = check_gate_up(w, mode, row_src, a, a_scale, a_rows, w_gate_up, w_gu_scale); r != MOE_OK)
+    return r;
+  if (moe_status r = check_down(w, w_down, w_d_scale, y_dtype, y); r != MOE_OK) return r;
+  const int d = shape->d, I = shape->inter;
+  const size_t need = moe::ffn_ws_bytes(w, n_rows, I);
+  if (!workspace || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "grouped_ffn: workspace of %zu bytes < %zu needed", ws_bytes, need);
+  float* h_scale = nullptr;
+  if (w == MOE_F8E4M3)
+    h_scale = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(static_cast<size_t>(n_rows) * I));
+  moe::FfnArgs p{d, I, n_experts, n_rows, a_rows, expert_offsets, mode, row_src, a, a_scale, w_gate_up, w_gu_scale,
+                 w_down, w_d_scale, y_dtype, y, workspace, h_scale};
+  auto st = static_cast<hipStream_t>(stream);
+  hipError_t e = run_gate_up(w, p, st);
+  if (e == hipSuccess) e = run_down(w, p, st);
+  return finish(e, "moe_grouped_ffn", st);
+}
+
+moe_status moe_ffn_gate_up(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                           const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src, const void* a,
+                           const float* a_scale, int32_t a_rows, const void* w_gate_up, const float* w_gu_scale,
+                           void* h, float* h_scale, void* stream) {
+  g_err.clear();
+  if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 1); r != MOE_OK) return r;
+  if (moe_status r = check_gate_up(w, mode, row_src, a, a_scale, a_rows, w_gate_up, w_gu_scale); r != MOE_OK)
+    return r;
+  REQUIRE(h != nullptr, "ffn_gate_up: h is NULL");
+  REQUIRE(w != MOE_F8E4M3 || h_scale != nullptr, "ffn_gate_up: fp8 needs h_scale");
+  moe::FfnArgs p{shape->d, shape->inter, n_experts, n_rows, a_rows, expert_offsets, mode, row_src, a, a_scale,
+                 w_gate_up, w_gu_scale, nullptr, nullptr, MOE_BF16, nullptr, h, h_scale};
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(run_gate_up(w, p, st), "moe_ffn_gate_up", st);
+}
+
+moe_status moe_ffn_down(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                        const int32_t* expert_offsets, const void* h, const float* h_scale, const void* w_down,
+                        const float* w_d_scale, moe_dtype y_dtype, void* y, void* stream) {
+  g_err.clear();
+  if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 2); r != MOE_OK) return r;
+  if (moe_status r = check_down(w, w_down, w_d_scale, y_dtype, y); r != MOE_OK) return r;
+  REQUIRE(h != nullptr, "ffn_down: h is NULL");
+  REQUIRE(w != MOE_F8E4M3 || h_scale != nullptr, "ffn_down: fp8 needs h_scale");
+  moe::FfnArgs p{shape->d, shape->inter, n_experts, n_rows, n_rows, expert_offsets, MOE_ROWS_DIRECT, nullptr,
+                 nullptr, nullptr, nullptr, nullptr, w_down, w_d_scale, y_dtype, y, const_cast<void*>(h),
+                 const_cast<float*>(h_scale)};
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(run_down(w, p, st), "moe_ffn_down", st);
+}
+
+moe_status moe_combine(const moe_shape* shape, moe_dtype io, const void* u, const void* y_routed,
+                       const int32_t* row_of, const float* topk_gate, const void* y_shared, void* out, void* stream) {
+  g_err.clear();
+  if (moe_status st = check_shape(shape); st != MOE_OK) return st;
+  REQUIRE(io == MOE_F32 || io == MOE_BF16, "combine: io must be MOE_F32 or MOE_BF16");
+  REQUIRE(u && y_routed && row_of && topk_gate && out, "combine: a required pointer is NULL");
+  REQUIRE(shape->n_shared == 0 || y_shared != nullptr, "combine: y_shared is NULL with n_shared = %d",
+          shape->n_shared);
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_combine(moe::to_shape(*shape), io, u, y_routed, row_of, topk_gate,
+                                    shape->n_shared ? y_shared : nullptr, out, st),
+                "moe_combine", st);
+}
+
+moe_status moe_bias_update(const moe_shape* shape, const int32_t* expert_load, float gamma, float* bias,
+                           void* stream) {
+  g_err.clear();
+  if (moe_status st = check_shape(shape); st != MOE_OK) return st;
+  REQUIRE(expert_load && bias, "bias_update: a required pointer is NULL");
+  REQUIRE(gamma == gamma && gamma >= 0.0f, "bias_update: gamma must be a non-negative number");
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_bias_update(moe::to_shape(*shape), expert_load, gamma, bias, st), "moe_bias_update",
+                st);
+}
+
+moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, const void* w_bf16, void* w_codes,
+                                float* w_scale, void* stream) {
+  g_err.clear();
+  REQUIRE(n_mats > 0 && rows > 0 && cols > 0, "quantize_weights: sizes must be positive");
+  SUPPORT(rows % 128 == 0 && cols % 128 == 0, "quantize_weights: rows (%d) and cols (%d) must be multiples of 128",
+          rows, cols);
+  REQUIRE(w_bf16 && w_codes && w_scale, "quantize_weights: a required pointer is NULL");
+  SUPPORT(static_cast<long long>(n_mats) * (rows / 128) * (cols / 128) < (1LL << 31), "quantize_weights: too many blocks");
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_quantize_weights(n_mats, rows, cols, w_bf16, w_codes, w_scale, st),
+                "moe_quantize_weights", st);
+}
+
+}  // extern "C"

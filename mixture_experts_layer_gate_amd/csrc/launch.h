@@ -1,0 +1,72 @@
+// Internal host-side launchers; the C ABI in api.hip validates arguments and
+// then calls these. Every launcher only enqueues work on `st`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+struct Shape {
+  int T, d, N, G, M, topn, K, Ns, I;
+};
+
+inline Shape to_shape(const moe_shape& s) {
+  return Shape{s.T, s.d, s.n_routed, s.n_groups, s.topk_groups, s.group_topn, s.topk, s.n_shared, s.inter};
+}
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// ---- route
+hipError_t launch_route(const Shape& s, moe_dtype act, const void* u, const void* cent, const float* bias,
+                        int32_t* idx, float* gate, int32_t* load, float* scores, hipStream_t st);
+
+// ---- permute
+size_t permute_ws_bytes(const Shape& s);
+hipError_t launch_permute_maps(const Shape& s, const int32_t* idx, int32_t* offsets, int32_t* perm,
+                               int32_t* row_of, void* ws, hipStream_t st);
+// rows r < n_rows of dst = src[index[r]] (index may be null: identity); dst in
+// dst_dtype (same as src, or E4M3 with 1x128 scales).
+hipError_t launch_rows_copy(int n_rows, int d, moe_dtype src_dtype, const void* src, int src_rows,
+                            const int32_t* index, moe_dtype dst_dtype, void* dst, float* dst_scale,
+                            hipStream_t st);
+
+// ---- combine / bias
+hipError_t launch_combine(const Shape& s, moe_dtype io, const void* u, const void* y, const int32_t* row_of,
+                          const float* gate, const void* ysh, void* out, hipStream_t st);
+hipError_t launch_bias_update(const Shape& s, const int32_t* load, float gamma, float* bias, hipStream_t st);
+
+// ---- expert FFN
+struct FfnArgs {
+  int d, I, n_experts, n_rows, a_rows;
+  const int32_t* offsets;
+  moe_row_mode mode;
+  const int32_t* row_src;
+  const void* a;
+  const float* a_scale;
+  const void* w_gu;
+  const float* w_gu_scale;
+  const void* w_d;
+  const float* w_d_scale;
+  moe_dtype y_dtype;
+  void* y;
+  void* h;         // SwiGLU output [n_rows, I]
+  float* h_scale;  // fp8: [n_rows, I/128]
+};
+size_t ffn_ws_bytes(moe_dtype w, int n_rows, int I);
+hipError_t launch_ffn_f32_gate_up(const FfnArgs& a, hipStream_t st);
+hipError_t launch_ffn_f32_down(const FfnArgs& a, hipStream_t st);
+hipError_t launch_ffn_bf16_gate_up(const FfnArgs& a, hipStream_t st);
+hipError_t launch_ffn_bf16_down(const FfnArgs& a, hipStream_t st);
+hipError_t launch_ffn_fp8_gate_up(const FfnArgs& a, hipStream_t st);
+hipError_t launch_ffn_fp8_down(const FfnArgs& a, hipStream_t st);
+
+// ---- weight preparation
+hipError_t launch_quantize_weights(int n_mats, int rows, int cols, const void* w, void* codes, float* scale,
+                                   hipStream_t st);
+
+}  // namespace moe

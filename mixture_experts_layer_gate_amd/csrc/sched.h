@@ -1,0 +1,98 @@
+// Persistent grouped-GEMM schedule shared by the expert FFN kernels.
+//
+// Work unit = (expert e, n-block, m-block) with m-blocks of BM rows over the
+// expert's ragged row segment [off[e], off[e+1]). Units are numbered expert by
+// expert, n-block by n-block, m-block fastest, so consecutive units share the
+// same weight tile (all m-blocks of one n-block) and the same expert.
+// Workgroup b of a grid of G (G % 8 == 0) takes units v, v+G, v+2G... with
+// v = (b % 8) * (G / 8) + b / 8: workgroups are handed to the 8 XCDs round-robin,
+// so this keeps runs of consecutive units -- one expert's weight and
+// activation tiles -- inside one XCD's L2.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// In-place exclusive scan of a[0..n) in LDS, a[n] = total. Every thread of the
+// block must call it.
+__device__ __forceinline__ void block_exclusive_scan(int* a, int n, int* wtmp /* >= 16 ints */) {
+  const int nt = blockDim.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (n + nt - 1) / nt;
+  const int lo = min(tid * per, n), hi = min(lo + per, n);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += a[i];
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wtmp[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += wtmp[i];
+  const int excl = before + incl - sum;
+  int run = excl;
+  for (int i = lo; i < hi; ++i) {
+    const int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  if (tid == nt - 1) a[n] = excl + sum;
+  __syncthreads();
+}
+
+struct Unit {
+  int e, nb, m0, rows, seg0;  // expert, n-block, first row, valid rows (<= BM), segment start
+};
+
+// Fill cum[0..E] (LDS) with units-before-expert; returns the total.
+__device__ __forceinline__ int build_units(const int32_t* __restrict__ off, int E, int n_rows, int BM, int NB,
+                                           int* cum, int* wtmp) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int lo = clampi(off[e], 0, n_rows);
+    const int hi = clampi(off[e + 1], lo, n_rows);
+    cum[e] = cdiv(hi - lo, BM) * NB;
+  }
+  __syncthreads();
+  block_exclusive_scan(cum, E, wtmp);
+  return cum[E];
+}
+
+__device__ __forceinline__ Unit find_unit(int t, const int32_t* __restrict__ off, int E, int n_rows, int BM,
+                                          const int* cum) {
+  int lo = 0, hi = E;  // largest e with cum[e] <= t
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cum[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int s0 = clampi(off[e], 0, n_rows);
+  const int s1 = clampi(off[e + 1], s0, n_rows);
+  const int nmb = cdiv(s1 - s0, BM);
+  const int local = t - cum[e];
+  Unit u;
+  u.e = e;
+  u.nb = local / nmb;
+  u.m0 = s0 + (local % nmb) * BM;
+  u.rows = min(BM, s1 - u.m0);
+  u.seg0 = s0;
+  return u;
+}
+
+__device__ __forceinline__ int xcd_virtual_block() {
+  const int G = gridDim.x, b = blockIdx.x;
+  return (b & 7) * (G >> 3) + (b >> 3);
+}
+
+// Index of the input row for output row r (absolute) of an expert whose segment starts at seg0.
+__device__ __forceinline__ int source_row(moe_row_mode mode, const int32_t* __restrict__ row_src, int r, int seg0,
+                                          int a_rows) {
+  int s = r;
+  if (mode == MOE_ROWS_GATHER) s = row_src[r];
+  else if (mode == MOE_ROWS_SEGMENT) s = r - seg0;
+  return (s >= 0 && s < a_rows) ? s : -1;
+}
+
+}  // namespace moe

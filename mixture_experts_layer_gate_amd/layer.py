@@ -1,0 +1,195 @@
+"""A DeepSeekMoE layer forward composed from the five libmoe calls.
+
+``MoELayer`` holds the expert weights, centroids and the bias on the GPU and
+runs, on one stream with no host synchronisation:
+
+  moe_route -> moe_permute -> moe_grouped_ffn (routed) -> moe_grouped_ffn
+  (shared) -> moe_combine, then moe_bias_update at the end of a step.
+
+Torch only allocates device memory and provides the stream; every step runs
+in libmoe.so.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import torch
+
+from . import binding as B
+
+
+@dataclass
+class LayerOutputs:
+    topk_idx: torch.Tensor
+    topk_gate: torch.Tensor
+    expert_load: torch.Tensor
+    expert_offsets: torch.Tensor
+    perm_token: torch.Tensor
+    row_of: torch.Tensor
+    y_routed: torch.Tensor
+    y_shared: Optional[torch.Tensor]
+    out: torch.Tensor
+    scores: Optional[torch.Tensor] = None
+    a_q: Optional[torch.Tensor] = None
+    a_scale: Optional[torch.Tensor] = None
+
+
+class MoELayer:
+    """One MoE layer on the current CUDA device.
+
+    cfg: an object with T, d, n_routed, n_groups, topk_groups, group_topn,
+    topk, n_shared, inter, gemm ("f32" | "bf16" | "fp8"), gamma.
+    weights: w_gate_up [N_r,2I,d], w_down [N_r,d,I], s_gate_up [N_s,2I,d],
+    s_down [N_s,d,I] (fp32 or bf16), centroids [N_r,d], bias [N_r] fp32.
+    For fp8 the bf16 weights are block-quantised on the device by
+    moe_quantize_weights and the bf16 copies are dropped unless keep_bf16.
+    """
+
+    def __init__(self, cfg, weights: Dict[str, torch.Tensor], device="cuda", keep_bf16: bool = False,
+                 gather_in_gemm: bool = True):
+        self.cfg = cfg
+        self.shape = B.moe_shape.of(cfg)
+        self.dev = torch.device(device)
+        self.gemm = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_F8E4M3}[cfg.gemm]
+        self.gather_in_gemm = gather_in_gemm
+        to = lambda t: t.to(self.dev).contiguous()
+        self.centroids = to(weights["centroids"])
+        self.bias = weights["bias"].to(self.dev, torch.float32).clone()  # layer-owned state
+        self.act_dtype = self.centroids.dtype
+        if self.gemm == B.MOE_F8E4M3:
+            self.w = {}
+            for k in ("w_gate_up", "w_down", "s_gate_up", "s_down"):
+                src = to(weights[k])
+                n, r, c = src.shape
+                codes = torch.empty((n, r, c), dtype=torch.uint8, device=self.dev)
+                scale = torch.empty((n, r // 128, c // 128), dtype=torch.float32, device=self.dev)
+                if n:
+                    B.moe_quantize_weights(src, codes, scale)
+                self.w[k] = codes
+                self.w[k + "_scale"] = scale
+                if keep_bf16:
+                    self.w[k + "_bf16"] = src
+        else:
+            self.w = {k: to(weights[k]) for k in ("w_gate_up", "w_down", "s_gate_up", "s_down")}
+        self.ws = torch.empty(max(B.moe_workspace_bytes(self.shape, self.gemm), 256), dtype=torch.uint8,
+                              device=self.dev)
+        self._alloc()
+
+    def _alloc(self):
+        c, dev = self.cfg, self.dev
+        T, K, N, d = c.T, c.topk, c.n_routed, c.d
+        ydt = torch.float32 if c.gemm == "f32" else torch.bfloat16
+        self.topk_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        self.topk_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.expert_load = torch.empty((N,), dtype=torch.int32, device=dev)
+        self.scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+        self.expert_offsets = torch.empty((N + 1,), dtype=torch.int32, device=dev)
+        self.perm_token = torch.empty((T * K,), dtype=torch.int32, device=dev)
+        self.row_of = torch.empty((T * K,), dtype=torch.int32, device=dev)
+        self.shared_offsets = (torch.arange(c.n_shared + 1, dtype=torch.int32, device=dev) * T).contiguous()
+        self.y_routed = torch.empty((T * K, d), dtype=ydt, device=dev)
+        self.y_shared = torch.empty((max(c.n_shared, 1) * T, d), dtype=ydt, device=dev)
+        self.out = torch.empty((T, d), dtype=self.act_dtype, device=dev)
+        if self.gemm == B.MOE_F8E4M3:
+            # u quantised once per token (1x128 tiles); the GEMMs gather its rows
+            self.u_q = torch.empty((T, d), dtype=torch.uint8, device=dev)
+            self.u_scale = torch.empty((T, d // 128), dtype=torch.float32, device=dev)
+        elif not self.gather_in_gemm:
+            self.a_perm = torch.empty((T * K, d), dtype=self.act_dtype, device=dev)
+
+    # ---------------------------------------------------------------- steps
+    def route(self, u):
+        B.moe_route(self.shape, u, self.centroids, self.bias, self.topk_idx, self.topk_gate, self.expert_load,
+                    self.scores, self.ws)
+
+    def permute(self, u):
+        if self.gemm == B.MOE_F8E4M3:
+            B.moe_permute(self.shape, self.topk_idx, u, self.expert_offsets, self.perm_token, self.row_of,
+                          self.u_q, B.MOE_F8E4M3, self.u_scale, 0, self.ws)
+        elif self.gather_in_gemm:
+            B.moe_permute(self.shape, self.topk_idx, u, self.expert_offsets, self.perm_token, self.row_of,
+                          None, None, None, 1, self.ws)
+        else:
+            B.moe_permute(self.shape, self.topk_idx, u, self.expert_offsets, self.perm_token, self.row_of,
+                          self.a_perm, None, None, 1, self.ws)
+
+    def ffn_routed(self, u):
+        c = self.cfg
+        n_rows = c.T * c.topk
+        a_scale = None
+        if self.gemm == B.MOE_F8E4M3:
+            a, a_scale, a_rows, mode = self.u_q, self.u_scale, c.T, B.MOE_ROWS_GATHER
+        elif self.gather_in_gemm:
+            a, a_rows, mode = u, c.T, B.MOE_ROWS_GATHER
+        else:
+            a, a_rows, mode = self.a_perm, n_rows, B.MOE_ROWS_DIRECT
+        B.moe_grouped_ffn(self.shape, self.gemm, c.n_routed, n_rows, self.expert_offsets, mode,
+                          self.perm_token if mode == B.MOE_ROWS_GATHER else None, a, a_scale, a_rows,
+                          self.w["w_gate_up"], self.w.get("w_gate_up_scale"), self.w["w_down"],
+                          self.w.get("w_down_scale"), self.y_routed, self.ws)
+
+    def ffn_routed_phases(self, u, between=None):
+        """The routed FFN as its two calls (moe_ffn_gate_up, moe_ffn_down); ``between`` runs in between."""
+        c = self.cfg
+        n_rows = c.T * c.topk
+        if not hasattr(self, "h"):
+            hdt = {B.MOE_F32: torch.float32, B.MOE_BF16: torch.bfloat16, B.MOE_F8E4M3: torch.uint8}[self.gemm]
+            self.h = torch.empty((n_rows, c.inter), dtype=hdt, device=self.dev)
+            self.h_scale = (torch.empty((n_rows, c.inter // 128), dtype=torch.float32, device=self.dev)
+                            if self.gemm == B.MOE_F8E4M3 else None)
+        a_scale = None
+        if self.gemm == B.MOE_F8E4M3:
+            a, a_scale, a_rows, mode = self.u_q, self.u_scale, c.T, B.MOE_ROWS_GATHER
+        elif self.gather_in_gemm:
+            a, a_rows, mode = u, c.T, B.MOE_ROWS_GATHER
+        else:
+            a, a_rows, mode = self.a_perm, n_rows, B.MOE_ROWS_DIRECT
+        B.moe_ffn_gate_up(self.shape, self.gemm, c.n_routed, n_rows, self.expert_offsets, mode,
+                          self.perm_token if mode == B.MOE_ROWS_GATHER else None, a, a_scale, a_rows,
+                          self.w["w_gate_up"], self.w.get("w_gate_up_scale"), self.h, self.h_scale)
+        if between is not None:
+            between()
+        B.moe_ffn_down(self.shape, self.gemm, c.n_routed, n_rows, self.expert_offsets, self.h, self.h_scale,
+                       self.w["w_down"], self.w.get("w_down_scale"), self.y_routed)
+
+    def ffn_shared(self, u):
+        c = self.cfg
+        if not c.n_shared:
+            return
+        if self.gemm == B.MOE_F8E4M3:
+            a, a_scale = self.u_q, self.u_scale
+        else:
+            a, a_scale = u, None
+        B.moe_grouped_ffn(self.shape, self.gemm, c.n_shared, c.n_shared * c.T, self.shared_offsets,
+                          B.MOE_ROWS_SEGMENT, None, a, a_scale, c.T, self.w["s_gate_up"],
+                          self.w.get("s_gate_up_scale"), self.w["s_down"], self.w.get("s_down_scale"),
+                          self.y_shared, self.ws)
+
+    def combine(self, u):
+        B.moe_combine(self.shape, u, self.y_routed, self.row_of, self.topk_gate,
+                      self.y_shared if self.cfg.n_shared else None, self.out)
+
+    def bias_update(self):
+        B.moe_bias_update(self.shape, self.expert_load, self.cfg.gamma, self.bias)
+
+    def forward(self, u: torch.Tensor) -> torch.Tensor:
+        """Layer output for tokens u [T, d] (no bias update)."""
+        u = u.contiguous()
+        self.route(u)
+        self.permute(u)
+        self.ffn_routed(u)
+        self.ffn_shared(u)
+        self.combine(u)
+        return self.out
+
+    def step(self, u: torch.Tensor) -> torch.Tensor:
+        """forward + the step-end bias update."""
+        out = self.forward(u)
+        self.bias_update()
+        return out
+
+    def outputs(self) -> LayerOutputs:
+        return LayerOutputs(self.topk_idx, self.topk_gate, self.expert_load, self.expert_offsets, self.perm_token,
+                            self.row_of, self.y_routed, self.y_shared if self.cfg.n_shared else None, self.out,
+                            self.scores, getattr(self, "u_q", None), getattr(self, "u_scale", None))

@@ -1,0 +1,108 @@
+"""The C ABI loads, exports every call declared in include/moe.h, and rejects
+bad arguments on the host before any HIP call (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_gate_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "moe.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_bias_update"} <= set(names)
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moe_version().startswith(b"moe-gfx950")
+
+
+def _shape(**kw):
+    base = dict(T=64, d=256, n_routed=16, n_groups=4, topk_groups=2, group_topn=2, topk=2, n_shared=1, inter=128)
+    base.update(kw)
+    return B.moe_shape(*[base[k] for k, _ in B.moe_shape._fields_])
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _route(shape, **ptrs):
+    p = dict(u=FAKE, c=FAKE, b=FAKE, i=FAKE, g=FAKE, l=FAKE, s=FAKE)
+    p.update(ptrs)
+    L = B.lib()
+    st = L.moe_route(ctypes.byref(shape), B.MOE_BF16, p["u"], p["c"], p["b"], p["i"], p["g"], p["l"], p["s"],
+                     None, 0, None)
+    return st, L.moe_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(T=0), B.MOE_E_INVALID, "non-positive"),
+    (dict(n_routed=15), B.MOE_E_INVALID, "multiple of n_groups"),
+    (dict(topk_groups=5), B.MOE_E_INVALID, "topk_groups"),
+    (dict(topk=9), B.MOE_E_INVALID, "topk"),
+    (dict(group_topn=5), B.MOE_E_INVALID, "group_topn"),
+    (dict(d=200), B.MOE_E_UNSUPPORTED, "multiple of 128"),
+    (dict(inter=100), B.MOE_E_UNSUPPORTED, "multiple of 128"),
+    (dict(n_routed=2048, n_groups=2048 // 4, topk_groups=2), B.MOE_E_UNSUPPORTED, ""),
+    (dict(topk=17, n_routed=64, n_groups=1, topk_groups=1), B.MOE_E_UNSUPPORTED, "topk"),
+])
+def test_route_rejects_bad_shapes(kw, status, needle):
+    st, msg = _route(_shape(**kw))
+    assert st == status, msg
+    assert needle in msg
+
+
+def test_route_rejects_null_and_missing_workspace():
+    st, msg = _route(_shape(), u=None)
+    assert st == B.MOE_E_INVALID and "NULL" in msg
+    st, msg = _route(_shape(), s=None)   # no scores buffer and no workspace
+    assert st == B.MOE_E_WORKSPACE and "workspace" in msg
+
+
+def test_grouped_ffn_validation():
+    L = B.lib()
+    sh = _shape()
+    args = lambda **o: [ctypes.byref(sh), o.get("w", B.MOE_BF16), o.get("ne", 4), o.get("nr", 10), FAKE,
+                        o.get("mode", B.MOE_ROWS_GATHER), o.get("rs", FAKE), FAKE, o.get("asc", None),
+                        o.get("ar", 10), FAKE, o.get("gs", None), FAKE, o.get("ds", None), o.get("ydt", B.MOE_BF16),
+                        FAKE, None, o.get("ws", 0), None]
+    assert L.moe_grouped_ffn(*args(rs=None)) == B.MOE_E_INVALID
+    assert L.moe_grouped_ffn(*args(mode=7)) == B.MOE_E_INVALID
+    assert L.moe_grouped_ffn(*args(ydt=B.MOE_F32)) == B.MOE_E_INVALID
+    assert L.moe_grouped_ffn(*args(w=B.MOE_F8E4M3)) == B.MOE_E_INVALID     # missing scales
+    assert L.moe_grouped_ffn(*args()) == B.MOE_E_WORKSPACE
+    assert b"workspace" in L.moe_last_error()
+
+
+def test_permute_combine_bias_validation():
+    L = B.lib()
+    sh = _shape()
+    assert L.moe_permute(ctypes.byref(sh), B.MOE_BF16, None, FAKE, FAKE, FAKE, FAKE, None, B.MOE_BF16, None, 1,
+                         None, 0, None) == B.MOE_E_INVALID
+    # gather=0 without quantisation is refused
+    assert L.moe_permute(ctypes.byref(sh), B.MOE_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B.MOE_BF16, None, 0,
+                         FAKE, 1 << 20, None) == B.MOE_E_INVALID
+    assert L.moe_permute(ctypes.byref(sh), B.MOE_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, None, B.MOE_BF16, None, 1,
+                         FAKE, 16, None) == B.MOE_E_WORKSPACE
+    assert L.moe_combine(ctypes.byref(sh), B.MOE_BF16, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_bias_update(ctypes.byref(sh), FAKE, ctypes.c_float(-1.0), FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_quantize_weights(1, 100, 128, FAKE, FAKE, FAKE, None) == B.MOE_E_UNSUPPORTED
+
+
+def test_workspace_size_covers_each_call():
+    sh = _shape(T=8192, d=7168, n_routed=256, n_groups=8, topk_groups=4, topk=8, inter=2048)
+    n = B.moe_workspace_bytes(sh, B.MOE_BF16)
+    assert n >= 8192 * 8 * 2048 * 2         # H for the routed rows in bf16
+    assert n >= 8192 * 256 * 4              # the router scores
+    n8 = B.moe_workspace_bytes(sh, B.MOE_F8E4M3)
+    assert 8192 * 8 * 2048 <= n8 < n
+    assert B.moe_workspace_bytes(_shape(T=-1), B.MOE_BF16) == 0

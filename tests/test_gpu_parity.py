@@ -1,0 +1,338 @@
+"""GPU parity of each libmoe call and of the whole layer against the CPU oracle.
+
+Every call is fed inputs that the generator or the oracle produced (never the
+output of another GPU call), so a near-tie routing flip cannot cascade. The
+small workloads are checked element by element; the V3-shaped one on its full
+routing and permutation and on sampled experts / tokens for the FFN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_inputs import get_config, generate, generate_expert
+from mixture_experts_layer_gate_amd import binding as B
+from mixture_experts_layer_gate_amd import MoELayer
+from parity import TOL, np64, npi, rel_l2, report, routing_mismatches
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _i32(x):
+    return torch.as_tensor(np.asarray(x), dtype=torch.int32, device=DEV).contiguous()
+
+
+_CACHE = {}
+
+
+def _inputs(name, **over):
+    key = (name, tuple(sorted(over.items())))
+    if key not in _CACHE:
+        _CACHE.clear()
+        torch.cuda.empty_cache()
+        cfg = get_config(name, **over)
+        _CACHE[key] = (cfg, generate(cfg, DEV))
+    return _CACHE[key]
+
+
+def _oracle_route(cfg, inp):
+    return oracle.route(inp["u"], inp["centroids"], inp["bias"], cfg.n_groups, cfg.topk_groups, cfg.group_topn,
+                        cfg.topk)
+
+
+def _ws(cfg):
+    sh = B.moe_shape.of(cfg)
+    gemm = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_F8E4M3}[cfg.gemm]
+    return torch.empty(B.moe_workspace_bytes(sh, gemm), dtype=torch.uint8, device=DEV)
+
+
+ROUTE_CASES = [
+    ("c1", {}),
+    ("c2", {}),
+    ("c2", dict(n_groups=1, topk_groups=1)),           # no group limit
+    ("c2", dict(topk_groups=8)),                        # every group kept
+    ("c2", dict(T=1000, n_groups=4, topk_groups=1, topk=3, group_topn=3)),  # ragged T, 3-term group score
+    ("c3", {}),
+]
+
+
+@pytest.mark.parametrize("name,over", ROUTE_CASES)
+def test_route(name, over):
+    cfg, inp = _inputs(name, **over)
+    sh = B.moe_shape.of(cfg)
+    T, K, N = cfg.T, cfg.topk, cfg.n_routed
+    idx = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    gate = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    load = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    scores = torch.empty((T, N), dtype=torch.float32, device=DEV)
+    B.moe_route(sh, inp["u"], inp["centroids"], inp["bias"], idx, gate, load, scores, _ws(cfg))
+    torch.cuda.synchronize()
+    r = _oracle_route(cfg, inp)
+    ds = np.abs(np64(scores) - r["s"]).max()
+    print(f"[parity] {name} {over}: max |s_gpu - s_oracle| = {ds:.2e}")
+    assert ds < 1e-5
+    bad = routing_mismatches(idx, r)
+    gi = npi(idx)
+    assert np.all(np.diff(gi, axis=1) > 0), "topk_idx must be ascending per token"
+    assert np.array_equal(npi(load), np.bincount(gi.ravel(), minlength=N))
+    if bad.size == 0:
+        assert np.array_equal(npi(load), r["load"])
+    ok = np.ones(T, dtype=bool)
+    ok[bad] = False
+    report(f"{name} gates", rel_l2(np64(gate)[ok], r["gate"][ok]), 1e-5)
+    # groups touched per token never exceed M
+    S = N // cfg.n_groups
+    assert max(len(set(row)) for row in (gi // S)) <= cfg.topk_groups
+
+
+PERM_CASES = ["c1", "c2", "c3", "one_expert", "ragged", "single_token"]
+
+
+def _perm_idx(case):
+    rng = np.random.default_rng(11)
+    if case in ("c1", "c2", "c3"):
+        cfg, inp = _inputs(case)
+        return cfg, _oracle_route(cfg, inp)["idx"]
+    if case == "one_expert":      # every token picks experts {0..K-1}: most experts empty
+        cfg = get_config("c2", T=777)
+        return cfg, np.tile(np.arange(cfg.topk), (cfg.T, 1))
+    if case == "ragged":
+        cfg = get_config("c2", T=4096 + 37)
+        return cfg, np.sort(np.stack([rng.choice(cfg.n_routed, cfg.topk, replace=False) for _ in range(cfg.T)]), 1)
+    cfg = get_config("c3", T=1)
+    return cfg, np.sort(rng.choice(cfg.n_routed, cfg.topk, replace=False))[None, :]
+
+
+@pytest.mark.parametrize("case", PERM_CASES)
+def test_permute_maps(case):
+    cfg, idx = _perm_idx(case)
+    sh = B.moe_shape.of(cfg)
+    T, K, N = cfg.T, cfg.topk, cfg.n_routed
+    off = torch.full((N + 1,), -1, dtype=torch.int32, device=DEV)
+    perm = torch.full((T * K,), -1, dtype=torch.int32, device=DEV)
+    row_of = torch.full((T * K,), -1, dtype=torch.int32, device=DEV)
+    B.moe_permute(sh, _i32(idx), None, off, perm, row_of, workspace=_ws(cfg))
+    torch.cuda.synchronize()
+    o_off, o_perm, o_row = oracle.permute(idx, N)
+    assert np.array_equal(npi(off), o_off)
+    assert np.array_equal(npi(perm), o_perm)
+    assert np.array_equal(npi(row_of), o_row)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_permute_gather_rows(name):
+    cfg, inp = _inputs(name)
+    sh = B.moe_shape.of(cfg)
+    T, K, N, d = cfg.T, cfg.topk, cfg.n_routed, cfg.d
+    r = _oracle_route(cfg, inp)
+    o_off, o_perm, _ = oracle.permute(r["idx"], N)
+    off = torch.empty((N + 1,), dtype=torch.int32, device=DEV)
+    perm = torch.empty((T * K,), dtype=torch.int32, device=DEV)
+    row_of = torch.empty((T * K,), dtype=torch.int32, device=DEV)
+    a = torch.empty((T * K, d), dtype=inp["u"].dtype, device=DEV)
+    B.moe_permute(sh, _i32(r["idx"]), inp["u"], off, perm, row_of, a, None, None, 1, _ws(cfg))
+    torch.cuda.synchronize()
+    assert torch.equal(a.cpu(), inp["u"].cpu()[torch.from_numpy(o_perm)])
+
+
+@pytest.mark.parametrize("gather", [0, 1])
+def test_permute_fp8_quantisation_bit_exact(gather):
+    cfg, inp = _inputs("c2")
+    sh = B.moe_shape.of(cfg)
+    T, K, N, d = cfg.T, cfg.topk, cfg.n_routed, cfg.d
+    r = _oracle_route(cfg, inp)
+    o_off, o_perm, _ = oracle.permute(r["idx"], N)
+    rows = T * K if gather else T
+    u = inp["u"].clone()
+    u[5] = 0                         # an all-zero row: scale 1, zero codes
+    u[9, :128] = 0
+    off = torch.empty((N + 1,), dtype=torch.int32, device=DEV)
+    perm = torch.empty((T * K,), dtype=torch.int32, device=DEV)
+    row_of = torch.empty((T * K,), dtype=torch.int32, device=DEV)
+    q = torch.empty((rows, d), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((rows, d // 128), dtype=torch.float32, device=DEV)
+    B.moe_permute(sh, _i32(r["idx"]), u, off, perm, row_of, q, B.MOE_F8E4M3, sc, gather, _ws(cfg))
+    torch.cuda.synchronize()
+    codes, scale = oracle.quantize_tiles(u.cpu().float().numpy())
+    if gather:
+        codes, scale = codes[o_perm], scale[o_perm]
+    assert np.array_equal(q.cpu().numpy(), codes)
+    assert np.array_equal(sc.cpu().numpy(), scale)
+
+
+def test_quantize_weights_bit_exact():
+    cfg, inp = _inputs("c2")
+    w = inp["w_gate_up"][:3].contiguous()
+    n, rr, cc = w.shape
+    codes = torch.empty((n, rr, cc), dtype=torch.uint8, device=DEV)
+    scale = torch.empty((n, rr // 128, cc // 128), dtype=torch.float32, device=DEV)
+    B.moe_quantize_weights(w, codes, scale)
+    torch.cuda.synchronize()
+    for e in range(n):
+        oc, os_ = oracle.quantize_blocks(w[e].cpu().float().numpy())
+        assert np.array_equal(codes[e].cpu().numpy(), oc)
+        assert np.array_equal(scale[e].cpu().numpy(), os_)
+
+
+def _oracle_ffn_rows(cfg, inp, e, rows_tok, shared=False, wq=None):
+    u = np64(inp["u"])
+    wg = inp["s_gate_up" if shared else "w_gate_up"][e].cpu()
+    wd = inp["s_down" if shared else "w_down"][e].cpu()
+    return oracle.expert_ffn(u[rows_tok], wg, wd, cfg.gemm, wq)
+
+
+@pytest.mark.parametrize("name,mode", [("c1", "gather"), ("c1", "direct"), ("c2", "gather"), ("c2", "direct")])
+def test_grouped_ffn_routed(name, mode):
+    cfg, inp = _inputs(name)
+    sh = B.moe_shape.of(cfg)
+    T, K, N, d = cfg.T, cfg.topk, cfg.n_routed, cfg.d
+    r = _oracle_route(cfg, inp)
+    o_off, o_perm, _ = oracle.permute(r["idx"], N)
+    wdt = B.MOE_F32 if cfg.gemm == "f32" else B.MOE_BF16
+    y = torch.empty((T * K, d), dtype=torch.float32 if cfg.gemm == "f32" else torch.bfloat16, device=DEV)
+    if mode == "gather":
+        a, a_rows, m, src = inp["u"], T, B.MOE_ROWS_GATHER, _i32(o_perm)
+    else:
+        a = inp["u"][torch.from_numpy(o_perm).to(DEV)].contiguous()
+        a_rows, m, src = T * K, B.MOE_ROWS_DIRECT, None
+    B.moe_grouped_ffn(sh, wdt, N, T * K, _i32(o_off), m, src, a, None, a_rows, inp["w_gate_up"], None,
+                      inp["w_down"], None, y, _ws(cfg))
+    torch.cuda.synchronize()
+    ref = np.zeros((T * K, d))
+    for e in range(N):
+        lo, hi = o_off[e], o_off[e + 1]
+        if hi > lo:
+            ref[lo:hi] = _oracle_ffn_rows(cfg, inp, e, o_perm[lo:hi])
+    report(f"{name} routed y ({mode})", rel_l2(y, ref), TOL[cfg.gemm])
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_grouped_ffn_shared_segments(name):
+    cfg, inp = _inputs(name)
+    sh = B.moe_shape.of(cfg)
+    T, Ns, d = cfg.T, cfg.n_shared, cfg.d
+    wdt = B.MOE_F32 if cfg.gemm == "f32" else B.MOE_BF16
+    y = torch.empty((Ns * T, d), dtype=torch.float32 if cfg.gemm == "f32" else torch.bfloat16, device=DEV)
+    off = _i32(np.arange(Ns + 1) * T)
+    B.moe_grouped_ffn(sh, wdt, Ns, Ns * T, off, B.MOE_ROWS_SEGMENT, None, inp["u"], None, T, inp["s_gate_up"],
+                      None, inp["s_down"], None, y, _ws(cfg))
+    torch.cuda.synchronize()
+    ref = np.concatenate([_oracle_ffn_rows(cfg, inp, s, np.arange(T), shared=True) for s in range(Ns)])
+    report(f"{name} shared y", rel_l2(y, ref), TOL[cfg.gemm])
+
+
+def test_grouped_ffn_ragged_and_empty_experts():
+    """Segments of 0, 1, 127, 128, 129 and 300 rows across experts (bf16)."""
+    cfg = get_config("c2", n_routed=8, n_groups=1, topk_groups=1, T=512, topk=2)
+    inp = generate(cfg, DEV)
+    sh = B.moe_shape.of(cfg)
+    sizes = [0, 1, 127, 128, 129, 0, 300, 339]
+    assert sum(sizes) == cfg.T * cfg.topk
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    src = np.random.default_rng(5).integers(0, cfg.T, off[-1])
+    y = torch.empty((off[-1], cfg.d), dtype=torch.bfloat16, device=DEV)
+    B.moe_grouped_ffn(sh, B.MOE_BF16, 8, int(off[-1]), _i32(off), B.MOE_ROWS_GATHER, _i32(src), inp["u"], None,
+                      cfg.T, inp["w_gate_up"], None, inp["w_down"], None, y, _ws(cfg))
+    torch.cuda.synchronize()
+    ref = np.zeros((off[-1], cfg.d))
+    for e in range(8):
+        if sizes[e]:
+            ref[off[e]:off[e + 1]] = _oracle_ffn_rows(cfg, inp, e, src[off[e]:off[e + 1]])
+    report("ragged y", rel_l2(y, ref), TOL["bf16"])
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_combine(name):
+    cfg, inp = _inputs(name)
+    sh = B.moe_shape.of(cfg)
+    T, K, N, d, Ns = cfg.T, cfg.topk, cfg.n_routed, cfg.d, cfg.n_shared
+    rng = np.random.default_rng(3)
+    r = _oracle_route(cfg, inp)
+    _, _, o_row = oracle.permute(r["idx"], N)
+    dt = inp["u"].dtype
+    # y inputs drawn here (the combine is linear; any y exercises it)
+    y = torch.from_numpy(rng.standard_normal((T * K, d))).to(dt).to(DEV)
+    ysh = torch.from_numpy(rng.standard_normal((Ns * T, d))).to(dt).to(DEV)
+    out = torch.empty((T, d), dtype=dt, device=DEV)
+    B.moe_combine(sh, inp["u"], y, _i32(o_row), torch.from_numpy(r["gate"]).float().to(DEV), ysh, out)
+    torch.cuda.synchronize()
+    g32 = r["gate"].astype(np.float32).astype(np.float64)
+    ref = oracle.combine(inp["u"], y, o_row, g32, np64(ysh).reshape(Ns, T, d))
+    report(f"{name} combine out", rel_l2(out, ref), TOL[cfg.gemm] if cfg.gemm == "f32" else 4e-3)
+
+
+def test_bias_update_bit_exact():
+    cfg = get_config("c2")
+    sh = B.moe_shape.of(cfg)
+    N, mean = cfg.n_routed, cfg.T * cfg.topk // cfg.n_routed
+    rng = np.random.default_rng(9)
+    load = rng.integers(mean - 3, mean + 4, N)
+    load[:4] = mean
+    b0 = rng.uniform(-0.01, 0.01, N).astype(np.float32)
+    bias = torch.from_numpy(b0).to(DEV)
+    B.moe_bias_update(sh, _i32(load), 0.001, bias)
+    torch.cuda.synchronize()
+    assert np.array_equal(bias.cpu().numpy(), oracle.bias_update(b0, load, cfg.T, cfg.topk, 0.001))
+
+
+@pytest.mark.parametrize("name,gather", [("c1", True), ("c1", False), ("c2", True)])
+def test_layer_end_to_end(name, gather):
+    cfg, inp = _inputs(name)
+    layer = MoELayer(cfg, inp, DEV, gather_in_gemm=gather)
+    out = layer.step(inp["u"])
+    torch.cuda.synchronize()
+    res = oracle.layer_forward(cfg, inp)
+    bad = routing_mismatches(layer.topk_idx, res["route"])
+    ok = np.ones(cfg.T, dtype=bool)
+    ok[bad] = False
+    u64 = np64(inp["u"])
+    report(f"{name} out", rel_l2(np64(out)[ok], res["out"][ok]), TOL[cfg.gemm])
+    report(f"{name} out - u", rel_l2((np64(out) - u64)[ok], (res["out"] - u64)[ok]), TOL[cfg.gemm])
+    if bad.size == 0:
+        assert np.array_equal(layer.bias.cpu().numpy(), res["bias"])
+        assert np.array_equal(npi(layer.expert_offsets), res["offsets"])
+
+
+# ------------------------------------------------------------------ V3 shape, sampled
+
+def test_v3_bf16_sampled_experts_and_tokens():
+    cfg, inp = _inputs("c3")
+    T, K, N, d = cfg.T, cfg.topk, cfg.n_routed, cfg.d
+    layer = MoELayer(cfg, inp, DEV)
+    out = layer.step(inp["u"])
+    torch.cuda.synchronize()
+    r = _oracle_route(cfg, inp)
+    bad = routing_mismatches(layer.topk_idx, r)
+    o_off, o_perm, o_row = oracle.permute(r["idx"], N)
+    if bad.size == 0:
+        assert np.array_equal(npi(layer.expert_offsets), o_off)
+        assert np.array_equal(npi(layer.perm_token), o_perm)
+        assert np.array_equal(npi(layer.row_of), o_row)
+        b_ref = oracle.bias_update(inp["bias"].cpu().numpy(), r["load"], T, K, cfg.gamma)
+        assert np.array_equal(layer.bias.cpu().numpy(), b_ref)
+    load = r["load"]
+    experts = sorted({0, N - 1, int(np.argmax(load)), int(np.argmin(load)), 77})
+    y = layer.y_routed
+    goff = npi(layer.expert_offsets)
+    gperm = npi(layer.perm_token)
+    for e in experts:
+        lo, hi = goff[e], goff[e + 1]
+        if hi == lo:
+            continue
+        toks = gperm[lo:hi]
+        ref = _oracle_ffn_rows(cfg, inp, e, toks)
+        report(f"c3 expert {e} ({hi - lo} rows) y", rel_l2(y[lo:hi], ref), TOL["bf16"])
+    sample = np.random.default_rng(0).choice(T, 64, replace=False)
+    ref = _oracle_ffn_rows(cfg, inp, 0, sample, shared=True)
+    report("c3 shared y (64 tokens)", rel_l2(layer.y_shared[torch.from_numpy(sample).to(DEV)], ref), TOL["bf16"])
+    # whole-layer output on a few tokens, every FFN recomputed by the oracle
+    toks = [t for t in np.random.default_rng(1).choice(T, 6, replace=False) if t not in set(bad)][:4]
+    u64 = np64(inp["u"])
+    for t in toks:
+        acc = u64[t] + _oracle_ffn_rows(cfg, inp, 0, [t], shared=True)[0]
+        for k in range(K):
+            acc = acc + r["gate"][t, k] * _oracle_ffn_rows(cfg, inp, int(r["idx"][t, k]), [t])[0]
+        report(f"c3 out token {t}", rel_l2(np64(out[t]), acc), TOL["bf16"])
+        report(f"c3 out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["bf16"])
