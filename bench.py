@@ -51,7 +51,8 @@ def recorded_traffic(kernel: str, workload: str):
     import re
     csrc = os.path.join(ROOT, "mixture_experts_layer_gate_amd", "csrc")
     h = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in FFN_SOURCES)).hexdigest()[:16]
-    for name in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+    pdir = os.path.join(ROOT, "profiles")
+    for name in (sorted(os.listdir(pdir)) if os.path.isdir(pdir) else []):
         for line in open(os.path.join(ROOT, "profiles", name)):
             m = re.match(r"traffic-record: (\{.*\})", line.strip())
             if m:

@@ -181,6 +181,7 @@ moe_status check_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int
   SUPPORT(static_cast<long long>(n_rows) * (d > I ? d : I) < (1LL << 40), "grouped_ffn: too many rows");
   REQUIRE(offsets != nullptr, "grouped_ffn: expert_offsets is NULL");
   REQUIRE(w == MOE_F32 || w == MOE_BF16 || w == MOE_F8E4M3, "grouped_ffn: bad weight dtype %d", static_cast<int>(w));
+  SUPPORT(w != MOE_F8E4M3 || d % 256 == 0, "grouped_ffn: the fp8 path needs d (%d) to be a multiple of 256", d);
   (void)phase;
   return MOE_OK;
 }

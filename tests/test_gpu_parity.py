@@ -336,3 +336,83 @@ def test_v3_bf16_sampled_experts_and_tokens():
             acc = acc + r["gate"][t, k] * _oracle_ffn_rows(cfg, inp, int(r["idx"][t, k]), [t])[0]
         report(f"c3 out token {t}", rel_l2(np64(out[t]), acc), TOL["bf16"])
         report(f"c3 out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["bf16"])
+
+
+# ------------------------------------------------------------------ fp8 (E4M3, 1x128 / 128x128 scales)
+
+_WQ = {}
+
+
+def _oracle_wq(inp, e, shared=False):
+    key = (id(inp), e, shared)
+    if key in _WQ:
+        return _WQ[key]
+    if len(_WQ) > 48:
+        _WQ.clear()
+    wg = inp["s_gate_up" if shared else "w_gate_up"][e].cpu().float().numpy()
+    wd = inp["s_down" if shared else "w_down"][e].cpu().float().numpy()
+    gq, gs = oracle.quantize_blocks(wg)
+    dq, ds = oracle.quantize_blocks(wd)
+    _WQ[key] = (gq, gs, dq, ds)
+    return _WQ[key]
+
+
+def _check_fp8_experts(cfg, inp, layer, experts, tag):
+    goff = npi(layer.expert_offsets)
+    gperm = npi(layer.perm_token)
+    u32 = inp["u"].cpu().float().numpy()
+    for e in experts:
+        lo, hi = goff[e], goff[e + 1]
+        if hi == lo:
+            continue
+        wq = _oracle_wq(inp, e)
+        ref, aux = oracle.ffn_fp8(u32[gperm[lo:hi]], *wq, return_h=True)
+        report(f"{tag} fp8 expert {e} ({hi - lo} rows) y", rel_l2(layer.y_routed[lo:hi], ref), TOL["fp8"])
+        if hasattr(layer, "h"):
+            codes = layer.h[lo:hi].cpu().numpy()
+            same = float(np.mean(codes == aux["h_codes"]))
+            sdiff = np.max(np.abs(layer.h_scale[lo:hi].cpu().numpy() / aux["h_scale"] - 1))
+            print(f"[parity] {tag} expert {e}: H codes equal {same:.4f}, max rel scale diff {sdiff:.2e}")
+            assert same > 0.99 and sdiff < 1e-4
+
+
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_fp8_layer_sampled(name):
+    over = dict(gemm="fp8") if name == "c2" else {}
+    cfg, inp = _inputs(name, **over)
+    T, K, N, d = cfg.T, cfg.topk, cfg.n_routed, cfg.d
+    layer = MoELayer(cfg, inp, DEV)
+    layer.route(inp["u"])
+    layer.permute(inp["u"])
+    layer.ffn_routed_phases(inp["u"])       # keeps H codes for the diagnostic
+    layer.ffn_shared(inp["u"])
+    layer.combine(inp["u"])
+    layer.bias_update()
+    out = layer.out
+    torch.cuda.synchronize()
+    r = _oracle_route(cfg, inp)
+    bad = routing_mismatches(layer.topk_idx, r)
+    # token quantisation is bit-exact with the oracle's 1x128 rule
+    codes, scale = oracle.quantize_tiles(inp["u"].cpu().float().numpy())
+    assert np.array_equal(layer.u_q.cpu().numpy(), codes)
+    assert np.array_equal(layer.u_scale.cpu().numpy(), scale)
+    load = r["load"]
+    experts = sorted({0, N - 1, int(np.argmax(load)), int(np.argmin(load)), N // 3})
+    _check_fp8_experts(cfg, inp, layer, experts, name)
+    u32 = inp["u"].cpu().float().numpy()
+    sample = np.random.default_rng(0).choice(T, 64, replace=False)
+    sq = _oracle_wq(inp, 0, shared=True)
+    ref_sh = oracle.ffn_fp8(u32[sample], *sq)
+    report(f"{name} fp8 shared y (64 tokens)", rel_l2(layer.y_shared[torch.from_numpy(sample).to(DEV)], ref_sh),
+           TOL["fp8"])
+    n_tok = 3 if T <= 4096 else 1
+    toks = [t for t in np.random.default_rng(1).choice(T, 6, replace=False) if t not in set(bad)][:n_tok]
+    u64 = np64(inp["u"])
+    for t in toks:
+        acc = u64[t].copy()
+        for sh_e in range(cfg.n_shared):
+            acc = acc + oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, sh_e, shared=True))[0]
+        for k in range(K):
+            e = int(r["idx"][t, k])
+            acc = acc + r["gate"][t, k] * oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, e))[0]
+        report(f"{name} fp8 out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["fp8"])
