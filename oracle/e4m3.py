@@ -19,8 +19,8 @@ import numpy as np
 E4M3_MAX = 448.0
 
 
-def e4m3_decode(codes) -> np.ndarray:
-    """Decode uint8 codes to float64 (NaN for the two NaN codes)."""
+def _decode_fields(codes) -> np.ndarray:
+    """Decode from the bit fields (the definition)."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
@@ -28,29 +28,54 @@ def e4m3_decode(codes) -> np.ndarray:
     sub = m / 8.0 * 2.0 ** -6
     nrm = (1.0 + m / 8.0) * np.ldexp(1.0, (e - 7).astype(np.int64))
     v = np.where(e == 0, sub, nrm) * sign
-    v = np.where((c & 0x7F) == 0x7F, np.nan, v)
-    return v
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
 
 
-# Non-negative finite values in code order 0x00..0x7E; the order of codes is
-# also the order of values, which the encoder's search relies on.
-_GRID = e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+_TABLE = _decode_fields(np.arange(256, dtype=np.uint8))       # value of every code
+_GRID = _TABLE[:0x7F]                                         # non-negative finite values, code order
 assert np.all(np.diff(_GRID) > 0)
 
 
+def e4m3_decode(codes) -> np.ndarray:
+    """Decode uint8 codes to float64 (NaN for the two NaN codes)."""
+    return _TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
 def e4m3_encode(x) -> np.ndarray:
-    """Round float values to E4M3 codes: saturate to 448, nearest, ties to even."""
+    """Round float values to E4M3 codes: saturate to 448, nearest, ties to even.
+
+    Within a binade [2^E, 2^(E+1)) (E >= -6) the representable values are the
+    multiples of the quantum 2^(E-3); below 2^-6 the quantum is 2^-9. Rounding
+    to the nearest multiple with ties to the even multiple is exactly rounding
+    to the nearest code with ties to the even mantissa, and a carry into the
+    next binade lands on its first value. Division and multiplication by the
+    power-of-two quantum are exact.
+    """
     x = np.asarray(x, dtype=np.float64)
     neg = np.signbit(x)
     a = np.minimum(np.abs(x), E4M3_MAX)
-    hi = np.searchsorted(_GRID, a, side="left")          # _GRID[hi-1] < a <= _GRID[hi]
-    hi = np.clip(hi, 0, len(_GRID) - 1)
+    _, ex = np.frexp(a)                     # a = m * 2^ex, m in [0.5, 1)  =>  binade E = ex - 1
+    q = np.ldexp(1.0, np.maximum(ex - 1, -6) - 3)
+    v = np.minimum(np.rint(a / q) * q, E4M3_MAX)
+    # code of the grid value v: exponent field E + 7 and mantissa v / 2^(E-3) - 8 in
+    # the normal range, v / 2^-9 below 2^-6
+    _, ev = np.frexp(v)
+    ev = ev - 1
+    normal = v >= 2.0 ** -6
+    code = np.where(normal, (ev + 7) * 8 + (np.ldexp(v, 3 - ev) - 8), np.ldexp(v, 9)).astype(np.uint8)
+    code |= np.where(neg, 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def e4m3_encode_nearest(x) -> np.ndarray:
+    """Reference encoder by exhaustive nearest-value search (slow; used to cross-check)."""
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_GRID, a, side="left"), 0, len(_GRID) - 1)
     lo = np.clip(hi - 1, 0, len(_GRID) - 1)
-    d_lo = a - _GRID[lo]
-    d_hi = _GRID[hi] - a
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo)
-    code = np.where(a == _GRID[hi], hi, code)
-    code = code.astype(np.uint8) | np.where(neg, 0x80, 0).astype(np.uint8)
-    code = np.where(np.isnan(x), np.uint8(0x7F), code)
-    return code.astype(np.uint8)
+    d_lo, d_hi = a - _GRID[lo], _GRID[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    code = np.where(a == _GRID[hi], hi, code).astype(np.uint8)
+    code |= np.where(neg, 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)

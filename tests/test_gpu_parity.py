@@ -416,3 +416,46 @@ def test_fp8_layer_sampled(name):
             e = int(r["idx"][t, k])
             acc = acc + r["gate"][t, k] * oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, e))[0]
         report(f"{name} fp8 out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["fp8"])
+
+
+def test_v4_decode_fp8_ten_bias_steps():
+    """Zipf-skewed decode batch, fp8: 10 steps of route -> FFN -> combine -> bias update.
+
+    Selections and the bias trajectory are compared at every step; the layer
+    output on a sampled token and the most popular expert's rows at steps 0 and 9.
+    """
+    from moe_inputs import generate_tokens
+    cfg, inp = _inputs("c5")
+    T, K, N = cfg.T, cfg.topk, cfg.n_routed
+    layer = MoELayer(cfg, inp, DEV)
+    b_or = inp["bias"].cpu().numpy().copy()
+    flips = 0
+    for step in range(cfg.steps):
+        u = generate_tokens(cfg, DEV, step)
+        out = layer.step(u)
+        torch.cuda.synchronize()
+        r = oracle.route(u, inp["centroids"], b_or, cfg.n_groups, cfg.topk_groups, cfg.group_topn, K)
+        bad = routing_mismatches(layer.topk_idx, r)
+        flips += bad.size
+        load = r["load"]
+        print(f"[parity] c5 step {step}: experts touched {int((load > 0).sum())}, empty {int((load == 0).sum())}, "
+              f"max load {int(load.max())}, flips {bad.size}")
+        if step in (0, cfg.steps - 1):
+            u32 = u.cpu().float().numpy()
+            u64 = u.cpu().double().numpy()
+            e_top = int(np.argmax(load))
+            if bad.size == 0:
+                goff, gperm = npi(layer.expert_offsets), npi(layer.perm_token)
+                lo, hi = goff[e_top], goff[e_top + 1]
+                ref = oracle.ffn_fp8(u32[gperm[lo:hi]], *_oracle_wq(inp, e_top))
+                report(f"c5 step {step} expert {e_top} ({hi - lo} rows) y", rel_l2(layer.y_routed[lo:hi], ref),
+                       TOL["fp8"])
+            t = int([x for x in range(T) if x not in set(bad)][7])
+            acc = u64[t] + oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, 0, shared=True))[0]
+            for k in range(K):
+                acc = acc + r["gate"][t, k] * oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, int(r["idx"][t, k])))[0]
+            report(f"c5 step {step} out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["fp8"])
+        b_or = oracle.bias_update(b_or, load, T, K, cfg.gamma)
+        if flips == 0:
+            assert np.array_equal(layer.bias.cpu().numpy(), b_or), f"bias differs after step {step}"
+    print(f"[parity] c5: {flips} exempt near-tie flips over {cfg.steps} steps; final |b| max {np.abs(b_or).max():.4f}")

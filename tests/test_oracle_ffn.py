@@ -41,6 +41,18 @@ def test_p10_encode_matches_library_rne_in_range():
     assert np.array_equal(e4m3_encode(vals), lib)
 
 
+def test_p10_quantum_encoder_matches_nearest_search():
+    from oracle.e4m3 import e4m3_encode_nearest
+    rng = np.random.default_rng(12)
+    grid = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (grid[:-1] + grid[1:]) / 2
+    eps = np.nextafter(mids, np.inf) - mids
+    vals = np.concatenate([grid, mids, mids + eps, mids - eps, rng.uniform(0, 500, 200000),
+                           np.exp(rng.uniform(np.log(1e-5), np.log(600), 200000)), [0.0, 448.0, 464.0, 480.0, 1e9]])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    assert np.array_equal(e4m3_encode(vals), e4m3_encode_nearest(vals))
+
+
 def test_p10_saturation_and_roundtrip_error():
     assert e4m3_encode(np.float32(1e6)) == 0x7E and e4m3_encode(np.float32(-500.0)) == 0xFE
     x = np.random.default_rng(1).uniform(2.0 ** -6, 448, 100000)
