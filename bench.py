@@ -42,7 +42,7 @@ def parse():
     return ap.parse_args()
 
 
-FFN_SOURCES = ["ffn_bf16.hip", "gemm_bf16.h", "sched.h", "common.h"]
+FFN_SOURCES = ["ffn_bf16.hip", "gemm_pipe.h", "sched.h", "common.h"]
 
 
 def recorded_traffic(kernel: str, workload: str):

@@ -182,14 +182,21 @@ moe_status check_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int
   REQUIRE(offsets != nullptr, "grouped_ffn: expert_offsets is NULL");
   REQUIRE(w == MOE_F32 || w == MOE_BF16 || w == MOE_F8E4M3, "grouped_ffn: bad weight dtype %d", static_cast<int>(w));
   SUPPORT(w != MOE_F8E4M3 || d % 256 == 0, "grouped_ffn: the fp8 path needs d (%d) to be a multiple of 256", d);
+  // the bf16 kernels address H and one expert's weight matrices through 32-bit byte offsets
+  SUPPORT(w != MOE_BF16 || (static_cast<long long>(n_rows) * I * 2 < (1LL << 32) &&
+                            static_cast<long long>(2 * I) * d * 2 < (1LL << 32)),
+          "grouped_ffn: bf16 path needs n_rows * inter and 2 * inter * d below 2^31 elements");
   (void)phase;
   return MOE_OK;
 }
 
-moe_status check_gate_up(moe_dtype w, moe_row_mode mode, const int32_t* row_src, const void* a,
-                         const float* a_scale, int32_t a_rows, const void* w_gate_up, const float* w_gu_scale) {
+moe_status check_gate_up(const moe_shape* shape, moe_dtype w, moe_row_mode mode, const int32_t* row_src,
+                         const void* a, const float* a_scale, int32_t a_rows, const void* w_gate_up,
+                         const float* w_gu_scale) {
   REQUIRE(a && w_gate_up, "grouped_ffn: a or w_gate_up is NULL");
   REQUIRE(a_rows > 0, "grouped_ffn: a_rows must be positive");
+  SUPPORT(w != MOE_BF16 || static_cast<long long>(a_rows) * shape->d * 2 < (1LL << 32),
+          "grouped_ffn: bf16 path needs a_rows * d below 2^31 elements");
   REQUIRE(mode == MOE_ROWS_DIRECT || mode == MOE_ROWS_GATHER || mode == MOE_ROWS_SEGMENT,
           "grouped_ffn: bad row mode %d", static_cast<int>(mode));
   REQUIRE(mode != MOE_ROWS_GATHER || row_src != nullptr, "grouped_ffn: MOE_ROWS_GATHER needs row_src");
@@ -228,7 +235,7 @@ moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_expert
                            size_t ws_bytes, void* stream) {
   g_err.clear();
   if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 0); r != MOE_OK) return r;
-  if (moe_status r = check_gate_up(w, mode, row_src, a, a_scale, a_rows, w_gate_up, w_gu_scale); r != MOE_OK)
+  if (moe_status r = check_gate_up(shape, w, mode, row_src, a, a_scale, a_rows, w_gate_up, w_gu_scale); r != MOE_OK)
     return r;
   if (moe_status r = check_down(w, w_down, w_d_scale, y_dtype, y); r != MOE_OK) return r;
   const int d = shape->d, I = shape->inter;
@@ -252,7 +259,7 @@ moe_status moe_ffn_gate_up(const moe_shape* shape, moe_dtype w, int32_t n_expert
                            void* h, float* h_scale, void* stream) {
   g_err.clear();
   if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 1); r != MOE_OK) return r;
-  if (moe_status r = check_gate_up(w, mode, row_src, a, a_scale, a_rows, w_gate_up, w_gu_scale); r != MOE_OK)
+  if (moe_status r = check_gate_up(shape, w, mode, row_src, a, a_scale, a_rows, w_gate_up, w_gu_scale); r != MOE_OK)
     return r;
   REQUIRE(h != nullptr, "ffn_gate_up: h is NULL");
   REQUIRE(w != MOE_F8E4M3 || h_scale != nullptr, "ffn_gate_up: fp8 needs h_scale");

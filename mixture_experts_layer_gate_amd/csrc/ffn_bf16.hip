@@ -1,116 +1,164 @@
 // Grouped SwiGLU expert FFN in bf16 with fp32 MFMA accumulation
 // ("DeepSeek_V3_Report: Annotation", SwiGLU paragraph and eq. (12)).
 //
-// Two persistent launches over all experts, 128 x 128 tiles, both operands
-// staged through double-buffered LDS:
-//  1. gate/up: H[r, c] = SiLU(x_r . Wg[c]) * (x_r . Wu[c]) for 64 H columns;
-//     the B tile interleaves 32 gate rows and the matching 32 up rows per
-//     wave, so the SwiGLU product is formed in registers. Input rows are read
-//     through the row mode (the gather is fused into the A load).
-//  2. down:    y[r, n] = H_r . Wd[n] for 128 output columns.
+// Two persistent launches over all experts, one 256-thread workgroup per CU,
+// 256 weight rows x 256 token rows per tile on the pipelined direct-to-LDS
+// main loop (gemm_pipe.h) and balanced blocks (an expert's rows split into
+// near-equal blocks of at most 256 rows; empty 32-row sub-tiles are skipped):
+//  1. gate/up: H[r, c] = SiLU(x_r . Wg[c]) * (x_r . Wu[c]) for 128 H columns;
+//     each wave holds 64 gate rows and the matching 64 up rows, so the SwiGLU
+//     product is formed in registers. Token rows are read through the row
+//     mode (the gather is fused into the operand load).
+//  2. down:    y[r, n] = H_r . Wd[n] for 256 output columns.
 // H lives in the workspace as bf16 [n_rows, I].
 #include <mutex>
 
 #include "common.h"
-#include "gemm_bf16.h"
+#include "gemm_pipe.h"
 #include "launch.h"
 #include "sched.h"
 
 namespace moe {
 
-using FfnTile = TileBF16<128, 128, 2, 2>;
-constexpr int kGuBNh = 64;  // H columns per gate/up tile
+using FP = Pipe<256, 256>;  // 256 weight rows x 256 token rows per tile, waves of 128 x 128
+constexpr int kHcols = FP::BW / 2;  // H columns per gate/up tile
 
-__global__ __launch_bounds__(FfnTile::NT) void ffn_gate_up_bf16_kernel(
-    int d, int I, int E, int n_rows, int a_rows, const int32_t* __restrict__ off, moe_row_mode mode,
-    const int32_t* __restrict__ row_src, const uint16_t* __restrict__ a, const uint16_t* __restrict__ wgu,
-    uint16_t* __restrict__ H) {
-  using G = FfnTile;
-  extern __shared__ __align__(16) uint16_t lds_ffn[];
-  int* cum = reinterpret_cast<int*>(lds_ffn + G::LDS_BYTES / 2);
-  __shared__ int wtmp[16];
-  const int NB = I / kGuBNh;
-  const int total = build_units(off, E, n_rows, G::BM, NB, cum, wtmp);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wn = (tid >> 6) / G::WM;
-  for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
-    const Unit un = find_unit(t, off, E, n_rows, G::BM, cum);
-    const uint16_t* pa[G::AC];
-    const uint16_t* pb[G::BC];
+__device__ __forceinline__ int live_token_subtiles(int nsub) {
+  const int wt = (threadIdx.x >> 6) & 1;
+  return clampi((nsub - wt + 1) / 2, 0, 4);
+}
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+// One tile with MS live token sub-tiles per wave: main loop and epilogue in
+// one instantiation, so the accumulators never merge across variants.
+template <int MS>
+__device__ __forceinline__ void gate_up_tile(const PipeRows<FP>& rows, int d, int I, const Unit& un, uint8_t* lds,
+                                             uint16_t* __restrict__ H) {
+  f32x16 acc[FP::TW][FP::TT];
 #pragma unroll
-    for (int j = 0; j < G::AC; ++j) {
-      const int r = chunk_row<G>(tid, j);
-      const int sr = r < un.rows ? source_row(mode, row_src, un.m0 + r, un.seg0, a_rows) : -1;
-      pa[j] = sr >= 0 ? a + static_cast<size_t>(sr) * d + chunk_col<G>(tid, j) : nullptr;
+  for (int j = 0; j < FP::TW; ++j)
+#pragma unroll
+    for (int i = 0; i < FP::TT; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+  pipe_mainloop<FP, MS>(rows, d, lds, acc);
+  const int ww = threadIdx.x >> 7, h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int tr = pipe_token_row(i);
+    if (tr < un.rows) {
+      uint16_t* hrow = H + static_cast<size_t>(un.m0 + tr) * I + un.nb * kHcols + ww * 64 + 4 * h;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          store_bf16x4(hrow + j * 32 + 8 * q, silu(acc[j][i][4 * q]) * acc[j + 2][i][4 * q],
+                       silu(acc[j][i][4 * q + 1]) * acc[j + 2][i][4 * q + 1],
+                       silu(acc[j][i][4 * q + 2]) * acc[j + 2][i][4 * q + 2],
+                       silu(acc[j][i][4 * q + 3]) * acc[j + 2][i][4 * q + 3]);
     }
-    // B tile rows: per wave column group wn, 32 gate rows then the matching 32 up rows
-    const uint16_t* wexp = wgu + static_cast<size_t>(un.e) * 2 * I * d;
-#pragma unroll
-    for (int j = 0; j < G::BC; ++j) {
-      const int rb = chunk_row<G>(tid, j);
-      const int hcol = un.nb * kGuBNh + (rb >> 6) * 32 + (rb & 31);
-      const int wrow = ((rb >> 5) & 1) ? I + hcol : hcol;
-      pb[j] = wexp + static_cast<size_t>(wrow) * d + chunk_col<G>(tid, j);
-    }
-    f32x16 acc[G::TM][G::TN];
-    zero_acc<G>(acc);
-    mainloop_bf16<G>(pa, pb, d, lds_ffn, acc);
-    const int col = un.nb * kGuBNh + wn * 32 + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < G::TM; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = acc_row<G>(i, v);
-        if (r < un.rows) {
-          const float h = silu(acc[i][0][v]) * acc[i][1][v];
-          H[static_cast<size_t>(un.m0 + r) * I + col] = f32_to_bf16(h);
-        }
-      }
   }
 }
 
-__global__ __launch_bounds__(FfnTile::NT) void ffn_down_bf16_kernel(int d, int I, int E, int n_rows,
-                                                                    const int32_t* __restrict__ off,
-                                                                    const uint16_t* __restrict__ H,
-                                                                    const uint16_t* __restrict__ wd,
-                                                                    uint16_t* __restrict__ y) {
-  using G = FfnTile;
-  extern __shared__ __align__(16) uint16_t lds_ffn[];
-  int* cum = reinterpret_cast<int*>(lds_ffn + G::LDS_BYTES / 2);
+template <int MS>
+__device__ __forceinline__ void down_tile(const PipeRows<FP>& rows, int d, int I, const Unit& un, uint8_t* lds,
+                                          uint16_t* __restrict__ y) {
+  f32x16 acc[FP::TW][FP::TT];
+#pragma unroll
+  for (int j = 0; j < FP::TW; ++j)
+#pragma unroll
+    for (int i = 0; i < FP::TT; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+  pipe_mainloop<FP, MS>(rows, I, lds, acc);
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int tr = pipe_token_row(i);
+    if (tr < un.rows) {
+      uint16_t* yrow = y + static_cast<size_t>(un.m0 + tr) * d + un.nb * FP::BW;
+#pragma unroll
+      for (int j = 0; j < FP::TW; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          store_bf16x4(yrow + pipe_wcol<FP>(j, q), acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                       acc[j][i][4 * q + 3]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(FP::NT, 1) void ffn_gate_up_bf16_kernel(
+    int d, int I, int E, int n_rows, int a_rows, const int32_t* __restrict__ off, moe_row_mode mode,
+    const int32_t* __restrict__ row_src, const uint16_t* __restrict__ a, const uint16_t* __restrict__ wgu,
+    uint16_t* __restrict__ H) {
+  extern __shared__ __align__(16) uint8_t lds_p[];
+  int* cum = reinterpret_cast<int*>(lds_p + FP::LDS_BYTES);
   __shared__ int wtmp[16];
-  const int NB = d / G::BN;
-  const int total = build_units(off, E, n_rows, G::BM, NB, cum, wtmp);
-  const int tid = threadIdx.x;
+  const int NB = I / kHcols;
+  const int total = build_units_balanced(off, E, n_rows, FP::BT / 32, NB, cum, wtmp);
   for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
-    const Unit un = find_unit(t, off, E, n_rows, G::BM, cum);
-    const uint16_t* pa[G::AC];
-    const uint16_t* pb[G::BC];
+    const Unit un = find_unit_balanced(t, off, E, n_rows, FP::BT / 32, cum);
+    int s_first = source_row(mode, row_src, un.m0, un.seg0, a_rows);
+    if (s_first < 0) s_first = 0;
+    PipeRows<FP> rows;
+    rows.trs = pipe_rsrc(a, static_cast<uint64_t>(a_rows) * d * 2);
 #pragma unroll
-    for (int j = 0; j < G::AC; ++j) {
-      const int r = chunk_row<G>(tid, j);
-      pa[j] = r < un.rows ? H + static_cast<size_t>(un.m0 + r) * I + chunk_col<G>(tid, j) : nullptr;
+    for (int q = 0; q < FP::TL; ++q) {
+      const int r = pipe_load_row(q);
+      int sr = r < un.rows ? source_row(mode, row_src, un.m0 + r, un.seg0, a_rows) : -1;
+      if (sr < 0) sr = s_first;                       // rows past the block: any valid row, never stored
+      rows.ot[q] = (static_cast<uint32_t>(sr) * d + pipe_load_chunk(q) * 8) * 2;
     }
-    const uint16_t* wexp = wd + static_cast<size_t>(un.e) * d * I;
+    rows.wrs = pipe_rsrc(wgu + static_cast<size_t>(un.e) * 2 * I * d, static_cast<uint64_t>(2 * I) * d * 2);
 #pragma unroll
-    for (int j = 0; j < G::BC; ++j) {
-      const int n = un.nb * G::BN + chunk_row<G>(tid, j);
-      pb[j] = wexp + static_cast<size_t>(n) * I + chunk_col<G>(tid, j);
+    for (int q = 0; q < FP::WL; ++q) {
+      const int rw = pipe_load_row(q);
+      const int j = (rw >> 5) & 3;                    // sub-tiles 0,1: gate rows; 2,3: the matching up rows
+      const int hcol = un.nb * kHcols + (rw >> 7) * 64 + (j & 1) * 32 + (rw & 31);
+      rows.ow[q] = (static_cast<uint32_t>(j >= 2 ? I + hcol : hcol) * d + pipe_load_chunk(q) * 8) * 2;
     }
-    f32x16 acc[G::TM][G::TN];
-    zero_acc<G>(acc);
-    mainloop_bf16<G>(pa, pb, I, lds_ffn, acc);
+    switch (live_token_subtiles(un.nsub)) {
+      case 4: gate_up_tile<4>(rows, d, I, un, lds_p, H); break;
+      case 3: gate_up_tile<3>(rows, d, I, un, lds_p, H); break;
+      case 2: gate_up_tile<2>(rows, d, I, un, lds_p, H); break;
+      case 1: gate_up_tile<1>(rows, d, I, un, lds_p, H); break;
+      default: gate_up_tile<0>(rows, d, I, un, lds_p, H); break;
+    }
+  }
+}
+
+__global__ __launch_bounds__(FP::NT, 1) void ffn_down_bf16_kernel(int d, int I, int E, int n_rows,
+                                                                  const int32_t* __restrict__ off,
+                                                                  const uint16_t* __restrict__ H,
+                                                                  const uint16_t* __restrict__ wd,
+                                                                  uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) uint8_t lds_p[];
+  int* cum = reinterpret_cast<int*>(lds_p + FP::LDS_BYTES);
+  __shared__ int wtmp[16];
+  const int NB = d / FP::BW;
+  const int total = build_units_balanced(off, E, n_rows, FP::BT / 32, NB, cum, wtmp);
+  for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
+    const Unit un = find_unit_balanced(t, off, E, n_rows, FP::BT / 32, cum);
+    PipeRows<FP> rows;
+    rows.trs = pipe_rsrc(H, static_cast<uint64_t>(n_rows) * I * 2);
 #pragma unroll
-    for (int i = 0; i < G::TM; ++i)
+    for (int q = 0; q < FP::TL; ++q) {
+      const int r = pipe_load_row(q);
+      rows.ot[q] = (static_cast<uint32_t>(un.m0 + (r < un.rows ? r : 0)) * I + pipe_load_chunk(q) * 8) * 2;
+    }
+    rows.wrs = pipe_rsrc(wd + static_cast<size_t>(un.e) * d * I, static_cast<uint64_t>(d) * I * 2);
 #pragma unroll
-      for (int j = 0; j < G::TN; ++j) {
-        const int n = un.nb * G::BN + acc_col<G>(j);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = acc_row<G>(i, v);
-          if (r < un.rows) y[static_cast<size_t>(un.m0 + r) * d + n] = f32_to_bf16(acc[i][j][v]);
-        }
-      }
+    for (int q = 0; q < FP::WL; ++q)
+      rows.ow[q] = (static_cast<uint32_t>(un.nb * FP::BW + pipe_load_row(q)) * I + pipe_load_chunk(q) * 8) * 2;
+    switch (live_token_subtiles(un.nsub)) {
+      case 4: down_tile<4>(rows, d, I, un, lds_p, y); break;
+      case 3: down_tile<3>(rows, d, I, un, lds_p, y); break;
+      case 2: down_tile<2>(rows, d, I, un, lds_p, y); break;
+      case 1: down_tile<1>(rows, d, I, un, lds_p, y); break;
+      default: down_tile<0>(rows, d, I, un, lds_p, y); break;
+    }
   }
 }
 
@@ -124,32 +172,33 @@ static int persistent_grid(long long units_upper, int per_cu) {
 static void set_lds_limits() {
   static std::once_flag once;
   std::call_once(once, [] {
+    // ring + schedule for up to 4096 experts; a refused request must not leave a sticky error
+    const int need = FP::LDS_BYTES + 4 * 4097;
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_gate_up_bf16_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, need);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_down_bf16_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, need);
+    (void)hipGetLastError();
   });
 }
 
 hipError_t launch_ffn_bf16_gate_up(const FfnArgs& p, hipStream_t st) {
-  using G = FfnTile;
   set_lds_limits();
-  const size_t lds = G::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
-  const long long mblocks = p.n_rows / G::BM + p.n_experts;
-  const int g1 = persistent_grid(mblocks * (p.I / kGuBNh), 2);
-  hipLaunchKernelGGL(ffn_gate_up_bf16_kernel, dim3(g1), dim3(G::NT), lds, st, p.d, p.I, p.n_experts, p.n_rows,
+  const size_t lds = FP::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
+  const long long mblocks = p.n_rows / FP::BT + p.n_experts;
+  const int g1 = persistent_grid(mblocks * (p.I / kHcols), 1);
+  hipLaunchKernelGGL(ffn_gate_up_bf16_kernel, dim3(g1), dim3(FP::NT), lds, st, p.d, p.I, p.n_experts, p.n_rows,
                      p.a_rows, p.offsets, p.mode, p.row_src, static_cast<const uint16_t*>(p.a),
                      static_cast<const uint16_t*>(p.w_gu), static_cast<uint16_t*>(p.h));
   return hipGetLastError();
 }
 
 hipError_t launch_ffn_bf16_down(const FfnArgs& p, hipStream_t st) {
-  using G = FfnTile;
   set_lds_limits();
-  const size_t lds = G::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
-  const long long mblocks = p.n_rows / G::BM + p.n_experts;
-  const int g2 = persistent_grid(mblocks * (p.d / G::BN), 2);
-  hipLaunchKernelGGL(ffn_down_bf16_kernel, dim3(g2), dim3(G::NT), lds, st, p.d, p.I, p.n_experts, p.n_rows,
+  const size_t lds = FP::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
+  const long long mblocks = p.n_rows / FP::BT + p.n_experts;
+  const int g2 = persistent_grid(mblocks * (p.d / FP::BW), 1);
+  hipLaunchKernelGGL(ffn_down_bf16_kernel, dim3(g2), dim3(FP::NT), lds, st, p.d, p.I, p.n_experts, p.n_rows,
                      p.offsets, static_cast<const uint16_t*>(p.h), static_cast<const uint16_t*>(p.w_d),
                      static_cast<uint16_t*>(p.y));
   return hipGetLastError();

@@ -291,6 +291,7 @@ static void f8_set_lds_limits() {
                               hipFuncAttributeMaxDynamicSharedMemorySize, 120 * 1024);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_down_fp8_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 120 * 1024);
+    (void)hipGetLastError();
   });
 }
 

@@ -43,8 +43,19 @@ __device__ __forceinline__ void block_exclusive_scan(int* a, int n, int* wtmp /*
   __syncthreads();
 }
 
+// The unit is the same for every lane (derived from the block index and LDS
+// values read at uniform addresses); saying so keeps it in SGPRs.
+__device__ __forceinline__ int wave_uniform(int x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_readfirstlane(x);
+#else
+  return x;
+#endif
+}
+
 struct Unit {
   int e, nb, m0, rows, seg0;  // expert, n-block, first row, valid rows (<= BM), segment start
+  int nsub;                   // 32-row sub-tiles in this block (balanced schedule)
 };
 
 // Fill cum[0..E] (LDS) with units-before-expert; returns the total.
@@ -78,6 +89,46 @@ __device__ __forceinline__ Unit find_unit(int t, const int32_t* __restrict__ off
   u.m0 = s0 + (local % nmb) * BM;
   u.rows = min(BM, s1 - u.m0);
   u.seg0 = s0;
+  return u;
+}
+
+// Balanced blocks: an expert's rows are cut into 32-row sub-tiles, and the
+// sub-tiles into nmb = ceil(n32 / MAXSUB) blocks of nearly equal size, so a
+// 260-row expert becomes 2 x 130 rows instead of 256 + 4.
+__device__ __forceinline__ int build_units_balanced(const int32_t* __restrict__ off, int E, int n_rows, int MAXSUB,
+                                                    int NB, int* cum, int* wtmp) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int lo = clampi(off[e], 0, n_rows);
+    const int hi = clampi(off[e + 1], lo, n_rows);
+    cum[e] = cdiv(cdiv(hi - lo, 32), MAXSUB) * NB;
+  }
+  __syncthreads();
+  block_exclusive_scan(cum, E, wtmp);
+  return cum[E];
+}
+
+__device__ __forceinline__ Unit find_unit_balanced(int t, const int32_t* __restrict__ off, int E, int n_rows,
+                                                   int MAXSUB, const int* cum) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cum[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int s0 = clampi(off[e], 0, n_rows);
+  const int s1 = clampi(off[e + 1], s0, n_rows);
+  const int n32 = cdiv(s1 - s0, 32);
+  const int nmb = cdiv(n32, MAXSUB);
+  const int local = t - cum[e];
+  const int b = local % nmb;
+  const int first = b * n32 / nmb, last = (b + 1) * n32 / nmb;
+  Unit u;
+  u.e = wave_uniform(e);
+  u.nb = wave_uniform(local / nmb);
+  u.m0 = wave_uniform(s0 + 32 * first);
+  u.rows = wave_uniform(min(32 * (last - first), s1 - u.m0));
+  u.seg0 = wave_uniform(s0);
+  u.nsub = wave_uniform(last - first);
   return u;
 }
 
