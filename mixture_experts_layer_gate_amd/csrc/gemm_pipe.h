@@ -77,20 +77,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pipe_rsrc(const void* base, ui
                                           static_cast<int>(static_cast<uint32_t>(bytes)), 0x00020000);
 }
 
-template <class P>
-__device__ __forceinline__ void pipe_issue(const PipeRows<P>& r, uint8_t* lds, int stage, int k0) {
+// Part A of a stage = its weight rows (WL loads per thread), part B = its
+// token rows (TL loads per thread). Load q of a part goes to LDS chunk block
+// q * 4 + wave (1 KB each).
+template <class P, bool A>
+__device__ __forceinline__ void pipe_issue_one(const PipeRows<P>& r, uint8_t* st, int kb, int q) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists only in the device pass
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: LDS address in SGPRs
-  uint8_t* st = lds + stage * P::STAGE;
-  const int kb = k0 * 2;
-#pragma unroll
-  for (int q = 0; q < P::WL; ++q)
+  if (A)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.wrs, (lds_void_t*)(st + (q * 4 + w) * 1024), 16, r.ow[q], kb, 0, 0);
-#pragma unroll
-  for (int q = 0; q < P::TL; ++q)
+  else
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.trs, (lds_void_t*)(st + P::W_BYTES + (q * 4 + w) * 1024), 16, r.ot[q],
                                              kb, 0, 0);
 #endif
+}
+
+template <class P, bool A>
+__device__ __forceinline__ void pipe_issue_part(const PipeRows<P>& r, uint8_t* lds, int stage, int k0) {
+#pragma unroll
+  for (int q = 0; q < (A ? P::WL : P::TL); ++q) pipe_issue_one<P, A>(r, lds + stage * P::STAGE, k0 * 2, q);
 }
 
 template <class P, int MS>
@@ -117,28 +122,66 @@ __device__ __forceinline__ void pipe_mma(const PipeFrags<P, MS>& f, f32x16 (&acc
     for (int j = 0; j < P::TW; ++j) acc[j][i] = mfma_32x32x16_bf16(f.w[j], f.t[i], acc[j][i]);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm_only_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// Keeps the scheduler from moving MFMAs across phase boundaries, so each
-// fragment read is separated from its first use by a full block of MFMAs.
+// Keeps the scheduler from moving instructions across this point.
 __device__ __forceinline__ void sched_fence() {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_sched_barrier(0);
 #endif
 }
 
-// acc[j][i]: weight sub-tile j x token sub-tile i of this wave.
-//
-// Stage s is loaded into buffer s % 4 during iteration s - 3 (stages 0..2 in
-// the prologue). Iteration kt: read the step-1 fragments of stage kt; MFMAs on
-// the step-0 fragments; wait until stage kt+1 has landed and barrier; load
-// stage kt+3 into buffer (kt+3) % 4 -- the buffer of stage kt-1, which every
-// wave finished reading before it could reach this barrier; read the step-0
-// fragments of stage kt+1; MFMAs on the step-1 fragments. No LDS read has to
-// be complete at the barrier, so it waits on vmcnt only.
+// The MFMAs of one K16 step with one part of a stage's loads spread evenly
+// among them (load q before MFMA q * M / L), so the vector-memory pipe is fed
+// steadily: issued as one burst, the loads back up and the wave, which issues
+// in order, stalls with its MFMAs behind them.
+template <class P, int MS, int PART>  // PART: 0 none, 1 part A, 2 part B
+__device__ __forceinline__ void pipe_mma_loads(const PipeFrags<P, MS>& f, f32x16 (&acc)[P::TW][P::TT],
+                                               const PipeRows<P>& r, uint8_t* st, int kb) {
+  constexpr int M = P::TW * MS;
+  constexpr int L = PART == 0 ? 0 : (PART == 1 ? P::WL : P::TL);
+#pragma unroll
+  for (int m = 0; m < (M > L ? M : L); ++m) {
+#pragma unroll
+    for (int q = 0; q < L; ++q)
+      if ((M == 0 && q == m) || (M > 0 && q * M / L == m)) {
+        pipe_issue_one<P, PART == 1>(r, st, kb, q);
+        sched_fence();
+      }
+    if (m < M) acc[m % P::TW][m / P::TW] = mfma_32x32x16_bf16(f.w[m % P::TW], f.t[m / P::TW], acc[m % P::TW][m / P::TW]);
+  }
+  sched_fence();
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_only_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One stage kt (two K16 steps) per wave. Stage s is issued in two parts: part
+// A (weights) among the step-1 MFMAs of iteration s - 3, part B (tokens) among
+// the step-0 MFMAs of iteration s - 2; both follow the barrier of iteration
+// s - 3, after which every wave has finished reading the buffer s % 4 (it last
+// held stage s - 4, read for iteration s - 4). At the barrier of iteration kt
+// only stage kt + 2 may still be in flight (LPS loads), so stage kt + 1 is
+// complete. The barrier needs no LDS read to be complete.
+//   ISSUE_B: issue part B of stage kt + 2; WAIT: vmcnt at the barrier, or -1
+//   for no barrier (last stage); ISSUE_A: issue part A of stage kt + 3.
+template <class P, int MS, bool ISSUE_B, int WAIT, bool ISSUE_A>
+__device__ __forceinline__ void pipe_iteration(const PipeRows<P>& rows, uint8_t* lds, int kt, int w_off, int t_off,
+                                               PipeFrags<P, MS>& f0, PipeFrags<P, MS>& f1,
+                                               f32x16 (&acc)[P::TW][P::TT]) {
+  pipe_read<P, MS>(f1, lds + (kt & 3) * P::STAGE, w_off, t_off, 32);
+  sched_fence();
+  pipe_mma_loads<P, MS, ISSUE_B ? 2 : 0>(f0, acc, rows, lds + ((kt + 2) & 3) * P::STAGE, (kt + 2) * P::BK * 2);
+  if (WAIT >= 0) {
+    wait_vm_only_barrier<(WAIT >= 0 ? WAIT : 0)>();
+    pipe_read<P, MS>(f0, lds + ((kt + 1) & 3) * P::STAGE, w_off, t_off, 0);
+    sched_fence();
+  }
+  pipe_mma_loads<P, MS, ISSUE_A ? 1 : 0>(f1, acc, rows, lds + ((kt + 3) & 3) * P::STAGE, (kt + 3) * P::BK * 2);
+}
+
+// acc[j][i]: weight sub-tile j x token sub-tile i of this wave. K % 128 == 0,
+// so there are at least four stages.
 template <class P, int MS>
 __device__ __forceinline__ void pipe_mainloop(const PipeRows<P>& rows, int K, uint8_t* lds,
                                               f32x16 (&acc)[P::TW][P::TT]) {
@@ -151,12 +194,12 @@ __device__ __forceinline__ void pipe_mainloop(const PipeRows<P>& rows, int K, ui
   const int w_off = (ww * (P::BW / 2) + (l & 31)) * P::ROWB + cofs;
   const int t_off = P::W_BYTES + (wt * 32 + (l & 31)) * P::ROWB + cofs;
 
-#pragma unroll
-  for (int s = 0; s < 3; ++s)
-    if (s < nk) pipe_issue<P>(rows, lds, s, s * P::BK);
-  if (nk >= 3) wait_vm_only_barrier<2 * P::LPS>();
-  else if (nk == 2) wait_vm_only_barrier<P::LPS>();
-  else wait_vm_only_barrier<0>();
+  pipe_issue_part<P, true>(rows, lds, 0, 0);
+  pipe_issue_part<P, false>(rows, lds, 0, 0);
+  pipe_issue_part<P, true>(rows, lds, 1, P::BK);
+  pipe_issue_part<P, false>(rows, lds, 1, P::BK);
+  pipe_issue_part<P, true>(rows, lds, 2, 2 * P::BK);
+  wait_vm_only_barrier<P::LPS + P::WL>();                   // stage 0 complete
 #if defined(__HIP_DEVICE_COMPILE__)
   // Retire any scalar load still in flight (lgkmcnt(0), other counters left
   // free) in a form the compiler sees: with none pending, the LDS counter
@@ -167,30 +210,10 @@ __device__ __forceinline__ void pipe_mainloop(const PipeRows<P>& rows, int K, ui
   PipeFrags<P, MS> f0, f1;
   pipe_read<P, MS>(f0, lds, w_off, t_off, 0);
   int kt = 0;
-  // steady state: stage kt+2 is still in flight, stage kt+3 gets issued
-  for (; kt + 3 < nk; ++kt) {
-    pipe_read<P, MS>(f1, lds + (kt & 3) * P::STAGE, w_off, t_off, 32);
-    sched_fence();
-    pipe_mma<P, MS>(f0, acc);
-    sched_fence();
-    wait_vm_only_barrier<P::LPS>();
-    pipe_issue<P>(rows, lds, (kt + 3) & 3, (kt + 3) * P::BK);
-    pipe_read<P, MS>(f0, lds + ((kt + 1) & 3) * P::STAGE, w_off, t_off, 0);
-    sched_fence();
-    pipe_mma<P, MS>(f1, acc);
-    sched_fence();
-  }
-  // drain: nothing left to issue
-  for (; kt < nk; ++kt) {
-    pipe_read<P, MS>(f1, lds + (kt & 3) * P::STAGE, w_off, t_off, 32);
-    pipe_mma<P, MS>(f0, acc);
-    if (kt + 1 < nk) {
-      if (kt + 2 < nk) wait_vm_only_barrier<P::LPS>();
-      else wait_vm_only_barrier<0>();
-      pipe_read<P, MS>(f0, lds + ((kt + 1) & 3) * P::STAGE, w_off, t_off, 0);
-    }
-    pipe_mma<P, MS>(f1, acc);
-  }
+  for (; kt + 3 < nk; ++kt) pipe_iteration<P, MS, true, P::LPS, true>(rows, lds, kt, w_off, t_off, f0, f1, acc);
+  pipe_iteration<P, MS, true, P::LPS, false>(rows, lds, kt, w_off, t_off, f0, f1, acc);     // kt = nk - 3
+  pipe_iteration<P, MS, false, 0, false>(rows, lds, kt + 1, w_off, t_off, f0, f1, acc);     // kt = nk - 2
+  pipe_iteration<P, MS, false, -1, false>(rows, lds, kt + 2, w_off, t_off, f0, f1, acc);    // kt = nk - 1
   // every wave has read the ring before the next tile's loads overwrite it
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
