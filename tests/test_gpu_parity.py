@@ -243,6 +243,39 @@ def test_grouped_ffn_ragged_and_empty_experts():
     report("ragged y", rel_l2(y, ref), TOL["bf16"])
 
 
+@pytest.mark.parametrize("mode", ["gather", "direct"])
+def test_grouped_ffn_tile_shapes(mode):
+    """Expert segment sizes that reach every block shape of the bf16 kernels.
+
+    Rows are cut into 32-row sub-tiles and an expert's sub-tiles into
+    ceil(n32 / 8) near-equal blocks of at most 256 rows, each wave row taking
+    every other sub-tile. Sizes: empty, 1 and 2 sub-tiles, exactly 8, 9 with a
+    1-row tail (5 + 4), 9 full, 10 ragged and full, 11, 17 (3 blocks), 20 and 21.
+    """
+    cfg = get_config("c2", n_routed=12, n_groups=1, topk_groups=1, T=2048, topk=2)
+    inp = generate(cfg, DEV)
+    sh = B.moe_shape.of(cfg)
+    sizes = [0, 1, 33, 256, 257, 288, 289, 320, 321, 544, 640, 672]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    assert n <= cfg.T * cfg.topk
+    rng = np.random.default_rng(17)
+    src = rng.integers(0, cfg.T, n)
+    y = torch.empty((n, cfg.d), dtype=torch.bfloat16, device=DEV)
+    if mode == "gather":
+        B.moe_grouped_ffn(sh, B.MOE_BF16, 12, n, _i32(off), B.MOE_ROWS_GATHER, _i32(src), inp["u"], None,
+                          cfg.T, inp["w_gate_up"], None, inp["w_down"], None, y, _ws(cfg))
+    else:
+        a = inp["u"][torch.from_numpy(src).to(DEV)].contiguous()
+        B.moe_grouped_ffn(sh, B.MOE_BF16, 12, n, _i32(off), B.MOE_ROWS_DIRECT, None, a, None,
+                          n, inp["w_gate_up"], None, inp["w_down"], None, y, _ws(cfg))
+    torch.cuda.synchronize()
+    for e in range(12):
+        if sizes[e]:
+            ref = _oracle_ffn_rows(cfg, inp, e, src[off[e]:off[e + 1]])
+            report(f"{mode} expert {e} ({sizes[e]} rows) y", rel_l2(y[off[e]:off[e + 1]], ref), TOL["bf16"])
+
+
 @pytest.mark.parametrize("name", ["c1", "c2"])
 def test_combine(name):
     cfg, inp = _inputs(name)
