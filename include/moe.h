@@ -143,9 +143,9 @@ moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* top
  *   w_d_scale    [n_experts, d/128, I/128] fp32 block scales (fp8 only, else NULL).
  *   y_dtype      MOE_F32 (only with w = MOE_F32) or MOE_BF16.
  *   y            out [n_rows, d].
- * Limits: d and I multiples of 128 (fp8: d a multiple of 256); with MOE_BF16,
- * a_rows * d, n_rows * I and 2 * I * d below 2^31 elements (32-bit byte
- * offsets); otherwise MOE_E_UNSUPPORTED.
+ * Limits: d and I multiples of 128; with MOE_BF16, a_rows * d, n_rows * I and
+ * 2 * I * d below 2^31 elements, with MOE_F8E4M3 below 2^32 and d, I <= 32768
+ * (32-bit byte offsets); otherwise MOE_E_UNSUPPORTED.
  */
 moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                            const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,

@@ -181,7 +181,11 @@ moe_status check_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int
   SUPPORT(static_cast<long long>(n_rows) * (d > I ? d : I) < (1LL << 40), "grouped_ffn: too many rows");
   REQUIRE(offsets != nullptr, "grouped_ffn: expert_offsets is NULL");
   REQUIRE(w == MOE_F32 || w == MOE_BF16 || w == MOE_F8E4M3, "grouped_ffn: bad weight dtype %d", static_cast<int>(w));
-  SUPPORT(w != MOE_F8E4M3 || d % 256 == 0, "grouped_ffn: the fp8 path needs d (%d) to be a multiple of 256", d);
+  SUPPORT(w != MOE_F8E4M3 || (d <= 32768 && I <= 32768), "grouped_ffn: the fp8 path needs d and inter <= 32768");
+  // the fp8 kernels address codes and scales through 32-bit byte offsets
+  SUPPORT(w != MOE_F8E4M3 || (static_cast<long long>(n_rows) * I < (1LL << 32) &&
+                              static_cast<long long>(2 * I) * d < (1LL << 32)),
+          "grouped_ffn: fp8 path needs n_rows * inter and 2 * inter * d below 2^32");
   // the bf16 kernels address H and one expert's weight matrices through 32-bit byte offsets
   SUPPORT(w != MOE_BF16 || (static_cast<long long>(n_rows) * I * 2 < (1LL << 32) &&
                             static_cast<long long>(2 * I) * d * 2 < (1LL << 32)),
@@ -197,6 +201,8 @@ moe_status check_gate_up(const moe_shape* shape, moe_dtype w, moe_row_mode mode,
   REQUIRE(a_rows > 0, "grouped_ffn: a_rows must be positive");
   SUPPORT(w != MOE_BF16 || static_cast<long long>(a_rows) * shape->d * 2 < (1LL << 32),
           "grouped_ffn: bf16 path needs a_rows * d below 2^31 elements");
+  SUPPORT(w != MOE_F8E4M3 || static_cast<long long>(a_rows) * shape->d < (1LL << 32),
+          "grouped_ffn: fp8 path needs a_rows * d below 2^32");
   REQUIRE(mode == MOE_ROWS_DIRECT || mode == MOE_ROWS_GATHER || mode == MOE_ROWS_SEGMENT,
           "grouped_ffn: bad row mode %d", static_cast<int>(mode));
   REQUIRE(mode != MOE_ROWS_GATHER || row_src != nullptr, "grouped_ffn: MOE_ROWS_GATHER needs row_src");

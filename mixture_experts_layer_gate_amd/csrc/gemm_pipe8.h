@@ -1,0 +1,308 @@
+// Pipelined E4M3 MFMA main loop with per-128 fp32 promotion, for the fp8
+// expert GEMMs ("DeepSeek_V3_Report: Annotation", sections "Fine-Grained
+// Quantization" and "Increasing Accumulation Precision").
+//
+// Operands are E4M3 codes: weights with one fp32 scale per 128x128 block,
+// tokens with one fp32 scale per 1x128 tile. Every 128-wide K chunk c is
+// accumulated raw -- two v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0
+// scales into a temporary T (the first with C = 0) -- and then promoted into
+// the fp32 accumulator: acc += T * (s_token[n, c] * s_weight[block, c]).
+// gfx950's block-scaled MFMA takes power-of-two scales only, so the fp32
+// scales are applied on the VALU: the accumulator lives in VGPRs, T (the
+// MFMA destination) in AGPRs.
+//
+// Tile: BW = 256 weight rows x BT = 128 token rows, eight waves (two per
+// SIMD) in a 4 (weight) x 2 (token) grid of 64 x 64: TW = 2 weight sub-tiles
+// x up to 2 token sub-tiles of 32x32, so a wave holds 64 accumulator and 64
+// temporary registers, and one wave's promotion runs while the other wave on
+// its SIMD issues MFMAs. (One wave per SIMD with 128 x 64 each spilled: the
+// accumulator, the temporaries and the fragments do not fit 512 registers.)
+// Both operands stream into LDS with buffer_load ... lds through a ring of
+// four stages of 64 K-bytes (one MFMA K-step), rows of 64 bytes XOR-swizzled
+// as in the bf16 loop; each stage also brings the 128 token scales of its
+// chunk. Weight scales of the tile sit in LDS.
+//
+// Iteration kt (stage kt, chunk kt / 2): wait until stage kt+1 has landed +
+// barrier; read stage kt+1's fragments (and, in a chunk's second stage, this
+// chunk's token scales, before the buffer is refilled); the MFMAs of stage kt
+// with the loads of stage kt+3 spread among them. In a chunk's first stage
+// each element of T is promoted (chunk c-1, whose MFMAs were issued a block
+// earlier) just before the C = 0 MFMA that restarts it.
+#pragma once
+
+#include "common.h"
+#include "gemm_pipe.h"
+
+namespace moe {
+
+struct Pipe8 {
+  static constexpr int BW = 256, BT = 128, BK = 64, NS = 4, NT = 512, NWAVE = NT / 64;
+  static constexpr int TW = 2, TT = 2;                    // 32x32 sub-tiles per wave
+  static constexpr int ROWB = BK;                          // bytes per row per stage
+  static constexpr int W_BYTES = BW * ROWB, T_BYTES = BT * ROWB;
+  static constexpr int S_BYTES = 4 * NT;                   // token scales: waves 0,1 real, the others spare copies
+  static constexpr int STAGE = W_BYTES + T_BYTES + S_BYTES;
+  static constexpr int WL = W_BYTES / 16 / NT, TL = T_BYTES / 16 / NT;
+  static constexpr int LPS = WL + TL + 1;
+  static constexpr int RING = NS * STAGE;
+  static constexpr int MAX_CHUNKS = 256;                   // K <= 32768
+  static constexpr int SW_BYTES = 2 * MAX_CHUNKS * 4;      // weight scales of the tile: 2 block rows
+  static constexpr int LDS_BYTES = RING + SW_BYTES;
+  static_assert(WL * NT * 16 == W_BYTES && TL * NT * 16 == T_BYTES, "stage must split evenly over the threads");
+  static_assert(LPS * 3 <= 63, "vmcnt range");
+};
+
+// Wave coordinates: token half wt (rows 32 * (2i + wt) + lane % 32), weight
+// quarter ww (tile rows 64 ww .. 64 ww + 63).
+__device__ __forceinline__ int p8_wt() { return (threadIdx.x >> 6) & 1; }
+__device__ __forceinline__ int p8_ww() { return threadIdx.x >> 7; }
+
+// Tile row and logical 16-byte chunk of load q of this thread (16 rows of 64
+// bytes per wave instruction).
+__device__ __forceinline__ int pipe8_load_row(int q) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  return (q * Pipe8::NWAVE + w) * 16 + (l >> 2);
+}
+__device__ __forceinline__ int pipe8_load_chunk(int q) {
+  const int l = threadIdx.x & 63;
+  return (l & 3) ^ ((pipe8_load_row(q) >> 2) & 3);
+}
+
+// Operands: weights and token codes through buffer resources with 32-bit
+// byte offsets (row * K + logical chunk * 16), token scales likewise
+// (scale row * K / 128 * 4; the chunk goes in soffset).
+struct Pipe8Rows {
+  __amdgpu_buffer_rsrc_t wrs, trs, srs;
+  uint32_t ow[Pipe8::WL];
+  uint32_t ot[Pipe8::TL];
+  uint32_t os;
+};
+
+// Loads of stage s (K bytes s * 64 .. +63) into ring buffer st; load q of a
+// thread: weights q < WL, tokens q < WL + TL, then the scale dword.
+__device__ __forceinline__ void pipe8_issue_one(const Pipe8Rows& r, uint8_t* st, int s, int q) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using P = Pipe8;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = s * P::BK;
+  if (q < P::WL) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.wrs, (lds_void_t*)(st + (q * P::NWAVE + w) * 1024), 16, r.ow[q], kb,
+                                             0, 0);
+  } else if (q < P::WL + P::TL) {
+    const int qq = q - P::WL;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.trs, (lds_void_t*)(st + P::W_BYTES + (qq * P::NWAVE + w) * 1024), 16,
+                                             r.ot[qq], kb, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.srs, (lds_void_t*)(st + P::W_BYTES + P::T_BYTES + w * 256), 4, r.os,
+                                             (s >> 1) * 4, 0, 0);
+  }
+#endif
+}
+
+template <int MS>
+struct Pipe8Frags {
+  i32x8 w[Pipe8::TW];
+  i32x8 t[MS > 0 ? MS : 1];
+};
+
+// Fragment of tile row `row` (its 64-byte stage row): lane half h holds K bytes
+// 32h .. 32h+31, i.e. logical chunks 2h and 2h+1, stored at chunk ^ ((row >> 2) & 3).
+__device__ __forceinline__ i32x8 pipe8_frag(const uint8_t* st, int row) {
+  const int l = threadIdx.x & 63, sw = (row >> 2) & 3, c0 = 2 * (l >> 5);
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(st + row * Pipe8::ROWB + ((c0 ^ sw) << 4));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(st + row * Pipe8::ROWB + (((c0 + 1) ^ sw) << 4));
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <int MS>
+__device__ __forceinline__ void pipe8_read(Pipe8Frags<MS>& f, const uint8_t* st) {
+  const int l = threadIdx.x & 63, wt = p8_wt(), ww = p8_ww();
+#pragma unroll
+  for (int j = 0; j < Pipe8::TW; ++j) f.w[j] = pipe8_frag(st, ww * 64 + j * 32 + (l & 31));
+#pragma unroll
+  for (int i = 0; i < MS; ++i) f.t[i] = pipe8_frag(st + Pipe8::W_BYTES, 32 * (2 * i + wt) + (l & 31));
+}
+
+// Token scales of this lane's token rows for the chunk held in ring buffer st.
+template <int MS>
+__device__ __forceinline__ void pipe8_read_scales(float (&sa)[Pipe8::TT], const uint8_t* st) {
+  const int l = threadIdx.x & 63, wt = p8_wt();
+  const float* s = reinterpret_cast<const float*>(st + Pipe8::W_BYTES + Pipe8::T_BYTES);
+#pragma unroll
+  for (int i = 0; i < MS; ++i) sa[i] = s[32 * (2 * i + wt) + (l & 31)];
+}
+
+// One element of an MFMA result, read out of its AGPR at the promotion and
+// not earlier (with a plain use the register allocator copies all of T into
+// VGPRs at the top of the block). The MFMA that wrote the value was issued a
+// whole block (MFMAs, a barrier and the loads) before this read, far beyond
+// the wait states the read needs after an MFMA. Using an AGPR operand also
+// keeps the compiler on the AGPR form of the scaled MFMA: in the VGPR form it
+// has placed the destination over the instruction's own scale and A operands.
+__device__ __forceinline__ float agpr_read(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
+#else
+  return x;
+#endif
+}
+
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// An empty use of the fragments after the last MFMA that reads them: while
+// they are live no MFMA destination can be allocated on top of them (the
+// compiler otherwise places a restarted T over the A/B fragments of its own
+// scaled MFMA, which this code does not rely on being safe).
+template <int MS>
+__device__ __forceinline__ void pipe8_hold(const Pipe8Frags<MS>& f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int j = 0; j < Pipe8::TW; ++j) asm volatile("" ::"a"(f.w[j]));
+#pragma unroll
+  for (int i = 0; i < MS; ++i) asm volatile("" ::"a"(f.t[i]));
+#endif
+}
+
+// The MFMAs of one stage (fragments f), token sub-tile i fastest, with the
+// loads of stage `ls` spread among them (load q before MFMA q * M / LPS) when
+// ISSUE, and, for a chunk's first stage (PROMOTE), the previous chunk's
+// T[j][i] promoted just before the C = 0 MFMA that restarts it (FIRST: T
+// restarts from 0).
+template <int MS, bool FIRST, bool PROMOTE, bool ISSUE>
+__device__ __forceinline__ void pipe8_block(const Pipe8Frags<MS>& f, f32x16 (&T)[Pipe8::TW][Pipe8::TT],
+                                            f32x16 (&acc)[Pipe8::TW][Pipe8::TT], const float (&fac)[Pipe8::TW][Pipe8::TT],
+                                            const Pipe8Rows& rows, uint8_t* lds, int ls) {
+  using P = Pipe8;
+  constexpr int M = P::TW * MS;
+  constexpr int L = ISSUE ? P::LPS : 0;
+  uint8_t* st = lds + (ls & 3) * P::STAGE;
+#pragma unroll
+  for (int m = 0; m < (M > L ? M : L); ++m) {
+#pragma unroll
+    for (int q = 0; q < L; ++q)
+      if ((M == 0 && q == m) || (M > 0 && q * M / L == m)) {
+        pipe8_issue_one(rows, st, ls, q);
+        sched_fence();
+      }
+    if (m < M) {
+      const int j = m / MS, i = m % MS;
+      if (PROMOTE) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][i][v] = fmaf(agpr_read(T[j][i][v]), fac[j][i], acc[j][i][v]);
+      }
+      T[j][i] = mfma_f8(f.w[j], f.t[i], FIRST ? f32x16{} : T[j][i]);
+      sched_fence();   // keeps each promotion beside its MFMA
+    }
+  }
+  pipe8_hold(f);
+  sched_fence();
+}
+
+// Weight-scale row of weight sub-tile j of this wave: gate/up tiles use block
+// row 0 (gate) for j = 0 and 1 (up) for j = 1; down tiles the 128-row block of
+// this wave's 64 rows.
+template <bool GATE_UP>
+__device__ __forceinline__ int pipe8_sw_row(int j) {
+  return GATE_UP ? j : (p8_ww() >> 1);
+}
+
+template <int MS, bool GATE_UP>
+__device__ __forceinline__ void pipe8_factors(float (&fac)[Pipe8::TW][Pipe8::TT], const float (&sa)[Pipe8::TT],
+                                              const float* swt, int c) {
+#pragma unroll
+  for (int j = 0; j < Pipe8::TW; ++j)
+#pragma unroll
+    for (int i = 0; i < MS; ++i) fac[j][i] = sa[i] * swt[pipe8_sw_row<GATE_UP>(j) * Pipe8::MAX_CHUNKS + c];
+}
+
+// Keeps a value's computation (and the LDS read it needs) before the next
+// barrier: an empty asm that uses the value.
+__device__ __forceinline__ void pipe8_settle(const float (&fac)[Pipe8::TW][Pipe8::TT], int ms) {
+#pragma unroll
+  for (int j = 0; j < Pipe8::TW; ++j)
+#pragma unroll
+    for (int i = 0; i < Pipe8::TT; ++i)
+      if (i < ms) asm volatile("" ::"v"(fac[j][i]));
+}
+
+// One stage kt < nk - 1: fa holds its fragments, fb receives stage kt+1's.
+// WAIT: loads allowed in flight at the barrier (LPS while stage kt+2 exists,
+// else 0); ISSUE: load stage kt+3. A chunk's first stage promotes the previous
+// chunk with fac (when kt > 0); its second stage reads its token scales from
+// this stage's buffer -- which the next iteration refills -- and settles fac
+// before this wave can reach the next barrier.
+template <int MS, bool GATE_UP, bool FIRST, int WAIT, bool ISSUE>
+__device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds, const float* swt, int kt,
+                                            const Pipe8Frags<MS>& fa, Pipe8Frags<MS>& fb,
+                                            f32x16 (&T)[Pipe8::TW][Pipe8::TT], f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
+                                            float (&fac)[Pipe8::TW][Pipe8::TT]) {
+  using P = Pipe8;
+  wait_vm_only_barrier<WAIT>();
+  pipe8_read<MS>(fb, lds + ((kt + 1) & 3) * P::STAGE);
+  float sa[P::TT];
+  if (!FIRST) pipe8_read_scales<MS>(sa, lds + (kt & 3) * P::STAGE);
+  sched_fence();
+  if (FIRST) {
+    if (kt > 0) pipe8_block<MS, true, true, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
+    else pipe8_block<MS, true, false, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
+  } else {
+    pipe8_block<MS, false, false, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
+    pipe8_factors<MS, GATE_UP>(fac, sa, swt, kt >> 1);
+    pipe8_settle(fac, MS);
+  }
+}
+
+// acc[j][i] = sum over chunks of promoted T; K % 128 == 0 (nk = K / 64 even).
+// swt: weight scales of the tile in LDS, [2][MAX_CHUNKS].
+template <int MS, bool GATE_UP>
+__device__ __forceinline__ void pipe8_mainloop(const Pipe8Rows& rows, int K, uint8_t* lds, const float* swt,
+                                               f32x16 (&acc)[Pipe8::TW][Pipe8::TT]) {
+  using P = Pipe8;
+  const int nk = K / P::BK;
+  for (int s = 0; s < 3 && s < nk; ++s) {
+#pragma unroll
+    for (int q = 0; q < P::LPS; ++q) pipe8_issue_one(rows, lds + s * P::STAGE, s, q);
+  }
+  if (nk >= 3) wait_vm_only_barrier<2 * P::LPS>();
+  else wait_vm_only_barrier<P::LPS>();                 // nk == 2
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0xc07f);                  // no scalar load pending: LDS waits stay partial
+#endif
+  f32x16 T[P::TW][P::TT];
+  float fac[P::TW][P::TT];
+  Pipe8Frags<MS> f0, f1;
+  pipe8_read<MS>(f0, lds);
+  int kt = 0;
+  for (; kt + 4 < nk; kt += 2) {                       // both stages refill the ring
+    pipe8_stage<MS, GATE_UP, true, P::LPS, true>(rows, lds, swt, kt, f0, f1, T, acc, fac);
+    pipe8_stage<MS, GATE_UP, false, P::LPS, true>(rows, lds, swt, kt + 1, f1, f0, T, acc, fac);
+  }
+  if (kt + 4 == nk) {                                  // stage nk-1 is the last to load
+    pipe8_stage<MS, GATE_UP, true, P::LPS, true>(rows, lds, swt, kt, f0, f1, T, acc, fac);
+    pipe8_stage<MS, GATE_UP, false, P::LPS, false>(rows, lds, swt, kt + 1, f1, f0, T, acc, fac);
+    kt += 2;
+  }
+  // last chunk: stage nk-2 reads nk-1; stage nk-1 reads nothing and is not refilled
+  pipe8_stage<MS, GATE_UP, true, 0, false>(rows, lds, swt, kt, f0, f1, T, acc, fac);
+  float sa[P::TT];
+  pipe8_read_scales<MS>(sa, lds + ((kt + 1) & 3) * P::STAGE);
+  pipe8_block<MS, false, false, false>(f1, T, acc, fac, rows, lds, 0);
+  pipe8_factors<MS, GATE_UP>(fac, sa, swt, (nk >> 1) - 1);
+  // the reads below follow the last MFMAs closely: give them the wait states
+  // an MFMA result needs before a v_accvgpr_read (the asm read is opaque to
+  // the compiler's hazard checks)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < P::TW; ++j)
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = fmaf(agpr_read(T[j][i][v]), fac[j][i], acc[j][i][v]);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace moe

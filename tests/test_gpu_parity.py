@@ -409,6 +409,54 @@ def _check_fp8_experts(cfg, inp, layer, experts, tag):
             assert same > 0.99 and sdiff < 1e-4
 
 
+@pytest.mark.parametrize("inter,mode", [(128, "gather"), (1408, "gather"), (1408, "direct")])
+def test_grouped_ffn_fp8_tile_shapes(inter, mode):
+    """fp8 grouped FFN on expert segments that reach every block shape.
+
+    Blocks hold at most four 32-row sub-tiles (two per wave row). Sizes: empty,
+    1 row, 1 and 2 sub-tiles, 3 with a tail, exactly 4, 5 (split 2 + 3), 9 and
+    13 (four blocks). inter = 128 gives the down projection a two-stage K loop
+    (one 128 chunk); 1408 an odd number of chunks (11), which ends the loop on
+    its drain branch. Inputs: oracle-quantised activations and weights; the
+    H codes and scales are compared as well.
+    """
+    cfg = get_config("c2", gemm="fp8", n_routed=10, n_groups=1, topk_groups=1, T=1024, topk=2, inter=inter)
+    inp = generate(cfg, DEV)
+    sh = B.moe_shape.of(cfg)
+    sizes = [0, 1, 32, 64, 65 + 30, 128, 160, 288, 0, 416]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    assert n <= cfg.T * cfg.topk
+    rng = np.random.default_rng(23)
+    src = rng.integers(0, cfg.T, n)
+    u32 = inp["u"].cpu().float().numpy()
+    uq, us = oracle.quantize_tiles(u32)
+    wq = [_oracle_wq(inp, e) for e in range(cfg.n_routed)]
+    dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    wgu = dev8(np.stack([w[0] for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
+    wdn = dev8(np.stack([w[2] for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
+    h = torch.empty((n, inter), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((n, inter // 128), dtype=torch.float32, device=DEV)
+    y = torch.empty((n, cfg.d), dtype=torch.bfloat16, device=DEV)
+    if mode == "gather":
+        a, a_s, a_rows, rmode, rsrc = dev8(uq), dev8(us), cfg.T, B.MOE_ROWS_GATHER, _i32(src)
+    else:
+        a, a_s, a_rows, rmode, rsrc = dev8(uq[src]), dev8(us[src]), n, B.MOE_ROWS_DIRECT, None
+    B.moe_ffn_gate_up(sh, B.MOE_F8E4M3, cfg.n_routed, n, _i32(off), rmode, rsrc, a, a_s, a_rows, wgu, wgs, h, hs)
+    B.moe_ffn_down(sh, B.MOE_F8E4M3, cfg.n_routed, n, _i32(off), h, hs, wdn, wds, y)
+    torch.cuda.synchronize()
+    for e in range(cfg.n_routed):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        ref, aux = oracle.ffn_fp8(u32[src[lo:hi]], *wq[e], return_h=True)
+        report(f"fp8 I={inter} {mode} expert {e} ({hi - lo} rows) y", rel_l2(y[lo:hi], ref), TOL["fp8"])
+        same = float(np.mean(h[lo:hi].cpu().numpy() == aux["h_codes"]))
+        sdiff = np.max(np.abs(hs[lo:hi].cpu().numpy() / aux["h_scale"] - 1))
+        print(f"[parity] expert {e}: H codes equal {same:.4f}, max rel scale diff {sdiff:.2e}")
+        assert same > 0.99 and sdiff < 1e-4
+
+
 @pytest.mark.parametrize("name", ["c2", "c4"])
 def test_fp8_layer_sampled(name):
     over = dict(gemm="fp8") if name == "c2" else {}
