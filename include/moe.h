@@ -144,7 +144,7 @@ moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* top
  *   y_dtype      MOE_F32 (only with w = MOE_F32) or MOE_BF16.
  *   y            out [n_rows, d].
  * Limits: d and I multiples of 128; with MOE_BF16, a_rows * d, n_rows * I and
- * 2 * I * d below 2^31 elements, with MOE_F8E4M3 below 2^32 and d, I <= 32768
+ * 2 * I * d below 2^31 elements, with MOE_F8E4M3 below 2^32 and d, I <= 10240
  * (32-bit byte offsets); otherwise MOE_E_UNSUPPORTED.
  */
 moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,

@@ -181,7 +181,7 @@ moe_status check_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int
   SUPPORT(static_cast<long long>(n_rows) * (d > I ? d : I) < (1LL << 40), "grouped_ffn: too many rows");
   REQUIRE(offsets != nullptr, "grouped_ffn: expert_offsets is NULL");
   REQUIRE(w == MOE_F32 || w == MOE_BF16 || w == MOE_F8E4M3, "grouped_ffn: bad weight dtype %d", static_cast<int>(w));
-  SUPPORT(w != MOE_F8E4M3 || (d <= 32768 && I <= 32768), "grouped_ffn: the fp8 path needs d and inter <= 32768");
+  SUPPORT(w != MOE_F8E4M3 || (d <= 10240 && I <= 10240), "grouped_ffn: the fp8 path needs d and inter <= 10240");
   // the fp8 kernels address codes and scales through 32-bit byte offsets
   SUPPORT(w != MOE_F8E4M3 || (static_cast<long long>(n_rows) * I < (1LL << 32) &&
                               static_cast<long long>(2 * I) * d < (1LL << 32)),

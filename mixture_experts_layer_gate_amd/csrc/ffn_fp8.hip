@@ -5,10 +5,10 @@
 // Activations carry one fp32 scale per 1x128 tile (row, K chunk), weights one
 // per 128x128 block; every 128-wide K chunk is promoted into fp32 with the
 // product of the two scales (gemm_pipe8.h). Two persistent launches over all
-// experts, one 512-thread workgroup per CU, 256 weight rows x 128 token rows
+// experts, one 256-thread workgroup per CU, 256 weight rows x 128 token rows
 // per tile, balanced blocks of at most four 32-row sub-tiles:
-//  1. gate/up: H[r, c] = SiLU(g) * u for 128 H columns per tile (each wave 32
-//     gate rows + the matching 32 up rows, so the product forms in registers);
+//  1. gate/up: H[r, c] = SiLU(g) * u for 128 H columns per tile (each wave 64
+//     gate rows + the matching 64 up rows, so the product forms in registers);
 //     H is then re-quantised per 1x128 tile along I -- the tile owns exactly
 //     one such tile per row: amax over its 128 columns, inv = fl32(448 / amax),
 //     codes = E4M3(fl32(h * inv)), scale = fl32(amax / 448) (1 for amax = 0).
@@ -44,7 +44,7 @@ __device__ __forceinline__ void zero_acc8(f32x16 (&acc)[P8::TW][P8::TT]) {
 // weight sub-tile j: four consecutive columns per lane.
 __device__ __forceinline__ int p8_wcol(int j, int q) {
   const int l = threadIdx.x & 63;
-  return p8_ww() * 64 + j * 32 + 8 * q + 4 * (l >> 5);
+  return p8_ww() * (P8::BW / 2) + j * 32 + 8 * q + 4 * (l >> 5);
 }
 
 // Tile row of token sub-tile i of this lane.
@@ -54,23 +54,27 @@ __device__ __forceinline__ int p8_token_row(int i) {
 }
 
 template <int MS>
-__device__ __forceinline__ void gate_up8_tile(const Pipe8Rows& rows, int d, int I, const Unit& un, uint8_t* lds,
-                                              const float* swt, uint8_t* __restrict__ Hq, float* __restrict__ Hs) {
+__device__ __forceinline__ void gate_up8_tile(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
+                                              const Unit& un, uint8_t* lds, uint8_t* __restrict__ Hq,
+                                              float* __restrict__ Hs) {
   f32x16 acc[P8::TW][P8::TT];
   zero_acc8<MS>(acc);
-  pipe8_mainloop<MS, true>(rows, d, lds, swt, acc);
-  // SwiGLU in fp32; this wave holds 32 of the tile's 128 H columns of each row
+  pipe8_mainloop<MS, true>(rows, srs, d, lds, acc);
+  // SwiGLU in fp32; this wave holds 64 of the tile's 128 H columns of each row
+  // (gate sub-tiles 0, 1 with the up sub-tiles 2, 3)
   const int l = threadIdx.x & 63, ww = p8_ww();
-  float* amax_x = reinterpret_cast<float*>(lds);   // [4][BT], the ring is free after the main loop
-  float hv[P8::TT][16];
+  float* amax_x = reinterpret_cast<float*>(lds);   // [2][BT], the ring is free after the main loop
+  float hv[P8::TT][2][16];
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     float x = 0.0f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      hv[i][v] = silu(acc[0][i][v]) * acc[1][i][v];
-      x = fmaxf(x, __builtin_fabsf(hv[i][v]));
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        hv[i][j][v] = silu(acc[j][i][v]) * acc[j + 2][i][v];
+        x = fmaxf(x, __builtin_fabsf(hv[i][j][v]));
+      }
     x = fmaxf(x, __shfl_xor(x, 32, kWave));
     if (l < 32) amax_x[ww * P8::BT + p8_token_row(i)] = x;
   }
@@ -78,29 +82,31 @@ __device__ __forceinline__ void gate_up8_tile(const Pipe8Rows& rows, int d, int 
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     const int tr = p8_token_row(i);
-    const float amax = fmaxf(fmaxf(amax_x[tr], amax_x[P8::BT + tr]), fmaxf(amax_x[2 * P8::BT + tr], amax_x[3 * P8::BT + tr]));
+    const float amax = fmaxf(amax_x[tr], amax_x[P8::BT + tr]);
     if (tr < un.rows) {
       const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
-      uint8_t* hrow = Hq + static_cast<size_t>(un.m0 + tr) * I + un.nb * 128 + ww * 32 + 4 * (l >> 5);
+      uint8_t* hrow = Hq + static_cast<size_t>(un.m0 + tr) * I + un.nb * 128 + ww * 64 + 4 * (l >> 5);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t packed = 0;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) packed |= f32_to_e4m3(hv[i][4 * q + r] * inv) << (8 * r);
-        *reinterpret_cast<uint32_t*>(hrow + 8 * q) = packed;
-      }
+        for (int q = 0; q < 4; ++q) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) packed |= f32_to_e4m3(hv[i][j][4 * q + r] * inv) << (8 * r);
+          *reinterpret_cast<uint32_t*>(hrow + j * 32 + 8 * q) = packed;
+        }
       if (ww == 0 && l < 32) Hs[static_cast<size_t>(un.m0 + tr) * (I / 128) + un.nb] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
     }
   }
-  __syncthreads();   // amax_x and the weight scales are rewritten by the next tile
+  __syncthreads();   // amax_x and the LDS tables are rewritten by the next tile
 }
 
 template <int MS>
-__device__ __forceinline__ void down8_tile(const Pipe8Rows& rows, int d, int I, const Unit& un, uint8_t* lds,
-                                           const float* swt, uint16_t* __restrict__ y) {
+__device__ __forceinline__ void down8_tile(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
+                                           const Unit& un, uint8_t* lds, uint16_t* __restrict__ y) {
   f32x16 acc[P8::TW][P8::TT];
   zero_acc8<MS>(acc);
-  pipe8_mainloop<MS, false>(rows, I, lds, swt, acc);
+  pipe8_mainloop<MS, false>(rows, srs, I, lds, acc);
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     const int tr = p8_token_row(i);
@@ -115,7 +121,7 @@ __device__ __forceinline__ void down8_tile(const Pipe8Rows& rows, int d, int I, 
                     pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])};
     }
   }
-  __syncthreads();   // the weight scales are rewritten by the next tile
+  __syncthreads();   // the LDS tables are rewritten by the next tile
 }
 
 __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
@@ -124,51 +130,49 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
     const uint8_t* __restrict__ wgu, const float* __restrict__ wgu_scale, uint8_t* __restrict__ Hq,
     float* __restrict__ Hs) {
   extern __shared__ __align__(16) uint8_t lds8[];
-  float* swt = reinterpret_cast<float*>(lds8 + P8::RING);
+  float* swt = reinterpret_cast<float*>(lds8 + P8::SW_OFF);
+  int* srcrow = reinterpret_cast<int*>(lds8 + P8::SRC_OFF);
   int* cum = reinterpret_cast<int*>(lds8 + P8::LDS_BYTES);
   __shared__ int wtmp[16];
   const int kc = d / 128;
   const int total = build_units_balanced(off, E, n_rows, kMaxSub8, I / 128, cum, wtmp);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t trs = pipe_rsrc(a, static_cast<uint64_t>(a_rows) * d);
+  const __amdgpu_buffer_rsrc_t srs = pipe_rsrc(a_scale, static_cast<uint64_t>(a_rows) * kc * 4);
   for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
     const Unit un = find_unit_balanced(t, off, E, n_rows, kMaxSub8, cum);
-    // weight scales of the tile: gate block row nb, up block row I/128 + nb
+    // LDS tables of the tile: weight scales (gate block row nb, up block row
+    // I/128 + nb) and the source row of each tile row (rows past the block
+    // read any valid row and are never stored)
     const float* sexp = wgu_scale + static_cast<size_t>(un.e) * (2 * I / 128) * kc;
     for (int x = tid; x < 2 * kc; x += P8::NT) {
       const int b = x / kc, c = x - b * kc;
       swt[b * P8::MAX_CHUNKS + c] = sexp[static_cast<size_t>(b ? I / 128 + un.nb : un.nb) * kc + c];
     }
+    if (tid < P8::BT) {
+      int s_first = source_row(mode, row_src, un.m0, un.seg0, a_rows);
+      if (s_first < 0) s_first = 0;
+      const int sr = tid < un.rows ? source_row(mode, row_src, un.m0 + tid, un.seg0, a_rows) : -1;
+      srcrow[tid] = sr < 0 ? s_first : sr;
+    }
     __syncthreads();
-    int s_first = source_row(mode, row_src, un.m0, un.seg0, a_rows);
-    if (s_first < 0) s_first = 0;
     Pipe8Rows rows;
-    rows.trs = pipe_rsrc(a, static_cast<uint64_t>(a_rows) * d);
+    rows.trs = trs;
 #pragma unroll
-    for (int q = 0; q < P8::TL; ++q) {
-      const int r = pipe8_load_row(q);
-      int sr = r < un.rows ? source_row(mode, row_src, un.m0 + r, un.seg0, a_rows) : -1;
-      if (sr < 0) sr = s_first;                       // rows past the block: any valid row, never stored
-      rows.ot[q] = static_cast<uint32_t>(sr) * d + pipe8_load_chunk(q) * 16;
-    }
-    {
-      const int r = (w & 1) * 64 + l;                 // waves 2..7 repeat waves 0, 1 into spare copies
-      int sr = r < un.rows ? source_row(mode, row_src, un.m0 + r, un.seg0, a_rows) : -1;
-      if (sr < 0) sr = s_first;
-      rows.srs = pipe_rsrc(a_scale, static_cast<uint64_t>(a_rows) * kc * 4);
-      rows.os = static_cast<uint32_t>(sr) * kc * 4;
-    }
+    for (int q = 0; q < P8::TL; ++q)
+      rows.ot[q] = static_cast<uint32_t>(srcrow[pipe8_load_row(q)]) * d + pipe8_load_chunk(q) * 16;
     rows.wrs = pipe_rsrc(wgu + static_cast<size_t>(un.e) * 2 * I * d, static_cast<uint64_t>(2 * I) * d);
 #pragma unroll
     for (int q = 0; q < P8::WL; ++q) {
       const int rw = pipe8_load_row(q);
-      const int hcol = un.nb * 128 + (rw >> 6) * 32 + (rw & 31);   // wave quarter rw / 64 owns 32 H columns:
-      const bool up = (rw >> 5) & 1;                               // its sub-tile 0 gate rows, 1 the up rows
-      rows.ow[q] = static_cast<uint32_t>(up ? I + hcol : hcol) * d + pipe8_load_chunk(q) * 16;
+      const int j = (rw >> 5) & 3;                    // wave half rw / 128 owns 64 H columns: its
+      const int hcol = un.nb * 128 + (rw >> 7) * 64 + (j & 1) * 32 + (rw & 31);   // sub-tiles 0,1 gate rows,
+      rows.ow[q] = static_cast<uint32_t>(j >= 2 ? I + hcol : hcol) * d + pipe8_load_chunk(q) * 16;  // 2,3 up rows
     }
     switch (live_token_subtiles8(un.nsub)) {
-      case 2: gate_up8_tile<2>(rows, d, I, un, lds8, swt, Hq, Hs); break;
-      case 1: gate_up8_tile<1>(rows, d, I, un, lds8, swt, Hq, Hs); break;
-      default: gate_up8_tile<0>(rows, d, I, un, lds8, swt, Hq, Hs); break;
+      case 2: gate_up8_tile<2>(rows, srs, d, I, un, lds8, Hq, Hs); break;
+      case 1: gate_up8_tile<1>(rows, srs, d, I, un, lds8, Hq, Hs); break;
+      default: gate_up8_tile<0>(rows, srs, d, I, un, lds8, Hq, Hs); break;
     }
   }
 }
@@ -181,41 +185,38 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
                                                                  const float* __restrict__ wd_scale,
                                                                  uint16_t* __restrict__ y) {
   extern __shared__ __align__(16) uint8_t lds8[];
-  float* swt = reinterpret_cast<float*>(lds8 + P8::RING);
+  float* swt = reinterpret_cast<float*>(lds8 + P8::SW_OFF);
+  int* srcrow = reinterpret_cast<int*>(lds8 + P8::SRC_OFF);
   int* cum = reinterpret_cast<int*>(lds8 + P8::LDS_BYTES);
   __shared__ int wtmp[16];
   const int kc = I / 128;
   const int total = build_units_balanced(off, E, n_rows, kMaxSub8, d / P8::BW, cum, wtmp);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t trs = pipe_rsrc(Hq, static_cast<uint64_t>(n_rows) * I);
+  const __amdgpu_buffer_rsrc_t srs = pipe_rsrc(Hs, static_cast<uint64_t>(n_rows) * kc * 4);
   for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
     const Unit un = find_unit_balanced(t, off, E, n_rows, kMaxSub8, cum);
-    // weight scales: waves ww = 0,1 cover output columns nb*256 .. +127 (block row 2nb), ww = 2,3 the next 128
+    // weight scales: wave half ww covers output columns nb*256 + 128ww .. +127 = block row 2nb + ww
     const float* sexp = wd_scale + static_cast<size_t>(un.e) * (d / 128) * kc;
     for (int x = tid; x < 2 * kc; x += P8::NT) {
       const int b = x / kc, c = x - b * kc;
       swt[b * P8::MAX_CHUNKS + c] = sexp[static_cast<size_t>(2 * un.nb + b) * kc + c];
     }
+    if (tid < P8::BT) srcrow[tid] = un.m0 + (tid < un.rows ? tid : 0);
     __syncthreads();
     Pipe8Rows rows;
-    rows.trs = pipe_rsrc(Hq, static_cast<uint64_t>(n_rows) * I);
+    rows.trs = trs;
 #pragma unroll
-    for (int q = 0; q < P8::TL; ++q) {
-      const int r = pipe8_load_row(q);
-      rows.ot[q] = static_cast<uint32_t>(un.m0 + (r < un.rows ? r : 0)) * I + pipe8_load_chunk(q) * 16;
-    }
-    {
-      const int r = (w & 1) * 64 + l;
-      rows.srs = pipe_rsrc(Hs, static_cast<uint64_t>(n_rows) * kc * 4);
-      rows.os = static_cast<uint32_t>(un.m0 + (r < un.rows ? r : 0)) * kc * 4;
-    }
+    for (int q = 0; q < P8::TL; ++q)
+      rows.ot[q] = static_cast<uint32_t>(srcrow[pipe8_load_row(q)]) * I + pipe8_load_chunk(q) * 16;
     rows.wrs = pipe_rsrc(wd + static_cast<size_t>(un.e) * d * I, static_cast<uint64_t>(d) * I);
 #pragma unroll
     for (int q = 0; q < P8::WL; ++q)
       rows.ow[q] = static_cast<uint32_t>(un.nb * P8::BW + pipe8_load_row(q)) * I + pipe8_load_chunk(q) * 16;
     switch (live_token_subtiles8(un.nsub)) {
-      case 2: down8_tile<2>(rows, d, I, un, lds8, swt, y); break;
-      case 1: down8_tile<1>(rows, d, I, un, lds8, swt, y); break;
-      default: down8_tile<0>(rows, d, I, un, lds8, swt, y); break;
+      case 2: down8_tile<2>(rows, srs, d, I, un, lds8, y); break;
+      case 1: down8_tile<1>(rows, srs, d, I, un, lds8, y); break;
+      default: down8_tile<0>(rows, srs, d, I, un, lds8, y); break;
     }
   }
 }

@@ -11,23 +11,24 @@
 // scales are applied on the VALU: the accumulator lives in VGPRs, T (the
 // MFMA destination) in AGPRs.
 //
-// Tile: BW = 256 weight rows x BT = 128 token rows, eight waves (two per
-// SIMD) in a 4 (weight) x 2 (token) grid of 64 x 64: TW = 2 weight sub-tiles
-// x up to 2 token sub-tiles of 32x32, so a wave holds 64 accumulator and 64
-// temporary registers, and one wave's promotion runs while the other wave on
-// its SIMD issues MFMAs. (One wave per SIMD with 128 x 64 each spilled: the
-// accumulator, the temporaries and the fragments do not fit 512 registers.)
-// Both operands stream into LDS with buffer_load ... lds through a ring of
-// four stages of 64 K-bytes (one MFMA K-step), rows of 64 bytes XOR-swizzled
-// as in the bf16 loop; each stage also brings the 128 token scales of its
-// chunk. Weight scales of the tile sit in LDS.
+// Tile: BW = 256 weight rows x BT = 128 token rows, four waves (one per
+// SIMD) in a 2 x 2 grid of 128 x 64: TW = 4 weight sub-tiles x up to 2 token
+// sub-tiles of 32x32; a wave holds 128 accumulator VGPRs and 128 temporary
+// AGPRs (the fragments share the AGPRs). A 256 x 256 tile would need twice
+// the register file.
+// Weight and token rows stream into LDS with buffer_load ... lds through a
+// ring of four stages of 64 K-bytes (one MFMA K-step), rows of 64 bytes
+// XOR-swizzled as in the bf16 loop. The tile's token scales (128 rows x all
+// chunks) and weight scales are loaded into LDS tables once per tile: loaded
+// per stage, the 4-byte scales of 128 scattered rows cost more L2 requests
+// than the stage's 24 KB of operands.
 //
 // Iteration kt (stage kt, chunk kt / 2): wait until stage kt+1 has landed +
-// barrier; read stage kt+1's fragments (and, in a chunk's second stage, this
-// chunk's token scales, before the buffer is refilled); the MFMAs of stage kt
-// with the loads of stage kt+3 spread among them. In a chunk's first stage
-// each element of T is promoted (chunk c-1, whose MFMAs were issued a block
-// earlier) just before the C = 0 MFMA that restarts it.
+// barrier; read stage kt+1's fragments; the MFMAs of stage kt with the loads
+// of stage kt+3 spread among them. In a chunk's first stage each element of
+// T is promoted (chunk c-1, whose MFMAs were issued a block earlier) just
+// before the C = 0 MFMA that restarts it; the second stage prepares the
+// promotion factors of its chunk.
 #pragma once
 
 #include "common.h"
@@ -36,24 +37,26 @@
 namespace moe {
 
 struct Pipe8 {
-  static constexpr int BW = 256, BT = 128, BK = 64, NS = 4, NT = 512, NWAVE = NT / 64;
-  static constexpr int TW = 2, TT = 2;                    // 32x32 sub-tiles per wave
+  static constexpr int BW = 256, BT = 128, BK = 64, NS = 4, NT = 256, NWAVE = NT / 64;
+  static constexpr int TW = 4, TT = 2;                    // 32x32 sub-tiles per wave
   static constexpr int ROWB = BK;                          // bytes per row per stage
   static constexpr int W_BYTES = BW * ROWB, T_BYTES = BT * ROWB;
-  static constexpr int S_BYTES = 4 * NT;                   // token scales: waves 0,1 real, the others spare copies
-  static constexpr int STAGE = W_BYTES + T_BYTES + S_BYTES;
+  static constexpr int STAGE = W_BYTES + T_BYTES;
   static constexpr int WL = W_BYTES / 16 / NT, TL = T_BYTES / 16 / NT;
-  static constexpr int LPS = WL + TL + 1;
+  static constexpr int LPS = WL + TL;                      // loads per thread per stage
   static constexpr int RING = NS * STAGE;
-  static constexpr int MAX_CHUNKS = 256;                   // K <= 32768
-  static constexpr int SW_BYTES = 2 * MAX_CHUNKS * 4;      // weight scales of the tile: 2 block rows
-  static constexpr int LDS_BYTES = RING + SW_BYTES;
+  static constexpr int MAX_CHUNKS = 80;                    // K <= 10240
+  static constexpr int SW_OFF = RING;                      // weight scales [2][MAX_CHUNKS]
+  static constexpr int SA_OFF = SW_OFF + 2 * MAX_CHUNKS * 4;   // token scales [BT][kc_pad]
+  static constexpr int SRC_OFF = SA_OFF + BT * MAX_CHUNKS * 4; // source row of each tile row [BT]
+  static constexpr int LDS_BYTES = SRC_OFF + BT * 4;
   static_assert(WL * NT * 16 == W_BYTES && TL * NT * 16 == T_BYTES, "stage must split evenly over the threads");
   static_assert(LPS * 3 <= 63, "vmcnt range");
+  static_assert((BT * 4) % NT == 0, "four chunks of the scale table split evenly over the threads");
 };
 
 // Wave coordinates: token half wt (rows 32 * (2i + wt) + lane % 32), weight
-// quarter ww (tile rows 64 ww .. 64 ww + 63).
+// half ww (tile rows 128 ww .. 128 ww + 127).
 __device__ __forceinline__ int p8_wt() { return (threadIdx.x >> 6) & 1; }
 __device__ __forceinline__ int p8_ww() { return threadIdx.x >> 7; }
 
@@ -69,17 +72,15 @@ __device__ __forceinline__ int pipe8_load_chunk(int q) {
 }
 
 // Operands: weights and token codes through buffer resources with 32-bit
-// byte offsets (row * K + logical chunk * 16), token scales likewise
-// (scale row * K / 128 * 4; the chunk goes in soffset).
+// byte offsets (row * K + logical chunk * 16).
 struct Pipe8Rows {
-  __amdgpu_buffer_rsrc_t wrs, trs, srs;
+  __amdgpu_buffer_rsrc_t wrs, trs;
   uint32_t ow[Pipe8::WL];
   uint32_t ot[Pipe8::TL];
-  uint32_t os;
 };
 
-// Loads of stage s (K bytes s * 64 .. +63) into ring buffer st; load q of a
-// thread: weights q < WL, tokens q < WL + TL, then the scale dword.
+// Load q of stage s (K bytes s * 64 .. +63) into ring buffer st: weights for
+// q < WL, then token rows.
 __device__ __forceinline__ void pipe8_issue_one(const Pipe8Rows& r, uint8_t* st, int s, int q) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using P = Pipe8;
@@ -88,13 +89,29 @@ __device__ __forceinline__ void pipe8_issue_one(const Pipe8Rows& r, uint8_t* st,
   if (q < P::WL) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.wrs, (lds_void_t*)(st + (q * P::NWAVE + w) * 1024), 16, r.ow[q], kb,
                                              0, 0);
-  } else if (q < P::WL + P::TL) {
+  } else {
     const int qq = q - P::WL;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.trs, (lds_void_t*)(st + P::W_BYTES + (qq * P::NWAVE + w) * 1024), 16,
                                              r.ot[qq], kb, 0, 0);
-  } else {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.srs, (lds_void_t*)(st + P::W_BYTES + P::T_BYTES + w * 256), 4, r.os,
-                                             (s >> 1) * 4, 0, 0);
+  }
+#endif
+}
+
+// Token-scale table of the tile: entry (r, c) = scales[src[r] * kc + min(c, kc-1)]
+// at LDS float r * kc_pad + c, kc_pad = kc rounded up to a multiple of 4 so each
+// thread issues exactly kc_pad / 4 dword loads (a wave's load covers 64
+// consecutive entries: one or a few rows, contiguous in memory). The loads
+// count in vmcnt like the ring's and complete at the prologue's wait.
+__device__ __forceinline__ void pipe8_issue_scale_table(__amdgpu_buffer_rsrc_t srs, uint8_t* lds, int kc, int kc_pad) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using P = Pipe8;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int* src = reinterpret_cast<const int*>(lds + P::SRC_OFF);
+  for (int q = 0; q < kc_pad * P::BT / P::NT; ++q) {
+    const int e = q * P::NT + tid, r = e / kc_pad, c = min(e - r * kc_pad, kc - 1);
+    const uint32_t off = (static_cast<uint32_t>(src[r]) * kc + c) * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void_t*)(lds + P::SA_OFF + (q * P::NT + w * 64) * 4), 4, off, 0,
+                                             0, 0);
   }
 #endif
 }
@@ -118,18 +135,9 @@ template <int MS>
 __device__ __forceinline__ void pipe8_read(Pipe8Frags<MS>& f, const uint8_t* st) {
   const int l = threadIdx.x & 63, wt = p8_wt(), ww = p8_ww();
 #pragma unroll
-  for (int j = 0; j < Pipe8::TW; ++j) f.w[j] = pipe8_frag(st, ww * 64 + j * 32 + (l & 31));
+  for (int j = 0; j < Pipe8::TW; ++j) f.w[j] = pipe8_frag(st, ww * (Pipe8::BW / 2) + j * 32 + (l & 31));
 #pragma unroll
   for (int i = 0; i < MS; ++i) f.t[i] = pipe8_frag(st + Pipe8::W_BYTES, 32 * (2 * i + wt) + (l & 31));
-}
-
-// Token scales of this lane's token rows for the chunk held in ring buffer st.
-template <int MS>
-__device__ __forceinline__ void pipe8_read_scales(float (&sa)[Pipe8::TT], const uint8_t* st) {
-  const int l = threadIdx.x & 63, wt = p8_wt();
-  const float* s = reinterpret_cast<const float*>(st + Pipe8::W_BYTES + Pipe8::T_BYTES);
-#pragma unroll
-  for (int i = 0; i < MS; ++i) sa[i] = s[32 * (2 * i + wt) + (l & 31)];
 }
 
 // One element of an MFMA result, read out of its AGPR at the promotion and
@@ -202,72 +210,62 @@ __device__ __forceinline__ void pipe8_block(const Pipe8Frags<MS>& f, f32x16 (&T)
   sched_fence();
 }
 
-// Weight-scale row of weight sub-tile j of this wave: gate/up tiles use block
-// row 0 (gate) for j = 0 and 1 (up) for j = 1; down tiles the 128-row block of
-// this wave's 64 rows.
-template <bool GATE_UP>
-__device__ __forceinline__ int pipe8_sw_row(int j) {
-  return GATE_UP ? j : (p8_ww() >> 1);
-}
-
+// Promotion factors of chunk c: token scale of this lane's row of sub-tile i
+// times the weight-block scale of sub-tile j (gate/up tiles: block row 0 for
+// the gate sub-tiles j < TW / 2, 1 for the up sub-tiles; down tiles: the
+// 128-row block of this wave's rows).
 template <int MS, bool GATE_UP>
-__device__ __forceinline__ void pipe8_factors(float (&fac)[Pipe8::TW][Pipe8::TT], const float (&sa)[Pipe8::TT],
-                                              const float* swt, int c) {
+__device__ __forceinline__ void pipe8_factors(float (&fac)[Pipe8::TW][Pipe8::TT], const uint8_t* lds, int kc_pad,
+                                              int c) {
+  const float* swt = reinterpret_cast<const float*>(lds + Pipe8::SW_OFF);
+  const float* sat = reinterpret_cast<const float*>(lds + Pipe8::SA_OFF);
+  const int l = threadIdx.x & 63, wt = p8_wt();
 #pragma unroll
-  for (int j = 0; j < Pipe8::TW; ++j)
+  for (int i = 0; i < MS; ++i) {
+    const float sa = sat[(32 * (2 * i + wt) + (l & 31)) * kc_pad + c];
 #pragma unroll
-    for (int i = 0; i < MS; ++i) fac[j][i] = sa[i] * swt[pipe8_sw_row<GATE_UP>(j) * Pipe8::MAX_CHUNKS + c];
-}
-
-// Keeps a value's computation (and the LDS read it needs) before the next
-// barrier: an empty asm that uses the value.
-__device__ __forceinline__ void pipe8_settle(const float (&fac)[Pipe8::TW][Pipe8::TT], int ms) {
-#pragma unroll
-  for (int j = 0; j < Pipe8::TW; ++j)
-#pragma unroll
-    for (int i = 0; i < Pipe8::TT; ++i)
-      if (i < ms) asm volatile("" ::"v"(fac[j][i]));
+    for (int j = 0; j < Pipe8::TW; ++j)
+      fac[j][i] = sa * swt[(GATE_UP ? (j >= Pipe8::TW / 2 ? 1 : 0) : p8_ww()) * Pipe8::MAX_CHUNKS + c];
+  }
 }
 
 // One stage kt < nk - 1: fa holds its fragments, fb receives stage kt+1's.
 // WAIT: loads allowed in flight at the barrier (LPS while stage kt+2 exists,
 // else 0); ISSUE: load stage kt+3. A chunk's first stage promotes the previous
-// chunk with fac (when kt > 0); its second stage reads its token scales from
-// this stage's buffer -- which the next iteration refills -- and settles fac
-// before this wave can reach the next barrier.
+// chunk with fac (when kt > 0); its second stage computes fac for its chunk.
 template <int MS, bool GATE_UP, bool FIRST, int WAIT, bool ISSUE>
-__device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds, const float* swt, int kt,
+__device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds, int kc_pad, int kt,
                                             const Pipe8Frags<MS>& fa, Pipe8Frags<MS>& fb,
                                             f32x16 (&T)[Pipe8::TW][Pipe8::TT], f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
                                             float (&fac)[Pipe8::TW][Pipe8::TT]) {
   using P = Pipe8;
   wait_vm_only_barrier<WAIT>();
   pipe8_read<MS>(fb, lds + ((kt + 1) & 3) * P::STAGE);
-  float sa[P::TT];
-  if (!FIRST) pipe8_read_scales<MS>(sa, lds + (kt & 3) * P::STAGE);
   sched_fence();
   if (FIRST) {
     if (kt > 0) pipe8_block<MS, true, true, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
     else pipe8_block<MS, true, false, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
   } else {
     pipe8_block<MS, false, false, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
-    pipe8_factors<MS, GATE_UP>(fac, sa, swt, kt >> 1);
-    pipe8_settle(fac, MS);
+    pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, kt >> 1);
   }
 }
 
-// acc[j][i] = sum over chunks of promoted T; K % 128 == 0 (nk = K / 64 even).
-// swt: weight scales of the tile in LDS, [2][MAX_CHUNKS].
+// acc[j][i] = sum over chunks of promoted T; K % 128 == 0 (nk = K / 64 even),
+// K / 128 <= MAX_CHUNKS. Before the call the tile's source rows and weight
+// scales are in LDS (and visible to every wave); the token-scale table is
+// loaded here from srs (kc = K / 128 scales per source row).
 template <int MS, bool GATE_UP>
-__device__ __forceinline__ void pipe8_mainloop(const Pipe8Rows& rows, int K, uint8_t* lds, const float* swt,
+__device__ __forceinline__ void pipe8_mainloop(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int K, uint8_t* lds,
                                                f32x16 (&acc)[Pipe8::TW][Pipe8::TT]) {
   using P = Pipe8;
-  const int nk = K / P::BK;
+  const int nk = K / P::BK, kc = K / 128, kc_pad = (kc + 3) & ~3;
+  pipe8_issue_scale_table(srs, lds, kc, kc_pad);
   for (int s = 0; s < 3 && s < nk; ++s) {
 #pragma unroll
     for (int q = 0; q < P::LPS; ++q) pipe8_issue_one(rows, lds + s * P::STAGE, s, q);
   }
-  if (nk >= 3) wait_vm_only_barrier<2 * P::LPS>();
+  if (nk >= 3) wait_vm_only_barrier<2 * P::LPS>();    // scale table and stage 0 have landed
   else wait_vm_only_barrier<P::LPS>();                 // nk == 2
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_s_waitcnt(0xc07f);                  // no scalar load pending: LDS waits stay partial
@@ -278,20 +276,18 @@ __device__ __forceinline__ void pipe8_mainloop(const Pipe8Rows& rows, int K, uin
   pipe8_read<MS>(f0, lds);
   int kt = 0;
   for (; kt + 4 < nk; kt += 2) {                       // both stages refill the ring
-    pipe8_stage<MS, GATE_UP, true, P::LPS, true>(rows, lds, swt, kt, f0, f1, T, acc, fac);
-    pipe8_stage<MS, GATE_UP, false, P::LPS, true>(rows, lds, swt, kt + 1, f1, f0, T, acc, fac);
+    pipe8_stage<MS, GATE_UP, true, P::LPS, true>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
+    pipe8_stage<MS, GATE_UP, false, P::LPS, true>(rows, lds, kc_pad, kt + 1, f1, f0, T, acc, fac);
   }
   if (kt + 4 == nk) {                                  // stage nk-1 is the last to load
-    pipe8_stage<MS, GATE_UP, true, P::LPS, true>(rows, lds, swt, kt, f0, f1, T, acc, fac);
-    pipe8_stage<MS, GATE_UP, false, P::LPS, false>(rows, lds, swt, kt + 1, f1, f0, T, acc, fac);
+    pipe8_stage<MS, GATE_UP, true, P::LPS, true>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
+    pipe8_stage<MS, GATE_UP, false, P::LPS, false>(rows, lds, kc_pad, kt + 1, f1, f0, T, acc, fac);
     kt += 2;
   }
-  // last chunk: stage nk-2 reads nk-1; stage nk-1 reads nothing and is not refilled
-  pipe8_stage<MS, GATE_UP, true, 0, false>(rows, lds, swt, kt, f0, f1, T, acc, fac);
-  float sa[P::TT];
-  pipe8_read_scales<MS>(sa, lds + ((kt + 1) & 3) * P::STAGE);
+  // last chunk: stage nk-2 reads nk-1; stage nk-1 reads nothing
+  pipe8_stage<MS, GATE_UP, true, 0, false>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
   pipe8_block<MS, false, false, false>(f1, T, acc, fac, rows, lds, 0);
-  pipe8_factors<MS, GATE_UP>(fac, sa, swt, (nk >> 1) - 1);
+  pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, (nk >> 1) - 1);
   // the reads below follow the last MFMAs closely: give them the wait states
   // an MFMA result needs before a v_accvgpr_read (the asm read is opaque to
   // the compiler's hazard checks)
