@@ -2,8 +2,9 @@
 """MoE-layer forward throughput on one MI355X.
 
 One step = one pass of the whole layer on one batch: moe_route, moe_permute,
-the routed grouped FFN (moe_ffn_gate_up + moe_ffn_down), the shared-expert
-FFN, moe_combine and the step-end moe_bias_update. Inputs (seeded synthetic
+the grouped FFN over the routed and the shared experts together
+(moe_ffn_gate_up + moe_ffn_down), moe_combine and the step-end
+moe_bias_update. Inputs (seeded synthetic
 tokens and random-init weights of the workload's shape) are resident in HBM
 before the timed region. The default workload is the DeepSeek-V3-shaped layer
 (T=8192, d=7168, 256 routed experts in 8 groups, top-8 of 4 groups, 1 shared
@@ -27,7 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12               # bytes/s, MI355X published
 MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}
 METRIC = "MoE-layer fwd tokens/s at V3 shape + % of MFMA peak (bf16, fp8)"
-CALLS = ["route", "permute", "ffn_gate_up", "ffn_down", "ffn_shared", "combine", "bias_update"]
+CALLS = ["route", "permute", "ffn_gate_up", "ffn_down", "combine", "bias_update"]
 
 
 def parse():
@@ -132,14 +133,12 @@ def main():
         rec(1)
         layer.permute(u)
         rec(2)
-        layer.ffn_routed_phases(u, between=lambda: rec(3))
+        layer.ffn_all_phases(u, between=lambda: rec(3))
         rec(4)
-        layer.ffn_shared(u)
-        rec(5)
         layer.combine(u)
-        rec(6)
+        rec(5)
         layer.bias_update()
-        rec(7)
+        rec(6)
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -151,7 +150,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -167,9 +166,9 @@ def main():
     T, d, I, K, N, Ns = cfg.T, cfg.d, cfg.inter, cfg.topk, cfg.n_routed, cfg.n_shared
     wb = 1 if cfg.gemm == "fp8" else 2          # weight bytes per element
     ab = 2                                      # u / out bytes per element (bf16)
-    # dominant kernel: routed gate/up projection
-    gu_bytes = n_touch * 2 * I * d * wb + T * d * ab
-    gu_flops = 2.0 * T * K * d * 2 * I
+    # dominant kernel: the gate/up projection of the routed and shared experts (one launch)
+    gu_bytes = (n_touch + Ns) * 2 * I * d * wb + T * d * ab
+    gu_flops = 2.0 * T * (K + Ns) * d * 2 * I
     gu_s = per_call["ffn_gate_up"] / 1e3
     gu_bound = "hbm" if gu_bytes / HBM_PEAK >= gu_flops / MFMA_PEAK[cfg.gemm] else "mfma"
     if gu_bound == "hbm":
@@ -178,18 +177,19 @@ def main():
         roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": MFMA_PEAK[cfg.gemm] / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = recorded_traffic(f"ffn_gate_up_{cfg.gemm} routed", cfg.name)
-    roof["kernel"] = "ffn_gate_up (routed experts)"
+    roof["traffic"] = recorded_traffic(f"ffn_gate_up_{cfg.gemm} routed+shared", cfg.name)
+    roof["kernel"] = "ffn_gate_up (routed + shared experts)"
     roof["mfma_frac"] = gu_flops / gu_s / MFMA_PEAK[cfg.gemm]
 
     ffn_flops = cfg.ffn_flops()
-    ffn_s = (per_call["ffn_gate_up"] + per_call["ffn_down"] + per_call["ffn_shared"]) / 1e3
+    ffn_s = (per_call["ffn_gate_up"] + per_call["ffn_down"]) / 1e3
     layer_bytes = (n_touch * 3 * I * d * wb + Ns * 3 * I * d * wb + 2 * T * d * ab + N * d * ab)
     calls = {c: {"ms": round(per_call[c], 4)} for c in CALLS}
     calls["route"]["GB/s"] = round((T * d * ab + N * d * ab) / (per_call["route"] / 1e3) / 1e9, 1)
     calls["combine"]["GB/s"] = round((T * d * ab * 2 + (T * K + T * Ns) * d * ab) / (per_call["combine"] / 1e3) / 1e9, 1)
-    calls["ffn_down"]["GB/s_weights"] = round(n_touch * I * d * wb / (per_call["ffn_down"] / 1e3) / 1e9, 1)
-    calls["ffn_shared"]["TFLOP/s"] = round(6.0 * T * Ns * d * I / (per_call["ffn_shared"] / 1e3) / 1e12, 1)
+    calls["ffn_gate_up"]["TFLOP/s"] = round(gu_flops / gu_s / 1e12, 1)
+    calls["ffn_down"]["GB/s_weights"] = round((n_touch + Ns) * I * d * wb / (per_call["ffn_down"] / 1e3) / 1e9, 1)
+    calls["ffn_down"]["TFLOP/s"] = round(2.0 * T * (K + Ns) * I * d / (per_call["ffn_down"] / 1e3) / 1e12, 1)
 
     res = {
         "metric": METRIC,

@@ -202,9 +202,10 @@ moe_status moe_bias_update(const moe_shape* shape, const int32_t* expert_load, f
 moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, const void* w_bf16,
                                 void* w_codes, float* w_scale, void* stream);
 
-/* Host: bytes of workspace that any single call above needs for this shape
- * (with the routed FFN sized for T*K rows and the shared FFN for N_s*T rows).
- * One workspace can serve all calls issued in order on one stream. */
+/* Host: bytes of workspace that any single call above needs for this shape,
+ * with moe_grouped_ffn sized for T*(K + N_s) rows: the routed and the shared
+ * experts in one call (shared expert s as one more expert whose rows are all
+ * T tokens). One workspace can serve all calls issued in order on one stream. */
 size_t moe_workspace_bytes(const moe_shape* shape, moe_dtype gemm);
 
 /* Host: message of the calling thread's last non-OK status ("" if none). */

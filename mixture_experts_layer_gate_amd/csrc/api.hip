@@ -113,7 +113,7 @@ size_t moe_workspace_bytes(const moe_shape* shape, moe_dtype gemm) {
   const moe::Shape s = moe::to_shape(*shape);
   const size_t route = align256(static_cast<size_t>(s.T) * s.N * sizeof(float));
   const size_t perm = align256(moe::permute_ws_bytes(s));
-  const int rows = s.T * (s.K > s.Ns ? s.K : s.Ns);
+  const int rows = s.T * (s.K + s.Ns);   // routed and shared experts in one grouped call
   const size_t ffn = moe::ffn_ws_bytes(gemm, rows, s.I);
   size_t m = route > perm ? route : perm;
   return m > ffn ? m : ffn;

@@ -95,12 +95,16 @@ __device__ __forceinline__ Unit find_unit(int t, const int32_t* __restrict__ off
 // Balanced blocks: an expert's rows are cut into 32-row sub-tiles, and the
 // sub-tiles into nmb = ceil(n32 / MAXSUB) blocks of nearly equal size, so a
 // 260-row expert becomes 2 x 130 rows instead of 256 + 4.
+// Units are enumerated from the last expert down (cum[k] counts the units of
+// experts E-1 .. E-k): the shared experts, appended after the routed ones and
+// the largest, are handed out first and the routed tiles fill the tail.
 __device__ __forceinline__ int build_units_balanced(const int32_t* __restrict__ off, int E, int n_rows, int MAXSUB,
                                                     int NB, int* cum, int* wtmp) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  for (int k = threadIdx.x; k < E; k += blockDim.x) {
+    const int e = E - 1 - k;
     const int lo = clampi(off[e], 0, n_rows);
     const int hi = clampi(off[e + 1], lo, n_rows);
-    cum[e] = cdiv(cdiv(hi - lo, 32), MAXSUB) * NB;
+    cum[k] = cdiv(cdiv(hi - lo, 32), MAXSUB) * NB;
   }
   __syncthreads();
   block_exclusive_scan(cum, E, wtmp);
@@ -114,12 +118,12 @@ __device__ __forceinline__ Unit find_unit_balanced(int t, const int32_t* __restr
     const int mid = (lo + hi) >> 1;
     if (cum[mid] <= t) lo = mid; else hi = mid;
   }
-  const int e = lo;
+  const int e = E - 1 - lo;
   const int s0 = clampi(off[e], 0, n_rows);
   const int s1 = clampi(off[e + 1], s0, n_rows);
   const int n32 = cdiv(s1 - s0, 32);
   const int nmb = cdiv(n32, MAXSUB);
-  const int local = t - cum[e];
+  const int local = t - cum[lo];
   const int b = local % nmb;
   const int first = b * n32 / nmb, last = (b + 1) * n32 / nmb;
   Unit u;

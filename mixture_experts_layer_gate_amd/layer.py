@@ -3,8 +3,15 @@
 ``MoELayer`` holds the expert weights, centroids and the bias on the GPU and
 runs, on one stream with no host synchronisation:
 
-  moe_route -> moe_permute -> moe_grouped_ffn (routed) -> moe_grouped_ffn
-  (shared) -> moe_combine, then moe_bias_update at the end of a step.
+  moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine, then
+  moe_bias_update at the end of a step.
+
+The grouped FFN covers the routed and the shared experts in one call: the
+weights sit routed-then-shared in one array, shared expert s is expert
+N_r + s with segment [T*K + s*T, T*K + (s+1)*T) and rows gathered through
+the identity, so its tiles fill the routed experts' tail in the same
+persistent launch. (With permuted copies instead of the fused gather the
+two run as separate calls.)
 
 Torch only allocates device memory and provides the stream; every step runs
 in libmoe.so.
@@ -57,21 +64,24 @@ class MoELayer:
         self.centroids = to(weights["centroids"])
         self.bias = weights["bias"].to(self.dev, torch.float32).clone()  # layer-owned state
         self.act_dtype = self.centroids.dtype
-        if self.gemm == B.MOE_F8E4M3:
-            self.w = {}
-            for k in ("w_gate_up", "w_down", "s_gate_up", "s_down"):
-                src = to(weights[k])
-                n, r, c = src.shape
+        N, Ns = cfg.n_routed, cfg.n_shared
+        self.w = {}
+        for kind in ("gate_up", "down"):
+            # routed experts, then shared ones, in one array; the per-kind views alias it
+            both = torch.cat([to(weights["w_" + kind]), to(weights["s_" + kind])]) if Ns else to(weights["w_" + kind])
+            if self.gemm == B.MOE_F8E4M3:
+                n, r, c = both.shape
                 codes = torch.empty((n, r, c), dtype=torch.uint8, device=self.dev)
                 scale = torch.empty((n, r // 128, c // 128), dtype=torch.float32, device=self.dev)
-                if n:
-                    B.moe_quantize_weights(src, codes, scale)
-                self.w[k] = codes
-                self.w[k + "_scale"] = scale
+                B.moe_quantize_weights(both, codes, scale)
                 if keep_bf16:
-                    self.w[k + "_bf16"] = src
-        else:
-            self.w = {k: to(weights[k]) for k in ("w_gate_up", "w_down", "s_gate_up", "s_down")}
+                    self.w["w_" + kind + "_bf16"], self.w["s_" + kind + "_bf16"] = both[:N], both[N:]
+                del both
+                self.w["all_" + kind], self.w["all_" + kind + "_scale"] = codes, scale
+                self.w["w_" + kind + "_scale"], self.w["s_" + kind + "_scale"] = scale[:N], scale[N:]
+                both = codes
+            self.w["all_" + kind] = both
+            self.w["w_" + kind], self.w["s_" + kind] = both[:N], both[N:]
         self.ws = torch.empty(max(B.moe_workspace_bytes(self.shape, self.gemm), 256), dtype=torch.uint8,
                               device=self.dev)
         self._alloc()
@@ -84,12 +94,19 @@ class MoELayer:
         self.topk_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
         self.expert_load = torch.empty((N,), dtype=torch.int32, device=dev)
         self.scores = torch.empty((T, N), dtype=torch.float32, device=dev)
-        self.expert_offsets = torch.empty((N + 1,), dtype=torch.int32, device=dev)
-        self.perm_token = torch.empty((T * K,), dtype=torch.int32, device=dev)
+        Ns = c.n_shared
+        # routed entries first (written by moe_permute), then the shared experts' fixed ones
+        self.offsets_all = torch.empty((N + Ns + 1,), dtype=torch.int32, device=dev)
+        self.offsets_all[N + 1:] = T * K + T * torch.arange(1, Ns + 1, dtype=torch.int32, device=dev)
+        self.expert_offsets = self.offsets_all[:N + 1]
+        self.rows_all = torch.empty((T * K + Ns * T,), dtype=torch.int32, device=dev)
+        self.rows_all[T * K:] = torch.arange(T, dtype=torch.int32, device=dev).repeat(Ns)
+        self.perm_token = self.rows_all[:T * K]
         self.row_of = torch.empty((T * K,), dtype=torch.int32, device=dev)
-        self.shared_offsets = (torch.arange(c.n_shared + 1, dtype=torch.int32, device=dev) * T).contiguous()
-        self.y_routed = torch.empty((T * K, d), dtype=ydt, device=dev)
-        self.y_shared = torch.empty((max(c.n_shared, 1) * T, d), dtype=ydt, device=dev)
+        self.shared_offsets = (torch.arange(Ns + 1, dtype=torch.int32, device=dev) * T).contiguous()
+        self.y_all = torch.empty((T * K + max(Ns, 1) * T, d), dtype=ydt, device=dev)
+        self.y_routed = self.y_all[:T * K]
+        self.y_shared = self.y_all[T * K:]
         self.out = torch.empty((T, d), dtype=self.act_dtype, device=dev)
         if self.gemm == B.MOE_F8E4M3:
             # u quantised once per token (1x128 tiles); the GEMMs gather its rows
@@ -113,6 +130,46 @@ class MoELayer:
         else:
             B.moe_permute(self.shape, self.topk_idx, u, self.expert_offsets, self.perm_token, self.row_of,
                           self.a_perm, None, None, 1, self.ws)
+
+    def _a(self, u):
+        """Token operand of the gathered FFN: u (or its fp8 codes and scales)."""
+        if self.gemm == B.MOE_F8E4M3:
+            return self.u_q, self.u_scale
+        return u, None
+
+    @property
+    def fused(self) -> bool:
+        """Routed and shared experts in one grouped call (needs the gather-in-GEMM path)."""
+        return self.gemm == B.MOE_F8E4M3 or self.gather_in_gemm
+
+    def ffn_all(self, u):
+        """Routed and shared experts in one moe_grouped_ffn call."""
+        c = self.cfg
+        a, a_scale = self._a(u)
+        n_rows = c.T * (c.topk + c.n_shared)
+        B.moe_grouped_ffn(self.shape, self.gemm, c.n_routed + c.n_shared, n_rows, self.offsets_all,
+                          B.MOE_ROWS_GATHER, self.rows_all, a, a_scale, c.T, self.w["all_gate_up"],
+                          self.w.get("all_gate_up_scale"), self.w["all_down"], self.w.get("all_down_scale"),
+                          self.y_all, self.ws)
+
+    def ffn_all_phases(self, u, between=None):
+        """ffn_all as its two calls (moe_ffn_gate_up, moe_ffn_down); ``between`` runs in between."""
+        c = self.cfg
+        n_rows = c.T * (c.topk + c.n_shared)
+        if getattr(self, "h_all", None) is None:
+            hdt = {B.MOE_F32: torch.float32, B.MOE_BF16: torch.bfloat16, B.MOE_F8E4M3: torch.uint8}[self.gemm]
+            self.h_all = torch.empty((n_rows, c.inter), dtype=hdt, device=self.dev)
+            self.h_all_scale = (torch.empty((n_rows, c.inter // 128), dtype=torch.float32, device=self.dev)
+                                if self.gemm == B.MOE_F8E4M3 else None)
+        a, a_scale = self._a(u)
+        E = c.n_routed + c.n_shared
+        B.moe_ffn_gate_up(self.shape, self.gemm, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all,
+                          a, a_scale, c.T, self.w["all_gate_up"], self.w.get("all_gate_up_scale"), self.h_all,
+                          self.h_all_scale)
+        if between is not None:
+            between()
+        B.moe_ffn_down(self.shape, self.gemm, E, n_rows, self.offsets_all, self.h_all, self.h_all_scale,
+                       self.w["all_down"], self.w.get("all_down_scale"), self.y_all)
 
     def ffn_routed(self, u):
         c = self.cfg
@@ -178,8 +235,11 @@ class MoELayer:
         u = u.contiguous()
         self.route(u)
         self.permute(u)
-        self.ffn_routed(u)
-        self.ffn_shared(u)
+        if self.fused:
+            self.ffn_all(u)
+        else:
+            self.ffn_routed(u)
+            self.ffn_shared(u)
         self.combine(u)
         return self.out
 
