@@ -32,9 +32,10 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, floa
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
 }
 
-// One tile with MS live token sub-tiles per wave: main loop and epilogue in
-// one instantiation, so the accumulators never merge across variants.
-template <int MS>
+// One tile with MS live token sub-tiles per wave and LT token load groups per
+// stage: main loop and epilogue in one instantiation, so the accumulators
+// never merge across variants.
+template <int MS, int LT>
 __device__ __forceinline__ void gate_up_tile(const PipeRows<FP>& rows, int d, int I, const Unit& un, uint8_t* lds,
                                              uint16_t* __restrict__ H) {
   f32x16 acc[FP::TW][FP::TT];
@@ -44,7 +45,7 @@ __device__ __forceinline__ void gate_up_tile(const PipeRows<FP>& rows, int d, in
     for (int i = 0; i < FP::TT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-  pipe_mainloop<FP, MS>(rows, d, lds, acc);
+  pipe_mainloop<FP, MS, LT>(rows, d, lds, acc);
   const int ww = threadIdx.x >> 7, h = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
@@ -63,7 +64,7 @@ __device__ __forceinline__ void gate_up_tile(const PipeRows<FP>& rows, int d, in
   }
 }
 
-template <int MS>
+template <int MS, int LT>
 __device__ __forceinline__ void down_tile(const PipeRows<FP>& rows, int d, int I, const Unit& un, uint8_t* lds,
                                           uint16_t* __restrict__ y) {
   f32x16 acc[FP::TW][FP::TT];
@@ -73,7 +74,7 @@ __device__ __forceinline__ void down_tile(const PipeRows<FP>& rows, int d, int I
     for (int i = 0; i < FP::TT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-  pipe_mainloop<FP, MS>(rows, I, lds, acc);
+  pipe_mainloop<FP, MS, LT>(rows, I, lds, acc);
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     const int tr = pipe_token_row(i);
@@ -119,12 +120,13 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_gate_up_bf16_kernel(
       const int hcol = un.nb * kHcols + (rw >> 7) * 64 + (j & 1) * 32 + (rw & 31);
       rows.ow[q] = (static_cast<uint32_t>(j >= 2 ? I + hcol : hcol) * d + pipe_load_chunk(q) * 8) * 2;
     }
-    switch (live_token_subtiles(un.nsub)) {
-      case 4: gate_up_tile<4>(rows, d, I, un, lds_p, H); break;
-      case 3: gate_up_tile<3>(rows, d, I, un, lds_p, H); break;
-      case 2: gate_up_tile<2>(rows, d, I, un, lds_p, H); break;
-      case 1: gate_up_tile<1>(rows, d, I, un, lds_p, H); break;
-      default: gate_up_tile<0>(rows, d, I, un, lds_p, H); break;
+    // LT = ceil(nsub / 2) token load groups; wave row 0 has LT live sub-tiles, row 1 LT or LT - 1
+    const bool full = live_token_subtiles(un.nsub) * 2 >= un.nsub;
+    switch ((un.nsub + 1) / 2) {
+      case 4: full ? gate_up_tile<4, 4>(rows, d, I, un, lds_p, H) : gate_up_tile<3, 4>(rows, d, I, un, lds_p, H); break;
+      case 3: full ? gate_up_tile<3, 3>(rows, d, I, un, lds_p, H) : gate_up_tile<2, 3>(rows, d, I, un, lds_p, H); break;
+      case 2: full ? gate_up_tile<2, 2>(rows, d, I, un, lds_p, H) : gate_up_tile<1, 2>(rows, d, I, un, lds_p, H); break;
+      default: full ? gate_up_tile<1, 1>(rows, d, I, un, lds_p, H) : gate_up_tile<0, 1>(rows, d, I, un, lds_p, H); break;
     }
   }
 }
@@ -152,12 +154,12 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_down_bf16_kernel(int d, int I, 
 #pragma unroll
     for (int q = 0; q < FP::WL; ++q)
       rows.ow[q] = (static_cast<uint32_t>(un.nb * FP::BW + pipe_load_row(q)) * I + pipe_load_chunk(q) * 8) * 2;
-    switch (live_token_subtiles(un.nsub)) {
-      case 4: down_tile<4>(rows, d, I, un, lds_p, y); break;
-      case 3: down_tile<3>(rows, d, I, un, lds_p, y); break;
-      case 2: down_tile<2>(rows, d, I, un, lds_p, y); break;
-      case 1: down_tile<1>(rows, d, I, un, lds_p, y); break;
-      default: down_tile<0>(rows, d, I, un, lds_p, y); break;
+    const bool full = live_token_subtiles(un.nsub) * 2 >= un.nsub;
+    switch ((un.nsub + 1) / 2) {
+      case 4: full ? down_tile<4, 4>(rows, d, I, un, lds_p, y) : down_tile<3, 4>(rows, d, I, un, lds_p, y); break;
+      case 3: full ? down_tile<3, 3>(rows, d, I, un, lds_p, y) : down_tile<2, 3>(rows, d, I, un, lds_p, y); break;
+      case 2: full ? down_tile<2, 2>(rows, d, I, un, lds_p, y) : down_tile<1, 2>(rows, d, I, un, lds_p, y); break;
+      default: full ? down_tile<1, 1>(rows, d, I, un, lds_p, y) : down_tile<0, 1>(rows, d, I, un, lds_p, y); break;
     }
   }
 }

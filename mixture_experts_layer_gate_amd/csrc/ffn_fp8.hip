@@ -53,13 +53,13 @@ __device__ __forceinline__ int p8_token_row(int i) {
   return 32 * (2 * i + p8_wt()) + (l & 31);
 }
 
-template <int MS>
+template <int MS, int LT>
 __device__ __forceinline__ void gate_up8_tile(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
                                               const Unit& un, uint8_t* lds, uint8_t* __restrict__ Hq,
                                               float* __restrict__ Hs) {
   f32x16 acc[P8::TW][P8::TT];
   zero_acc8<MS>(acc);
-  pipe8_mainloop<MS, true>(rows, srs, d, lds, acc);
+  pipe8_mainloop<MS, LT, true>(rows, srs, d, lds, acc);
   // SwiGLU in fp32; this wave holds 64 of the tile's 128 H columns of each row
   // (gate sub-tiles 0, 1 with the up sub-tiles 2, 3)
   const int l = threadIdx.x & 63, ww = p8_ww();
@@ -101,12 +101,12 @@ __device__ __forceinline__ void gate_up8_tile(const Pipe8Rows& rows, __amdgpu_bu
   __syncthreads();   // amax_x and the LDS tables are rewritten by the next tile
 }
 
-template <int MS>
+template <int MS, int LT>
 __device__ __forceinline__ void down8_tile(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
                                            const Unit& un, uint8_t* lds, uint16_t* __restrict__ y) {
   f32x16 acc[P8::TW][P8::TT];
   zero_acc8<MS>(acc);
-  pipe8_mainloop<MS, false>(rows, srs, I, lds, acc);
+  pipe8_mainloop<MS, LT, false>(rows, srs, I, lds, acc);
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     const int tr = p8_token_row(i);
@@ -169,10 +169,14 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
       const int hcol = un.nb * 128 + (rw >> 7) * 64 + (j & 1) * 32 + (rw & 31);   // sub-tiles 0,1 gate rows,
       rows.ow[q] = static_cast<uint32_t>(j >= 2 ? I + hcol : hcol) * d + pipe8_load_chunk(q) * 16;  // 2,3 up rows
     }
-    switch (live_token_subtiles8(un.nsub)) {
-      case 2: gate_up8_tile<2>(rows, srs, d, I, un, lds8, Hq, Hs); break;
-      case 1: gate_up8_tile<1>(rows, srs, d, I, un, lds8, Hq, Hs); break;
-      default: gate_up8_tile<0>(rows, srs, d, I, un, lds8, Hq, Hs); break;
+    // LT = ceil(nsub / 2) token load groups; wave row 0 has LT live sub-tiles, row 1 LT or LT - 1
+    const bool full = live_token_subtiles8(un.nsub) * 2 >= un.nsub;
+    if (un.nsub > 2) {
+      if (full) gate_up8_tile<2, 2>(rows, srs, d, I, un, lds8, Hq, Hs);
+      else gate_up8_tile<1, 2>(rows, srs, d, I, un, lds8, Hq, Hs);
+    } else {
+      if (full) gate_up8_tile<1, 1>(rows, srs, d, I, un, lds8, Hq, Hs);
+      else gate_up8_tile<0, 1>(rows, srs, d, I, un, lds8, Hq, Hs);
     }
   }
 }
@@ -213,10 +217,13 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
 #pragma unroll
     for (int q = 0; q < P8::WL; ++q)
       rows.ow[q] = static_cast<uint32_t>(un.nb * P8::BW + pipe8_load_row(q)) * I + pipe8_load_chunk(q) * 16;
-    switch (live_token_subtiles8(un.nsub)) {
-      case 2: down8_tile<2>(rows, srs, d, I, un, lds8, y); break;
-      case 1: down8_tile<1>(rows, srs, d, I, un, lds8, y); break;
-      default: down8_tile<0>(rows, srs, d, I, un, lds8, y); break;
+    const bool full = live_token_subtiles8(un.nsub) * 2 >= un.nsub;
+    if (un.nsub > 2) {
+      if (full) down8_tile<2, 2>(rows, srs, d, I, un, lds8, y);
+      else down8_tile<1, 2>(rows, srs, d, I, un, lds8, y);
+    } else {
+      if (full) down8_tile<1, 1>(rows, srs, d, I, un, lds8, y);
+      else down8_tile<0, 1>(rows, srs, d, I, un, lds8, y);
     }
   }
 }

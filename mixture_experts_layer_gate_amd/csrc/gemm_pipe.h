@@ -92,10 +92,12 @@ __device__ __forceinline__ void pipe_issue_one(const PipeRows<P>& r, uint8_t* st
 #endif
 }
 
-template <class P, bool A>
+// LT: token load groups issued per stage (group q covers tile rows 64q .. 64q+63);
+// blocks with fewer live rows skip the groups past them.
+template <class P, bool A, int LT>
 __device__ __forceinline__ void pipe_issue_part(const PipeRows<P>& r, uint8_t* lds, int stage, int k0) {
 #pragma unroll
-  for (int q = 0; q < (A ? P::WL : P::TL); ++q) pipe_issue_one<P, A>(r, lds + stage * P::STAGE, k0 * 2, q);
+  for (int q = 0; q < (A ? P::WL : LT); ++q) pipe_issue_one<P, A>(r, lds + stage * P::STAGE, k0 * 2, q);
 }
 
 template <class P, int MS>
@@ -133,11 +135,11 @@ __device__ __forceinline__ void sched_fence() {
 // among them (load q before MFMA q * M / L), so the vector-memory pipe is fed
 // steadily: issued as one burst, the loads back up and the wave, which issues
 // in order, stalls with its MFMAs behind them.
-template <class P, int MS, int PART>  // PART: 0 none, 1 part A, 2 part B
+template <class P, int MS, int LT, int PART>  // PART: 0 none, 1 part A, 2 part B
 __device__ __forceinline__ void pipe_mma_loads(const PipeFrags<P, MS>& f, f32x16 (&acc)[P::TW][P::TT],
                                                const PipeRows<P>& r, uint8_t* st, int kb) {
   constexpr int M = P::TW * MS;
-  constexpr int L = PART == 0 ? 0 : (PART == 1 ? P::WL : P::TL);
+  constexpr int L = PART == 0 ? 0 : (PART == 1 ? P::WL : LT);
 #pragma unroll
   for (int m = 0; m < (M > L ? M : L); ++m) {
 #pragma unroll
@@ -165,27 +167,30 @@ __device__ __forceinline__ void wait_vm_only_barrier() {
 // complete. The barrier needs no LDS read to be complete.
 //   ISSUE_B: issue part B of stage kt + 2; WAIT: vmcnt at the barrier, or -1
 //   for no barrier (last stage); ISSUE_A: issue part A of stage kt + 3.
-template <class P, int MS, bool ISSUE_B, int WAIT, bool ISSUE_A>
+template <class P, int MS, int LT, bool ISSUE_B, int WAIT, bool ISSUE_A>
 __device__ __forceinline__ void pipe_iteration(const PipeRows<P>& rows, uint8_t* lds, int kt, int w_off, int t_off,
                                                PipeFrags<P, MS>& f0, PipeFrags<P, MS>& f1,
                                                f32x16 (&acc)[P::TW][P::TT]) {
   pipe_read<P, MS>(f1, lds + (kt & 3) * P::STAGE, w_off, t_off, 32);
   sched_fence();
-  pipe_mma_loads<P, MS, ISSUE_B ? 2 : 0>(f0, acc, rows, lds + ((kt + 2) & 3) * P::STAGE, (kt + 2) * P::BK * 2);
+  pipe_mma_loads<P, MS, LT, ISSUE_B ? 2 : 0>(f0, acc, rows, lds + ((kt + 2) & 3) * P::STAGE, (kt + 2) * P::BK * 2);
   if (WAIT >= 0) {
     wait_vm_only_barrier<(WAIT >= 0 ? WAIT : 0)>();
     pipe_read<P, MS>(f0, lds + ((kt + 1) & 3) * P::STAGE, w_off, t_off, 0);
     sched_fence();
   }
-  pipe_mma_loads<P, MS, ISSUE_A ? 1 : 0>(f1, acc, rows, lds + ((kt + 3) & 3) * P::STAGE, (kt + 3) * P::BK * 2);
+  pipe_mma_loads<P, MS, LT, ISSUE_A ? 1 : 0>(f1, acc, rows, lds + ((kt + 3) & 3) * P::STAGE, (kt + 3) * P::BK * 2);
 }
 
 // acc[j][i]: weight sub-tile j x token sub-tile i of this wave. K % 128 == 0,
-// so there are at least four stages.
-template <class P, int MS>
+// so there are at least four stages. LT (>= MS of every wave) token load
+// groups per stage.
+template <class P, int MS, int LT>
 __device__ __forceinline__ void pipe_mainloop(const PipeRows<P>& rows, int K, uint8_t* lds,
                                               f32x16 (&acc)[P::TW][P::TT]) {
   static_assert(P::NS == 4, "schedule written for a ring of four stages");
+  static_assert(LT >= 1 && LT <= P::TL && 2 * LT >= 2 * MS, "token load groups must cover the live sub-tiles");
+  constexpr int LPS = P::WL + LT;                           // loads per stage per thread
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wt = w & 1, ww = w >> 1;
   const int nk = K / P::BK;
@@ -194,12 +199,12 @@ __device__ __forceinline__ void pipe_mainloop(const PipeRows<P>& rows, int K, ui
   const int w_off = (ww * (P::BW / 2) + (l & 31)) * P::ROWB + cofs;
   const int t_off = P::W_BYTES + (wt * 32 + (l & 31)) * P::ROWB + cofs;
 
-  pipe_issue_part<P, true>(rows, lds, 0, 0);
-  pipe_issue_part<P, false>(rows, lds, 0, 0);
-  pipe_issue_part<P, true>(rows, lds, 1, P::BK);
-  pipe_issue_part<P, false>(rows, lds, 1, P::BK);
-  pipe_issue_part<P, true>(rows, lds, 2, 2 * P::BK);
-  wait_vm_only_barrier<P::LPS + P::WL>();                   // stage 0 complete
+  pipe_issue_part<P, true, LT>(rows, lds, 0, 0);
+  pipe_issue_part<P, false, LT>(rows, lds, 0, 0);
+  pipe_issue_part<P, true, LT>(rows, lds, 1, P::BK);
+  pipe_issue_part<P, false, LT>(rows, lds, 1, P::BK);
+  pipe_issue_part<P, true, LT>(rows, lds, 2, 2 * P::BK);
+  wait_vm_only_barrier<LPS + P::WL>();                      // stage 0 complete
 #if defined(__HIP_DEVICE_COMPILE__)
   // Retire any scalar load still in flight (lgkmcnt(0), other counters left
   // free) in a form the compiler sees: with none pending, the LDS counter
@@ -210,10 +215,10 @@ __device__ __forceinline__ void pipe_mainloop(const PipeRows<P>& rows, int K, ui
   PipeFrags<P, MS> f0, f1;
   pipe_read<P, MS>(f0, lds, w_off, t_off, 0);
   int kt = 0;
-  for (; kt + 3 < nk; ++kt) pipe_iteration<P, MS, true, P::LPS, true>(rows, lds, kt, w_off, t_off, f0, f1, acc);
-  pipe_iteration<P, MS, true, P::LPS, false>(rows, lds, kt, w_off, t_off, f0, f1, acc);     // kt = nk - 3
-  pipe_iteration<P, MS, false, 0, false>(rows, lds, kt + 1, w_off, t_off, f0, f1, acc);     // kt = nk - 2
-  pipe_iteration<P, MS, false, -1, false>(rows, lds, kt + 2, w_off, t_off, f0, f1, acc);    // kt = nk - 1
+  for (; kt + 3 < nk; ++kt) pipe_iteration<P, MS, LT, true, LPS, true>(rows, lds, kt, w_off, t_off, f0, f1, acc);
+  pipe_iteration<P, MS, LT, true, LPS, false>(rows, lds, kt, w_off, t_off, f0, f1, acc);     // kt = nk - 3
+  pipe_iteration<P, MS, LT, false, 0, false>(rows, lds, kt + 1, w_off, t_off, f0, f1, acc);  // kt = nk - 2
+  pipe_iteration<P, MS, LT, false, -1, false>(rows, lds, kt + 2, w_off, t_off, f0, f1, acc); // kt = nk - 1
   // every wave has read the ring before the next tile's loads overwrite it
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

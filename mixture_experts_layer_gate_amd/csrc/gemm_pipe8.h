@@ -43,7 +43,7 @@ struct Pipe8 {
   static constexpr int W_BYTES = BW * ROWB, T_BYTES = BT * ROWB;
   static constexpr int STAGE = W_BYTES + T_BYTES;
   static constexpr int WL = W_BYTES / 16 / NT, TL = T_BYTES / 16 / NT;
-  static constexpr int LPS = WL + TL;                      // loads per thread per stage
+  static constexpr int LPS = WL + TL;                      // loads per thread per stage (all token groups)
   static constexpr int RING = NS * STAGE;
   static constexpr int MAX_CHUNKS = 80;                    // K <= 10240
   static constexpr int SW_OFF = RING;                      // weight scales [2][MAX_CHUNKS]
@@ -180,13 +180,13 @@ __device__ __forceinline__ void pipe8_hold(const Pipe8Frags<MS>& f) {
 // ISSUE, and, for a chunk's first stage (PROMOTE), the previous chunk's
 // T[j][i] promoted just before the C = 0 MFMA that restarts it (FIRST: T
 // restarts from 0).
-template <int MS, bool FIRST, bool PROMOTE, bool ISSUE>
+template <int MS, int LT, bool FIRST, bool PROMOTE, bool ISSUE>
 __device__ __forceinline__ void pipe8_block(const Pipe8Frags<MS>& f, f32x16 (&T)[Pipe8::TW][Pipe8::TT],
                                             f32x16 (&acc)[Pipe8::TW][Pipe8::TT], const float (&fac)[Pipe8::TW][Pipe8::TT],
                                             const Pipe8Rows& rows, uint8_t* lds, int ls) {
   using P = Pipe8;
   constexpr int M = P::TW * MS;
-  constexpr int L = ISSUE ? P::LPS : 0;
+  constexpr int L = ISSUE ? P::WL + LT : 0;      // weight loads, then LT token load groups
   uint8_t* st = lds + (ls & 3) * P::STAGE;
 #pragma unroll
   for (int m = 0; m < (M > L ? M : L); ++m) {
@@ -230,10 +230,10 @@ __device__ __forceinline__ void pipe8_factors(float (&fac)[Pipe8::TW][Pipe8::TT]
 }
 
 // One stage kt < nk - 1: fa holds its fragments, fb receives stage kt+1's.
-// WAIT: loads allowed in flight at the barrier (LPS while stage kt+2 exists,
-// else 0); ISSUE: load stage kt+3. A chunk's first stage promotes the previous
-// chunk with fac (when kt > 0); its second stage computes fac for its chunk.
-template <int MS, bool GATE_UP, bool FIRST, int WAIT, bool ISSUE>
+// WAIT: loads allowed in flight at the barrier (one stage's while stage kt+2
+// exists, else 0); ISSUE: load stage kt+3. A chunk's first stage promotes the
+// previous chunk with fac (when kt > 0); its second stage computes fac for its chunk.
+template <int MS, int LT, bool GATE_UP, bool FIRST, int WAIT, bool ISSUE>
 __device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds, int kc_pad, int kt,
                                             const Pipe8Frags<MS>& fa, Pipe8Frags<MS>& fb,
                                             f32x16 (&T)[Pipe8::TW][Pipe8::TT], f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
@@ -243,10 +243,10 @@ __device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds,
   pipe8_read<MS>(fb, lds + ((kt + 1) & 3) * P::STAGE);
   sched_fence();
   if (FIRST) {
-    if (kt > 0) pipe8_block<MS, true, true, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
-    else pipe8_block<MS, true, false, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
+    if (kt > 0) pipe8_block<MS, LT, true, true, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
+    else pipe8_block<MS, LT, true, false, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
   } else {
-    pipe8_block<MS, false, false, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
+    pipe8_block<MS, LT, false, false, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
     pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, kt >> 1);
   }
 }
@@ -254,19 +254,22 @@ __device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds,
 // acc[j][i] = sum over chunks of promoted T; K % 128 == 0 (nk = K / 64 even),
 // K / 128 <= MAX_CHUNKS. Before the call the tile's source rows and weight
 // scales are in LDS (and visible to every wave); the token-scale table is
-// loaded here from srs (kc = K / 128 scales per source row).
-template <int MS, bool GATE_UP>
+// loaded here from srs (kc = K / 128 scales per source row). LT (>= MS of
+// every wave) token load groups of 64 rows per stage.
+template <int MS, int LT, bool GATE_UP>
 __device__ __forceinline__ void pipe8_mainloop(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int K, uint8_t* lds,
                                                f32x16 (&acc)[Pipe8::TW][Pipe8::TT]) {
   using P = Pipe8;
+  static_assert(LT >= 1 && LT <= P::TL && LT >= MS, "token load groups must cover the live sub-tiles");
+  constexpr int LPS = P::WL + LT;                      // loads per stage per thread
   const int nk = K / P::BK, kc = K / 128, kc_pad = (kc + 3) & ~3;
   pipe8_issue_scale_table(srs, lds, kc, kc_pad);
   for (int s = 0; s < 3 && s < nk; ++s) {
 #pragma unroll
-    for (int q = 0; q < P::LPS; ++q) pipe8_issue_one(rows, lds + s * P::STAGE, s, q);
+    for (int q = 0; q < LPS; ++q) pipe8_issue_one(rows, lds + s * P::STAGE, s, q);
   }
-  if (nk >= 3) wait_vm_only_barrier<2 * P::LPS>();    // scale table and stage 0 have landed
-  else wait_vm_only_barrier<P::LPS>();                 // nk == 2
+  if (nk >= 3) wait_vm_only_barrier<2 * LPS>();        // scale table and stage 0 have landed
+  else wait_vm_only_barrier<LPS>();                    // nk == 2
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_s_waitcnt(0xc07f);                  // no scalar load pending: LDS waits stay partial
 #endif
@@ -276,17 +279,17 @@ __device__ __forceinline__ void pipe8_mainloop(const Pipe8Rows& rows, __amdgpu_b
   pipe8_read<MS>(f0, lds);
   int kt = 0;
   for (; kt + 4 < nk; kt += 2) {                       // both stages refill the ring
-    pipe8_stage<MS, GATE_UP, true, P::LPS, true>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
-    pipe8_stage<MS, GATE_UP, false, P::LPS, true>(rows, lds, kc_pad, kt + 1, f1, f0, T, acc, fac);
+    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
+    pipe8_stage<MS, LT, GATE_UP, false, LPS, true>(rows, lds, kc_pad, kt + 1, f1, f0, T, acc, fac);
   }
   if (kt + 4 == nk) {                                  // stage nk-1 is the last to load
-    pipe8_stage<MS, GATE_UP, true, P::LPS, true>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
-    pipe8_stage<MS, GATE_UP, false, P::LPS, false>(rows, lds, kc_pad, kt + 1, f1, f0, T, acc, fac);
+    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
+    pipe8_stage<MS, LT, GATE_UP, false, LPS, false>(rows, lds, kc_pad, kt + 1, f1, f0, T, acc, fac);
     kt += 2;
   }
   // last chunk: stage nk-2 reads nk-1; stage nk-1 reads nothing
-  pipe8_stage<MS, GATE_UP, true, 0, false>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
-  pipe8_block<MS, false, false, false>(f1, T, acc, fac, rows, lds, 0);
+  pipe8_stage<MS, LT, GATE_UP, true, 0, false>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
+  pipe8_block<MS, LT, false, false, false>(f1, T, acc, fac, rows, lds, 0);
   pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, (nk >> 1) - 1);
   // the reads below follow the last MFMAs closely: give them the wait states
   // an MFMA result needs before a v_accvgpr_read (the asm read is opaque to
