@@ -6,7 +6,8 @@
 // per 128x128 block; every 128-wide K chunk is promoted into fp32 with the
 // product of the two scales (gemm_pipe8.h). Two persistent launches over all
 // experts, one 256-thread workgroup per CU, 256 weight rows x 128 token rows
-// per tile, balanced blocks of at most four 32-row sub-tiles:
+// per tile, balanced blocks of at most four 32-row sub-tiles; a unit streams
+// up to four consecutive output-column tiles of one token block:
 //  1. gate/up: H[r, c] = SiLU(g) * u for 128 H columns per tile (each wave 64
 //     gate rows + the matching 64 up rows, so the product forms in registers);
 //     H is then re-quantised per 1x128 tile along I -- the tile owns exactly
@@ -30,16 +31,6 @@ __device__ __forceinline__ int live_token_subtiles8(int nsub) {
   return clampi((nsub - p8_wt() + 1) / 2, 0, P8::TT);
 }
 
-template <int MS>
-__device__ __forceinline__ void zero_acc8(f32x16 (&acc)[P8::TW][P8::TT]) {
-#pragma unroll
-  for (int j = 0; j < P8::TW; ++j)
-#pragma unroll
-    for (int i = 0; i < MS; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-}
-
 // Output column (weight row within the tile) of accumulator element 4q of
 // weight sub-tile j: four consecutive columns per lane.
 __device__ __forceinline__ int p8_wcol(int j, int q) {
@@ -53,75 +44,100 @@ __device__ __forceinline__ int p8_token_row(int i) {
   return 32 * (2 * i + p8_wt()) + (l & 31);
 }
 
-template <int MS, int LT>
-__device__ __forceinline__ void gate_up8_tile(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
-                                              const Unit& un, uint8_t* lds, uint8_t* __restrict__ Hq,
-                                              float* __restrict__ Hs) {
-  f32x16 acc[P8::TW][P8::TT];
-  zero_acc8<MS>(acc);
-  pipe8_mainloop<MS, LT, true>(rows, srs, d, lds, acc);
-  // SwiGLU in fp32; this wave holds 64 of the tile's 128 H columns of each row
-  // (gate sub-tiles 0, 1 with the up sub-tiles 2, 3)
-  const int l = threadIdx.x & 63, ww = p8_ww();
-  float* amax_x = reinterpret_cast<float*>(lds);   // [2][BT], the ring is free after the main loop
-  float hv[P8::TT][2][16];
+// Barrier for LDS data only: the ring's loads stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// gate/up epilogue of output-column tile nb0 + seg: SwiGLU in fp32 (this wave
+// holds 64 of the tile's 128 H columns of each row: gate sub-tiles 0, 1 with
+// up sub-tiles 2, 3), then the 1x128 re-quantisation of H over the tile's
+// 128 columns (row amax exchanged through LDS).
+template <int MS>
+struct GateUpEpi8 {
+  const Unit& un;
+  int I, nb0;
+  uint8_t* lds;
+  uint8_t* __restrict__ Hq;
+  float* __restrict__ Hs;
+  __device__ __forceinline__ void operator()(int seg, f32x16 (&acc)[P8::TW][P8::TT]) {
+    const int l = threadIdx.x & 63, ww = p8_ww(), nb = nb0 + seg;
+    float* amax_x = reinterpret_cast<float*>(lds + P8::AMAX_OFF);   // [2][BT]
+    float hv[P8::TT][2][16];
 #pragma unroll
-  for (int i = 0; i < MS; ++i) {
-    float x = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        hv[i][j][v] = silu(acc[j][i][v]) * acc[j + 2][i][v];
-        x = fmaxf(x, __builtin_fabsf(hv[i][j][v]));
-      }
-    x = fmaxf(x, __shfl_xor(x, 32, kWave));
-    if (l < 32) amax_x[ww * P8::BT + p8_token_row(i)] = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < MS; ++i) {
-    const int tr = p8_token_row(i);
-    const float amax = fmaxf(amax_x[tr], amax_x[P8::BT + tr]);
-    if (tr < un.rows) {
-      const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
-      uint8_t* hrow = Hq + static_cast<size_t>(un.m0 + tr) * I + un.nb * 128 + ww * 64 + 4 * (l >> 5);
+    for (int i = 0; i < MS; ++i) {
+      float x = 0.0f;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t packed = 0;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) packed |= f32_to_e4m3(hv[i][j][4 * q + r] * inv) << (8 * r);
-          *reinterpret_cast<uint32_t*>(hrow + j * 32 + 8 * q) = packed;
+        for (int v = 0; v < 16; ++v) {
+          hv[i][j][v] = silu(acc[j][i][v]) * acc[j + 2][i][v];
+          x = fmaxf(x, __builtin_fabsf(hv[i][j][v]));
         }
-      if (ww == 0 && l < 32) Hs[static_cast<size_t>(un.m0 + tr) * (I / 128) + un.nb] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+      x = fmaxf(x, __shfl_xor(x, 32, kWave));
+      if (l < 32) amax_x[ww * P8::BT + p8_token_row(i)] = x;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const int tr = p8_token_row(i);
+      const float amax = fmaxf(amax_x[tr], amax_x[P8::BT + tr]);
+      if (tr < un.rows) {
+        const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
+        uint8_t* hrow = Hq + static_cast<size_t>(un.m0 + tr) * I + nb * 128 + ww * 64 + 4 * (l >> 5);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) packed |= f32_to_e4m3(hv[i][j][4 * q + r] * inv) << (8 * r);
+            *reinterpret_cast<uint32_t*>(hrow + j * 32 + 8 * q) = packed;
+          }
+        if (ww == 0 && l < 32) Hs[static_cast<size_t>(un.m0 + tr) * (I / 128) + nb] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+      }
+    }
+    // amax_x is next written in the following tile's epilogue, after at least
+    // one ring barrier that every wave reaches with these reads consumed
+  }
+};
+
+// down epilogue of output-column tile nb0 + seg: bf16 rows of y.
+template <int MS>
+struct DownEpi8 {
+  const Unit& un;
+  int d, nb0;
+  uint16_t* __restrict__ y;
+  __device__ __forceinline__ void operator()(int seg, f32x16 (&acc)[P8::TW][P8::TT]) {
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const int tr = p8_token_row(i);
+      if (tr < un.rows) {
+        uint16_t* yrow = y + static_cast<size_t>(un.m0 + tr) * d + (nb0 + seg) * P8::BW;
+#pragma unroll
+        for (int j = 0; j < P8::TW; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<u32x2*>(yrow + p8_wcol(j, q)) =
+                u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
+                      pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])};
+      }
     }
   }
-  __syncthreads();   // amax_x and the LDS tables are rewritten by the next tile
+};
+
+template <int MS, int LT>
+__device__ __forceinline__ void gate_up8_unit(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
+                                              const Unit& un, int nb0, int nseg, uint8_t* lds,
+                                              uint8_t* __restrict__ Hq, float* __restrict__ Hs) {
+  GateUpEpi8<MS> epi{un, I, nb0, lds, Hq, Hs};
+  pipe8_stream<MS, LT, true>(rows, srs, d, nseg, 128 * d, lds, epi);   // the next tile's rows: 128 further
 }
 
 template <int MS, int LT>
-__device__ __forceinline__ void down8_tile(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
-                                           const Unit& un, uint8_t* lds, uint16_t* __restrict__ y) {
-  f32x16 acc[P8::TW][P8::TT];
-  zero_acc8<MS>(acc);
-  pipe8_mainloop<MS, LT, false>(rows, srs, I, lds, acc);
-#pragma unroll
-  for (int i = 0; i < MS; ++i) {
-    const int tr = p8_token_row(i);
-    if (tr < un.rows) {
-      uint16_t* yrow = y + static_cast<size_t>(un.m0 + tr) * d + un.nb * P8::BW;
-#pragma unroll
-      for (int j = 0; j < P8::TW; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<u32x2*>(yrow + p8_wcol(j, q)) =
-              u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
-                    pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])};
-    }
-  }
-  __syncthreads();   // the LDS tables are rewritten by the next tile
+__device__ __forceinline__ void down8_unit(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
+                                           const Unit& un, int nb0, int nseg, uint8_t* lds,
+                                           uint16_t* __restrict__ y) {
+  DownEpi8<MS> epi{un, d, nb0, y};
+  pipe8_stream<MS, LT, false>(rows, srs, I, nseg, P8::BW * I, lds, epi);
 }
 
 __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
@@ -134,20 +150,21 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
   int* srcrow = reinterpret_cast<int*>(lds8 + P8::SRC_OFF);
   int* cum = reinterpret_cast<int*>(lds8 + P8::LDS_BYTES);
   __shared__ int wtmp[16];
-  const int kc = d / 128;
-  const int total = build_units_balanced(off, E, n_rows, kMaxSub8, I / 128, cum, wtmp);
+  const int kc = d / 128, NB = I / 128;
+  const int total = build_units_balanced(off, E, n_rows, kMaxSub8, cdiv(NB, P8::MAX_SEG), cum, wtmp);
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t trs = pipe_rsrc(a, static_cast<uint64_t>(a_rows) * d);
   const __amdgpu_buffer_rsrc_t srs = pipe_rsrc(a_scale, static_cast<uint64_t>(a_rows) * kc * 4);
   for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
     const Unit un = find_unit_balanced(t, off, E, n_rows, kMaxSub8, cum);
-    // LDS tables of the tile: weight scales (gate block row nb, up block row
-    // I/128 + nb) and the source row of each tile row (rows past the block
-    // read any valid row and are never stored)
+    const int nb0 = un.nb * P8::MAX_SEG, nseg = min(P8::MAX_SEG, NB - nb0);
+    // LDS tables of the unit: weight scales of each tile (gate block row nb,
+    // up block row I/128 + nb) and the source row of each tile row (rows past
+    // the block read any valid row and are never stored)
     const float* sexp = wgu_scale + static_cast<size_t>(un.e) * (2 * I / 128) * kc;
-    for (int x = tid; x < 2 * kc; x += P8::NT) {
-      const int b = x / kc, c = x - b * kc;
-      swt[b * P8::MAX_CHUNKS + c] = sexp[static_cast<size_t>(b ? I / 128 + un.nb : un.nb) * kc + c];
+    for (int x = tid; x < nseg * 2 * kc; x += P8::NT) {
+      const int sb = x / kc, c = x - sb * kc, seg = sb >> 1, b = sb & 1;
+      swt[(seg * 2 + b) * P8::MAX_CHUNKS + c] = sexp[static_cast<size_t>(b ? I / 128 + nb0 + seg : nb0 + seg) * kc + c];
     }
     if (tid < P8::BT) {
       int s_first = source_row(mode, row_src, un.m0, un.seg0, a_rows);
@@ -166,17 +183,17 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
     for (int q = 0; q < P8::WL; ++q) {
       const int rw = pipe8_load_row(q);
       const int j = (rw >> 5) & 3;                    // wave half rw / 128 owns 64 H columns: its
-      const int hcol = un.nb * 128 + (rw >> 7) * 64 + (j & 1) * 32 + (rw & 31);   // sub-tiles 0,1 gate rows,
+      const int hcol = nb0 * 128 + (rw >> 7) * 64 + (j & 1) * 32 + (rw & 31);   // sub-tiles 0,1 gate rows,
       rows.ow[q] = static_cast<uint32_t>(j >= 2 ? I + hcol : hcol) * d + pipe8_load_chunk(q) * 16;  // 2,3 up rows
     }
     // LT = ceil(nsub / 2) token load groups; wave row 0 has LT live sub-tiles, row 1 LT or LT - 1
     const bool full = live_token_subtiles8(un.nsub) * 2 >= un.nsub;
     if (un.nsub > 2) {
-      if (full) gate_up8_tile<2, 2>(rows, srs, d, I, un, lds8, Hq, Hs);
-      else gate_up8_tile<1, 2>(rows, srs, d, I, un, lds8, Hq, Hs);
+      if (full) gate_up8_unit<2, 2>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs);
+      else gate_up8_unit<1, 2>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs);
     } else {
-      if (full) gate_up8_tile<1, 1>(rows, srs, d, I, un, lds8, Hq, Hs);
-      else gate_up8_tile<0, 1>(rows, srs, d, I, un, lds8, Hq, Hs);
+      if (full) gate_up8_unit<1, 1>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs);
+      else gate_up8_unit<0, 1>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs);
     }
   }
 }
@@ -193,18 +210,19 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
   int* srcrow = reinterpret_cast<int*>(lds8 + P8::SRC_OFF);
   int* cum = reinterpret_cast<int*>(lds8 + P8::LDS_BYTES);
   __shared__ int wtmp[16];
-  const int kc = I / 128;
-  const int total = build_units_balanced(off, E, n_rows, kMaxSub8, d / P8::BW, cum, wtmp);
+  const int kc = I / 128, NB = d / P8::BW;
+  const int total = build_units_balanced(off, E, n_rows, kMaxSub8, cdiv(NB, P8::MAX_SEG), cum, wtmp);
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t trs = pipe_rsrc(Hq, static_cast<uint64_t>(n_rows) * I);
   const __amdgpu_buffer_rsrc_t srs = pipe_rsrc(Hs, static_cast<uint64_t>(n_rows) * kc * 4);
   for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
     const Unit un = find_unit_balanced(t, off, E, n_rows, kMaxSub8, cum);
-    // weight scales: wave half ww covers output columns nb*256 + 128ww .. +127 = block row 2nb + ww
+    const int nb0 = un.nb * P8::MAX_SEG, nseg = min(P8::MAX_SEG, NB - nb0);
+    // weight scales: wave half ww of tile nb covers output columns nb*256 + 128ww .. +127 = block row 2nb + ww
     const float* sexp = wd_scale + static_cast<size_t>(un.e) * (d / 128) * kc;
-    for (int x = tid; x < 2 * kc; x += P8::NT) {
-      const int b = x / kc, c = x - b * kc;
-      swt[b * P8::MAX_CHUNKS + c] = sexp[static_cast<size_t>(2 * un.nb + b) * kc + c];
+    for (int x = tid; x < nseg * 2 * kc; x += P8::NT) {
+      const int sb = x / kc, c = x - sb * kc;
+      swt[sb * P8::MAX_CHUNKS + c] = sexp[static_cast<size_t>(2 * nb0 + sb) * kc + c];
     }
     if (tid < P8::BT) srcrow[tid] = un.m0 + (tid < un.rows ? tid : 0);
     __syncthreads();
@@ -216,14 +234,14 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
     rows.wrs = pipe_rsrc(wd + static_cast<size_t>(un.e) * d * I, static_cast<uint64_t>(d) * I);
 #pragma unroll
     for (int q = 0; q < P8::WL; ++q)
-      rows.ow[q] = static_cast<uint32_t>(un.nb * P8::BW + pipe8_load_row(q)) * I + pipe8_load_chunk(q) * 16;
+      rows.ow[q] = static_cast<uint32_t>(nb0 * P8::BW + pipe8_load_row(q)) * I + pipe8_load_chunk(q) * 16;
     const bool full = live_token_subtiles8(un.nsub) * 2 >= un.nsub;
     if (un.nsub > 2) {
-      if (full) down8_tile<2, 2>(rows, srs, d, I, un, lds8, y);
-      else down8_tile<1, 2>(rows, srs, d, I, un, lds8, y);
+      if (full) down8_unit<2, 2>(rows, srs, d, I, un, nb0, nseg, lds8, y);
+      else down8_unit<1, 2>(rows, srs, d, I, un, nb0, nseg, lds8, y);
     } else {
-      if (full) down8_tile<1, 1>(rows, srs, d, I, un, lds8, y);
-      else down8_tile<0, 1>(rows, srs, d, I, un, lds8, y);
+      if (full) down8_unit<1, 1>(rows, srs, d, I, un, nb0, nseg, lds8, y);
+      else down8_unit<0, 1>(rows, srs, d, I, un, nb0, nseg, lds8, y);
     }
   }
 }
@@ -255,7 +273,8 @@ hipError_t launch_ffn_fp8_gate_up(const FfnArgs& p, hipStream_t st) {
   f8_set_lds_limits();
   const size_t lds = P8::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / P8::BT + p.n_experts;
-  hipLaunchKernelGGL(ffn_gate_up_fp8_kernel, dim3(f8_grid(mblocks * (p.I / 128))), dim3(P8::NT), lds, st, p.d, p.I,
+  hipLaunchKernelGGL(ffn_gate_up_fp8_kernel, dim3(f8_grid(mblocks * cdiv(p.I / 128, P8::MAX_SEG))), dim3(P8::NT), lds,
+                     st, p.d, p.I,
                      p.n_experts, p.n_rows, p.a_rows, p.offsets, p.mode, p.row_src,
                      static_cast<const uint8_t*>(p.a), p.a_scale, static_cast<const uint8_t*>(p.w_gu), p.w_gu_scale,
                      static_cast<uint8_t*>(p.h), p.h_scale);
@@ -267,7 +286,8 @@ hipError_t launch_ffn_fp8_down(const FfnArgs& p, hipStream_t st) {
   f8_set_lds_limits();
   const size_t lds = P8::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / P8::BT + p.n_experts;
-  hipLaunchKernelGGL(ffn_down_fp8_kernel, dim3(f8_grid(mblocks * (p.d / P8::BW))), dim3(P8::NT), lds, st, p.d, p.I,
+  hipLaunchKernelGGL(ffn_down_fp8_kernel, dim3(f8_grid(mblocks * cdiv(p.d / P8::BW, P8::MAX_SEG))), dim3(P8::NT), lds,
+                     st, p.d, p.I,
                      p.n_experts, p.n_rows, p.offsets, static_cast<const uint8_t*>(p.h), p.h_scale,
                      static_cast<const uint8_t*>(p.w_d), p.w_d_scale, static_cast<uint16_t*>(p.y));
   return hipGetLastError();

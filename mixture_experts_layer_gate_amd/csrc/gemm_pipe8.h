@@ -28,7 +28,9 @@
 // of stage kt+3 spread among them. In a chunk's first stage each element of
 // T is promoted (chunk c-1, whose MFMAs were issued a block earlier) just
 // before the C = 0 MFMA that restarts it; the second stage prepares the
-// promotion factors of its chunk.
+// promotion factors of its chunk. A unit streams up to MAX_SEG blocks of
+// output columns that share its token rows as one sequence of stages, so
+// the ring's fill and drain and the unit's setup are paid once per unit.
 #pragma once
 
 #include "common.h"
@@ -46,10 +48,12 @@ struct Pipe8 {
   static constexpr int LPS = WL + TL;                      // loads per thread per stage (all token groups)
   static constexpr int RING = NS * STAGE;
   static constexpr int MAX_CHUNKS = 80;                    // K <= 10240
-  static constexpr int SW_OFF = RING;                      // weight scales [2][MAX_CHUNKS]
-  static constexpr int SA_OFF = SW_OFF + 2 * MAX_CHUNKS * 4;   // token scales [BT][kc_pad]
-  static constexpr int SRC_OFF = SA_OFF + BT * MAX_CHUNKS * 4; // source row of each tile row [BT]
-  static constexpr int LDS_BYTES = SRC_OFF + BT * 4;
+  static constexpr int MAX_SEG = 4;                        // output-column blocks streamed per unit
+  static constexpr int SW_OFF = RING;                      // weight scales [MAX_SEG][2][MAX_CHUNKS]
+  static constexpr int SA_OFF = SW_OFF + MAX_SEG * 2 * MAX_CHUNKS * 4;   // token scales [BT][kc_pad]
+  static constexpr int SRC_OFF = SA_OFF + BT * MAX_CHUNKS * 4;           // source row of each tile row [BT]
+  static constexpr int AMAX_OFF = SRC_OFF + BT * 4;                      // epilogue exchange [2][BT]
+  static constexpr int LDS_BYTES = AMAX_OFF + 2 * BT * 4;
   static_assert(WL * NT * 16 == W_BYTES && TL * NT * 16 == T_BYTES, "stage must split evenly over the threads");
   static_assert(LPS * 3 <= 63, "vmcnt range");
   static_assert((BT * 4) % NT == 0, "four chunks of the scale table split evenly over the threads");
@@ -79,20 +83,28 @@ struct Pipe8Rows {
   uint32_t ot[Pipe8::TL];
 };
 
-// Load q of stage s (K bytes s * 64 .. +63) into ring buffer st: weights for
-// q < WL, then token rows.
-__device__ __forceinline__ void pipe8_issue_one(const Pipe8Rows& r, uint8_t* st, int s, int q) {
+// A stage of the stream: output-column block seg = s / nk (its weight rows lie
+// wseg bytes after the previous block's), K bytes (s % nk) * 64 .. +63.
+struct Pipe8Off {
+  int w, t;   // SGPR byte offsets of the stage's weight and token loads
+};
+__device__ __forceinline__ Pipe8Off pipe8_offsets(int s, int nk, int wseg) {
+  const int seg = s / nk, ks = s - seg * nk;
+  return {seg * wseg + ks * Pipe8::BK, ks * Pipe8::BK};
+}
+
+// Load q of a stage into ring buffer st: weights for q < WL, then token rows.
+__device__ __forceinline__ void pipe8_issue_one(const Pipe8Rows& r, uint8_t* st, Pipe8Off o, int q) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using P = Pipe8;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kb = s * P::BK;
   if (q < P::WL) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.wrs, (lds_void_t*)(st + (q * P::NWAVE + w) * 1024), 16, r.ow[q], kb,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.wrs, (lds_void_t*)(st + (q * P::NWAVE + w) * 1024), 16, r.ow[q], o.w,
                                              0, 0);
   } else {
     const int qq = q - P::WL;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.trs, (lds_void_t*)(st + P::W_BYTES + (qq * P::NWAVE + w) * 1024), 16,
-                                             r.ot[qq], kb, 0, 0);
+                                             r.ot[qq], o.t, 0, 0);
   }
 #endif
 }
@@ -183,7 +195,7 @@ __device__ __forceinline__ void pipe8_hold(const Pipe8Frags<MS>& f) {
 template <int MS, int LT, bool FIRST, bool PROMOTE, bool ISSUE>
 __device__ __forceinline__ void pipe8_block(const Pipe8Frags<MS>& f, f32x16 (&T)[Pipe8::TW][Pipe8::TT],
                                             f32x16 (&acc)[Pipe8::TW][Pipe8::TT], const float (&fac)[Pipe8::TW][Pipe8::TT],
-                                            const Pipe8Rows& rows, uint8_t* lds, int ls) {
+                                            const Pipe8Rows& rows, uint8_t* lds, int ls, Pipe8Off lo) {
   using P = Pipe8;
   constexpr int M = P::TW * MS;
   constexpr int L = ISSUE ? P::WL + LT : 0;      // weight loads, then LT token load groups
@@ -193,7 +205,7 @@ __device__ __forceinline__ void pipe8_block(const Pipe8Frags<MS>& f, f32x16 (&T)
 #pragma unroll
     for (int q = 0; q < L; ++q)
       if ((M == 0 && q == m) || (M > 0 && q * M / L == m)) {
-        pipe8_issue_one(rows, st, ls, q);
+        pipe8_issue_one(rows, st, lo, q);
         sched_fence();
       }
     if (m < M) {
@@ -216,8 +228,8 @@ __device__ __forceinline__ void pipe8_block(const Pipe8Frags<MS>& f, f32x16 (&T)
 // 128-row block of this wave's rows).
 template <int MS, bool GATE_UP>
 __device__ __forceinline__ void pipe8_factors(float (&fac)[Pipe8::TW][Pipe8::TT], const uint8_t* lds, int kc_pad,
-                                              int c) {
-  const float* swt = reinterpret_cast<const float*>(lds + Pipe8::SW_OFF);
+                                              int c, int seg) {
+  const float* swt = reinterpret_cast<const float*>(lds + Pipe8::SW_OFF) + seg * 2 * Pipe8::MAX_CHUNKS;
   const float* sat = reinterpret_cast<const float*>(lds + Pipe8::SA_OFF);
   const int l = threadIdx.x & 63, wt = p8_wt();
 #pragma unroll
@@ -229,78 +241,127 @@ __device__ __forceinline__ void pipe8_factors(float (&fac)[Pipe8::TW][Pipe8::TT]
   }
 }
 
-// One stage kt < nk - 1: fa holds its fragments, fb receives stage kt+1's.
-// WAIT: loads allowed in flight at the barrier (one stage's while stage kt+2
-// exists, else 0); ISSUE: load stage kt+3. A chunk's first stage promotes the
-// previous chunk with fac (when kt > 0); its second stage computes fac for its chunk.
+// One stage of the stream (global index g, local index kt within its
+// output-column block seg) that is not the stream's last: fa holds its
+// fragments, fb receives stage g+1's. WAIT: loads allowed in flight at the
+// barrier (one stage's while stage g+2 exists, else 0); ISSUE: load stage g+3.
+// A chunk's first stage promotes the previous chunk with fac (zero at a
+// block's first chunk, so T * 0 adds nothing); its second stage computes fac
+// for its chunk.
 template <int MS, int LT, bool GATE_UP, bool FIRST, int WAIT, bool ISSUE>
-__device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds, int kc_pad, int kt,
-                                            const Pipe8Frags<MS>& fa, Pipe8Frags<MS>& fb,
+__device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds, int kc_pad, int kt, int g, int nk,
+                                            int wseg, int seg, const Pipe8Frags<MS>& fa, Pipe8Frags<MS>& fb,
                                             f32x16 (&T)[Pipe8::TW][Pipe8::TT], f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
                                             float (&fac)[Pipe8::TW][Pipe8::TT]) {
   using P = Pipe8;
   wait_vm_only_barrier<WAIT>();
-  pipe8_read<MS>(fb, lds + ((kt + 1) & 3) * P::STAGE);
+  pipe8_read<MS>(fb, lds + ((g + 1) & 3) * P::STAGE);
   sched_fence();
+  const Pipe8Off lo = ISSUE ? pipe8_offsets(g + 3, nk, wseg) : Pipe8Off{0, 0};
   if (FIRST) {
-    if (kt > 0) pipe8_block<MS, LT, true, true, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
-    else pipe8_block<MS, LT, true, false, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
+    pipe8_block<MS, LT, true, true, ISSUE>(fa, T, acc, fac, rows, lds, g + 3, lo);
   } else {
-    pipe8_block<MS, LT, false, false, ISSUE>(fa, T, acc, fac, rows, lds, kt + 3);
-    pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, kt >> 1);
+    pipe8_block<MS, LT, false, false, ISSUE>(fa, T, acc, fac, rows, lds, g + 3, lo);
+    pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, kt >> 1, seg);
   }
 }
 
-// acc[j][i] = sum over chunks of promoted T; K % 128 == 0 (nk = K / 64 even),
-// K / 128 <= MAX_CHUNKS. Before the call the tile's source rows and weight
-// scales are in LDS (and visible to every wave); the token-scale table is
-// loaded here from srs (kc = K / 128 scales per source row). LT (>= MS of
-// every wave) token load groups of 64 rows per stage.
-template <int MS, int LT, bool GATE_UP>
-__device__ __forceinline__ void pipe8_mainloop(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int K, uint8_t* lds,
-                                               f32x16 (&acc)[Pipe8::TW][Pipe8::TT]) {
-  using P = Pipe8;
-  static_assert(LT >= 1 && LT <= P::TL && LT >= MS, "token load groups must cover the live sub-tiles");
-  constexpr int LPS = P::WL + LT;                      // loads per stage per thread
-  const int nk = K / P::BK, kc = K / 128, kc_pad = (kc + 3) & ~3;
-  pipe8_issue_scale_table(srs, lds, kc, kc_pad);
-  for (int s = 0; s < 3 && s < nk; ++s) {
-#pragma unroll
-    for (int q = 0; q < LPS; ++q) pipe8_issue_one(rows, lds + s * P::STAGE, s, q);
-  }
-  if (nk >= 3) wait_vm_only_barrier<2 * LPS>();        // scale table and stage 0 have landed
-  else wait_vm_only_barrier<LPS>();                    // nk == 2
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_s_waitcnt(0xc07f);                  // no scalar load pending: LDS waits stay partial
-#endif
-  f32x16 T[P::TW][P::TT];
-  float fac[P::TW][P::TT];
-  Pipe8Frags<MS> f0, f1;
-  pipe8_read<MS>(f0, lds);
-  int kt = 0;
-  for (; kt + 4 < nk; kt += 2) {                       // both stages refill the ring
-    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
-    pipe8_stage<MS, LT, GATE_UP, false, LPS, true>(rows, lds, kc_pad, kt + 1, f1, f0, T, acc, fac);
-  }
-  if (kt + 4 == nk) {                                  // stage nk-1 is the last to load
-    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
-    pipe8_stage<MS, LT, GATE_UP, false, LPS, false>(rows, lds, kc_pad, kt + 1, f1, f0, T, acc, fac);
-    kt += 2;
-  }
-  // last chunk: stage nk-2 reads nk-1; stage nk-1 reads nothing
-  pipe8_stage<MS, LT, GATE_UP, true, 0, false>(rows, lds, kc_pad, kt, f0, f1, T, acc, fac);
-  pipe8_block<MS, LT, false, false, false>(f1, T, acc, fac, rows, lds, 0);
-  pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, (nk >> 1) - 1);
-  // the reads below follow the last MFMAs closely: give them the wait states
-  // an MFMA result needs before a v_accvgpr_read (the asm read is opaque to
-  // the compiler's hazard checks)
+// End of output-column block seg: promote its last chunk, hand acc to the
+// epilogue, restart acc and the factors from zero. The last chunk's MFMAs
+// are the latest issued, so the reads get the wait states an MFMA result
+// needs before a v_accvgpr_read (the asm read is opaque to the compiler's
+// hazard checks).
+template <int MS, class EPI>
+__device__ __forceinline__ void pipe8_finish(f32x16 (&T)[Pipe8::TW][Pipe8::TT], f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
+                                             float (&fac)[Pipe8::TW][Pipe8::TT], EPI& epi, int seg) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-  for (int j = 0; j < P::TW; ++j)
+  for (int j = 0; j < Pipe8::TW; ++j)
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = fmaf(agpr_read(T[j][i][v]), fac[j][i], acc[j][i][v]);
+  epi(seg, acc);
+#pragma unroll
+  for (int j = 0; j < Pipe8::TW; ++j)
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      fac[j][i] = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+    }
+}
+
+// The K loops of nseg output-column blocks of one unit as one stream of
+// total = nseg * nk stages through the ring: the next block's stages are in
+// flight while a block ends. For each block: acc = sum over chunks of
+// promoted T, then epi(seg, acc) (stores; may use AMAX_OFF with an LDS-only
+// barrier). K % 128 == 0, K / 128 <= MAX_CHUNKS, nseg <= MAX_SEG. Before the
+// call the unit's source rows and weight scales ([seg][2][chunk]) are in LDS
+// and visible to every wave; the token-scale table is loaded here from srs
+// (kc = K / 128 scales per source row). LT (>= MS of every wave) token load
+// groups of 64 rows per stage.
+template <int MS, int LT, bool GATE_UP, class EPI>
+__device__ __forceinline__ void pipe8_stream(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int K, int nseg,
+                                             int wseg, uint8_t* lds, EPI& epi) {
+  using P = Pipe8;
+  static_assert(LT >= 1 && LT <= P::TL && LT >= MS, "token load groups must cover the live sub-tiles");
+  constexpr int LPS = P::WL + LT;                      // loads per stage per thread
+  const int nk = K / P::BK, kc = K / 128, kc_pad = (kc + 3) & ~3, total = nseg * nk;   // nk even, total >= 2
+  pipe8_issue_scale_table(srs, lds, kc, kc_pad);
+  for (int s = 0; s < 3 && s < total; ++s) {
+    const Pipe8Off o = pipe8_offsets(s, nk, wseg);
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) pipe8_issue_one(rows, lds + s * P::STAGE, o, q);
+  }
+  if (total >= 3) wait_vm_only_barrier<2 * LPS>();     // scale table and stage 0 have landed
+  else wait_vm_only_barrier<LPS>();                    // total == 2
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0xc07f);                  // no scalar load pending: LDS waits stay partial
+#endif
+  f32x16 T[P::TW][P::TT];
+  f32x16 acc[P::TW][P::TT];
+  float fac[P::TW][P::TT];
+#pragma unroll
+  for (int j = 0; j < P::TW; ++j)
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      T[j][i] = f32x16{};
+      fac[j][i] = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+    }
+  Pipe8Frags<MS> f0, f1;
+  pipe8_read<MS>(f0, lds);
+  int kt = 0, seg = 0, g = 0;
+  for (; g + 4 < total; g += 2) {                      // both stages refill the ring
+    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt, g, nk, wseg, seg, f0, f1, T, acc, fac);
+    pipe8_stage<MS, LT, GATE_UP, false, LPS, true>(rows, lds, kc_pad, kt + 1, g + 1, nk, wseg, seg, f1, f0, T, acc,
+                                                   fac);
+    kt += 2;
+    if (kt == nk) {
+      pipe8_finish<MS>(T, acc, fac, epi, seg);
+      ++seg;
+      kt = 0;
+    }
+  }
+  if (g + 4 == total) {                                // stage total-1 is the last to load
+    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt, g, nk, wseg, seg, f0, f1, T, acc, fac);
+    pipe8_stage<MS, LT, GATE_UP, false, LPS, false>(rows, lds, kc_pad, kt + 1, g + 1, nk, wseg, seg, f1, f0, T, acc,
+                                                    fac);
+    kt += 2;
+    if (kt == nk) {
+      pipe8_finish<MS>(T, acc, fac, epi, seg);
+      ++seg;
+      kt = 0;
+    }
+  }
+  // the stream's last pair: stage total-1 reads nothing
+  pipe8_stage<MS, LT, GATE_UP, true, 0, false>(rows, lds, kc_pad, kt, total - 2, nk, wseg, seg, f0, f1, T, acc, fac);
+  pipe8_block<MS, LT, false, false, false>(f1, T, acc, fac, rows, lds, 0, Pipe8Off{0, 0});
+  pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, (kt + 1) >> 1, seg);
+  pipe8_finish<MS>(T, acc, fac, epi, seg);
+  // every wave has read the ring before the next unit's loads overwrite it
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
