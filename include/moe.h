@@ -90,6 +90,8 @@ typedef struct {
  *   topk_gate  out [T, K] fp32, gate of each selected expert (sums to 1 per token).
  *   expert_load out [N_r] int32, number of tokens per expert (overwritten, not accumulated).
  *   scores     out [T, N_r] fp32 sigmoid affinities, or NULL (then kept in the workspace).
+ *   workspace  device scratch of at least moe_workspace_bytes(shape, ...) bytes, always
+ *              required: bf16 logits are summed over K slices through it.
  * Selection compares fp32 values s + b; ties go to the lower group / expert id.
  */
 moe_status moe_route(const moe_shape* shape, moe_dtype act, const void* u, const void* centroids,

@@ -6,10 +6,12 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <string>
 
 #include "launch.h"
+#include "sched.h"
 
 namespace {
 
@@ -93,6 +95,35 @@ int device_cu_count() {
   return g_cu[dev];
 }
 
+int* unit_queue_slot() {
+  constexpr int kSlots = 64;
+  static std::mutex mu;
+  static int* bufs[64] = {};
+  static std::atomic<unsigned> next{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  int* b;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (!bufs[dev]) {
+      void* p = nullptr;
+      const size_t bytes = sizeof(int) * kQueueInts * kSlots;
+      if (hipMalloc(&p, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+      }
+      if (hipMemset(p, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(p);
+        (void)hipGetLastError();
+        return nullptr;
+      }
+      bufs[dev] = static_cast<int*>(p);
+    }
+    b = bufs[dev];
+  }
+  return b + kQueueInts * (next.fetch_add(1, std::memory_order_relaxed) % kSlots);
+}
+
 size_t ffn_ws_bytes(moe_dtype w, int n_rows, int I) {
   const size_t n = static_cast<size_t>(n_rows) * I;
   if (w == MOE_F32) return align256(n * 4);
@@ -111,7 +142,7 @@ const char* moe_version(void) { return "moe-gfx950 0.1"; }
 size_t moe_workspace_bytes(const moe_shape* shape, moe_dtype gemm) {
   if (!shape || check_shape(shape) != MOE_OK) return 0;
   const moe::Shape s = moe::to_shape(*shape);
-  const size_t route = align256(static_cast<size_t>(s.T) * s.N * sizeof(float));
+  const size_t route = align256(moe::route_ws_bytes(s, MOE_BF16));
   const size_t perm = align256(moe::permute_ws_bytes(s));
   const int rows = s.T * (s.K + s.Ns);   // routed and shared experts in one grouped call
   const size_t ffn = moe::ffn_ws_bytes(gemm, rows, s.I);
@@ -127,14 +158,12 @@ moe_status moe_route(const moe_shape* shape, moe_dtype act, const void* u, const
   REQUIRE(act == MOE_F32 || act == MOE_BF16, "route: act must be MOE_F32 or MOE_BF16 (got %d)", static_cast<int>(act));
   REQUIRE(u && centroids && bias && topk_idx && topk_gate && expert_load, "route: a required pointer is NULL");
   const moe::Shape s = moe::to_shape(*shape);
-  if (!scores) {
-    const size_t need = static_cast<size_t>(s.T) * s.N * sizeof(float);
-    if (!workspace || ws_bytes < need)
-      return fail(MOE_E_WORKSPACE, "route: workspace of %zu bytes < %zu needed for the scores", ws_bytes, need);
-    scores = static_cast<float*>(workspace);
-  }
+  const size_t need = moe::route_ws_bytes(s, act);
+  if (!workspace || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "route: workspace of %zu bytes < %zu needed", ws_bytes, need);
+  if (!scores) scores = static_cast<float*>(workspace);
   auto st = static_cast<hipStream_t>(stream);
-  return finish(moe::launch_route(s, act, u, centroids, bias, topk_idx, topk_gate, expert_load, scores, st),
+  return finish(moe::launch_route(s, act, u, centroids, bias, topk_idx, topk_gate, expert_load, scores, workspace, st),
                 "moe_route", st);
 }
 

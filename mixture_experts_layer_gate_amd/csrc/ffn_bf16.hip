@@ -93,13 +93,15 @@ __device__ __forceinline__ void down_tile(const PipeRows<FP>& rows, int d, int I
 __global__ __launch_bounds__(FP::NT, 1) void ffn_gate_up_bf16_kernel(
     int d, int I, int E, int n_rows, int a_rows, const int32_t* __restrict__ off, moe_row_mode mode,
     const int32_t* __restrict__ row_src, const uint16_t* __restrict__ a, const uint16_t* __restrict__ wgu,
-    uint16_t* __restrict__ H) {
+    uint16_t* __restrict__ H, int* __restrict__ q) {
   extern __shared__ __align__(16) uint8_t lds_p[];
   int* cum = reinterpret_cast<int*>(lds_p + FP::LDS_BYTES);
   __shared__ int wtmp[16];
   const int NB = I / kHcols;
   const int total = build_units_balanced(off, E, n_rows, FP::BT / 32, NB, cum, wtmp);
-  for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
+  __shared__ int tslot;
+  int x_off = 0;
+  for (int t; (t = unit_queue_next(q, total, x_off, &tslot)) >= 0;) {
     const Unit un = find_unit_balanced(t, off, E, n_rows, FP::BT / 32, cum);
     int s_first = source_row(mode, row_src, un.m0, un.seg0, a_rows);
     if (s_first < 0) s_first = 0;
@@ -135,13 +137,16 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_down_bf16_kernel(int d, int I, 
                                                                   const int32_t* __restrict__ off,
                                                                   const uint16_t* __restrict__ H,
                                                                   const uint16_t* __restrict__ wd,
-                                                                  uint16_t* __restrict__ y) {
+                                                                  uint16_t* __restrict__ y,
+                                                                  int* __restrict__ q) {
   extern __shared__ __align__(16) uint8_t lds_p[];
   int* cum = reinterpret_cast<int*>(lds_p + FP::LDS_BYTES);
   __shared__ int wtmp[16];
   const int NB = d / FP::BW;
   const int total = build_units_balanced(off, E, n_rows, FP::BT / 32, NB, cum, wtmp);
-  for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
+  __shared__ int tslot;
+  int x_off = 0;
+  for (int t; (t = unit_queue_next(q, total, x_off, &tslot)) >= 0;) {
     const Unit un = find_unit_balanced(t, off, E, n_rows, FP::BT / 32, cum);
     PipeRows<FP> rows;
     rows.trs = pipe_rsrc(H, static_cast<uint64_t>(n_rows) * I * 2);
@@ -186,23 +191,27 @@ static void set_lds_limits() {
 
 hipError_t launch_ffn_bf16_gate_up(const FfnArgs& p, hipStream_t st) {
   set_lds_limits();
+  int* q = unit_queue_slot();
+  if (!q) return hipErrorOutOfMemory;
   const size_t lds = FP::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / FP::BT + p.n_experts;
   const int g1 = persistent_grid(mblocks * (p.I / kHcols), 1);
   hipLaunchKernelGGL(ffn_gate_up_bf16_kernel, dim3(g1), dim3(FP::NT), lds, st, p.d, p.I, p.n_experts, p.n_rows,
                      p.a_rows, p.offsets, p.mode, p.row_src, static_cast<const uint16_t*>(p.a),
-                     static_cast<const uint16_t*>(p.w_gu), static_cast<uint16_t*>(p.h));
+                     static_cast<const uint16_t*>(p.w_gu), static_cast<uint16_t*>(p.h), q);
   return hipGetLastError();
 }
 
 hipError_t launch_ffn_bf16_down(const FfnArgs& p, hipStream_t st) {
   set_lds_limits();
+  int* q = unit_queue_slot();
+  if (!q) return hipErrorOutOfMemory;
   const size_t lds = FP::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / FP::BT + p.n_experts;
   const int g2 = persistent_grid(mblocks * (p.d / FP::BW), 1);
   hipLaunchKernelGGL(ffn_down_bf16_kernel, dim3(g2), dim3(FP::NT), lds, st, p.d, p.I, p.n_experts, p.n_rows,
                      p.offsets, static_cast<const uint16_t*>(p.h), static_cast<const uint16_t*>(p.w_d),
-                     static_cast<uint16_t*>(p.y));
+                     static_cast<uint16_t*>(p.y), q);
   return hipGetLastError();
 }
 

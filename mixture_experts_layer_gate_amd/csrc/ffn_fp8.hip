@@ -144,7 +144,7 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
     int d, int I, int E, int n_rows, int a_rows, const int32_t* __restrict__ off, moe_row_mode mode,
     const int32_t* __restrict__ row_src, const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
     const uint8_t* __restrict__ wgu, const float* __restrict__ wgu_scale, uint8_t* __restrict__ Hq,
-    float* __restrict__ Hs) {
+    float* __restrict__ Hs, int* __restrict__ q) {
   extern __shared__ __align__(16) uint8_t lds8[];
   float* swt = reinterpret_cast<float*>(lds8 + P8::SW_OFF);
   int* srcrow = reinterpret_cast<int*>(lds8 + P8::SRC_OFF);
@@ -155,7 +155,9 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t trs = pipe_rsrc(a, static_cast<uint64_t>(a_rows) * d);
   const __amdgpu_buffer_rsrc_t srs = pipe_rsrc(a_scale, static_cast<uint64_t>(a_rows) * kc * 4);
-  for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
+  __shared__ int tslot;
+  int x_off = 0;
+  for (int t; (t = unit_queue_next(q, total, x_off, &tslot)) >= 0;) {
     const Unit un = find_unit_balanced(t, off, E, n_rows, kMaxSub8, cum);
     const int nb0 = un.nb * P8::MAX_SEG, nseg = min(P8::MAX_SEG, NB - nb0);
     // LDS tables of the unit: weight scales of each tile (gate block row nb,
@@ -204,7 +206,8 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
                                                                  const float* __restrict__ Hs,
                                                                  const uint8_t* __restrict__ wd,
                                                                  const float* __restrict__ wd_scale,
-                                                                 uint16_t* __restrict__ y) {
+                                                                 uint16_t* __restrict__ y,
+                                                                 int* __restrict__ q) {
   extern __shared__ __align__(16) uint8_t lds8[];
   float* swt = reinterpret_cast<float*>(lds8 + P8::SW_OFF);
   int* srcrow = reinterpret_cast<int*>(lds8 + P8::SRC_OFF);
@@ -215,7 +218,9 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t trs = pipe_rsrc(Hq, static_cast<uint64_t>(n_rows) * I);
   const __amdgpu_buffer_rsrc_t srs = pipe_rsrc(Hs, static_cast<uint64_t>(n_rows) * kc * 4);
-  for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
+  __shared__ int tslot;
+  int x_off = 0;
+  for (int t; (t = unit_queue_next(q, total, x_off, &tslot)) >= 0;) {
     const Unit un = find_unit_balanced(t, off, E, n_rows, kMaxSub8, cum);
     const int nb0 = un.nb * P8::MAX_SEG, nseg = min(P8::MAX_SEG, NB - nb0);
     // weight scales: wave half ww of tile nb covers output columns nb*256 + 128ww .. +127 = block row 2nb + ww
@@ -271,25 +276,29 @@ static void f8_set_lds_limits() {
 hipError_t launch_ffn_fp8_gate_up(const FfnArgs& p, hipStream_t st) {
   if (p.n_experts > kMaxExperts8) return hipErrorInvalidValue;
   f8_set_lds_limits();
+  int* q = unit_queue_slot();
+  if (!q) return hipErrorOutOfMemory;
   const size_t lds = P8::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / P8::BT + p.n_experts;
   hipLaunchKernelGGL(ffn_gate_up_fp8_kernel, dim3(f8_grid(mblocks * cdiv(p.I / 128, P8::MAX_SEG))), dim3(P8::NT), lds,
                      st, p.d, p.I,
                      p.n_experts, p.n_rows, p.a_rows, p.offsets, p.mode, p.row_src,
                      static_cast<const uint8_t*>(p.a), p.a_scale, static_cast<const uint8_t*>(p.w_gu), p.w_gu_scale,
-                     static_cast<uint8_t*>(p.h), p.h_scale);
+                     static_cast<uint8_t*>(p.h), p.h_scale, q);
   return hipGetLastError();
 }
 
 hipError_t launch_ffn_fp8_down(const FfnArgs& p, hipStream_t st) {
   if (p.n_experts > kMaxExperts8) return hipErrorInvalidValue;
   f8_set_lds_limits();
+  int* q = unit_queue_slot();
+  if (!q) return hipErrorOutOfMemory;
   const size_t lds = P8::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / P8::BT + p.n_experts;
   hipLaunchKernelGGL(ffn_down_fp8_kernel, dim3(f8_grid(mblocks * cdiv(p.d / P8::BW, P8::MAX_SEG))), dim3(P8::NT), lds,
                      st, p.d, p.I,
                      p.n_experts, p.n_rows, p.offsets, static_cast<const uint8_t*>(p.h), p.h_scale,
-                     static_cast<const uint8_t*>(p.w_d), p.w_d_scale, static_cast<uint16_t*>(p.y));
+                     static_cast<const uint8_t*>(p.w_d), p.w_d_scale, static_cast<uint16_t*>(p.y), q);
   return hipGetLastError();
 }
 

@@ -21,9 +21,19 @@ inline Shape to_shape(const moe_shape& s) {
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Counters for one launch of a grouped FFN kernel's dynamic unit queue
+// (sched.h): the next of 64 zeroed slots of a buffer the library allocates on
+// the current device at its first use; null if that allocation fails. Each
+// launch leaves its slot zeroed, so up to 64 such launches may run at once
+// on one device.
+int* unit_queue_slot();
+
 // ---- route
+// workspace: the scores [T, N] fp32 (used when the caller passes none), then
+// for bf16 the partial logit sums of the K slices.
+size_t route_ws_bytes(const Shape& s, moe_dtype act);
 hipError_t launch_route(const Shape& s, moe_dtype act, const void* u, const void* cent, const float* bias,
-                        int32_t* idx, float* gate, int32_t* load, float* scores, hipStream_t st);
+                        int32_t* idx, float* gate, int32_t* load, float* scores, void* ws, hipStream_t st);
 
 // ---- permute
 size_t permute_ws_bytes(const Shape& s);

@@ -6,52 +6,67 @@
 #include <float.h>
 #include <limits.h>
 
+#include <mutex>
+
 #include "common.h"
-#include "gemm_bf16.h"
+#include "gemm_pipe.h"
 #include "launch.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------- logits
-// scores[t, e] = Sigmoid(u[t] . centroid[e]); bf16 operands, fp32 MFMA accumulation.
-using RouteTile = TileBF16<64, 128, 2, 2>;
+// u . e_i for bf16 operands: the pipelined main loop of the expert GEMMs
+// (gemm_pipe.h) on tiles of 256 centroids x 128 tokens, with K split into S
+// slices so that a V3-sized batch fills every CU (64 token tiles x 4 slices).
+// Slice s writes fp32 partial sums part[s][t][e]; the selection kernel adds the
+// S partials in slice order and applies the sigmoid. Centroid rows past N and
+// token rows past T read a valid row and are never stored.
+using RouteTile = Pipe<256, 128>;
 
-__global__ __launch_bounds__(RouteTile::NT) void route_logits_bf16_kernel(
-    int T, int d, int N, const uint16_t* __restrict__ u, const uint16_t* __restrict__ cent,
-    float* __restrict__ scores, int32_t* __restrict__ load) {
-  using G = RouteTile;
-  extern __shared__ __align__(16) uint16_t lds_route[];
+__global__ __launch_bounds__(RouteTile::NT, 1) void route_logits_bf16_kernel(
+    int T, int d, int N, int n_wt, int kslice, int t_begin, int t_count, const uint16_t* __restrict__ u,
+    const uint16_t* __restrict__ cent, float* __restrict__ part, int32_t* __restrict__ load) {
+  using P = RouteTile;
+  extern __shared__ __align__(16) uint8_t lds_route[];
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int e = tid; e < N; e += G::NT) load[e] = 0;   // histogram is rebuilt by the select kernel
-  const int n0 = blockIdx.x * G::BN;
-  const int m0 = blockIdx.y * G::BM;
-  const uint16_t* pa[G::AC];
-  const uint16_t* pb[G::BC];
+  if (blockIdx.x == 0 && t_begin == 0)
+    for (int e = tid; e < N; e += P::NT) load[e] = 0;   // histogram is rebuilt by the select kernel
+  const int S = cdiv(d, kslice);
+  const int ks = blockIdx.x % S, tile = blockIdx.x / S;
+  const int w0 = (tile % n_wt) * P::BW, t0 = (tile / n_wt) * P::BT;   // t0 within this launch's token range
+  const int k0 = ks * kslice, K = min(kslice, d - k0);
+  PipeRows<P> rows;
+  rows.wrs = pipe_rsrc(cent + k0, (static_cast<uint64_t>(N) * d - k0) * 2);
+  rows.trs = pipe_rsrc(u + static_cast<size_t>(t_begin) * d + k0, (static_cast<uint64_t>(t_count) * d - k0) * 2);
 #pragma unroll
-  for (int j = 0; j < G::AC; ++j) {
-    const int r = m0 + chunk_row<G>(tid, j);
-    pa[j] = r < T ? u + static_cast<size_t>(r) * d + chunk_col<G>(tid, j) : nullptr;
-  }
+  for (int q = 0; q < P::WL; ++q)
+    rows.ow[q] = static_cast<uint32_t>(min(w0 + pipe_load_row(q), N - 1)) * d * 2 + pipe_load_chunk(q) * 16;
 #pragma unroll
-  for (int j = 0; j < G::BC; ++j) {
-    const int e = n0 + chunk_row<G>(tid, j);
-    pb[j] = e < N ? cent + static_cast<size_t>(e) * d + chunk_col<G>(tid, j) : nullptr;
-  }
-  f32x16 acc[G::TM][G::TN];
-  zero_acc<G>(acc);
-  mainloop_bf16<G>(pa, pb, d, lds_route, acc);
+  for (int q = 0; q < P::TL; ++q)
+    rows.ot[q] = static_cast<uint32_t>(min(t0 + pipe_load_row(q), t_count - 1)) * d * 2 + pipe_load_chunk(q) * 16;
+  f32x16 acc[P::TW][P::TT];
 #pragma unroll
-  for (int i = 0; i < G::TM; ++i)
+  for (int j = 0; j < P::TW; ++j)
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j) {
-      const int e = n0 + acc_col<G>(j);
+    for (int i = 0; i < P::TT; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = m0 + acc_row<G>(i, v);
-        if (t < T && e < N) scores[static_cast<size_t>(t) * N + e] = 1.0f / (1.0f + expf(-acc[i][j][v]));
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+  pipe_mainloop<P, P::TT, P::TL>(rows, K, lds_route, acc);
+#pragma unroll
+  for (int i = 0; i < P::TT; ++i) {
+    const int t = t0 + pipe_token_row(i);
+    if (t >= t_count) continue;
+    float* prow = part + (static_cast<size_t>(ks) * T + t_begin + t) * N;
+#pragma unroll
+    for (int j = 0; j < P::TW; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = w0 + pipe_wcol<P>(j, q);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (e + r < N) prow[e + r] = acc[j][i][4 * q + r];
       }
-    }
+  }
 }
 
 // fp32 operands: 16x16 output tile per block, 16-wide K slices through LDS.
@@ -102,7 +117,11 @@ __device__ __forceinline__ void argmax_pair(float& v, int& id) {
 
 constexpr int kSelWaves = 4;
 
-__global__ __launch_bounds__(64 * kSelWaves) void route_select_kernel(Shape s, const float* __restrict__ scores,
+// part != nullptr: S partial logit sums per token (slice-major), added in
+// slice order, then s = Sigmoid(sum) is written to scores; otherwise scores
+// already holds the affinities.
+__global__ __launch_bounds__(64 * kSelWaves) void route_select_kernel(Shape s, const float* __restrict__ part,
+                                                                      int S_part, float* __restrict__ scores,
                                                                       const float* __restrict__ bias,
                                                                       int32_t* __restrict__ idx,
                                                                       float* __restrict__ gate,
@@ -124,7 +143,15 @@ __global__ __launch_bounds__(64 * kSelWaves) void route_select_kernel(Shape s, c
     const bool active = t < s.T;
     if (active) {
       for (int e = lane; e < N; e += kWave) {
-        const float v = scores[static_cast<size_t>(t) * N + e];
+        float v;
+        if (part) {
+          float x = part[static_cast<size_t>(t) * N + e];
+          for (int p = 1; p < S_part; ++p) x += part[(static_cast<size_t>(p) * s.T + t) * N + e];
+          v = 1.0f / (1.0f + expf(-x));
+          scores[static_cast<size_t>(t) * N + e] = v;
+        } else {
+          v = scores[static_cast<size_t>(t) * N + e];
+        }
         sr[e] = v;
         sb[e] = v + bias[e];
       }
@@ -192,13 +219,53 @@ __global__ __launch_bounds__(64 * kSelWaves) void route_select_kernel(Shape s, c
   }
 }
 
+// K slices of the bf16 logits GEMM: enough tiles to give every CU one
+// (256-centroid x 128-token tiles), at most 16 slices, whole 128-wide chunks.
+static int route_kslice(const Shape& s) {
+  const int tiles = cdiv(s.N, RouteTile::BW) * cdiv(s.T, RouteTile::BT);
+  const int chunks = s.d / 128;
+  int S = device_cu_count() / tiles;
+  S = S < 1 ? 1 : (S > 16 ? 16 : S);
+  S = S > chunks ? chunks : S;
+  return cdiv(chunks, S) * 128;
+}
+
+size_t route_ws_bytes(const Shape& s, moe_dtype act) {
+  const size_t scores = (static_cast<size_t>(s.T) * s.N * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  if (act != MOE_BF16) return scores;
+  const size_t S = cdiv(s.d, route_kslice(s));
+  return scores + S * s.T * s.N * sizeof(float);
+}
+
 hipError_t launch_route(const Shape& s, moe_dtype act, const void* u, const void* cent, const float* bias,
-                        int32_t* idx, float* gate, int32_t* load, float* scores, hipStream_t st) {
+                        int32_t* idx, float* gate, int32_t* load, float* scores, void* ws, hipStream_t st) {
+  const float* part = nullptr;
+  int S = 0;
   if (act == MOE_BF16) {
-    using G = RouteTile;
-    dim3 grid(cdiv(s.N, G::BN), cdiv(s.T, G::BM));
-    hipLaunchKernelGGL(route_logits_bf16_kernel, grid, dim3(G::NT), G::LDS_BYTES, st, s.T, s.d, s.N,
-                       static_cast<const uint16_t*>(u), static_cast<const uint16_t*>(cent), scores, load);
+    using P = RouteTile;
+    const int kslice = route_kslice(s);
+    S = cdiv(s.d, kslice);
+    float* p = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                        ((static_cast<size_t>(s.T) * s.N * sizeof(float) + 255) & ~static_cast<size_t>(255)));
+    part = p;
+    static std::once_flag once;
+    std::call_once(once, [] {
+      // a refused request must not leave a sticky error
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(route_logits_bf16_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, RouteTile::LDS_BYTES);
+      (void)hipGetLastError();
+    });
+    const int n_wt = cdiv(s.N, P::BW);
+    // token ranges whose rows span less than 4 GiB (32-bit buffer offsets)
+    const long long max_t = ((1LL << 32) - 1) / (2LL * s.d);
+    const int t_step = static_cast<int>(max_t < s.T ? (max_t / P::BT) * P::BT : s.T);
+    for (int t_begin = 0; t_begin < s.T; t_begin += t_step) {
+      const int t_count = s.T - t_begin < t_step ? s.T - t_begin : t_step;
+      const int grid = n_wt * cdiv(t_count, P::BT) * S;
+      hipLaunchKernelGGL(route_logits_bf16_kernel, dim3(grid), dim3(P::NT), P::LDS_BYTES, st, s.T, s.d, s.N, n_wt,
+                         kslice, t_begin, t_count, static_cast<const uint16_t*>(u),
+                         static_cast<const uint16_t*>(cent), p, load);
+    }
   } else {
     dim3 grid(cdiv(s.N, 16), cdiv(s.T, 16));
     hipLaunchKernelGGL(route_logits_f32_kernel, grid, dim3(256), 0, st, s.T, s.d, s.N,
@@ -209,8 +276,8 @@ hipError_t launch_route(const Shape& s, moe_dtype act, const void* u, const void
   const size_t lds = sizeof(float) * (static_cast<size_t>(s.N) + 2 * kSelWaves * static_cast<size_t>(s.N));
   int blocks = cdiv(s.T, kSelWaves);
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(route_select_kernel, dim3(blocks), dim3(64 * kSelWaves), lds, st, s, scores, bias, idx, gate,
-                     load);
+  hipLaunchKernelGGL(route_select_kernel, dim3(blocks), dim3(64 * kSelWaves), lds, st, s, part, S, scores, bias, idx,
+                     gate, load);
   return hipGetLastError();
 }
 

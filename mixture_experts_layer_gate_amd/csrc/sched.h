@@ -4,10 +4,13 @@
 // expert's ragged row segment [off[e], off[e+1]). Units are numbered expert by
 // expert, n-block by n-block, m-block fastest, so consecutive units share the
 // same weight tile (all m-blocks of one n-block) and the same expert.
-// Workgroup b of a grid of G (G % 8 == 0) takes units v, v+G, v+2G... with
-// v = (b % 8) * (G / 8) + b / 8: workgroups are handed to the 8 XCDs round-robin,
-// so this keeps runs of consecutive units -- one expert's weight and
-// activation tiles -- inside one XCD's L2.
+// Units are handed out dynamically (unit_queue_next): the unit list is cut
+// into 8 contiguous ranges, one per XCD (workgroups go to the 8 XCDs
+// round-robin, so workgroup b runs on XCD b % 8), and a workgroup takes the
+// next unit of its XCD's range with an atomic counter, then helps the other
+// ranges. Runs of consecutive units -- one expert's weight and activation
+// tiles -- stay inside one XCD's L2, and unequal units (ragged experts) no
+// longer leave some CUs a whole unit behind the others.
 #pragma once
 
 #include "common.h"
@@ -139,6 +142,43 @@ __device__ __forceinline__ Unit find_unit_balanced(int t, const int32_t* __restr
 __device__ __forceinline__ int xcd_virtual_block() {
   const int G = gridDim.x, b = blockIdx.x;
   return (b & 7) * (G >> 3) + (b >> 3);
+}
+
+// Counters of one launch: q[0..7] units taken from each XCD range, q[8]
+// workgroups done. They start at zero; the last workgroup to run out of
+// units puts them back to zero for the next launch that uses this slot.
+constexpr int kQueueInts = 32;   // ints per slot (128 bytes)
+
+// Next unit for this workgroup, or -1 when every range is exhausted. Every
+// thread of the block calls it; x_off (the ranges this workgroup has
+// exhausted) is only used by thread 0. slot: one int of shared memory.
+__device__ __forceinline__ int unit_queue_next(int* __restrict__ q, int total, int& x_off, int* slot) {
+  if (threadIdx.x == 0) {
+    int t = -1;
+    const int x0 = blockIdx.x & 7;
+    while (x_off < 8) {
+      const int x = (x0 + x_off) & 7;
+      const int lo = static_cast<int>(static_cast<long long>(x) * total / 8);
+      const int hi = static_cast<int>(static_cast<long long>(x + 1) * total / 8);
+      if (lo < hi) {
+        const int v = lo + atomicAdd(&q[x], 1);
+        if (v < hi) {
+          t = v;
+          break;
+        }
+      }
+      ++x_off;
+    }
+    if (t < 0 && atomicAdd(&q[8], 1) == static_cast<int>(gridDim.x) - 1) {
+      // every workgroup has stopped taking units: reset for the next launch
+      for (int x = 0; x < 9; ++x) atomicExch(&q[x], 0);
+    }
+    *slot = t;
+  }
+  __syncthreads();
+  const int t = wave_uniform(*slot);
+  __syncthreads();
+  return t;
 }
 
 // Index of the input row for output row r (absolute) of an expert whose segment starts at seg0.
