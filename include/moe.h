@@ -164,15 +164,19 @@ moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_expert
  *   h        [n_rows, I]: fp32 (w = MOE_F32), bf16 (w = MOE_BF16) or E4M3 codes
  *            (w = MOE_F8E4M3, quantised per 1x128 tile along I with h_scale).
  *   h_scale  [n_rows, I/128] fp32 for fp8, else NULL.
+ *   workspace device scratch of at least 128 bytes (the counters of the
+ *            kernel's dynamic work queue, cleared by the call itself); it must
+ *            not overlap h or another call's workspace that is in flight.
  */
 moe_status moe_ffn_gate_up(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                            const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
                            const void* a, const float* a_scale, int32_t a_rows,
                            const void* w_gate_up, const float* w_gu_scale,
-                           void* h, float* h_scale, void* stream);
+                           void* h, float* h_scale, void* workspace, size_t ws_bytes, void* stream);
 moe_status moe_ffn_down(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                         const int32_t* expert_offsets, const void* h, const float* h_scale,
-                        const void* w_down, const float* w_d_scale, moe_dtype y_dtype, void* y, void* stream);
+                        const void* w_down, const float* w_d_scale, moe_dtype y_dtype, void* y,
+                        void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * moe_combine -- eq. (12): out[t] = u[t] + sum_s y_shared[s*T + t] + sum_k gate[t,k] * y_routed[row_of[t*K+k]].

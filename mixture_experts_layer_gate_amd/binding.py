@@ -49,8 +49,8 @@ _SIGS = {
     "moe_route": [_S, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_permute": [_S, _I, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, ctypes.c_size_t, _P],
     "moe_grouped_ffn": [_S, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
-    "moe_ffn_gate_up": [_S, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P],
-    "moe_ffn_down": [_S, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P],
+    "moe_ffn_gate_up": [_S, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_ffn_down": [_S, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
     "moe_combine": [_S, _I, _P, _P, _P, _P, _P, _P, _P],
     "moe_bias_update": [_S, _P, ctypes.c_float, _P, _P],
     "moe_quantize_weights": [_I, _I, _I, _P, _P, _P, _P],
@@ -170,7 +170,7 @@ def moe_grouped_ffn(shape: moe_shape, w: int, n_experts: int, n_rows: int, exper
 
 
 def moe_ffn_gate_up(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_offsets, mode: int, row_src,
-                    a, a_scale, a_rows: int, w_gate_up, w_gu_scale, h, h_scale=None, stream=None):
+                    a, a_scale, a_rows: int, w_gate_up, w_gu_scale, h, h_scale=None, workspace=None, stream=None):
     d, I = shape.d, shape.inter
     _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a, a_rows * d, "a")
     _need(w_gate_up, n_experts * 2 * I * d, "w_gate_up"); _need(h, n_rows * I, "h")
@@ -182,11 +182,11 @@ def moe_ffn_gate_up(shape: moe_shape, w: int, n_experts: int, n_rows: int, exper
         _need(h_scale, n_rows * (I // 128), "h_scale")
     _check(lib().moe_ffn_gate_up(ctypes.byref(shape), w, n_experts, n_rows, _ptr(expert_offsets), mode,
                                  _ptr(row_src), _ptr(a), _ptr(a_scale), a_rows, _ptr(w_gate_up), _ptr(w_gu_scale),
-                                 _ptr(h), _ptr(h_scale), _stream(stream)))
+                                 _ptr(h), _ptr(h_scale), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def moe_ffn_down(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_offsets, h, h_scale, w_down,
-                 w_d_scale, y, stream=None):
+                 w_d_scale, y, workspace=None, stream=None):
     d, I = shape.d, shape.inter
     _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(h, n_rows * I, "h")
     _need(w_down, n_experts * d * I, "w_down"); _need(y, n_rows * d, "y")
@@ -194,7 +194,8 @@ def moe_ffn_down(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_o
         _need(h_scale, n_rows * (I // 128), "h_scale")
         _need(w_d_scale, n_experts * (d // 128) * (I // 128), "w_d_scale")
     _check(lib().moe_ffn_down(ctypes.byref(shape), w, n_experts, n_rows, _ptr(expert_offsets), _ptr(h),
-                              _ptr(h_scale), _ptr(w_down), _ptr(w_d_scale), _dt(y), _ptr(y), _stream(stream)))
+                              _ptr(h_scale), _ptr(w_down), _ptr(w_d_scale), _dt(y), _ptr(y), _ptr(workspace),
+                              _nbytes(workspace), _stream(stream)))
 
 
 def moe_combine(shape: moe_shape, u, y_routed, row_of, topk_gate, y_shared, out, stream=None):

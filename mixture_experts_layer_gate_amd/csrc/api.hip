@@ -95,41 +95,23 @@ int device_cu_count() {
   return g_cu[dev];
 }
 
-int* unit_queue_slot() {
-  constexpr int kSlots = 64;
-  static std::mutex mu;
-  static int* bufs[64] = {};
-  static std::atomic<unsigned> next{0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  int* b;
-  {
-    std::lock_guard<std::mutex> lk(mu);
-    if (!bufs[dev]) {
-      void* p = nullptr;
-      const size_t bytes = sizeof(int) * kQueueInts * kSlots;
-      if (hipMalloc(&p, bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-      }
-      if (hipMemset(p, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-        (void)hipFree(p);
-        (void)hipGetLastError();
-        return nullptr;
-      }
-      bufs[dev] = static_cast<int*>(p);
-    }
-    b = bufs[dev];
-  }
-  return b + kQueueInts * (next.fetch_add(1, std::memory_order_relaxed) % kSlots);
+__global__ void queue_reset_kernel(int* q) {
+  if (threadIdx.x < kQueueInts) q[threadIdx.x] = 0;
 }
 
-size_t ffn_ws_bytes(moe_dtype w, int n_rows, int I) {
+hipError_t launch_queue_reset(int* q, hipStream_t st) {
+  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, st, q);
+  return hipGetLastError();
+}
+
+size_t ffn_queue_offset(moe_dtype w, int n_rows, int I) {
   const size_t n = static_cast<size_t>(n_rows) * I;
   if (w == MOE_F32) return align256(n * 4);
   if (w == MOE_BF16) return align256(n * 2);
   return align256(n) + align256(static_cast<size_t>(n_rows) * (I / 128) * 4);
 }
+
+size_t ffn_ws_bytes(moe_dtype w, int n_rows, int I) { return ffn_queue_offset(w, n_rows, I) + 2 * kFfnQueueBytes; }
 
 }  // namespace moe
 
@@ -280,10 +262,12 @@ moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_expert
   float* h_scale = nullptr;
   if (w == MOE_F8E4M3)
     h_scale = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(static_cast<size_t>(n_rows) * I));
+  int* queue = reinterpret_cast<int*>(static_cast<char*>(workspace) + moe::ffn_queue_offset(w, n_rows, I));
   moe::FfnArgs p{d, I, n_experts, n_rows, a_rows, expert_offsets, mode, row_src, a, a_scale, w_gate_up, w_gu_scale,
-                 w_down, w_d_scale, y_dtype, y, workspace, h_scale};
+                 w_down, w_d_scale, y_dtype, y, workspace, h_scale, queue};
   auto st = static_cast<hipStream_t>(stream);
   hipError_t e = run_gate_up(w, p, st);
+  p.queue = queue + moe::kFfnQueueBytes / sizeof(int);
   if (e == hipSuccess) e = run_down(w, p, st);
   return finish(e, "moe_grouped_ffn", st);
 }
@@ -291,30 +275,35 @@ moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_expert
 moe_status moe_ffn_gate_up(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                            const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src, const void* a,
                            const float* a_scale, int32_t a_rows, const void* w_gate_up, const float* w_gu_scale,
-                           void* h, float* h_scale, void* stream) {
+                           void* h, float* h_scale, void* workspace, size_t ws_bytes, void* stream) {
   g_err.clear();
   if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 1); r != MOE_OK) return r;
   if (moe_status r = check_gate_up(shape, w, mode, row_src, a, a_scale, a_rows, w_gate_up, w_gu_scale); r != MOE_OK)
     return r;
   REQUIRE(h != nullptr, "ffn_gate_up: h is NULL");
   REQUIRE(w != MOE_F8E4M3 || h_scale != nullptr, "ffn_gate_up: fp8 needs h_scale");
+  if (!workspace || ws_bytes < moe::kFfnQueueBytes)
+    return fail(MOE_E_WORKSPACE, "ffn_gate_up: workspace of %zu bytes < %zu needed", ws_bytes, moe::kFfnQueueBytes);
   moe::FfnArgs p{shape->d, shape->inter, n_experts, n_rows, a_rows, expert_offsets, mode, row_src, a, a_scale,
-                 w_gate_up, w_gu_scale, nullptr, nullptr, MOE_BF16, nullptr, h, h_scale};
+                 w_gate_up, w_gu_scale, nullptr, nullptr, MOE_BF16, nullptr, h, h_scale, static_cast<int*>(workspace)};
   auto st = static_cast<hipStream_t>(stream);
   return finish(run_gate_up(w, p, st), "moe_ffn_gate_up", st);
 }
 
 moe_status moe_ffn_down(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                         const int32_t* expert_offsets, const void* h, const float* h_scale, const void* w_down,
-                        const float* w_d_scale, moe_dtype y_dtype, void* y, void* stream) {
+                        const float* w_d_scale, moe_dtype y_dtype, void* y, void* workspace, size_t ws_bytes,
+                        void* stream) {
   g_err.clear();
   if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 2); r != MOE_OK) return r;
   if (moe_status r = check_down(w, w_down, w_d_scale, y_dtype, y); r != MOE_OK) return r;
   REQUIRE(h != nullptr, "ffn_down: h is NULL");
   REQUIRE(w != MOE_F8E4M3 || h_scale != nullptr, "ffn_down: fp8 needs h_scale");
+  if (!workspace || ws_bytes < moe::kFfnQueueBytes)
+    return fail(MOE_E_WORKSPACE, "ffn_down: workspace of %zu bytes < %zu needed", ws_bytes, moe::kFfnQueueBytes);
   moe::FfnArgs p{shape->d, shape->inter, n_experts, n_rows, n_rows, expert_offsets, MOE_ROWS_DIRECT, nullptr,
                  nullptr, nullptr, nullptr, nullptr, w_down, w_d_scale, y_dtype, y, const_cast<void*>(h),
-                 const_cast<float*>(h_scale)};
+                 const_cast<float*>(h_scale), static_cast<int*>(workspace)};
   auto st = static_cast<hipStream_t>(stream);
   return finish(run_down(w, p, st), "moe_ffn_down", st);
 }

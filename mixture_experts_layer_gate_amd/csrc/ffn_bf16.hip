@@ -191,8 +191,8 @@ static void set_lds_limits() {
 
 hipError_t launch_ffn_bf16_gate_up(const FfnArgs& p, hipStream_t st) {
   set_lds_limits();
-  int* q = unit_queue_slot();
-  if (!q) return hipErrorOutOfMemory;
+  int* q = p.queue;
+  if (hipError_t e = launch_queue_reset(q, st); e != hipSuccess) return e;
   const size_t lds = FP::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / FP::BT + p.n_experts;
   const int g1 = persistent_grid(mblocks * (p.I / kHcols), 1);
@@ -204,8 +204,8 @@ hipError_t launch_ffn_bf16_gate_up(const FfnArgs& p, hipStream_t st) {
 
 hipError_t launch_ffn_bf16_down(const FfnArgs& p, hipStream_t st) {
   set_lds_limits();
-  int* q = unit_queue_slot();
-  if (!q) return hipErrorOutOfMemory;
+  int* q = p.queue;
+  if (hipError_t e = launch_queue_reset(q, st); e != hipSuccess) return e;
   const size_t lds = FP::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / FP::BT + p.n_experts;
   const int g2 = persistent_grid(mblocks * (p.d / FP::BW), 1);

@@ -276,8 +276,8 @@ static void f8_set_lds_limits() {
 hipError_t launch_ffn_fp8_gate_up(const FfnArgs& p, hipStream_t st) {
   if (p.n_experts > kMaxExperts8) return hipErrorInvalidValue;
   f8_set_lds_limits();
-  int* q = unit_queue_slot();
-  if (!q) return hipErrorOutOfMemory;
+  int* q = p.queue;
+  if (hipError_t e = launch_queue_reset(q, st); e != hipSuccess) return e;
   const size_t lds = P8::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / P8::BT + p.n_experts;
   hipLaunchKernelGGL(ffn_gate_up_fp8_kernel, dim3(f8_grid(mblocks * cdiv(p.I / 128, P8::MAX_SEG))), dim3(P8::NT), lds,
@@ -291,8 +291,8 @@ hipError_t launch_ffn_fp8_gate_up(const FfnArgs& p, hipStream_t st) {
 hipError_t launch_ffn_fp8_down(const FfnArgs& p, hipStream_t st) {
   if (p.n_experts > kMaxExperts8) return hipErrorInvalidValue;
   f8_set_lds_limits();
-  int* q = unit_queue_slot();
-  if (!q) return hipErrorOutOfMemory;
+  int* q = p.queue;
+  if (hipError_t e = launch_queue_reset(q, st); e != hipSuccess) return e;
   const size_t lds = P8::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / P8::BT + p.n_experts;
   hipLaunchKernelGGL(ffn_down_fp8_kernel, dim3(f8_grid(mblocks * cdiv(p.d / P8::BW, P8::MAX_SEG))), dim3(P8::NT), lds,

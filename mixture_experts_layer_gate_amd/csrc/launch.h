@@ -21,12 +21,9 @@ inline Shape to_shape(const moe_shape& s) {
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
-// Counters for one launch of a grouped FFN kernel's dynamic unit queue
-// (sched.h): the next of 64 zeroed slots of a buffer the library allocates on
-// the current device at its first use; null if that allocation fails. Each
-// launch leaves its slot zeroed, so up to 64 such launches may run at once
-// on one device.
-int* unit_queue_slot();
+// Zero the kQueueInts counters of a grouped FFN launch's unit queue
+// (sched.h) on st, with a kernel (graph-capture safe).
+hipError_t launch_queue_reset(int* q, hipStream_t st);
 
 // ---- route
 // workspace: the scores [T, N] fp32 (used when the caller passes none), then
@@ -66,7 +63,12 @@ struct FfnArgs {
   void* y;
   void* h;         // SwiGLU output [n_rows, I]
   float* h_scale;  // fp8: [n_rows, I/128]
+  int* queue;      // unit-queue counters of this launch (kQueueInts ints of workspace)
 };
+constexpr size_t kFfnQueueBytes = 128;   // per launch
+// Workspace of moe_grouped_ffn: H (+ its fp8 scales), then the queue
+// counters of the gate/up and the down launch at ffn_queue_offset.
+size_t ffn_queue_offset(moe_dtype w, int n_rows, int I);
 size_t ffn_ws_bytes(moe_dtype w, int n_rows, int I);
 hipError_t launch_ffn_f32_gate_up(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_f32_down(const FfnArgs& a, hipStream_t st);

@@ -144,10 +144,10 @@ __device__ __forceinline__ int xcd_virtual_block() {
   return (b & 7) * (G >> 3) + (b >> 3);
 }
 
-// Counters of one launch: q[0..7] units taken from each XCD range, q[8]
-// workgroups done. They start at zero; the last workgroup to run out of
-// units puts them back to zero for the next launch that uses this slot.
-constexpr int kQueueInts = 32;   // ints per slot (128 bytes)
+// Counters of one launch: q[x] = units taken so far from XCD range x. They
+// live in the caller's workspace and are zeroed (launch_queue_reset) on the
+// same stream right before the launch.
+constexpr int kQueueInts = 32;   // ints per launch (128 bytes)
 
 // Next unit for this workgroup, or -1 when every range is exhausted. Every
 // thread of the block calls it; x_off (the ranges this workgroup has
@@ -168,10 +168,6 @@ __device__ __forceinline__ int unit_queue_next(int* __restrict__ q, int total, i
         }
       }
       ++x_off;
-    }
-    if (t < 0 && atomicAdd(&q[8], 1) == static_cast<int>(gridDim.x) - 1) {
-      // every workgroup has stopped taking units: reset for the next launch
-      for (int x = 0; x < 9; ++x) atomicExch(&q[x], 0);
     }
     *slot = t;
   }

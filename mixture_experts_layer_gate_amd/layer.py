@@ -165,11 +165,11 @@ class MoELayer:
         E = c.n_routed + c.n_shared
         B.moe_ffn_gate_up(self.shape, self.gemm, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all,
                           a, a_scale, c.T, self.w["all_gate_up"], self.w.get("all_gate_up_scale"), self.h_all,
-                          self.h_all_scale)
+                          self.h_all_scale, self.ws)
         if between is not None:
             between()
         B.moe_ffn_down(self.shape, self.gemm, E, n_rows, self.offsets_all, self.h_all, self.h_all_scale,
-                       self.w["all_down"], self.w.get("all_down_scale"), self.y_all)
+                       self.w["all_down"], self.w.get("all_down_scale"), self.y_all, self.ws)
 
     def ffn_routed(self, u):
         c = self.cfg
@@ -204,11 +204,11 @@ class MoELayer:
             a, a_rows, mode = self.a_perm, n_rows, B.MOE_ROWS_DIRECT
         B.moe_ffn_gate_up(self.shape, self.gemm, c.n_routed, n_rows, self.expert_offsets, mode,
                           self.perm_token if mode == B.MOE_ROWS_GATHER else None, a, a_scale, a_rows,
-                          self.w["w_gate_up"], self.w.get("w_gate_up_scale"), self.h, self.h_scale)
+                          self.w["w_gate_up"], self.w.get("w_gate_up_scale"), self.h, self.h_scale, self.ws)
         if between is not None:
             between()
         B.moe_ffn_down(self.shape, self.gemm, c.n_routed, n_rows, self.expert_offsets, self.h, self.h_scale,
-                       self.w["w_down"], self.w.get("w_down_scale"), self.y_routed)
+                       self.w["w_down"], self.w.get("w_down_scale"), self.y_routed, self.ws)
 
     def ffn_shared(self, u):
         c = self.cfg

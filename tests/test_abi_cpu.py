@@ -66,6 +66,20 @@ def test_route_rejects_null_and_missing_workspace():
     assert st == B.MOE_E_INVALID and "NULL" in msg
     st, msg = _route(_shape(), s=None)   # no scores buffer and no workspace
     assert st == B.MOE_E_WORKSPACE and "workspace" in msg
+    st, msg = _route(_shape())           # scores given: the K-slice partial sums still need the workspace
+    assert st == B.MOE_E_WORKSPACE and "workspace" in msg
+
+
+def test_ffn_phases_need_queue_workspace():
+    """The split FFN calls take their work-queue counters from the caller's workspace (no allocation)."""
+    L = B.lib()
+    sh = _shape()
+    for ws, nb in ((None, 0), (FAKE, 64)):
+        assert L.moe_ffn_gate_up(ctypes.byref(sh), B.MOE_BF16, 4, 10, FAKE, B.MOE_ROWS_DIRECT, None, FAKE, None, 10,
+                                 FAKE, None, FAKE, None, ws, nb, None) == B.MOE_E_WORKSPACE
+        assert b"workspace" in L.moe_last_error()
+        assert L.moe_ffn_down(ctypes.byref(sh), B.MOE_BF16, 4, 10, FAKE, FAKE, None, FAKE, None, B.MOE_BF16, FAKE,
+                              ws, nb, None) == B.MOE_E_WORKSPACE
 
 
 def test_grouped_ffn_validation():

@@ -442,8 +442,9 @@ def test_grouped_ffn_fp8_tile_shapes(inter, mode):
         a, a_s, a_rows, rmode, rsrc = dev8(uq), dev8(us), cfg.T, B.MOE_ROWS_GATHER, _i32(src)
     else:
         a, a_s, a_rows, rmode, rsrc = dev8(uq[src]), dev8(us[src]), n, B.MOE_ROWS_DIRECT, None
-    B.moe_ffn_gate_up(sh, B.MOE_F8E4M3, cfg.n_routed, n, _i32(off), rmode, rsrc, a, a_s, a_rows, wgu, wgs, h, hs)
-    B.moe_ffn_down(sh, B.MOE_F8E4M3, cfg.n_routed, n, _i32(off), h, hs, wdn, wds, y)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    B.moe_ffn_gate_up(sh, B.MOE_F8E4M3, cfg.n_routed, n, _i32(off), rmode, rsrc, a, a_s, a_rows, wgu, wgs, h, hs, ws)
+    B.moe_ffn_down(sh, B.MOE_F8E4M3, cfg.n_routed, n, _i32(off), h, hs, wdn, wds, y, ws)
     torch.cuda.synchronize()
     for e in range(cfg.n_routed):
         lo, hi = off[e], off[e + 1]
