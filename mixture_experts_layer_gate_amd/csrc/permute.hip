@@ -43,17 +43,32 @@ __global__ __launch_bounds__(256) void perm_mask_kernel(int T, int K, int N, con
     for (int e = lane; e < N; e += kWave) masks[static_cast<size_t>(c) * N + e] = m[e];
 }
 
-// One block of 1024 threads; thread e owns expert e (N <= 1024).
+// One block of 1024 threads. Thread (p, e) = (tid / N, tid % N) counts expert
+// e's pairs over the p-th of P = 1024 / N runs of chunks (N <= 1024), so the
+// chunk loop is P times shorter than with one thread per expert; the run
+// sums give each run's start, and an exclusive scan of the expert totals
+// gives the offsets.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int N, const unsigned long long* __restrict__ masks,
                                                          int32_t* __restrict__ base, int32_t* __restrict__ offsets) {
+  __shared__ int run_cnt[1024];
   __shared__ int wsum[16];
-  const int e = threadIdx.x;
+  const int tid = threadIdx.x;
   const int nch = cdiv(T, kChunk);
+  const int P = 1024 / N;
+  const int e = tid % N, p = tid / N;
+  const bool act = p < P;
+  const int c0 = act ? static_cast<int>(static_cast<long long>(p) * nch / P) : 0;
+  const int c1 = act ? static_cast<int>(static_cast<long long>(p + 1) * nch / P) : 0;
+  int cnt = 0;
+#pragma unroll 8
+  for (int c = c0; c < c1; ++c) cnt += __popcll(masks[static_cast<size_t>(c) * N + e]);
+  if (act) run_cnt[tid] = cnt;
+  __syncthreads();
+  // expert totals (threads e < N), then the exclusive scan over experts
   int total = 0;
-  if (e < N)
-    for (int c = 0; c < nch; ++c) total += __popcll(masks[static_cast<size_t>(c) * N + e]);
-  // exclusive block scan of total over e
-  const int lane = e & 63, w = e >> 6;
+  if (tid < N)
+    for (int q = 0; q < P; ++q) total += run_cnt[q * N + tid];
+  const int lane = tid & 63, w = tid >> 6;
   int incl = total;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -65,11 +80,22 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int N, const uns
   int before = 0;
   for (int i = 0; i < w; ++i) before += wsum[i];
   const int excl = before + incl - total;
-  if (e < N) {
-    offsets[e] = excl;
-    if (e == N - 1) offsets[N] = excl + total;
+  if (tid < N) {
+    offsets[tid] = excl;
+    if (tid == N - 1) offsets[N] = excl + total;
+    // start of run q of expert tid, written over its count
     int run = excl;
-    for (int c = 0; c < nch; ++c) {
+    for (int q = 0; q < P; ++q) {
+      const int c = run_cnt[q * N + tid];
+      run_cnt[q * N + tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (act) {
+    int run = run_cnt[tid];
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) {
       base[static_cast<size_t>(c) * N + e] = run;
       run += __popcll(masks[static_cast<size_t>(c) * N + e]);
     }

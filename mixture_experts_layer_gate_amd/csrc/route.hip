@@ -237,6 +237,179 @@ size_t route_ws_bytes(const Shape& s, moe_dtype act) {
   return scores + S * s.T * s.N * sizeof(float);
 }
 
+// Register form of the selection, for shapes where each lane can own V
+// consecutive experts and a group is a power-of-two run of whole lanes
+// (S % V == 0, S / V a power of two <= 64; or no group limit). One wavefront
+// per token, no LDS staging: each lane keeps its V biased scores, the group
+// score comes from a butterfly merge of the lanes' top-4 lists, and each of
+// the M group and K expert picks is a wave argmax. Same order of operations
+// and tie rules as route_select_kernel.
+// Insert v into the descending list a0 >= a1 >= a2 >= a3 (the largest four
+// stay), as a min/max bubble: no branches, no indexed registers.
+__device__ __forceinline__ void top4_insert(float v, float& a0, float& a1, float& a2, float& a3) {
+  float t = fminf(a0, v);
+  a0 = fmaxf(a0, v);
+  const float t1 = fminf(a1, t);
+  a1 = fmaxf(a1, t);
+  const float t2 = fminf(a2, t1);
+  a2 = fmaxf(a2, t1);
+  a3 = fmaxf(a3, t2);
+}
+
+template <int V>
+__global__ __launch_bounds__(256) void route_select_reg_kernel(Shape s, const float* __restrict__ part, int S_part,
+                                                               float* __restrict__ scores,
+                                                               const float* __restrict__ bias,
+                                                               int32_t* __restrict__ idx, float* __restrict__ gate) {
+  const int N = s.N, G = s.G, M = s.M, K = s.K, topn = s.topn;
+  const int S = N / G;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool grouped = G > 1 && M < G;
+  const int lpg = grouped ? S / V : 64;          // lanes per group
+  const int my_group = grouped ? lane / lpg : 0;
+  const int e0 = lane * V;
+  float b[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) b[v] = e0 + v < N ? bias[e0 + v] : 0.0f;
+
+  for (int t = blockIdx.x * 4 + w; t < s.T; t += gridDim.x * 4) {
+    float sr[V], sb[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = e0 + v;
+      if (e < N) {
+        float x;
+        if (part) {
+          x = part[static_cast<size_t>(t) * N + e];
+          for (int p = 1; p < S_part; ++p) x += part[(static_cast<size_t>(p) * s.T + t) * N + e];
+          x = 1.0f / (1.0f + expf(-x));
+          scores[static_cast<size_t>(t) * N + e] = x;
+        } else {
+          x = scores[static_cast<size_t>(t) * N + e];
+        }
+        sr[v] = x;
+        sb[v] = x + b[v];
+      } else {
+        sr[v] = 0.0f;
+        sb[v] = -INFINITY;
+      }
+    }
+    uint64_t keep = ~0ull;
+    if (grouped) {
+      float a0 = -INFINITY, a1 = -INFINITY, a2 = -INFINITY, a3 = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < V; ++v) top4_insert(sb[v], a0, a1, a2, a3);
+      for (int o = 1; o < lpg; o <<= 1) {
+        const float c0 = __shfl_xor(a0, o, kWave), c1 = __shfl_xor(a1, o, kWave);
+        const float c2 = __shfl_xor(a2, o, kWave), c3 = __shfl_xor(a3, o, kWave);
+        top4_insert(c0, a0, a1, a2, a3);
+        top4_insert(c1, a0, a1, a2, a3);
+        top4_insert(c2, a0, a1, a2, a3);
+        top4_insert(c3, a0, a1, a2, a3);
+      }
+      float gs = a0;                                 // summed from the largest down, in fp32
+      if (topn > 1) gs = gs + a1;
+      if (topn > 2) gs = gs + a2;
+      if (topn > 3) gs = gs + a3;
+      if (my_group >= G) gs = -INFINITY;
+      keep = 0ull;
+      for (int m = 0; m < M; ++m) {
+        const bool open = my_group < G && !((keep >> my_group) & 1ull);
+        float v = open ? gs : -INFINITY;
+        int id = open ? my_group : INT_MAX;
+        argmax_pair(v, id);
+        if (id < 64) keep |= 1ull << id;
+      }
+      if (!((keep >> (my_group < 64 ? my_group : 0)) & 1ull) || my_group >= G) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) sb[v] = -INFINITY;
+      }
+    }
+    int my_pick = -1;
+    for (int k = 0; k < K; ++k) {
+      float bv = -INFINITY;
+      int be = INT_MAX;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (sb[v] > bv) { bv = sb[v]; be = e0 + v; }
+      argmax_pair(bv, be);
+      if (lane == k) my_pick = be < N ? be : -1;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (e0 + v == be) sb[v] = -INFINITY;
+    }
+    // ascending expert order; gates over the raw affinities of the picks
+    float my_s = 0.0f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      // lane k fetches the raw score of its pick from the owner lane
+      const int owner = my_pick >= 0 ? my_pick / V : lane;
+      const float cand = __shfl(sr[v], owner, kWave);
+      if (my_pick >= 0 && my_pick - owner * V == v) my_s = cand;
+    }
+    int rank = 0;
+    float sum = 0.0f;
+    for (int j = 0; j < K; ++j) {
+      const int pj = __shfl(my_pick, j, kWave);
+      sum += __shfl(my_s, j, kWave);
+      rank += (pj < my_pick) ? 1 : 0;
+    }
+    if (lane < K) {
+      idx[static_cast<size_t>(t) * K + rank] = my_pick;
+      gate[static_cast<size_t>(t) * K + rank] = my_s / sum;
+    }
+  }
+}
+
+// Expert-load histogram of the selections: a few blocks, each an LDS
+// histogram of a contiguous run of topk_idx, added into load (zeroed by the
+// logits kernel) -- one global atomic per expert and block.
+__global__ __launch_bounds__(1024) void route_hist_kernel(long long n, int N, const int32_t* __restrict__ idx,
+                                                          int32_t* __restrict__ load) {
+  __shared__ int hist[1024];
+  for (int e = threadIdx.x; e < N; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const long long lo = n * blockIdx.x / gridDim.x, hi = n * (blockIdx.x + 1) / gridDim.x;
+  for (long long i = lo + threadIdx.x; i < hi; i += blockDim.x) {
+    const int e = idx[i];
+    if (e >= 0 && e < N) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    const int c = hist[e];
+    if (c) atomicAdd(&load[e], c);
+  }
+}
+
+// Experts per lane for the register selection, or 0 when the shape needs the
+// LDS form.
+static int select_lanes_v(const Shape& s) {
+  const bool grouped = s.G > 1 && s.M < s.G;
+  const int S = s.N / s.G;
+  for (int V = cdiv(s.N, 64); V <= 16; ++V) {
+    if (!grouped) return V;
+    if (S % V) continue;
+    const int lpg = S / V;
+    if (lpg <= 64 && (lpg & (lpg - 1)) == 0) return V;
+  }
+  return 0;
+}
+
+template <int V>
+static hipError_t launch_select_reg(const Shape& s, const float* part, int S, float* scores, const float* bias,
+                                    int32_t* idx, float* gate, int32_t* load, hipStream_t st) {
+  int blocks = cdiv(s.T, 4);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(route_select_reg_kernel<V>, dim3(blocks), dim3(256), 0, st, s, part, S, scores, bias, idx, gate);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long n = static_cast<long long>(s.T) * s.K;
+  long long hb = (n + 16383) / 16384;
+  hb = hb < 1 ? 1 : (hb > 64 ? 64 : hb);
+  hipLaunchKernelGGL(route_hist_kernel, dim3(static_cast<unsigned>(hb)), dim3(1024), 0, st, n, s.N, idx, load);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const Shape& s, moe_dtype act, const void* u, const void* cent, const float* bias,
                         int32_t* idx, float* gate, int32_t* load, float* scores, void* ws, hipStream_t st) {
   const float* part = nullptr;
@@ -273,6 +446,15 @@ hipError_t launch_route(const Shape& s, moe_dtype act, const void* u, const void
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  switch (select_lanes_v(s)) {
+#define MOE_SEL_CASE(V) \
+  case V: return launch_select_reg<V>(s, part, S, scores, bias, idx, gate, load, st);
+    MOE_SEL_CASE(1) MOE_SEL_CASE(2) MOE_SEL_CASE(3) MOE_SEL_CASE(4) MOE_SEL_CASE(5) MOE_SEL_CASE(6)
+    MOE_SEL_CASE(7) MOE_SEL_CASE(8) MOE_SEL_CASE(9) MOE_SEL_CASE(10) MOE_SEL_CASE(11) MOE_SEL_CASE(12)
+    MOE_SEL_CASE(13) MOE_SEL_CASE(14) MOE_SEL_CASE(15) MOE_SEL_CASE(16)
+#undef MOE_SEL_CASE
+    default: break;
+  }
   const size_t lds = sizeof(float) * (static_cast<size_t>(s.N) + 2 * kSelWaves * static_cast<size_t>(s.N));
   int blocks = cdiv(s.T, kSelWaves);
   if (blocks > 8192) blocks = 8192;

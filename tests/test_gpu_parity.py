@@ -54,7 +54,10 @@ ROUTE_CASES = [
     ("c2", dict(n_groups=1, topk_groups=1)),           # no group limit
     ("c2", dict(topk_groups=8)),                        # every group kept
     ("c2", dict(T=1000, n_groups=4, topk_groups=1, topk=3, group_topn=3)),  # ragged T, 3-term group score
+    ("c2", dict(n_routed=96, n_groups=8, topk_groups=3)),   # 3 experts per lane, 4-lane groups
+    ("c2", dict(n_routed=68, n_groups=4, topk_groups=2)),   # 17-expert groups: the LDS form of the selection
     ("c3", {}),
+    ("c5", {}),                                             # 384 experts, no group limit: 6 per lane
 ]
 
 
