@@ -43,15 +43,22 @@ def parse():
     return ap.parse_args()
 
 
-FFN_SOURCES = ["ffn_bf16.hip", "gemm_pipe.h", "sched.h", "common.h"]
+FFN_SOURCES = {"bf16": ["ffn_bf16.hip", "gemm_pipe.h", "sched.h", "common.h"],
+               "fp8": ["ffn_fp8.hip", "gemm_pipe8.h", "gemm_pipe.h", "sched.h", "common.h"]}
 
 
-def recorded_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, if the kernel is unchanged since."""
+def sources_hash(gemm: str) -> str:
+    """First 16 hex digits of the sha256 of the grouped-FFN kernel sources of this GEMM dtype."""
     import hashlib
-    import re
     csrc = os.path.join(ROOT, "mixture_experts_layer_gate_amd", "csrc")
-    h = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in FFN_SOURCES)).hexdigest()[:16]
+    files = FFN_SOURCES.get(gemm, [])
+    return hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in files)).hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: str, gemm: str):
+    """HBM bytes per launch from the committed counter summary, if the kernel is unchanged since."""
+    import re
+    h = sources_hash(gemm)
     pdir = os.path.join(ROOT, "profiles")
     for name in (sorted(os.listdir(pdir)) if os.path.isdir(pdir) else []):
         for line in open(os.path.join(ROOT, "profiles", name)):
@@ -177,7 +184,7 @@ def main():
         roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": MFMA_PEAK[cfg.gemm] / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = recorded_traffic(f"ffn_gate_up_{cfg.gemm} routed+shared", cfg.name)
+    roof["traffic"] = recorded_traffic(f"ffn_gate_up_{cfg.gemm} routed+shared", cfg.name, cfg.gemm)
     roof["kernel"] = "ffn_gate_up (routed + shared experts)"
     roof["mfma_frac"] = gu_flops / gu_s / MFMA_PEAK[cfg.gemm]
 
