@@ -144,7 +144,7 @@ __device__ __forceinline__ void pipe_mma_loads(const PipeFrags<P, MS>& f, f32x16
   for (int m = 0; m < (M > L ? M : L); ++m) {
 #pragma unroll
     for (int q = 0; q < L; ++q)
-      if ((M == 0 && q == m) || (M > 0 && q * M / L == m)) {
+      if ((M == 0 && q == m) || (M > 0 && q * M / (L > 0 ? L : 1) == m)) {
         pipe_issue_one<P, PART == 1>(r, st, kb, q);
         sched_fence();
       }

@@ -1,21 +1,25 @@
-// Pipelined E4M3 MFMA main loop with per-128 fp32 promotion, for the fp8
-// expert GEMMs ("DeepSeek_V3_Report: Annotation", sections "Fine-Grained
-// Quantization" and "Increasing Accumulation Precision").
+// Pipelined E4M3 MFMA main loop with the scales applied per 128-wide K
+// chunk, for the fp8 expert GEMMs ("DeepSeek_V3_Report: Annotation",
+// sections "Fine-Grained Quantization" and "Increasing Accumulation
+// Precision").
 //
 // Operands are E4M3 codes: weights with one fp32 scale per 128x128 block,
-// tokens with one fp32 scale per 1x128 tile. Every 128-wide K chunk c is
-// accumulated raw -- two v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0
-// scales into a temporary T (the first with C = 0) -- and then promoted into
-// the fp32 accumulator: acc += T * (s_token[n, c] * s_weight[block, c]).
-// gfx950's block-scaled MFMA takes power-of-two scales only, so the fp32
-// scales are applied on the VALU: the accumulator lives in VGPRs, T (the
-// MFMA destination) in AGPRs.
+// tokens with one fp32 scale per 1x128 tile, so output element (w, n) needs
+// y = sum over chunks c of f_c * raw_c with f_c = s_token[n, c] *
+// s_weight[block(w), c] and raw_c the chunk's code dot product. gfx950's
+// block-scaled MFMA takes power-of-two scales only, so the fp32 factors are
+// applied on the VALU; its MFMA accumulates fp8 products in fp32, so no
+// separate low-precision partial sum needs promoting. The accumulator is kept
+// in the frame of the current chunk, acc = (sum over c' <= c of f_c' *
+// raw_c') / f_c: the two v_mfma_scale_f32_32x32x64_f8f6f4 of chunk c add raw_c
+// to it directly, and between chunks it is multiplied by f_c / f_{c+1} (one
+// VALU multiply per element per chunk); the epilogue multiplies by the last
+// chunk's factor. Factors below 1e-20 are raised to 1e-20 so the frame never
+// overflows; that changes no output by more than about 3e-13.
 //
 // Tile: BW = 256 weight rows x BT = 128 token rows, four waves (one per
 // SIMD) in a 2 x 2 grid of 128 x 64: TW = 4 weight sub-tiles x up to 2 token
-// sub-tiles of 32x32; a wave holds 128 accumulator VGPRs and 128 temporary
-// AGPRs (the fragments share the AGPRs). A 256 x 256 tile would need twice
-// the register file.
+// sub-tiles of 32x32, 128 accumulator VGPRs per wave.
 // Weight and token rows stream into LDS with buffer_load ... lds through a
 // ring of four stages of 64 K-bytes (one MFMA K-step), rows of 64 bytes
 // XOR-swizzled as in the bf16 loop. The tile's token scales (128 rows x all
@@ -25,12 +29,13 @@
 //
 // Iteration kt (stage kt, chunk kt / 2): wait until stage kt+1 has landed +
 // barrier; read stage kt+1's fragments; the MFMAs of stage kt with the loads
-// of stage kt+3 spread among them. In a chunk's first stage each element of
-// T is promoted (chunk c-1, whose MFMAs were issued a block earlier) just
-// before the C = 0 MFMA that restarts it; the second stage prepares the
-// promotion factors of its chunk. A unit streams up to MAX_SEG blocks of
-// output columns that share its token rows as one sequence of stages, so
-// the ring's fill and drain and the unit's setup are paid once per unit.
+// of stage kt+3 spread among them. A chunk's second stage computes the next
+// chunk's factors and moves each accumulator tile to the next frame two MFMAs
+// after its last MFMA of the chunk (the last two tiles at the start of the
+// next stage), so the multiplies run beside the MFMAs. A unit streams up to
+// MAX_SEG blocks of output columns that share its token rows as one sequence
+// of stages, so the ring's fill and drain and the unit's setup are paid once
+// per unit.
 #pragma once
 
 #include "common.h"
@@ -152,80 +157,58 @@ __device__ __forceinline__ void pipe8_read(Pipe8Frags<MS>& f, const uint8_t* st)
   for (int i = 0; i < MS; ++i) f.t[i] = pipe8_frag(st + Pipe8::W_BYTES, 32 * (2 * i + wt) + (l & 31));
 }
 
-// One element of an MFMA result, read out of its AGPR at the promotion and
-// not earlier (with a plain use the register allocator copies all of T into
-// VGPRs at the top of the block). The MFMA that wrote the value was issued a
-// whole block (MFMAs, a barrier and the loads) before this read, far beyond
-// the wait states the read needs after an MFMA. Using an AGPR operand also
-// keeps the compiler on the AGPR form of the scaled MFMA: in the VGPR form it
-// has placed the destination over the instruction's own scale and A operands.
-__device__ __forceinline__ float agpr_read(float x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  float r;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
-  return r;
-#else
-  return x;
-#endif
-}
-
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// An empty use of the fragments after the last MFMA that reads them: while
-// they are live no MFMA destination can be allocated on top of them (the
-// compiler otherwise places a restarted T over the A/B fragments of its own
-// scaled MFMA, which this code does not rely on being safe).
+constexpr float kMinFactor = 1e-20f;
+
+// Accumulator tile t = (j, i) = (t / MS, t % MS) moved to the next chunk's frame.
 template <int MS>
-__device__ __forceinline__ void pipe8_hold(const Pipe8Frags<MS>& f) {
-#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ void pipe8_rescale(f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
+                                              const float (&r)[Pipe8::TW][Pipe8::TT], int t) {
+  constexpr int D = MS > 0 ? MS : 1;
+  const int j = t / D, i = t % D;
 #pragma unroll
-  for (int j = 0; j < Pipe8::TW; ++j) asm volatile("" ::"a"(f.w[j]));
-#pragma unroll
-  for (int i = 0; i < MS; ++i) asm volatile("" ::"a"(f.t[i]));
-#endif
+  for (int v = 0; v < 16; ++v) acc[j][i][v] *= r[j][i];
 }
 
-// The MFMAs of one stage (fragments f), token sub-tile i fastest, with the
-// loads of stage `ls` spread among them (load q before MFMA q * M / LPS) when
-// ISSUE, and, for a chunk's first stage (PROMOTE), the previous chunk's
-// T[j][i] promoted just before the C = 0 MFMA that restarts it (FIRST: T
-// restarts from 0).
-template <int MS, int LT, bool FIRST, bool PROMOTE, bool ISSUE>
-__device__ __forceinline__ void pipe8_block(const Pipe8Frags<MS>& f, f32x16 (&T)[Pipe8::TW][Pipe8::TT],
-                                            f32x16 (&acc)[Pipe8::TW][Pipe8::TT], const float (&fac)[Pipe8::TW][Pipe8::TT],
-                                            const Pipe8Rows& rows, uint8_t* lds, int ls, Pipe8Off lo) {
+// The MFMAs of one stage (fragments f), tile m = (m / MS, m % MS) in order,
+// with the loads of stage `ls` spread among them (load q before MFMA
+// q * M / LPS) when ISSUE. SECOND (a chunk's second stage): tile m - 2 moves
+// to the next frame right after MFMA m; otherwise (a chunk's first stage)
+// tiles M - 2 and M - 1, whose last MFMAs closed the previous stage, move
+// before MFMAs 0 and 1.
+template <int MS, int LT, bool SECOND, bool ISSUE>
+__device__ __forceinline__ void pipe8_block(const Pipe8Frags<MS>& f, f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
+                                            const float (&r)[Pipe8::TW][Pipe8::TT], const Pipe8Rows& rows,
+                                            uint8_t* lds, int ls, Pipe8Off lo) {
   using P = Pipe8;
-  constexpr int M = P::TW * MS;
+  constexpr int M = P::TW * MS, D = MS > 0 ? MS : 1;
   constexpr int L = ISSUE ? P::WL + LT : 0;      // weight loads, then LT token load groups
   uint8_t* st = lds + (ls & 3) * P::STAGE;
 #pragma unroll
   for (int m = 0; m < (M > L ? M : L); ++m) {
 #pragma unroll
     for (int q = 0; q < L; ++q)
-      if ((M == 0 && q == m) || (M > 0 && q * M / L == m)) {
+      if ((M == 0 && q == m) || (M > 0 && q * M / (L > 0 ? L : 1) == m)) {
         pipe8_issue_one(rows, st, lo, q);
         sched_fence();
       }
     if (m < M) {
-      const int j = m / MS, i = m % MS;
-      if (PROMOTE) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[j][i][v] = fmaf(agpr_read(T[j][i][v]), fac[j][i], acc[j][i][v]);
-      }
-      T[j][i] = mfma_f8(f.w[j], f.t[i], FIRST ? f32x16{} : T[j][i]);
-      sched_fence();   // keeps each promotion beside its MFMA
+      if (!SECOND && m < 2) pipe8_rescale<MS>(acc, r, M - 2 + m);
+      acc[m / D][m % D] = mfma_f8(f.w[m / D], f.t[m % D], acc[m / D][m % D]);
+      if (SECOND && m >= 2) pipe8_rescale<MS>(acc, r, m - 2);
+      sched_fence();
     }
   }
-  pipe8_hold(f);
   sched_fence();
 }
 
-// Promotion factors of chunk c: token scale of this lane's row of sub-tile i
-// times the weight-block scale of sub-tile j (gate/up tiles: block row 0 for
-// the gate sub-tiles j < TW / 2, 1 for the up sub-tiles; down tiles: the
-// 128-row block of this wave's rows).
+// Factors of chunk c of output-column block seg: token scale of this lane's
+// row of sub-tile i times the weight-block scale of sub-tile j (gate/up
+// tiles: block row 0 for the gate sub-tiles j < TW / 2, 1 for the up
+// sub-tiles; down tiles: the 128-row block of this wave's rows).
 template <int MS, bool GATE_UP>
 __device__ __forceinline__ void pipe8_factors(float (&fac)[Pipe8::TW][Pipe8::TT], const uint8_t* lds, int kc_pad,
                                               int c, int seg) {
@@ -237,68 +220,76 @@ __device__ __forceinline__ void pipe8_factors(float (&fac)[Pipe8::TW][Pipe8::TT]
     const float sa = sat[(32 * (2 * i + wt) + (l & 31)) * kc_pad + c];
 #pragma unroll
     for (int j = 0; j < Pipe8::TW; ++j)
-      fac[j][i] = sa * swt[(GATE_UP ? (j >= Pipe8::TW / 2 ? 1 : 0) : p8_ww()) * Pipe8::MAX_CHUNKS + c];
+      fac[j][i] = fmaxf(sa * swt[(GATE_UP ? (j >= Pipe8::TW / 2 ? 1 : 0) : p8_ww()) * Pipe8::MAX_CHUNKS + c],
+                        kMinFactor);
   }
+}
+
+// Frame change into chunk c + 1 of the same block (r = f_c / f_{c+1}, fac
+// becomes f_{c+1}), or r = 1 when c is the block's last chunk (fac stays f_c
+// for the epilogue).
+template <int MS, bool GATE_UP>
+__device__ __forceinline__ void pipe8_next_frame(float (&fac)[Pipe8::TW][Pipe8::TT], float (&r)[Pipe8::TW][Pipe8::TT],
+                                                 const uint8_t* lds, int kc_pad, int c, int nchunks, int seg) {
+  const bool next = c + 1 < nchunks;
+  float fn[Pipe8::TW][Pipe8::TT];
+  pipe8_factors<MS, GATE_UP>(fn, lds, kc_pad, next ? c + 1 : c, seg);
+#pragma unroll
+  for (int j = 0; j < Pipe8::TW; ++j)
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      r[j][i] = next ? fac[j][i] * __builtin_amdgcn_rcpf(fn[j][i]) : 1.0f;
+      fac[j][i] = fn[j][i];
+    }
 }
 
 // One stage of the stream (global index g, local index kt within its
 // output-column block seg) that is not the stream's last: fa holds its
 // fragments, fb receives stage g+1's. WAIT: loads allowed in flight at the
 // barrier (one stage's while stage g+2 exists, else 0); ISSUE: load stage g+3.
-// A chunk's first stage promotes the previous chunk with fac (zero at a
-// block's first chunk, so T * 0 adds nothing); its second stage computes fac
-// for its chunk.
-template <int MS, int LT, bool GATE_UP, bool FIRST, int WAIT, bool ISSUE>
+template <int MS, int LT, bool GATE_UP, bool SECOND, int WAIT, bool ISSUE>
 __device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds, int kc_pad, int kt, int g, int nk,
                                             int wseg, int seg, const Pipe8Frags<MS>& fa, Pipe8Frags<MS>& fb,
-                                            f32x16 (&T)[Pipe8::TW][Pipe8::TT], f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
-                                            float (&fac)[Pipe8::TW][Pipe8::TT]) {
+                                            f32x16 (&acc)[Pipe8::TW][Pipe8::TT], float (&fac)[Pipe8::TW][Pipe8::TT],
+                                            float (&r)[Pipe8::TW][Pipe8::TT]) {
   using P = Pipe8;
   wait_vm_only_barrier<WAIT>();
+  if (SECOND) pipe8_next_frame<MS, GATE_UP>(fac, r, lds, kc_pad, kt >> 1, nk >> 1, seg);
   pipe8_read<MS>(fb, lds + ((g + 1) & 3) * P::STAGE);
   sched_fence();
   const Pipe8Off lo = ISSUE ? pipe8_offsets(g + 3, nk, wseg) : Pipe8Off{0, 0};
-  if (FIRST) {
-    pipe8_block<MS, LT, true, true, ISSUE>(fa, T, acc, fac, rows, lds, g + 3, lo);
-  } else {
-    pipe8_block<MS, LT, false, false, ISSUE>(fa, T, acc, fac, rows, lds, g + 3, lo);
-    pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, kt >> 1, seg);
-  }
+  pipe8_block<MS, LT, SECOND, ISSUE>(fa, acc, r, rows, lds, g + 3, lo);
 }
 
-// End of output-column block seg: promote its last chunk, hand acc to the
-// epilogue, restart acc and the factors from zero. The last chunk's MFMAs
-// are the latest issued, so the reads get the wait states an MFMA result
-// needs before a v_accvgpr_read (the asm read is opaque to the compiler's
-// hazard checks).
-template <int MS, class EPI>
-__device__ __forceinline__ void pipe8_finish(f32x16 (&T)[Pipe8::TW][Pipe8::TT], f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
-                                             float (&fac)[Pipe8::TW][Pipe8::TT], EPI& epi, int seg) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+// End of output-column block seg: y = acc * (last chunk's factor) for the
+// epilogue, then acc restarts from zero with the factors of the next block's
+// first chunk.
+template <int MS, bool GATE_UP, class EPI>
+__device__ __forceinline__ void pipe8_finish(f32x16 (&acc)[Pipe8::TW][Pipe8::TT], float (&fac)[Pipe8::TW][Pipe8::TT],
+                                             EPI& epi, int seg, int nseg, const uint8_t* lds, int kc_pad) {
 #pragma unroll
   for (int j = 0; j < Pipe8::TW; ++j)
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[j][i][v] = fmaf(agpr_read(T[j][i][v]), fac[j][i], acc[j][i][v]);
+      for (int v = 0; v < 16; ++v) acc[j][i][v] *= fac[j][i];
   epi(seg, acc);
 #pragma unroll
   for (int j = 0; j < Pipe8::TW; ++j)
 #pragma unroll
-    for (int i = 0; i < MS; ++i) {
-      fac[j][i] = 0.0f;
+    for (int i = 0; i < MS; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-    }
+  if (seg + 1 < nseg) pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, 0, seg + 1);
 }
 
 // The K loops of nseg output-column blocks of one unit as one stream of
 // total = nseg * nk stages through the ring: the next block's stages are in
-// flight while a block ends. For each block: acc = sum over chunks of
-// promoted T, then epi(seg, acc) (stores; may use AMAX_OFF with an LDS-only
-// barrier). K % 128 == 0, K / 128 <= MAX_CHUNKS, nseg <= MAX_SEG. Before the
-// call the unit's source rows and weight scales ([seg][2][chunk]) are in LDS
-// and visible to every wave; the token-scale table is loaded here from srs
+// flight while a block ends. For each block: acc = the block's outputs, then
+// epi(seg, acc) (stores; may use AMAX_OFF with an LDS-only barrier).
+// K % 128 == 0, K / 128 <= MAX_CHUNKS, nseg <= MAX_SEG. Before the call the
+// unit's source rows and weight scales ([seg][2][chunk]) are in LDS and
+// visible to every wave; the token-scale table is loaded here from srs
 // (kc = K / 128 scales per source row). LT (>= MS of every wave) token load
 // groups of 64 rows per stage.
 template <int MS, int LT, bool GATE_UP, class EPI>
@@ -319,48 +310,47 @@ __device__ __forceinline__ void pipe8_stream(const Pipe8Rows& rows, __amdgpu_buf
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_s_waitcnt(0xc07f);                  // no scalar load pending: LDS waits stay partial
 #endif
-  f32x16 T[P::TW][P::TT];
   f32x16 acc[P::TW][P::TT];
-  float fac[P::TW][P::TT];
+  float fac[P::TW][P::TT], r[P::TW][P::TT];
 #pragma unroll
   for (int j = 0; j < P::TW; ++j)
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
-      T[j][i] = f32x16{};
-      fac[j][i] = 0.0f;
+      r[j][i] = 1.0f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
     }
+  pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, 0, 0);
   Pipe8Frags<MS> f0, f1;
   pipe8_read<MS>(f0, lds);
   int kt = 0, seg = 0, g = 0;
   for (; g + 4 < total; g += 2) {                      // both stages refill the ring
-    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt, g, nk, wseg, seg, f0, f1, T, acc, fac);
-    pipe8_stage<MS, LT, GATE_UP, false, LPS, true>(rows, lds, kc_pad, kt + 1, g + 1, nk, wseg, seg, f1, f0, T, acc,
-                                                   fac);
+    pipe8_stage<MS, LT, GATE_UP, false, LPS, true>(rows, lds, kc_pad, kt, g, nk, wseg, seg, f0, f1, acc, fac, r);
+    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt + 1, g + 1, nk, wseg, seg, f1, f0, acc, fac,
+                                                  r);
     kt += 2;
     if (kt == nk) {
-      pipe8_finish<MS>(T, acc, fac, epi, seg);
+      pipe8_finish<MS, GATE_UP>(acc, fac, epi, seg, nseg, lds, kc_pad);
       ++seg;
       kt = 0;
     }
   }
   if (g + 4 == total) {                                // stage total-1 is the last to load
-    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt, g, nk, wseg, seg, f0, f1, T, acc, fac);
-    pipe8_stage<MS, LT, GATE_UP, false, LPS, false>(rows, lds, kc_pad, kt + 1, g + 1, nk, wseg, seg, f1, f0, T, acc,
-                                                    fac);
+    pipe8_stage<MS, LT, GATE_UP, false, LPS, true>(rows, lds, kc_pad, kt, g, nk, wseg, seg, f0, f1, acc, fac, r);
+    pipe8_stage<MS, LT, GATE_UP, true, LPS, false>(rows, lds, kc_pad, kt + 1, g + 1, nk, wseg, seg, f1, f0, acc, fac,
+                                                   r);
     kt += 2;
     if (kt == nk) {
-      pipe8_finish<MS>(T, acc, fac, epi, seg);
+      pipe8_finish<MS, GATE_UP>(acc, fac, epi, seg, nseg, lds, kc_pad);
       ++seg;
       kt = 0;
     }
   }
   // the stream's last pair: stage total-1 reads nothing
-  pipe8_stage<MS, LT, GATE_UP, true, 0, false>(rows, lds, kc_pad, kt, total - 2, nk, wseg, seg, f0, f1, T, acc, fac);
-  pipe8_block<MS, LT, false, false, false>(f1, T, acc, fac, rows, lds, 0, Pipe8Off{0, 0});
-  pipe8_factors<MS, GATE_UP>(fac, lds, kc_pad, (kt + 1) >> 1, seg);
-  pipe8_finish<MS>(T, acc, fac, epi, seg);
+  pipe8_stage<MS, LT, GATE_UP, false, 0, false>(rows, lds, kc_pad, kt, total - 2, nk, wseg, seg, f0, f1, acc, fac, r);
+  pipe8_next_frame<MS, GATE_UP>(fac, r, lds, kc_pad, (kt + 1) >> 1, nk >> 1, seg);
+  pipe8_block<MS, LT, true, false>(f1, acc, r, rows, lds, 0, Pipe8Off{0, 0});
+  pipe8_finish<MS, GATE_UP>(acc, fac, epi, seg, nseg, lds, kc_pad);
   // every wave has read the ring before the next unit's loads overwrite it
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
