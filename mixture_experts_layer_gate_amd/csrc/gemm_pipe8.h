@@ -29,10 +29,11 @@
 //
 // Iteration kt (stage kt, chunk kt / 2): wait until stage kt+1 has landed +
 // barrier; read stage kt+1's fragments; the MFMAs of stage kt with the loads
-// of stage kt+3 spread among them. A chunk's second stage computes the next
-// chunk's factors and moves each accumulator tile to the next frame two MFMAs
-// after its last MFMA of the chunk (the last two tiles at the start of the
-// next stage), so the multiplies run beside the MFMAs. A unit streams up to
+// of stage kt+3 spread among them. A chunk's first stage prepares the next
+// chunk's factors behind its MFMAs; its second stage moves each accumulator
+// tile to the next frame two MFMAs after the tile's last MFMA of the chunk
+// (the last two tiles at the start of the next stage), so the multiplies run
+// beside the MFMAs. A unit streams up to
 // MAX_SEG blocks of output columns that share its token rows as one sequence
 // of stages, so the ring's fill and drain and the unit's setup are paid once
 // per unit.
@@ -225,21 +226,41 @@ __device__ __forceinline__ void pipe8_factors(float (&fac)[Pipe8::TW][Pipe8::TT]
   }
 }
 
-// Frame change into chunk c + 1 of the same block (r = f_c / f_{c+1}, fac
-// becomes f_{c+1}), or r = 1 when c is the block's last chunk (fac stays f_c
-// for the epilogue).
+// The scales behind the factors of one chunk, read from the LDS tables: the
+// token scale of this lane's row of each sub-tile i, and the weight-block
+// scale(s) (gate/up tiles: [0] gate block, [1] up block; down tiles: [0] the
+// 128-row block of this wave's rows).
+struct Pipe8Scales {
+  float sa[Pipe8::TT];
+  float sw[2];
+};
+
 template <int MS, bool GATE_UP>
-__device__ __forceinline__ void pipe8_next_frame(float (&fac)[Pipe8::TW][Pipe8::TT], float (&r)[Pipe8::TW][Pipe8::TT],
-                                                 const uint8_t* lds, int kc_pad, int c, int nchunks, int seg) {
-  const bool next = c + 1 < nchunks;
-  float fn[Pipe8::TW][Pipe8::TT];
-  pipe8_factors<MS, GATE_UP>(fn, lds, kc_pad, next ? c + 1 : c, seg);
+__device__ __forceinline__ void pipe8_scale_loads(Pipe8Scales& sc, const uint8_t* lds, int kc_pad, int c, int seg) {
+  const float* swt = reinterpret_cast<const float*>(lds + Pipe8::SW_OFF) + seg * 2 * Pipe8::MAX_CHUNKS;
+  const float* sat = reinterpret_cast<const float*>(lds + Pipe8::SA_OFF);
+  const int l = threadIdx.x & 63, wt = p8_wt();
+#pragma unroll
+  for (int i = 0; i < MS; ++i) sc.sa[i] = sat[(32 * (2 * i + wt) + (l & 31)) * kc_pad + c];
+  sc.sw[0] = swt[(GATE_UP ? 0 : p8_ww()) * Pipe8::MAX_CHUNKS + c];
+  sc.sw[1] = GATE_UP ? swt[Pipe8::MAX_CHUNKS + c] : sc.sw[0];
+}
+
+// Frame change into chunk c + 1 of the same block: sc holds the scales of
+// chunk c + 1 (of chunk c when c is the block's last, next = false).
+// r = f_c / f_{c+1} and fac becomes f_{c+1}; for the last chunk r = 1 and fac
+// stays f_c for the epilogue.
+template <int MS, bool GATE_UP>
+__device__ __forceinline__ void pipe8_frame_update(float (&fac)[Pipe8::TW][Pipe8::TT],
+                                                   float (&r)[Pipe8::TW][Pipe8::TT], const Pipe8Scales& sc,
+                                                   bool next) {
 #pragma unroll
   for (int j = 0; j < Pipe8::TW; ++j)
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
-      r[j][i] = next ? fac[j][i] * __builtin_amdgcn_rcpf(fn[j][i]) : 1.0f;
-      fac[j][i] = fn[j][i];
+      const float fn = fmaxf(sc.sa[i] * sc.sw[GATE_UP && j >= Pipe8::TW / 2 ? 1 : 0], kMinFactor);
+      r[j][i] = next ? fac[j][i] * __builtin_amdgcn_rcpf(fn) : 1.0f;
+      fac[j][i] = fn;
     }
 }
 
@@ -247,18 +268,26 @@ __device__ __forceinline__ void pipe8_next_frame(float (&fac)[Pipe8::TW][Pipe8::
 // output-column block seg) that is not the stream's last: fa holds its
 // fragments, fb receives stage g+1's. WAIT: loads allowed in flight at the
 // barrier (one stage's while stage g+2 exists, else 0); ISSUE: load stage g+3.
+// A chunk's first stage also reads the next chunk's factors (before its
+// MFMAs) and forms the frame change (after them), so the second stage's
+// multiplies find r ready.
 template <int MS, int LT, bool GATE_UP, bool SECOND, int WAIT, bool ISSUE>
 __device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds, int kc_pad, int kt, int g, int nk,
                                             int wseg, int seg, const Pipe8Frags<MS>& fa, Pipe8Frags<MS>& fb,
                                             f32x16 (&acc)[Pipe8::TW][Pipe8::TT], float (&fac)[Pipe8::TW][Pipe8::TT],
                                             float (&r)[Pipe8::TW][Pipe8::TT]) {
   using P = Pipe8;
-  wait_vm_only_barrier<WAIT>();
-  if (SECOND) pipe8_next_frame<MS, GATE_UP>(fac, r, lds, kc_pad, kt >> 1, nk >> 1, seg);
-  pipe8_read<MS>(fb, lds + ((g + 1) & 3) * P::STAGE);
+  if (WAIT >= 0) {
+    wait_vm_only_barrier<(WAIT >= 0 ? WAIT : 0)>();
+    pipe8_read<MS>(fb, lds + ((g + 1) & 3) * P::STAGE);
+  }
+  const bool next = (kt >> 1) + 1 < (nk >> 1);
+  Pipe8Scales sc;
+  if (!SECOND) pipe8_scale_loads<MS, GATE_UP>(sc, lds, kc_pad, next ? (kt >> 1) + 1 : kt >> 1, seg);
   sched_fence();
   const Pipe8Off lo = ISSUE ? pipe8_offsets(g + 3, nk, wseg) : Pipe8Off{0, 0};
   pipe8_block<MS, LT, SECOND, ISSUE>(fa, acc, r, rows, lds, g + 3, lo);
+  if (!SECOND) pipe8_frame_update<MS, GATE_UP>(fac, r, sc, next);
 }
 
 // End of output-column block seg: y = acc * (last chunk's factor) for the
@@ -348,8 +377,8 @@ __device__ __forceinline__ void pipe8_stream(const Pipe8Rows& rows, __amdgpu_buf
   }
   // the stream's last pair: stage total-1 reads nothing
   pipe8_stage<MS, LT, GATE_UP, false, 0, false>(rows, lds, kc_pad, kt, total - 2, nk, wseg, seg, f0, f1, acc, fac, r);
-  pipe8_next_frame<MS, GATE_UP>(fac, r, lds, kc_pad, (kt + 1) >> 1, nk >> 1, seg);
-  pipe8_block<MS, LT, true, false>(f1, acc, r, rows, lds, 0, Pipe8Off{0, 0});
+  pipe8_stage<MS, LT, GATE_UP, true, -1, false>(rows, lds, kc_pad, kt + 1, total - 1, nk, wseg, seg, f1, f0, acc, fac,
+                                                r);
   pipe8_finish<MS, GATE_UP>(acc, fac, epi, seg, nseg, lds, kc_pad);
   // every wave has read the ring before the next unit's loads overwrite it
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
