@@ -27,9 +27,9 @@
 // per stage, the 4-byte scales of 128 scattered rows cost more L2 requests
 // than the stage's 24 KB of operands.
 //
-// Iteration kt (stage kt, chunk kt / 2): wait until stage kt+1 has landed +
-// barrier; read stage kt+1's fragments; the MFMAs of stage kt with the loads
-// of stage kt+3 spread among them. A chunk's first stage prepares the next
+// Iteration kt (stage kt, chunk kt / 2): the first half of stage kt's MFMAs;
+// wait until stage kt+1 has landed + barrier; read stage kt+1's fragments;
+// the second half of the MFMAs with the loads of stage kt+3 spread among them. A chunk's first stage prepares the next
 // chunk's factors behind its MFMAs; its second stage moves each accumulator
 // tile to the next frame two MFMAs after the tile's last MFMA of the chunk
 // (the last two tiles at the start of the next stage), so the multiplies run
@@ -174,29 +174,31 @@ __device__ __forceinline__ void pipe8_rescale(f32x16 (&acc)[Pipe8::TW][Pipe8::TT
   for (int v = 0; v < 16; ++v) acc[j][i][v] *= r[j][i];
 }
 
-// The MFMAs of one stage (fragments f), tile m = (m / MS, m % MS) in order,
-// with the loads of stage `ls` spread among them (load q before MFMA
-// q * M / LPS) when ISSUE. SECOND (a chunk's second stage): tile m - 2 moves
-// to the next frame right after MFMA m; otherwise (a chunk's first stage)
-// tiles M - 2 and M - 1, whose last MFMAs closed the previous stage, move
-// before MFMAs 0 and 1.
-template <int MS, int LT, bool SECOND, bool ISSUE>
-__device__ __forceinline__ void pipe8_block(const Pipe8Frags<MS>& f, f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
-                                            const float (&r)[Pipe8::TW][Pipe8::TT], const Pipe8Rows& rows,
-                                            uint8_t* lds, int ls, Pipe8Off lo) {
+// One half of a stage's MFMAs (fragments f), tile m = (m / MS, m % MS) in
+// order: HALF 0 takes tiles [0, M/2), HALF 1 tiles [M/2, M) with the loads of
+// stage `ls` spread among them (load q before the MFMA at q * H / L) when
+// ISSUE. SECOND (a chunk's second stage): tile m - 2 moves to the next frame
+// right after MFMA m; otherwise (a chunk's first stage) tiles M - 2 and M - 1,
+// whose last MFMAs closed the previous stage, move before MFMAs 0 and 1.
+template <int MS, int LT, bool SECOND, int HALF, bool ISSUE>
+__device__ __forceinline__ void pipe8_half(const Pipe8Frags<MS>& f, f32x16 (&acc)[Pipe8::TW][Pipe8::TT],
+                                           const float (&r)[Pipe8::TW][Pipe8::TT], const Pipe8Rows& rows,
+                                           uint8_t* lds, int ls, Pipe8Off lo) {
   using P = Pipe8;
-  constexpr int M = P::TW * MS, D = MS > 0 ? MS : 1;
-  constexpr int L = ISSUE ? P::WL + LT : 0;      // weight loads, then LT token load groups
+  constexpr int M = P::TW * MS, D = MS > 0 ? MS : 1, H = M / 2;
+  constexpr int M0 = HALF ? H : 0, N = HALF ? M - H : H;      // this half's first MFMA, count
+  constexpr int L = ISSUE ? P::WL + LT : 0;                   // weight loads, then LT token load groups
   uint8_t* st = lds + (ls & 3) * P::STAGE;
 #pragma unroll
-  for (int m = 0; m < (M > L ? M : L); ++m) {
+  for (int n = 0; n < (N > L ? N : L); ++n) {
 #pragma unroll
     for (int q = 0; q < L; ++q)
-      if ((M == 0 && q == m) || (M > 0 && q * M / (L > 0 ? L : 1) == m)) {
+      if ((N == 0 && q == n) || (N > 0 && q * N / (L > 0 ? L : 1) == n)) {
         pipe8_issue_one(rows, st, lo, q);
         sched_fence();
       }
-    if (m < M) {
+    if (n < N) {
+      const int m = M0 + n;
       if (!SECOND && m < 2) pipe8_rescale<MS>(acc, r, M - 2 + m);
       acc[m / D][m % D] = mfma_f8(f.w[m / D], f.t[m % D], acc[m / D][m % D]);
       if (SECOND && m >= 2) pipe8_rescale<MS>(acc, r, m - 2);
@@ -265,28 +267,34 @@ __device__ __forceinline__ void pipe8_frame_update(float (&fac)[Pipe8::TW][Pipe8
 }
 
 // One stage of the stream (global index g, local index kt within its
-// output-column block seg) that is not the stream's last: fa holds its
-// fragments, fb receives stage g+1's. WAIT: loads allowed in flight at the
-// barrier (one stage's while stage g+2 exists, else 0); ISSUE: load stage g+3.
-// A chunk's first stage also reads the next chunk's factors (before its
-// MFMAs) and forms the frame change (after them), so the second stage's
-// multiplies find r ready.
+// output-column block seg): fa holds its fragments, fb receives stage g+1's.
+// The first half of its MFMAs runs before the barrier, so the MFMA pipe still
+// has queued work while the wave waits there; after the barrier it reads stage
+// g+1's fragments and issues the second half with stage g+3's loads (into the
+// buffer of stage g-1, which every wave has finished with once it has issued
+// stage g's first MFMAs). WAIT: loads allowed in flight at the barrier (one
+// stage's while stage g+2 exists, else 0), or -1 for the stream's last stage
+// (no barrier, nothing to read); ISSUE: load stage g+3. A chunk's first stage
+// also reads the next chunk's scales (before its MFMAs) and forms the frame
+// change (after them), so the second stage's multiplies find r ready.
 template <int MS, int LT, bool GATE_UP, bool SECOND, int WAIT, bool ISSUE>
 __device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds, int kc_pad, int kt, int g, int nk,
                                             int wseg, int seg, const Pipe8Frags<MS>& fa, Pipe8Frags<MS>& fb,
                                             f32x16 (&acc)[Pipe8::TW][Pipe8::TT], float (&fac)[Pipe8::TW][Pipe8::TT],
                                             float (&r)[Pipe8::TW][Pipe8::TT]) {
   using P = Pipe8;
-  if (WAIT >= 0) {
-    wait_vm_only_barrier<(WAIT >= 0 ? WAIT : 0)>();
-    pipe8_read<MS>(fb, lds + ((g + 1) & 3) * P::STAGE);
-  }
   const bool next = (kt >> 1) + 1 < (nk >> 1);
   Pipe8Scales sc;
   if (!SECOND) pipe8_scale_loads<MS, GATE_UP>(sc, lds, kc_pad, next ? (kt >> 1) + 1 : kt >> 1, seg);
   sched_fence();
+  pipe8_half<MS, LT, SECOND, 0, false>(fa, acc, r, rows, lds, 0, Pipe8Off{0, 0});
+  if (WAIT >= 0) {
+    wait_vm_only_barrier<(WAIT >= 0 ? WAIT : 0)>();
+    pipe8_read<MS>(fb, lds + ((g + 1) & 3) * P::STAGE);
+    sched_fence();
+  }
   const Pipe8Off lo = ISSUE ? pipe8_offsets(g + 3, nk, wseg) : Pipe8Off{0, 0};
-  pipe8_block<MS, LT, SECOND, ISSUE>(fa, acc, r, rows, lds, g + 3, lo);
+  pipe8_half<MS, LT, SECOND, 1, ISSUE>(fa, acc, r, rows, lds, g + 3, lo);
   if (!SECOND) pipe8_frame_update<MS, GATE_UP>(fac, r, sc, next);
 }
 
