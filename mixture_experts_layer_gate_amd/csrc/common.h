@@ -58,6 +58,17 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | ((static_cast<uint32_t>(e + 7) << 3) + q);
 }
 
+// Four fp32 values to E4M3 codes packed little-endian (byte r = value r), by
+// gfx950's v_cvt_pk_fp8_f32 (round to nearest even) after a clamp to +-448
+// that supplies the saturation; NaN stays NaN. Same codes as f32_to_e4m3 for
+// every non-NaN input: checked on the GPU over every fp32 value of magnitude
+// <= 448, and the clamp maps larger ones to the saturated code.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+  auto sat = [](float x) { return x != x ? x : fminf(fmaxf(x, -kE4M3Max), kE4M3Max); };
+  const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), lo, true);
+}
+
 // ---------------------------------------------------------------- MFMA
 // 32x32x16 bf16 -> fp32. Operand lane layout: lane l supplies row/column
 // (l % 32) and the 8 consecutive K values starting at 8 * (l / 32).

@@ -86,12 +86,10 @@ struct GateUpEpi8 {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t packed = 0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) packed |= f32_to_e4m3(hv[i][j][4 * q + r] * inv) << (8 * r);
-            *reinterpret_cast<uint32_t*>(hrow + j * 32 + 8 * q) = packed;
-          }
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<uint32_t*>(hrow + j * 32 + 8 * q) =
+                f32x4_to_e4m3(hv[i][j][4 * q] * inv, hv[i][j][4 * q + 1] * inv, hv[i][j][4 * q + 2] * inv,
+                              hv[i][j][4 * q + 3] * inv);
         if (ww == 0 && l < 32) Hs[static_cast<size_t>(un.m0 + tr) * (I / 128) + nb] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
       }
     }

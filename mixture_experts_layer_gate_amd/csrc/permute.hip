@@ -187,11 +187,8 @@ __global__ __launch_bounds__(256) void rows_copy_kernel(int n_rows, int d, moe_d
 #pragma unroll
       for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
       const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(x[i] * inv) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(x[4 + i] * inv) << (8 * i);
+      const uint32_t lo = f32x4_to_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+      const uint32_t hi = f32x4_to_e4m3(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
       *reinterpret_cast<uint2*>(static_cast<uint8_t*>(dst) + doff) = make_uint2(lo, hi);
       if (sub == 0) dscale[static_cast<size_t>(r) * tiles_per_row + c] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
     } else if (ddt == MOE_BF16) {

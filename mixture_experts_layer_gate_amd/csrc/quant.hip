@@ -43,10 +43,8 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(int rows, int cols
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) word |= f32_to_e4m3(x[16 * v + 4 * i + b] * inv) << (8 * b);
-      o[i] = word;
+      const float* xi = x + 16 * v + 4 * i;
+      o[i] = f32x4_to_e4m3(xi[0] * inv, xi[1] * inv, xi[2] * inv, xi[3] * inv);
     }
     *reinterpret_cast<uint4*>(q + base + 16 * v) = make_uint4(o[0], o[1], o[2], o[3]);
   }

@@ -165,6 +165,50 @@ def test_permute_fp8_quantisation_bit_exact(gather):
     assert np.array_equal(sc.cpu().numpy(), scale)
 
 
+def _e4m3_edge_row(d):
+    """bf16-exact values that probe the E4M3 encode: every code's value, the midpoints between neighbouring
+    codes (ties to even), the subnormal grid and its midpoints, and values just off the ties; each 128-wide
+    tile holds 448 so its scale is exactly 1 and the encode sees the values unchanged."""
+    import numpy as _np
+    vals = []
+    for e in range(-9, 9):
+        for m in range(8):
+            v = (1 + m / 8) * 2.0 ** e if e >= -6 else m / 8 * 2.0 ** -6
+            vals.append(v)
+    vals = sorted(set(v for v in vals if v <= 448))
+    mids = [(a + b) / 2 for a, b in zip(vals, vals[1:])]
+    off = [m * (1 + 2 ** -7) for m in mids] + [m * (1 - 2 ** -7) for m in mids]
+    pool = _np.array(vals + mids + off, dtype=_np.float64)
+    pool = _np.concatenate([pool, -pool])
+    row = _np.resize(pool, d).astype(_np.float32)
+    row[::128] = 448.0
+    return torch.from_numpy(row).to(torch.bfloat16)
+
+
+def test_permute_fp8_quantisation_edge_values():
+    """Ties, subnormals and saturation through the 1x128 row quantisation, bit-exact against the oracle."""
+    cfg, inp = _inputs("c2")
+    sh = B.moe_shape.of(cfg)
+    T, d = cfg.T, cfg.d
+    u = inp["u"].clone()
+    for t in range(8):
+        u[t] = torch.roll(_e4m3_edge_row(d), shifts=t * 37)
+        u[t, ::128] = 448.0
+    u[8] = _e4m3_edge_row(d) * 1e4   # beyond 448 in every tile: saturates after scaling
+    idx = _i32(_oracle_route(cfg, inp)["idx"])
+    off = torch.empty((cfg.n_routed + 1,), dtype=torch.int32, device=DEV)
+    perm = torch.empty((T * cfg.topk,), dtype=torch.int32, device=DEV)
+    row_of = torch.empty((T * cfg.topk,), dtype=torch.int32, device=DEV)
+    q = torch.empty((T, d), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((T, d // 128), dtype=torch.float32, device=DEV)
+    B.moe_permute(sh, idx, u, off, perm, row_of, q, B.MOE_F8E4M3, sc, 0, _ws(cfg))
+    torch.cuda.synchronize()
+    codes, scale = oracle.quantize_tiles(u.cpu().float().numpy())
+    assert np.array_equal(q.cpu().numpy()[:16], codes[:16])
+    assert np.array_equal(sc.cpu().numpy()[:16], scale[:16])
+    assert np.array_equal(q.cpu().numpy(), codes)
+
+
 def test_quantize_weights_bit_exact():
     cfg, inp = _inputs("c2")
     w = inp["w_gate_up"][:3].contiguous()
