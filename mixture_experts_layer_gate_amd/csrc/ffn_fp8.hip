@@ -3,11 +3,12 @@
 // "DeepSeek V3 / V4 Infra", V3 FP8 section).
 //
 // Activations carry one fp32 scale per 1x128 tile (row, K chunk), weights one
-// per 128x128 block; every 128-wide K chunk is promoted into fp32 with the
-// product of the two scales (gemm_pipe8.h). Two persistent launches over all
-// experts, one 256-thread workgroup per CU, 256 weight rows x 128 token rows
-// per tile, balanced blocks of at most four 32-row sub-tiles; a unit streams
-// up to four consecutive output-column tiles of one token block:
+// per 128x128 block; every 128-wide K chunk of the products is scaled by the
+// product of the two scales in fp32 (gemm_pipe8.h). Two persistent launches
+// over all experts, one 256-thread workgroup per CU, 256 weight rows x 128
+// token rows per tile, an expert's rows in blocks of four 32-row sub-tiles
+// (the remainder last); a unit streams up to four consecutive output-column
+// tiles of one token block:
 //  1. gate/up: H[r, c] = SiLU(g) * u for 128 H columns per tile (each wave 64
 //     gate rows + the matching 64 up rows, so the product forms in registers);
 //     H is then re-quantised per 1x128 tile along I -- the tile owns exactly
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
   __shared__ int tslot;
   int x_off = 0;
   for (int t; (t = unit_queue_next(q, total, x_off, &tslot)) >= 0;) {
-    const Unit un = find_unit_balanced(t, off, E, n_rows, kMaxSub8, cum);
+    const Unit un = find_unit_balanced<false>(t, off, E, n_rows, kMaxSub8, cum);
     const int nb0 = un.nb * P8::MAX_SEG, nseg = min(P8::MAX_SEG, NB - nb0);
     // LDS tables of the unit: weight scales of each tile (gate block row nb,
     // up block row I/128 + nb) and the source row of each tile row (rows past
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
   __shared__ int tslot;
   int x_off = 0;
   for (int t; (t = unit_queue_next(q, total, x_off, &tslot)) >= 0;) {
-    const Unit un = find_unit_balanced(t, off, E, n_rows, kMaxSub8, cum);
+    const Unit un = find_unit_balanced<false>(t, off, E, n_rows, kMaxSub8, cum);
     const int nb0 = un.nb * P8::MAX_SEG, nseg = min(P8::MAX_SEG, NB - nb0);
     // weight scales: wave half ww of tile nb covers output columns nb*256 + 128ww .. +127 = block row 2nb + ww
     const float* sexp = wd_scale + static_cast<size_t>(un.e) * (d / 128) * kc;

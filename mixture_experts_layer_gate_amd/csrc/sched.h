@@ -95,9 +95,12 @@ __device__ __forceinline__ Unit find_unit(int t, const int32_t* __restrict__ off
   return u;
 }
 
-// Balanced blocks: an expert's rows are cut into 32-row sub-tiles, and the
-// sub-tiles into nmb = ceil(n32 / MAXSUB) blocks of nearly equal size, so a
-// 260-row expert becomes 2 x 130 rows instead of 256 + 4.
+// Blocks of an expert: its rows are cut into 32-row sub-tiles, and the
+// sub-tiles into nmb = ceil(n32 / MAXSUB) blocks, either of nearly equal size
+// (BALANCED: a 260-row expert becomes 2 x 130 rows; best for the bf16 tiles of
+// 8 sub-tiles) or full blocks first and the remainder last (260 rows with 4
+// sub-tiles per block: 128 + 128 + 4; best for the fp8 tiles, where a full
+// block runs at full MFMA rate and a one-sub-tile block is cheap).
 // Units are enumerated from the last expert down (cum[k] counts the units of
 // experts E-1 .. E-k): the shared experts, appended after the routed ones and
 // the largest, are handed out first and the routed tiles fill the tail.
@@ -114,6 +117,7 @@ __device__ __forceinline__ int build_units_balanced(const int32_t* __restrict__ 
   return cum[E];
 }
 
+template <bool BALANCED = true>
 __device__ __forceinline__ Unit find_unit_balanced(int t, const int32_t* __restrict__ off, int E, int n_rows,
                                                    int MAXSUB, const int* cum) {
   int lo = 0, hi = E;
@@ -128,7 +132,8 @@ __device__ __forceinline__ Unit find_unit_balanced(int t, const int32_t* __restr
   const int nmb = cdiv(n32, MAXSUB);
   const int local = t - cum[lo];
   const int b = local % nmb;
-  const int first = b * n32 / nmb, last = (b + 1) * n32 / nmb;
+  const int first = BALANCED ? b * n32 / nmb : b * MAXSUB;
+  const int last = BALANCED ? (b + 1) * n32 / nmb : min(n32, (b + 1) * MAXSUB);
   Unit u;
   u.e = wave_uniform(e);
   u.nb = wave_uniform(local / nmb);
