@@ -240,13 +240,16 @@ size_t route_ws_bytes(const Shape& s, moe_dtype act) {
 // Register form of the selection, for shapes where each lane can own V
 // consecutive experts and a group is a power-of-two run of whole lanes
 // (S % V == 0, S / V a power of two <= 64; or no group limit). One wavefront
-// per token, no LDS staging: each lane keeps its V biased scores, the group
-// score comes from a butterfly merge of the lanes' top-4 lists, and each of
-// the M group and K expert picks is a wave argmax. Same order of operations
-// and tie rules as route_select_kernel.
-// Insert v into the descending list a0 >= a1 >= a2 >= a3 (the largest four
-// stay), as a min/max bubble: no branches, no indexed registers.
+// per token, no LDS staging: each lane keeps its V biased scores; the group
+// score comes from a butterfly merge of the lanes' top-4 lists. The M kept
+// groups and the K picks are each found as a threshold: a 32-step binary
+// search on order-preserving integer keys of the fp32 values, counting with
+// wave ballots, then the values above the threshold plus the lowest-index
+// ones equal to it. Same choices as route_select_kernel (larger value first,
+// then the lower index), with no cross-lane shuffles in the searches.
 __device__ __forceinline__ void top4_insert(float v, float& a0, float& a1, float& a2, float& a3) {
+  // insert into the descending list a0 >= a1 >= a2 >= a3 (the largest four
+  // stay), as a min/max bubble: no branches, no indexed registers
   float t = fminf(a0, v);
   a0 = fmaxf(a0, v);
   const float t1 = fminf(a1, t);
@@ -254,6 +257,53 @@ __device__ __forceinline__ void top4_insert(float v, float& a0, float& a1, float
   const float t2 = fminf(a2, t1);
   a2 = fmaxf(a2, t1);
   a3 = fmaxf(a3, t2);
+}
+
+// Unsigned key with the order of the (non-NaN) fp32 values; 0 marks "absent".
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_popc(uint64_t m) { return __builtin_popcountll(m); }
+
+// Largest key t with #{candidates with key >= t} >= need (need >= 1 and at
+// least need candidates have a key > 0); keys[v] of this lane, 0 = absent.
+template <int V>
+__device__ __forceinline__ uint32_t kth_key(const uint32_t (&keys)[V], int need) {
+  uint32_t t = 0;
+#pragma unroll 1
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) cnt += wave_popc(__ballot(keys[v] >= c));
+    if (cnt >= need) t = c;
+  }
+  return t;
+}
+
+// sel[v]: whether this lane's candidate v is among the `need` largest keys
+// (ties at the threshold to the lower index lane * V + v).
+template <int V>
+__device__ __forceinline__ void select_top(const uint32_t (&keys)[V], int need, bool (&sel)[V]) {
+  const uint32_t t = kth_key<V>(keys, need);
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int above = 0, ties_before = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    above += wave_popc(__ballot(keys[v] > t));
+    ties_before += wave_popc(__ballot(keys[v] == t) & below);
+  }
+  int quota = need - above;                      // ties to take, in index order
+  int rank = ties_before;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const bool tie = keys[v] == t && keys[v] != 0;
+    sel[v] = keys[v] > t || (tie && rank < quota);
+    rank += tie ? 1 : 0;
+  }
 }
 
 template <int V>
@@ -268,6 +318,7 @@ __global__ __launch_bounds__(256) void route_select_reg_kernel(Shape s, const fl
   const int lpg = grouped ? S / V : 64;          // lanes per group
   const int my_group = grouped ? lane / lpg : 0;
   const int e0 = lane * V;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   float b[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) b[v] = e0 + v < N ? bias[e0 + v] : 0.0f;
@@ -294,7 +345,7 @@ __global__ __launch_bounds__(256) void route_select_reg_kernel(Shape s, const fl
         sb[v] = -INFINITY;
       }
     }
-    uint64_t keep = ~0ull;
+    bool live = true;                              // this lane's group is kept
     if (grouped) {
       float a0 = -INFINITY, a1 = -INFINITY, a2 = -INFINITY, a3 = -INFINITY;
 #pragma unroll
@@ -311,53 +362,36 @@ __global__ __launch_bounds__(256) void route_select_reg_kernel(Shape s, const fl
       if (topn > 1) gs = gs + a1;
       if (topn > 2) gs = gs + a2;
       if (topn > 3) gs = gs + a3;
-      if (my_group >= G) gs = -INFINITY;
-      keep = 0ull;
-      for (int m = 0; m < M; ++m) {
-        const bool open = my_group < G && !((keep >> my_group) & 1ull);
-        float v = open ? gs : -INFINITY;
-        int id = open ? my_group : INT_MAX;
-        argmax_pair(v, id);
-        if (id < 64) keep |= 1ull << id;
-      }
-      if (!((keep >> (my_group < 64 ? my_group : 0)) & 1ull) || my_group >= G) {
-#pragma unroll
-        for (int v = 0; v < V; ++v) sb[v] = -INFINITY;
-      }
+      // one candidate per group: its first lane
+      const uint32_t gk[1] = {(my_group < G && (lane % lpg) == 0) ? order_key(gs) : 0u};
+      bool gsel[1];
+      select_top<1>(gk, M, gsel);
+      const uint64_t kept = __ballot(gsel[0]);
+      live = my_group < G && ((kept >> (my_group * lpg)) & 1ull);
     }
-    int my_pick = -1;
-    for (int k = 0; k < K; ++k) {
-      float bv = -INFINITY;
-      int be = INT_MAX;
+    uint32_t keys[V];
 #pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (sb[v] > bv) { bv = sb[v]; be = e0 + v; }
-      argmax_pair(bv, be);
-      if (lane == k) my_pick = be < N ? be : -1;
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (e0 + v == be) sb[v] = -INFINITY;
-    }
-    // ascending expert order; gates over the raw affinities of the picks
-    float my_s = 0.0f;
+    for (int v = 0; v < V; ++v) keys[v] = (live && e0 + v < N) ? order_key(sb[v]) : 0u;
+    bool sel[V];
+    select_top<V>(keys, K, sel);
+    // slots in ascending expert order; gates over the raw affinities of the picks
+    int before = 0;
+    float part_sum = 0.0f;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      // lane k fetches the raw score of its pick from the owner lane
-      const int owner = my_pick >= 0 ? my_pick / V : lane;
-      const float cand = __shfl(sr[v], owner, kWave);
-      if (my_pick >= 0 && my_pick - owner * V == v) my_s = cand;
+      before += wave_popc(__ballot(sel[v]) & below);
+      part_sum += sel[v] ? sr[v] : 0.0f;
     }
-    int rank = 0;
-    float sum = 0.0f;
-    for (int j = 0; j < K; ++j) {
-      const int pj = __shfl(my_pick, j, kWave);
-      sum += __shfl(my_s, j, kWave);
-      rank += (pj < my_pick) ? 1 : 0;
-    }
-    if (lane < K) {
-      idx[static_cast<size_t>(t) * K + rank] = my_pick;
-      gate[static_cast<size_t>(t) * K + rank] = my_s / sum;
-    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part_sum += __shfl_xor(part_sum, o, kWave);
+    int slot = before;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (sel[v]) {
+        idx[static_cast<size_t>(t) * K + slot] = e0 + v;
+        gate[static_cast<size_t>(t) * K + slot] = sr[v] / part_sum;
+        ++slot;
+      }
   }
 }
 

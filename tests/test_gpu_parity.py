@@ -90,6 +90,35 @@ def test_route(name, over):
     assert max(len(set(row)) for row in (gi // S)) <= cfg.topk_groups
 
 
+def test_route_exact_ties():
+    """Exact ties follow the tie rule: experts in classes of four identical ones (same centroid and bias; groups
+    4..7 copy groups 0..3, so groups tie too). Within a class, a picked expert's lower-index twins are picked."""
+    cfg, inp = _inputs("c2")
+    N, K, T = cfg.n_routed, cfg.topk, cfg.T
+    cls = (np.arange(N) % 32) // 2                         # {2c, 2c+1, 2c+32, 2c+33} share class c
+    cent = inp["centroids"][torch.from_numpy(cls).to(DEV)].contiguous()
+    bias = inp["bias"][torch.from_numpy(cls).to(DEV)].contiguous()
+    sh = B.moe_shape.of(cfg)
+    idx = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    gate = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    load = torch.empty((N,), dtype=torch.int32, device=DEV)
+    B.moe_route(sh, inp["u"], cent, bias, idx, gate, load, None, _ws(cfg))
+    torch.cuda.synchronize()
+    gi = npi(idx)
+    members = [np.where(cls == c)[0] for c in range(16)]
+    for t in range(T):
+        picked = set(gi[t].tolist())
+        for m in members:
+            flags = [int(e) in picked for e in m]            # members in ascending index order
+            assert flags == sorted(flags, reverse=True), f"token {t}: class {m} picked {flags}"
+    r = oracle.route(inp["u"], cent, bias, cfg.n_groups, cfg.topk_groups, cfg.group_topn, K)
+    bad = routing_mismatches(idx, r)
+    ok = np.ones(T, dtype=bool)
+    ok[bad] = False
+    assert np.array_equal(gi[ok], r["idx"][ok])
+    report("tie gates", rel_l2(np64(gate)[ok], r["gate"][ok]), 1e-5)
+
+
 PERM_CASES = ["c1", "c2", "c3", "one_expert", "ragged", "single_token"]
 
 
