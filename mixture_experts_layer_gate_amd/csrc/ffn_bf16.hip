@@ -84,8 +84,9 @@ __device__ __forceinline__ void down_tile(const PipeRows<FP>& rows, int d, int I
       for (int j = 0; j < FP::TW; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          store_bf16x4(yrow + pipe_wcol<FP>(j, q), acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
-                       acc[j][i][4 * q + 3]);
+          if (un.nb * FP::BW + pipe_wcol<FP>(j, q) < d)   // d % 256 == 128: the last tile has 128 columns
+            store_bf16x4(yrow + pipe_wcol<FP>(j, q), acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                         acc[j][i][4 * q + 3]);
     }
   }
 }
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_down_bf16_kernel(int d, int I, 
   extern __shared__ __align__(16) uint8_t lds_p[];
   int* cum = reinterpret_cast<int*>(lds_p + FP::LDS_BYTES);
   __shared__ int wtmp[16];
-  const int NB = d / FP::BW;
+  const int NB = cdiv(d, FP::BW);                    // the last tile has 128 columns when d % 256 == 128
   const int total = build_units_balanced(off, E, n_rows, FP::BT / 32, NB, cum, wtmp);
   __shared__ int tslot;
   int x_off = 0;
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_down_bf16_kernel(int d, int I, 
     rows.wrs = pipe_rsrc(wd + static_cast<size_t>(un.e) * d * I, static_cast<uint64_t>(d) * I * 2);
 #pragma unroll
     for (int q = 0; q < FP::WL; ++q)
-      rows.ow[q] = (static_cast<uint32_t>(un.nb * FP::BW + pipe_load_row(q)) * I + pipe_load_chunk(q) * 8) * 2;
+      rows.ow[q] = (static_cast<uint32_t>(min(un.nb * FP::BW + pipe_load_row(q), d - 1)) * I + pipe_load_chunk(q) * 8) * 2;
     const bool full = live_token_subtiles(un.nsub) * 2 >= un.nsub;
     switch ((un.nsub + 1) / 2) {
       case 4: full ? down_tile<4, 4>(rows, d, I, un, lds_p, y) : down_tile<3, 4>(rows, d, I, un, lds_p, y); break;
@@ -208,7 +209,7 @@ hipError_t launch_ffn_bf16_down(const FfnArgs& p, hipStream_t st) {
   if (hipError_t e = launch_queue_reset(q, st); e != hipSuccess) return e;
   const size_t lds = FP::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / FP::BT + p.n_experts;
-  const int g2 = persistent_grid(mblocks * (p.d / FP::BW), 1);
+  const int g2 = persistent_grid(mblocks * cdiv(p.d, FP::BW), 1);
   hipLaunchKernelGGL(ffn_down_bf16_kernel, dim3(g2), dim3(FP::NT), lds, st, p.d, p.I, p.n_experts, p.n_rows,
                      p.offsets, static_cast<const uint16_t*>(p.h), static_cast<const uint16_t*>(p.w_d),
                      static_cast<uint16_t*>(p.y), q);

@@ -115,9 +115,10 @@ struct DownEpi8 {
         for (int j = 0; j < P8::TW; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<u32x2*>(yrow + p8_wcol(j, q)) =
-                u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
-                      pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])};
+            if ((nb0 + seg) * P8::BW + p8_wcol(j, q) < d)   // the 128-column last tile of d % 256 == 128
+              *reinterpret_cast<u32x2*>(yrow + p8_wcol(j, q)) =
+                  u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
+                        pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])};
       }
     }
   }
@@ -212,8 +213,12 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
   int* srcrow = reinterpret_cast<int*>(lds8 + P8::SRC_OFF);
   int* cum = reinterpret_cast<int*>(lds8 + P8::LDS_BYTES);
   __shared__ int wtmp[16];
-  const int kc = I / 128, NB = d / P8::BW;
-  const int total = build_units_balanced(off, E, n_rows, kMaxSub8, cdiv(NB, P8::MAX_SEG), cum, wtmp);
+  // Output-column tiles of 256 in groups of MAX_SEG per unit; when d % 256 == 128
+  // the last 128 columns form a group of their own, so their weight rows past
+  // d lie past the end of the expert's buffer by their own offset (read as 0).
+  const int kc = I / 128, NBF = d / P8::BW, NGF = cdiv(NBF, P8::MAX_SEG);
+  const int NG = NGF + (d % P8::BW ? 1 : 0);
+  const int total = build_units_balanced(off, E, n_rows, kMaxSub8, NG, cum, wtmp);
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t trs = pipe_rsrc(Hq, static_cast<uint64_t>(n_rows) * I);
   const __amdgpu_buffer_rsrc_t srs = pipe_rsrc(Hs, static_cast<uint64_t>(n_rows) * kc * 4);
@@ -221,12 +226,14 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
   int x_off = 0;
   for (int t; (t = unit_queue_next(q, total, x_off, &tslot)) >= 0;) {
     const Unit un = find_unit_balanced<false>(t, off, E, n_rows, kMaxSub8, cum);
-    const int nb0 = un.nb * P8::MAX_SEG, nseg = min(P8::MAX_SEG, NB - nb0);
+    const int nb0 = un.nb < NGF ? un.nb * P8::MAX_SEG : NBF;
+    const int nseg = un.nb < NGF ? min(P8::MAX_SEG, NBF - nb0) : 1;
     // weight scales: wave half ww of tile nb covers output columns nb*256 + 128ww .. +127 = block row 2nb + ww
+    // (past d: no block, factor 1, never stored)
     const float* sexp = wd_scale + static_cast<size_t>(un.e) * (d / 128) * kc;
     for (int x = tid; x < nseg * 2 * kc; x += P8::NT) {
-      const int sb = x / kc, c = x - sb * kc;
-      swt[sb * P8::MAX_CHUNKS + c] = sexp[static_cast<size_t>(2 * nb0 + sb) * kc + c];
+      const int sb = x / kc, c = x - sb * kc, br = 2 * nb0 + sb;
+      swt[sb * P8::MAX_CHUNKS + c] = br < d / 128 ? sexp[static_cast<size_t>(br) * kc + c] : 1.0f;
     }
     if (tid < P8::BT) srcrow[tid] = un.m0 + (tid < un.rows ? tid : 0);
     __syncthreads();
@@ -294,7 +301,8 @@ hipError_t launch_ffn_fp8_down(const FfnArgs& p, hipStream_t st) {
   if (hipError_t e = launch_queue_reset(q, st); e != hipSuccess) return e;
   const size_t lds = P8::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / P8::BT + p.n_experts;
-  hipLaunchKernelGGL(ffn_down_fp8_kernel, dim3(f8_grid(mblocks * cdiv(p.d / P8::BW, P8::MAX_SEG))), dim3(P8::NT), lds,
+  hipLaunchKernelGGL(ffn_down_fp8_kernel, dim3(f8_grid(mblocks * (cdiv(p.d / P8::BW, P8::MAX_SEG) + 1))), dim3(P8::NT),
+                     lds,
                      st, p.d, p.I,
                      p.n_experts, p.n_rows, p.offsets, static_cast<const uint8_t*>(p.h), p.h_scale,
                      static_cast<const uint8_t*>(p.w_d), p.w_d_scale, static_cast<uint16_t*>(p.y), q);

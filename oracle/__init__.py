@@ -23,6 +23,7 @@ closed forms, invariants, or a library routine). The absolute output values of
 the full layer have no worked example on the pages: beyond those pins they
 are "parity unpinned".
 """
+from .accumulation import keep_bits, limited_precision_gemm  # noqa: F401
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode  # noqa: F401
 from .moe import (  # noqa: F401
     affinity, route, permute, swiglu_ffn, quantize_tiles, quantize_blocks,

@@ -352,6 +352,28 @@ def test_grouped_ffn_tile_shapes(mode):
             report(f"{mode} expert {e} ({sizes[e]} rows) y", rel_l2(y[off[e]:off[e + 1]], ref), TOL["bf16"])
 
 
+@pytest.mark.parametrize("d", [384, 640])
+def test_grouped_ffn_bf16_half_column_tile(d):
+    """d % 256 == 128: the down projection's last output-column tile has 128 columns (the other half of the
+    tile must be neither computed into y nor written past the row)."""
+    cfg = get_config("c2", n_routed=4, n_groups=1, topk_groups=1, T=512, topk=2, d=d, inter=256)
+    inp = generate(cfg, DEV)
+    sh = B.moe_shape.of(cfg)
+    sizes = [0, 40, 300, 129]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    src = np.random.default_rng(5).integers(0, cfg.T, n)
+    y = torch.full((n + 1, d), 7.0, dtype=torch.bfloat16, device=DEV)     # one guard row past the end
+    B.moe_grouped_ffn(sh, B.MOE_BF16, 4, n, _i32(off), B.MOE_ROWS_GATHER, _i32(src), inp["u"], None, cfg.T,
+                      inp["w_gate_up"], None, inp["w_down"], None, y[:n], _ws(cfg))
+    torch.cuda.synchronize()
+    assert torch.all(y[n] == 7.0)
+    for e in range(4):
+        if sizes[e]:
+            ref = _oracle_ffn_rows(cfg, inp, e, src[off[e]:off[e + 1]])
+            report(f"d={d} expert {e} ({sizes[e]} rows) y", rel_l2(y[off[e]:off[e + 1]], ref), TOL["bf16"])
+
+
 @pytest.mark.parametrize("name", ["c1", "c2"])
 def test_combine(name):
     cfg, inp = _inputs(name)
@@ -532,6 +554,75 @@ def test_grouped_ffn_fp8_tile_shapes(inter, mode):
         sdiff = np.max(np.abs(hs[lo:hi].cpu().numpy() / aux["h_scale"] - 1))
         print(f"[parity] expert {e}: H codes equal {same:.4f}, max rel scale diff {sdiff:.2e}")
         assert same > 0.99 and sdiff < 1e-4
+
+
+@pytest.mark.parametrize("d", [384, 640])
+def test_grouped_ffn_fp8_half_column_tile(d):
+    """fp8 with d % 256 == 128: the last 128 output columns form a unit of their own (rows past d read as zero,
+    no weight-block scale, no store past the row); d also sets the gate/up K loop to 3 or 5 chunks."""
+    cfg = get_config("c2", gemm="fp8", n_routed=4, n_groups=1, topk_groups=1, T=512, topk=2, d=d, inter=256)
+    inp = generate(cfg, DEV)
+    sh = B.moe_shape.of(cfg)
+    sizes = [0, 40, 300, 129]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    src = np.random.default_rng(6).integers(0, cfg.T, n)
+    u32 = inp["u"].cpu().float().numpy()
+    uq, us = oracle.quantize_tiles(u32)
+    wq = [_oracle_wq(inp, e) for e in range(cfg.n_routed)]
+    dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    wgu = dev8(np.stack([w[0] for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
+    wdn = dev8(np.stack([w[2] for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
+    h = torch.empty((n, cfg.inter), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((n, cfg.inter // 128), dtype=torch.float32, device=DEV)
+    y = torch.full((n + 1, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    B.moe_ffn_gate_up(sh, B.MOE_F8E4M3, 4, n, _i32(off), B.MOE_ROWS_GATHER, _i32(src), dev8(uq), dev8(us), cfg.T,
+                      wgu, wgs, h, hs, ws)
+    B.moe_ffn_down(sh, B.MOE_F8E4M3, 4, n, _i32(off), h, hs, wdn, wds, y[:n], ws)
+    torch.cuda.synchronize()
+    assert torch.all(y[n] == 7.0)
+    for e in range(4):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            ref = oracle.ffn_fp8(u32[src[lo:hi]], *wq[e])
+            report(f"fp8 d={d} expert {e} ({hi - lo} rows) y", rel_l2(y[lo:hi], ref), TOL["fp8"])
+
+
+def test_fp8_accumulation_k4096():
+    """The pages' K = 4096 experiment on this path: E4M3 operands (unit scales) through the fp8 down GEMM
+    accumulate at fp32 grade -- the bf16 output equals the exact product rounded to bf16 almost everywhere --
+    while the limited-precision accumulator of the pages' reading shows ~2% error on the same matrices."""
+    M, Dout, K = 64, 128, 4096
+    cfg = get_config("c2", gemm="fp8", n_routed=1, n_groups=1, topk_groups=1, group_topn=1, topk=1, T=M, d=Dout,
+                     inter=K)
+    sh = B.moe_shape.of(cfg)
+    rng = np.random.default_rng(41)
+    ha = oracle.e4m3_encode(rng.standard_normal((M, K)).astype(np.float32))
+    wb = oracle.e4m3_encode(rng.standard_normal((Dout, K)).astype(np.float32))
+    A, W = oracle.e4m3_decode(ha), oracle.e4m3_decode(wb)
+    exact = A @ W.T
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    y = torch.empty((M, Dout), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    B.moe_ffn_down(sh, B.MOE_F8E4M3, 1, M, _i32(np.array([0, M])), dev(ha), dev(np.ones((M, K // 128), np.float32)),
+                   dev(wb[None]), dev(np.ones((1, Dout // 128, K // 128), np.float32)), y, ws)
+    torch.cuda.synchronize()
+    yg = np64(y)
+    rounded = torch.from_numpy(exact).to(torch.bfloat16).double().numpy()
+    same = float(np.mean(yg == rounded))
+    err = np.abs(yg - exact).max() / np.abs(exact).max()
+    lim = oracle.limited_precision_gemm(A, W)
+    err_lim = np.abs(lim - exact).max() / np.abs(exact).max()
+    # fp32 accumulation in any order errs by at most K * 2^-24 * sum |a_k w_k| (recursive-summation
+    # bound); the bf16 output adds at most one ulp of the value (8 significant bits)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(exact))[1] - 8)
+    bound = ulp + K * 2.0 ** -24 * (np.abs(A) @ np.abs(W).T)
+    print(f"[parity] K=4096 fp8: GPU max err {err:.2e} (bf16 output), equal to rounded exact {same:.4f}, "
+          f"max |err| / fp32 bound {np.max(np.abs(yg - exact) / bound):.3f}; limited-precision accumulator "
+          f"{err_lim:.2e}")
+    assert np.all(np.abs(yg - exact) <= bound) and same > 0.97 and err < 2.0 ** -8
+    assert 0.01 < err_lim < 0.03
 
 
 @pytest.mark.parametrize("name", ["c2", "c4"])
