@@ -199,6 +199,26 @@ moe_status moe_bias_update(const moe_shape* shape, const int32_t* expert_load, f
                            float* bias, void* stream);
 
 /*
+ * moe_balance_stats -- complementary sequence-wise balance statistics, eq. (17)-(20) of
+ * "DeepSeek_V3_Report: Annotation", section "Complementary Sequence-Wise Auxiliary Loss",
+ * for each run of seq_len consecutive tokens (the last run may be shorter, T_s tokens):
+ *   f_i  = N_r / (K T_s) * #{t in the run : i in topk_idx[t, :]}
+ *   P_i  = (1 / T_s) * sum_t s_{i,t} / sum_j s_{j,t}
+ *   loss = alpha * sum_i f_i P_i
+ * The selection indicator is the routing's own choice (topk_idx, after the bias and the
+ * group limit).
+ *   scores    [T, N_r] fp32 affinities s (moe_route's scores output).
+ *   topk_idx  [T, K] int32 from moe_route; entries outside [0, N_r) are not counted.
+ *   seq_len   tokens per sequence, >= 1.
+ *   f, P      out [ceil(T / seq_len), N_r] fp32; loss out [ceil(T / seq_len)] fp32.
+ *   workspace at least moe_workspace_bytes(shape, ...) bytes (per-64-token partial sums).
+ * fp32 arithmetic; partial sums are added in a fixed order, so results are reproducible.
+ */
+moe_status moe_balance_stats(const moe_shape* shape, const float* scores, const int32_t* topk_idx,
+                             int32_t seq_len, float alpha, float* f, float* P, float* loss,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * moe_quantize_weights -- 128x128 block quantisation of expert weights to E4M3
  * ("DeepSeek_V3_Report: Annotation", section "Fine-Grained Quantization"): for
  * n_mats matrices [rows, cols] of bf16 (rows, cols multiples of 128), writes

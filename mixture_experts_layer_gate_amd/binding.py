@@ -52,6 +52,7 @@ _SIGS = {
     "moe_ffn_gate_up": [_S, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_ffn_down": [_S, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
     "moe_combine": [_S, _I, _P, _P, _P, _P, _P, _P, _P],
+    "moe_balance_stats": [_S, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_bias_update": [_S, _P, ctypes.c_float, _P, _P],
     "moe_quantize_weights": [_I, _I, _I, _P, _P, _P, _P],
     "moe_workspace_bytes": [_S, _I],
@@ -196,6 +197,17 @@ def moe_ffn_down(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_o
     _check(lib().moe_ffn_down(ctypes.byref(shape), w, n_experts, n_rows, _ptr(expert_offsets), _ptr(h),
                               _ptr(h_scale), _ptr(w_down), _ptr(w_d_scale), _dt(y), _ptr(y), _ptr(workspace),
                               _nbytes(workspace), _stream(stream)))
+
+
+def moe_balance_stats(shape: moe_shape, scores, topk_idx, seq_len: int, alpha: float, f, P, loss, workspace,
+                      stream=None):
+    T, N, K = shape.T, shape.n_routed, shape.topk
+    n_seq = -(-T // seq_len)
+    _need(scores, T * N, "scores"); _need(topk_idx, T * K, "topk_idx")
+    _need(f, n_seq * N, "f"); _need(P, n_seq * N, "P"); _need(loss, n_seq, "loss")
+    _check(lib().moe_balance_stats(ctypes.byref(shape), _ptr(scores), _ptr(topk_idx), seq_len, ctypes.c_float(alpha),
+                                   _ptr(f), _ptr(P), _ptr(loss), _ptr(workspace), _nbytes(workspace),
+                                   _stream(stream)))
 
 
 def moe_combine(shape: moe_shape, u, y_routed, row_of, topk_gate, y_shared, out, stream=None):

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "route.hip", "permute.hip", "combine.hip", "ffn_f32.hip", "ffn_bf16.hip",
-           "ffn_fp8.hip", "quant.hip"]
+           "ffn_fp8.hip", "quant.hip", "balance.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # no packed fp32 instructions in device code

@@ -125,10 +125,12 @@ size_t moe_workspace_bytes(const moe_shape* shape, moe_dtype gemm) {
   if (!shape || check_shape(shape) != MOE_OK) return 0;
   const moe::Shape s = moe::to_shape(*shape);
   const size_t route = align256(moe::route_ws_bytes(s, MOE_BF16));
+  const size_t bal = align256(moe::balance_ws_bytes(s, 1));     // seq_len = 1 needs the most
   const size_t perm = align256(moe::permute_ws_bytes(s));
   const int rows = s.T * (s.K + s.Ns);   // routed and shared experts in one grouped call
   const size_t ffn = moe::ffn_ws_bytes(gemm, rows, s.I);
   size_t m = route > perm ? route : perm;
+  m = m > bal ? m : bal;
   return m > ffn ? m : ffn;
 }
 
@@ -306,6 +308,22 @@ moe_status moe_ffn_down(const moe_shape* shape, moe_dtype w, int32_t n_experts, 
                  const_cast<float*>(h_scale), static_cast<int*>(workspace)};
   auto st = static_cast<hipStream_t>(stream);
   return finish(run_down(w, p, st), "moe_ffn_down", st);
+}
+
+moe_status moe_balance_stats(const moe_shape* shape, const float* scores, const int32_t* topk_idx, int32_t seq_len,
+                             float alpha, float* f, float* P, float* loss, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  g_err.clear();
+  if (moe_status st = check_shape(shape); st != MOE_OK) return st;
+  REQUIRE(scores && topk_idx && f && P && loss, "balance_stats: a required pointer is NULL");
+  REQUIRE(seq_len >= 1, "balance_stats: seq_len (%d) must be positive", seq_len);
+  const moe::Shape s = moe::to_shape(*shape);
+  const size_t need = moe::balance_ws_bytes(s, seq_len);
+  if (!workspace || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "balance_stats: workspace of %zu bytes < %zu needed", ws_bytes, need);
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_balance_stats(s, scores, topk_idx, seq_len, alpha, f, P, loss, workspace, st),
+                "moe_balance_stats", st);
 }
 
 moe_status moe_combine(const moe_shape* shape, moe_dtype io, const void* u, const void* y_routed,

@@ -42,6 +42,11 @@ hipError_t launch_rows_copy(int n_rows, int d, moe_dtype src_dtype, const void* 
                             const int32_t* index, moe_dtype dst_dtype, void* dst, float* dst_scale,
                             hipStream_t st);
 
+// ---- balance statistics (eq. (17)-(20))
+size_t balance_ws_bytes(const Shape& s, int seq_len);
+hipError_t launch_balance_stats(const Shape& s, const float* scores, const int32_t* idx, int seq_len, float alpha,
+                                float* f, float* P, float* loss, void* ws, hipStream_t st);
+
 // ---- combine / bias
 hipError_t launch_combine(const Shape& s, moe_dtype io, const void* u, const void* y, const int32_t* row_of,
                           const float* gate, const void* ysh, void* out, hipStream_t st);

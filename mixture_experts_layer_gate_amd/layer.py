@@ -120,6 +120,16 @@ class MoELayer:
         B.moe_route(self.shape, u, self.centroids, self.bias, self.topk_idx, self.topk_gate, self.expert_load,
                     self.scores, self.ws)
 
+    def balance_stats(self, seq_len: int, alpha: float = 1e-4):
+        """Eq. (17)-(20) on the last route's scores and selection: (f, P, loss) per run of seq_len tokens."""
+        c = self.cfg
+        n_seq = -(-c.T // seq_len)
+        f = torch.empty((n_seq, c.n_routed), dtype=torch.float32, device=self.dev)
+        P = torch.empty((n_seq, c.n_routed), dtype=torch.float32, device=self.dev)
+        loss = torch.empty((n_seq,), dtype=torch.float32, device=self.dev)
+        B.moe_balance_stats(self.shape, self.scores, self.topk_idx, seq_len, alpha, f, P, loss, self.ws)
+        return f, P, loss
+
     def permute(self, u):
         if self.gemm == B.MOE_F8E4M3:
             B.moe_permute(self.shape, self.topk_idx, u, self.expert_offsets, self.perm_token, self.row_of,

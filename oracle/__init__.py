@@ -26,7 +26,7 @@ are "parity unpinned".
 from .accumulation import keep_bits, limited_precision_gemm  # noqa: F401
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode  # noqa: F401
 from .moe import (  # noqa: F401
-    affinity, route, permute, swiglu_ffn, quantize_tiles, quantize_blocks,
+    affinity, balance_stats, route, permute, swiglu_ffn, quantize_tiles, quantize_blocks,
     dequantize_tiles, dequantize_blocks, ffn_fp8, combine, bias_update,
     expert_ffn, layer_forward,
 )

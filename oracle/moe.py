@@ -314,6 +314,40 @@ def bias_update(bias, load, T: int, K: int, gamma: float = 0.001) -> np.ndarray:
     return b
 
 
+def balance_stats(scores, topk_idx, seq_len: int, alpha: float = 1e-4):
+    """Complementary sequence-wise balance statistics, eq. (17)-(20) of
+    "DeepSeek_V3_Report: Annotation", section "Complementary Sequence-Wise
+    Auxiliary Loss", for each run of seq_len consecutive tokens (the last run
+    may be shorter, T_s tokens):
+
+        f_i = N_r / (K_r T_s) * #{t in the run : expert i selected for t}
+        s'_{i,t} = s_{i,t} / sum_j s_{j,t}
+        P_i = (1 / T_s) * sum_t s'_{i,t}
+        L_Bal = alpha * sum_i f_i P_i
+
+    Reading: the selection indicator of eq. (18) is the routing's own choice
+    (topk_idx, after the bias and the group limit) rather than a plain top-K
+    of the raw s. scores [T, N_r] are the affinities s (any dtype, widened to
+    fp64). Returns f [n_seq, N_r], P [n_seq, N_r], loss [n_seq] in fp64.
+    """
+    s = np.asarray(scores, np.float64)
+    idx = np.asarray(topk_idx, np.int64)
+    T, N = s.shape
+    K = idx.shape[1]
+    n_seq = -(-T // seq_len)
+    f = np.zeros((n_seq, N))
+    P = np.zeros((n_seq, N))
+    loss = np.zeros(n_seq)
+    for q in range(n_seq):
+        lo, hi = q * seq_len, min(T, (q + 1) * seq_len)
+        Ts = hi - lo
+        cnt = np.bincount(idx[lo:hi].ravel(), minlength=N)[:N]
+        f[q] = N * cnt / (K * Ts)
+        P[q] = (s[lo:hi] / s[lo:hi].sum(axis=1, keepdims=True)).sum(axis=0) / Ts
+        loss[q] = alpha * np.sum(f[q] * P[q])
+    return f, P, loss
+
+
 # --------------------------------------------------------------------------
 # Whole layer (small configs; large ones are checked per expert / per token)
 # --------------------------------------------------------------------------

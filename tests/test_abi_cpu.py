@@ -70,6 +70,18 @@ def test_route_rejects_null_and_missing_workspace():
     assert st == B.MOE_E_WORKSPACE and "workspace" in msg
 
 
+def test_balance_stats_validation():
+    L = B.lib()
+    sh = _shape()
+    call = lambda seq, ws, nb: L.moe_balance_stats(ctypes.byref(sh), FAKE, FAKE, seq, ctypes.c_float(1e-4), FAKE, FAKE,
+                                                    FAKE, ws, nb, None)
+    assert call(0, FAKE, 1 << 20) == B.MOE_E_INVALID
+    assert call(16, None, 0) == B.MOE_E_WORKSPACE
+    assert L.moe_balance_stats(ctypes.byref(sh), None, FAKE, 16, ctypes.c_float(1e-4), FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                               None) == B.MOE_E_INVALID
+    assert B.moe_workspace_bytes(sh, B.MOE_BF16) >= 64 * 16 * 8     # seq_len = 1: one chunk per token
+
+
 def test_ffn_phases_need_queue_workspace():
     """The split FFN calls take their work-queue counters from the caller's workspace (no allocation)."""
     L = B.lib()

@@ -119,6 +119,28 @@ def test_route_exact_ties():
     report("tie gates", rel_l2(np64(gate)[ok], r["gate"][ok]), 1e-5)
 
 
+@pytest.mark.parametrize("name,seq_len", [("c2", 4096), ("c2", 1000), ("c2", 1), ("c3", 4096), ("c5", 100)])
+def test_balance_stats(name, seq_len):
+    """Eq. (17)-(20) per sequence on the oracle's own routing (affinities rounded to fp32): f exact up to
+    one fp32 rounding, P and the loss to 1e-5 relative; sum f = N_r per sequence."""
+    cfg, inp = _inputs(name)
+    sh = B.moe_shape.of(cfg)
+    T, N = cfg.T, cfg.n_routed
+    r = _oracle_route(cfg, inp)
+    s32 = r["s"].astype(np.float32)
+    n_seq = -(-T // seq_len)
+    f = torch.empty((n_seq, N), dtype=torch.float32, device=DEV)
+    P = torch.empty((n_seq, N), dtype=torch.float32, device=DEV)
+    loss = torch.empty((n_seq,), dtype=torch.float32, device=DEV)
+    B.moe_balance_stats(sh, torch.from_numpy(s32).to(DEV), _i32(r["idx"]), seq_len, 1e-4, f, P, loss, _ws(cfg))
+    torch.cuda.synchronize()
+    of, oP, ol = oracle.balance_stats(s32, r["idx"], seq_len, alpha=1e-4)
+    assert np.allclose(np64(f), of, rtol=2 ** -23, atol=0)
+    report(f"{name} seq {seq_len} P", rel_l2(np64(P), oP), 1e-5)
+    report(f"{name} seq {seq_len} loss", rel_l2(np64(loss), ol), 1e-5)
+    assert np.allclose(np64(f).sum(axis=1), N, rtol=1e-5)
+
+
 PERM_CASES = ["c1", "c2", "c3", "one_expert", "ragged", "single_token"]
 
 

@@ -199,3 +199,29 @@ def test_c1_route_sanity():
     inp = generate(cfg, "cpu", with_weights=False)
     r = oracle.route(inp["u"], inp["centroids"], inp["bias"], cfg.n_groups, cfg.topk_groups, cfg.group_topn, cfg.topk)
     assert r["idx"].shape == (64, 2) and r["load"].sum() == 128
+
+
+# ---------------------------------------------------------------- eq. (17)-(20) balance statistics
+
+def test_balance_stats_closed_forms():
+    """Sum f_i = N_r and sum P_i = 1 per sequence; a perfectly balanced selection with equal affinities
+    gives f_i = 1, P_i = 1/N_r and L_Bal = alpha; all tokens on the same K experts with all affinity mass
+    there gives f = N_r/K on them and L_Bal = alpha * N_r / K."""
+    rng = np.random.default_rng(4)
+    T, N, K, L = 100, 16, 2, 32
+    s = rng.random((T, N))
+    idx = np.sort(np.stack([rng.choice(N, K, replace=False) for _ in range(T)]), axis=1)
+    f, P, loss = oracle.balance_stats(s, idx, L, alpha=0.5)
+    assert f.shape == (4, N) and loss.shape == (4,)
+    assert np.allclose(f.sum(axis=1), N) and np.allclose(P.sum(axis=1), 1.0)
+    # last run has 4 tokens
+    cnt = np.bincount(idx[96:].ravel(), minlength=N)
+    assert np.allclose(f[3], N * cnt / (K * 4))
+    # perfectly balanced: each token t picks experts {2t mod N, 2t+1 mod N}; equal affinities
+    idx_b = np.stack([(2 * np.arange(64)) % N, (2 * np.arange(64) + 1) % N], axis=1)
+    fb, Pb, lb = oracle.balance_stats(np.ones((64, N)), idx_b, 64, alpha=1e-4)
+    assert np.allclose(fb, 1.0) and np.allclose(Pb, 1.0 / N) and np.allclose(lb, 1e-4)
+    # fully collapsed: every token on experts {0, 1}, which hold all the affinity
+    sc = np.zeros((32, N)); sc[:, :2] = 0.5
+    fc, Pc, lc = oracle.balance_stats(sc, np.tile([0, 1], (32, 1)), 32, alpha=1e-4)
+    assert np.allclose(fc[0, :2], N / K) and np.allclose(Pc[0, :2], 0.5) and np.allclose(lc, 1e-4 * N / K)
