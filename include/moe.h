@@ -50,7 +50,8 @@ typedef enum {
 typedef enum {
   MOE_F32 = 0,     /* IEEE binary32 */
   MOE_BF16 = 1,    /* bfloat16 */
-  MOE_F8E4M3 = 2   /* OCP E4M3FN: bias 7, max 448, no infinities */
+  MOE_F8E4M3 = 2,  /* OCP E4M3FN: bias 7, max 448, no infinities */
+  MOE_F8E4M3_POW2 = 3 /* E4M3FN codes with power-of-two tile scales (an a_dtype of moe_permute only) */
 } moe_dtype;
 
 /* How moe_grouped_ffn finds the input row of output row r of expert e. */
@@ -110,13 +111,18 @@ moe_status moe_route(const moe_shape* shape, moe_dtype act, const void* u, const
  *   perm_token     out [T*K] int32: token of each row (rows ordered by expert, then token).
  *   row_of         out [T*K] int32: row of pair (t, k) at index t*K + k.
  *   a              out or NULL. gather=1: [T*K, d] rows a[r] = u[perm_token[r]];
- *                  gather=0: [T, d] in token order (only with a_dtype = MOE_F8E4M3:
+ *                  gather=0: [T, d] in token order (only with a quantised a_dtype:
  *                  the quantised u, to be gathered inside moe_grouped_ffn).
- *   a_dtype        dtype of a: act (plain copy) or MOE_F8E4M3 (quantised).
- *   a_scale        out [rows of a, d/128] fp32 scales when a_dtype = MOE_F8E4M3, else NULL.
+ *   a_dtype        dtype of a: act (plain copy), MOE_F8E4M3 (quantised) or
+ *                  MOE_F8E4M3_POW2 (quantised with power-of-two scales: the form the
+ *                  section "Low-Precision Communication" gives the activations
+ *                  dispatched to the up-projection; a then feeds moe_grouped_ffn
+ *                  with w = MOE_F8E4M3 like any other E4M3 operand).
+ *   a_scale        out [rows of a, d/128] fp32 scales when a is quantised, else NULL.
  *                  Quantisation of a tile x: amax = max|x|; amax = 0 gives scale 1
- *                  and zero codes; else q = E4M3_rne_sat(x * fl32(448/amax)),
- *                  scale = fl32(amax/448).
+ *                  and zero codes; else, MOE_F8E4M3: q = E4M3_rne_sat(x * fl32(448/amax)),
+ *                  scale = fl32(amax/448); MOE_F8E4M3_POW2: scale = the smallest power
+ *                  of two >= fl32(amax/448), q = E4M3_rne(x / scale) (x / scale is exact).
  * Deterministic: the result does not depend on the order atomics complete in.
  */
 moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* topk_idx, const void* u,

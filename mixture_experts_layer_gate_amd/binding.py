@@ -17,7 +17,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_F8E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_F8E4M3, MOE_F8E4M3_POW2 = 0, 1, 2, 3
 MOE_ROWS_DIRECT, MOE_ROWS_GATHER, MOE_ROWS_SEGMENT = 0, 1, 2
 
 _STATUS = {1: "MOE_E_INVALID", 2: "MOE_E_UNSUPPORTED", 3: "MOE_E_WORKSPACE", 4: "MOE_E_HIP"}
@@ -144,7 +144,7 @@ def moe_permute(shape: moe_shape, topk_idx, u, expert_offsets, perm_token, row_o
         _need(u, T * d, "u"); _need(a, rows * d, "a")
         if a_dtype is None:
             a_dtype = _dt(a)
-        if a_dtype == MOE_F8E4M3:
+        if a_dtype in (MOE_F8E4M3, MOE_F8E4M3_POW2):
             _need(a_scale, rows * (d // 128), "a_scale")
     _check(lib().moe_permute(ctypes.byref(shape), act, _ptr(topk_idx), _ptr(u), _ptr(expert_offsets),
                              _ptr(perm_token), _ptr(row_of), _ptr(a), a_dtype if a_dtype is not None else act,

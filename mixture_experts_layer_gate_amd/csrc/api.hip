@@ -161,10 +161,11 @@ moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* top
   if (a) {
     REQUIRE(u != nullptr, "permute: u is NULL but an output a is requested");
     REQUIRE(act == MOE_F32 || act == MOE_BF16, "permute: act must be MOE_F32 or MOE_BF16");
-    REQUIRE(a_dtype == act || a_dtype == MOE_F8E4M3, "permute: a_dtype must equal act or be MOE_F8E4M3");
-    REQUIRE(a_dtype != MOE_F8E4M3 || a_scale != nullptr, "permute: fp8 output needs a_scale");
+    const bool quant = a_dtype == MOE_F8E4M3 || a_dtype == MOE_F8E4M3_POW2;
+    REQUIRE(a_dtype == act || quant, "permute: a_dtype must equal act or be MOE_F8E4M3 / MOE_F8E4M3_POW2");
+    REQUIRE(!quant || a_scale != nullptr, "permute: fp8 output needs a_scale");
     REQUIRE(gather == 0 || gather == 1, "permute: gather must be 0 or 1");
-    REQUIRE(gather == 1 || a_dtype == MOE_F8E4M3, "permute: gather=0 is only meaningful for fp8 quantisation");
+    REQUIRE(gather == 1 || quant, "permute: gather=0 is only meaningful for fp8 quantisation");
   }
   const size_t need = moe::permute_ws_bytes(s);
   if (!workspace || ws_bytes < need)

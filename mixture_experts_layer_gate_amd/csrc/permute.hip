@@ -180,17 +180,34 @@ __global__ __launch_bounds__(256) void rows_copy_kernel(int n_rows, int d, moe_d
       for (int i = 0; i < 8; ++i) x[i] = 0.0f;
     }
     const size_t doff = static_cast<size_t>(r) * d + c * 128 + sub * 8;
-    if (ddt == MOE_F8E4M3) {
+    if (ddt == MOE_F8E4M3 || ddt == MOE_F8E4M3_POW2) {
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(x[i]));
 #pragma unroll
       for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
-      const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
-      const uint32_t lo = f32x4_to_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
-      const uint32_t hi = f32x4_to_e4m3(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
+      float scale = 1.0f;
+      uint32_t lo = 0, hi = 0;
+      if (ddt == MOE_F8E4M3) {
+        const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
+        lo = f32x4_to_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+        hi = f32x4_to_e4m3(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
+        if (amax > 0.0f) scale = amax / kE4M3Max;
+      } else if (amax > 0.0f) {
+        // scale = 2^n, the smallest power of two >= fl32(amax / 448); x * 2^-n is exact (ldexp), so
+        // the codes are the encode of x / scale with no second rounding
+        int e;
+        const float m = __builtin_frexpf(amax / kE4M3Max, &e);  // v = m 2^e, 0.5 <= m < 1
+        const int n = m == 0.5f ? e - 1 : e;
+        scale = __builtin_ldexpf(1.0f, n);
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = __builtin_ldexpf(x[i], -n);
+        lo = f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
+        hi = f32x4_to_e4m3(y[4], y[5], y[6], y[7]);
+      }
       *reinterpret_cast<uint2*>(static_cast<uint8_t*>(dst) + doff) = make_uint2(lo, hi);
-      if (sub == 0) dscale[static_cast<size_t>(r) * tiles_per_row + c] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+      if (sub == 0) dscale[static_cast<size_t>(r) * tiles_per_row + c] = scale;
     } else if (ddt == MOE_BF16) {
       uint4 v;
       v.x = pack_bf16x2(x[0], x[1]);

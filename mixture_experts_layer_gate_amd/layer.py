@@ -54,12 +54,14 @@ class MoELayer:
     """
 
     def __init__(self, cfg, weights: Dict[str, torch.Tensor], device="cuda", keep_bf16: bool = False,
-                 gather_in_gemm: bool = True):
+                 gather_in_gemm: bool = True, pow2_act_scales: bool = False):
         self.cfg = cfg
         self.shape = B.moe_shape.of(cfg)
         self.dev = torch.device(device)
         self.gemm = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_F8E4M3}[cfg.gemm]
         self.gather_in_gemm = gather_in_gemm
+        # fp8: the up-projection input quantised with power-of-two tile scales
+        self.a_qdtype = B.MOE_F8E4M3_POW2 if pow2_act_scales else B.MOE_F8E4M3
         to = lambda t: t.to(self.dev).contiguous()
         self.centroids = to(weights["centroids"])
         self.bias = weights["bias"].to(self.dev, torch.float32).clone()  # layer-owned state
@@ -133,7 +135,7 @@ class MoELayer:
     def permute(self, u):
         if self.gemm == B.MOE_F8E4M3:
             B.moe_permute(self.shape, self.topk_idx, u, self.expert_offsets, self.perm_token, self.row_of,
-                          self.u_q, B.MOE_F8E4M3, self.u_scale, 0, self.ws)
+                          self.u_q, self.a_qdtype, self.u_scale, 0, self.ws)
         elif self.gather_in_gemm:
             B.moe_permute(self.shape, self.topk_idx, u, self.expert_offsets, self.perm_token, self.row_of,
                           None, None, None, 1, self.ws)

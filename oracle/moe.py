@@ -196,12 +196,36 @@ def _quantize_groups(x32: np.ndarray):
     return codes, scale
 
 
-def quantize_tiles(x) -> tuple:
-    """1x128 tiles along the last axis: x [R, C] -> codes [R, C] uint8, scales [R, C/128] fp32."""
+def _quantize_groups_pow2(x32: np.ndarray):
+    """Quantise each row of x32 [n, g] with a power-of-two scale.
+
+    "DeepSeek_V3_Report: Annotation", FP8 framework, "Low-Precision
+    Communication": the activations quantised before the MoE up-projection
+    (and dispatched) take scaling factors that are integral powers of 2.
+    Reading: the scale is the smallest power of two s with fl32(amax / 448)
+    <= s, so no element exceeds 448 after scaling; s = 1 and codes 0 when
+    amax = 0. x / s is exact, code = E4M3(x / s).
+    """
+    x32 = np.asarray(x32, dtype=F32)
+    amax = np.max(np.abs(x32), axis=1)
+    zero = amax == 0
+    v = (np.where(zero, F32(1), amax).astype(F32) / F32(E4M3_MAX)).astype(F32).astype(np.float64)
+    m, e = np.frexp(v)                                   # v = m * 2**e, 0.5 <= m < 1
+    scale = np.ldexp(1.0, np.where(m == 0.5, e - 1, e))  # 2**ceil(log2 v)
+    scale = np.where(zero, 1.0, scale)
+    codes = e4m3_encode((x32.astype(np.float64) / scale[:, None]).astype(F32))
+    codes[zero] = 0
+    return codes, scale.astype(F32)
+
+
+def quantize_tiles(x, pow2: bool = False) -> tuple:
+    """1x128 tiles along the last axis: x [R, C] -> codes [R, C] uint8, scales [R, C/128] fp32
+    (pow2: power-of-two scales, see _quantize_groups_pow2)."""
     x32 = _f32(x)
     R, C = x32.shape
     assert C % 128 == 0
-    codes, scale = _quantize_groups(x32.reshape(R * (C // 128), 128))
+    q = _quantize_groups_pow2 if pow2 else _quantize_groups
+    codes, scale = q(x32.reshape(R * (C // 128), 128))
     return codes.reshape(R, C), scale.reshape(R, C // 128)
 
 
@@ -229,7 +253,7 @@ def dequantize_blocks(codes, scale) -> np.ndarray:
     return v.reshape(R, C)
 
 
-def ffn_fp8(a, wgu_codes, wgu_scale, wd_codes, wd_scale, return_h=False):
+def ffn_fp8(a, wgu_codes, wgu_scale, wd_codes, wd_scale, return_h=False, pow2_input=False):
     """The SwiGLU FFN with the V3 fp8 recipe, in fp64 over the quantised values.
 
     a [n, d] (fp32/bf16 values) is quantised per 1x128 tile; the weights come
@@ -239,8 +263,10 @@ def ffn_fp8(a, wgu_codes, wgu_scale, wd_codes, wd_scale, return_h=False):
     products of two E4M3 values, exactly representable in fp64. The SwiGLU
     output is rounded to fp32 and quantised per 1x128 tile along I before the
     down projection (the activations of every fp8 GEMM are quantised online).
+    pow2_input: the up-projection input takes power-of-two scales (the
+    dispatched-activation variant); H keeps fp32 scales.
     """
-    a_codes, a_scale = quantize_tiles(a)
+    a_codes, a_scale = quantize_tiles(a, pow2=pow2_input)
     a_dq = dequantize_tiles(a_codes, a_scale)
     wgu = dequantize_blocks(wgu_codes, wgu_scale)
     I = wgu.shape[0] // 2
@@ -254,13 +280,13 @@ def ffn_fp8(a, wgu_codes, wgu_scale, wd_codes, wd_scale, return_h=False):
     return y
 
 
-def expert_ffn(a, w_gate_up, w_down, gemm: str = "bf16", wq=None):
+def expert_ffn(a, w_gate_up, w_down, gemm: str = "bf16", wq=None, pow2_input: bool = False):
     """FFN of one expert on rows a, in the precision recipe of ``gemm``.
 
     ``gemm`` "f32" / "bf16": exact fp64 arithmetic on the stored values.
     ``gemm`` "fp8": the weights are quantised per 128x128 block (unless
     ``wq`` = (gu_codes, gu_scale, d_codes, d_scale) is given) and the FFN runs
-    through :func:`ffn_fp8`.
+    through :func:`ffn_fp8` (``pow2_input``: power-of-two scales on its input).
     """
     if gemm != "fp8":
         return swiglu_ffn(a, w_gate_up, w_down)
@@ -269,7 +295,7 @@ def expert_ffn(a, w_gate_up, w_down, gemm: str = "bf16", wq=None):
         dq, ds = quantize_blocks(w_down)
     else:
         gq, gs, dq, ds = wq
-    return ffn_fp8(a, gq, gs, dq, ds)
+    return ffn_fp8(a, gq, gs, dq, ds, pow2_input=pow2_input)
 
 
 # --------------------------------------------------------------------------
@@ -352,13 +378,14 @@ def balance_stats(scores, topk_idx, seq_len: int, alpha: float = 1e-4):
 # Whole layer (small configs; large ones are checked per expert / per token)
 # --------------------------------------------------------------------------
 
-def layer_forward(cfg, inputs, shared_fp8: bool = True):
+def layer_forward(cfg, inputs, shared_fp8: bool = True, pow2_input: bool = False):
     """One layer forward plus the step-end bias update, for a config object.
 
     ``inputs``: u, centroids, bias, w_gate_up [N_r,2I,d], w_down [N_r,d,I],
     s_gate_up [N_s,2I,d], s_down [N_s,d,I]. For fp8 configs the shared
     expert also runs in fp8 (``shared_fp8``); its output and the combine stay
-    in high precision.
+    in high precision. ``pow2_input``: the fp8 up-projection inputs take
+    power-of-two tile scales (see _quantize_groups_pow2).
     """
     r = route(inputs["u"], inputs["centroids"], inputs["bias"], cfg.n_groups, cfg.topk_groups,
               cfg.group_topn, cfg.topk)
@@ -368,9 +395,10 @@ def layer_forward(cfg, inputs, shared_fp8: bool = True):
     for e in range(cfg.n_routed):
         lo, hi = offsets[e], offsets[e + 1]
         if hi > lo:
-            y[lo:hi] = expert_ffn(u64[perm_token[lo:hi]], inputs["w_gate_up"][e], inputs["w_down"][e], cfg.gemm)
+            y[lo:hi] = expert_ffn(u64[perm_token[lo:hi]], inputs["w_gate_up"][e], inputs["w_down"][e], cfg.gemm,
+                                  pow2_input=pow2_input)
     sgemm = cfg.gemm if (cfg.gemm != "fp8" or shared_fp8) else "bf16"
-    ysh = np.stack([expert_ffn(u64, inputs["s_gate_up"][s], inputs["s_down"][s], sgemm)
+    ysh = np.stack([expert_ffn(u64, inputs["s_gate_up"][s], inputs["s_down"][s], sgemm, pow2_input=pow2_input)
                     for s in range(cfg.n_shared)]) if cfg.n_shared else None
     out = combine(u64, y, row_of, r["gate"], ysh)
     new_bias = bias_update(inputs["bias"], r["load"], cfg.T, cfg.topk, cfg.gamma)

@@ -105,6 +105,7 @@ def test_grouped_ffn_validation():
     assert L.moe_grouped_ffn(*args(mode=7)) == B.MOE_E_INVALID
     assert L.moe_grouped_ffn(*args(ydt=B.MOE_F32)) == B.MOE_E_INVALID
     assert L.moe_grouped_ffn(*args(w=B.MOE_F8E4M3)) == B.MOE_E_INVALID     # missing scales
+    assert L.moe_grouped_ffn(*args(w=B.MOE_F8E4M3_POW2, asc=FAKE, gs=FAKE, ds=FAKE)) == B.MOE_E_INVALID
     assert L.moe_grouped_ffn(*args()) == B.MOE_E_WORKSPACE
     assert b"workspace" in L.moe_last_error()
 
@@ -119,6 +120,11 @@ def test_permute_combine_bias_validation():
                          FAKE, 1 << 20, None) == B.MOE_E_INVALID
     assert L.moe_permute(ctypes.byref(sh), B.MOE_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, None, B.MOE_BF16, None, 1,
                          FAKE, 16, None) == B.MOE_E_WORKSPACE
+    # power-of-two fp8 output needs its scales; an unknown a_dtype is refused; E4M3_POW2 is no weight dtype
+    assert L.moe_permute(ctypes.byref(sh), B.MOE_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B.MOE_F8E4M3_POW2, None,
+                         0, FAKE, 1 << 20, None) == B.MOE_E_INVALID
+    assert L.moe_permute(ctypes.byref(sh), B.MOE_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0,
+                         FAKE, 1 << 20, None) == B.MOE_E_INVALID
     assert L.moe_combine(ctypes.byref(sh), B.MOE_BF16, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == B.MOE_E_INVALID
     assert L.moe_bias_update(ctypes.byref(sh), FAKE, ctypes.c_float(-1.0), FAKE, None) == B.MOE_E_INVALID
     assert L.moe_quantize_weights(1, 100, 128, FAKE, FAKE, FAKE, None) == B.MOE_E_UNSUPPORTED

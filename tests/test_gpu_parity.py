@@ -260,6 +260,75 @@ def test_permute_fp8_quantisation_edge_values():
     assert np.array_equal(q.cpu().numpy(), codes)
 
 
+@pytest.mark.parametrize("gather", [0, 1])
+def test_permute_fp8_pow2_scales_bit_exact(gather):
+    """Power-of-two tile scales: codes and scales bit-exact against the oracle, with an all-zero row and
+    tile, E4M3 ties, saturating rows, rows whose amax / 448 is itself a power of two, and tiny and huge
+    magnitudes (scales far from 1 in both directions)."""
+    cfg, inp = _inputs("c2")
+    sh = B.moe_shape.of(cfg)
+    T, K, N, d = cfg.T, cfg.topk, cfg.n_routed, cfg.d
+    r = _oracle_route(cfg, inp)
+    o_off, o_perm, _ = oracle.permute(r["idx"], N)
+    rows = T * K if gather else T
+    u = inp["u"].clone()
+    u[5] = 0
+    u[9, :128] = 0
+    for t in range(10, 14):
+        u[t] = torch.roll(_e4m3_edge_row(d), shifts=t * 29)
+    u[14] = _e4m3_edge_row(d) * 1e4
+    u[15] = u[15] * 2.0 ** -100
+    u[16] = u[16] * 2.0 ** 100
+    u[17, ::128] = 448.0 * 2.0 ** -3        # amax / 448 = 2^-3 in every tile
+    u[18] = u[18] * 1e-36                   # amax / 448 below the fp32 normal range
+    off = torch.empty((N + 1,), dtype=torch.int32, device=DEV)
+    perm = torch.empty((T * K,), dtype=torch.int32, device=DEV)
+    row_of = torch.empty((T * K,), dtype=torch.int32, device=DEV)
+    q = torch.empty((rows, d), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((rows, d // 128), dtype=torch.float32, device=DEV)
+    B.moe_permute(sh, _i32(r["idx"]), u, off, perm, row_of, q, B.MOE_F8E4M3_POW2, sc, gather, _ws(cfg))
+    torch.cuda.synchronize()
+    codes, scale = oracle.quantize_tiles(u.cpu().float().numpy(), pow2=True)
+    if gather:
+        codes, scale = codes[o_perm], scale[o_perm]
+    assert np.array_equal(sc.cpu().numpy(), scale)
+    assert np.array_equal(q.cpu().numpy(), codes)
+
+
+def test_fp8_layer_pow2_act_scales():
+    """The fp8 layer with power-of-two scales on the up-projection input: the token quantisation bit-exact,
+    sampled experts and tokens against the oracle's fp8 FFN with the same input scales."""
+    cfg, inp = _inputs("c2", gemm="fp8")
+    T, K, N = cfg.T, cfg.topk, cfg.n_routed
+    layer = MoELayer(cfg, inp, DEV, pow2_act_scales=True)
+    layer.route(inp["u"])
+    layer.permute(inp["u"])
+    layer.ffn_routed_phases(inp["u"])
+    layer.ffn_shared(inp["u"])
+    layer.combine(inp["u"])
+    out = layer.out
+    torch.cuda.synchronize()
+    r = _oracle_route(cfg, inp)
+    bad = routing_mismatches(layer.topk_idx, r)
+    u32 = inp["u"].cpu().float().numpy()
+    codes, scale = oracle.quantize_tiles(u32, pow2=True)
+    assert np.array_equal(layer.u_q.cpu().numpy(), codes)
+    assert np.array_equal(layer.u_scale.cpu().numpy(), scale)
+    load = r["load"]
+    experts = sorted({0, N - 1, int(np.argmax(load)), int(np.argmin(load))})
+    _check_fp8_experts(cfg, inp, layer, experts, "c2 pow2", pow2=True)
+    u64 = np64(inp["u"])
+    toks = [t for t in np.random.default_rng(2).choice(T, 6, replace=False) if t not in set(bad)][:3]
+    for t in toks:
+        acc = u64[t].copy()
+        for sh_e in range(cfg.n_shared):
+            acc = acc + oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, sh_e, shared=True), pow2_input=True)[0]
+        for k in range(K):
+            e = int(r["idx"][t, k])
+            acc = acc + r["gate"][t, k] * oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, e), pow2_input=True)[0]
+        report(f"c2 fp8 pow2 out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["fp8"])
+
+
 def test_quantize_weights_bit_exact():
     cfg, inp = _inputs("c2")
     w = inp["w_gate_up"][:3].contiguous()
@@ -510,7 +579,7 @@ def _oracle_wq(inp, e, shared=False):
     return _WQ[key]
 
 
-def _check_fp8_experts(cfg, inp, layer, experts, tag):
+def _check_fp8_experts(cfg, inp, layer, experts, tag, pow2=False):
     goff = npi(layer.expert_offsets)
     gperm = npi(layer.perm_token)
     u32 = inp["u"].cpu().float().numpy()
@@ -519,7 +588,7 @@ def _check_fp8_experts(cfg, inp, layer, experts, tag):
         if hi == lo:
             continue
         wq = _oracle_wq(inp, e)
-        ref, aux = oracle.ffn_fp8(u32[gperm[lo:hi]], *wq, return_h=True)
+        ref, aux = oracle.ffn_fp8(u32[gperm[lo:hi]], *wq, return_h=True, pow2_input=pow2)
         report(f"{tag} fp8 expert {e} ({hi - lo} rows) y", rel_l2(layer.y_routed[lo:hi], ref), TOL["fp8"])
         if hasattr(layer, "h"):
             codes = layer.h[lo:hi].cpu().numpy()

@@ -213,3 +213,32 @@ def test_p12_flop_accounting():
     # V4-Pro: 6hd FLOPs against 3h bytes per pair is 2d with d = 3072
     h, d = 7168, 3072
     assert (6 * h * d) / (3 * h) == 2 * d == 6144
+
+
+# ---------------------------------------------------------------- power-of-two activation scales
+
+def test_pow2_tile_scales():
+    """Scales are powers of two, the smallest with every |x| / s <= 448; codes are the plain E4M3 encode of
+    x / s; when amax / 448 is itself a power of two the fp32-scale quantiser gives the same codes."""
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((64, 512)) * 10.0 ** rng.integers(-3, 4, (64, 1))).astype(np.float32)
+    x[3] = 0.0
+    codes, scale = oracle.quantize_tiles(x, pow2=True)
+    m, _ = np.frexp(scale.astype(np.float64))
+    assert np.all(m == 0.5)                                          # powers of two
+    amax = np.abs(x).reshape(64, 4, 128).max(axis=2)
+    v = (amax / np.float32(448)).astype(np.float32)
+    nz = amax > 0
+    assert np.all(v[nz] <= scale[nz]) and np.all(scale[nz] / 2 < v[nz])   # the smallest such power
+    assert np.all(scale[~nz] == 1) and np.all(codes[3] == 0)
+    xs = (x.reshape(64, 4, 128) / scale[:, :, None]).reshape(64, 512).astype(np.float32)
+    assert np.array_equal(codes, e4m3_encode(xs))
+    deq = oracle.dequantize_tiles(codes, scale)
+    assert np.all(np.abs(deq - x) <= np.abs(x) * 2.0 ** -4 + scale.repeat(128, axis=1) * 2.0 ** -10)
+    # amax = 448 * 2^k: both quantisers agree
+    y = rng.standard_normal((8, 128)).astype(np.float32)
+    y[:, 0] = np.float32(448.0 * 2.0 ** -5)
+    y[:, 1:] = np.clip(y[:, 1:], -448.0 * 2.0 ** -5, 448.0 * 2.0 ** -5)
+    c1, s1 = oracle.quantize_tiles(y, pow2=True)
+    c2, s2 = oracle.quantize_tiles(y)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
