@@ -37,6 +37,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--batch-invariant", action="store_true",
+                    help="router K split fixed by d, so per-token results do not depend on the batch")
+    ap.add_argument("--pow2-act-scales", action="store_true",
+                    help="fp8: power-of-two scales on the up-projection input")
     ap.add_argument("--cpu-sample", type=int, default=32, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (HBM counter calibration)")
@@ -125,11 +129,11 @@ def main():
     from moe_inputs import get_config, generate
     from mixture_experts_layer_gate_amd import MoELayer
 
-    cfg = get_config(args.config)
+    cfg = get_config(args.config, batch_invariant=int(args.batch_invariant))
     dev = "cuda"
     torch.cuda.set_device(0)
     inp = generate(cfg, dev)
-    layer = MoELayer(cfg, inp, dev)
+    layer = MoELayer(cfg, inp, dev, pow2_act_scales=args.pow2_act_scales)
     u = inp["u"]
     stream = torch.cuda.current_stream()
 
@@ -213,7 +217,8 @@ def main():
         "data": "synthetic: seeded N(0,1) tokens, random-init N(0,0.02^2) weights of the workload's shape",
         "config": {"workload": f"{cfg.name}: {cfg.description}", "T": T, "d": d, "n_routed": N,
                    "groups": cfg.n_groups, "topk_groups": cfg.topk_groups, "topk": K, "n_shared": Ns, "inter": I,
-                   "gemm": cfg.gemm},
+                   "gemm": cfg.gemm, "batch_invariant": bool(args.batch_invariant),
+                   **({"act_scales": "pow2" if args.pow2_act_scales else "fp32"} if cfg.gemm == "fp8" else {})},
         "roofline": roof,
         "ffn": {"TFLOP/s": ffn_flops / ffn_s / 1e12, "mfma_frac": ffn_flops / ffn_s / MFMA_PEAK[cfg.gemm],
                 "hbm_frac_weights": (n_touch + Ns) * 3 * I * d * wb / ffn_s / HBM_PEAK},

@@ -75,7 +75,21 @@ typedef struct {
   int32_t topk;         /* K <= 16, K <= M * S                     */
   int32_t n_shared;     /* N_s >= 0                                */
   int32_t inter;        /* I, SwiGLU width, multiple of 128        */
+  int32_t batch_invariant; /* 0 or 1: see below                    */
 } moe_shape;
+
+/*
+ * batch_invariant = 1 makes every per-token result (affinities, selection,
+ * gates, expert rows, layer output) bit-identical whatever other tokens share
+ * the batch and wherever the token sits in it: the property the
+ * batch-invariant kernels of "DeepSeek V3 / V4 Infra" (the V4 section on
+ * determinism and batch invariance) are built for. The grouped FFN and the
+ * combine have it in both modes (no reduction is split across rows or
+ * blocks); the router's logits GEMM splits its K reduction into slices, by
+ * default as many as fill the GPU for this T, with batch_invariant = 1 into
+ * four slices of whole 128-wide chunks (d alone fixes them). The bias update
+ * and the load histogram are batch statistics by definition.
+ */
 
 /*
  * moe_route -- affinities, biased group-limited top-K, gates and load histogram.

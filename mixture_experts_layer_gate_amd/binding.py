@@ -31,12 +31,13 @@ class MoEError(RuntimeError):
 
 class moe_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("T", "d", "n_routed", "n_groups", "topk_groups", "group_topn", "topk", "n_shared", "inter")]
+                ("T", "d", "n_routed", "n_groups", "topk_groups", "group_topn", "topk", "n_shared", "inter",
+                 "batch_invariant")]
 
     @classmethod
     def of(cls, cfg) -> "moe_shape":
         return cls(cfg.T, cfg.d, cfg.n_routed, cfg.n_groups, cfg.topk_groups, cfg.group_topn, cfg.topk,
-                   cfg.n_shared, cfg.inter)
+                   cfg.n_shared, cfg.inter, int(getattr(cfg, "batch_invariant", 0)))
 
 
 _lib = None

@@ -56,6 +56,8 @@ moe_status check_shape(const moe_shape* s) {
               s->group_topn > 0 && s->topk > 0 && s->inter > 0 && s->n_shared >= 0,
           "non-positive size in shape (T=%d d=%d N_r=%d G=%d M=%d topn=%d K=%d N_s=%d I=%d)", s->T, s->d,
           s->n_routed, s->n_groups, s->topk_groups, s->group_topn, s->topk, s->n_shared, s->inter);
+  REQUIRE(s->batch_invariant == 0 || s->batch_invariant == 1, "batch_invariant must be 0 or 1 (got %d)",
+          s->batch_invariant);
   REQUIRE(s->n_routed % s->n_groups == 0, "n_routed (%d) is not a multiple of n_groups (%d)", s->n_routed,
           s->n_groups);
   REQUIRE(s->topk_groups <= s->n_groups, "topk_groups (%d) > n_groups (%d)", s->topk_groups, s->n_groups);

@@ -12,10 +12,12 @@ namespace moe {
 
 struct Shape {
   int T, d, N, G, M, topn, K, Ns, I;
+  int bi;   // batch-invariant mode
 };
 
 inline Shape to_shape(const moe_shape& s) {
-  return Shape{s.T, s.d, s.n_routed, s.n_groups, s.topk_groups, s.group_topn, s.topk, s.n_shared, s.inter};
+  return Shape{s.T, s.d, s.n_routed, s.n_groups, s.topk_groups, s.group_topn, s.topk, s.n_shared, s.inter,
+               s.batch_invariant};
 }
 
 // Compute units of the current device (cached per device).

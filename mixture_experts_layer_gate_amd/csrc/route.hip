@@ -115,6 +115,33 @@ __device__ __forceinline__ void argmax_pair(float& v, int& id) {
   }
 }
 
+// Logits of this lane's V experts (e0 .. e0 + nv - 1, nv <= V) from the slice
+// partials part[p * slice + off + v], added in slice order; the loads of four
+// slices are issued together so that the chain of adds does not wait on one
+// load at a time.
+template <int V>
+__device__ __forceinline__ void sum_slices(const float* __restrict__ part, int S_part, size_t slice, size_t off,
+                                           int nv, float (&x)[V]) {
+#pragma unroll
+  for (int v = 0; v < V; ++v) x[v] = v < nv ? part[off + v] : 0.0f;
+  int p = 1;
+  for (; p + 4 <= S_part; p += 4) {
+    float y[4][V];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int v = 0; v < V; ++v) y[q][v] = v < nv ? part[(p + q) * slice + off + v] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int v = 0; v < V; ++v) x[v] += y[q][v];
+  }
+  for (; p < S_part; ++p)
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (v < nv) x[v] += part[p * slice + off + v];
+}
+
 constexpr int kSelWaves = 4;
 
 // part != nullptr: S partial logit sums per token (slice-major), added in
@@ -145,9 +172,9 @@ __global__ __launch_bounds__(64 * kSelWaves) void route_select_kernel(Shape s, c
       for (int e = lane; e < N; e += kWave) {
         float v;
         if (part) {
-          float x = part[static_cast<size_t>(t) * N + e];
-          for (int p = 1; p < S_part; ++p) x += part[(static_cast<size_t>(p) * s.T + t) * N + e];
-          v = 1.0f / (1.0f + expf(-x));
+          float x[1];
+          sum_slices<1>(part, S_part, static_cast<size_t>(s.T) * N, static_cast<size_t>(t) * N + e, 1, x);
+          v = 1.0f / (1.0f + expf(-x[0]));
           scores[static_cast<size_t>(t) * N + e] = v;
         } else {
           v = scores[static_cast<size_t>(t) * N + e];
@@ -221,7 +248,13 @@ __global__ __launch_bounds__(64 * kSelWaves) void route_select_kernel(Shape s, c
 
 // K slices of the bf16 logits GEMM: enough tiles to give every CU one
 // (256-centroid x 128-token tiles), at most 16 slices, whole 128-wide chunks.
+// Batch-invariant mode: four slices (whole chunks) whatever T is, so each
+// logit is the same sum of the same partials in the same order for any batch;
+// four is what a V3-sized batch (64 token tiles) needs to fill the GPU.
+constexpr int kInvariantSlices = 4;
+
 static int route_kslice(const Shape& s) {
+  if (s.bi) return cdiv(s.d / 128, kInvariantSlices) * 128;
   const int tiles = cdiv(s.N, RouteTile::BW) * cdiv(s.T, RouteTile::BT);
   const int chunks = s.d / 128;
   int S = device_cu_count() / tiles;
@@ -324,16 +357,16 @@ __global__ __launch_bounds__(256) void route_select_reg_kernel(Shape s, const fl
   for (int v = 0; v < V; ++v) b[v] = e0 + v < N ? bias[e0 + v] : 0.0f;
 
   for (int t = blockIdx.x * 4 + w; t < s.T; t += gridDim.x * 4) {
-    float sr[V], sb[V];
+    float sr[V], sb[V], lg[V];
+    if (part)
+      sum_slices<V>(part, S_part, static_cast<size_t>(s.T) * N, static_cast<size_t>(t) * N + e0, N - e0, lg);
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const int e = e0 + v;
       if (e < N) {
         float x;
         if (part) {
-          x = part[static_cast<size_t>(t) * N + e];
-          for (int p = 1; p < S_part; ++p) x += part[(static_cast<size_t>(p) * s.T + t) * N + e];
-          x = 1.0f / (1.0f + expf(-x));
+          x = 1.0f / (1.0f + expf(-lg[v]));
           scores[static_cast<size_t>(t) * N + e] = x;
         } else {
           x = scores[static_cast<size_t>(t) * N + e];

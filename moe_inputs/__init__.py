@@ -59,6 +59,7 @@ class MoEConfig:
     centroids: str = "iid"     # "iid" | "renorm" | "zipf"
     bias_init: str = "uniform"  # "uniform" U(-0.01, 0.01) | "zero"
     w_std: float = 0.02
+    batch_invariant: int = 0    # 1: per-token results independent of the batch (router K split fixed by d)
     description: str = ""
 
     @property

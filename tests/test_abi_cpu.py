@@ -27,7 +27,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def _shape(**kw):
-    base = dict(T=64, d=256, n_routed=16, n_groups=4, topk_groups=2, group_topn=2, topk=2, n_shared=1, inter=128)
+    base = dict(T=64, d=256, n_routed=16, n_groups=4, topk_groups=2, group_topn=2, topk=2, n_shared=1, inter=128,
+                batch_invariant=0)
     base.update(kw)
     return B.moe_shape(*[base[k] for k, _ in B.moe_shape._fields_])
 
@@ -46,6 +47,7 @@ def _route(shape, **ptrs):
 
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(T=0), B.MOE_E_INVALID, "non-positive"),
+    (dict(batch_invariant=2), B.MOE_E_INVALID, "batch_invariant"),
     (dict(n_routed=15), B.MOE_E_INVALID, "multiple of n_groups"),
     (dict(topk_groups=5), B.MOE_E_INVALID, "topk_groups"),
     (dict(topk=9), B.MOE_E_INVALID, "topk"),

@@ -329,6 +329,42 @@ def test_fp8_layer_pow2_act_scales():
         report(f"c2 fp8 pow2 out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["fp8"])
 
 
+@pytest.mark.parametrize("gemm", ["bf16", "fp8"])
+def test_batch_invariance(gemm):
+    """batch_invariant = 1: 100 tokens of a 4096-token batch, placed among other tokens in a 160-token batch,
+    and one of them alone, get bit-identical affinities, selections, gates and layer outputs. The default
+    mode's differing affinities are printed for contrast (its router K split follows T)."""
+    from dataclasses import replace
+    from moe_inputs import generate_tokens
+    cfg, inp = _inputs("c2", gemm=gemm, batch_invariant=1)
+    T = cfg.T
+    sel = np.random.default_rng(5).choice(T, 100, replace=False)
+    other = generate_tokens(cfg, DEV, step=3)[:60]
+    u_b = torch.cat([other[:30], inp["u"][torch.from_numpy(sel).to(DEV)], other[30:]]).contiguous()
+    u_c = inp["u"][int(sel[7])].reshape(1, -1).contiguous()
+    rows_b = np.arange(30, 130)
+    res = {}
+    for bi in (1, 0):
+        outs = []
+        for u in (inp["u"], u_b, u_c):
+            c = replace(cfg, T=u.shape[0], batch_invariant=bi)
+            layer = MoELayer(c, inp, DEV)
+            layer.forward(u)
+            torch.cuda.synchronize()
+            outs.append({k: getattr(layer, k).cpu() for k in ("scores", "topk_idx", "topk_gate", "out")})
+            del layer
+        res[bi] = outs
+    full, part, one = res[1]
+    for k in ("scores", "topk_idx", "topk_gate", "out"):
+        a = full[k][torch.from_numpy(sel)]
+        assert torch.equal(a, part[k][torch.from_numpy(rows_b)]), k
+        assert torch.equal(a[7:8], one[k]), k
+    full0, part0, _ = res[0]
+    n_diff = int((full0["scores"][torch.from_numpy(sel)] != part0["scores"][torch.from_numpy(rows_b)]).sum())
+    print(f"[parity] {gemm} batch-invariant mode: 0 differing results; default mode: {n_diff} of "
+          f"{100 * cfg.n_routed} affinities differ between the two batches")
+
+
 def test_quantize_weights_bit_exact():
     cfg, inp = _inputs("c2")
     w = inp["w_gate_up"][:3].contiguous()
