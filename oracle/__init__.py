@@ -9,8 +9,9 @@ layer computes, written from the DeepSeek-V3 pages:
   "Increasing Accumulation Precision", "Mantissa over Exponents" and "Online
   Quantization" of the FP8 framework; the SwiGLU paragraph.
 * "DeepSeek V3 / V4 Infra" (blog digest), section on V3 FP8 (1x128 activation
-  tiles, 128x128 weight blocks, promotion every 128 elements) and the 6hd
-  FLOP count per token-expert pair.
+  tiles, 128x128 weight blocks, promotion every 128 elements), the 6hd
+  FLOP count per token-expert pair, and the V4 post-training FP4 (MXFP4)
+  expert weights (``mxfp4.py``).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The GPU library never calls it, links
@@ -25,8 +26,11 @@ are "parity unpinned".
 """
 from .accumulation import keep_bits, limited_precision_gemm  # noqa: F401
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode  # noqa: F401
+from .mxfp4 import (  # noqa: F401
+    e2m1_decode, e2m1_encode, quantize_mxfp4, dequantize_mxfp4, pack_e2m1, unpack_e2m1, mxfp4_to_e4m3_blocks,
+)
 from .moe import (  # noqa: F401
     affinity, balance_stats, route, permute, swiglu_ffn, quantize_tiles, quantize_blocks,
-    dequantize_tiles, dequantize_blocks, ffn_fp8, combine, bias_update,
+    dequantize_tiles, dequantize_blocks, ffn_fp8, ffn_mxfp4, combine, bias_update,
     expert_ffn, layer_forward,
 )

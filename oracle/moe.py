@@ -266,18 +266,35 @@ def ffn_fp8(a, wgu_codes, wgu_scale, wd_codes, wd_scale, return_h=False, pow2_in
     pow2_input: the up-projection input takes power-of-two scales (the
     dispatched-activation variant); H keeps fp32 scales.
     """
+    return _ffn_quantised_acts(a, dequantize_blocks(wgu_codes, wgu_scale), dequantize_blocks(wd_codes, wd_scale),
+                               return_h, pow2_input)
+
+
+def _ffn_quantised_acts(a, wgu, wd, return_h=False, pow2_input=False):
+    """SwiGLU FFN over exact weight values wgu [2I, d], wd [d, I] (float64), with the activations of both
+    GEMMs quantised online per 1x128 tile (E4M3, fp32 scales; the input optionally with power-of-two
+    scales) and the products summed exactly in fp64."""
     a_codes, a_scale = quantize_tiles(a, pow2=pow2_input)
     a_dq = dequantize_tiles(a_codes, a_scale)
-    wgu = dequantize_blocks(wgu_codes, wgu_scale)
     I = wgu.shape[0] // 2
     gate = a_dq @ wgu[:I].T
     up = a_dq @ wgu[I:].T
     h32 = (silu(gate) * up).astype(F32)
     h_codes, h_scale = quantize_tiles(h32)
-    y = dequantize_tiles(h_codes, h_scale) @ dequantize_blocks(wd_codes, wd_scale).T
+    y = dequantize_tiles(h_codes, h_scale) @ wd.T
     if return_h:
         return y, dict(h32=h32, h_codes=h_codes, h_scale=h_scale, a_codes=a_codes, a_scale=a_scale)
     return y
+
+
+def ffn_mxfp4(a, wgu_codes, wgu_scales, wd_codes, wd_scales, return_h=False, pow2_input=False):
+    """The SwiGLU FFN with MXFP4 expert weights ("DeepSeek V3 / V4 Infra", V4 post-training FP4 QAT
+    section): weights given as E2M1 codes [2I, d] / [d, I] (one per value) with E8M0 scales per 32
+    consecutive K values ([2I, d/32] / [d, I/32]); activations quantised to E4M3 per 1x128 tile as in the
+    fp8 recipe. Products of an E2M1 and an E4M3 value and their sums are exact in fp64."""
+    from .mxfp4 import dequantize_mxfp4
+    return _ffn_quantised_acts(a, dequantize_mxfp4(wgu_codes, wgu_scales), dequantize_mxfp4(wd_codes, wd_scales),
+                               return_h, pow2_input)
 
 
 def expert_ffn(a, w_gate_up, w_down, gemm: str = "bf16", wq=None, pow2_input: bool = False):
