@@ -26,7 +26,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12               # bytes/s, MI355X published
-MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}
+# dense MFMA; E2M1 x E4M3 products run at the fp8 rate (the fp4 rate needs both operands in fp4/fp6)
+MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "mxfp4": 5.0e15, "f32": 157.3e12}
+# weight bytes per element: bf16 2, E4M3 1 (+ one fp32 per 128x128 block), E2M1 1/2 + one E8M0 byte per 32
+WEIGHT_BYTES = {"bf16": 2.0, "f32": 4.0, "fp8": 1.0 + 4.0 / 16384, "mxfp4": 0.5 + 1.0 / 32}
 METRIC = "MoE-layer fwd tokens/s at V3 shape + % of MFMA peak (bf16, fp8)"
 CALLS = ["route", "permute", "ffn_gate_up", "ffn_down", "combine", "bias_update"]
 
@@ -39,6 +42,8 @@ def parse():
     ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
     ap.add_argument("--batch-invariant", action="store_true",
                     help="router K split fixed by d, so per-token results do not depend on the batch")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="fp8 workloads: MXFP4 expert weights (E2M1 with E8M0 1x32 scales) instead of E4M3 blocks")
     ap.add_argument("--pow2-act-scales", action="store_true",
                     help="fp8: power-of-two scales on the up-projection input")
     ap.add_argument("--cpu-sample", type=int, default=32, help="tokens for the CPU oracle baseline (0: skip)")
@@ -48,7 +53,9 @@ def parse():
 
 
 FFN_SOURCES = {"bf16": ["ffn_bf16.hip", "gemm_pipe.h", "sched.h", "common.h"],
-               "fp8": ["ffn_fp8.hip", "gemm_pipe8.h", "gemm_pipe.h", "sched.h", "common.h"]}
+               "fp8": ["ffn_fp8.hip", "ffn_epi8.h", "gemm_pipe8.h", "gemm_pipe.h", "sched.h", "common.h"],
+               "mxfp4": ["ffn_fp4.hip", "ffn_epi8.h", "gemm_pipe4.h", "gemm_pipe8.h", "gemm_pipe.h", "sched.h",
+                         "common.h"]}
 
 
 def sources_hash(gemm: str) -> str:
@@ -129,7 +136,13 @@ def main():
     from moe_inputs import get_config, generate
     from mixture_experts_layer_gate_amd import MoELayer
 
-    cfg = get_config(args.config, batch_invariant=int(args.batch_invariant))
+    over = dict(batch_invariant=int(args.batch_invariant))
+    if args.mxfp4:
+        if get_config(args.config).gemm != "fp8":
+            print("bench.py: --mxfp4 applies to the fp8 workloads (c4, c5)", file=sys.stderr)
+            sys.exit(2)
+        over["gemm"] = "mxfp4"
+    cfg = get_config(args.config, **over)
     dev = "cuda"
     torch.cuda.set_device(0)
     inp = generate(cfg, dev)
@@ -175,7 +188,7 @@ def main():
     load = layer.expert_load.cpu().numpy()
     n_touch = touched_experts(load)
     T, d, I, K, N, Ns = cfg.T, cfg.d, cfg.inter, cfg.topk, cfg.n_routed, cfg.n_shared
-    wb = 1 if cfg.gemm == "fp8" else 2          # weight bytes per element
+    wb = WEIGHT_BYTES[cfg.gemm]                 # weight bytes per element (with scales)
     ab = 2                                      # u / out bytes per element (bf16)
     # dominant kernel: the gate/up projection of the routed and shared experts (one launch)
     gu_bytes = (n_touch + Ns) * 2 * I * d * wb + T * d * ab
@@ -215,7 +228,8 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.gemm,
         "data": "synthetic: seeded N(0,1) tokens, random-init N(0,0.02^2) weights of the workload's shape",
-        "config": {"workload": f"{cfg.name}: {cfg.description}", "T": T, "d": d, "n_routed": N,
+        "config": {"workload": f"{cfg.name}: {cfg.description}" + (", MXFP4 expert weights" if cfg.gemm == "mxfp4"
+                                                                     else ""), "T": T, "d": d, "n_routed": N,
                    "groups": cfg.n_groups, "topk_groups": cfg.topk_groups, "topk": K, "n_shared": Ns, "inter": I,
                    "gemm": cfg.gemm, "batch_invariant": bool(args.batch_invariant),
                    **({"act_scales": "pow2" if args.pow2_act_scales else "fp32"} if cfg.gemm == "fp8" else {})},

@@ -51,7 +51,10 @@ typedef enum {
   MOE_F32 = 0,     /* IEEE binary32 */
   MOE_BF16 = 1,    /* bfloat16 */
   MOE_F8E4M3 = 2,  /* OCP E4M3FN: bias 7, max 448, no infinities */
-  MOE_F8E4M3_POW2 = 3 /* E4M3FN codes with power-of-two tile scales (an a_dtype of moe_permute only) */
+  MOE_F8E4M3_POW2 = 3, /* E4M3FN codes with power-of-two tile scales (an a_dtype of moe_permute only) */
+  MOE_F4E2M1 = 4      /* OCP MXFP4 weights (a weight dtype only): E2M1 codes, two per byte with the
+                         even K index in the low nibble, one E8M0 scale byte (2^(b - 127)) per 32
+                         consecutive K values, in the tiled layout of moe_quantize_weights_mxfp4 */
 } moe_dtype;
 
 /* How moe_grouped_ffn finds the input row of output row r of expert e. */
@@ -149,31 +152,41 @@ moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* top
  * y[r] = (SiLU(x W_g^T) * (x W_u^T)) W_d^T for every row r of every expert
  * (SwiGLU paragraph of "DeepSeek_V3_Report: Annotation", beta = 1; the three
  * projections cost 6*d*I FLOPs per row, "DeepSeek V3 / V4 Infra", V4 EP section).
- *   w            weight dtype: MOE_F32 (a f32), MOE_BF16 (a bf16) or MOE_F8E4M3
+ *   w            weight dtype: MOE_F32 (a f32), MOE_BF16 (a bf16), MOE_F8E4M3
  *                (a is fp8 with a_scale; weights fp8 with 128x128 block scales;
  *                fp32 accumulation with the scales applied per 128-wide K chunk,
  *                section "Increasing Accumulation Precision"; the SwiGLU output
- *                is re-quantised per 1x128 tile along I before the down projection).
+ *                is re-quantised per 1x128 tile along I before the down projection)
+ *                or MOE_F4E2M1 (MXFP4 expert weights, "DeepSeek V3 / V4 Infra",
+ *                V4 post-training FP4 QAT; a and H as with MOE_F8E4M3, the E8M0
+ *                weight scales applied by the matrix instruction, fp32 accumulation).
  *   n_experts    experts in this call (routed N_r, or N_s for the shared experts).
  *   n_rows       total rows = expert_offsets[n_experts] (T*K routed, N_s*T shared).
  *   expert_offsets [n_experts + 1] int32 device array.
  *   mode, row_src  see moe_row_mode; row_src [n_rows] int32 for MOE_ROWS_GATHER, else NULL.
  *   a            input rows [a_rows, d]; a_scale [a_rows, d/128] fp32 for fp8, else NULL.
- *   w_gate_up    [n_experts, 2I, d]: gate rows [0, I) then up rows [I, 2I), K-contiguous.
- *   w_gu_scale   [n_experts, 2I/128, d/128] fp32 block scales (fp8 only, else NULL).
- *   w_down       [n_experts, d, I], K-contiguous.
- *   w_d_scale    [n_experts, d/128, I/128] fp32 block scales (fp8 only, else NULL).
+ *   w_gate_up    [n_experts, 2I, d]: gate rows [0, I) then up rows [I, 2I), K-contiguous
+ *                (MOE_F4E2M1: the tiled codes of moe_quantize_weights_mxfp4 with
+ *                gate_up = 1, I * d bytes per expert).
+ *   w_gu_scale   MOE_F8E4M3: [n_experts, 2I/128, d/128] fp32 block scales;
+ *                MOE_F4E2M1: the tiled scales (gate_up = 1, 2I * d/32 bytes per expert);
+ *                else NULL.
+ *   w_down       [n_experts, d, I], K-contiguous (MOE_F4E2M1: tiled codes with
+ *                gate_up = 0, ceil(d/256) * 256 * I/2 bytes per expert).
+ *   w_d_scale    MOE_F8E4M3: [n_experts, d/128, I/128] fp32; MOE_F4E2M1: tiled
+ *                scales (gate_up = 0, ceil(d/256) * 256 * I/32 bytes per expert); else NULL.
  *   y_dtype      MOE_F32 (only with w = MOE_F32) or MOE_BF16.
  *   y            out [n_rows, d].
  * Limits: d and I multiples of 128; with MOE_BF16, a_rows * d, n_rows * I and
- * 2 * I * d below 2^31 elements, with MOE_F8E4M3 below 2^32 and d, I <= 10240
- * (32-bit byte offsets); otherwise MOE_E_UNSUPPORTED.
+ * 2 * I * d below 2^31 elements, with MOE_F8E4M3 / MOE_F4E2M1 below 2^32 and
+ * d, I <= 10240 (32-bit byte offsets; MOE_F4E2M1: d, I <= 8192); otherwise
+ * MOE_E_UNSUPPORTED.
  */
 moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                            const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
                            const void* a, const float* a_scale, int32_t a_rows,
-                           const void* w_gate_up, const float* w_gu_scale,
-                           const void* w_down, const float* w_d_scale,
+                           const void* w_gate_up, const void* w_gu_scale,
+                           const void* w_down, const void* w_d_scale,
                            moe_dtype y_dtype, void* y, void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -182,8 +195,8 @@ moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_expert
  * moe_grouped_ffn(...) == moe_ffn_gate_up(...) into its workspace, then moe_ffn_down(...).
  * Arguments as in moe_grouped_ffn, plus the SwiGLU output
  *   h        [n_rows, I]: fp32 (w = MOE_F32), bf16 (w = MOE_BF16) or E4M3 codes
- *            (w = MOE_F8E4M3, quantised per 1x128 tile along I with h_scale).
- *   h_scale  [n_rows, I/128] fp32 for fp8, else NULL.
+ *            (w = MOE_F8E4M3 / MOE_F4E2M1, quantised per 1x128 tile along I with h_scale).
+ *   h_scale  [n_rows, I/128] fp32 for fp8 / mxfp4, else NULL.
  *   workspace device scratch of at least 128 bytes (the counters of the
  *            kernel's dynamic work queue, cleared by the call itself); it must
  *            not overlap h or another call's workspace that is in flight.
@@ -191,11 +204,11 @@ moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_expert
 moe_status moe_ffn_gate_up(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                            const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
                            const void* a, const float* a_scale, int32_t a_rows,
-                           const void* w_gate_up, const float* w_gu_scale,
+                           const void* w_gate_up, const void* w_gu_scale,
                            void* h, float* h_scale, void* workspace, size_t ws_bytes, void* stream);
 moe_status moe_ffn_down(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                         const int32_t* expert_offsets, const void* h, const float* h_scale,
-                        const void* w_down, const float* w_d_scale, moe_dtype y_dtype, void* y,
+                        const void* w_down, const void* w_d_scale, moe_dtype y_dtype, void* y,
                         void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -247,6 +260,34 @@ moe_status moe_balance_stats(const moe_shape* shape, const float* scores, const 
  */
 moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, const void* w_bf16,
                                 void* w_codes, float* w_scale, void* stream);
+
+/*
+ * moe_quantize_weights_mxfp4 -- MXFP4 (OCP microscaling FP4) quantisation of
+ * expert weights for MOE_F4E2M1 ("DeepSeek V3 / V4 Infra", V4 post-training FP4
+ * QAT of the MoE expert weights), written in the tiled layout the grouped FFN
+ * streams. For n_mats bf16 matrices [rows, cols] (cols = K, a multiple of 128),
+ * per 32 consecutive values of a row: k = floor(log2(amax)) - 2 (at least -127;
+ * 0 for an all-zero block), scale byte k + 127, codes E2M1 of x * 2^-k, round
+ * to nearest with ties to the even code, saturating at 6, sign bit from x.
+ *
+ * Layout. Rows go in tiles of 256, ntiles = ceil(rows / 256); tile row rw
+ * (0..255) of tile t holds matrix row
+ *   gate_up = 0:  256 t + rw (rows past the matrix: codes 0, scale byte 127);
+ *   gate_up = 1 (rows = 2I, I a multiple of 128, the gate rows then the up
+ *   rows): with j = (rw >> 5) & 3 and hc = 128 t + 64 (rw >> 7) + 32 (j & 1) +
+ *   (rw & 31), row hc for j < 2 (gate) and I + hc for j >= 2 (up), so that a
+ *   tile holds the gate and up rows of 128 H columns.
+ * codes  [n_mats][ntiles][K/64][8192] bytes: per 64-wide K step, the 32 code
+ *        bytes of K values 64s .. 64s+63 of tile row rw start at 32 rw; their
+ *        16-byte halves k16 = 0, 1 (K 64s + 32 k16 .. +31) sit at byte
+ *        32 rw + 16 (k16 ^ ((rw >> 3) & 1)); two codes per byte, the even K
+ *        index in the low nibble.
+ * scales [n_mats][ntiles][K/128][4][256] bytes: scale of tile row rw for the
+ *        32-value block 4c + b at [c][b][rw].
+ * Weight preparation, not part of a forward.
+ */
+moe_status moe_quantize_weights_mxfp4(int32_t n_mats, int32_t rows, int32_t cols, int32_t gate_up,
+                                      const void* w_bf16, void* w_codes, void* w_scale, void* stream);
 
 /* Host: bytes of workspace that any single call above needs for this shape,
  * with moe_grouped_ffn sized for T*(K + N_s) rows: the routed and the shared

@@ -17,7 +17,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_F8E4M3, MOE_F8E4M3_POW2 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_F8E4M3, MOE_F8E4M3_POW2, MOE_F4E2M1 = 0, 1, 2, 3, 4
 MOE_ROWS_DIRECT, MOE_ROWS_GATHER, MOE_ROWS_SEGMENT = 0, 1, 2
 
 _STATUS = {1: "MOE_E_INVALID", 2: "MOE_E_UNSUPPORTED", 3: "MOE_E_WORKSPACE", 4: "MOE_E_HIP"}
@@ -56,6 +56,7 @@ _SIGS = {
     "moe_balance_stats": [_S, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_bias_update": [_S, _P, ctypes.c_float, _P, _P],
     "moe_quantize_weights": [_I, _I, _I, _P, _P, _P, _P],
+    "moe_quantize_weights_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P],
     "moe_workspace_bytes": [_S, _I],
     "moe_last_error": [],
     "moe_version": [],
@@ -152,19 +153,32 @@ def moe_permute(shape: moe_shape, topk_idx, u, expert_offsets, perm_token, row_o
                              _ptr(a_scale), int(gather), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
+def _wscale_count(w: int, rows: int, cols: int) -> int:
+    """Weight-scale entries of one [rows, cols] matrix: fp32 per 128x128 block, or E8M0 bytes per 1x32 (MXFP4,
+    rows padded to whole 256-row tiles)."""
+    return mx_rows(rows) * cols // 32 if w == MOE_F4E2M1 else (rows // 128) * (cols // 128)
+
+
+def mx_rows(rows: int) -> int:
+    """Rows of a matrix in the tiled MXFP4 layout: whole 256-row tiles."""
+    return -(-rows // 256) * 256
+
+
 def moe_grouped_ffn(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_offsets, mode: int, row_src,
                     a, a_scale, a_rows: int, w_gate_up, w_gu_scale, w_down, w_d_scale, y, workspace=None,
                     stream=None):
     d, I = shape.d, shape.inter
+    wdiv = 2 if w == MOE_F4E2M1 else 1            # MXFP4: two codes per byte
     _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a, a_rows * d, "a")
-    _need(w_gate_up, n_experts * 2 * I * d, "w_gate_up"); _need(w_down, n_experts * d * I, "w_down")
+    _need(w_gate_up, n_experts * 2 * I * d // wdiv, "w_gate_up")
+    _need(w_down, n_experts * (mx_rows(d) if wdiv == 2 else d) * I // wdiv, "w_down")
     _need(y, n_rows * d, "y")
     if mode == MOE_ROWS_GATHER:
         _need(row_src, n_rows, "row_src")
-    if w == MOE_F8E4M3:
+    if w in (MOE_F8E4M3, MOE_F4E2M1):
         _need(a_scale, a_rows * (d // 128), "a_scale")
-        _need(w_gu_scale, n_experts * (2 * I // 128) * (d // 128), "w_gu_scale")
-        _need(w_d_scale, n_experts * (d // 128) * (I // 128), "w_d_scale")
+        _need(w_gu_scale, n_experts * _wscale_count(w, 2 * I, d), "w_gu_scale")
+        _need(w_d_scale, n_experts * _wscale_count(w, d, I), "w_d_scale")
     _check(lib().moe_grouped_ffn(ctypes.byref(shape), w, n_experts, n_rows, _ptr(expert_offsets), mode,
                                  _ptr(row_src), _ptr(a), _ptr(a_scale), a_rows, _ptr(w_gate_up), _ptr(w_gu_scale),
                                  _ptr(w_down), _ptr(w_d_scale), _dt(y), _ptr(y), _ptr(workspace),
@@ -174,13 +188,14 @@ def moe_grouped_ffn(shape: moe_shape, w: int, n_experts: int, n_rows: int, exper
 def moe_ffn_gate_up(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_offsets, mode: int, row_src,
                     a, a_scale, a_rows: int, w_gate_up, w_gu_scale, h, h_scale=None, workspace=None, stream=None):
     d, I = shape.d, shape.inter
+    wdiv = 2 if w == MOE_F4E2M1 else 1
     _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a, a_rows * d, "a")
-    _need(w_gate_up, n_experts * 2 * I * d, "w_gate_up"); _need(h, n_rows * I, "h")
+    _need(w_gate_up, n_experts * 2 * I * d // wdiv, "w_gate_up"); _need(h, n_rows * I, "h")
     if mode == MOE_ROWS_GATHER:
         _need(row_src, n_rows, "row_src")
-    if w == MOE_F8E4M3:
+    if w in (MOE_F8E4M3, MOE_F4E2M1):
         _need(a_scale, a_rows * (d // 128), "a_scale")
-        _need(w_gu_scale, n_experts * (2 * I // 128) * (d // 128), "w_gu_scale")
+        _need(w_gu_scale, n_experts * _wscale_count(w, 2 * I, d), "w_gu_scale")
         _need(h_scale, n_rows * (I // 128), "h_scale")
     _check(lib().moe_ffn_gate_up(ctypes.byref(shape), w, n_experts, n_rows, _ptr(expert_offsets), mode,
                                  _ptr(row_src), _ptr(a), _ptr(a_scale), a_rows, _ptr(w_gate_up), _ptr(w_gu_scale),
@@ -190,11 +205,12 @@ def moe_ffn_gate_up(shape: moe_shape, w: int, n_experts: int, n_rows: int, exper
 def moe_ffn_down(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_offsets, h, h_scale, w_down,
                  w_d_scale, y, workspace=None, stream=None):
     d, I = shape.d, shape.inter
+    wdiv = 2 if w == MOE_F4E2M1 else 1
     _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(h, n_rows * I, "h")
-    _need(w_down, n_experts * d * I, "w_down"); _need(y, n_rows * d, "y")
-    if w == MOE_F8E4M3:
+    _need(w_down, n_experts * (mx_rows(d) if wdiv == 2 else d) * I // wdiv, "w_down"); _need(y, n_rows * d, "y")
+    if w in (MOE_F8E4M3, MOE_F4E2M1):
         _need(h_scale, n_rows * (I // 128), "h_scale")
-        _need(w_d_scale, n_experts * (d // 128) * (I // 128), "w_d_scale")
+        _need(w_d_scale, n_experts * _wscale_count(w, d, I), "w_d_scale")
     _check(lib().moe_ffn_down(ctypes.byref(shape), w, n_experts, n_rows, _ptr(expert_offsets), _ptr(h),
                               _ptr(h_scale), _ptr(w_down), _ptr(w_d_scale), _dt(y), _ptr(y), _ptr(workspace),
                               _nbytes(workspace), _stream(stream)))
@@ -232,3 +248,12 @@ def moe_quantize_weights(w, codes, scale, stream=None):
     n, rows, cols = w.shape
     _need(codes, n * rows * cols, "codes"); _need(scale, n * (rows // 128) * (cols // 128), "scale")
     _check(lib().moe_quantize_weights(n, rows, cols, _ptr(w), _ptr(codes), _ptr(scale), _stream(stream)))
+
+
+def moe_quantize_weights_mxfp4(w, codes, scales, gate_up: bool, stream=None):
+    """w [n, rows, cols] bf16 -> MXFP4 in the tiled layout: codes n * ceil(rows/256)*256 * cols/2 bytes, scales
+    n * ceil(rows/256)*256 * cols/32 bytes (gate_up: rows = 2I, gate rows then up rows)."""
+    n, rows, cols = w.shape
+    _need(codes, n * mx_rows(rows) * cols // 2, "codes"); _need(scales, n * mx_rows(rows) * (cols // 32), "scales")
+    _check(lib().moe_quantize_weights_mxfp4(n, rows, cols, int(gate_up), _ptr(w), _ptr(codes), _ptr(scales),
+                                            _stream(stream)))

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "route.hip", "permute.hip", "combine.hip", "ffn_f32.hip", "ffn_bf16.hip",
-           "ffn_fp8.hip", "quant.hip", "balance.hip"]
+           "ffn_fp8.hip", "ffn_fp4.hip", "quant.hip", "balance.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # no packed fp32 instructions in device code
@@ -31,7 +31,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # VALU between K chunks, so the accumulators must be MFMA destinations in
 # VGPRs (left to itself the compiler keeps them in AGPRs and copies every
 # element out and back for each multiply).
-EXTRA = {"ffn_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"ffn_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "ffn_fp4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

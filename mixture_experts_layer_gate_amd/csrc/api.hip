@@ -196,12 +196,14 @@ moe_status check_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int
   SUPPORT(n_experts <= 4096, "grouped_ffn: n_experts (%d) > 4096", n_experts);
   SUPPORT(static_cast<long long>(n_rows) * (d > I ? d : I) < (1LL << 40), "grouped_ffn: too many rows");
   REQUIRE(offsets != nullptr, "grouped_ffn: expert_offsets is NULL");
-  REQUIRE(w == MOE_F32 || w == MOE_BF16 || w == MOE_F8E4M3, "grouped_ffn: bad weight dtype %d", static_cast<int>(w));
-  SUPPORT(w != MOE_F8E4M3 || (d <= 10240 && I <= 10240), "grouped_ffn: the fp8 path needs d and inter <= 10240");
-  // the fp8 kernels address codes and scales through 32-bit byte offsets
-  SUPPORT(w != MOE_F8E4M3 || (static_cast<long long>(n_rows) * I < (1LL << 32) &&
-                              static_cast<long long>(2 * I) * d < (1LL << 32)),
-          "grouped_ffn: fp8 path needs n_rows * inter and 2 * inter * d below 2^32");
+  REQUIRE(w == MOE_F32 || w == MOE_BF16 || w == MOE_F8E4M3 || w == MOE_F4E2M1, "grouped_ffn: bad weight dtype %d",
+          static_cast<int>(w));
+  const bool q8 = w == MOE_F8E4M3 || w == MOE_F4E2M1;   // E4M3 activations and H
+  SUPPORT(!q8 || (d <= 10240 && I <= 10240), "grouped_ffn: the fp8 / mxfp4 paths need d and inter <= 10240");
+  SUPPORT(w != MOE_F4E2M1 || (d <= 8192 && I <= 8192), "grouped_ffn: the mxfp4 path needs d and inter <= 8192");
+  // the fp8 / mxfp4 kernels address codes and scales through 32-bit byte offsets
+  SUPPORT(!q8 || (static_cast<long long>(n_rows) * I < (1LL << 32) && static_cast<long long>(2 * I) * d < (1LL << 32)),
+          "grouped_ffn: fp8 / mxfp4 paths need n_rows * inter and 2 * inter * d below 2^32");
   // the bf16 kernels address H and one expert's weight matrices through 32-bit byte offsets
   SUPPORT(w != MOE_BF16 || (static_cast<long long>(n_rows) * I * 2 < (1LL << 32) &&
                             static_cast<long long>(2 * I) * d * 2 < (1LL << 32)),
@@ -212,37 +214,40 @@ moe_status check_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int
 
 moe_status check_gate_up(const moe_shape* shape, moe_dtype w, moe_row_mode mode, const int32_t* row_src,
                          const void* a, const float* a_scale, int32_t a_rows, const void* w_gate_up,
-                         const float* w_gu_scale) {
+                         const void* w_gu_scale) {
   REQUIRE(a && w_gate_up, "grouped_ffn: a or w_gate_up is NULL");
   REQUIRE(a_rows > 0, "grouped_ffn: a_rows must be positive");
   SUPPORT(w != MOE_BF16 || static_cast<long long>(a_rows) * shape->d * 2 < (1LL << 32),
           "grouped_ffn: bf16 path needs a_rows * d below 2^31 elements");
-  SUPPORT(w != MOE_F8E4M3 || static_cast<long long>(a_rows) * shape->d < (1LL << 32),
-          "grouped_ffn: fp8 path needs a_rows * d below 2^32");
+  SUPPORT((w != MOE_F8E4M3 && w != MOE_F4E2M1) || static_cast<long long>(a_rows) * shape->d < (1LL << 32),
+          "grouped_ffn: fp8 / mxfp4 paths need a_rows * d below 2^32");
   REQUIRE(mode == MOE_ROWS_DIRECT || mode == MOE_ROWS_GATHER || mode == MOE_ROWS_SEGMENT,
           "grouped_ffn: bad row mode %d", static_cast<int>(mode));
   REQUIRE(mode != MOE_ROWS_GATHER || row_src != nullptr, "grouped_ffn: MOE_ROWS_GATHER needs row_src");
-  if (w == MOE_F8E4M3) REQUIRE(a_scale && w_gu_scale, "grouped_ffn: fp8 needs a_scale and w_gu_scale");
+  if (w == MOE_F8E4M3 || w == MOE_F4E2M1)
+    REQUIRE(a_scale && w_gu_scale, "grouped_ffn: fp8 / mxfp4 need a_scale and w_gu_scale");
   return MOE_OK;
 }
 
-moe_status check_down(moe_dtype w, const void* w_down, const float* w_d_scale, moe_dtype y_dtype, const void* y) {
+moe_status check_down(moe_dtype w, const void* w_down, const void* w_d_scale, moe_dtype y_dtype, const void* y) {
   REQUIRE(w_down && y, "grouped_ffn: w_down or y is NULL");
   REQUIRE(y_dtype == MOE_BF16 || (y_dtype == MOE_F32 && w == MOE_F32),
           "grouped_ffn: y_dtype must be MOE_BF16 (or MOE_F32 with MOE_F32 weights)");
-  if (w == MOE_F8E4M3) REQUIRE(w_d_scale != nullptr, "grouped_ffn: fp8 needs w_d_scale");
+  if (w == MOE_F8E4M3 || w == MOE_F4E2M1) REQUIRE(w_d_scale != nullptr, "grouped_ffn: fp8 / mxfp4 need w_d_scale");
   return MOE_OK;
 }
 
 hipError_t run_gate_up(moe_dtype w, const moe::FfnArgs& p, hipStream_t st) {
   if (w == MOE_F32) return moe::launch_ffn_f32_gate_up(p, st);
   if (w == MOE_BF16) return moe::launch_ffn_bf16_gate_up(p, st);
+  if (w == MOE_F4E2M1) return moe::launch_ffn_fp4_gate_up(p, st);
   return moe::launch_ffn_fp8_gate_up(p, st);
 }
 
 hipError_t run_down(moe_dtype w, const moe::FfnArgs& p, hipStream_t st) {
   if (w == MOE_F32) return moe::launch_ffn_f32_down(p, st);
   if (w == MOE_BF16) return moe::launch_ffn_bf16_down(p, st);
+  if (w == MOE_F4E2M1) return moe::launch_ffn_fp4_down(p, st);
   return moe::launch_ffn_fp8_down(p, st);
 }
 
@@ -252,8 +257,8 @@ extern "C" {
 
 moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                            const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src, const void* a,
-                           const float* a_scale, int32_t a_rows, const void* w_gate_up, const float* w_gu_scale,
-                           const void* w_down, const float* w_d_scale, moe_dtype y_dtype, void* y, void* workspace,
+                           const float* a_scale, int32_t a_rows, const void* w_gate_up, const void* w_gu_scale,
+                           const void* w_down, const void* w_d_scale, moe_dtype y_dtype, void* y, void* workspace,
                            size_t ws_bytes, void* stream) {
   g_err.clear();
   if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 0); r != MOE_OK) return r;
@@ -265,7 +270,7 @@ moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_expert
   if (!workspace || ws_bytes < need)
     return fail(MOE_E_WORKSPACE, "grouped_ffn: workspace of %zu bytes < %zu needed", ws_bytes, need);
   float* h_scale = nullptr;
-  if (w == MOE_F8E4M3)
+  if (w == MOE_F8E4M3 || w == MOE_F4E2M1)
     h_scale = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(static_cast<size_t>(n_rows) * I));
   int* queue = reinterpret_cast<int*>(static_cast<char*>(workspace) + moe::ffn_queue_offset(w, n_rows, I));
   moe::FfnArgs p{d, I, n_experts, n_rows, a_rows, expert_offsets, mode, row_src, a, a_scale, w_gate_up, w_gu_scale,
@@ -279,14 +284,14 @@ moe_status moe_grouped_ffn(const moe_shape* shape, moe_dtype w, int32_t n_expert
 
 moe_status moe_ffn_gate_up(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                            const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src, const void* a,
-                           const float* a_scale, int32_t a_rows, const void* w_gate_up, const float* w_gu_scale,
+                           const float* a_scale, int32_t a_rows, const void* w_gate_up, const void* w_gu_scale,
                            void* h, float* h_scale, void* workspace, size_t ws_bytes, void* stream) {
   g_err.clear();
   if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 1); r != MOE_OK) return r;
   if (moe_status r = check_gate_up(shape, w, mode, row_src, a, a_scale, a_rows, w_gate_up, w_gu_scale); r != MOE_OK)
     return r;
   REQUIRE(h != nullptr, "ffn_gate_up: h is NULL");
-  REQUIRE(w != MOE_F8E4M3 || h_scale != nullptr, "ffn_gate_up: fp8 needs h_scale");
+  REQUIRE((w != MOE_F8E4M3 && w != MOE_F4E2M1) || h_scale != nullptr, "ffn_gate_up: fp8 / mxfp4 need h_scale");
   if (!workspace || ws_bytes < moe::kFfnQueueBytes)
     return fail(MOE_E_WORKSPACE, "ffn_gate_up: workspace of %zu bytes < %zu needed", ws_bytes, moe::kFfnQueueBytes);
   moe::FfnArgs p{shape->d, shape->inter, n_experts, n_rows, a_rows, expert_offsets, mode, row_src, a, a_scale,
@@ -297,13 +302,13 @@ moe_status moe_ffn_gate_up(const moe_shape* shape, moe_dtype w, int32_t n_expert
 
 moe_status moe_ffn_down(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
                         const int32_t* expert_offsets, const void* h, const float* h_scale, const void* w_down,
-                        const float* w_d_scale, moe_dtype y_dtype, void* y, void* workspace, size_t ws_bytes,
+                        const void* w_d_scale, moe_dtype y_dtype, void* y, void* workspace, size_t ws_bytes,
                         void* stream) {
   g_err.clear();
   if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 2); r != MOE_OK) return r;
   if (moe_status r = check_down(w, w_down, w_d_scale, y_dtype, y); r != MOE_OK) return r;
   REQUIRE(h != nullptr, "ffn_down: h is NULL");
-  REQUIRE(w != MOE_F8E4M3 || h_scale != nullptr, "ffn_down: fp8 needs h_scale");
+  REQUIRE((w != MOE_F8E4M3 && w != MOE_F4E2M1) || h_scale != nullptr, "ffn_down: fp8 / mxfp4 need h_scale");
   if (!workspace || ws_bytes < moe::kFfnQueueBytes)
     return fail(MOE_E_WORKSPACE, "ffn_down: workspace of %zu bytes < %zu needed", ws_bytes, moe::kFfnQueueBytes);
   moe::FfnArgs p{shape->d, shape->inter, n_experts, n_rows, n_rows, expert_offsets, MOE_ROWS_DIRECT, nullptr,
@@ -365,6 +370,20 @@ moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, cons
   auto st = static_cast<hipStream_t>(stream);
   return finish(moe::launch_quantize_weights(n_mats, rows, cols, w_bf16, w_codes, w_scale, st),
                 "moe_quantize_weights", st);
+}
+
+moe_status moe_quantize_weights_mxfp4(int32_t n_mats, int32_t rows, int32_t cols, int32_t gate_up, const void* w_bf16,
+                                      void* w_codes, void* w_scale, void* stream) {
+  g_err.clear();
+  REQUIRE(n_mats > 0 && rows > 0 && cols > 0, "quantize_weights_mxfp4: sizes must be positive");
+  REQUIRE(gate_up == 0 || gate_up == 1, "quantize_weights_mxfp4: gate_up must be 0 or 1");
+  SUPPORT(cols % 128 == 0, "quantize_weights_mxfp4: cols (%d) must be a multiple of 128", cols);
+  SUPPORT(!gate_up || rows % 256 == 0, "quantize_weights_mxfp4: gate_up needs rows = 2I with I a multiple of 128");
+  REQUIRE(w_bf16 && w_codes && w_scale, "quantize_weights_mxfp4: a required pointer is NULL");
+  SUPPORT(static_cast<long long>(n_mats) * (rows + 255) * cols < (1LL << 40), "quantize_weights_mxfp4: too many values");
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_quantize_weights_mxfp4(n_mats, rows, cols, gate_up, w_bf16, w_codes, w_scale, st),
+                "moe_quantize_weights_mxfp4", st);
 }
 
 }  // extern "C"

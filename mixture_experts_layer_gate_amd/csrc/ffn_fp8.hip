@@ -18,117 +18,20 @@
 #include <mutex>
 
 #include "common.h"
+#include "ffn_epi8.h"
 #include "gemm_pipe8.h"
 #include "launch.h"
 #include "sched.h"
 
 namespace moe {
 
-using P8 = Pipe8;
-constexpr int kMaxSub8 = P8::BT / 32;   // 32-row sub-tiles per block
 constexpr int kMaxExperts8 = 4096;
-
-__device__ __forceinline__ int live_token_subtiles8(int nsub) {
-  return clampi((nsub - p8_wt() + 1) / 2, 0, P8::TT);
-}
-
-// Output column (weight row within the tile) of accumulator element 4q of
-// weight sub-tile j: four consecutive columns per lane.
-__device__ __forceinline__ int p8_wcol(int j, int q) {
-  const int l = threadIdx.x & 63;
-  return p8_ww() * (P8::BW / 2) + j * 32 + 8 * q + 4 * (l >> 5);
-}
-
-// Tile row of token sub-tile i of this lane.
-__device__ __forceinline__ int p8_token_row(int i) {
-  const int l = threadIdx.x & 63;
-  return 32 * (2 * i + p8_wt()) + (l & 31);
-}
-
-// Barrier for LDS data only: the ring's loads stay in flight.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// gate/up epilogue of output-column tile nb0 + seg: SwiGLU in fp32 (this wave
-// holds 64 of the tile's 128 H columns of each row: gate sub-tiles 0, 1 with
-// up sub-tiles 2, 3), then the 1x128 re-quantisation of H over the tile's
-// 128 columns (row amax exchanged through LDS).
-template <int MS>
-struct GateUpEpi8 {
-  const Unit& un;
-  int I, nb0;
-  uint8_t* lds;
-  uint8_t* __restrict__ Hq;
-  float* __restrict__ Hs;
-  __device__ __forceinline__ void operator()(int seg, f32x16 (&acc)[P8::TW][P8::TT]) {
-    const int l = threadIdx.x & 63, ww = p8_ww(), nb = nb0 + seg;
-    float* amax_x = reinterpret_cast<float*>(lds + P8::AMAX_OFF);   // [2][BT]
-    float hv[P8::TT][2][16];
-#pragma unroll
-    for (int i = 0; i < MS; ++i) {
-      float x = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          hv[i][j][v] = silu(acc[j][i][v]) * acc[j + 2][i][v];
-          x = fmaxf(x, __builtin_fabsf(hv[i][j][v]));
-        }
-      x = fmaxf(x, __shfl_xor(x, 32, kWave));
-      if (l < 32) amax_x[ww * P8::BT + p8_token_row(i)] = x;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < MS; ++i) {
-      const int tr = p8_token_row(i);
-      const float amax = fmaxf(amax_x[tr], amax_x[P8::BT + tr]);
-      if (tr < un.rows) {
-        const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
-        uint8_t* hrow = Hq + static_cast<size_t>(un.m0 + tr) * I + nb * 128 + ww * 64 + 4 * (l >> 5);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<uint32_t*>(hrow + j * 32 + 8 * q) =
-                f32x4_to_e4m3(hv[i][j][4 * q] * inv, hv[i][j][4 * q + 1] * inv, hv[i][j][4 * q + 2] * inv,
-                              hv[i][j][4 * q + 3] * inv);
-        if (ww == 0 && l < 32) Hs[static_cast<size_t>(un.m0 + tr) * (I / 128) + nb] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
-      }
-    }
-    // amax_x is next written in the following tile's epilogue, after at least
-    // one ring barrier that every wave reaches with these reads consumed
-  }
-};
-
-// down epilogue of output-column tile nb0 + seg: bf16 rows of y.
-template <int MS>
-struct DownEpi8 {
-  const Unit& un;
-  int d, nb0;
-  uint16_t* __restrict__ y;
-  __device__ __forceinline__ void operator()(int seg, f32x16 (&acc)[P8::TW][P8::TT]) {
-#pragma unroll
-    for (int i = 0; i < MS; ++i) {
-      const int tr = p8_token_row(i);
-      if (tr < un.rows) {
-        uint16_t* yrow = y + static_cast<size_t>(un.m0 + tr) * d + (nb0 + seg) * P8::BW;
-#pragma unroll
-        for (int j = 0; j < P8::TW; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if ((nb0 + seg) * P8::BW + p8_wcol(j, q) < d)   // the 128-column last tile of d % 256 == 128
-              *reinterpret_cast<u32x2*>(yrow + p8_wcol(j, q)) =
-                  u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
-                        pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])};
-      }
-    }
-  }
-};
 
 template <int MS, int LT>
 __device__ __forceinline__ void gate_up8_unit(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
                                               const Unit& un, int nb0, int nseg, uint8_t* lds,
                                               uint8_t* __restrict__ Hq, float* __restrict__ Hs) {
-  GateUpEpi8<MS> epi{un, I, nb0, lds, Hq, Hs};
+  GateUpEpi8<MS, P8::AMAX_OFF> epi{un, I, nb0, lds, Hq, Hs};
   pipe8_stream<MS, LT, true>(rows, srs, d, nseg, 128 * d, lds, epi);   // the next tile's rows: 128 further
 }
 
@@ -289,7 +192,7 @@ hipError_t launch_ffn_fp8_gate_up(const FfnArgs& p, hipStream_t st) {
   hipLaunchKernelGGL(ffn_gate_up_fp8_kernel, dim3(f8_grid(mblocks * cdiv(p.I / 128, P8::MAX_SEG))), dim3(P8::NT), lds,
                      st, p.d, p.I,
                      p.n_experts, p.n_rows, p.a_rows, p.offsets, p.mode, p.row_src,
-                     static_cast<const uint8_t*>(p.a), p.a_scale, static_cast<const uint8_t*>(p.w_gu), p.w_gu_scale,
+                     static_cast<const uint8_t*>(p.a), p.a_scale, static_cast<const uint8_t*>(p.w_gu), static_cast<const float*>(p.w_gu_scale),
                      static_cast<uint8_t*>(p.h), p.h_scale, q);
   return hipGetLastError();
 }
@@ -305,7 +208,7 @@ hipError_t launch_ffn_fp8_down(const FfnArgs& p, hipStream_t st) {
                      lds,
                      st, p.d, p.I,
                      p.n_experts, p.n_rows, p.offsets, static_cast<const uint8_t*>(p.h), p.h_scale,
-                     static_cast<const uint8_t*>(p.w_d), p.w_d_scale, static_cast<uint16_t*>(p.y), q);
+                     static_cast<const uint8_t*>(p.w_d), static_cast<const float*>(p.w_d_scale), static_cast<uint16_t*>(p.y), q);
   return hipGetLastError();
 }
 

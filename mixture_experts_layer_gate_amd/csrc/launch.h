@@ -63,9 +63,9 @@ struct FfnArgs {
   const void* a;
   const float* a_scale;
   const void* w_gu;
-  const float* w_gu_scale;
+  const void* w_gu_scale;   // fp32 per 128x128 block (E4M3 weights) or E8M0 bytes (MXFP4)
   const void* w_d;
-  const float* w_d_scale;
+  const void* w_d_scale;
   moe_dtype y_dtype;
   void* y;
   void* h;         // SwiGLU output [n_rows, I]
@@ -83,9 +83,13 @@ hipError_t launch_ffn_bf16_gate_up(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_bf16_down(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_fp8_gate_up(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_fp8_down(const FfnArgs& a, hipStream_t st);
+hipError_t launch_ffn_fp4_gate_up(const FfnArgs& a, hipStream_t st);
+hipError_t launch_ffn_fp4_down(const FfnArgs& a, hipStream_t st);
 
 // ---- weight preparation
 hipError_t launch_quantize_weights(int n_mats, int rows, int cols, const void* w, void* codes, float* scale,
                                    hipStream_t st);
+hipError_t launch_quantize_weights_mxfp4(int n_mats, int rows, int cols, int gate_up, const void* w, void* codes,
+                                         void* scales, hipStream_t st);
 
 }  // namespace moe

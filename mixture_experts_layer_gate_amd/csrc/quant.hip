@@ -60,4 +60,99 @@ hipError_t launch_quantize_weights(int n_mats, int rows, int cols, const void* w
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- MXFP4
+// OCP microscaling FP4 of bf16 weights along each row ("DeepSeek V3 / V4
+// Infra", V4 post-training FP4 QAT of the expert weights): per 32 consecutive
+// values of a row, k = floor(log2(amax)) - 2 (at least -127; 0 for an
+// all-zero block), E8M0 scale byte k + 127, and E2M1 codes of x * 2^-k, round
+// to nearest with ties to the even code, saturating at 6, sign from x.
+
+// E2M1 code of y: count the decision points below |y| (a tie goes to the even
+// code: 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0).
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = fminf(__builtin_fabsf(y), 6.0f);
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(y) >> 31) << 3);
+}
+
+// One thread per (tile row, 32-value block); a wave covers 64 consecutive tile
+// rows of one K block, so its scale bytes are one contiguous run. Output in
+// the tiled layout the MXFP4 grouped FFN streams (see moe_quantize_weights_mxfp4):
+// tile row rw of tile t is matrix row 256 t + rw, or for gate_up the gate / up
+// row of the tile's 128 H columns that the tile's waves pair; rows past the
+// matrix are zero.
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(long long n_blocks, int rows, int cols, int gate_up,
+                                                             const uint16_t* __restrict__ w,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  const int kbs = cols / 32, ntiles = cdiv(rows, 256), half = rows / 2;
+  for (long long b = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; b < n_blocks;
+       b += static_cast<long long>(gridDim.x) * blockDim.x) {
+    const int rw = static_cast<int>(b & 255);
+    long long rest = b >> 8;
+    const int kb = static_cast<int>(rest % kbs);
+    rest /= kbs;
+    const int t = static_cast<int>(rest % ntiles);
+    const long long mat = rest / ntiles;
+    int row;
+    if (gate_up) {
+      const int j = (rw >> 5) & 3;
+      const int hc = 128 * t + 64 * (rw >> 7) + 32 * (j & 1) + (rw & 31);
+      row = j >= 2 ? half + hc : hc;
+    } else {
+      row = 256 * t + rw;
+    }
+    float x[32];
+    if (row < rows) {
+      const uint16_t* src = w + (static_cast<size_t>(mat) * rows + row) * cols + static_cast<size_t>(kb) * 32;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 p = *reinterpret_cast<const uint4*>(src + 8 * v);
+        const uint32_t ww[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[8 * v + 2 * i] = __uint_as_float(ww[i] << 16);
+          x[8 * v + 2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, __builtin_fabsf(x[i]));
+    int k = 0;
+    if (amax > 0.0f) {
+      int e;
+      (void)__builtin_frexpf(amax, &e);   // amax = m 2^e, 0.5 <= m < 1: floor(log2 amax) = e - 1
+      k = max(e - 3, -127);
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= e2m1_code(__builtin_ldexpf(x[8 * v + i], -k)) << (4 * i);
+      o[v] = word;
+    }
+    const size_t tile = static_cast<size_t>(mat) * ntiles + t;
+    const size_t coff = (tile * (cols / 64) + (kb >> 1)) * 8192 + 32 * rw + 16 * ((kb & 1) ^ ((rw >> 3) & 1));
+    *reinterpret_cast<uint4*>(codes + coff) = make_uint4(o[0], o[1], o[2], o[3]);
+    scales[(tile * (cols / 128) + (kb >> 2)) * 1024 + (kb & 3) * 256 + rw] = static_cast<uint8_t>(k + 127);
+  }
+}
+
+hipError_t launch_quantize_weights_mxfp4(int n_mats, int rows, int cols, int gate_up, const void* w, void* codes,
+                                         void* scales, hipStream_t st) {
+  const long long n = static_cast<long long>(n_mats) * cdiv(rows, 256) * 256 * (cols / 32);
+  long long blocks = (n + 255) / 256;
+  const long long cap = static_cast<long long>(device_cu_count()) * 32;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, n, rows, cols,
+                     gate_up, static_cast<const uint16_t*>(w), static_cast<uint8_t*>(codes),
+                     static_cast<uint8_t*>(scales));
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -46,7 +46,7 @@ class MoELayer:
     """One MoE layer on the current CUDA device.
 
     cfg: an object with T, d, n_routed, n_groups, topk_groups, group_topn,
-    topk, n_shared, inter, gemm ("f32" | "bf16" | "fp8"), gamma.
+    topk, n_shared, inter, gemm ("f32" | "bf16" | "fp8" | "mxfp4"), gamma.
     weights: w_gate_up [N_r,2I,d], w_down [N_r,d,I], s_gate_up [N_s,2I,d],
     s_down [N_s,d,I] (fp32 or bf16), centroids [N_r,d], bias [N_r] fp32.
     For fp8 the bf16 weights are block-quantised on the device by
@@ -58,7 +58,9 @@ class MoELayer:
         self.cfg = cfg
         self.shape = B.moe_shape.of(cfg)
         self.dev = torch.device(device)
-        self.gemm = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_F8E4M3}[cfg.gemm]
+        self.gemm = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_F8E4M3, "mxfp4": B.MOE_F4E2M1}[cfg.gemm]
+        # E4M3 activations and H (fp8 and MXFP4 weights)
+        self.q8 = self.gemm in (B.MOE_F8E4M3, B.MOE_F4E2M1)
         self.gather_in_gemm = gather_in_gemm
         # fp8: the up-projection input quantised with power-of-two tile scales
         self.a_qdtype = B.MOE_F8E4M3_POW2 if pow2_act_scales else B.MOE_F8E4M3
@@ -71,11 +73,17 @@ class MoELayer:
         for kind in ("gate_up", "down"):
             # routed experts, then shared ones, in one array; the per-kind views alias it
             both = torch.cat([to(weights["w_" + kind]), to(weights["s_" + kind])]) if Ns else to(weights["w_" + kind])
-            if self.gemm == B.MOE_F8E4M3:
+            if self.q8:
                 n, r, c = both.shape
-                codes = torch.empty((n, r, c), dtype=torch.uint8, device=self.dev)
-                scale = torch.empty((n, r // 128, c // 128), dtype=torch.float32, device=self.dev)
-                B.moe_quantize_weights(both, codes, scale)
+                if self.gemm == B.MOE_F8E4M3:
+                    codes = torch.empty((n, r, c), dtype=torch.uint8, device=self.dev)
+                    scale = torch.empty((n, r // 128, c // 128), dtype=torch.float32, device=self.dev)
+                    B.moe_quantize_weights(both, codes, scale)
+                else:
+                    rt = B.mx_rows(r)               # tiled MXFP4: whole 256-row tiles
+                    codes = torch.empty((n, rt, c // 2), dtype=torch.uint8, device=self.dev)
+                    scale = torch.empty((n, rt, c // 32), dtype=torch.uint8, device=self.dev)
+                    B.moe_quantize_weights_mxfp4(both, codes, scale, gate_up=(kind == "gate_up"))
                 if keep_bf16:
                     self.w["w_" + kind + "_bf16"], self.w["s_" + kind + "_bf16"] = both[:N], both[N:]
                 del both
@@ -110,7 +118,7 @@ class MoELayer:
         self.y_routed = self.y_all[:T * K]
         self.y_shared = self.y_all[T * K:]
         self.out = torch.empty((T, d), dtype=self.act_dtype, device=dev)
-        if self.gemm == B.MOE_F8E4M3:
+        if self.q8:
             # u quantised once per token (1x128 tiles); the GEMMs gather its rows
             self.u_q = torch.empty((T, d), dtype=torch.uint8, device=dev)
             self.u_scale = torch.empty((T, d // 128), dtype=torch.float32, device=dev)
@@ -133,7 +141,7 @@ class MoELayer:
         return f, P, loss
 
     def permute(self, u):
-        if self.gemm == B.MOE_F8E4M3:
+        if self.q8:
             B.moe_permute(self.shape, self.topk_idx, u, self.expert_offsets, self.perm_token, self.row_of,
                           self.u_q, self.a_qdtype, self.u_scale, 0, self.ws)
         elif self.gather_in_gemm:
@@ -145,14 +153,14 @@ class MoELayer:
 
     def _a(self, u):
         """Token operand of the gathered FFN: u (or its fp8 codes and scales)."""
-        if self.gemm == B.MOE_F8E4M3:
+        if self.q8:
             return self.u_q, self.u_scale
         return u, None
 
     @property
     def fused(self) -> bool:
         """Routed and shared experts in one grouped call (needs the gather-in-GEMM path)."""
-        return self.gemm == B.MOE_F8E4M3 or self.gather_in_gemm
+        return self.q8 or self.gather_in_gemm
 
     def ffn_all(self, u):
         """Routed and shared experts in one moe_grouped_ffn call."""
@@ -169,10 +177,10 @@ class MoELayer:
         c = self.cfg
         n_rows = c.T * (c.topk + c.n_shared)
         if getattr(self, "h_all", None) is None:
-            hdt = {B.MOE_F32: torch.float32, B.MOE_BF16: torch.bfloat16, B.MOE_F8E4M3: torch.uint8}[self.gemm]
+            hdt = {B.MOE_F32: torch.float32, B.MOE_BF16: torch.bfloat16, B.MOE_F8E4M3: torch.uint8, B.MOE_F4E2M1: torch.uint8}[self.gemm]
             self.h_all = torch.empty((n_rows, c.inter), dtype=hdt, device=self.dev)
             self.h_all_scale = (torch.empty((n_rows, c.inter // 128), dtype=torch.float32, device=self.dev)
-                                if self.gemm == B.MOE_F8E4M3 else None)
+                                if self.q8 else None)
         a, a_scale = self._a(u)
         E = c.n_routed + c.n_shared
         B.moe_ffn_gate_up(self.shape, self.gemm, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all,
@@ -187,7 +195,7 @@ class MoELayer:
         c = self.cfg
         n_rows = c.T * c.topk
         a_scale = None
-        if self.gemm == B.MOE_F8E4M3:
+        if self.q8:
             a, a_scale, a_rows, mode = self.u_q, self.u_scale, c.T, B.MOE_ROWS_GATHER
         elif self.gather_in_gemm:
             a, a_rows, mode = u, c.T, B.MOE_ROWS_GATHER
@@ -203,12 +211,12 @@ class MoELayer:
         c = self.cfg
         n_rows = c.T * c.topk
         if not hasattr(self, "h"):
-            hdt = {B.MOE_F32: torch.float32, B.MOE_BF16: torch.bfloat16, B.MOE_F8E4M3: torch.uint8}[self.gemm]
+            hdt = {B.MOE_F32: torch.float32, B.MOE_BF16: torch.bfloat16, B.MOE_F8E4M3: torch.uint8, B.MOE_F4E2M1: torch.uint8}[self.gemm]
             self.h = torch.empty((n_rows, c.inter), dtype=hdt, device=self.dev)
             self.h_scale = (torch.empty((n_rows, c.inter // 128), dtype=torch.float32, device=self.dev)
-                            if self.gemm == B.MOE_F8E4M3 else None)
+                            if self.q8 else None)
         a_scale = None
-        if self.gemm == B.MOE_F8E4M3:
+        if self.q8:
             a, a_scale, a_rows, mode = self.u_q, self.u_scale, c.T, B.MOE_ROWS_GATHER
         elif self.gather_in_gemm:
             a, a_rows, mode = u, c.T, B.MOE_ROWS_GATHER
@@ -226,7 +234,7 @@ class MoELayer:
         c = self.cfg
         if not c.n_shared:
             return
-        if self.gemm == B.MOE_F8E4M3:
+        if self.q8:
             a, a_scale = self.u_q, self.u_scale
         else:
             a, a_scale = u, None

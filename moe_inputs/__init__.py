@@ -52,7 +52,7 @@ class MoEConfig:
     topk: int              # K_r
     n_shared: int          # N_s
     inter: int             # SwiGLU intermediate size I
-    gemm: str              # "f32" | "bf16" | "fp8"
+    gemm: str              # "f32" | "bf16" | "fp8" | "mxfp4" (E4M3 activations, MXFP4 weights)
     act: str               # storage dtype of u, centroids, weights: "f32" | "bf16"
     steps: int = 1         # bias-update steps
     gamma: float = 0.001   # bias update speed

@@ -303,8 +303,15 @@ def expert_ffn(a, w_gate_up, w_down, gemm: str = "bf16", wq=None, pow2_input: bo
     ``gemm`` "f32" / "bf16": exact fp64 arithmetic on the stored values.
     ``gemm`` "fp8": the weights are quantised per 128x128 block (unless
     ``wq`` = (gu_codes, gu_scale, d_codes, d_scale) is given) and the FFN runs
-    through :func:`ffn_fp8` (``pow2_input``: power-of-two scales on its input).
+    through :func:`ffn_fp8` (``pow2_input``: power-of-two scales on its input);
+    ``gemm`` "mxfp4": MXFP4 weights (``wq`` as from quantize_mxfp4) through
+    :func:`ffn_mxfp4`.
     """
+    if gemm == "mxfp4":
+        from .mxfp4 import quantize_mxfp4
+        if wq is None:
+            wq = (*quantize_mxfp4(w_gate_up), *quantize_mxfp4(w_down))
+        return ffn_mxfp4(a, *wq, pow2_input=pow2_input)
     if gemm != "fp8":
         return swiglu_ffn(a, w_gate_up, w_down)
     if wq is None:

@@ -17,7 +17,8 @@ code:
 Readings taken here (the pages name the format, not its conversion rule):
 
 * shared scale of a block = 2^(floor(log2(amax)) - 2), 2 being the exponent
-  of E2M1's largest value (the OCP rule); an all-zero block takes 2^0;
+  of E2M1's largest value (the OCP rule), at least 2^-127; an all-zero block
+  takes 2^0;
 * elements = E2M1 of x / scale, round to nearest with ties to the even code,
   saturating at +-6 (so a block maximum in [6, 8) * scale clips to 6); the
   sign bit is the sign of x, so a negative value that rounds to 0 keeps it;
@@ -81,10 +82,11 @@ def e2m1_encode(x) -> np.ndarray:
 
 
 def mx_block_exponent(amax) -> np.ndarray:
-    """E8M0 exponent k of a block: floor(log2(amax)) - 2 (0 for an all-zero block)."""
+    """E8M0 exponent k of a block: floor(log2(amax)) - 2 (0 for an all-zero block), at least -127
+    (E8M0's smallest; only blocks with amax below 2^-125 meet the bound)."""
     amax = np.asarray(amax, dtype=np.float64)
     _, e = np.frexp(np.where(amax > 0, amax, 1.0))      # amax = m 2^e, 0.5 <= m < 1
-    return np.where(amax > 0, e - 1 - E2M1_EMAX, 0).astype(np.int64)
+    return np.where(amax > 0, np.maximum(e - 1 - E2M1_EMAX, -127), 0).astype(np.int64)
 
 
 def quantize_mxfp4(w):

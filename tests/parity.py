@@ -1,7 +1,8 @@
 """Comparison helpers for the GPU-vs-oracle parity tests.
 
 Tolerances (relative L2 per output tensor): 1e-4 for the fp32 workload, 2e-2
-for bf16, 1e-2 against the quantisation-emulating oracle for fp8. Expert
+for bf16, 1e-2 against the quantisation-emulating oracle for fp8 and for MXFP4
+weights (the same E4M3 activations; the oracle sums exact products). Expert
 indices, permutation and loads must match exactly, except that a token's
 selection may differ where the oracle's K-th and (K+1)-th biased scores (or
 M-th and (M+1)-th group scores) are closer than 1e-6; such tokens are counted
@@ -12,7 +13,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 1e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 1e-2, "mxfp4": 1e-2}
 NEAR_TIE = 1e-6
 
 

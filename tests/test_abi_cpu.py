@@ -108,6 +108,8 @@ def test_grouped_ffn_validation():
     assert L.moe_grouped_ffn(*args(ydt=B.MOE_F32)) == B.MOE_E_INVALID
     assert L.moe_grouped_ffn(*args(w=B.MOE_F8E4M3)) == B.MOE_E_INVALID     # missing scales
     assert L.moe_grouped_ffn(*args(w=B.MOE_F8E4M3_POW2, asc=FAKE, gs=FAKE, ds=FAKE)) == B.MOE_E_INVALID
+    assert L.moe_grouped_ffn(*args(w=B.MOE_F4E2M1)) == B.MOE_E_INVALID       # MXFP4 needs its scales too
+    assert L.moe_grouped_ffn(*args(w=B.MOE_F4E2M1, asc=FAKE, gs=FAKE, ds=FAKE)) == B.MOE_E_WORKSPACE
     assert L.moe_grouped_ffn(*args()) == B.MOE_E_WORKSPACE
     assert b"workspace" in L.moe_last_error()
 
@@ -130,6 +132,11 @@ def test_permute_combine_bias_validation():
     assert L.moe_combine(ctypes.byref(sh), B.MOE_BF16, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == B.MOE_E_INVALID
     assert L.moe_bias_update(ctypes.byref(sh), FAKE, ctypes.c_float(-1.0), FAKE, None) == B.MOE_E_INVALID
     assert L.moe_quantize_weights(1, 100, 128, FAKE, FAKE, FAKE, None) == B.MOE_E_UNSUPPORTED
+    assert L.moe_quantize_weights_mxfp4(1, 100, 96, 0, FAKE, FAKE, FAKE, None) == B.MOE_E_UNSUPPORTED   # K % 128
+    assert L.moe_quantize_weights_mxfp4(1, 384, 128, 1, FAKE, FAKE, FAKE, None) == B.MOE_E_UNSUPPORTED  # 2I % 256
+    assert L.moe_quantize_weights_mxfp4(1, 100, 128, 2, FAKE, FAKE, FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_quantize_weights_mxfp4(1, 100, 128, 0, FAKE, None, FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_quantize_weights_mxfp4(0, 100, 128, 0, FAKE, FAKE, FAKE, None) == B.MOE_E_INVALID
 
 
 def test_workspace_size_covers_each_call():
