@@ -166,13 +166,15 @@ moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* top
  *   mode, row_src  see moe_row_mode; row_src [n_rows] int32 for MOE_ROWS_GATHER, else NULL.
  *   a            input rows [a_rows, d]; a_scale [a_rows, d/128] fp32 for fp8, else NULL.
  *   w_gate_up    [n_experts, 2I, d]: gate rows [0, I) then up rows [I, 2I), K-contiguous
- *                (MOE_F4E2M1: the tiled codes of moe_quantize_weights_mxfp4 with
- *                gate_up = 1, I * d bytes per expert).
+ *                (MOE_F8E4M3: the tiled codes of moe_quantize_weights with gate_up = 1,
+ *                2I * d bytes per expert; MOE_F4E2M1: the tiled codes of
+ *                moe_quantize_weights_mxfp4 with gate_up = 1, I * d bytes per expert).
  *   w_gu_scale   MOE_F8E4M3: [n_experts, 2I/128, d/128] fp32 block scales;
  *                MOE_F4E2M1: the tiled scales (gate_up = 1, 2I * d/32 bytes per expert);
  *                else NULL.
- *   w_down       [n_experts, d, I], K-contiguous (MOE_F4E2M1: tiled codes with
- *                gate_up = 0, ceil(d/256) * 256 * I/2 bytes per expert).
+ *   w_down       [n_experts, d, I], K-contiguous (MOE_F8E4M3: tiled codes with
+ *                gate_up = 0, ceil(d/256) * 256 * I bytes per expert; MOE_F4E2M1:
+ *                tiled codes with gate_up = 0, ceil(d/256) * 256 * I/2 bytes per expert).
  *   w_d_scale    MOE_F8E4M3: [n_experts, d/128, I/128] fp32; MOE_F4E2M1: tiled
  *                scales (gate_up = 0, ceil(d/256) * 256 * I/32 bytes per expert); else NULL.
  *   y_dtype      MOE_F32 (only with w = MOE_F32) or MOE_BF16.
@@ -253,12 +255,22 @@ moe_status moe_balance_stats(const moe_shape* shape, const float* scores, const 
 
 /*
  * moe_quantize_weights -- 128x128 block quantisation of expert weights to E4M3
- * ("DeepSeek_V3_Report: Annotation", section "Fine-Grained Quantization"): for
- * n_mats matrices [rows, cols] of bf16 (rows, cols multiples of 128), writes
- * codes [n_mats, rows, cols] and scales [n_mats, rows/128, cols/128] fp32 with
- * the same tile rule as moe_permute. Weight preparation, not part of a forward.
+ * ("DeepSeek_V3_Report: Annotation", section "Fine-Grained Quantization") for
+ * MOE_F8E4M3: for n_mats bf16 matrices [rows, cols] (multiples of 128), one fp32
+ * scale per block with the same tile rule as moe_permute (scales
+ * [n_mats, rows/128, cols/128]), and the codes in the tiled layout the grouped
+ * FFN streams:
+ *   rows go in tiles of 256, ntiles = ceil(rows / 256), tile row rw of tile t
+ *   holding matrix row 256 t + rw (gate_up = 0; rows past the matrix: zero
+ *   codes) or, with gate_up = 1 (rows = 2I, I a multiple of 128), j = (rw >> 5) & 3
+ *   and hc = 128 t + 64 (rw >> 7) + 32 (j & 1) + (rw & 31): row hc for j < 2
+ *   (gate), I + hc for j >= 2 (up);
+ *   codes [n_mats][ntiles][cols/64][16384] bytes: per 64-wide K step s, the 64
+ *   codes of tile row rw (K 64s .. 64s+63) at 64 rw, their 16-byte quarter c at
+ *   64 rw + 16 (c ^ ((rw >> 2) & 3)).
+ * Weight preparation, not part of a forward.
  */
-moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, const void* w_bf16,
+moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, int32_t gate_up, const void* w_bf16,
                                 void* w_codes, float* w_scale, void* stream);
 
 /*

@@ -55,7 +55,7 @@ _SIGS = {
     "moe_combine": [_S, _I, _P, _P, _P, _P, _P, _P, _P],
     "moe_balance_stats": [_S, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_bias_update": [_S, _P, ctypes.c_float, _P, _P],
-    "moe_quantize_weights": [_I, _I, _I, _P, _P, _P, _P],
+    "moe_quantize_weights": [_I, _I, _I, _I, _P, _P, _P, _P],
     "moe_quantize_weights_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P],
     "moe_workspace_bytes": [_S, _I],
     "moe_last_error": [],
@@ -160,7 +160,7 @@ def _wscale_count(w: int, rows: int, cols: int) -> int:
 
 
 def mx_rows(rows: int) -> int:
-    """Rows of a matrix in the tiled MXFP4 layout: whole 256-row tiles."""
+    """Rows of a matrix in the tiled E4M3 / MXFP4 weight layouts: whole 256-row tiles."""
     return -(-rows // 256) * 256
 
 
@@ -171,7 +171,7 @@ def moe_grouped_ffn(shape: moe_shape, w: int, n_experts: int, n_rows: int, exper
     wdiv = 2 if w == MOE_F4E2M1 else 1            # MXFP4: two codes per byte
     _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a, a_rows * d, "a")
     _need(w_gate_up, n_experts * 2 * I * d // wdiv, "w_gate_up")
-    _need(w_down, n_experts * (mx_rows(d) if wdiv == 2 else d) * I // wdiv, "w_down")
+    _need(w_down, n_experts * (mx_rows(d) if w in (MOE_F8E4M3, MOE_F4E2M1) else d) * I // wdiv, "w_down")
     _need(y, n_rows * d, "y")
     if mode == MOE_ROWS_GATHER:
         _need(row_src, n_rows, "row_src")
@@ -207,7 +207,8 @@ def moe_ffn_down(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_o
     d, I = shape.d, shape.inter
     wdiv = 2 if w == MOE_F4E2M1 else 1
     _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(h, n_rows * I, "h")
-    _need(w_down, n_experts * (mx_rows(d) if wdiv == 2 else d) * I // wdiv, "w_down"); _need(y, n_rows * d, "y")
+    _need(w_down, n_experts * (mx_rows(d) if w in (MOE_F8E4M3, MOE_F4E2M1) else d) * I // wdiv, "w_down")
+    _need(y, n_rows * d, "y")
     if w in (MOE_F8E4M3, MOE_F4E2M1):
         _need(h_scale, n_rows * (I // 128), "h_scale")
         _need(w_d_scale, n_experts * _wscale_count(w, d, I), "w_d_scale")
@@ -243,11 +244,13 @@ def moe_bias_update(shape: moe_shape, expert_load, gamma: float, bias, stream=No
                                  _stream(stream)))
 
 
-def moe_quantize_weights(w, codes, scale, stream=None):
-    """w [n, rows, cols] bf16 -> codes [n, rows, cols] uint8, scale [n, rows/128, cols/128] fp32."""
+def moe_quantize_weights(w, codes, scale, gate_up: bool, stream=None):
+    """w [n, rows, cols] bf16 -> E4M3 codes in the tiled layout (n * ceil(rows/256)*256 * cols bytes) and fp32
+    block scales [n, rows/128, cols/128] (gate_up: rows = 2I, gate rows then up rows)."""
     n, rows, cols = w.shape
-    _need(codes, n * rows * cols, "codes"); _need(scale, n * (rows // 128) * (cols // 128), "scale")
-    _check(lib().moe_quantize_weights(n, rows, cols, _ptr(w), _ptr(codes), _ptr(scale), _stream(stream)))
+    _need(codes, n * mx_rows(rows) * cols, "codes"); _need(scale, n * (rows // 128) * (cols // 128), "scale")
+    _check(lib().moe_quantize_weights(n, rows, cols, int(gate_up), _ptr(w), _ptr(codes), _ptr(scale),
+                                      _stream(stream)))
 
 
 def moe_quantize_weights_mxfp4(w, codes, scales, gate_up: bool, stream=None):

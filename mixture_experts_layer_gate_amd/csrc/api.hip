@@ -359,16 +359,18 @@ moe_status moe_bias_update(const moe_shape* shape, const int32_t* expert_load, f
                 st);
 }
 
-moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, const void* w_bf16, void* w_codes,
-                                float* w_scale, void* stream) {
+moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, int32_t gate_up, const void* w_bf16,
+                                void* w_codes, float* w_scale, void* stream) {
   g_err.clear();
   REQUIRE(n_mats > 0 && rows > 0 && cols > 0, "quantize_weights: sizes must be positive");
+  REQUIRE(gate_up == 0 || gate_up == 1, "quantize_weights: gate_up must be 0 or 1");
   SUPPORT(rows % 128 == 0 && cols % 128 == 0, "quantize_weights: rows (%d) and cols (%d) must be multiples of 128",
           rows, cols);
+  SUPPORT(!gate_up || rows % 256 == 0, "quantize_weights: gate_up needs rows = 2I with I a multiple of 128");
   REQUIRE(w_bf16 && w_codes && w_scale, "quantize_weights: a required pointer is NULL");
   SUPPORT(static_cast<long long>(n_mats) * (rows / 128) * (cols / 128) < (1LL << 31), "quantize_weights: too many blocks");
   auto st = static_cast<hipStream_t>(stream);
-  return finish(moe::launch_quantize_weights(n_mats, rows, cols, w_bf16, w_codes, w_scale, st),
+  return finish(moe::launch_quantize_weights(n_mats, rows, cols, gate_up, w_bf16, w_codes, w_scale, st),
                 "moe_quantize_weights", st);
 }
 

@@ -4,7 +4,9 @@
 //
 // Activations carry one fp32 scale per 1x128 tile (row, K chunk), weights one
 // per 128x128 block; every 128-wide K chunk of the products is scaled by the
-// product of the two scales in fp32 (gemm_pipe8.h). Two persistent launches
+// product of the two scales in fp32 (gemm_pipe8.h). The weight codes come in
+// the tiled layout of moe_quantize_weights (per expert, tiles of 256 rows whose
+// 64-wide K steps are contiguous 16 KB blocks in LDS order). Two persistent launches
 // over all experts, one 256-thread workgroup per CU, 256 weight rows x 128
 // token rows per tile, an expert's rows in blocks of four 32-row sub-tiles
 // (the remainder last); a unit streams up to four consecutive output-column
@@ -32,7 +34,7 @@ __device__ __forceinline__ void gate_up8_unit(const Pipe8Rows& rows, __amdgpu_bu
                                               const Unit& un, int nb0, int nseg, uint8_t* lds,
                                               uint8_t* __restrict__ Hq, float* __restrict__ Hs) {
   GateUpEpi8<MS, P8::AMAX_OFF> epi{un, I, nb0, lds, Hq, Hs};
-  pipe8_stream<MS, LT, true>(rows, srs, d, nseg, 128 * d, lds, epi);   // the next tile's rows: 128 further
+  pipe8_stream<MS, LT, true>(rows, srs, d, nseg, lds, epi);
 }
 
 template <int MS, int LT>
@@ -40,7 +42,7 @@ __device__ __forceinline__ void down8_unit(const Pipe8Rows& rows, __amdgpu_buffe
                                            const Unit& un, int nb0, int nseg, uint8_t* lds,
                                            uint16_t* __restrict__ y) {
   DownEpi8<MS> epi{un, d, nb0, y};
-  pipe8_stream<MS, LT, false>(rows, srs, I, nseg, P8::BW * I, lds, epi);
+  pipe8_stream<MS, LT, false>(rows, srs, I, nseg, lds, epi);
 }
 
 __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
@@ -83,14 +85,10 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
 #pragma unroll
     for (int q = 0; q < P8::TL; ++q)
       rows.ot[q] = static_cast<uint32_t>(srcrow[pipe8_load_row(q)]) * d + pipe8_load_chunk(q) * 16;
-    rows.wrs = pipe_rsrc(wgu + static_cast<size_t>(un.e) * 2 * I * d, static_cast<uint64_t>(2 * I) * d);
-#pragma unroll
-    for (int q = 0; q < P8::WL; ++q) {
-      const int rw = pipe8_load_row(q);
-      const int j = (rw >> 5) & 3;                    // wave half rw / 128 owns 64 H columns: its
-      const int hcol = nb0 * 128 + (rw >> 7) * 64 + (j & 1) * 32 + (rw & 31);   // sub-tiles 0,1 gate rows,
-      rows.ow[q] = static_cast<uint32_t>(j >= 2 ? I + hcol : hcol) * d + pipe8_load_chunk(q) * 16;  // 2,3 up rows
-    }
+    // tiled weights: tile nb holds the gate and up rows of H columns 128 nb .. +127 (each wave half 64 of
+    // them: sub-tiles 0, 1 the gate rows, 2, 3 the matching up rows), 256 rows x d bytes per tile
+    rows.wrs = pipe_rsrc(wgu + (static_cast<size_t>(un.e) * NB + nb0) * P8::BW * d,
+                         static_cast<uint64_t>(nseg) * P8::BW * d);
     // LT = ceil(nsub / 2) token load groups; wave row 0 has LT live sub-tiles, row 1 LT or LT - 1
     const bool full = live_token_subtiles8(un.nsub) * 2 >= un.nsub;
     if (un.nsub > 2) {
@@ -117,10 +115,10 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
   int* cum = reinterpret_cast<int*>(lds8 + P8::LDS_BYTES);
   __shared__ int wtmp[16];
   // Output-column tiles of 256 in groups of MAX_SEG per unit; when d % 256 == 128
-  // the last 128 columns form a group of their own, so their weight rows past
-  // d lie past the end of the expert's buffer by their own offset (read as 0).
+  // the last 128 columns form a group of their own (their tile is padded with
+  // zero codes; outputs past d are never stored).
   const int kc = I / 128, NBF = d / P8::BW, NGF = cdiv(NBF, P8::MAX_SEG);
-  const int NG = NGF + (d % P8::BW ? 1 : 0);
+  const int NG = NGF + (d % P8::BW ? 1 : 0), NG8 = cdiv(d, P8::BW);
   const int total = build_units_balanced(off, E, n_rows, kMaxSub8, NG, cum, wtmp);
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t trs = pipe_rsrc(Hq, static_cast<uint64_t>(n_rows) * I);
@@ -145,10 +143,10 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
 #pragma unroll
     for (int q = 0; q < P8::TL; ++q)
       rows.ot[q] = static_cast<uint32_t>(srcrow[pipe8_load_row(q)]) * I + pipe8_load_chunk(q) * 16;
-    rows.wrs = pipe_rsrc(wd + static_cast<size_t>(un.e) * d * I, static_cast<uint64_t>(d) * I);
-#pragma unroll
-    for (int q = 0; q < P8::WL; ++q)
-      rows.ow[q] = static_cast<uint32_t>(nb0 * P8::BW + pipe8_load_row(q)) * I + pipe8_load_chunk(q) * 16;
+    // tiled weights: ceil(d / 256) tiles of 256 output rows x I bytes per expert (the last padded with zero
+    // codes when d % 256 == 128)
+    rows.wrs = pipe_rsrc(wd + (static_cast<size_t>(un.e) * NG8 + nb0) * P8::BW * I,
+                         static_cast<uint64_t>(nseg) * P8::BW * I);
     const bool full = live_token_subtiles8(un.nsub) * 2 >= un.nsub;
     if (un.nsub > 2) {
       if (full) down8_unit<2, 2>(rows, srs, d, I, un, nb0, nseg, lds8, y);

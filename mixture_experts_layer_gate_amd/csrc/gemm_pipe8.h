@@ -81,22 +81,27 @@ __device__ __forceinline__ int pipe8_load_chunk(int q) {
   return (l & 3) ^ ((pipe8_load_row(q) >> 2) & 3);
 }
 
-// Operands: weights and token codes through buffer resources with 32-bit
-// byte offsets (row * K + logical chunk * 16).
+// Operands: the unit's weight blocks (from its first column block on) and the
+// token codes through buffer resources; token loads with 32-bit byte offsets
+// (row * K + logical chunk * 16). Weight load q of a thread reads the 16 bytes
+// at ((q * NWAVE + wave) * 64 + lane) * 16 of the stage's block, which is the
+// stage's LDS image.
 struct Pipe8Rows {
   __amdgpu_buffer_rsrc_t wrs, trs;
-  uint32_t ow[Pipe8::WL];
   uint32_t ot[Pipe8::TL];
 };
 
-// A stage of the stream: output-column block seg = s / nk (its weight rows lie
-// wseg bytes after the previous block's), K bytes (s % nk) * 64 .. +63.
+// A stage of the stream: output-column block seg = s / nk, K bytes
+// (s % nk) * 64 .. +63. The weights are in the tiled layout of
+// moe_quantize_weights, whose stage blocks of 16 KB follow each other for
+// consecutive K steps and column blocks: the stage's weights are the block at
+// s * 16 KB from the unit's first.
 struct Pipe8Off {
   int w, t;   // SGPR byte offsets of the stage's weight and token loads
 };
-__device__ __forceinline__ Pipe8Off pipe8_offsets(int s, int nk, int wseg) {
+__device__ __forceinline__ Pipe8Off pipe8_offsets(int s, int nk) {
   const int seg = s / nk, ks = s - seg * nk;
-  return {seg * wseg + ks * Pipe8::BK, ks * Pipe8::BK};
+  return {s * Pipe8::W_BYTES, ks * Pipe8::BK};
 }
 
 // Load q of a stage into ring buffer st: weights for q < WL, then token rows.
@@ -105,8 +110,8 @@ __device__ __forceinline__ void pipe8_issue_one(const Pipe8Rows& r, uint8_t* st,
   using P = Pipe8;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (q < P::WL) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.wrs, (lds_void_t*)(st + (q * P::NWAVE + w) * 1024), 16, r.ow[q], o.w,
-                                             0, 0);
+    const uint32_t ow = static_cast<uint32_t>(((q * P::NWAVE + w) * 64 + (threadIdx.x & 63)) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.wrs, (lds_void_t*)(st + (q * P::NWAVE + w) * 1024), 16, ow, o.w, 0, 0);
   } else {
     const int qq = q - P::WL;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.trs, (lds_void_t*)(st + P::W_BYTES + (qq * P::NWAVE + w) * 1024), 16,
@@ -279,7 +284,7 @@ __device__ __forceinline__ void pipe8_frame_update(float (&fac)[Pipe8::TW][Pipe8
 // change (after them), so the second stage's multiplies find r ready.
 template <int MS, int LT, bool GATE_UP, bool SECOND, int WAIT, bool ISSUE>
 __device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds, int kc_pad, int kt, int g, int nk,
-                                            int wseg, int seg, const Pipe8Frags<MS>& fa, Pipe8Frags<MS>& fb,
+                                            int seg, const Pipe8Frags<MS>& fa, Pipe8Frags<MS>& fb,
                                             f32x16 (&acc)[Pipe8::TW][Pipe8::TT], float (&fac)[Pipe8::TW][Pipe8::TT],
                                             float (&r)[Pipe8::TW][Pipe8::TT]) {
   using P = Pipe8;
@@ -293,7 +298,7 @@ __device__ __forceinline__ void pipe8_stage(const Pipe8Rows& rows, uint8_t* lds,
     pipe8_read<MS>(fb, lds + ((g + 1) & 3) * P::STAGE);
     sched_fence();
   }
-  const Pipe8Off lo = ISSUE ? pipe8_offsets(g + 3, nk, wseg) : Pipe8Off{0, 0};
+  const Pipe8Off lo = ISSUE ? pipe8_offsets(g + 3, nk) : Pipe8Off{0, 0};
   pipe8_half<MS, LT, SECOND, 1, ISSUE>(fa, acc, r, rows, lds, g + 3, lo);
   if (!SECOND) pipe8_frame_update<MS, GATE_UP>(fac, r, sc, next);
 }
@@ -331,14 +336,14 @@ __device__ __forceinline__ void pipe8_finish(f32x16 (&acc)[Pipe8::TW][Pipe8::TT]
 // groups of 64 rows per stage.
 template <int MS, int LT, bool GATE_UP, class EPI>
 __device__ __forceinline__ void pipe8_stream(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int K, int nseg,
-                                             int wseg, uint8_t* lds, EPI& epi) {
+                                             uint8_t* lds, EPI& epi) {
   using P = Pipe8;
   static_assert(LT >= 1 && LT <= P::TL && LT >= MS, "token load groups must cover the live sub-tiles");
   constexpr int LPS = P::WL + LT;                      // loads per stage per thread
   const int nk = K / P::BK, kc = K / 128, kc_pad = (kc + 3) & ~3, total = nseg * nk;   // nk even, total >= 2
   pipe8_issue_scale_table(srs, lds, kc, kc_pad);
   for (int s = 0; s < 3 && s < total; ++s) {
-    const Pipe8Off o = pipe8_offsets(s, nk, wseg);
+    const Pipe8Off o = pipe8_offsets(s, nk);
 #pragma unroll
     for (int q = 0; q < LPS; ++q) pipe8_issue_one(rows, lds + s * P::STAGE, o, q);
   }
@@ -362,8 +367,8 @@ __device__ __forceinline__ void pipe8_stream(const Pipe8Rows& rows, __amdgpu_buf
   pipe8_read<MS>(f0, lds);
   int kt = 0, seg = 0, g = 0;
   for (; g + 4 < total; g += 2) {                      // both stages refill the ring
-    pipe8_stage<MS, LT, GATE_UP, false, LPS, true>(rows, lds, kc_pad, kt, g, nk, wseg, seg, f0, f1, acc, fac, r);
-    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt + 1, g + 1, nk, wseg, seg, f1, f0, acc, fac,
+    pipe8_stage<MS, LT, GATE_UP, false, LPS, true>(rows, lds, kc_pad, kt, g, nk, seg, f0, f1, acc, fac, r);
+    pipe8_stage<MS, LT, GATE_UP, true, LPS, true>(rows, lds, kc_pad, kt + 1, g + 1, nk, seg, f1, f0, acc, fac,
                                                   r);
     kt += 2;
     if (kt == nk) {
@@ -373,8 +378,8 @@ __device__ __forceinline__ void pipe8_stream(const Pipe8Rows& rows, __amdgpu_buf
     }
   }
   if (g + 4 == total) {                                // stage total-1 is the last to load
-    pipe8_stage<MS, LT, GATE_UP, false, LPS, true>(rows, lds, kc_pad, kt, g, nk, wseg, seg, f0, f1, acc, fac, r);
-    pipe8_stage<MS, LT, GATE_UP, true, LPS, false>(rows, lds, kc_pad, kt + 1, g + 1, nk, wseg, seg, f1, f0, acc, fac,
+    pipe8_stage<MS, LT, GATE_UP, false, LPS, true>(rows, lds, kc_pad, kt, g, nk, seg, f0, f1, acc, fac, r);
+    pipe8_stage<MS, LT, GATE_UP, true, LPS, false>(rows, lds, kc_pad, kt + 1, g + 1, nk, seg, f1, f0, acc, fac,
                                                    r);
     kt += 2;
     if (kt == nk) {
@@ -384,8 +389,8 @@ __device__ __forceinline__ void pipe8_stream(const Pipe8Rows& rows, __amdgpu_buf
     }
   }
   // the stream's last pair: stage total-1 reads nothing
-  pipe8_stage<MS, LT, GATE_UP, false, 0, false>(rows, lds, kc_pad, kt, total - 2, nk, wseg, seg, f0, f1, acc, fac, r);
-  pipe8_stage<MS, LT, GATE_UP, true, -1, false>(rows, lds, kc_pad, kt + 1, total - 1, nk, wseg, seg, f1, f0, acc, fac,
+  pipe8_stage<MS, LT, GATE_UP, false, 0, false>(rows, lds, kc_pad, kt, total - 2, nk, seg, f0, f1, acc, fac, r);
+  pipe8_stage<MS, LT, GATE_UP, true, -1, false>(rows, lds, kc_pad, kt + 1, total - 1, nk, seg, f1, f0, acc, fac,
                                                 r);
   pipe8_finish<MS, GATE_UP>(acc, fac, epi, seg, nseg, lds, kc_pad);
   // every wave has read the ring before the next unit's loads overwrite it

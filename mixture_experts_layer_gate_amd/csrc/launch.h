@@ -87,8 +87,8 @@ hipError_t launch_ffn_fp4_gate_up(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_fp4_down(const FfnArgs& a, hipStream_t st);
 
 // ---- weight preparation
-hipError_t launch_quantize_weights(int n_mats, int rows, int cols, const void* w, void* codes, float* scale,
-                                   hipStream_t st);
+hipError_t launch_quantize_weights(int n_mats, int rows, int cols, int gate_up, const void* w, void* codes,
+                                   float* scale, hipStream_t st);
 hipError_t launch_quantize_weights_mxfp4(int n_mats, int rows, int cols, int gate_up, const void* w, void* codes,
                                          void* scales, hipStream_t st);
 

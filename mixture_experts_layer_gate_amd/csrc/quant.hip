@@ -1,17 +1,33 @@
 // 128x128 block quantisation of bf16 expert weights to E4M3 with one fp32
 // scale per block ("DeepSeek_V3_Report: Annotation", section "Fine-Grained
-// Quantization"; scale from the block's max-abs, section "Online Quantization").
+// Quantization"; scale from the block's max-abs, section "Online Quantization"),
+// and the MXFP4 quantisation; both write the codes in the tiled layouts the
+// grouped FFN kernels stream.
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 
-// One block of 256 threads per 128x128 tile; thread t covers row t/2,
-// columns 64*(t%2) .. +63.
-__global__ __launch_bounds__(256) void quantize_blocks_kernel(int rows, int cols, const uint16_t* __restrict__ w,
+// Tiled code layout (the E4M3 grouped FFN streams it; see moe_quantize_weights):
+// tiles of 256 rows, tile row rw of tile t being matrix row 256 t + rw, or for
+// gate_up the gate / up row of the tile's 128 H columns that the tile's waves
+// pair; per 64-wide K step a tile's 64-byte row pieces form one 16 KB block,
+// row rw at 64 rw with its 16-byte quarter c at 16 (c ^ ((rw >> 2) & 3)).
+__device__ __forceinline__ int tiled_row(int t, int rw, int gate_up, int half) {
+  if (!gate_up) return 256 * t + rw;
+  const int j = (rw >> 5) & 3;
+  const int hc = 128 * t + 64 * (rw >> 7) + 32 * (j & 1) + (rw & 31);
+  return j >= 2 ? half + hc : hc;
+}
+
+// One block of 256 threads per 128x128 weight block; thread t covers row t/2,
+// columns 64*(t%2) .. +63. Codes go to the tiled layout, scales to
+// [mat][rows/128][cols/128].
+__global__ __launch_bounds__(256) void quantize_blocks_kernel(int rows, int cols, int gate_up,
+                                                              const uint16_t* __restrict__ w,
                                                               uint8_t* __restrict__ q, float* __restrict__ scale) {
   __shared__ float wmax[4];
-  const int bc = cols / 128, br = rows / 128;
+  const int bc = cols / 128, br = rows / 128, ntiles = (rows + 255) / 256;
   const long long blk = blockIdx.x;
   const long long mat = blk / (static_cast<long long>(br) * bc);
   const int rem = static_cast<int>(blk % (static_cast<long long>(br) * bc));
@@ -38,6 +54,18 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(int rows, int cols
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
+  // tile position of matrix row r (the inverse of tiled_row)
+  int t, rw;
+  if (gate_up) {
+    const int half = rows / 2, up = r >= half, hc = up ? r - half : r;
+    t = hc / 128;
+    const int hl = hc % 128;                        // H column within the tile
+    rw = 128 * (hl >> 6) + 32 * ((up ? 2 : 0) + ((hl >> 5) & 1)) + (hl & 31);
+  } else {
+    t = r / 256;
+    rw = r % 256;
+  }
+  const size_t tile = static_cast<size_t>(mat) * ntiles + t;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     uint32_t o[4];
@@ -46,17 +74,44 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(int rows, int cols
       const float* xi = x + 16 * v + 4 * i;
       o[i] = f32x4_to_e4m3(xi[0] * inv, xi[1] * inv, xi[2] * inv, xi[3] * inv);
     }
-    *reinterpret_cast<uint4*>(q + base + 16 * v) = make_uint4(o[0], o[1], o[2], o[3]);
+    const int k = c0 + 16 * v;                      // first K index of this 16-byte piece
+    const size_t off = (tile * (cols / 64) + k / 64) * 16384 + 64 * rw + 16 * (((k % 64) / 16) ^ ((rw >> 2) & 3));
+    *reinterpret_cast<uint4*>(q + off) = make_uint4(o[0], o[1], o[2], o[3]);
   }
   if (threadIdx.x == 0)
     scale[(static_cast<size_t>(mat) * br + bi) * bc + bj] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
 }
 
-hipError_t launch_quantize_weights(int n_mats, int rows, int cols, const void* w, void* codes, float* scale,
-                                   hipStream_t st) {
+// Zero codes of the padding rows of the last tile (rows % 256 == 128, not gate_up).
+__global__ __launch_bounds__(256) void zero_tile_padding_kernel(long long n, int rows, int cols, uint8_t* __restrict__ q) {
+  const int ntiles = (rows + 255) / 256, nst = cols / 64;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<long long>(gridDim.x) * blockDim.x) {
+    // i enumerates (mat, stage, padding row rw in 128..255, 16-byte quarter)
+    const int quarter = static_cast<int>(i & 3);
+    const int rw = 128 + static_cast<int>((i >> 2) & 127);
+    const long long ms = i >> 9;
+    const int st = static_cast<int>(ms % nst);
+    const long long mat = ms / nst;
+    const size_t off = ((static_cast<size_t>(mat) * ntiles + ntiles - 1) * nst + st) * 16384 + 64 * rw + 16 * quarter;
+    *reinterpret_cast<uint4*>(q + off) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+hipError_t launch_quantize_weights(int n_mats, int rows, int cols, int gate_up, const void* w, void* codes,
+                                   float* scale, hipStream_t st) {
   const long long blocks = static_cast<long long>(n_mats) * (rows / 128) * (cols / 128);
-  hipLaunchKernelGGL(quantize_blocks_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, rows, cols,
+  hipLaunchKernelGGL(quantize_blocks_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, rows, cols, gate_up,
                      static_cast<const uint16_t*>(w), static_cast<uint8_t*>(codes), scale);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (rows % 256 != 0) {
+    const long long n = static_cast<long long>(n_mats) * (cols / 64) * 128 * 4;
+    long long b = (n + 255) / 256;
+    const long long cap = static_cast<long long>(device_cu_count()) * 32;
+    if (b > cap) b = cap;
+    hipLaunchKernelGGL(zero_tile_padding_kernel, dim3(static_cast<unsigned>(b)), dim3(256), 0, st, n, rows, cols,
+                       static_cast<uint8_t*>(codes));
+  }
   return hipGetLastError();
 }
 
@@ -94,14 +149,7 @@ __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(long long n_blocks,
     rest /= kbs;
     const int t = static_cast<int>(rest % ntiles);
     const long long mat = rest / ntiles;
-    int row;
-    if (gate_up) {
-      const int j = (rw >> 5) & 3;
-      const int hc = 128 * t + 64 * (rw >> 7) + 32 * (j & 1) + (rw & 31);
-      row = j >= 2 ? half + hc : hc;
-    } else {
-      row = 256 * t + rw;
-    }
+    const int row = tiled_row(t, rw, gate_up, half);
     float x[32];
     if (row < rows) {
       const uint16_t* src = w + (static_cast<size_t>(mat) * rows + row) * cols + static_cast<size_t>(kb) * 32;

@@ -76,9 +76,9 @@ class MoELayer:
             if self.q8:
                 n, r, c = both.shape
                 if self.gemm == B.MOE_F8E4M3:
-                    codes = torch.empty((n, r, c), dtype=torch.uint8, device=self.dev)
+                    codes = torch.empty((n, B.mx_rows(r), c), dtype=torch.uint8, device=self.dev)   # tiled
                     scale = torch.empty((n, r // 128, c // 128), dtype=torch.float32, device=self.dev)
-                    B.moe_quantize_weights(both, codes, scale)
+                    B.moe_quantize_weights(both, codes, scale, gate_up=(kind == "gate_up"))
                 else:
                     rt = B.mx_rows(r)               # tiled MXFP4: whole 256-row tiles
                     codes = torch.empty((n, rt, c // 2), dtype=torch.uint8, device=self.dev)

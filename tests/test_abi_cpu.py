@@ -131,7 +131,9 @@ def test_permute_combine_bias_validation():
                          FAKE, 1 << 20, None) == B.MOE_E_INVALID
     assert L.moe_combine(ctypes.byref(sh), B.MOE_BF16, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == B.MOE_E_INVALID
     assert L.moe_bias_update(ctypes.byref(sh), FAKE, ctypes.c_float(-1.0), FAKE, None) == B.MOE_E_INVALID
-    assert L.moe_quantize_weights(1, 100, 128, FAKE, FAKE, FAKE, None) == B.MOE_E_UNSUPPORTED
+    assert L.moe_quantize_weights(1, 100, 128, 0, FAKE, FAKE, FAKE, None) == B.MOE_E_UNSUPPORTED
+    assert L.moe_quantize_weights(1, 384, 128, 1, FAKE, FAKE, FAKE, None) == B.MOE_E_UNSUPPORTED     # 2I % 256
+    assert L.moe_quantize_weights(1, 256, 128, 2, FAKE, FAKE, FAKE, None) == B.MOE_E_INVALID
     assert L.moe_quantize_weights_mxfp4(1, 100, 96, 0, FAKE, FAKE, FAKE, None) == B.MOE_E_UNSUPPORTED   # K % 128
     assert L.moe_quantize_weights_mxfp4(1, 384, 128, 1, FAKE, FAKE, FAKE, None) == B.MOE_E_UNSUPPORTED  # 2I % 256
     assert L.moe_quantize_weights_mxfp4(1, 100, 128, 2, FAKE, FAKE, FAKE, None) == B.MOE_E_INVALID

@@ -9,7 +9,7 @@ import oracle
 from moe_inputs import generate, generate_expert, get_config
 from mixture_experts_layer_gate_amd import binding as B
 from mixture_experts_layer_gate_amd import MoELayer
-from parity import TOL, np64, npi, rel_l2, report, routing_mismatches
+from parity import TOL, np64, npi, rel_l2, report, routing_mismatches, tile_e4m3, tile_mxfp4
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -23,37 +23,10 @@ def _dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
 
 
-def _tile_mx(codes, scales, gate_up):
-    """Oracle codes [R, K] (one per value) and scales [R, K/32] -> the library's tiled MXFP4 layout as
-    documented with moe_quantize_weights_mxfp4 (flat codes, flat scales)."""
-    R, K = codes.shape
-    nt = -(-R // 256)
-    rw = np.arange(256)
-    rows = np.empty((nt, 256), dtype=np.int64)
-    for t in range(nt):
-        if gate_up:
-            j = (rw >> 5) & 3
-            hc = 128 * t + 64 * (rw >> 7) + 32 * (j & 1) + (rw & 31)
-            rows[t] = np.where(j >= 2, R // 2 + hc, hc)
-        else:
-            rows[t] = 256 * t + rw
-    valid = rows < R
-    c = np.zeros((nt, 256, K), dtype=np.uint8)
-    sc = np.full((nt, 256, K // 32), 127, dtype=np.uint8)
-    c[valid] = codes[rows[valid]]
-    sc[valid] = scales[rows[valid]]
-    packed = oracle.pack_e2m1(c).reshape(nt, 256, K // 64, 2, 16)       # [t][rw][stage][half][16 bytes]
-    out = np.zeros((nt, K // 64, 256, 2, 16), dtype=np.uint8)          # [t][stage][rw][slot][16 bytes]
-    swz = (rw >> 3) & 1
-    for k16 in (0, 1):
-        out[:, :, rw, k16 ^ swz, :] = packed[:, :, :, k16, :].transpose(0, 2, 1, 3)
-    return out.reshape(-1), np.ascontiguousarray(sc.reshape(nt, 256, K // 128, 4).transpose(0, 2, 3, 1)).reshape(-1)
-
-
 def _oracle_mx(w, gate_up):
     """Oracle MXFP4 of one matrix [R, K] in the library's tiled layout, plus the oracle's own (codes, scales)."""
     codes, scales = oracle.quantize_mxfp4(w)
-    tc, ts = _tile_mx(codes, scales, gate_up)
+    tc, ts = tile_mxfp4(codes, scales, gate_up, oracle.pack_e2m1)
     return tc, ts, (codes, scales)
 
 
@@ -170,8 +143,8 @@ def test_mxfp4_through_fp8_kernels_on_lossless_conversion():
     conv_g = [oracle.mxfp4_to_e4m3_blocks(*m[2]) for m in r["mg"]]
     conv_d = [oracle.mxfp4_to_e4m3_blocks(*m[2]) for m in r["md"]]
     assert all(np.all(c[2]) for c in conv_g + conv_d)
-    wgu, wgs = _dev(np.stack([c[0] for c in conv_g])), _dev(np.stack([c[1] for c in conv_g]))
-    wdn, wds = _dev(np.stack([c[0] for c in conv_d])), _dev(np.stack([c[1] for c in conv_d]))
+    wgu, wgs = _dev(np.stack([tile_e4m3(c[0], True) for c in conv_g])), _dev(np.stack([c[1] for c in conv_g]))
+    wdn, wds = _dev(np.stack([tile_e4m3(c[0], False) for c in conv_d])), _dev(np.stack([c[1] for c in conv_d]))
     n, off, src = r["n"], r["off"], r["src"]
     uq, us = oracle.quantize_tiles(r["u32"])
     h8 = torch.empty_like(r["h"]); hs8 = torch.empty_like(r["hs"]); y8 = torch.empty_like(r["y"])

@@ -13,7 +13,7 @@ import oracle
 from moe_inputs import get_config, generate, generate_expert
 from mixture_experts_layer_gate_amd import binding as B
 from mixture_experts_layer_gate_amd import MoELayer
-from parity import TOL, np64, npi, rel_l2, report, routing_mismatches
+from parity import TOL, np64, npi, rel_l2, report, routing_mismatches, tile_e4m3
 
 pytestmark = pytest.mark.gpu
 
@@ -365,17 +365,25 @@ def test_batch_invariance(gemm):
           f"{100 * cfg.n_routed} affinities differ between the two batches")
 
 
-def test_quantize_weights_bit_exact():
+@pytest.mark.parametrize("kind", ["gate_up", "down", "down_padded"])
+def test_quantize_weights_bit_exact(kind):
+    """E4M3 codes in the tiled layout and the block scales, bit for bit: c2's gate/up matrices (gate and up rows
+    interleaved per 128 H columns), its down matrices, and 384-row matrices whose second tile is padded."""
     cfg, inp = _inputs("c2")
-    w = inp["w_gate_up"][:3].contiguous()
+    if kind == "gate_up":
+        w = inp["w_gate_up"][:3].contiguous()
+    elif kind == "down":
+        w = inp["w_down"][:3].contiguous()
+    else:
+        w = (torch.randn((2, 384, 256), generator=torch.Generator().manual_seed(3)) * 0.02).to(torch.bfloat16).to(DEV)
     n, rr, cc = w.shape
-    codes = torch.empty((n, rr, cc), dtype=torch.uint8, device=DEV)
+    codes = torch.empty((n, B.mx_rows(rr), cc), dtype=torch.uint8, device=DEV)
     scale = torch.empty((n, rr // 128, cc // 128), dtype=torch.float32, device=DEV)
-    B.moe_quantize_weights(w, codes, scale)
+    B.moe_quantize_weights(w, codes, scale, gate_up=(kind == "gate_up"))
     torch.cuda.synchronize()
     for e in range(n):
         oc, os_ = oracle.quantize_blocks(w[e].cpu().float().numpy())
-        assert np.array_equal(codes[e].cpu().numpy(), oc)
+        assert np.array_equal(codes[e].cpu().numpy().reshape(-1), tile_e4m3(oc, kind == "gate_up"))
         assert np.array_equal(scale[e].cpu().numpy(), os_)
 
 
@@ -658,8 +666,8 @@ def test_grouped_ffn_fp8_tile_shapes(inter, mode):
     uq, us = oracle.quantize_tiles(u32)
     wq = [_oracle_wq(inp, e) for e in range(cfg.n_routed)]
     dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
-    wgu = dev8(np.stack([w[0] for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
-    wdn = dev8(np.stack([w[2] for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
+    wgu = dev8(np.stack([tile_e4m3(w[0], True) for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
+    wdn = dev8(np.stack([tile_e4m3(w[2], False) for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
     h = torch.empty((n, inter), dtype=torch.uint8, device=DEV)
     hs = torch.empty((n, inter // 128), dtype=torch.float32, device=DEV)
     y = torch.empty((n, cfg.d), dtype=torch.bfloat16, device=DEV)
@@ -698,8 +706,8 @@ def test_grouped_ffn_fp8_half_column_tile(d):
     uq, us = oracle.quantize_tiles(u32)
     wq = [_oracle_wq(inp, e) for e in range(cfg.n_routed)]
     dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
-    wgu = dev8(np.stack([w[0] for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
-    wdn = dev8(np.stack([w[2] for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
+    wgu = dev8(np.stack([tile_e4m3(w[0], True) for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
+    wdn = dev8(np.stack([tile_e4m3(w[2], False) for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
     h = torch.empty((n, cfg.inter), dtype=torch.uint8, device=DEV)
     hs = torch.empty((n, cfg.inter // 128), dtype=torch.float32, device=DEV)
     y = torch.full((n + 1, d), 7.0, dtype=torch.bfloat16, device=DEV)
@@ -733,7 +741,7 @@ def test_fp8_accumulation_k4096():
     y = torch.empty((M, Dout), dtype=torch.bfloat16, device=DEV)
     ws = torch.empty(256, dtype=torch.uint8, device=DEV)
     B.moe_ffn_down(sh, B.MOE_F8E4M3, 1, M, _i32(np.array([0, M])), dev(ha), dev(np.ones((M, K // 128), np.float32)),
-                   dev(wb[None]), dev(np.ones((1, Dout // 128, K // 128), np.float32)), y, ws)
+                   dev(tile_e4m3(wb, False)[None]), dev(np.ones((1, Dout // 128, K // 128), np.float32)), y, ws)
     torch.cuda.synchronize()
     yg = np64(y)
     rounded = torch.from_numpy(exact).to(torch.bfloat16).double().numpy()
