@@ -52,9 +52,11 @@ typedef enum {
   MOE_BF16 = 1,    /* bfloat16 */
   MOE_F8E4M3 = 2,  /* OCP E4M3FN: bias 7, max 448, no infinities */
   MOE_F8E4M3_POW2 = 3, /* E4M3FN codes with power-of-two tile scales (an a_dtype of moe_permute only) */
-  MOE_F4E2M1 = 4      /* OCP MXFP4 weights (a weight dtype only): E2M1 codes, two per byte with the
+  MOE_F4E2M1 = 4,     /* OCP MXFP4 weights (a weight dtype only): E2M1 codes, two per byte with the
                          even K index in the low nibble, one E8M0 scale byte (2^(b - 127)) per 32
                          consecutive K values, in the tiled layout of moe_quantize_weights_mxfp4 */
+  MOE_BF16_TILED = 5  /* bf16 weights in the tiled layout of moe_tile_weights_bf16 (a weight dtype
+                         only; activations, H and y as with MOE_BF16) */
 } moe_dtype;
 
 /* How moe_grouped_ffn finds the input row of output row r of expert e. */
@@ -152,7 +154,8 @@ moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* top
  * y[r] = (SiLU(x W_g^T) * (x W_u^T)) W_d^T for every row r of every expert
  * (SwiGLU paragraph of "DeepSeek_V3_Report: Annotation", beta = 1; the three
  * projections cost 6*d*I FLOPs per row, "DeepSeek V3 / V4 Infra", V4 EP section).
- *   w            weight dtype: MOE_F32 (a f32), MOE_BF16 (a bf16), MOE_F8E4M3
+ *   w            weight dtype: MOE_F32 (a f32), MOE_BF16 (a bf16; MOE_BF16_TILED: the same
+ *                with the weights from moe_tile_weights_bf16), MOE_F8E4M3
  *                (a is fp8 with a_scale; weights fp8 with 128x128 block scales;
  *                fp32 accumulation with the scales applied per 128-wide K chunk,
  *                section "Increasing Accumulation Precision"; the SwiGLU output
@@ -272,6 +275,23 @@ moe_status moe_balance_stats(const moe_shape* shape, const float* scores, const 
  */
 moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, int32_t gate_up, const void* w_bf16,
                                 void* w_codes, float* w_scale, void* stream);
+
+/*
+ * moe_tile_weights_bf16 -- copies bf16 expert weights into the tiled layout of
+ * MOE_BF16_TILED, in which every 32-wide K step of a 256-row tile is one
+ * contiguous 16 KB block (the grouped FFN's load pattern). n_mats matrices
+ * [rows, cols] (cols a multiple of 128) from w_bf16 to w_tiled
+ * (n_mats * ceil(rows/256) * 256 * cols bf16 values, not overlapping w_bf16):
+ * tile row rw of tile t holds matrix row 256 t + rw (gate_up = 0; rows past the
+ * matrix are zero) or, with gate_up = 1 (rows = 2I, I a multiple of 128),
+ * j = (rw >> 5) & 3 and hc = 128 t + 64 (rw >> 7) + 32 (j & 1) + (rw & 31): row
+ * hc for j < 2 (gate), I + hc for j >= 2 (up). Per K step s the 64 bytes of
+ * tile row rw (K 32s .. 32s+31) sit at 64 rw of the step's block, their
+ * 16-byte quarter c at 64 rw + 16 (c ^ ((rw >> 2) & 3)); the blocks run
+ * [n_mats][ntiles][cols/32]. Weight preparation, not part of a forward.
+ */
+moe_status moe_tile_weights_bf16(int32_t n_mats, int32_t rows, int32_t cols, int32_t gate_up, const void* w_bf16,
+                                 void* w_tiled, void* stream);
 
 /*
  * moe_quantize_weights_mxfp4 -- MXFP4 (OCP microscaling FP4) quantisation of

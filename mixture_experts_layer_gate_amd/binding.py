@@ -17,7 +17,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_F8E4M3, MOE_F8E4M3_POW2, MOE_F4E2M1 = 0, 1, 2, 3, 4
+MOE_F32, MOE_BF16, MOE_F8E4M3, MOE_F8E4M3_POW2, MOE_F4E2M1, MOE_BF16_TILED = 0, 1, 2, 3, 4, 5
 MOE_ROWS_DIRECT, MOE_ROWS_GATHER, MOE_ROWS_SEGMENT = 0, 1, 2
 
 _STATUS = {1: "MOE_E_INVALID", 2: "MOE_E_UNSUPPORTED", 3: "MOE_E_WORKSPACE", 4: "MOE_E_HIP"}
@@ -57,6 +57,7 @@ _SIGS = {
     "moe_bias_update": [_S, _P, ctypes.c_float, _P, _P],
     "moe_quantize_weights": [_I, _I, _I, _I, _P, _P, _P, _P],
     "moe_quantize_weights_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P],
+    "moe_tile_weights_bf16": [_I, _I, _I, _I, _P, _P, _P],
     "moe_workspace_bytes": [_S, _I],
     "moe_last_error": [],
     "moe_version": [],
@@ -171,7 +172,8 @@ def moe_grouped_ffn(shape: moe_shape, w: int, n_experts: int, n_rows: int, exper
     wdiv = 2 if w == MOE_F4E2M1 else 1            # MXFP4: two codes per byte
     _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a, a_rows * d, "a")
     _need(w_gate_up, n_experts * 2 * I * d // wdiv, "w_gate_up")
-    _need(w_down, n_experts * (mx_rows(d) if w in (MOE_F8E4M3, MOE_F4E2M1) else d) * I // wdiv, "w_down")
+    _need(w_down, n_experts * (mx_rows(d) if w in (MOE_F8E4M3, MOE_F4E2M1, MOE_BF16_TILED) else d) * I // wdiv,
+          "w_down")
     _need(y, n_rows * d, "y")
     if mode == MOE_ROWS_GATHER:
         _need(row_src, n_rows, "row_src")
@@ -207,7 +209,8 @@ def moe_ffn_down(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_o
     d, I = shape.d, shape.inter
     wdiv = 2 if w == MOE_F4E2M1 else 1
     _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(h, n_rows * I, "h")
-    _need(w_down, n_experts * (mx_rows(d) if w in (MOE_F8E4M3, MOE_F4E2M1) else d) * I // wdiv, "w_down")
+    _need(w_down, n_experts * (mx_rows(d) if w in (MOE_F8E4M3, MOE_F4E2M1, MOE_BF16_TILED) else d) * I // wdiv,
+          "w_down")
     _need(y, n_rows * d, "y")
     if w in (MOE_F8E4M3, MOE_F4E2M1):
         _need(h_scale, n_rows * (I // 128), "h_scale")
@@ -260,3 +263,10 @@ def moe_quantize_weights_mxfp4(w, codes, scales, gate_up: bool, stream=None):
     _need(codes, n * mx_rows(rows) * cols // 2, "codes"); _need(scales, n * mx_rows(rows) * (cols // 32), "scales")
     _check(lib().moe_quantize_weights_mxfp4(n, rows, cols, int(gate_up), _ptr(w), _ptr(codes), _ptr(scales),
                                             _stream(stream)))
+
+
+def moe_tile_weights_bf16(w, out, gate_up: bool, stream=None):
+    """w [n, rows, cols] bf16 -> out: the tiled layout of MOE_BF16_TILED (n * ceil(rows/256)*256 * cols bf16)."""
+    n, rows, cols = w.shape
+    _need(out, n * mx_rows(rows) * cols, "out")
+    _check(lib().moe_tile_weights_bf16(n, rows, cols, int(gate_up), _ptr(w), _ptr(out), _stream(stream)))

@@ -109,7 +109,7 @@ hipError_t launch_queue_reset(int* q, hipStream_t st) {
 size_t ffn_queue_offset(moe_dtype w, int n_rows, int I) {
   const size_t n = static_cast<size_t>(n_rows) * I;
   if (w == MOE_F32) return align256(n * 4);
-  if (w == MOE_BF16) return align256(n * 2);
+  if (w == MOE_BF16 || w == MOE_BF16_TILED) return align256(n * 2);
   return align256(n) + align256(static_cast<size_t>(n_rows) * (I / 128) * 4);
 }
 
@@ -196,8 +196,8 @@ moe_status check_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int
   SUPPORT(n_experts <= 4096, "grouped_ffn: n_experts (%d) > 4096", n_experts);
   SUPPORT(static_cast<long long>(n_rows) * (d > I ? d : I) < (1LL << 40), "grouped_ffn: too many rows");
   REQUIRE(offsets != nullptr, "grouped_ffn: expert_offsets is NULL");
-  REQUIRE(w == MOE_F32 || w == MOE_BF16 || w == MOE_F8E4M3 || w == MOE_F4E2M1, "grouped_ffn: bad weight dtype %d",
-          static_cast<int>(w));
+  REQUIRE(w == MOE_F32 || w == MOE_BF16 || w == MOE_BF16_TILED || w == MOE_F8E4M3 || w == MOE_F4E2M1,
+          "grouped_ffn: bad weight dtype %d", static_cast<int>(w));
   const bool q8 = w == MOE_F8E4M3 || w == MOE_F4E2M1;   // E4M3 activations and H
   SUPPORT(!q8 || (d <= 10240 && I <= 10240), "grouped_ffn: the fp8 / mxfp4 paths need d and inter <= 10240");
   SUPPORT(w != MOE_F4E2M1 || (d <= 8192 && I <= 8192), "grouped_ffn: the mxfp4 path needs d and inter <= 8192");
@@ -205,8 +205,8 @@ moe_status check_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int
   SUPPORT(!q8 || (static_cast<long long>(n_rows) * I < (1LL << 32) && static_cast<long long>(2 * I) * d < (1LL << 32)),
           "grouped_ffn: fp8 / mxfp4 paths need n_rows * inter and 2 * inter * d below 2^32");
   // the bf16 kernels address H and one expert's weight matrices through 32-bit byte offsets
-  SUPPORT(w != MOE_BF16 || (static_cast<long long>(n_rows) * I * 2 < (1LL << 32) &&
-                            static_cast<long long>(2 * I) * d * 2 < (1LL << 32)),
+  SUPPORT((w != MOE_BF16 && w != MOE_BF16_TILED) || (static_cast<long long>(n_rows) * I * 2 < (1LL << 32) &&
+                                                     static_cast<long long>(2 * I) * d * 2 < (1LL << 32)),
           "grouped_ffn: bf16 path needs n_rows * inter and 2 * inter * d below 2^31 elements");
   (void)phase;
   return MOE_OK;
@@ -217,7 +217,7 @@ moe_status check_gate_up(const moe_shape* shape, moe_dtype w, moe_row_mode mode,
                          const void* w_gu_scale) {
   REQUIRE(a && w_gate_up, "grouped_ffn: a or w_gate_up is NULL");
   REQUIRE(a_rows > 0, "grouped_ffn: a_rows must be positive");
-  SUPPORT(w != MOE_BF16 || static_cast<long long>(a_rows) * shape->d * 2 < (1LL << 32),
+  SUPPORT((w != MOE_BF16 && w != MOE_BF16_TILED) || static_cast<long long>(a_rows) * shape->d * 2 < (1LL << 32),
           "grouped_ffn: bf16 path needs a_rows * d below 2^31 elements");
   SUPPORT((w != MOE_F8E4M3 && w != MOE_F4E2M1) || static_cast<long long>(a_rows) * shape->d < (1LL << 32),
           "grouped_ffn: fp8 / mxfp4 paths need a_rows * d below 2^32");
@@ -239,14 +239,14 @@ moe_status check_down(moe_dtype w, const void* w_down, const void* w_d_scale, mo
 
 hipError_t run_gate_up(moe_dtype w, const moe::FfnArgs& p, hipStream_t st) {
   if (w == MOE_F32) return moe::launch_ffn_f32_gate_up(p, st);
-  if (w == MOE_BF16) return moe::launch_ffn_bf16_gate_up(p, st);
+  if (w == MOE_BF16 || w == MOE_BF16_TILED) return moe::launch_ffn_bf16_gate_up(p, st, w == MOE_BF16_TILED);
   if (w == MOE_F4E2M1) return moe::launch_ffn_fp4_gate_up(p, st);
   return moe::launch_ffn_fp8_gate_up(p, st);
 }
 
 hipError_t run_down(moe_dtype w, const moe::FfnArgs& p, hipStream_t st) {
   if (w == MOE_F32) return moe::launch_ffn_f32_down(p, st);
-  if (w == MOE_BF16) return moe::launch_ffn_bf16_down(p, st);
+  if (w == MOE_BF16 || w == MOE_BF16_TILED) return moe::launch_ffn_bf16_down(p, st, w == MOE_BF16_TILED);
   if (w == MOE_F4E2M1) return moe::launch_ffn_fp4_down(p, st);
   return moe::launch_ffn_fp8_down(p, st);
 }
@@ -372,6 +372,21 @@ moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, int3
   auto st = static_cast<hipStream_t>(stream);
   return finish(moe::launch_quantize_weights(n_mats, rows, cols, gate_up, w_bf16, w_codes, w_scale, st),
                 "moe_quantize_weights", st);
+}
+
+moe_status moe_tile_weights_bf16(int32_t n_mats, int32_t rows, int32_t cols, int32_t gate_up, const void* w_bf16,
+                                 void* w_tiled, void* stream) {
+  g_err.clear();
+  REQUIRE(n_mats > 0 && rows > 0 && cols > 0, "tile_weights_bf16: sizes must be positive");
+  REQUIRE(gate_up == 0 || gate_up == 1, "tile_weights_bf16: gate_up must be 0 or 1");
+  SUPPORT(cols % 128 == 0, "tile_weights_bf16: cols (%d) must be a multiple of 128", cols);
+  SUPPORT(!gate_up || rows % 256 == 0, "tile_weights_bf16: gate_up needs rows = 2I with I a multiple of 128");
+  REQUIRE(w_bf16 && w_tiled, "tile_weights_bf16: a required pointer is NULL");
+  REQUIRE(w_bf16 != w_tiled, "tile_weights_bf16: the copy cannot be made in place");
+  SUPPORT(static_cast<long long>(n_mats) * (rows + 255) * cols < (1LL << 40), "tile_weights_bf16: too many values");
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_tile_weights_bf16(n_mats, rows, cols, gate_up, w_bf16, w_tiled, st),
+                "moe_tile_weights_bf16", st);
 }
 
 moe_status moe_quantize_weights_mxfp4(int32_t n_mats, int32_t rows, int32_t cols, int32_t gate_up, const void* w_bf16,

@@ -10,7 +10,9 @@
 //     product is formed in registers. Token rows are read through the row
 //     mode (the gather is fused into the operand load).
 //  2. down:    y[r, n] = H_r . Wd[n] for 256 output columns.
-// H lives in the workspace as bf16 [n_rows, I].
+// H lives in the workspace as bf16 [n_rows, I]. The weights come row-major
+// (MOE_BF16) or in the tiled layout of moe_tile_weights_bf16 (MOE_BF16_TILED:
+// every stage's weight loads read one contiguous 16 KB block).
 #include <mutex>
 
 #include "common.h"
@@ -20,7 +22,8 @@
 
 namespace moe {
 
-using FP = Pipe<256, 256>;  // 256 weight rows x 256 token rows per tile, waves of 128 x 128
+using FP = Pipe<256, 256>;         // 256 weight rows x 256 token rows per tile, waves of 128 x 128
+using FPT = Pipe<256, 256, true>;  // the same with the weights in the tiled layout
 constexpr int kHcols = FP::BW / 2;  // H columns per gate/up tile
 
 __device__ __forceinline__ int live_token_subtiles(int nsub) {
@@ -35,8 +38,8 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, floa
 // One tile with MS live token sub-tiles per wave and LT token load groups per
 // stage: main loop and epilogue in one instantiation, so the accumulators
 // never merge across variants.
-template <int MS, int LT>
-__device__ __forceinline__ void gate_up_tile(const PipeRows<FP>& rows, int d, int I, const Unit& un, uint8_t* lds,
+template <class P, int MS, int LT>
+__device__ __forceinline__ void gate_up_tile(const PipeRows<P>& rows, int d, int I, const Unit& un, uint8_t* lds,
                                              uint16_t* __restrict__ H) {
   f32x16 acc[FP::TW][FP::TT];
 #pragma unroll
@@ -45,7 +48,7 @@ __device__ __forceinline__ void gate_up_tile(const PipeRows<FP>& rows, int d, in
     for (int i = 0; i < FP::TT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-  pipe_mainloop<FP, MS, LT>(rows, d, lds, acc);
+  pipe_mainloop<P, MS, LT>(rows, d, lds, acc);
   const int ww = threadIdx.x >> 7, h = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
@@ -64,8 +67,8 @@ __device__ __forceinline__ void gate_up_tile(const PipeRows<FP>& rows, int d, in
   }
 }
 
-template <int MS, int LT>
-__device__ __forceinline__ void down_tile(const PipeRows<FP>& rows, int d, int I, const Unit& un, uint8_t* lds,
+template <class P, int MS, int LT>
+__device__ __forceinline__ void down_tile(const PipeRows<P>& rows, int d, int I, const Unit& un, uint8_t* lds,
                                           uint16_t* __restrict__ y) {
   f32x16 acc[FP::TW][FP::TT];
 #pragma unroll
@@ -74,7 +77,7 @@ __device__ __forceinline__ void down_tile(const PipeRows<FP>& rows, int d, int I
     for (int i = 0; i < FP::TT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-  pipe_mainloop<FP, MS, LT>(rows, I, lds, acc);
+  pipe_mainloop<P, MS, LT>(rows, I, lds, acc);
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     const int tr = pipe_token_row(i);
@@ -91,6 +94,7 @@ __device__ __forceinline__ void down_tile(const PipeRows<FP>& rows, int d, int I
   }
 }
 
+template <class P>
 __global__ __launch_bounds__(FP::NT, 1) void ffn_gate_up_bf16_kernel(
     int d, int I, int E, int n_rows, int a_rows, const int32_t* __restrict__ off, moe_row_mode mode,
     const int32_t* __restrict__ row_src, const uint16_t* __restrict__ a, const uint16_t* __restrict__ wgu,
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_gate_up_bf16_kernel(
     const Unit un = find_unit_balanced(t, off, E, n_rows, FP::BT / 32, cum);
     int s_first = source_row(mode, row_src, un.m0, un.seg0, a_rows);
     if (s_first < 0) s_first = 0;
-    PipeRows<FP> rows;
+    PipeRows<P> rows;
     rows.trs = pipe_rsrc(a, static_cast<uint64_t>(a_rows) * d * 2);
 #pragma unroll
     for (int q = 0; q < FP::TL; ++q) {
@@ -115,25 +119,33 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_gate_up_bf16_kernel(
       if (sr < 0) sr = s_first;                       // rows past the block: any valid row, never stored
       rows.ot[q] = (static_cast<uint32_t>(sr) * d + pipe_load_chunk(q) * 8) * 2;
     }
-    rows.wrs = pipe_rsrc(wgu + static_cast<size_t>(un.e) * 2 * I * d, static_cast<uint64_t>(2 * I) * d * 2);
+    if (P::TILED) {                                   // tile nb: the gate and up rows of H columns 128 nb ..
+      rows.wrs = pipe_rsrc(wgu + (static_cast<size_t>(un.e) * NB + un.nb) * FP::BW * d,
+                           static_cast<uint64_t>(FP::BW) * d * 2);
 #pragma unroll
-    for (int q = 0; q < FP::WL; ++q) {
-      const int rw = pipe_load_row(q);
-      const int j = (rw >> 5) & 3;                    // sub-tiles 0,1: gate rows; 2,3: the matching up rows
-      const int hcol = un.nb * kHcols + (rw >> 7) * 64 + (j & 1) * 32 + (rw & 31);
-      rows.ow[q] = (static_cast<uint32_t>(j >= 2 ? I + hcol : hcol) * d + pipe_load_chunk(q) * 8) * 2;
+      for (int q = 0; q < FP::WL; ++q) rows.ow[q] = ((q * 4 + (threadIdx.x >> 6)) * 64 + (threadIdx.x & 63)) * 16;
+    } else {
+      rows.wrs = pipe_rsrc(wgu + static_cast<size_t>(un.e) * 2 * I * d, static_cast<uint64_t>(2 * I) * d * 2);
+#pragma unroll
+      for (int q = 0; q < FP::WL; ++q) {
+        const int rw = pipe_load_row(q);
+        const int j = (rw >> 5) & 3;                  // sub-tiles 0,1: gate rows; 2,3: the matching up rows
+        const int hcol = un.nb * kHcols + (rw >> 7) * 64 + (j & 1) * 32 + (rw & 31);
+        rows.ow[q] = (static_cast<uint32_t>(j >= 2 ? I + hcol : hcol) * d + pipe_load_chunk(q) * 8) * 2;
+      }
     }
     // LT = ceil(nsub / 2) token load groups; wave row 0 has LT live sub-tiles, row 1 LT or LT - 1
     const bool full = live_token_subtiles(un.nsub) * 2 >= un.nsub;
     switch ((un.nsub + 1) / 2) {
-      case 4: full ? gate_up_tile<4, 4>(rows, d, I, un, lds_p, H) : gate_up_tile<3, 4>(rows, d, I, un, lds_p, H); break;
-      case 3: full ? gate_up_tile<3, 3>(rows, d, I, un, lds_p, H) : gate_up_tile<2, 3>(rows, d, I, un, lds_p, H); break;
-      case 2: full ? gate_up_tile<2, 2>(rows, d, I, un, lds_p, H) : gate_up_tile<1, 2>(rows, d, I, un, lds_p, H); break;
-      default: full ? gate_up_tile<1, 1>(rows, d, I, un, lds_p, H) : gate_up_tile<0, 1>(rows, d, I, un, lds_p, H); break;
+      case 4: full ? gate_up_tile<P, 4, 4>(rows, d, I, un, lds_p, H) : gate_up_tile<P, 3, 4>(rows, d, I, un, lds_p, H); break;
+      case 3: full ? gate_up_tile<P, 3, 3>(rows, d, I, un, lds_p, H) : gate_up_tile<P, 2, 3>(rows, d, I, un, lds_p, H); break;
+      case 2: full ? gate_up_tile<P, 2, 2>(rows, d, I, un, lds_p, H) : gate_up_tile<P, 1, 2>(rows, d, I, un, lds_p, H); break;
+      default: full ? gate_up_tile<P, 1, 1>(rows, d, I, un, lds_p, H) : gate_up_tile<P, 0, 1>(rows, d, I, un, lds_p, H); break;
     }
   }
 }
 
+template <class P>
 __global__ __launch_bounds__(FP::NT, 1) void ffn_down_bf16_kernel(int d, int I, int E, int n_rows,
                                                                   const int32_t* __restrict__ off,
                                                                   const uint16_t* __restrict__ H,
@@ -149,23 +161,31 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_down_bf16_kernel(int d, int I, 
   int x_off = 0;
   for (int t; (t = unit_queue_next(q, total, x_off, &tslot)) >= 0;) {
     const Unit un = find_unit_balanced(t, off, E, n_rows, FP::BT / 32, cum);
-    PipeRows<FP> rows;
+    PipeRows<P> rows;
     rows.trs = pipe_rsrc(H, static_cast<uint64_t>(n_rows) * I * 2);
 #pragma unroll
     for (int q = 0; q < FP::TL; ++q) {
       const int r = pipe_load_row(q);
       rows.ot[q] = (static_cast<uint32_t>(un.m0 + (r < un.rows ? r : 0)) * I + pipe_load_chunk(q) * 8) * 2;
     }
-    rows.wrs = pipe_rsrc(wd + static_cast<size_t>(un.e) * d * I, static_cast<uint64_t>(d) * I * 2);
+    if (P::TILED) {                                   // ceil(d / 256) tiles per expert, the last padded with zeros
+      rows.wrs = pipe_rsrc(wd + (static_cast<size_t>(un.e) * NB + un.nb) * FP::BW * I,
+                           static_cast<uint64_t>(FP::BW) * I * 2);
 #pragma unroll
-    for (int q = 0; q < FP::WL; ++q)
-      rows.ow[q] = (static_cast<uint32_t>(min(un.nb * FP::BW + pipe_load_row(q), d - 1)) * I + pipe_load_chunk(q) * 8) * 2;
+      for (int q = 0; q < FP::WL; ++q) rows.ow[q] = ((q * 4 + (threadIdx.x >> 6)) * 64 + (threadIdx.x & 63)) * 16;
+    } else {
+      rows.wrs = pipe_rsrc(wd + static_cast<size_t>(un.e) * d * I, static_cast<uint64_t>(d) * I * 2);
+#pragma unroll
+      for (int q = 0; q < FP::WL; ++q)
+        rows.ow[q] =
+            (static_cast<uint32_t>(min(un.nb * FP::BW + pipe_load_row(q), d - 1)) * I + pipe_load_chunk(q) * 8) * 2;
+    }
     const bool full = live_token_subtiles(un.nsub) * 2 >= un.nsub;
     switch ((un.nsub + 1) / 2) {
-      case 4: full ? down_tile<4, 4>(rows, d, I, un, lds_p, y) : down_tile<3, 4>(rows, d, I, un, lds_p, y); break;
-      case 3: full ? down_tile<3, 3>(rows, d, I, un, lds_p, y) : down_tile<2, 3>(rows, d, I, un, lds_p, y); break;
-      case 2: full ? down_tile<2, 2>(rows, d, I, un, lds_p, y) : down_tile<1, 2>(rows, d, I, un, lds_p, y); break;
-      default: full ? down_tile<1, 1>(rows, d, I, un, lds_p, y) : down_tile<0, 1>(rows, d, I, un, lds_p, y); break;
+      case 4: full ? down_tile<P, 4, 4>(rows, d, I, un, lds_p, y) : down_tile<P, 3, 4>(rows, d, I, un, lds_p, y); break;
+      case 3: full ? down_tile<P, 3, 3>(rows, d, I, un, lds_p, y) : down_tile<P, 2, 3>(rows, d, I, un, lds_p, y); break;
+      case 2: full ? down_tile<P, 2, 2>(rows, d, I, un, lds_p, y) : down_tile<P, 1, 2>(rows, d, I, un, lds_p, y); break;
+      default: full ? down_tile<P, 1, 1>(rows, d, I, un, lds_p, y) : down_tile<P, 0, 1>(rows, d, I, un, lds_p, y); break;
     }
   }
 }
@@ -182,35 +202,38 @@ static void set_lds_limits() {
   std::call_once(once, [] {
     // ring + schedule for up to 4096 experts; a refused request must not leave a sticky error
     const int need = FP::LDS_BYTES + 4 * 4097;
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_gate_up_bf16_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, need);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_down_bf16_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, need);
+    for (const void* k : {reinterpret_cast<const void*>(ffn_gate_up_bf16_kernel<FP>),
+                          reinterpret_cast<const void*>(ffn_gate_up_bf16_kernel<FPT>),
+                          reinterpret_cast<const void*>(ffn_down_bf16_kernel<FP>),
+                          reinterpret_cast<const void*>(ffn_down_bf16_kernel<FPT>)})
+      (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, need);
     (void)hipGetLastError();
   });
 }
 
-hipError_t launch_ffn_bf16_gate_up(const FfnArgs& p, hipStream_t st) {
+hipError_t launch_ffn_bf16_gate_up(const FfnArgs& p, hipStream_t st, bool tiled) {
   set_lds_limits();
   int* q = p.queue;
   if (hipError_t e = launch_queue_reset(q, st); e != hipSuccess) return e;
   const size_t lds = FP::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / FP::BT + p.n_experts;
   const int g1 = persistent_grid(mblocks * (p.I / kHcols), 1);
-  hipLaunchKernelGGL(ffn_gate_up_bf16_kernel, dim3(g1), dim3(FP::NT), lds, st, p.d, p.I, p.n_experts, p.n_rows,
+  hipLaunchKernelGGL(tiled ? ffn_gate_up_bf16_kernel<FPT> : ffn_gate_up_bf16_kernel<FP>, dim3(g1), dim3(FP::NT), lds,
+                     st, p.d, p.I, p.n_experts, p.n_rows,
                      p.a_rows, p.offsets, p.mode, p.row_src, static_cast<const uint16_t*>(p.a),
                      static_cast<const uint16_t*>(p.w_gu), static_cast<uint16_t*>(p.h), q);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_bf16_down(const FfnArgs& p, hipStream_t st) {
+hipError_t launch_ffn_bf16_down(const FfnArgs& p, hipStream_t st, bool tiled) {
   set_lds_limits();
   int* q = p.queue;
   if (hipError_t e = launch_queue_reset(q, st); e != hipSuccess) return e;
   const size_t lds = FP::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
   const long long mblocks = p.n_rows / FP::BT + p.n_experts;
   const int g2 = persistent_grid(mblocks * cdiv(p.d, FP::BW), 1);
-  hipLaunchKernelGGL(ffn_down_bf16_kernel, dim3(g2), dim3(FP::NT), lds, st, p.d, p.I, p.n_experts, p.n_rows,
+  hipLaunchKernelGGL(tiled ? ffn_down_bf16_kernel<FPT> : ffn_down_bf16_kernel<FP>, dim3(g2), dim3(FP::NT), lds, st,
+                     p.d, p.I, p.n_experts, p.n_rows,
                      p.offsets, static_cast<const uint16_t*>(p.h), static_cast<const uint16_t*>(p.w_d),
                      static_cast<uint16_t*>(p.y), q);
   return hipGetLastError();

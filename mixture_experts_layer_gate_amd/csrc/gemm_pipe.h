@@ -36,9 +36,14 @@ namespace moe {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int BW_, int BT_>
+// TILED: the weight rows come in the tiled layout of moe_tile_weights_bf16 (a
+// tile's 32-wide K steps are contiguous 16 KB blocks that are the stages' LDS
+// images); weight load q of a thread then reads the 16 bytes at
+// ((q * 4 + wave) * 64 + lane) * 16 of the block of K step kb / 64.
+template <int BW_, int BT_, bool TILED_ = false>
 struct Pipe {
   static constexpr int BW = BW_, BT = BT_, BK = 32, NS = 4, NT = 256;
+  static constexpr bool TILED = TILED_;
   static constexpr int TW = BW / 64, TT = BT / 64;          // 32x32 sub-tiles per wave
   static constexpr int ROWB = BK * 2;                        // bytes per row per stage
   static constexpr int W_BYTES = BW * ROWB, T_BYTES = BT * ROWB, STAGE = W_BYTES + T_BYTES;
@@ -85,7 +90,8 @@ __device__ __forceinline__ void pipe_issue_one(const PipeRows<P>& r, uint8_t* st
 #if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists only in the device pass
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: LDS address in SGPRs
   if (A)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.wrs, (lds_void_t*)(st + (q * 4 + w) * 1024), 16, r.ow[q], kb, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.wrs, (lds_void_t*)(st + (q * 4 + w) * 1024), 16, r.ow[q],
+                                             P::TILED ? kb * (P::W_BYTES / P::ROWB) : kb, 0, 0);
   else
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.trs, (lds_void_t*)(st + P::W_BYTES + (q * 4 + w) * 1024), 16, r.ot[q],
                                              kb, 0, 0);

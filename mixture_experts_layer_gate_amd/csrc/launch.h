@@ -79,8 +79,8 @@ size_t ffn_queue_offset(moe_dtype w, int n_rows, int I);
 size_t ffn_ws_bytes(moe_dtype w, int n_rows, int I);
 hipError_t launch_ffn_f32_gate_up(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_f32_down(const FfnArgs& a, hipStream_t st);
-hipError_t launch_ffn_bf16_gate_up(const FfnArgs& a, hipStream_t st);
-hipError_t launch_ffn_bf16_down(const FfnArgs& a, hipStream_t st);
+hipError_t launch_ffn_bf16_gate_up(const FfnArgs& a, hipStream_t st, bool tiled);
+hipError_t launch_ffn_bf16_down(const FfnArgs& a, hipStream_t st, bool tiled);
 hipError_t launch_ffn_fp8_gate_up(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_fp8_down(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_fp4_gate_up(const FfnArgs& a, hipStream_t st);
@@ -89,6 +89,8 @@ hipError_t launch_ffn_fp4_down(const FfnArgs& a, hipStream_t st);
 // ---- weight preparation
 hipError_t launch_quantize_weights(int n_mats, int rows, int cols, int gate_up, const void* w, void* codes,
                                    float* scale, hipStream_t st);
+hipError_t launch_tile_weights_bf16(int n_mats, int rows, int cols, int gate_up, const void* src, void* dst,
+                                    hipStream_t st);
 hipError_t launch_quantize_weights_mxfp4(int n_mats, int rows, int cols, int gate_up, const void* w, void* codes,
                                          void* scales, hipStream_t st);
 

@@ -115,6 +115,40 @@ hipError_t launch_quantize_weights(int n_mats, int rows, int cols, int gate_up, 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- bf16 tiles
+// Rows of row_bytes bytes (a multiple of 64) rearranged into the tiled layout
+// with 64-byte K steps (moe_tile_weights_bf16): a thread per 16-byte quarter,
+// quarters fastest, then tile rows, so a wave reads 16 rows' 64-byte pieces.
+__global__ __launch_bounds__(256) void tile_rows_kernel(long long n, int rows, int row_bytes, int gate_up,
+                                                        const uint8_t* __restrict__ src, uint8_t* __restrict__ dst) {
+  const int ntiles = (rows + 255) / 256, nst = row_bytes / 64, half = rows / 2;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<long long>(gridDim.x) * blockDim.x) {
+    const int c = static_cast<int>(i & 3), rw = static_cast<int>((i >> 2) & 255);
+    long long rest = i >> 10;
+    const int st = static_cast<int>(rest % nst);
+    rest /= nst;
+    const int t = static_cast<int>(rest % ntiles);
+    const long long mat = rest / ntiles;
+    const int row = tiled_row(t, rw, gate_up, half);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < rows) v = *reinterpret_cast<const uint4*>(src + (static_cast<size_t>(mat) * rows + row) * row_bytes + st * 64 + 16 * c);
+    const size_t off = ((static_cast<size_t>(mat) * ntiles + t) * nst + st) * 16384 + 64 * rw + 16 * (c ^ ((rw >> 2) & 3));
+    *reinterpret_cast<uint4*>(dst + off) = v;
+  }
+}
+
+hipError_t launch_tile_weights_bf16(int n_mats, int rows, int cols, int gate_up, const void* src, void* dst,
+                                    hipStream_t st) {
+  const long long n = static_cast<long long>(n_mats) * ((rows + 255) / 256) * (cols * 2 / 64) * 1024;
+  long long blocks = (n + 255) / 256;
+  const long long cap = static_cast<long long>(device_cu_count()) * 32;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(tile_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, n, rows, cols * 2, gate_up,
+                     static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst));
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- MXFP4
 // OCP microscaling FP4 of bf16 weights along each row ("DeepSeek V3 / V4
 // Infra", V4 post-training FP4 QAT of the expert weights): per 32 consecutive

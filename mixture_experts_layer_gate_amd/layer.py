@@ -54,13 +54,16 @@ class MoELayer:
     """
 
     def __init__(self, cfg, weights: Dict[str, torch.Tensor], device="cuda", keep_bf16: bool = False,
-                 gather_in_gemm: bool = True, pow2_act_scales: bool = False):
+                 gather_in_gemm: bool = True, pow2_act_scales: bool = False, tiled_bf16: bool = True):
         self.cfg = cfg
         self.shape = B.moe_shape.of(cfg)
         self.dev = torch.device(device)
         self.gemm = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_F8E4M3, "mxfp4": B.MOE_F4E2M1}[cfg.gemm]
         # E4M3 activations and H (fp8 and MXFP4 weights)
         self.q8 = self.gemm in (B.MOE_F8E4M3, B.MOE_F4E2M1)
+        # bf16 weights copied once into the tiled layout (contiguous 16 KB stage blocks)
+        if self.gemm == B.MOE_BF16 and tiled_bf16:
+            self.gemm = B.MOE_BF16_TILED
         self.gather_in_gemm = gather_in_gemm
         # fp8: the up-projection input quantised with power-of-two tile scales
         self.a_qdtype = B.MOE_F8E4M3_POW2 if pow2_act_scales else B.MOE_F8E4M3
@@ -90,6 +93,12 @@ class MoELayer:
                 self.w["all_" + kind], self.w["all_" + kind + "_scale"] = codes, scale
                 self.w["w_" + kind + "_scale"], self.w["s_" + kind + "_scale"] = scale[:N], scale[N:]
                 both = codes
+            elif self.gemm == B.MOE_BF16_TILED:
+                n, r, c = both.shape
+                tiled = torch.empty((n, B.mx_rows(r), c), dtype=both.dtype, device=self.dev)
+                B.moe_tile_weights_bf16(both, tiled, gate_up=(kind == "gate_up"))
+                del both
+                both = tiled
             self.w["all_" + kind] = both
             self.w["w_" + kind], self.w["s_" + kind] = both[:N], both[N:]
         self.ws = torch.empty(max(B.moe_workspace_bytes(self.shape, self.gemm), 256), dtype=torch.uint8,
@@ -177,7 +186,8 @@ class MoELayer:
         c = self.cfg
         n_rows = c.T * (c.topk + c.n_shared)
         if getattr(self, "h_all", None) is None:
-            hdt = {B.MOE_F32: torch.float32, B.MOE_BF16: torch.bfloat16, B.MOE_F8E4M3: torch.uint8, B.MOE_F4E2M1: torch.uint8}[self.gemm]
+            hdt = {B.MOE_F32: torch.float32, B.MOE_BF16: torch.bfloat16, B.MOE_F8E4M3: torch.uint8,
+                   B.MOE_F4E2M1: torch.uint8, B.MOE_BF16_TILED: torch.bfloat16}[self.gemm]
             self.h_all = torch.empty((n_rows, c.inter), dtype=hdt, device=self.dev)
             self.h_all_scale = (torch.empty((n_rows, c.inter // 128), dtype=torch.float32, device=self.dev)
                                 if self.q8 else None)
@@ -211,7 +221,8 @@ class MoELayer:
         c = self.cfg
         n_rows = c.T * c.topk
         if not hasattr(self, "h"):
-            hdt = {B.MOE_F32: torch.float32, B.MOE_BF16: torch.bfloat16, B.MOE_F8E4M3: torch.uint8, B.MOE_F4E2M1: torch.uint8}[self.gemm]
+            hdt = {B.MOE_F32: torch.float32, B.MOE_BF16: torch.bfloat16, B.MOE_F8E4M3: torch.uint8,
+                   B.MOE_F4E2M1: torch.uint8, B.MOE_BF16_TILED: torch.bfloat16}[self.gemm]
             self.h = torch.empty((n_rows, c.inter), dtype=hdt, device=self.dev)
             self.h_scale = (torch.empty((n_rows, c.inter // 128), dtype=torch.float32, device=self.dev)
                             if self.q8 else None)

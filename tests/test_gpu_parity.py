@@ -509,6 +509,55 @@ def test_grouped_ffn_bf16_half_column_tile(d):
             report(f"d={d} expert {e} ({sizes[e]} rows) y", rel_l2(y[off[e]:off[e + 1]], ref), TOL["bf16"])
 
 
+@pytest.mark.parametrize("kind", ["gate_up", "down_padded"])
+def test_tile_weights_bf16_bit_exact(kind):
+    """The tiled bf16 layout, byte for byte: the rows' bytes rearranged exactly as the E4M3 tiles (64-byte steps,
+    gate/up interleave, zero padding rows), rebuilt here with the NumPy transform."""
+    if kind == "gate_up":
+        cfg, inp = _inputs("c2")
+        w = inp["w_gate_up"][:2].contiguous()
+    else:
+        w = (torch.randn((2, 384, 256), generator=torch.Generator().manual_seed(4)) * 0.02).to(torch.bfloat16).to(DEV)
+    n, rr, cc = w.shape
+    out = torch.empty((n, B.mx_rows(rr), cc), dtype=torch.bfloat16, device=DEV)
+    B.moe_tile_weights_bf16(w, out, gate_up=(kind == "gate_up"))
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.uint8).numpy().reshape(n, -1)
+    raw = w.cpu().view(torch.uint8).numpy()                      # [n, rr, 2 cc] bytes
+    for e in range(n):
+        assert np.array_equal(got[e], tile_e4m3(raw[e], kind == "gate_up"))
+
+
+@pytest.mark.parametrize("d,mode", [(2048, "gather"), (2048, "direct"), (384, "gather")])
+def test_grouped_ffn_bf16_tiled_equals_row_major(d, mode):
+    """MOE_BF16_TILED only changes where the weight bytes are read from: its outputs equal MOE_BF16's bit for bit
+    (c2-sized experts; d = 384 pads the last down tile)."""
+    cfg = get_config("c2", n_routed=6, n_groups=1, topk_groups=1, T=1024, topk=2, d=d, inter=1408)
+    inp = generate(cfg, DEV)
+    sh = B.moe_shape.of(cfg)
+    sizes = [0, 1, 97, 256, 300, 700]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    src = np.random.default_rng(8).integers(0, cfg.T, n)
+    if mode == "gather":
+        a, a_rows, m, rs = inp["u"], cfg.T, B.MOE_ROWS_GATHER, _i32(src)
+    else:
+        a, a_rows, m, rs = inp["u"][torch.from_numpy(src).to(DEV)].contiguous(), n, B.MOE_ROWS_DIRECT, None
+    tg = torch.empty((6, B.mx_rows(2 * cfg.inter), d), dtype=torch.bfloat16, device=DEV)
+    td = torch.empty((6, B.mx_rows(d), cfg.inter), dtype=torch.bfloat16, device=DEV)
+    B.moe_tile_weights_bf16(inp["w_gate_up"], tg, gate_up=True)
+    B.moe_tile_weights_bf16(inp["w_down"], td, gate_up=False)
+    y0 = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    y1 = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    B.moe_grouped_ffn(sh, B.MOE_BF16, 6, n, _i32(off), m, rs, a, None, a_rows, inp["w_gate_up"], None, inp["w_down"],
+                      None, y0, _ws(cfg))
+    B.moe_grouped_ffn(sh, B.MOE_BF16_TILED, 6, n, _i32(off), m, rs, a, None, a_rows, tg, None, td, None, y1, _ws(cfg))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    ref = _oracle_ffn_rows(cfg, inp, 5, src[off[5]:off[6]])
+    report(f"tiled bf16 d={d} expert 5 y", rel_l2(y1[off[5]:off[6]], ref), TOL["bf16"])
+
+
 @pytest.mark.parametrize("name", ["c1", "c2"])
 def test_combine(name):
     cfg, inp = _inputs(name)
