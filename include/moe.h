@@ -277,6 +277,88 @@ moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, int3
                                 void* w_codes, float* w_scale, void* stream);
 
 /*
+ * ---- Backward of the layer (bf16 weights, fp32 accumulation, fp32 weight
+ * gradients). Readings of "DeepSeek_V3_Report: Annotation" (eq. (12)-(15) and
+ * the FP8 framework's mixed-precision and low-precision-activation sections):
+ * the selection is fixed, so the loss reaches the affinities only through the
+ * gates of the selected experts and the bias gets no gradient; the gating and
+ * the combine stay in high precision; the SwiGLU inputs are cached in the
+ * forward (moe_ffn_gate_up_cache) and its output is recomputed in the
+ * backward. One backward step: moe_combine_backward, moe_ffn_backward (routed
+ * and shared experts in one call on their concatenated rows, like
+ * moe_grouped_ffn), moe_route_backward, moe_input_grad.
+ *
+ * moe_ffn_gate_up_cache -- moe_ffn_gate_up for bf16 weights (MOE_BF16 or
+ * MOE_BF16_TILED) that also writes the SwiGLU inputs gu_cache [n_rows, 2I] bf16:
+ * G = a W_g^T in columns [0, I), U = a W_u^T in [I, 2I).
+ */
+moe_status moe_ffn_gate_up_cache(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                                 const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
+                                 const void* a, int32_t a_rows, const void* w_gate_up, void* h, void* gu_cache,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine_backward -- from d_out [T, d] (the gradient of the layer output):
+ * dy [T*K + N_s*T, d] bf16, dy[row_of(t,k)] = gate[t,k] * d_out[t] for the routed
+ * rows and dy[T*K + s*T + t] = d_out[t] for shared expert s; d_gate [T, K] fp32,
+ * d_gate[t,k] = d_out[t] . y_routed[row_of(t,k)] (fp32 sums). io = MOE_BF16.
+ */
+moe_status moe_combine_backward(const moe_shape* shape, moe_dtype io, const void* d_out, const void* y_routed,
+                                const int32_t* row_of, const float* topk_gate, void* dy, float* d_gate,
+                                void* stream);
+
+/*
+ * moe_route_backward -- through the gates (eq. (13)-(14)) and the sigmoid
+ * affinity (eq. (15)): per token, over its selected experts (S = sum of their
+ * s), ds_k = (d_gate_k - sum_j g_j d_gate_j) / S and dz_k = ds_k s_k (1 - s_k);
+ *   du_router [T, d] fp32 = sum_k dz_k e_{idx_k};
+ *   d_centroids [N_r, d] fp32: row e = sum over expert e's permuted rows r (in
+ *   row order) of dz(r) * u[perm_token[r]] (zero for experts without rows).
+ * scores, topk_idx, expert_offsets, perm_token and row_of are the forward's.
+ * workspace: at least T*K*4 bytes.
+ */
+moe_status moe_route_backward(const moe_shape* shape, moe_dtype act, const void* u, const void* centroids,
+                              const float* scores, const int32_t* topk_idx, const float* d_gate,
+                              const int32_t* expert_offsets, const int32_t* perm_token, const int32_t* row_of,
+                              float* du_router, float* d_centroids, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * moe_transpose_weights_bf16 -- W [n_mats][rows][cols] bf16 (rows, cols multiples
+ * of 128) -> W^T [n_mats][cols][rows] in the tiled layout of moe_tile_weights_bf16
+ * with gate_up = 0: the weights of the input-gradient GEMMs, which contract over
+ * W's rows (W_down [E, d, I] -> [E, I, d]; W_gate_up [E, 2I, d] -> [E, d, 2I]).
+ */
+moe_status moe_transpose_weights_bf16(int32_t n_mats, int32_t rows, int32_t cols, const void* w_bf16,
+                                      void* w_t_tiled, void* stream);
+
+/*
+ * moe_ffn_backward -- backward of the grouped SwiGLU FFN for the rows of
+ * n_experts experts (expert_offsets, mode, row_src, a, a_rows as in the forward):
+ *   dh = dy W_d; dG = dh U SiLU'(G), dU = dh SiLU(G) (G, U from gu_cache, SiLU' =
+ *   sigma (1 + x (1 - sigma))); da [n_rows, d] bf16 = dG W_g + dU W_u;
+ *   dw_down [n_experts, d, I] fp32 = dy^T h (h = SiLU(G) U recomputed);
+ *   dw_gate_up [n_experts, 2I, d] fp32 = [dG | dU]^T a,
+ * the weight-gradient sums running over each expert's rows (zero for experts
+ * without rows). w = MOE_BF16_TILED; w_gate_up_t / w_down_t: the transposed
+ * weights from moe_transpose_weights_bf16. dy [n_rows, d] bf16 (moe_combine_backward).
+ * workspace: moe_ffn_backward_workspace_bytes(shape, n_rows) bytes.
+ */
+size_t moe_ffn_backward_workspace_bytes(const moe_shape* shape, int32_t n_rows);
+moe_status moe_ffn_backward(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                            const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src, const void* a,
+                            int32_t a_rows, const void* gu_cache, const void* w_gate_up_t, const void* w_down_t,
+                            const void* dy, void* da, float* dw_gate_up, float* dw_down, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * moe_input_grad -- du [T, d] fp32 = d_out[t] (the residual) + du_router[t] (or 0
+ * when NULL) + sum_k da[row_of(t,k)] + sum_s da[T*K + s*T + t], in that order.
+ */
+moe_status moe_input_grad(const moe_shape* shape, const void* d_out, const float* du_router, const void* da,
+                          const int32_t* row_of, float* du, void* stream);
+
+/*
  * moe_tile_weights_bf16 -- copies bf16 expert weights into the tiled layout of
  * MOE_BF16_TILED, in which every 32-wide K step of a 256-row tile is one
  * contiguous 16 KB block (the grouped FFN's load pattern). n_mats matrices

@@ -58,6 +58,13 @@ _SIGS = {
     "moe_quantize_weights": [_I, _I, _I, _I, _P, _P, _P, _P],
     "moe_quantize_weights_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P],
     "moe_tile_weights_bf16": [_I, _I, _I, _I, _P, _P, _P],
+    "moe_ffn_gate_up_cache": [_S, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_combine_backward": [_S, _I, _P, _P, _P, _P, _P, _P, _P],
+    "moe_route_backward": [_S, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_transpose_weights_bf16": [_I, _I, _I, _P, _P, _P],
+    "moe_ffn_backward_workspace_bytes": [_S, _I],
+    "moe_ffn_backward": [_S, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_input_grad": [_S, _P, _P, _P, _P, _P, _P],
     "moe_workspace_bytes": [_S, _I],
     "moe_last_error": [],
     "moe_version": [],
@@ -270,3 +277,73 @@ def moe_tile_weights_bf16(w, out, gate_up: bool, stream=None):
     n, rows, cols = w.shape
     _need(out, n * mx_rows(rows) * cols, "out")
     _check(lib().moe_tile_weights_bf16(n, rows, cols, int(gate_up), _ptr(w), _ptr(out), _stream(stream)))
+
+
+# ---------------------------------------------------------------- backward
+
+def moe_ffn_gate_up_cache(shape: moe_shape, w: int, n_experts: int, n_rows: int, expert_offsets, mode: int, row_src,
+                          a, a_rows: int, w_gate_up, h, gu_cache, workspace=None, stream=None):
+    d, I = shape.d, shape.inter
+    _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a, a_rows * d, "a")
+    _need(h, n_rows * I, "h"); _need(gu_cache, n_rows * 2 * I, "gu_cache")
+    if mode == MOE_ROWS_GATHER:
+        _need(row_src, n_rows, "row_src")
+    _check(lib().moe_ffn_gate_up_cache(ctypes.byref(shape), w, n_experts, n_rows, _ptr(expert_offsets), mode,
+                                       _ptr(row_src), _ptr(a), a_rows, _ptr(w_gate_up), _ptr(h), _ptr(gu_cache),
+                                       _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_combine_backward(shape: moe_shape, d_out, y_routed, row_of, topk_gate, dy, d_gate, stream=None):
+    T, d, K = shape.T, shape.d, shape.topk
+    _need(d_out, T * d, "d_out"); _need(y_routed, T * K * d, "y_routed"); _need(row_of, T * K, "row_of")
+    _need(topk_gate, T * K, "topk_gate"); _need(dy, (T * K + shape.n_shared * T) * d, "dy")
+    _need(d_gate, T * K, "d_gate")
+    _check(lib().moe_combine_backward(ctypes.byref(shape), _dt(d_out), _ptr(d_out), _ptr(y_routed), _ptr(row_of),
+                                      _ptr(topk_gate), _ptr(dy), _ptr(d_gate), _stream(stream)))
+
+
+def moe_route_backward(shape: moe_shape, u, centroids, scores, topk_idx, d_gate, expert_offsets, perm_token, row_of,
+                       du_router, d_centroids, workspace, stream=None):
+    T, d, N, K = shape.T, shape.d, shape.n_routed, shape.topk
+    _need(u, T * d, "u"); _need(centroids, N * d, "centroids"); _need(scores, T * N, "scores")
+    _need(du_router, T * d, "du_router"); _need(d_centroids, N * d, "d_centroids")
+    _check(lib().moe_route_backward(ctypes.byref(shape), _dt(u), _ptr(u), _ptr(centroids), _ptr(scores),
+                                    _ptr(topk_idx), _ptr(d_gate), _ptr(expert_offsets), _ptr(perm_token),
+                                    _ptr(row_of), _ptr(du_router), _ptr(d_centroids), _ptr(workspace),
+                                    _nbytes(workspace), _stream(stream)))
+
+
+def moe_transpose_weights_bf16(w, out, stream=None):
+    """w [n, rows, cols] bf16 -> out: W^T [n, cols, rows] in the tiled layout (n * ceil(cols/256)*256 * rows)."""
+    n, rows, cols = w.shape
+    _need(out, n * mx_rows(cols) * rows, "out")
+    _check(lib().moe_transpose_weights_bf16(n, rows, cols, _ptr(w), _ptr(out), _stream(stream)))
+
+
+def moe_ffn_backward_workspace_bytes(shape: moe_shape, n_rows: int) -> int:
+    return int(lib().moe_ffn_backward_workspace_bytes(ctypes.byref(shape), n_rows))
+
+
+def moe_ffn_backward(shape: moe_shape, n_experts: int, n_rows: int, expert_offsets, mode: int, row_src, a,
+                     a_rows: int, gu_cache, w_gate_up_t, w_down_t, dy, da, dw_gate_up, dw_down, workspace,
+                     stream=None):
+    d, I = shape.d, shape.inter
+    _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a, a_rows * d, "a")
+    _need(gu_cache, n_rows * 2 * I, "gu_cache"); _need(dy, n_rows * d, "dy"); _need(da, n_rows * d, "da")
+    _need(w_gate_up_t, n_experts * mx_rows(d) * 2 * I, "w_gate_up_t")
+    _need(w_down_t, n_experts * mx_rows(I) * d, "w_down_t")
+    _need(dw_gate_up, n_experts * 2 * I * d, "dw_gate_up"); _need(dw_down, n_experts * d * I, "dw_down")
+    if mode == MOE_ROWS_GATHER:
+        _need(row_src, n_rows, "row_src")
+    _check(lib().moe_ffn_backward(ctypes.byref(shape), MOE_BF16_TILED, n_experts, n_rows, _ptr(expert_offsets), mode,
+                                  _ptr(row_src), _ptr(a), a_rows, _ptr(gu_cache), _ptr(w_gate_up_t), _ptr(w_down_t),
+                                  _ptr(dy), _ptr(da), _ptr(dw_gate_up), _ptr(dw_down), _ptr(workspace),
+                                  _nbytes(workspace), _stream(stream)))
+
+
+def moe_input_grad(shape: moe_shape, d_out, du_router, da, row_of, du, stream=None):
+    T, d = shape.T, shape.d
+    _need(d_out, T * d, "d_out"); _need(du, T * d, "du")
+    _need(da, (T * shape.topk + shape.n_shared * T) * d, "da")
+    _check(lib().moe_input_grad(ctypes.byref(shape), _ptr(d_out), _ptr(du_router), _ptr(da), _ptr(row_of), _ptr(du),
+                                _stream(stream)))

@@ -403,4 +403,133 @@ moe_status moe_quantize_weights_mxfp4(int32_t n_mats, int32_t rows, int32_t cols
                 "moe_quantize_weights_mxfp4", st);
 }
 
+// ---------------------------------------------------------------- backward
+
+moe_status moe_ffn_gate_up_cache(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                                 const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
+                                 const void* a, int32_t a_rows, const void* w_gate_up, void* h, void* gu_cache,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 1); r != MOE_OK) return r;
+  REQUIRE(w == MOE_BF16 || w == MOE_BF16_TILED, "ffn_gate_up_cache: the SwiGLU-input cache needs bf16 weights");
+  if (moe_status r = check_gate_up(shape, w, mode, row_src, a, nullptr, a_rows, w_gate_up, nullptr); r != MOE_OK)
+    return r;
+  REQUIRE(h != nullptr && gu_cache != nullptr, "ffn_gate_up_cache: h or gu_cache is NULL");
+  if (!workspace || ws_bytes < moe::kFfnQueueBytes)
+    return fail(MOE_E_WORKSPACE, "ffn_gate_up_cache: workspace of %zu bytes < %zu needed", ws_bytes,
+                moe::kFfnQueueBytes);
+  moe::FfnArgs p{shape->d, shape->inter, n_experts, n_rows, a_rows, expert_offsets, mode, row_src, a, nullptr,
+                 w_gate_up, nullptr, nullptr, nullptr, MOE_BF16, nullptr, h, nullptr, static_cast<int*>(workspace)};
+  p.gu_cache = gu_cache;
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(run_gate_up(w, p, st), "moe_ffn_gate_up_cache", st);
+}
+
+moe_status moe_combine_backward(const moe_shape* shape, moe_dtype io, const void* d_out, const void* y_routed,
+                                const int32_t* row_of, const float* topk_gate, void* dy, float* d_gate, void* stream) {
+  g_err.clear();
+  if (moe_status st = check_shape(shape); st != MOE_OK) return st;
+  REQUIRE(io == MOE_BF16, "combine_backward: io must be MOE_BF16");
+  REQUIRE(d_out && y_routed && row_of && topk_gate && dy && d_gate, "combine_backward: a required pointer is NULL");
+  SUPPORT(shape->d % 2 == 0, "combine_backward: d must be even");
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_combine_backward(moe::to_shape(*shape), d_out, y_routed, row_of, topk_gate, dy, d_gate, st),
+                "moe_combine_backward", st);
+}
+
+moe_status moe_route_backward(const moe_shape* shape, moe_dtype act, const void* u, const void* centroids,
+                              const float* scores, const int32_t* topk_idx, const float* d_gate,
+                              const int32_t* expert_offsets, const int32_t* perm_token, const int32_t* row_of,
+                              float* du_router, float* d_centroids, void* workspace, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (moe_status st = check_shape(shape); st != MOE_OK) return st;
+  REQUIRE(act == MOE_F32 || act == MOE_BF16, "route_backward: act must be MOE_F32 or MOE_BF16");
+  REQUIRE(u && centroids && scores && topk_idx && d_gate && expert_offsets && perm_token && row_of && du_router &&
+              d_centroids,
+          "route_backward: a required pointer is NULL");
+  const size_t need = static_cast<size_t>(shape->T) * shape->topk * sizeof(float);
+  if (!workspace || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "route_backward: workspace of %zu bytes < %zu needed", ws_bytes, need);
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_route_backward(moe::to_shape(*shape), act, u, centroids, scores, topk_idx, d_gate,
+                                           expert_offsets, perm_token, row_of, du_router, d_centroids,
+                                           static_cast<float*>(workspace), st),
+                "moe_route_backward", st);
+}
+
+moe_status moe_transpose_weights_bf16(int32_t n_mats, int32_t rows, int32_t cols, const void* w_bf16, void* w_t_tiled,
+                                      void* stream) {
+  g_err.clear();
+  REQUIRE(n_mats > 0 && rows > 0 && cols > 0, "transpose_weights_bf16: sizes must be positive");
+  SUPPORT(rows % 128 == 0 && cols % 128 == 0, "transpose_weights_bf16: rows (%d) and cols (%d) must be multiples of 128",
+          rows, cols);
+  REQUIRE(w_bf16 && w_t_tiled && w_bf16 != w_t_tiled, "transpose_weights_bf16: bad pointers");
+  SUPPORT(static_cast<long long>(n_mats) * (rows / 32) * ((cols + 255) / 256) < (1LL << 31),
+          "transpose_weights_bf16: too many blocks");
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_transpose_tile_bf16(n_mats, rows, cols, w_bf16, w_t_tiled, st), "moe_transpose_weights_bf16",
+                st);
+}
+
+size_t moe_ffn_backward_workspace_bytes(const moe_shape* shape, int32_t n_rows) {
+  if (!shape || n_rows < 0 || shape->inter <= 0) return 0;
+  const size_t r = static_cast<size_t>(n_rows), I = static_cast<size_t>(shape->inter);
+  return align256(r * I * 2) + align256(r * 2 * I * 2) + align256(r * I * 2) + 2 * moe::kFfnQueueBytes;
+}
+
+moe_status moe_ffn_backward(const moe_shape* shape, moe_dtype w, int32_t n_experts, int32_t n_rows,
+                            const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src, const void* a,
+                            int32_t a_rows, const void* gu_cache, const void* w_gate_up_t, const void* w_down_t,
+                            const void* dy, void* da, float* dw_gate_up, float* dw_down, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (moe_status r = check_ffn(shape, w, n_experts, n_rows, expert_offsets, 0); r != MOE_OK) return r;
+  REQUIRE(w == MOE_BF16_TILED, "ffn_backward: w must be MOE_BF16_TILED (weights from moe_transpose_weights_bf16)");
+  REQUIRE(a && gu_cache && w_gate_up_t && w_down_t && dy && da && dw_gate_up && dw_down,
+          "ffn_backward: a required pointer is NULL");
+  REQUIRE(a_rows > 0, "ffn_backward: a_rows must be positive");
+  REQUIRE(mode == MOE_ROWS_DIRECT || mode == MOE_ROWS_GATHER || mode == MOE_ROWS_SEGMENT,
+          "ffn_backward: bad row mode %d", static_cast<int>(mode));
+  REQUIRE(mode != MOE_ROWS_GATHER || row_src != nullptr, "ffn_backward: MOE_ROWS_GATHER needs row_src");
+  const int d = shape->d, I = shape->inter;
+  SUPPORT(static_cast<long long>(n_rows) * 2 * I * 2 < (1LL << 32) && static_cast<long long>(n_rows) * d * 2 < (1LL << 32),
+          "ffn_backward: n_rows * 2I and n_rows * d must stay below 2^31 elements");
+  const size_t need = moe_ffn_backward_workspace_bytes(shape, n_rows);
+  if (!workspace || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "ffn_backward: workspace of %zu bytes < %zu needed", ws_bytes, need);
+  char* ws = static_cast<char*>(workspace);
+  const size_t r = static_cast<size_t>(n_rows);
+  void* dh = ws;
+  void* dgu = ws + align256(r * I * 2);
+  void* h = ws + align256(r * I * 2) + align256(r * 2 * I * 2);
+  int* q = reinterpret_cast<int*>(ws + align256(r * I * 2) + align256(r * 2 * I * 2) + align256(r * I * 2));
+  auto st = static_cast<hipStream_t>(stream);
+  // dh = dy . W_d: the down-projection kernel with W_d^T (I output rows, K = d)
+  moe::FfnArgs p1{I, d, n_experts, n_rows, n_rows, expert_offsets, MOE_ROWS_DIRECT, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, w_down_t, nullptr, MOE_BF16, dh, const_cast<void*>(dy), nullptr, q};
+  hipError_t e = moe::launch_ffn_bf16_down(p1, st, true);
+  if (e == hipSuccess) e = moe::launch_swiglu_backward(n_rows, I, dh, gu_cache, dgu, h, st);
+  // da = [dG | dU] . W_gate_up: the same kernel with W_gate_up^T (d output rows, K = 2I)
+  moe::FfnArgs p2{d, 2 * I, n_experts, n_rows, n_rows, expert_offsets, MOE_ROWS_DIRECT, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, w_gate_up_t, nullptr, MOE_BF16, da, dgu, nullptr, q + moe::kQueueInts};
+  if (e == hipSuccess) e = moe::launch_ffn_bf16_down(p2, st, true);
+  // weight gradients: dW_d = dy^T h, dW_gate_up = [dG | dU]^T a
+  if (e == hipSuccess)
+    e = moe::launch_wgrad(d, I, n_experts, n_rows, n_rows, expert_offsets, MOE_ROWS_DIRECT, nullptr, dy, h, dw_down,
+                          st);
+  if (e == hipSuccess)
+    e = moe::launch_wgrad(2 * I, d, n_experts, n_rows, a_rows, expert_offsets, mode, row_src, dgu, a, dw_gate_up, st);
+  return finish(e, "moe_ffn_backward", st);
+}
+
+moe_status moe_input_grad(const moe_shape* shape, const void* d_out, const float* du_router, const void* da,
+                          const int32_t* row_of, float* du, void* stream) {
+  g_err.clear();
+  if (moe_status st = check_shape(shape); st != MOE_OK) return st;
+  REQUIRE(d_out && da && row_of && du, "input_grad: a required pointer is NULL");
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_input_grad(moe::to_shape(*shape), d_out, du_router, da, row_of, du, st), "moe_input_grad",
+                st);
+}
+
 }  // extern "C"

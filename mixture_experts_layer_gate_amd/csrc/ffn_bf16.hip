@@ -40,7 +40,7 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, floa
 // never merge across variants.
 template <class P, int MS, int LT>
 __device__ __forceinline__ void gate_up_tile(const PipeRows<P>& rows, int d, int I, const Unit& un, uint8_t* lds,
-                                             uint16_t* __restrict__ H) {
+                                             uint16_t* __restrict__ H, uint16_t* __restrict__ GU) {
   f32x16 acc[FP::TW][FP::TT];
 #pragma unroll
   for (int j = 0; j < FP::TW; ++j)
@@ -63,6 +63,18 @@ __device__ __forceinline__ void gate_up_tile(const PipeRows<P>& rows, int d, int
                        silu(acc[j][i][4 * q + 1]) * acc[j + 2][i][4 * q + 1],
                        silu(acc[j][i][4 * q + 2]) * acc[j + 2][i][4 * q + 2],
                        silu(acc[j][i][4 * q + 3]) * acc[j + 2][i][4 * q + 3]);
+      if (GU) {                                       // the SwiGLU inputs for the backward: [G | U] rows of 2I
+        uint16_t* grow = GU + static_cast<size_t>(un.m0 + tr) * 2 * I + un.nb * kHcols + ww * 64 + 4 * h;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            store_bf16x4(grow + j * 32 + 8 * q, acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                         acc[j][i][4 * q + 3]);
+            store_bf16x4(grow + I + j * 32 + 8 * q, acc[j + 2][i][4 * q], acc[j + 2][i][4 * q + 1],
+                         acc[j + 2][i][4 * q + 2], acc[j + 2][i][4 * q + 3]);
+          }
+      }
     }
   }
 }
@@ -98,7 +110,7 @@ template <class P>
 __global__ __launch_bounds__(FP::NT, 1) void ffn_gate_up_bf16_kernel(
     int d, int I, int E, int n_rows, int a_rows, const int32_t* __restrict__ off, moe_row_mode mode,
     const int32_t* __restrict__ row_src, const uint16_t* __restrict__ a, const uint16_t* __restrict__ wgu,
-    uint16_t* __restrict__ H, int* __restrict__ q) {
+    uint16_t* __restrict__ H, uint16_t* __restrict__ GU, int* __restrict__ q) {
   extern __shared__ __align__(16) uint8_t lds_p[];
   int* cum = reinterpret_cast<int*>(lds_p + FP::LDS_BYTES);
   __shared__ int wtmp[16];
@@ -137,10 +149,10 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_gate_up_bf16_kernel(
     // LT = ceil(nsub / 2) token load groups; wave row 0 has LT live sub-tiles, row 1 LT or LT - 1
     const bool full = live_token_subtiles(un.nsub) * 2 >= un.nsub;
     switch ((un.nsub + 1) / 2) {
-      case 4: full ? gate_up_tile<P, 4, 4>(rows, d, I, un, lds_p, H) : gate_up_tile<P, 3, 4>(rows, d, I, un, lds_p, H); break;
-      case 3: full ? gate_up_tile<P, 3, 3>(rows, d, I, un, lds_p, H) : gate_up_tile<P, 2, 3>(rows, d, I, un, lds_p, H); break;
-      case 2: full ? gate_up_tile<P, 2, 2>(rows, d, I, un, lds_p, H) : gate_up_tile<P, 1, 2>(rows, d, I, un, lds_p, H); break;
-      default: full ? gate_up_tile<P, 1, 1>(rows, d, I, un, lds_p, H) : gate_up_tile<P, 0, 1>(rows, d, I, un, lds_p, H); break;
+      case 4: full ? gate_up_tile<P, 4, 4>(rows, d, I, un, lds_p, H, GU) : gate_up_tile<P, 3, 4>(rows, d, I, un, lds_p, H, GU); break;
+      case 3: full ? gate_up_tile<P, 3, 3>(rows, d, I, un, lds_p, H, GU) : gate_up_tile<P, 2, 3>(rows, d, I, un, lds_p, H, GU); break;
+      case 2: full ? gate_up_tile<P, 2, 2>(rows, d, I, un, lds_p, H, GU) : gate_up_tile<P, 1, 2>(rows, d, I, un, lds_p, H, GU); break;
+      default: full ? gate_up_tile<P, 1, 1>(rows, d, I, un, lds_p, H, GU) : gate_up_tile<P, 0, 1>(rows, d, I, un, lds_p, H, GU); break;
     }
   }
 }
@@ -221,7 +233,8 @@ hipError_t launch_ffn_bf16_gate_up(const FfnArgs& p, hipStream_t st, bool tiled)
   hipLaunchKernelGGL(tiled ? ffn_gate_up_bf16_kernel<FPT> : ffn_gate_up_bf16_kernel<FP>, dim3(g1), dim3(FP::NT), lds,
                      st, p.d, p.I, p.n_experts, p.n_rows,
                      p.a_rows, p.offsets, p.mode, p.row_src, static_cast<const uint16_t*>(p.a),
-                     static_cast<const uint16_t*>(p.w_gu), static_cast<uint16_t*>(p.h), q);
+                     static_cast<const uint16_t*>(p.w_gu), static_cast<uint16_t*>(p.h),
+                     static_cast<uint16_t*>(p.gu_cache), q);
   return hipGetLastError();
 }
 

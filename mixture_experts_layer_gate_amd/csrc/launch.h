@@ -71,6 +71,7 @@ struct FfnArgs {
   void* h;         // SwiGLU output [n_rows, I]
   float* h_scale;  // fp8: [n_rows, I/128]
   int* queue;      // unit-queue counters of this launch (kQueueInts ints of workspace)
+  void* gu_cache = nullptr;   // bf16 gate/up: the SwiGLU inputs [n_rows, 2I] for the backward, or NULL
 };
 constexpr size_t kFfnQueueBytes = 128;   // per launch
 // Workspace of moe_grouped_ffn: H (+ its fp8 scales), then the queue
@@ -85,6 +86,21 @@ hipError_t launch_ffn_fp8_gate_up(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_fp8_down(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_fp4_gate_up(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_fp4_down(const FfnArgs& a, hipStream_t st);
+
+// ---- backward
+hipError_t launch_combine_backward(const Shape& s, const void* dout, const void* y, const int32_t* row_of,
+                                   const float* gate, void* dy, float* dgate, hipStream_t st);
+hipError_t launch_route_backward(const Shape& s, moe_dtype act, const void* u, const void* cent, const float* scores,
+                                 const int32_t* idx, const float* dgate, const int32_t* off,
+                                 const int32_t* perm_token, const int32_t* row_of, float* du_router, float* dcent,
+                                 float* dz_row, hipStream_t st);
+hipError_t launch_swiglu_backward(long long n_rows, int I, const void* dh, const void* gu, void* dgu, void* h,
+                                  hipStream_t st);
+hipError_t launch_input_grad(const Shape& s, const void* dout, const float* du_router, const void* da,
+                             const int32_t* row_of, float* du, hipStream_t st);
+hipError_t launch_transpose_tile_bf16(int n_mats, int rows, int cols, const void* w, void* out, hipStream_t st);
+hipError_t launch_wgrad(int M, int N, int E, int n_rows, int a_rows, const int32_t* off, moe_row_mode mode,
+                        const int32_t* row_src, const void* X, const void* Y, float* C, hipStream_t st);
 
 // ---- weight preparation
 hipError_t launch_quantize_weights(int n_mats, int rows, int cols, int gate_up, const void* w, void* codes,

@@ -51,11 +51,20 @@ class MoELayer:
     s_down [N_s,d,I] (fp32 or bf16), centroids [N_r,d], bias [N_r] fp32.
     For fp8 the bf16 weights are block-quantised on the device by
     moe_quantize_weights and the bf16 copies are dropped unless keep_bf16.
+
+    train=True (bf16 weights only) also keeps the weights transposed for the
+    input-gradient GEMMs and caches the SwiGLU inputs in forward_train, so that
+    backward(d_out) returns du and leaves the centroid and expert-weight
+    gradients in self.grads.
     """
 
     def __init__(self, cfg, weights: Dict[str, torch.Tensor], device="cuda", keep_bf16: bool = False,
-                 gather_in_gemm: bool = True, pow2_act_scales: bool = False, tiled_bf16: bool = True):
+                 gather_in_gemm: bool = True, pow2_act_scales: bool = False, tiled_bf16: bool = True,
+                 train: bool = False):
         self.cfg = cfg
+        if train and cfg.gemm != "bf16":
+            raise ValueError("MoELayer(train=True) needs bf16 expert GEMMs")
+        self.train = train
         self.shape = B.moe_shape.of(cfg)
         self.dev = torch.device(device)
         self.gemm = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_F8E4M3, "mxfp4": B.MOE_F4E2M1}[cfg.gemm]
@@ -97,13 +106,41 @@ class MoELayer:
                 n, r, c = both.shape
                 tiled = torch.empty((n, B.mx_rows(r), c), dtype=both.dtype, device=self.dev)
                 B.moe_tile_weights_bf16(both, tiled, gate_up=(kind == "gate_up"))
+                if train:
+                    wt = torch.empty((n, B.mx_rows(c), r), dtype=both.dtype, device=self.dev)
+                    B.moe_transpose_weights_bf16(both, wt)
+                    self.w["all_" + kind + "_t"] = wt
                 del both
                 both = tiled
             self.w["all_" + kind] = both
             self.w["w_" + kind], self.w["s_" + kind] = both[:N], both[N:]
         self.ws = torch.empty(max(B.moe_workspace_bytes(self.shape, self.gemm), 256), dtype=torch.uint8,
                               device=self.dev)
+        if train and self.gemm != B.MOE_BF16_TILED:
+            raise ValueError("MoELayer(train=True) needs the tiled bf16 weights (tiled_bf16=True)")
         self._alloc()
+        if train:
+            self._alloc_train()
+
+    def _alloc_train(self):
+        c, dev = self.cfg, self.dev
+        T, K, N, Ns, d, I = c.T, c.topk, c.n_routed, c.n_shared, c.d, c.inter
+        n_rows = T * (K + Ns)
+        bf = torch.bfloat16
+        self.h_all = torch.empty((n_rows, I), dtype=bf, device=dev)
+        self.gu_cache = torch.empty((n_rows, 2 * I), dtype=bf, device=dev)
+        self.dy_all = torch.empty((n_rows, d), dtype=bf, device=dev)
+        self.da_all = torch.empty((n_rows, d), dtype=bf, device=dev)
+        self.d_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.du_router = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.du = torch.empty((T, d), dtype=torch.float32, device=dev)
+        dwg = torch.empty((N + Ns, 2 * I, d), dtype=torch.float32, device=dev)
+        dwd = torch.empty((N + Ns, d, I), dtype=torch.float32, device=dev)
+        self.grads = {"centroids": torch.empty((N, d), dtype=torch.float32, device=dev),
+                      "all_gate_up": dwg, "all_down": dwd, "w_gate_up": dwg[:N], "w_down": dwd[:N],
+                      "s_gate_up": dwg[N:], "s_down": dwd[N:]}
+        self.ws_bwd = torch.empty(max(B.moe_ffn_backward_workspace_bytes(self.shape, n_rows), T * K * 4, 256),
+                                  dtype=torch.uint8, device=dev)
 
     def _alloc(self):
         c, dev = self.cfg, self.dev
@@ -279,6 +316,40 @@ class MoELayer:
         out = self.forward(u)
         self.bias_update()
         return out
+
+    # ---------------------------------------------------------------- training
+    def forward_train(self, u: torch.Tensor) -> torch.Tensor:
+        """forward() that also caches the SwiGLU inputs of every row for backward() (train=True)."""
+        if not self.train:
+            raise RuntimeError("forward_train needs MoELayer(train=True)")
+        c = self.cfg
+        u = u.contiguous()
+        self.u_saved = u
+        self.route(u)
+        self.permute(u)
+        E, n_rows = c.n_routed + c.n_shared, c.T * (c.topk + c.n_shared)
+        B.moe_ffn_gate_up_cache(self.shape, self.gemm, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all,
+                                u, c.T, self.w["all_gate_up"], self.h_all, self.gu_cache, self.ws)
+        B.moe_ffn_down(self.shape, self.gemm, E, n_rows, self.offsets_all, self.h_all, None, self.w["all_down"],
+                       None, self.y_all, self.ws)
+        self.combine(u)
+        return self.out
+
+    def backward(self, d_out: torch.Tensor) -> torch.Tensor:
+        """Gradients of the last forward_train for the output gradient d_out [T, d]: returns du [T, d] fp32 and
+        fills self.grads (centroids, expert gate/up and down weights, fp32)."""
+        c = self.cfg
+        d_out = d_out.contiguous()
+        E, n_rows = c.n_routed + c.n_shared, c.T * (c.topk + c.n_shared)
+        B.moe_combine_backward(self.shape, d_out, self.y_routed, self.row_of, self.topk_gate, self.dy_all, self.d_gate)
+        B.moe_ffn_backward(self.shape, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all, self.u_saved,
+                           c.T, self.gu_cache, self.w["all_gate_up_t"], self.w["all_down_t"], self.dy_all,
+                           self.da_all, self.grads["all_gate_up"], self.grads["all_down"], self.ws_bwd)
+        B.moe_route_backward(self.shape, self.u_saved, self.centroids, self.scores, self.topk_idx, self.d_gate,
+                             self.expert_offsets, self.perm_token, self.row_of, self.du_router,
+                             self.grads["centroids"], self.ws_bwd)
+        B.moe_input_grad(self.shape, d_out, self.du_router, self.da_all, self.row_of, self.du)
+        return self.du
 
     def outputs(self) -> LayerOutputs:
         return LayerOutputs(self.topk_idx, self.topk_gate, self.expert_load, self.expert_offsets, self.perm_token,

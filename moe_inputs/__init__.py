@@ -37,7 +37,7 @@ import numpy as np
 import torch
 
 __all__ = ["MoEConfig", "CONFIGS", "get_config", "generate", "generate_tokens",
-           "generate_expert", "derive_seed", "zipf_norms"]
+           "generate_expert", "generate_output_grad", "derive_seed", "zipf_norms"]
 
 
 @dataclass(frozen=True)
@@ -100,7 +100,7 @@ CONFIGS: Dict[str, MoEConfig] = {
 
 _CFG_ID = {"c1": 1, "c2": 2, "c3": 3, "c4": 3, "c5": 5}  # c4 reuses c3's draws
 _TENSOR_ID = {"u": 1, "centroids": 2, "bias": 3, "w_gate_up": 4, "w_down": 5,
-              "s_gate_up": 6, "s_down": 7}
+              "s_gate_up": 6, "s_down": 7, "d_out": 8}
 
 
 def get_config(name: str, **overrides) -> MoEConfig:
@@ -171,6 +171,11 @@ def _centroids(cfg: MoEConfig, device, seed: int) -> torch.Tensor:
 def generate_tokens(cfg: MoEConfig, device="cpu", step: int = 0, seed: int = 0) -> torch.Tensor:
     """u [T, d] ~ N(0, 1) in the activation dtype (fresh draw per step)."""
     return _normal((cfg.T, cfg.d), 1.0, cfg.torch_dtype, device, derive_seed(seed, cfg, "u", step=step))
+
+
+def generate_output_grad(cfg: MoEConfig, device="cpu", step: int = 0, seed: int = 0) -> torch.Tensor:
+    """d_out [T, d] ~ N(0, 1) in the activation dtype: the gradient of a loss w.r.t. the layer output."""
+    return _normal((cfg.T, cfg.d), 1.0, cfg.torch_dtype, device, derive_seed(seed, cfg, "d_out", step=step))
 
 
 def generate_expert(cfg: MoEConfig, e: int, shared: bool = False, device="cpu", seed: int = 0):

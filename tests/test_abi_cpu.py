@@ -149,3 +149,34 @@ def test_workspace_size_covers_each_call():
     n8 = B.moe_workspace_bytes(sh, B.MOE_F8E4M3)
     assert 8192 * 8 * 2048 <= n8 < n
     assert B.moe_workspace_bytes(_shape(T=-1), B.MOE_BF16) == 0
+
+
+def test_backward_validation():
+    L = B.lib()
+    sh = _shape()
+    P = lambda: [FAKE] * 3
+    # the SwiGLU-input cache is a bf16-weight feature
+    assert L.moe_ffn_gate_up_cache(ctypes.byref(sh), B.MOE_F8E4M3, 4, 10, FAKE, B.MOE_ROWS_GATHER, FAKE, FAKE, 10,
+                                   FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == B.MOE_E_INVALID
+    assert L.moe_ffn_gate_up_cache(ctypes.byref(sh), B.MOE_BF16, 4, 10, FAKE, B.MOE_ROWS_GATHER, FAKE, FAKE, 10,
+                                   FAKE, FAKE, None, FAKE, 1 << 20, None) == B.MOE_E_INVALID
+    assert L.moe_ffn_gate_up_cache(ctypes.byref(sh), B.MOE_BF16, 4, 10, FAKE, B.MOE_ROWS_GATHER, FAKE, FAKE, 10,
+                                   FAKE, FAKE, FAKE, FAKE, 16, None) == B.MOE_E_WORKSPACE
+    assert L.moe_combine_backward(ctypes.byref(sh), B.MOE_F32, *P(), FAKE, FAKE, FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_combine_backward(ctypes.byref(sh), B.MOE_BF16, *P(), FAKE, None, FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_route_backward(ctypes.byref(sh), B.MOE_BF16, *P(), *P(), *P(), FAKE, FAKE, 64 * 2 * 4 - 4,
+                                None) == B.MOE_E_WORKSPACE
+    assert L.moe_route_backward(ctypes.byref(sh), B.MOE_F8E4M3, *P(), *P(), *P(), FAKE, FAKE, 1 << 20,
+                                None) == B.MOE_E_INVALID
+    assert L.moe_transpose_weights_bf16(1, 100, 128, FAKE, ctypes.c_void_p(32), None) == B.MOE_E_UNSUPPORTED
+    assert L.moe_transpose_weights_bf16(1, 128, 128, FAKE, FAKE, None) == B.MOE_E_INVALID        # in place
+    assert L.moe_transpose_weights_bf16(0, 128, 128, FAKE, ctypes.c_void_p(32), None) == B.MOE_E_INVALID
+    need = B.moe_ffn_backward_workspace_bytes(sh, 10)
+    assert need >= 10 * 128 * 2 * 4
+    args = lambda w=B.MOE_BF16_TILED, ws=need, dy=FAKE: [ctypes.byref(sh), w, 4, 10, FAKE, B.MOE_ROWS_GATHER, FAKE,
+                                                       FAKE, 10, FAKE, FAKE, FAKE, dy, FAKE, FAKE, FAKE, FAKE, ws, None]
+    assert L.moe_ffn_backward(*args(w=B.MOE_BF16)) == B.MOE_E_INVALID          # needs the transposed tiled weights
+    assert L.moe_ffn_backward(*args(dy=None)) == B.MOE_E_INVALID
+    assert L.moe_ffn_backward(*args(ws=need - 1)) == B.MOE_E_WORKSPACE
+    assert b"workspace" in L.moe_last_error()
+    assert L.moe_input_grad(ctypes.byref(sh), FAKE, None, None, FAKE, FAKE, None) == B.MOE_E_INVALID

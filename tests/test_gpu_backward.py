@@ -1,0 +1,166 @@
+"""GPU parity of the layer backward (bf16 expert GEMMs) against the fp64 oracle.
+
+The layer runs forward_train + backward through the libmoe backward calls
+(moe_ffn_gate_up_cache, moe_combine_backward, moe_ffn_backward,
+moe_route_backward, moe_input_grad); the oracle recomputes every gradient from
+the generated inputs and the generated output gradient only. Small workloads
+are compared whole; the DeepSeek-V3-shaped one on sampled experts, tokens and
+weight-gradient rows / columns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_inputs import generate, generate_output_grad, get_config
+from mixture_experts_layer_gate_amd import MoELayer
+from mixture_experts_layer_gate_amd import binding as B
+from parity import TOL, np64, npi, rel_l2, report, routing_mismatches, tile_e4m3
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("n,rows,cols", [(2, 384, 256), (1, 256, 384), (3, 128, 640)])
+def test_transpose_weights_bit_exact(n, rows, cols):
+    """W [n, rows, cols] -> W^T in the tiled bf16 layout, byte for byte (cols % 256 == 128 pads the last tile)."""
+    w = (torch.randn((n, rows, cols), generator=torch.Generator().manual_seed(rows + cols)) * 0.02).to(torch.bfloat16)
+    out = torch.empty((n, B.mx_rows(cols), rows), dtype=torch.bfloat16, device=DEV)
+    out.fill_(1.0)                                               # padding rows must come out zero
+    B.moe_transpose_weights_bf16(w.to(DEV), out)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.uint8).numpy().reshape(n, -1)
+    for e in range(n):
+        raw = w[e].t().contiguous().view(torch.uint8).numpy()    # W^T bytes [cols, 2 rows]
+        assert np.array_equal(got[e], tile_e4m3(raw, False))
+
+
+def _train_layer(cfg, inp, d_out):
+    layer = MoELayer(cfg, inp, DEV, train=True)
+    layer.forward_train(inp["u"])
+    du = layer.backward(d_out)
+    torch.cuda.synchronize()
+    return layer, du
+
+
+BWD_CASES = [
+    ("c1", dict(gemm="bf16", act="bf16")),
+    ("c1", dict(gemm="bf16", act="bf16", T=200, inter=384)),     # ragged T, 1.5 tiles of I
+    ("c2", {}),
+]
+
+
+@pytest.mark.parametrize("name,over", BWD_CASES)
+def test_layer_backward(name, over):
+    cfg = get_config(name, **over)
+    inp = generate(cfg, DEV)
+    d_out = generate_output_grad(cfg, DEV)
+    layer, du = _train_layer(cfg, inp, d_out)
+    res = oracle.layer_backward(cfg, inp, d_out)
+    N, Ns, tag = cfg.n_routed, cfg.n_shared, f"{name}{over}"
+    bad = routing_mismatches(layer.topk_idx, res["route"])
+    ok = np.ones(cfg.T, dtype=bool)
+    ok[bad] = False
+    # experts whose row set differs between the two selections are left out of the weight gradients
+    g_idx = npi(layer.topk_idx)
+    touched = set(g_idx[bad].ravel().tolist()) | set(res["route"]["idx"][bad].ravel().tolist())
+    good_e = np.array([e for e in range(N) if e not in touched], dtype=np.int64)
+    if bad.size:
+        print(f"[parity] {tag}: {bad.size} near-tie tokens excluded, {N - good_e.size} experts")
+    else:
+        assert np.array_equal(npi(layer.expert_offsets), res["offsets"])
+        assert np.array_equal(npi(layer.perm_token), res["perm_token"])
+    tol = TOL["bf16"]
+    report(f"{tag} d_gate", rel_l2(np64(layer.d_gate)[ok], res["d_gate"][ok]), tol)
+    report(f"{tag} du", rel_l2(np64(du)[ok], res["du"][ok]), tol)
+    report(f"{tag} du - d_out", rel_l2((np64(du) - np64(d_out))[ok], (res["du"] - np64(d_out))[ok]), tol)
+    report(f"{tag} d_centroids", rel_l2(np64(layer.grads["centroids"])[good_e], res["d_centroids"][good_e]), tol)
+    report(f"{tag} dW_gate_up routed", rel_l2(np64(layer.grads["w_gate_up"])[good_e], res["d_w_gate_up"][good_e]), tol)
+    report(f"{tag} dW_down routed", rel_l2(np64(layer.grads["w_down"])[good_e], res["d_w_down"][good_e]), tol)
+    if Ns:
+        report(f"{tag} dW_gate_up shared", rel_l2(np64(layer.grads["s_gate_up"]), res["d_s_gate_up"]), tol)
+        report(f"{tag} dW_down shared", rel_l2(np64(layer.grads["s_down"]), res["d_s_down"]), tol)
+    # experts without rows get exactly zero weight gradients
+    load = np.diff(npi(layer.expert_offsets))
+    for e in np.flatnonzero(load == 0)[:4]:
+        assert not torch.any(layer.grads["w_gate_up"][e]) and not torch.any(layer.grads["w_down"][e])
+        assert not torch.any(layer.grads["centroids"][e])
+
+
+def test_backward_is_deterministic():
+    """Every gradient sum runs in a fixed order: two backward passes give the same bits."""
+    cfg = get_config("c2", T=1024)
+    inp = generate(cfg, DEV)
+    d_out = generate_output_grad(cfg, DEV)
+    layer, du = _train_layer(cfg, inp, d_out)
+    first = {k: v.clone() for k, v in layer.grads.items() if k in ("centroids", "all_gate_up", "all_down")}
+    du0 = du.clone()
+    layer.forward_train(inp["u"])
+    layer.backward(d_out)
+    torch.cuda.synchronize()
+    assert torch.equal(du0, layer.du)
+    for k, v in first.items():
+        assert torch.equal(v, layer.grads[k]), k
+
+
+def _w64(inp, key, e):
+    return np64(inp[key][e])
+
+
+def test_v3_backward_sampled():
+    """DeepSeek-V3 shape: weight gradients of sampled routed experts in full, sampled rows / columns of the shared
+    expert's, and du on sampled tokens (every routed and shared row of the token recomputed by the oracle)."""
+    cfg = get_config("c3")
+    inp = generate(cfg, DEV)
+    d_out = generate_output_grad(cfg, DEV)
+    T, K, N, d, I = cfg.T, cfg.topk, cfg.n_routed, cfg.d, cfg.inter
+    layer, du = _train_layer(cfg, inp, d_out)
+    r = oracle.route(inp["u"], inp["centroids"], inp["bias"], cfg.n_groups, cfg.topk_groups, cfg.group_topn, K)
+    bad = set(routing_mismatches(layer.topk_idx, r).tolist())
+    o_off, o_perm, _ = oracle.permute(r["idx"], N)
+    u64, dO = np64(inp["u"]), np64(d_out)
+    tol = TOL["bf16"]
+    # routed experts: the smallest and the largest load, whole weight gradients
+    load = np.diff(o_off)
+    g_idx = npi(layer.topk_idx)
+    for e in sorted({int(np.argmin(load)), int(np.argmax(load))}):
+        toks = o_perm[o_off[e]:o_off[e + 1]]
+        if any(t in bad for t in toks) or any(e in g_idx[t] for t in bad):
+            continue
+        slot = np.array([int(np.flatnonzero(r["idx"][t] == e)[0]) for t in toks])
+        dy = r["gate"][toks, slot][:, None] * dO[toks]
+        _, dwg, dwd = oracle.ffn_backward(u64[toks], _w64(inp, "w_gate_up", e), _w64(inp, "w_down", e), dy)
+        report(f"c3 expert {e} ({toks.size} rows) dW_gate_up", rel_l2(layer.grads["w_gate_up"][e], dwg), tol)
+        report(f"c3 expert {e} dW_down", rel_l2(layer.grads["w_down"][e], dwd), tol)
+    # shared expert: dW_down columns j need h[:, j] only, dW_gate_up rows j and I + j need dh[:, j] only
+    wg, wd = _w64(inp, "s_gate_up", 0), _w64(inp, "s_down", 0)
+    for j in (0, 777, I - 1):
+        G, U = u64 @ wg[j], u64 @ wg[I + j]
+        sg = 1.0 / (1.0 + np.exp(-G))
+        dh = dO @ wd[:, j]
+        report(f"c3 shared dW_down[:, {j}]", rel_l2(layer.grads["s_down"][0][:, j], dO.T @ (G * sg * U)), tol)
+        dG = dh * U * sg * (1.0 + G * (1.0 - sg))
+        report(f"c3 shared dW_gate_up[{j}]", rel_l2(layer.grads["s_gate_up"][0][j], dG @ u64), tol)
+        report(f"c3 shared dW_gate_up[{I + j}]", rel_l2(layer.grads["s_gate_up"][0][I + j], (dh * G * sg) @ u64), tol)
+    # du of sampled tokens: residual + every routed / shared row's input gradient + the router's share
+    toks = [t for t in np.random.default_rng(2).choice(T, 6, replace=False) if t not in bad][:3]
+    cent = np64(inp["centroids"])
+    for t in toks:
+        acc = dO[t].copy()
+        dgate = np.zeros((1, K))
+        for k in range(K):
+            e = int(r["idx"][t, k])
+            wg, wd = _w64(inp, "w_gate_up", e), _w64(inp, "w_down", e)
+            y = oracle.swiglu_ffn(u64[t:t + 1], wg, wd)
+            dgate[0, k] = float(dO[t] @ y[0])
+            da, _, _ = oracle.ffn_backward(u64[t:t + 1], wg, wd, r["gate"][t, k] * dO[t:t + 1])
+            acc += da[0]
+        da, _, _ = oracle.ffn_backward(u64[t:t + 1], _w64(inp, "s_gate_up", 0), _w64(inp, "s_down", 0), dO[t:t + 1])
+        acc += da[0]
+        ds = oracle.gate_backward(r["s"][t:t + 1], r["idx"][t:t + 1], dgate)[0]
+        s_sel = r["s"][t, r["idx"][t]]
+        acc += (ds * s_sel * (1.0 - s_sel)) @ cent[r["idx"][t]]
+        report(f"c3 d_gate token {t}", rel_l2(layer.d_gate[t], dgate[0]), tol)
+        report(f"c3 du token {t}", rel_l2(du[t], acc), tol)
+        report(f"c3 du - d_out token {t}", rel_l2(np64(du[t]) - dO[t], acc - dO[t]), tol)
