@@ -13,6 +13,11 @@ expert, I=2048) in bf16; ``--config c4`` runs the same shape with fp8 GEMMs.
 Prints one JSON line with the throughput, the roofline of the dominant kernel
 (measured with HIP events on the launch stream), per-call times and the CPU
 oracle timed on a bounded token sample.
+
+``--backward`` (bf16 workloads) times one training step of the layer instead:
+the forward with the SwiGLU-input cache, the backward to du, the centroid and
+the expert-weight gradients (moe_combine_backward, moe_ffn_backward,
+moe_route_backward, moe_input_grad) and the bias update; no optimizer.
 """
 from __future__ import annotations
 
@@ -32,6 +37,9 @@ MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "mxfp4": 5.0e15, "f32": 157.3e12}
 WEIGHT_BYTES = {"bf16": 2.0, "f32": 4.0, "fp8": 1.0 + 4.0 / 16384, "mxfp4": 0.5 + 1.0 / 32}
 METRIC = "MoE-layer fwd tokens/s at V3 shape + % of MFMA peak (bf16, fp8)"
 CALLS = ["route", "permute", "ffn_gate_up", "ffn_down", "combine", "bias_update"]
+CALLS_TRAIN = ["route", "permute", "ffn_gate_up", "ffn_down", "combine", "combine_bwd", "ffn_bwd", "route_bwd",
+               "input_grad", "bias_update"]
+METRIC_TRAIN = "MoE-layer fwd+bwd tokens/s (bf16; gradients of u, centroids and expert weights)"
 
 
 def parse():
@@ -46,6 +54,8 @@ def parse():
                     help="fp8 workloads: MXFP4 expert weights (E2M1 with E8M0 1x32 scales) instead of E4M3 blocks")
     ap.add_argument("--pow2-act-scales", action="store_true",
                     help="fp8: power-of-two scales on the up-projection input")
+    ap.add_argument("--backward", action="store_true",
+                    help="bf16 workloads: time the training step (forward + backward + bias update)")
     ap.add_argument("--cpu-sample", type=int, default=32, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (HBM counter calibration)")
@@ -124,12 +134,133 @@ def cpu_baseline(cfg, inp, layer, n_tok):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def cpu_baseline_backward(cfg, inp, d_out, n_tok):
+    """The oracle's backward steps (route, per-expert FFN backward, gate and centroid gradients) on the first n_tok
+    tokens of the same batch (host cores); the expert-weight gradients of the touched experts only."""
+    import numpy as np
+    import oracle
+
+    u = inp["u"][:n_tok].cpu()
+    cent, bias = inp["centroids"].cpu(), inp["bias"].cpu()
+    r0 = oracle.route(u, cent, bias, cfg.n_groups, cfg.topk_groups, cfg.group_topn, cfg.topk)
+    need = sorted(set(int(e) for e in r0["idx"].ravel()))
+    wg = {e: inp["w_gate_up"][e].cpu() for e in need}
+    wd = {e: inp["w_down"][e].cpu() for e in need}
+    sg = [inp["s_gate_up"][s].cpu() for s in range(cfg.n_shared)]
+    sd = [inp["s_down"][s].cpu() for s in range(cfg.n_shared)]
+    dO = d_out[:n_tok].cpu().double().numpy()
+    t0 = time.perf_counter()
+    r = oracle.route(u, cent, bias, cfg.n_groups, cfg.topk_groups, cfg.group_topn, cfg.topk)
+    off, perm, _ = oracle.permute(r["idx"], cfg.n_routed)
+    u64 = u.double().numpy()
+    du = dO.copy()
+    d_gate = np.zeros((n_tok, cfg.topk))
+    for e in need:
+        toks = perm[off[e]:off[e + 1]]
+        slot = np.array([int(np.flatnonzero(r["idx"][t] == e)[0]) for t in toks])
+        d_gate[toks, slot] = (dO[toks] * oracle.swiglu_ffn(u64[toks], wg[e], wd[e])).sum(axis=1)
+        da, _, _ = oracle.ffn_backward(u64[toks], wg[e], wd[e], r["gate"][toks, slot][:, None] * dO[toks])
+        np.add.at(du, toks, da)
+    for s in range(cfg.n_shared):
+        du += oracle.ffn_backward(u64, sg[s], sd[s], dO)[0]
+    ds = oracle.gate_backward(r["s"], r["idx"], d_gate)
+    s_sel = np.take_along_axis(r["s"], r["idx"], axis=1)
+    dz = ds * s_sel * (1.0 - s_sel)
+    c64 = cent.double().numpy()
+    d_cent = np.zeros_like(c64)
+    for k in range(cfg.topk):
+        du += dz[:, k:k + 1] * c64[r["idx"][:, k]]
+        np.add.at(d_cent, r["idx"][:, k], dz[:, k:k + 1] * u64)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        blas = 1
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"first {n_tok} tokens of the same {cfg.name} batch: routing, the forward of the "
+                      f"{len(need)} touched routed experts (for the gate gradients), their and the {cfg.n_shared} "
+                      f"shared experts' FFN backward, gate / centroid / input gradients in fp64 (NumPy); "
+                      f"{dt:.1f} s wall", "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main_backward(args, cfg):
+    import numpy as np
+    import torch
+    from moe_inputs import generate, generate_output_grad
+    from mixture_experts_layer_gate_amd import MoELayer
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    inp = generate(cfg, dev)
+    d_out = generate_output_grad(cfg, dev)
+    layer = MoELayer(cfg, inp, dev, train=True)
+    u = inp["u"]
+    stream = torch.cuda.current_stream()
+    parts = [lambda: layer.route(u), lambda: layer.permute(u), lambda: layer.ffn_gate_up_train(u),
+             layer.ffn_down_train, lambda: layer.combine(u), lambda: layer.combine_backward(d_out),
+             layer.ffn_backward, layer.route_backward, lambda: layer.input_grad(d_out), layer.bias_update]
+
+    def step(ev=None):
+        for j, f in enumerate(parts):
+            if ev is not None:
+                ev[j].record(stream)
+            f()
+        if ev is not None:
+            ev[len(parts)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    per_call = {c: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
+                for j, c in enumerate(CALLS_TRAIN)}
+    T, d, I, K, N, Ns = cfg.T, cfg.d, cfg.inter, cfg.topk, cfg.n_routed, cfg.n_shared
+    rows = T * (K + Ns)
+    # dominant call: moe_ffn_backward, four GEMMs over every row (dh, da, dW_down, dW_gate_up)
+    bwd_flops = 2.0 * rows * d * I * (1 + 2 + 1 + 2)
+    bwd_s = per_call["ffn_bwd"] / 1e3
+    roof = {"bound": "mfma", "achieved": bwd_flops / bwd_s / 1e12, "peak": MFMA_PEAK["bf16"] / 1e12,
+            "unit": "TFLOP/s", "frac": bwd_flops / bwd_s / MFMA_PEAK["bf16"], "traffic": None,
+            "kernel": "moe_ffn_backward (dh, SwiGLU backward, da, dW_down, dW_gate_up)"}
+    fwd_flops = cfg.ffn_flops()
+    calls = {c: {"ms": round(per_call[c], 4)} for c in CALLS_TRAIN}
+    res = {
+        "metric": METRIC_TRAIN, "value": T / (ms_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) tokens and output gradient, random-init N(0,0.02^2) weights",
+        "config": {"workload": f"{cfg.name}: {cfg.description}, forward + backward", "T": T, "d": d,
+                   "n_routed": N, "topk": K, "n_shared": Ns, "inter": I, "gemm": "bf16"},
+        "roofline": roof,
+        "train_step": {"TFLOP/s": (fwd_flops + bwd_flops) / (ms_step / 1e3) / 1e12,
+                       "roofline_ms": (fwd_flops + bwd_flops + cfg.router_flops()) / MFMA_PEAK["bf16"] * 1e3},
+        "calls": calls,
+    }
+    res["train_step"]["frac_of_roofline"] = res["train_step"]["roofline_ms"] / ms_step
+    res["cpu_baseline"] = cpu_baseline_backward(cfg, inp, d_out, args.cpu_sample) if args.cpu_sample > 0 else None
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer runs on a single MI355X with no collectives; "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.backward:
+        from moe_inputs import get_config as _gc
+        cfg = _gc(args.config)
+        if cfg.gemm != "bf16" or args.mxfp4 or args.pow2_act_scales or args.batch_invariant:
+            print("bench.py: --backward runs the bf16 workloads (c2, c3) only", file=sys.stderr)
+            sys.exit(2)
+        main_backward(args, cfg)
+        return
 
     import numpy as np
     import torch

@@ -494,6 +494,8 @@ moe_status moe_ffn_backward(const moe_shape* shape, moe_dtype w, int32_t n_exper
   const int d = shape->d, I = shape->inter;
   SUPPORT(static_cast<long long>(n_rows) * 2 * I * 2 < (1LL << 32) && static_cast<long long>(n_rows) * d * 2 < (1LL << 32),
           "ffn_backward: n_rows * 2I and n_rows * d must stay below 2^31 elements");
+  SUPPORT(mode != MOE_ROWS_GATHER || static_cast<long long>(a_rows) * d * 2 < (1LL << 32) - 256,
+          "ffn_backward: a gathered a must stay below 4 GiB");
   const size_t need = moe_ffn_backward_workspace_bytes(shape, n_rows);
   if (!workspace || ws_bytes < need)
     return fail(MOE_E_WORKSPACE, "ffn_backward: workspace of %zu bytes < %zu needed", ws_bytes, need);

@@ -6,102 +6,253 @@
 // dW_gate_up = [dG | dU]^T a). bf16 operands, fp32 MFMA accumulation, fp32
 // output; experts without rows get zeros.
 //
-// A workgroup per (expert, 128 x 128 output tile), four waves in a 2 x 2 grid
-// of 64 x 64 (2 x 2 MFMA tiles of 32 x 32). The rows advance in chunks of 32:
-// each thread loads 16 consecutive columns of one row of X and of Y and writes
-// them transposed into LDS ([column][row], 32 rows + 8 pad per column, so a
-// lane's 8 consecutive rows are one 16-byte read and 16 lanes hit 16
-// different bank groups); two K16 MFMA steps per chunk. Rows past the expert's
-// last are zero.
+// Both operands hold the contraction index (the row) as their slow axis, the
+// transpose of what an MFMA operand wants (8 consecutive K values per lane).
+// The tiles are staged in LDS as they lie in HBM (row-major, 16-byte loads and
+// stores) and the transpose happens on the way out of LDS: gfx950's
+// ds_read_b64_tr_b16 gives lane i of each 16-lane group element i of the four
+// 4-element pieces that lanes 4j .. 4j + 3 point at, so pointing the 16 lanes
+// at 4 rows x 16 columns hands every lane 4 consecutive rows of one column.
+// Two such reads make one 32x32x16 operand.
+//
+// A workgroup per (expert, 256 x 128 output tile), four waves in a 2 x 2 grid
+// of 128 x 64 (4 x 2 MFMA tiles of 32 x 32), two workgroups per CU. Rows
+// advance in chunks of 32 through a ring of three 24 KB LDS stages filled by
+// direct-to-LDS buffer loads (no VGPR staging), two chunks ahead of the one
+// being multiplied. LDS rows are XOR-swizzled in 16-byte slots (slot = column
+// chunk ^ 4 (row % 4)) so the 4 rows of one transpose read fall in 4 different
+// bank quadrants; a DMA load writes 64 consecutive slots, so each lane fetches
+// the global chunk that belongs at its slot. Rows past the expert's last,
+// columns past M and unmapped source rows fall outside the loads' buffer range
+// and arrive as zeros. Blocks run expert-major, so an expert's rows stay in the
+// caches while all of its tiles are computed; the fp32 tile is written with
+// non-temporal stores (it is not read again by this pass).
+#include <mutex>
+
 #include "common.h"
+#include "gemm_pipe.h"
 #include "launch.h"
 #include "sched.h"
 
 namespace moe {
 
-constexpr int kWgTile = 128, kWgK = 32, kWgLd = kWgK + 8;
+namespace {
 
-__global__ __launch_bounds__(256) void wgrad_kernel(int M, int N, int E, int n_rows, int a_rows,
-                                                    const int32_t* __restrict__ off, moe_row_mode mode,
-                                                    const int32_t* __restrict__ row_src,
-                                                    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
-                                                    float* __restrict__ C) {
-  __shared__ __align__(16) uint16_t xs[kWgTile][kWgLd];
-  __shared__ __align__(16) uint16_t ys[kWgTile][kWgLd];
-  const int mt = M / kWgTile, nt = N / kWgTile;
+constexpr int kWgBM = 256, kWgBN = 128, kWgBK = 32;
+constexpr int kWgXBytes = kWgBK * kWgBM * 2;              // 16 KB
+constexpr int kWgStage = kWgXBytes + kWgBK * kWgBN * 2;   // + 8 KB
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte address of this lane's first transpose read of the 32 x 16 (column x
+// K) operand at column col0 of a row-major LDS tile of pitch `pitch` bytes at
+// LDS address `tile` (rows k0 = 0): lane l gets column col0 + l % 32, rows
+// 8 (l / 32) .. + 3 from this read and + 4 .. + 7 from the one 4 rows further.
+__device__ __forceinline__ uint32_t tr_addr(uint32_t tile, int pitch, int col0) {
+  const int l = threadIdx.x & 63, g = l >> 4, p = l & 15, j = p >> 2, q = p & 3;
+  const int col = col0 + 16 * (g & 1) + 4 * q;               // start of this lane's 4-column piece
+  const int k = 8 * (g >> 1) + j;                             // k % 4 == j
+  return tile + k * pitch + (((col >> 3) ^ (4 * j)) << 4) + ((col & 7) << 1);
+}
+
+// The twelve transpose reads of one K16 step (rows ks .. ks + 15 of the stage):
+// four X operands at xa[0..3], two Y operands at ya[0..1]. The reads are waited
+// for inside the same statement, so every output is complete when it returns.
+template <int KS>
+__device__ __forceinline__ void tr_step(i32x2 (&r)[12], const uint32_t (&xa)[4], const uint32_t (&ya)[2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %12 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %1, %12 offset:%19\n\t"
+      "ds_read_b64_tr_b16 %2, %13 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %3, %13 offset:%19\n\t"
+      "ds_read_b64_tr_b16 %4, %14 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %5, %14 offset:%19\n\t"
+      "ds_read_b64_tr_b16 %6, %15 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%19\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %10, %17 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:%21\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+      : "v"(xa[0]), "v"(xa[1]), "v"(xa[2]), "v"(xa[3]), "v"(ya[0]), "v"(ya[1]), "n"(KS * kWgBM * 2),
+        "n"((KS + 4) * kWgBM * 2), "n"(KS * kWgBN * 2), "n"((KS + 4) * kWgBN * 2));
+}
+
+__device__ __forceinline__ bf16x8 tr_pair(const i32x2& lo, const i32x2& hi) {
+  return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6,
+                                 7);
+}
+
+}  // namespace
+
+namespace {
+
+constexpr int kWgNS = 3;                                  // ring stages
+constexpr uint32_t kWgOut = 0xFFFFFFF0u;                  // a voffset past every buffer range: loads zero
+constexpr uint64_t kWgMaxRange = 0xFFFFFF00ull;
+
+__device__ __forceinline__ uint32_t range_bytes(long long bytes) {
+  return static_cast<uint32_t>(bytes <= 0 ? 0 : (bytes > static_cast<long long>(kWgMaxRange) ? kWgMaxRange : bytes));
+}
+
+template <int N>
+__device__ __forceinline__ void wg_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+}  // namespace
+
+// GATHER: the Y rows come through row_src (read with scalar loads when the
+// chunk's DMA is issued: four rows per wave and load, picked per lane), so the
+// vector-memory counter only ever counts the DMA loads; otherwise Y row r is r
+// (direct) or r - lo (segment).
+template <bool GATHER>
+__global__ __launch_bounds__(256, 2) void wgrad_kernel(int M, int N, int E, int n_rows, int a_rows,
+                                                       const int32_t* __restrict__ off, moe_row_mode mode,
+                                                       const int32_t* __restrict__ row_src,
+                                                       const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
+                                                       float* __restrict__ C) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int mt = cdiv(M, kWgBM), nt = N / kWgBN;
   const long long b = blockIdx.x;
   const int e = static_cast<int>(b / (static_cast<long long>(mt) * nt));
   const int rem = static_cast<int>(b % (static_cast<long long>(mt) * nt));
-  const int m0 = (rem / nt) * kWgTile, n0 = (rem % nt) * kWgTile;
+  const int m0 = (rem / nt) * kWgBM, n0 = (rem % nt) * kWgBN;
   if (e >= E) return;
   const int lo = clampi(off[e], 0, n_rows), hi = clampi(off[e + 1], lo, n_rows);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wm = w >> 1, wn = w & 1;
-  const int kk = tid >> 3, cs = (tid & 7) * 16;       // the row and 16 columns this thread loads
-  f32x16 acc[2][2];
+  const int tid = threadIdx.x, l = tid & 63, wm = (tid >> 6) >> 1, wn = (tid >> 6) & 1;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool active = m0 + wm * 128 < M;                      // M % 256 == 128: the last tile's second half is empty
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
-  for (int r0 = lo; r0 < hi; r0 += kWgK) {
-    const int r = r0 + kk;
-    uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0, y0 = x0, y1 = x0;
-    if (r < hi) {
-      const uint4* xp = reinterpret_cast<const uint4*>(X + static_cast<size_t>(r) * M + m0 + cs);
-      x0 = xp[0];
-      x1 = xp[1];
-      const int sr = source_row(mode, row_src, r, lo, a_rows);
-      if (sr >= 0) {
-        const uint4* yp = reinterpret_cast<const uint4*>(Y + static_cast<size_t>(sr) * N + n0 + cs);
-        y0 = yp[0];
-        y1 = yp[1];
+  const int nch = cdiv(hi - lo, kWgBK);
+  const uint32_t lds_addr =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)lds));
+  uint32_t xo[4], yo[2];                                      // transpose-read offsets within a stage
+#pragma unroll
+  for (int a = 0; a < 4; ++a) xo[a] = tr_addr(0, kWgBM * 2, wm * 128 + a * 32);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) yo[c] = tr_addr(kWgXBytes, kWgBN * 2, wn * 64 + c * 32);
+  auto mma_step = [&](const i32x2 (&r)[12], f32x16 (&ac)[4][2]) {
+    bf16x8 fb[2] = {tr_pair(r[8], r[9]), tr_pair(r[10], r[11])};
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const bf16x8 fa = tr_pair(r[2 * a], r[2 * a + 1]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) ac[a][c] = mfma_32x32x16_bf16(fa, fb[c], ac[a][c]);
+    }
+  };
+
+  if (nch > 0) {
+    // DMA load q of this wave fills LDS slots (q * 4 + w) * 64 + lane of the X (or Y) part of a stage
+    uint32_t vx[4], vy[2];
+    int yrow[2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 2 * (q * 4 + w) + (l >> 5), c = (l & 31) ^ (4 * (row & 3));
+      vx[q] = static_cast<uint32_t>(row * M * 2 + c * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      yrow[q] = 4 * (q * 4 + w) + (l >> 4);
+      const int c = (l & 15) ^ (4 * (yrow[q] & 3));
+      vy[q] = static_cast<uint32_t>(GATHER ? c * 16 : yrow[q] * N * 2 + c * 16);
+    }
+    auto issue = [&](int ch) {
+      const int r0 = lo + kWgBK * ch;
+      uint8_t* st = lds + (ch % kWgNS) * kWgStage;
+      const __amdgpu_buffer_rsrc_t rx =
+          pipe_rsrc(X + static_cast<size_t>(r0) * M + m0, range_bytes((static_cast<long long>(hi - r0) * M - m0) * 2));
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(st + (q * 4 + w) * 1024), 16, vx[q], 0, 0, 0);
+      if (GATHER) {
+        const __amdgpu_buffer_rsrc_t ry =
+            pipe_rsrc(Y + n0, range_bytes((static_cast<long long>(a_rows) * N - n0) * 2));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int base = r0 + 4 * (q * 4 + w);                 // wave-uniform: scalar loads, clamped to the rows
+          const int s0 = row_src[min(base, hi - 1)], s1 = row_src[min(base + 1, hi - 1)];
+          const int s2 = row_src[min(base + 2, hi - 1)], s3 = row_src[min(base + 3, hi - 1)];
+          const int sel = l >> 4;
+          const int sr = sel == 0 ? s0 : (sel == 1 ? s1 : (sel == 2 ? s2 : s3));
+          const bool ok = r0 + yrow[q] < hi && sr >= 0 && sr < a_rows;
+          const uint32_t vo = ok ? static_cast<uint32_t>(sr) * static_cast<uint32_t>(N * 2) + vy[q] : kWgOut;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void_t*)(st + kWgXBytes + (q * 4 + w) * 1024), 16, vo, 0,
+                                                   0, 0);
+        }
+      } else {
+        const int s0 = mode == MOE_ROWS_SEGMENT ? r0 - lo : r0;
+        const int yrows = min(hi - r0, a_rows - s0);
+        const __amdgpu_buffer_rsrc_t ry = pipe_rsrc(
+            Y + static_cast<size_t>(s0) * N + n0, yrows > 0 ? range_bytes((static_cast<long long>(yrows) * N - n0) * 2)
+                                                            : 0u);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void_t*)(st + kWgXBytes + (q * 4 + w) * 1024), 16, vy[q],
+                                                   0, 0, 0);
+      }
+    };
+    // prologue: chunks 0 and 1 in flight
+    issue(0);
+    if (nch > 1) issue(1);
+    // iteration ch: wait for chunk ch (only chunk ch + 1's six loads may still be in flight), issue the DMA of
+    // chunk ch + 2 into the stage chunk ch - 1 used, multiply chunk ch
+    for (int ch = 0; ch < nch; ++ch) {
+      if (ch + 1 < nch) wg_wait_barrier<6>();
+      else wg_wait_barrier<0>();
+      if (ch + 2 < nch) issue(ch + 2);
+      if (active) {
+        const uint32_t st = lds_addr + (ch % kWgNS) * kWgStage;
+        const uint32_t xa[4] = {st + xo[0], st + xo[1], st + xo[2], st + xo[3]};
+        const uint32_t ya[2] = {st + yo[0], st + yo[1]};
+        i32x2 r[12];
+        tr_step<0>(r, xa, ya);
+        mma_step(r, acc);
+        tr_step<16>(r, xa, ya);
+        mma_step(r, acc);
       }
     }
-    __syncthreads();                                   // the previous chunk's fragments have been read
-    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    const uint32_t yw[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xs[cs + 2 * i][kk] = static_cast<uint16_t>(xw[i] & 0xFFFFu);
-      xs[cs + 2 * i + 1][kk] = static_cast<uint16_t>(xw[i] >> 16);
-      ys[cs + 2 * i][kk] = static_cast<uint16_t>(yw[i] & 0xFFFFu);
-      ys[cs + 2 * i + 1][kk] = static_cast<uint16_t>(yw[i] >> 16);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int k = ks * 16 + 8 * (l >> 5);
-      bf16x8 fa[2], fb[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) fa[a] = *reinterpret_cast<const bf16x8*>(&xs[wm * 64 + a * 32 + (l & 31)][k]);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) fb[c] = *reinterpret_cast<const bf16x8*>(&ys[wn * 64 + c * 32 + (l & 31)][k]);
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) acc[a][c] = mfma_32x32x16_bf16(fa[a], fb[c], acc[a][c]);
-    }
   }
+  if (!active) return;
   float* Ce = C + static_cast<size_t>(e) * M * N;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int n = n0 + wn * 64 + c * 32 + (l & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-        Ce[static_cast<size_t>(m) * N + n] = acc[a][c][v];
+        const int m = m0 + wm * 128 + a * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+        __builtin_nontemporal_store(acc[a][c][v], Ce + static_cast<size_t>(m) * N + n);
       }
     }
 }
 
 hipError_t launch_wgrad(int M, int N, int E, int n_rows, int a_rows, const int32_t* off, moe_row_mode mode,
                         const int32_t* row_src, const void* X, const void* Y, float* C, hipStream_t st) {
-  const long long blocks = static_cast<long long>(E) * (M / kWgTile) * (N / kWgTile);
-  hipLaunchKernelGGL(wgrad_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, M, N, E, n_rows, a_rows, off,
-                     mode, row_src, static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Y), C);
+  static std::once_flag once;
+  std::call_once(once, [] {
+    for (const void* k : {reinterpret_cast<const void*>(wgrad_kernel<true>),
+                          reinterpret_cast<const void*>(wgrad_kernel<false>)})
+      (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kWgNS * kWgStage);
+    (void)hipGetLastError();
+  });
+  const long long blocks = static_cast<long long>(E) * cdiv(M, kWgBM) * (N / kWgBN);
+  const size_t lds = static_cast<size_t>(kWgNS) * kWgStage;
+  if (mode == MOE_ROWS_GATHER)
+    hipLaunchKernelGGL(wgrad_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, M, N, E, n_rows,
+                       a_rows, off, mode, row_src, static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Y), C);
+  else
+    hipLaunchKernelGGL(wgrad_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, M, N, E, n_rows,
+                       a_rows, off, mode, row_src, static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Y), C);
   return hipGetLastError();
 }
 

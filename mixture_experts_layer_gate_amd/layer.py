@@ -322,33 +322,54 @@ class MoELayer:
         """forward() that also caches the SwiGLU inputs of every row for backward() (train=True)."""
         if not self.train:
             raise RuntimeError("forward_train needs MoELayer(train=True)")
-        c = self.cfg
         u = u.contiguous()
-        self.u_saved = u
         self.route(u)
         self.permute(u)
+        self.ffn_gate_up_train(u)
+        self.ffn_down_train()
+        self.combine(u)
+        return self.out
+
+    def ffn_gate_up_train(self, u):
+        """Gate/up projection of every row that also writes the SwiGLU inputs [G | U] (routed + shared)."""
+        c = self.cfg
+        self.u_saved = u
         E, n_rows = c.n_routed + c.n_shared, c.T * (c.topk + c.n_shared)
         B.moe_ffn_gate_up_cache(self.shape, self.gemm, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all,
                                 u, c.T, self.w["all_gate_up"], self.h_all, self.gu_cache, self.ws)
+
+    def ffn_down_train(self):
+        c = self.cfg
+        E, n_rows = c.n_routed + c.n_shared, c.T * (c.topk + c.n_shared)
         B.moe_ffn_down(self.shape, self.gemm, E, n_rows, self.offsets_all, self.h_all, None, self.w["all_down"],
                        None, self.y_all, self.ws)
-        self.combine(u)
-        return self.out
+
+    def combine_backward(self, d_out):
+        B.moe_combine_backward(self.shape, d_out, self.y_routed, self.row_of, self.topk_gate, self.dy_all, self.d_gate)
+
+    def ffn_backward(self):
+        c = self.cfg
+        E, n_rows = c.n_routed + c.n_shared, c.T * (c.topk + c.n_shared)
+        B.moe_ffn_backward(self.shape, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all, self.u_saved,
+                           c.T, self.gu_cache, self.w["all_gate_up_t"], self.w["all_down_t"], self.dy_all,
+                           self.da_all, self.grads["all_gate_up"], self.grads["all_down"], self.ws_bwd)
+
+    def route_backward(self):
+        B.moe_route_backward(self.shape, self.u_saved, self.centroids, self.scores, self.topk_idx, self.d_gate,
+                             self.expert_offsets, self.perm_token, self.row_of, self.du_router,
+                             self.grads["centroids"], self.ws_bwd)
+
+    def input_grad(self, d_out):
+        B.moe_input_grad(self.shape, d_out, self.du_router, self.da_all, self.row_of, self.du)
 
     def backward(self, d_out: torch.Tensor) -> torch.Tensor:
         """Gradients of the last forward_train for the output gradient d_out [T, d]: returns du [T, d] fp32 and
         fills self.grads (centroids, expert gate/up and down weights, fp32)."""
-        c = self.cfg
         d_out = d_out.contiguous()
-        E, n_rows = c.n_routed + c.n_shared, c.T * (c.topk + c.n_shared)
-        B.moe_combine_backward(self.shape, d_out, self.y_routed, self.row_of, self.topk_gate, self.dy_all, self.d_gate)
-        B.moe_ffn_backward(self.shape, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all, self.u_saved,
-                           c.T, self.gu_cache, self.w["all_gate_up_t"], self.w["all_down_t"], self.dy_all,
-                           self.da_all, self.grads["all_gate_up"], self.grads["all_down"], self.ws_bwd)
-        B.moe_route_backward(self.shape, self.u_saved, self.centroids, self.scores, self.topk_idx, self.d_gate,
-                             self.expert_offsets, self.perm_token, self.row_of, self.du_router,
-                             self.grads["centroids"], self.ws_bwd)
-        B.moe_input_grad(self.shape, d_out, self.du_router, self.da_all, self.row_of, self.du)
+        self.combine_backward(d_out)
+        self.ffn_backward()
+        self.route_backward()
+        self.input_grad(d_out)
         return self.du
 
     def outputs(self) -> LayerOutputs:
