@@ -134,6 +134,17 @@ def cpu_baseline(cfg, inp, layer, n_tok):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def calib_copy(mib, dev):
+    """One plain device copy of mib MiB (the reference reading for the HBM byte counters)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def cpu_baseline_backward(cfg, inp, d_out, n_tok):
     """The oracle's backward steps (route, per-expert FFN backward, gate and centroid gradients) on the first n_tok
     tokens of the same batch (host cores); the expert-weight gradients of the touched experts only."""
@@ -197,6 +208,8 @@ def main_backward(args, cfg):
     layer = MoELayer(cfg, inp, dev, train=True)
     u = inp["u"]
     stream = torch.cuda.current_stream()
+    if args.calib_copy_mib > 0:
+        calib_copy(args.calib_copy_mib, dev)
     parts = [lambda: layer.route(u), lambda: layer.permute(u), lambda: layer.ffn_gate_up_train(u),
              layer.ffn_down_train, lambda: layer.combine(u), lambda: layer.combine_backward(d_out),
              layer.ffn_backward, layer.route_backward, lambda: layer.input_grad(d_out), layer.bias_update]
@@ -296,12 +309,7 @@ def main():
         rec(6)
 
     if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calib_copy(args.calib_copy_mib, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
