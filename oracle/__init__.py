@@ -25,7 +25,9 @@ the full layer have no worked example on the pages: beyond those pins they
 are "parity unpinned".
 """
 from .accumulation import keep_bits, limited_precision_gemm  # noqa: F401
-from .backward import ffn_backward, gate_backward, layer_backward  # noqa: F401
+from .backward import (  # noqa: F401
+    ffn_backward, ffn_backward_fp8, gate_backward, layer_backward, requant_cols_pow2,
+)
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode  # noqa: F401
 from .mxfp4 import (  # noqa: F401
     e2m1_decode, e2m1_encode, quantize_mxfp4, dequantize_mxfp4, pack_e2m1, unpack_e2m1, mxfp4_to_e4m3_blocks,

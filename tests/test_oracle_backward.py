@@ -107,3 +107,69 @@ def test_gate_backward_invariants():
     assert np.allclose((np.take_along_axis(s, idx, axis=1) * ds).sum(axis=1), 0, atol=1e-12)
     assert np.all(oracle.gate_backward(s, idx[:, :1], dg[:, :1]) == 0)
     assert np.allclose(oracle.gate_backward(s, idx, np.ones((20, 4)) * 3.0), 0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ FP8 recipe
+
+def test_requant_cols_pow2():
+    """The 128x1 re-tiling: per (128-row block of a segment, column) one power-of-two scale with every value an
+    E4M3 value times it and the block's largest magnitude in [224, 448] scale units; 128-row-aligned segments
+    agree with the 1x128 quantiser on the transpose; blocks restart at each segment; idempotent; error within
+    half an E4M3 step."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((556, 256)) * np.exp(rng.standard_normal((1, 256)))
+    off = [0, 300, 300, 556]                                  # an empty segment, blocks of 128, 128, 44 and 128, 128
+    r = oracle.requant_cols_pow2(x, off)
+    e4m3_values = np.unique(np.abs(oracle.e4m3_decode(np.arange(256, dtype=np.uint8))))
+    e4m3_values = e4m3_values[np.isfinite(e4m3_values)]
+    for b0, b1 in [(0, 128), (128, 256), (256, 300), (300, 428), (428, 556)]:
+        blk, xb = r[b0:b1], x[b0:b1]
+        for c in (0, 77, 255):
+            s = 2.0 ** np.ceil(np.log2(np.abs(xb[:, c]).max().astype(np.float32) / np.float32(448.0)))
+            assert np.isin(np.abs(blk[:, c]) / s, e4m3_values).all()
+            assert 224 <= np.abs(blk[:, c]).max() / s <= 448
+            step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(xb[:, c]) / s, 2.0 ** -6))) - 3) * s
+            assert np.all(np.abs(blk[:, c] - xb[:, c]) <= 0.5 * step + 1e-300)
+    aligned = oracle.requant_cols_pow2(x[:256], [0, 256])
+    c_, s_ = oracle.quantize_tiles(x[:256].T, pow2=True)
+    assert np.array_equal(aligned, oracle.dequantize_tiles(c_, s_).T)
+    assert np.array_equal(oracle.requant_cols_pow2(r, off), r)
+    # the block [256, 300) ends its segment: the rows after it (next segment) do not enter its scale
+    y = x.copy()
+    y[300:] *= 1e6
+    assert np.array_equal(oracle.requant_cols_pow2(y, off)[:300], r[:300])
+
+
+def _expert(seed, n=200, d=256, I=128):
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((n, d))
+    wgu = oracle.quantize_blocks(rng.standard_normal((2 * I, d)) * 0.05)
+    wd = oracle.quantize_blocks(rng.standard_normal((d, I)) * 0.05)
+    dy = rng.standard_normal((n, d))
+    return a, wgu, wd, dy
+
+
+def test_ffn_backward_fp8_reduces_to_exact(monkeypatch):
+    """With every activation quantisation replaced by the identity, the FP8 backward is the exact backward of
+    the same (block-quantised) weights: each GEMM takes the right operands."""
+    import oracle.backward as ob
+    a, wgu, wd, dy = _expert(0)
+    wgu64, wd64 = oracle.dequantize_blocks(*wgu), oracle.dequantize_blocks(*wd)
+    monkeypatch.setattr(ob, "_q1x128", lambda x: np.asarray(x, np.float64))
+    monkeypatch.setattr(ob, "requant_cols_pow2", lambda x, off: np.asarray(x, np.float64))
+    monkeypatch.setattr(ob, "quantize_tiles", lambda x, pow2=False: (np.asarray(x, np.float64), None))
+    monkeypatch.setattr(ob, "dequantize_tiles", lambda c, s: c)
+    got = ob.ffn_backward_fp8(a, *wgu, *wd, dy)
+    ref = oracle.ffn_backward(a, wgu64, wd64, dy)
+    for g, r_ in zip(got, ref):
+        np.testing.assert_allclose(g, r_, rtol=1e-12, atol=1e-12)
+
+
+def test_ffn_backward_fp8_error_size():
+    """The quantised backward stays within E4M3-sized relative error of the exact one (and is not exact)."""
+    a, wgu, wd, dy = _expert(1)
+    got = oracle.ffn_backward_fp8(a, *wgu, *wd, dy)
+    ref = oracle.ffn_backward(a, oracle.dequantize_blocks(*wgu), oracle.dequantize_blocks(*wd), dy)
+    for name, g, r_ in zip(("da", "dW_gate_up", "dW_down"), got, ref):
+        rel = np.linalg.norm(g - r_) / np.linalg.norm(r_)
+        assert 1e-3 < rel < 0.08, (name, rel)
