@@ -299,13 +299,14 @@ moe_status moe_ffn_gate_up_cache(const moe_shape* shape, moe_dtype w, int32_t n_
 
 /*
  * moe_combine_backward -- from d_out [T, d] (the gradient of the layer output):
- * dy [T*K + N_s*T, d] bf16, dy[row_of(t,k)] = gate[t,k] * d_out[t] for the routed
- * rows and dy[T*K + s*T + t] = d_out[t] for shared expert s; d_gate [T, K] fp32,
- * d_gate[t,k] = d_out[t] . y_routed[row_of(t,k)] (fp32 sums). io = MOE_BF16.
+ * dy [T*K + N_s*T, d] (dy_dtype MOE_BF16, the input of both FFN backward calls, or MOE_F32),
+ * dy[row_of(t,k)] = gate[t,k] * d_out[t] for the routed rows and
+ * dy[T*K + s*T + t] = d_out[t] for shared expert s; d_gate [T, K] fp32,
+ * d_gate[t,k] = d_out[t] . y_routed[row_of(t,k)] (fp32 sums). io (d_out, y_routed) = MOE_BF16.
  */
 moe_status moe_combine_backward(const moe_shape* shape, moe_dtype io, const void* d_out, const void* y_routed,
-                                const int32_t* row_of, const float* topk_gate, void* dy, float* d_gate,
-                                void* stream);
+                                const int32_t* row_of, const float* topk_gate, moe_dtype dy_dtype, void* dy,
+                                float* d_gate, void* stream);
 
 /*
  * moe_route_backward -- through the gates (eq. (13)-(14)) and the sigmoid
@@ -357,6 +358,59 @@ moe_status moe_ffn_backward(const moe_shape* shape, moe_dtype w, int32_t n_exper
  */
 moe_status moe_input_grad(const moe_shape* shape, const void* d_out, const float* du_router, const void* da,
                           const int32_t* row_of, float* du, void* stream);
+
+/*
+ * ---- FP8 form of the backward (the FP8 framework of "DeepSeek_V3_Report:
+ * Annotation": Fprop, Dgrad and Wgrad of every linear layer in FP8; the SwiGLU
+ * inputs cached as fine-grained FP8 tiles, the SwiGLU output recomputed; the
+ * Wgrad operands re-tiled from 1x128 to 128x1). Pairs with the fp8 forward
+ * (MOE_F8E4M3 weights, moe_permute's E4M3 tokens).
+ *
+ * moe_transpose_bf16 -- W [n_mats][rows][cols] bf16 -> W^T [n_mats][cols][rows]
+ * row-major (rows, cols multiples of 64). Quantising W^T with
+ * moe_quantize_weights (gate_up = 0) gives the transposed 128x128 blocks with the
+ * same scales: the weights of the FP8 input-gradient GEMMs.
+ */
+moe_status moe_transpose_bf16(int32_t n_mats, int32_t rows, int32_t cols, const void* src, void* dst, void* stream);
+
+/*
+ * moe_ffn_gate_up_cache_fp8 -- moe_ffn_gate_up for MOE_F8E4M3 that also writes the
+ * SwiGLU inputs as 1x128 E4M3 tiles: gu_codes [n_rows, 2I] (G in [0, I), U in
+ * [I, 2I)) and gu_scale [n_rows, 2I/128] fp32 (the forward's activation rule:
+ * scale = amax / 448, code = E4M3(x * 448 / amax)). a_codes / a_scale: the 1x128
+ * E4M3 tokens of moe_permute; h_codes / h_scale: the down projection's input.
+ */
+moe_status moe_ffn_gate_up_cache_fp8(const moe_shape* shape, int32_t n_experts, int32_t n_rows,
+                                     const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
+                                     const void* a_codes, const float* a_scale, int32_t a_rows, const void* w_gate_up,
+                                     const void* w_gu_scale, void* h_codes, float* h_scale, void* gu_codes,
+                                     float* gu_scale, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_ffn_backward_fp8 -- the FP8 backward of the grouped SwiGLU FFN (rows,
+ * offsets and row modes as in the forward; dy [n_rows, d] bf16 from
+ * moe_combine_backward):
+ *   Dgrad: dh (fp32) = Q(dy) W_d and da [n_rows, d] bf16 = Q([dG, dU]) W_gate_up on the
+ *          fp8 grouped GEMM, Q = 1x128 E4M3 tiles along K, the weights as
+ *          128x128 blocks of W^T (w_down_t: [n_experts][I rows, 256-row tiles][d],
+ *          w_gate_up_t: [n_experts][d][2I], codes from moe_quantize_weights of
+ *          moe_transpose_bf16's output, with their scales);
+ *   SwiGLU backward from the cached E4M3 [G, U] (gu_codes, gu_scale), h recomputed;
+ *   Wgrad: dw_down [n_experts, d, I] = R(dy)^T R(h), dw_gate_up [n_experts, 2I, d]
+ *          = R([dG, dU])^T R(a) fp32, R = the 128x1 re-tiling: per column and per
+ *          block of 128 consecutive rows of an expert (from its first row) one
+ *          power-of-two scale, the token operand a taken from its 1x128 E4M3
+ *          codes (a_codes, a_scale at the rows' source rows).
+ * workspace: moe_ffn_backward_fp8_workspace_bytes(shape, n_rows, n_experts)
+ * bytes. Needs 2I <= 10240.
+ */
+size_t moe_ffn_backward_fp8_workspace_bytes(const moe_shape* shape, int32_t n_rows, int32_t n_experts);
+moe_status moe_ffn_backward_fp8(const moe_shape* shape, int32_t n_experts, int32_t n_rows,
+                                const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
+                                const void* a_codes, const float* a_scale, int32_t a_rows, const void* gu_codes,
+                                const float* gu_scale, const void* w_gate_up_t, const float* w_gate_up_t_scale,
+                                const void* w_down_t, const float* w_down_t_scale, const void* dy, void* da,
+                                float* dw_gate_up, float* dw_down, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * moe_tile_weights_bf16 -- copies bf16 expert weights into the tiled layout of

@@ -59,12 +59,17 @@ _SIGS = {
     "moe_quantize_weights_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P],
     "moe_tile_weights_bf16": [_I, _I, _I, _I, _P, _P, _P],
     "moe_ffn_gate_up_cache": [_S, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P],
-    "moe_combine_backward": [_S, _I, _P, _P, _P, _P, _P, _P, _P],
+    "moe_combine_backward": [_S, _I, _P, _P, _P, _P, _I, _P, _P, _P],
     "moe_route_backward": [_S, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_transpose_weights_bf16": [_I, _I, _I, _P, _P, _P],
     "moe_ffn_backward_workspace_bytes": [_S, _I],
     "moe_ffn_backward": [_S, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_input_grad": [_S, _P, _P, _P, _P, _P, _P],
+    "moe_transpose_bf16": [_I, _I, _I, _P, _P, _P],
+    "moe_ffn_gate_up_cache_fp8": [_S, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_ffn_backward_fp8_workspace_bytes": [_S, _I, _I],
+    "moe_ffn_backward_fp8": [_S, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                             ctypes.c_size_t, _P],
     "moe_workspace_bytes": [_S, _I],
     "moe_last_error": [],
     "moe_version": [],
@@ -82,7 +87,7 @@ def lib() -> ctypes.CDLL:
             for name, args in _SIGS.items():
                 f = getattr(L, name)
                 f.argtypes = args
-                f.restype = ctypes.c_int
+                f.restype = ctypes.c_size_t if name.endswith("_bytes") else ctypes.c_int
             L.moe_workspace_bytes.restype = ctypes.c_size_t
             L.moe_last_error.restype = ctypes.c_char_p
             L.moe_version.restype = ctypes.c_char_p
@@ -299,7 +304,7 @@ def moe_combine_backward(shape: moe_shape, d_out, y_routed, row_of, topk_gate, d
     _need(topk_gate, T * K, "topk_gate"); _need(dy, (T * K + shape.n_shared * T) * d, "dy")
     _need(d_gate, T * K, "d_gate")
     _check(lib().moe_combine_backward(ctypes.byref(shape), _dt(d_out), _ptr(d_out), _ptr(y_routed), _ptr(row_of),
-                                      _ptr(topk_gate), _ptr(dy), _ptr(d_gate), _stream(stream)))
+                                      _ptr(topk_gate), _dt(dy), _ptr(dy), _ptr(d_gate), _stream(stream)))
 
 
 def moe_route_backward(shape: moe_shape, u, centroids, scores, topk_idx, d_gate, expert_offsets, perm_token, row_of,
@@ -347,3 +352,55 @@ def moe_input_grad(shape: moe_shape, d_out, du_router, da, row_of, du, stream=No
     _need(da, (T * shape.topk + shape.n_shared * T) * d, "da")
     _check(lib().moe_input_grad(ctypes.byref(shape), _ptr(d_out), _ptr(du_router), _ptr(da), _ptr(row_of), _ptr(du),
                                 _stream(stream)))
+
+
+# ---------------------------------------------------------------- FP8 backward
+
+def moe_transpose_bf16(w, out, stream=None):
+    """w [n, rows, cols] bf16 -> out [n, cols, rows] (row-major)."""
+    n, rows, cols = w.shape
+    _need(out, n * rows * cols, "out")
+    _check(lib().moe_transpose_bf16(n, rows, cols, _ptr(w), _ptr(out), _stream(stream)))
+
+
+def moe_ffn_gate_up_cache_fp8(shape: moe_shape, n_experts: int, n_rows: int, expert_offsets, mode: int, row_src,
+                              a_codes, a_scale, a_rows: int, w_gate_up, w_gu_scale, h_codes, h_scale, gu_codes,
+                              gu_scale, workspace=None, stream=None):
+    d, I = shape.d, shape.inter
+    _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a_codes, a_rows * d, "a_codes")
+    _need(a_scale, a_rows * (d // 128), "a_scale"); _need(h_codes, n_rows * I, "h_codes")
+    _need(h_scale, n_rows * (I // 128), "h_scale"); _need(gu_codes, n_rows * 2 * I, "gu_codes")
+    _need(gu_scale, n_rows * (2 * I // 128), "gu_scale")
+    _need(w_gate_up, n_experts * mx_rows(2 * I) * d, "w_gate_up")
+    if mode == MOE_ROWS_GATHER:
+        _need(row_src, n_rows, "row_src")
+    _check(lib().moe_ffn_gate_up_cache_fp8(ctypes.byref(shape), n_experts, n_rows, _ptr(expert_offsets), mode,
+                                           _ptr(row_src), _ptr(a_codes), _ptr(a_scale), a_rows, _ptr(w_gate_up),
+                                           _ptr(w_gu_scale), _ptr(h_codes), _ptr(h_scale), _ptr(gu_codes),
+                                           _ptr(gu_scale), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_ffn_backward_fp8_workspace_bytes(shape: moe_shape, n_rows: int, n_experts: int) -> int:
+    return int(lib().moe_ffn_backward_fp8_workspace_bytes(ctypes.byref(shape), n_rows, n_experts))
+
+
+def moe_ffn_backward_fp8(shape: moe_shape, n_experts: int, n_rows: int, expert_offsets, mode: int, row_src, a_codes,
+                         a_scale, a_rows: int, gu_codes, gu_scale, w_gate_up_t, w_gate_up_t_scale, w_down_t,
+                         w_down_t_scale, dy, da, dw_gate_up, dw_down, workspace, stream=None):
+    d, I = shape.d, shape.inter
+    _need(expert_offsets, n_experts + 1, "expert_offsets"); _need(a_codes, a_rows * d, "a_codes")
+    _need(a_scale, a_rows * (d // 128), "a_scale"); _need(gu_codes, n_rows * 2 * I, "gu_codes")
+    _need(gu_scale, n_rows * (2 * I // 128), "gu_scale")
+    _need(w_gate_up_t, n_experts * mx_rows(d) * 2 * I, "w_gate_up_t")
+    _need(w_gate_up_t_scale, n_experts * (d // 128) * (2 * I // 128), "w_gate_up_t_scale")
+    _need(w_down_t, n_experts * mx_rows(I) * d, "w_down_t")
+    _need(w_down_t_scale, n_experts * (I // 128) * (d // 128), "w_down_t_scale")
+    _need(dy, n_rows * d, "dy"); _need(da, n_rows * d, "da")
+    _need(dw_gate_up, n_experts * 2 * I * d, "dw_gate_up"); _need(dw_down, n_experts * d * I, "dw_down")
+    if mode == MOE_ROWS_GATHER:
+        _need(row_src, n_rows, "row_src")
+    _check(lib().moe_ffn_backward_fp8(ctypes.byref(shape), n_experts, n_rows, _ptr(expert_offsets), mode,
+                                      _ptr(row_src), _ptr(a_codes), _ptr(a_scale), a_rows, _ptr(gu_codes),
+                                      _ptr(gu_scale), _ptr(w_gate_up_t), _ptr(w_gate_up_t_scale), _ptr(w_down_t),
+                                      _ptr(w_down_t_scale), _ptr(dy), _ptr(da), _ptr(dw_gate_up), _ptr(dw_down),
+                                      _ptr(workspace), _nbytes(workspace), _stream(stream)))

@@ -426,14 +426,17 @@ moe_status moe_ffn_gate_up_cache(const moe_shape* shape, moe_dtype w, int32_t n_
 }
 
 moe_status moe_combine_backward(const moe_shape* shape, moe_dtype io, const void* d_out, const void* y_routed,
-                                const int32_t* row_of, const float* topk_gate, void* dy, float* d_gate, void* stream) {
+                                const int32_t* row_of, const float* topk_gate, moe_dtype dy_dtype, void* dy,
+                                float* d_gate, void* stream) {
   g_err.clear();
   if (moe_status st = check_shape(shape); st != MOE_OK) return st;
   REQUIRE(io == MOE_BF16, "combine_backward: io must be MOE_BF16");
+  REQUIRE(dy_dtype == MOE_BF16 || dy_dtype == MOE_F32, "combine_backward: dy_dtype must be MOE_BF16 or MOE_F32");
   REQUIRE(d_out && y_routed && row_of && topk_gate && dy && d_gate, "combine_backward: a required pointer is NULL");
   SUPPORT(shape->d % 2 == 0, "combine_backward: d must be even");
   auto st = static_cast<hipStream_t>(stream);
-  return finish(moe::launch_combine_backward(moe::to_shape(*shape), d_out, y_routed, row_of, topk_gate, dy, d_gate, st),
+  return finish(moe::launch_combine_backward(moe::to_shape(*shape), d_out, y_routed, row_of, topk_gate, dy,
+                                             dy_dtype == MOE_F32, d_gate, st),
                 "moe_combine_backward", st);
 }
 
@@ -532,6 +535,140 @@ moe_status moe_input_grad(const moe_shape* shape, const void* d_out, const float
   auto st = static_cast<hipStream_t>(stream);
   return finish(moe::launch_input_grad(moe::to_shape(*shape), d_out, du_router, da, row_of, du, st), "moe_input_grad",
                 st);
+}
+
+
+moe_status moe_transpose_bf16(int32_t n_mats, int32_t rows, int32_t cols, const void* src, void* dst, void* stream) {
+  g_err.clear();
+  REQUIRE(n_mats > 0 && rows > 0 && cols > 0, "transpose_bf16: sizes must be positive");
+  SUPPORT(rows % 64 == 0 && cols % 64 == 0 && n_mats <= 65535,
+          "transpose_bf16: rows (%d) and cols (%d) must be multiples of 64, n_mats <= 65535", rows, cols);
+  REQUIRE(src && dst && src != dst, "transpose_bf16: bad pointers");
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_transpose_rows_bf16(n_mats, rows, cols, src, dst, st), "moe_transpose_bf16", st);
+}
+
+moe_status moe_ffn_gate_up_cache_fp8(const moe_shape* shape, int32_t n_experts, int32_t n_rows,
+                                     const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
+                                     const void* a_codes, const float* a_scale, int32_t a_rows, const void* w_gate_up,
+                                     const void* w_gu_scale, void* h_codes, float* h_scale, void* gu_codes,
+                                     float* gu_scale, void* workspace, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (moe_status r = check_ffn(shape, MOE_F8E4M3, n_experts, n_rows, expert_offsets, 1); r != MOE_OK) return r;
+  if (moe_status r = check_gate_up(shape, MOE_F8E4M3, mode, row_src, a_codes, a_scale, a_rows, w_gate_up, w_gu_scale);
+      r != MOE_OK)
+    return r;
+  REQUIRE(h_codes && h_scale && gu_codes && gu_scale, "ffn_gate_up_cache_fp8: h or the cache is NULL");
+  SUPPORT(static_cast<long long>(n_rows) * 2 * shape->inter < (1LL << 32),
+          "ffn_gate_up_cache_fp8: n_rows * 2 * inter must stay below 2^32");
+  if (!workspace || ws_bytes < moe::kFfnQueueBytes)
+    return fail(MOE_E_WORKSPACE, "ffn_gate_up_cache_fp8: workspace of %zu bytes < %zu needed", ws_bytes,
+                moe::kFfnQueueBytes);
+  moe::FfnArgs p{shape->d, shape->inter, n_experts, n_rows, a_rows, expert_offsets, mode, row_src, a_codes, a_scale,
+                 w_gate_up, w_gu_scale, nullptr, nullptr, MOE_BF16, nullptr, h_codes, h_scale,
+                 static_cast<int*>(workspace)};
+  p.gu_cache = gu_codes;
+  p.gu_scale = gu_scale;
+  auto st = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_ffn_fp8_gate_up(p, st), "moe_ffn_gate_up_cache_fp8", st);
+}
+
+namespace {
+struct Bwd8Layout {
+  size_t dyq, dys, dh, dgu, dguq, dgus, h, dyr, hr, dgur, ar, pre, q, total;
+};
+Bwd8Layout bwd8_layout(const moe_shape* s, int32_t n_rows, int32_t n_experts) {
+  const size_t r = static_cast<size_t>(n_rows), d = static_cast<size_t>(s->d), I = static_cast<size_t>(s->inter);
+  Bwd8Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.dyq = take(r * d);
+  L.dys = take(r * (d / 128) * 4);
+  L.dh = take(r * I * 4);                             // fp32: the inputs of the quantisers
+  L.dgu = take(r * 2 * I * 4);
+  L.dguq = take(r * 2 * I);
+  L.dgus = take(r * (2 * I / 128) * 4);
+  L.h = take(r * I * 4);
+  L.dyr = take(r * d * 2);                              // bf16: the re-tiled Wgrad operands (exact E4M3 x 2^k)
+  L.hr = take(r * I * 2);
+  L.dgur = take(r * 2 * I * 2);
+  L.ar = take(r * d * 2);
+  L.pre = take((static_cast<size_t>(n_experts) + 1) * 4);
+  L.q = take(2 * moe::kFfnQueueBytes);
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+size_t moe_ffn_backward_fp8_workspace_bytes(const moe_shape* shape, int32_t n_rows, int32_t n_experts) {
+  if (!shape || n_rows < 0 || n_experts <= 0 || shape->d <= 0 || shape->inter <= 0) return 0;
+  return bwd8_layout(shape, n_rows, n_experts).total;
+}
+
+moe_status moe_ffn_backward_fp8(const moe_shape* shape, int32_t n_experts, int32_t n_rows,
+                                const int32_t* expert_offsets, moe_row_mode mode, const int32_t* row_src,
+                                const void* a_codes, const float* a_scale, int32_t a_rows, const void* gu_codes,
+                                const float* gu_scale, const void* w_gate_up_t, const float* w_gate_up_t_scale,
+                                const void* w_down_t, const float* w_down_t_scale, const void* dy, void* da,
+                                float* dw_gate_up, float* dw_down, void* workspace, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (moe_status r = check_ffn(shape, MOE_F8E4M3, n_experts, n_rows, expert_offsets, 0); r != MOE_OK) return r;
+  REQUIRE(a_codes && a_scale && gu_codes && gu_scale && w_gate_up_t && w_gate_up_t_scale && w_down_t &&
+              w_down_t_scale && dy && da && dw_gate_up && dw_down,
+          "ffn_backward_fp8: a required pointer is NULL");
+  REQUIRE(a_rows > 0, "ffn_backward_fp8: a_rows must be positive");
+  REQUIRE(mode == MOE_ROWS_DIRECT || mode == MOE_ROWS_GATHER || mode == MOE_ROWS_SEGMENT,
+          "ffn_backward_fp8: bad row mode %d", static_cast<int>(mode));
+  REQUIRE(mode != MOE_ROWS_GATHER || row_src != nullptr, "ffn_backward_fp8: MOE_ROWS_GATHER needs row_src");
+  const int d = shape->d, I = shape->inter;
+  SUPPORT(static_cast<long long>(n_rows) * 2 * I * 4 < (1LL << 32) && static_cast<long long>(n_rows) * d * 2 < (1LL << 32),
+          "ffn_backward_fp8: n_rows * 2I must stay below 2^30 and n_rows * d below 2^31 elements");
+  SUPPORT(2 * I <= 10240, "ffn_backward_fp8: the input-gradient GEMM of gate/up needs 2 * inter <= 10240");
+  const Bwd8Layout L = bwd8_layout(shape, n_rows, n_experts);
+  if (!workspace || ws_bytes < L.total)
+    return fail(MOE_E_WORKSPACE, "ffn_backward_fp8: workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  auto at = [&](size_t o) { return static_cast<void*>(ws + o); };
+  float* dys = reinterpret_cast<float*>(ws + L.dys);
+  float* dgus = reinterpret_cast<float*>(ws + L.dgus);
+  int* pre = reinterpret_cast<int*>(ws + L.pre);
+  int* q = reinterpret_cast<int*>(ws + L.q);
+  auto st = static_cast<hipStream_t>(stream);
+  // Dgrad of the down projection: dh = Q(dy) W_d, dy quantised per 1x128 tile along d
+  hipError_t e = moe::launch_quantize_rows(n_rows, d, dy, false, at(L.dyq), dys, st);
+  moe::FfnArgs p1{I, d, n_experts, n_rows, n_rows, expert_offsets, MOE_ROWS_DIRECT, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, w_down_t, w_down_t_scale, MOE_F32, at(L.dh), at(L.dyq), dys, q};
+  if (e == hipSuccess) e = moe::launch_ffn_fp8_down(p1, st);
+  // SwiGLU backward from the cached E4M3 [G, U]; h recomputed
+  if (e == hipSuccess) e = moe::launch_swiglu_backward8(n_rows, I, at(L.dh), gu_codes, gu_scale, at(L.dgu), at(L.h), st);
+  // Dgrad of gate/up: da = Q([dG, dU]) W_gate_up
+  if (e == hipSuccess) e = moe::launch_quantize_rows(n_rows, 2 * I, at(L.dgu), true, at(L.dguq), dgus, st);
+  moe::FfnArgs p2{d, 2 * I, n_experts, n_rows, n_rows, expert_offsets, MOE_ROWS_DIRECT, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, w_gate_up_t, w_gate_up_t_scale, MOE_BF16, da, at(L.dguq), dgus,
+                  q + moe::kQueueInts};
+  if (e == hipSuccess) e = moe::launch_ffn_fp8_down(p2, st);
+  // Wgrad operands re-tiled to 128x1 (power-of-two scales): dy, h and [dG, dU] by row, a from its 1x128 codes
+  if (e == hipSuccess) e = moe::launch_row_block_prefix(n_experts, n_rows, expert_offsets, pre, st);
+  if (e == hipSuccess)
+    e = moe::launch_requant_cols(d, n_experts, n_rows, expert_offsets, pre, MOE_ROWS_DIRECT, nullptr, n_rows, dy, false,
+                                 nullptr, nullptr, at(L.dyr), st);
+  if (e == hipSuccess)
+    e = moe::launch_requant_cols(I, n_experts, n_rows, expert_offsets, pre, MOE_ROWS_DIRECT, nullptr, n_rows, at(L.h),
+                                 true, nullptr, nullptr, at(L.hr), st);
+  if (e == hipSuccess)
+    e = moe::launch_requant_cols(2 * I, n_experts, n_rows, expert_offsets, pre, MOE_ROWS_DIRECT, nullptr, n_rows,
+                                 at(L.dgu), true, nullptr, nullptr, at(L.dgur), st);
+  if (e == hipSuccess)
+    e = moe::launch_requant_cols(d, n_experts, n_rows, expert_offsets, pre, mode, row_src, a_rows, nullptr, false,
+                                 a_codes, a_scale, at(L.ar), st);
+  // Wgrad: dW_d = R(dy)^T R(h), dW_gate_up = R([dG, dU])^T R(a)
+  if (e == hipSuccess)
+    e = moe::launch_wgrad(d, I, n_experts, n_rows, n_rows, expert_offsets, MOE_ROWS_DIRECT, nullptr, at(L.dyr),
+                          at(L.hr), dw_down, st);
+  if (e == hipSuccess)
+    e = moe::launch_wgrad(2 * I, d, n_experts, n_rows, n_rows, expert_offsets, MOE_ROWS_DIRECT, nullptr, at(L.dgur),
+                          at(L.ar), dw_gate_up, st);
+  return finish(e, "moe_ffn_backward_fp8", st);
 }
 
 }  // extern "C"

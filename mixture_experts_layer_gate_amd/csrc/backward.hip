@@ -17,17 +17,27 @@
 //  transpose_tile:    W [R, C] -> W^T [C, R] in the tiled bf16 layout (the input
 //                     gradient GEMMs contract over W's rows)
 // Every sum runs in a fixed order in fp32: the results are deterministic.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 
-// One wavefront per token; lanes stride over d in pairs of bf16.
+// One wavefront per token; lanes stride over d in pairs of bf16. DY: uint16_t
+// (bf16 rows) or float (fp32 rows, the input of the FP8 backward's quantisers).
+__device__ __forceinline__ void store_pair(uint32_t* p, int c, float a, float b) { p[c] = pack_bf16x2(a, b); }
+__device__ __forceinline__ void store_pair(float* p, int c, float a, float b) {
+  *reinterpret_cast<float2*>(p + 2 * c) = make_float2(a, b);
+}
+
+template <class DY>
 __global__ __launch_bounds__(256) void combine_backward_kernel(int T, int d, int K, int Ns, const uint16_t* __restrict__ dout,
                                                                const uint16_t* __restrict__ y,
                                                                const int32_t* __restrict__ row_of,
-                                                               const float* __restrict__ gate, uint16_t* __restrict__ dy,
+                                                               const float* __restrict__ gate, DY* __restrict__ dy,
                                                                float* __restrict__ dgate, int n_rows) {
+  using Row = typename std::conditional<sizeof(DY) == 2, uint32_t, float>::type;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   for (int t = blockIdx.x * 4 + w; t < T; t += gridDim.x * 4) {
     const uint32_t* o = reinterpret_cast<const uint32_t*>(dout + static_cast<size_t>(t) * d);
@@ -38,13 +48,13 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(int T, int d, int
       float dot = 0.0f;
       if (ok) {
         const uint32_t* yr = reinterpret_cast<const uint32_t*>(y + static_cast<size_t>(r) * d);
-        uint32_t* dr = reinterpret_cast<uint32_t*>(dy + static_cast<size_t>(r) * d);
+        Row* dr = reinterpret_cast<Row*>(dy + static_cast<size_t>(r) * d);
         for (int c = l; c < d / 2; c += 64) {
           const uint32_t ov = o[c], yv = yr[c];
           const float o0 = __uint_as_float(ov << 16), o1 = __uint_as_float(ov & 0xFFFF0000u);
           dot = fmaf(o0, __uint_as_float(yv << 16), dot);
           dot = fmaf(o1, __uint_as_float(yv & 0xFFFF0000u), dot);
-          dr[c] = pack_bf16x2(g * o0, g * o1);
+          store_pair(dr, c, g * o0, g * o1);
         }
       }
 #pragma unroll
@@ -52,8 +62,8 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(int T, int d, int
       if (l == 0) dgate[static_cast<size_t>(t) * K + k] = ok ? dot : 0.0f;
     }
     for (int s = 0; s < Ns; ++s) {
-      uint32_t* dr = reinterpret_cast<uint32_t*>(dy + (static_cast<size_t>(T) * K + static_cast<size_t>(s) * T + t) * d);
-      for (int c = l; c < d / 2; c += 64) dr[c] = o[c];
+      Row* dr = reinterpret_cast<Row*>(dy + (static_cast<size_t>(T) * K + static_cast<size_t>(s) * T + t) * d);
+      for (int c = l; c < d / 2; c += 64) store_pair(dr, c, __uint_as_float(o[c] << 16), __uint_as_float(o[c] & 0xFFFF0000u));
     }
   }
 }
@@ -198,11 +208,16 @@ static long long grid_cap(long long blocks) {
 }
 
 hipError_t launch_combine_backward(const Shape& s, const void* dout, const void* y, const int32_t* row_of,
-                                   const float* gate, void* dy, float* dgate, hipStream_t st) {
+                                   const float* gate, void* dy, bool dy_f32, float* dgate, hipStream_t st) {
   const long long blocks = grid_cap(cdiv(s.T, 4));
-  hipLaunchKernelGGL(combine_backward_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, s.T, s.d, s.K,
-                     s.Ns, static_cast<const uint16_t*>(dout), static_cast<const uint16_t*>(y), row_of, gate,
-                     static_cast<uint16_t*>(dy), dgate, s.T * s.K);
+  if (dy_f32)
+    hipLaunchKernelGGL(combine_backward_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, s.T, s.d,
+                       s.K, s.Ns, static_cast<const uint16_t*>(dout), static_cast<const uint16_t*>(y), row_of, gate,
+                       static_cast<float*>(dy), dgate, s.T * s.K);
+  else
+    hipLaunchKernelGGL(combine_backward_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, s.T,
+                       s.d, s.K, s.Ns, static_cast<const uint16_t*>(dout), static_cast<const uint16_t*>(y), row_of,
+                       gate, static_cast<uint16_t*>(dy), dgate, s.T * s.K);
   return hipGetLastError();
 }
 

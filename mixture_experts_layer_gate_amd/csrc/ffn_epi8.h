@@ -46,6 +46,9 @@ struct GateUpEpi8 {
   uint8_t* lds;
   uint8_t* __restrict__ Hq;
   float* __restrict__ Hs;
+  // backward cache (or NULL): the SwiGLU inputs [G, U] as 1x128 E4M3 tiles, rows of 2I codes and 2I/128 scales
+  uint8_t* __restrict__ GUq = nullptr;
+  float* __restrict__ GUs = nullptr;
   __device__ __forceinline__ void operator()(int seg, f32x16 (&acc)[P8::TW][P8::TT]) {
     const int l = threadIdx.x & 63, ww = p8_ww(), nb = nb0 + seg;
     float* amax_x = reinterpret_cast<float*>(lds + AMAX_OFF);   // [2][BT]
@@ -81,6 +84,43 @@ struct GateUpEpi8 {
         if (ww == 0 && l < 32) Hs[static_cast<size_t>(un.m0 + tr) * (I / 128) + nb] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
       }
     }
+    if (GUq != nullptr) {                              // G (sub-tiles 0, 1), then U (2, 3): same tile exchange
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        lds_barrier();                                  // every wave has read the previous amax_x
+#pragma unroll
+        for (int i = 0; i < MS; ++i) {
+          float x = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x = fmaxf(x, __builtin_fabsf(acc[j + 2 * part][i][v]));
+          x = fmaxf(x, __shfl_xor(x, 32, kWave));
+          if (l < 32) amax_x[ww * P8::BT + p8_token_row(i)] = x;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < MS; ++i) {
+          const int tr = p8_token_row(i);
+          const float amax = fmaxf(amax_x[tr], amax_x[P8::BT + tr]);
+          if (tr < un.rows) {
+            const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
+            uint8_t* grow = GUq + static_cast<size_t>(un.m0 + tr) * 2 * I + part * I + nb * 128 + ww * 64 + 4 * (l >> 5);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const f32x16& a = acc[j + 2 * part][i];
+                *reinterpret_cast<uint32_t*>(grow + j * 32 + 8 * q) =
+                    f32x4_to_e4m3(a[4 * q] * inv, a[4 * q + 1] * inv, a[4 * q + 2] * inv, a[4 * q + 3] * inv);
+              }
+            if (ww == 0 && l < 32)
+              GUs[static_cast<size_t>(un.m0 + tr) * (2 * I / 128) + part * (I / 128) + nb] =
+                  amax > 0.0f ? amax / kE4M3Max : 1.0f;
+          }
+        }
+      }
+    }
     // amax_x is next written in the following tile's epilogue, after at least
     // one ring barrier that every wave reaches with these reads consumed
   }
@@ -92,20 +132,26 @@ struct DownEpi8 {
   const Unit& un;
   int d, nb0;
   uint16_t* __restrict__ y;
+  float* __restrict__ yf = nullptr;   // fp32 rows instead (then y is unused)
   __device__ __forceinline__ void operator()(int seg, f32x16 (&acc)[P8::TW][P8::TT]) {
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const int tr = p8_token_row(i);
       if (tr < un.rows) {
-        uint16_t* yrow = y + static_cast<size_t>(un.m0 + tr) * d + (nb0 + seg) * P8::BW;
+        const size_t row0 = static_cast<size_t>(un.m0 + tr) * d + (nb0 + seg) * P8::BW;
 #pragma unroll
         for (int j = 0; j < P8::TW; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if ((nb0 + seg) * P8::BW + p8_wcol(j, q) < d)   // the 128-column last tile of d % 256 == 128
-              *reinterpret_cast<u32x2*>(yrow + p8_wcol(j, q)) =
-                  u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
-                        pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])};
+            if ((nb0 + seg) * P8::BW + p8_wcol(j, q) < d) {  // the 128-column last tile of d % 256 == 128
+              if (yf != nullptr)
+                *reinterpret_cast<f32x4*>(yf + row0 + p8_wcol(j, q)) =
+                    f32x4{acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]};
+              else
+                *reinterpret_cast<u32x2*>(y + row0 + p8_wcol(j, q)) =
+                    u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
+                          pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])};
+            }
       }
     }
   }

@@ -32,16 +32,17 @@ constexpr int kMaxExperts8 = 4096;
 template <int MS, int LT>
 __device__ __forceinline__ void gate_up8_unit(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
                                               const Unit& un, int nb0, int nseg, uint8_t* lds,
-                                              uint8_t* __restrict__ Hq, float* __restrict__ Hs) {
-  GateUpEpi8<MS, P8::AMAX_OFF> epi{un, I, nb0, lds, Hq, Hs};
+                                              uint8_t* __restrict__ Hq, float* __restrict__ Hs,
+                                              uint8_t* __restrict__ GUq, float* __restrict__ GUs) {
+  GateUpEpi8<MS, P8::AMAX_OFF> epi{un, I, nb0, lds, Hq, Hs, GUq, GUs};
   pipe8_stream<MS, LT, true>(rows, srs, d, nseg, lds, epi);
 }
 
 template <int MS, int LT>
 __device__ __forceinline__ void down8_unit(const Pipe8Rows& rows, __amdgpu_buffer_rsrc_t srs, int d, int I,
                                            const Unit& un, int nb0, int nseg, uint8_t* lds,
-                                           uint16_t* __restrict__ y) {
-  DownEpi8<MS> epi{un, d, nb0, y};
+                                           uint16_t* __restrict__ y, float* __restrict__ yf) {
+  DownEpi8<MS> epi{un, d, nb0, y, yf};
   pipe8_stream<MS, LT, false>(rows, srs, I, nseg, lds, epi);
 }
 
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
     int d, int I, int E, int n_rows, int a_rows, const int32_t* __restrict__ off, moe_row_mode mode,
     const int32_t* __restrict__ row_src, const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
     const uint8_t* __restrict__ wgu, const float* __restrict__ wgu_scale, uint8_t* __restrict__ Hq,
-    float* __restrict__ Hs, int* __restrict__ q) {
+    float* __restrict__ Hs, uint8_t* __restrict__ GUq, float* __restrict__ GUs, int* __restrict__ q) {
   extern __shared__ __align__(16) uint8_t lds8[];
   float* swt = reinterpret_cast<float*>(lds8 + P8::SW_OFF);
   int* srcrow = reinterpret_cast<int*>(lds8 + P8::SRC_OFF);
@@ -92,11 +93,11 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_gate_up_fp8_kernel(
     // LT = ceil(nsub / 2) token load groups; wave row 0 has LT live sub-tiles, row 1 LT or LT - 1
     const bool full = live_token_subtiles8(un.nsub) * 2 >= un.nsub;
     if (un.nsub > 2) {
-      if (full) gate_up8_unit<2, 2>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs);
-      else gate_up8_unit<1, 2>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs);
+      if (full) gate_up8_unit<2, 2>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs, GUq, GUs);
+      else gate_up8_unit<1, 2>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs, GUq, GUs);
     } else {
-      if (full) gate_up8_unit<1, 1>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs);
-      else gate_up8_unit<0, 1>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs);
+      if (full) gate_up8_unit<1, 1>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs, GUq, GUs);
+      else gate_up8_unit<0, 1>(rows, srs, d, I, un, nb0, nseg, lds8, Hq, Hs, GUq, GUs);
     }
   }
 }
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
                                                                  const float* __restrict__ Hs,
                                                                  const uint8_t* __restrict__ wd,
                                                                  const float* __restrict__ wd_scale,
-                                                                 uint16_t* __restrict__ y,
+                                                                 uint16_t* __restrict__ y, float* __restrict__ yf,
                                                                  int* __restrict__ q) {
   extern __shared__ __align__(16) uint8_t lds8[];
   float* swt = reinterpret_cast<float*>(lds8 + P8::SW_OFF);
@@ -149,11 +150,11 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
                          static_cast<uint64_t>(nseg) * P8::BW * I);
     const bool full = live_token_subtiles8(un.nsub) * 2 >= un.nsub;
     if (un.nsub > 2) {
-      if (full) down8_unit<2, 2>(rows, srs, d, I, un, nb0, nseg, lds8, y);
-      else down8_unit<1, 2>(rows, srs, d, I, un, nb0, nseg, lds8, y);
+      if (full) down8_unit<2, 2>(rows, srs, d, I, un, nb0, nseg, lds8, y, yf);
+      else down8_unit<1, 2>(rows, srs, d, I, un, nb0, nseg, lds8, y, yf);
     } else {
-      if (full) down8_unit<1, 1>(rows, srs, d, I, un, nb0, nseg, lds8, y);
-      else down8_unit<0, 1>(rows, srs, d, I, un, nb0, nseg, lds8, y);
+      if (full) down8_unit<1, 1>(rows, srs, d, I, un, nb0, nseg, lds8, y, yf);
+      else down8_unit<0, 1>(rows, srs, d, I, un, nb0, nseg, lds8, y, yf);
     }
   }
 }
@@ -191,7 +192,7 @@ hipError_t launch_ffn_fp8_gate_up(const FfnArgs& p, hipStream_t st) {
                      st, p.d, p.I,
                      p.n_experts, p.n_rows, p.a_rows, p.offsets, p.mode, p.row_src,
                      static_cast<const uint8_t*>(p.a), p.a_scale, static_cast<const uint8_t*>(p.w_gu), static_cast<const float*>(p.w_gu_scale),
-                     static_cast<uint8_t*>(p.h), p.h_scale, q);
+                     static_cast<uint8_t*>(p.h), p.h_scale, static_cast<uint8_t*>(p.gu_cache), p.gu_scale, q);
   return hipGetLastError();
 }
 
@@ -206,7 +207,9 @@ hipError_t launch_ffn_fp8_down(const FfnArgs& p, hipStream_t st) {
                      lds,
                      st, p.d, p.I,
                      p.n_experts, p.n_rows, p.offsets, static_cast<const uint8_t*>(p.h), p.h_scale,
-                     static_cast<const uint8_t*>(p.w_d), static_cast<const float*>(p.w_d_scale), static_cast<uint16_t*>(p.y), q);
+                     static_cast<const uint8_t*>(p.w_d), static_cast<const float*>(p.w_d_scale),
+                     p.y_dtype == MOE_F32 ? nullptr : static_cast<uint16_t*>(p.y),
+                     p.y_dtype == MOE_F32 ? static_cast<float*>(p.y) : nullptr, q);
   return hipGetLastError();
 }
 

@@ -71,7 +71,8 @@ struct FfnArgs {
   void* h;         // SwiGLU output [n_rows, I]
   float* h_scale;  // fp8: [n_rows, I/128]
   int* queue;      // unit-queue counters of this launch (kQueueInts ints of workspace)
-  void* gu_cache = nullptr;   // bf16 gate/up: the SwiGLU inputs [n_rows, 2I] for the backward, or NULL
+  void* gu_cache = nullptr;   // the SwiGLU inputs [n_rows, 2I] for the backward (bf16, or E4M3 codes), or NULL
+  float* gu_scale = nullptr;  // fp8: the cache's 1x128 scales [n_rows, 2I / 128]
 };
 constexpr size_t kFfnQueueBytes = 128;   // per launch
 // Workspace of moe_grouped_ffn: H (+ its fp8 scales), then the queue
@@ -89,7 +90,7 @@ hipError_t launch_ffn_fp4_down(const FfnArgs& a, hipStream_t st);
 
 // ---- backward
 hipError_t launch_combine_backward(const Shape& s, const void* dout, const void* y, const int32_t* row_of,
-                                   const float* gate, void* dy, float* dgate, hipStream_t st);
+                                   const float* gate, void* dy, bool dy_f32, float* dgate, hipStream_t st);
 hipError_t launch_route_backward(const Shape& s, moe_dtype act, const void* u, const void* cent, const float* scores,
                                  const int32_t* idx, const float* dgate, const int32_t* off,
                                  const int32_t* perm_token, const int32_t* row_of, float* du_router, float* dcent,
@@ -99,6 +100,16 @@ hipError_t launch_swiglu_backward(long long n_rows, int I, const void* dh, const
 hipError_t launch_input_grad(const Shape& s, const void* dout, const float* du_router, const void* da,
                              const int32_t* row_of, float* du, hipStream_t st);
 hipError_t launch_transpose_tile_bf16(int n_mats, int rows, int cols, const void* w, void* out, hipStream_t st);
+// FP8 backward (backward_fp8.hip)
+hipError_t launch_transpose_rows_bf16(int n_mats, int rows, int cols, const void* w, void* out, hipStream_t st);
+hipError_t launch_quantize_rows(long long n_rows, int cols, const void* x, bool f32_in, void* codes, float* scales,
+                                hipStream_t st);
+hipError_t launch_swiglu_backward8(long long n_rows, int I, const void* dh, const void* guq, const float* gus,
+                                   void* dgu, void* h, hipStream_t st);
+hipError_t launch_row_block_prefix(int E, int n_rows, const int32_t* off, int* pre, hipStream_t st);
+hipError_t launch_requant_cols(int C, int E, int n_rows, const int32_t* off, const int* pre, moe_row_mode mode,
+                               const int32_t* row_src, int a_rows, const void* x, bool f32_in, const void* xq,
+                               const float* xs, void* out, hipStream_t st);
 hipError_t launch_wgrad(int M, int N, int E, int n_rows, int a_rows, const int32_t* off, moe_row_mode mode,
                         const int32_t* row_src, const void* X, const void* Y, float* C, hipStream_t st);
 

@@ -62,8 +62,8 @@ class MoELayer:
                  gather_in_gemm: bool = True, pow2_act_scales: bool = False, tiled_bf16: bool = True,
                  train: bool = False):
         self.cfg = cfg
-        if train and cfg.gemm != "bf16":
-            raise ValueError("MoELayer(train=True) needs bf16 expert GEMMs")
+        if train and cfg.gemm not in ("bf16", "fp8"):
+            raise ValueError("MoELayer(train=True) needs bf16 or fp8 expert GEMMs")
         self.train = train
         self.shape = B.moe_shape.of(cfg)
         self.dev = torch.device(device)
@@ -91,6 +91,14 @@ class MoELayer:
                     codes = torch.empty((n, B.mx_rows(r), c), dtype=torch.uint8, device=self.dev)   # tiled
                     scale = torch.empty((n, r // 128, c // 128), dtype=torch.float32, device=self.dev)
                     B.moe_quantize_weights(both, codes, scale, gate_up=(kind == "gate_up"))
+                    if train:                       # W^T in 128x128 blocks for the FP8 input-gradient GEMMs
+                        wt = torch.empty((n, c, r), dtype=both.dtype, device=self.dev)
+                        B.moe_transpose_bf16(both, wt)
+                        ct = torch.empty((n, B.mx_rows(c), r), dtype=torch.uint8, device=self.dev)
+                        st = torch.empty((n, c // 128, r // 128), dtype=torch.float32, device=self.dev)
+                        B.moe_quantize_weights(wt, ct, st, gate_up=False)
+                        del wt
+                        self.w["all_" + kind + "_t"], self.w["all_" + kind + "_t_scale"] = ct, st
                 else:
                     rt = B.mx_rows(r)               # tiled MXFP4: whole 256-row tiles
                     codes = torch.empty((n, rt, c // 2), dtype=torch.uint8, device=self.dev)
@@ -116,8 +124,8 @@ class MoELayer:
             self.w["w_" + kind], self.w["s_" + kind] = both[:N], both[N:]
         self.ws = torch.empty(max(B.moe_workspace_bytes(self.shape, self.gemm), 256), dtype=torch.uint8,
                               device=self.dev)
-        if train and self.gemm != B.MOE_BF16_TILED:
-            raise ValueError("MoELayer(train=True) needs the tiled bf16 weights (tiled_bf16=True)")
+        if train and self.gemm not in (B.MOE_BF16_TILED, B.MOE_F8E4M3):
+            raise ValueError("MoELayer(train=True) needs the tiled bf16 weights (tiled_bf16=True) or fp8")
         self._alloc()
         if train:
             self._alloc_train()
@@ -127,8 +135,15 @@ class MoELayer:
         T, K, N, Ns, d, I = c.T, c.topk, c.n_routed, c.n_shared, c.d, c.inter
         n_rows = T * (K + Ns)
         bf = torch.bfloat16
-        self.h_all = torch.empty((n_rows, I), dtype=bf, device=dev)
-        self.gu_cache = torch.empty((n_rows, 2 * I), dtype=bf, device=dev)
+        if self.q8:                                  # E4M3 H and [G, U] cache with their 1x128 scales
+            self.h_all = torch.empty((n_rows, I), dtype=torch.uint8, device=dev)
+            self.h_all_scale = torch.empty((n_rows, I // 128), dtype=torch.float32, device=dev)
+            self.gu_cache = torch.empty((n_rows, 2 * I), dtype=torch.uint8, device=dev)
+            self.gu_scale = torch.empty((n_rows, 2 * I // 128), dtype=torch.float32, device=dev)
+        else:
+            self.h_all = torch.empty((n_rows, I), dtype=bf, device=dev)
+            self.h_all_scale = None
+            self.gu_cache = torch.empty((n_rows, 2 * I), dtype=bf, device=dev)
         self.dy_all = torch.empty((n_rows, d), dtype=bf, device=dev)
         self.da_all = torch.empty((n_rows, d), dtype=bf, device=dev)
         self.d_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
@@ -139,8 +154,9 @@ class MoELayer:
         self.grads = {"centroids": torch.empty((N, d), dtype=torch.float32, device=dev),
                       "all_gate_up": dwg, "all_down": dwd, "w_gate_up": dwg[:N], "w_down": dwd[:N],
                       "s_gate_up": dwg[N:], "s_down": dwd[N:]}
-        self.ws_bwd = torch.empty(max(B.moe_ffn_backward_workspace_bytes(self.shape, n_rows), T * K * 4, 256),
-                                  dtype=torch.uint8, device=dev)
+        wsb = (B.moe_ffn_backward_fp8_workspace_bytes(self.shape, n_rows, N + Ns) if self.q8
+               else B.moe_ffn_backward_workspace_bytes(self.shape, n_rows))
+        self.ws_bwd = torch.empty(max(wsb, T * K * 4, 256), dtype=torch.uint8, device=dev)
 
     def _alloc(self):
         c, dev = self.cfg, self.dev
@@ -335,14 +351,21 @@ class MoELayer:
         c = self.cfg
         self.u_saved = u
         E, n_rows = c.n_routed + c.n_shared, c.T * (c.topk + c.n_shared)
+        if self.q8:
+            B.moe_ffn_gate_up_cache_fp8(self.shape, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all,
+                                        self.u_q, self.u_scale, c.T, self.w["all_gate_up"],
+                                        self.w["all_gate_up_scale"], self.h_all, self.h_all_scale, self.gu_cache,
+                                        self.gu_scale, self.ws)
+            return
         B.moe_ffn_gate_up_cache(self.shape, self.gemm, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all,
                                 u, c.T, self.w["all_gate_up"], self.h_all, self.gu_cache, self.ws)
 
     def ffn_down_train(self):
         c = self.cfg
         E, n_rows = c.n_routed + c.n_shared, c.T * (c.topk + c.n_shared)
-        B.moe_ffn_down(self.shape, self.gemm, E, n_rows, self.offsets_all, self.h_all, None, self.w["all_down"],
-                       None, self.y_all, self.ws)
+        B.moe_ffn_down(self.shape, self.gemm, E, n_rows, self.offsets_all, self.h_all,
+                       self.h_all_scale if self.q8 else None, self.w["all_down"], self.w.get("all_down_scale"),
+                       self.y_all, self.ws)
 
     def combine_backward(self, d_out):
         B.moe_combine_backward(self.shape, d_out, self.y_routed, self.row_of, self.topk_gate, self.dy_all, self.d_gate)
@@ -350,6 +373,13 @@ class MoELayer:
     def ffn_backward(self):
         c = self.cfg
         E, n_rows = c.n_routed + c.n_shared, c.T * (c.topk + c.n_shared)
+        if self.q8:
+            B.moe_ffn_backward_fp8(self.shape, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all,
+                                   self.u_q, self.u_scale, c.T, self.gu_cache, self.gu_scale,
+                                   self.w["all_gate_up_t"], self.w["all_gate_up_t_scale"], self.w["all_down_t"],
+                                   self.w["all_down_t_scale"], self.dy_all, self.da_all, self.grads["all_gate_up"],
+                                   self.grads["all_down"], self.ws_bwd)
+            return
         B.moe_ffn_backward(self.shape, E, n_rows, self.offsets_all, B.MOE_ROWS_GATHER, self.rows_all, self.u_saved,
                            c.T, self.gu_cache, self.w["all_gate_up_t"], self.w["all_down_t"], self.dy_all,
                            self.da_all, self.grads["all_gate_up"], self.grads["all_down"], self.ws_bwd)

@@ -26,7 +26,7 @@ are "parity unpinned".
 """
 from .accumulation import keep_bits, limited_precision_gemm  # noqa: F401
 from .backward import (  # noqa: F401
-    ffn_backward, ffn_backward_fp8, gate_backward, layer_backward, requant_cols_pow2,
+    ffn_backward, ffn_backward_fp8, gate_backward, layer_backward, requant_cols_pow2, round_bf16,
 )
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode  # noqa: F401
 from .mxfp4 import (  # noqa: F401

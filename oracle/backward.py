@@ -29,7 +29,10 @@ rows of a column, the "transposed re-quantisation"). Readings: the 128-row
 blocks start at each expert's first row (the last one is shorter); the re-tiled
 operands take power-of-two scales (the pages' rule for activations converted
 from 1x128 to 128x1 tiles, so the conversion adds no scale rounding); the
-re-tiled token operand of dW_gate_up is the forward's dequantised 1x128 input.
+re-tiled token operand of dW_gate_up is the forward's dequantised 1x128 input;
+the combine backward's output dy is rounded to bf16 (the pages keep the combine
+in BF16 in both passes), the other GEMM outputs and SwiGLU backward values stay
+unrounded (the GEMMs output FP32).
 """
 from __future__ import annotations
 
@@ -76,6 +79,13 @@ def requant_cols_pow2(x, offsets):
             codes, scale = _quantize_groups_pow2(x[b0:b1].T)        # one group per column
             out[b0:b1] = (e4m3_decode(codes) * scale.astype(np.float64)[:, None]).T
     return out
+
+
+def round_bf16(x):
+    """Round to the nearest bf16 value (ties to even), via fp32 (exact for the fp32 products that feed it)."""
+    b = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32)).view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return b.view(np.float32).astype(np.float64)
 
 
 def _q1x128(x):
@@ -150,6 +160,7 @@ def layer_backward(cfg, inputs, d_out, pow2_input: bool = False):
         a = u[toks]
         dy = gate[toks, slot][:, None] * dO[toks]
         if fp8:
+            dy = round_bf16(dy)                                    # the combine backward's bf16 output
             wq = quantize_blocks(inputs["w_gate_up"][e]) + quantize_blocks(inputs["w_down"][e])
             y = expert_ffn(a, None, None, "fp8", wq, pow2_input)
             da, dg_w, dd_w = ffn_backward_fp8(a, *wq, dy, pow2_input)

@@ -162,8 +162,9 @@ def test_backward_validation():
                                    FAKE, FAKE, None, FAKE, 1 << 20, None) == B.MOE_E_INVALID
     assert L.moe_ffn_gate_up_cache(ctypes.byref(sh), B.MOE_BF16, 4, 10, FAKE, B.MOE_ROWS_GATHER, FAKE, FAKE, 10,
                                    FAKE, FAKE, FAKE, FAKE, 16, None) == B.MOE_E_WORKSPACE
-    assert L.moe_combine_backward(ctypes.byref(sh), B.MOE_F32, *P(), FAKE, FAKE, FAKE, None) == B.MOE_E_INVALID
-    assert L.moe_combine_backward(ctypes.byref(sh), B.MOE_BF16, *P(), FAKE, None, FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_combine_backward(ctypes.byref(sh), B.MOE_F32, *P(), FAKE, B.MOE_BF16, FAKE, FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_combine_backward(ctypes.byref(sh), B.MOE_BF16, *P(), FAKE, B.MOE_BF16, None, FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_combine_backward(ctypes.byref(sh), B.MOE_BF16, *P(), FAKE, B.MOE_F8E4M3, FAKE, FAKE, None) == B.MOE_E_INVALID
     assert L.moe_route_backward(ctypes.byref(sh), B.MOE_BF16, *P(), *P(), *P(), FAKE, FAKE, 64 * 2 * 4 - 4,
                                 None) == B.MOE_E_WORKSPACE
     assert L.moe_route_backward(ctypes.byref(sh), B.MOE_F8E4M3, *P(), *P(), *P(), FAKE, FAKE, 1 << 20,
@@ -180,3 +181,22 @@ def test_backward_validation():
     assert L.moe_ffn_backward(*args(ws=need - 1)) == B.MOE_E_WORKSPACE
     assert b"workspace" in L.moe_last_error()
     assert L.moe_input_grad(ctypes.byref(sh), FAKE, None, None, FAKE, FAKE, None) == B.MOE_E_INVALID
+
+
+def test_backward_fp8_validation():
+    L = B.lib()
+    sh = _shape()
+    assert L.moe_transpose_bf16(1, 100, 128, FAKE, ctypes.c_void_p(32), None) == B.MOE_E_UNSUPPORTED
+    assert L.moe_transpose_bf16(1, 128, 128, FAKE, FAKE, None) == B.MOE_E_INVALID
+    gu = lambda **o: [ctypes.byref(sh), 4, 10, FAKE, B.MOE_ROWS_GATHER, FAKE, FAKE, FAKE, 10, FAKE, FAKE, FAKE, FAKE,
+                      o.get("gq", FAKE), FAKE, FAKE, o.get("ws", 1 << 20), None]
+    assert L.moe_ffn_gate_up_cache_fp8(*gu(gq=None)) == B.MOE_E_INVALID
+    assert L.moe_ffn_gate_up_cache_fp8(*gu(ws=16)) == B.MOE_E_WORKSPACE
+    need = B.moe_ffn_backward_fp8_workspace_bytes(sh, 10, 4)
+    assert need >= 10 * 256 + 10 * 128 * 4 * 3
+    bw = lambda **o: [ctypes.byref(o.get("sh", sh)), 4, 10, FAKE, B.MOE_ROWS_GATHER, FAKE, FAKE, FAKE, 10, FAKE, FAKE,
+                      FAKE, FAKE, FAKE, FAKE, o.get("dy", FAKE), FAKE, FAKE, FAKE, FAKE, o.get("ws", need), None]
+    assert L.moe_ffn_backward_fp8(*bw(dy=None)) == B.MOE_E_INVALID
+    assert L.moe_ffn_backward_fp8(*bw(ws=need - 1)) == B.MOE_E_WORKSPACE
+    wide = _shape(inter=5248)                                 # 2I > 10240
+    assert L.moe_ffn_backward_fp8(*bw(sh=wide, ws=1 << 40)) == B.MOE_E_UNSUPPORTED

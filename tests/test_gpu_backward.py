@@ -1,8 +1,9 @@
-"""GPU parity of the layer backward (bf16 expert GEMMs) against the fp64 oracle.
+"""GPU parity of the layer backward (bf16 expert GEMMs, and the FP8 recipe) against the fp64 oracle.
 
 The layer runs forward_train + backward through the libmoe backward calls
-(moe_ffn_gate_up_cache, moe_combine_backward, moe_ffn_backward,
-moe_route_backward, moe_input_grad); the oracle recomputes every gradient from
+(moe_ffn_gate_up_cache / moe_ffn_gate_up_cache_fp8, moe_combine_backward,
+moe_ffn_backward / moe_ffn_backward_fp8, moe_route_backward, moe_input_grad);
+the oracle recomputes every gradient from
 the generated inputs and the generated output gradient only. Small workloads
 are compared whole; the DeepSeek-V3-shaped one on sampled experts, tokens and
 weight-gradient rows / columns.
@@ -164,3 +165,102 @@ def test_v3_backward_sampled():
         report(f"c3 d_gate token {t}", rel_l2(layer.d_gate[t], dgate[0]), tol)
         report(f"c3 du token {t}", rel_l2(du[t], acc), tol)
         report(f"c3 du - d_out token {t}", rel_l2(np64(du[t]) - dO[t], acc - dO[t]), tol)
+
+
+# ------------------------------------------------------------------ FP8 recipe
+
+def test_transpose_bf16_exact():
+    w = (torch.randn((3, 256, 384), generator=torch.Generator().manual_seed(5)) * 0.02).to(torch.bfloat16).to(DEV)
+    out = torch.empty((3, 384, 256), dtype=torch.bfloat16, device=DEV)
+    B.moe_transpose_bf16(w, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, w.transpose(1, 2).contiguous())
+
+
+BWD8_CASES = [
+    ("c1", dict(gemm="fp8", act="bf16")),
+    ("c1", dict(gemm="fp8", act="bf16", T=200, inter=384)),     # ragged T, 1.5 tiles of I, 128-row blocks cut short
+    ("c2", dict(gemm="fp8")),
+]
+
+
+@pytest.mark.parametrize("name,over", BWD8_CASES)
+def test_layer_backward_fp8(name, over):
+    cfg = get_config(name, **over)
+    inp = generate(cfg, DEV)
+    d_out = generate_output_grad(cfg, DEV)
+    layer, du = _train_layer(cfg, inp, d_out)
+    res = oracle.layer_backward(cfg, inp, d_out)
+    N, Ns, I, tag = cfg.n_routed, cfg.n_shared, cfg.inter, f"{name}{over}"
+    bad = routing_mismatches(layer.topk_idx, res["route"])
+    ok = np.ones(cfg.T, dtype=bool)
+    ok[bad] = False
+    g_idx = npi(layer.topk_idx)
+    touched = set(g_idx[bad].ravel().tolist()) | set(res["route"]["idx"][bad].ravel().tolist())
+    good_e = np.array([e for e in range(N) if e not in touched], dtype=np.int64)
+    tol = TOL["fp8"]
+    report(f"{tag} fp8 d_gate", rel_l2(np64(layer.d_gate)[ok], res["d_gate"][ok]), tol)
+    report(f"{tag} fp8 du - d_out", rel_l2((np64(du) - np64(d_out))[ok], (res["du"] - np64(d_out))[ok]), tol)
+    report(f"{tag} fp8 d_centroids", rel_l2(np64(layer.grads["centroids"])[good_e], res["d_centroids"][good_e]), tol)
+    report(f"{tag} fp8 dW_gate_up routed",
+           rel_l2(np64(layer.grads["w_gate_up"])[good_e], res["d_w_gate_up"][good_e]), tol)
+    report(f"{tag} fp8 dW_down routed", rel_l2(np64(layer.grads["w_down"])[good_e], res["d_w_down"][good_e]), tol)
+    report(f"{tag} fp8 dW_gate_up shared", rel_l2(np64(layer.grads["s_gate_up"]), res["d_s_gate_up"]), tol)
+    report(f"{tag} fp8 dW_down shared", rel_l2(np64(layer.grads["s_down"]), res["d_s_down"]), tol)
+    # the E4M3 [G, U] cache of the shared expert's rows against the oracle's quantisation of the same products
+    u32 = inp["u"].cpu().float().numpy()
+    a_q = oracle.dequantize_tiles(*oracle.quantize_tiles(u32))
+    wgu = oracle.dequantize_blocks(*oracle.quantize_blocks(inp["s_gate_up"][0].cpu()))
+    codes, scale = oracle.quantize_tiles(np.concatenate([a_q @ wgu[:I].T, a_q @ wgu[I:].T], axis=1))
+    T, K = cfg.T, cfg.topk
+    got_c = layer.gu_cache[T * K:T * K + T].cpu().numpy()
+    got_s = layer.gu_scale[T * K:T * K + T].cpu().numpy()
+    same = float(np.mean(got_c == codes))
+    sdiff = float(np.max(np.abs(got_s / scale - 1)))
+    print(f"[parity] {tag} shared [G, U] cache: codes equal {same:.5f}, max rel scale diff {sdiff:.2e}")
+    assert same > 0.999 and sdiff < 1e-4
+
+
+def test_v3_backward_fp8_sampled():
+    """DeepSeek-V3 shape, FP8 recipe: the weight gradients of two routed experts in full and du on sampled
+    tokens (per-row input gradients: the 1x128 quantisation of a Dgrad input is per row)."""
+    cfg = get_config("c4")
+    inp = generate(cfg, DEV)
+    d_out = generate_output_grad(cfg, DEV)
+    T, K, N = cfg.T, cfg.topk, cfg.n_routed
+    layer, du = _train_layer(cfg, inp, d_out)
+    r = oracle.route(inp["u"], inp["centroids"], inp["bias"], cfg.n_groups, cfg.topk_groups, cfg.group_topn, K)
+    bad = set(routing_mismatches(layer.topk_idx, r).tolist())
+    o_off, o_perm, _ = oracle.permute(r["idx"], N)
+    u64, dO = np64(inp["u"]), np64(d_out)
+    tol = TOL["fp8"]
+    g_idx = npi(layer.topk_idx)
+    load = np.diff(o_off)
+    wq = lambda key, e: oracle.quantize_blocks(inp[key][e].cpu())
+    for e in sorted({int(np.argmin(load)), int(np.argmax(load))}):
+        toks = o_perm[o_off[e]:o_off[e + 1]]
+        if any(t in bad for t in toks) or any(e in g_idx[t] for t in bad):
+            continue
+        slot = np.array([int(np.flatnonzero(r["idx"][t] == e)[0]) for t in toks])
+        dy = oracle.round_bf16(r["gate"][toks, slot][:, None] * dO[toks])       # the combine backward's bf16 rows
+        _, dwg, dwd = oracle.ffn_backward_fp8(u64[toks], *wq("w_gate_up", e), *wq("w_down", e), dy)
+        report(f"c4 fp8 expert {e} ({toks.size} rows) dW_gate_up", rel_l2(layer.grads["w_gate_up"][e], dwg), tol)
+        report(f"c4 fp8 expert {e} dW_down", rel_l2(layer.grads["w_down"][e], dwd), tol)
+    toks = [t for t in np.random.default_rng(2).choice(T, 6, replace=False) if t not in bad][:2]
+    cent = np64(inp["centroids"])
+    sq = (*wq("s_gate_up", 0), *wq("s_down", 0))
+    for t in toks:
+        acc = dO[t].copy()
+        dgate = np.zeros((1, K))
+        for k in range(K):
+            e = int(r["idx"][t, k])
+            q = (*wq("w_gate_up", e), *wq("w_down", e))
+            y = oracle.ffn_fp8(u64[t:t + 1], *q)
+            dgate[0, k] = float(dO[t] @ y[0])
+            acc += oracle.ffn_backward_fp8(u64[t:t + 1], *q, oracle.round_bf16(r["gate"][t, k] * dO[t:t + 1]))[0][0]
+        acc += oracle.ffn_backward_fp8(u64[t:t + 1], *sq, dO[t:t + 1])[0][0]
+        ds = oracle.gate_backward(r["s"][t:t + 1], r["idx"][t:t + 1], dgate)[0]
+        s_sel = r["s"][t, r["idx"][t]]
+        acc += (ds * s_sel * (1.0 - s_sel)) @ cent[r["idx"][t]]
+        report(f"c4 fp8 d_gate token {t}", rel_l2(layer.d_gate[t], dgate[0]), tol)
+        report(f"c4 fp8 du - d_out token {t}", rel_l2(np64(du[t]) - dO[t], acc - dO[t]), tol)

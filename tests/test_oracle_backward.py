@@ -173,3 +173,12 @@ def test_ffn_backward_fp8_error_size():
     for name, g, r_ in zip(("da", "dW_gate_up", "dW_down"), got, ref):
         rel = np.linalg.norm(g - r_) / np.linalg.norm(r_)
         assert 1e-3 < rel < 0.08, (name, rel)
+
+
+def test_round_bf16():
+    """The oracle's bf16 rounding (of the combine backward's output) equals torch's cast on wide-range values."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(50000) * np.exp(rng.standard_normal(50000) * 6)).astype(np.float32)
+    x[:4] = [0.0, -0.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8]               # exact ties round to even
+    ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(oracle.round_bf16(x), ref)
