@@ -39,7 +39,7 @@ METRIC = "MoE-layer fwd tokens/s at V3 shape + % of MFMA peak (bf16, fp8)"
 CALLS = ["route", "permute", "ffn_gate_up", "ffn_down", "combine", "bias_update"]
 CALLS_TRAIN = ["route", "permute", "ffn_gate_up", "ffn_down", "combine", "combine_bwd", "ffn_bwd", "route_bwd",
                "input_grad", "bias_update"]
-METRIC_TRAIN = "MoE-layer fwd+bwd tokens/s (bf16; gradients of u, centroids and expert weights)"
+METRIC_TRAIN = "MoE-layer fwd+bwd tokens/s (gradients of u, centroids and expert weights)"
 
 
 def parse():
@@ -159,6 +159,10 @@ def cpu_baseline_backward(cfg, inp, d_out, n_tok):
     wd = {e: inp["w_down"][e].cpu() for e in need}
     sg = [inp["s_gate_up"][s].cpu() for s in range(cfg.n_shared)]
     sd = [inp["s_down"][s].cpu() for s in range(cfg.n_shared)]
+    fp8 = cfg.gemm == "fp8"
+    if fp8:                                                  # weight blocks quantised before timing
+        wq = {e: oracle.quantize_blocks(wg[e]) + oracle.quantize_blocks(wd[e]) for e in need}
+        sq = [oracle.quantize_blocks(sg[s]) + oracle.quantize_blocks(sd[s]) for s in range(cfg.n_shared)]
     dO = d_out[:n_tok].cpu().double().numpy()
     t0 = time.perf_counter()
     r = oracle.route(u, cent, bias, cfg.n_groups, cfg.topk_groups, cfg.group_topn, cfg.topk)
@@ -169,11 +173,16 @@ def cpu_baseline_backward(cfg, inp, d_out, n_tok):
     for e in need:
         toks = perm[off[e]:off[e + 1]]
         slot = np.array([int(np.flatnonzero(r["idx"][t] == e)[0]) for t in toks])
-        d_gate[toks, slot] = (dO[toks] * oracle.swiglu_ffn(u64[toks], wg[e], wd[e])).sum(axis=1)
-        da, _, _ = oracle.ffn_backward(u64[toks], wg[e], wd[e], r["gate"][toks, slot][:, None] * dO[toks])
+        dy = r["gate"][toks, slot][:, None] * dO[toks]
+        if fp8:
+            d_gate[toks, slot] = (dO[toks] * oracle.ffn_fp8(u64[toks], *wq[e])).sum(axis=1)
+            da = oracle.ffn_backward_fp8(u64[toks], *wq[e], oracle.round_bf16(dy))[0]
+        else:
+            d_gate[toks, slot] = (dO[toks] * oracle.swiglu_ffn(u64[toks], wg[e], wd[e])).sum(axis=1)
+            da = oracle.ffn_backward(u64[toks], wg[e], wd[e], dy)[0]
         np.add.at(du, toks, da)
     for s in range(cfg.n_shared):
-        du += oracle.ffn_backward(u64, sg[s], sd[s], dO)[0]
+        du += (oracle.ffn_backward_fp8(u64, *sq[s], dO)[0] if fp8 else oracle.ffn_backward(u64, sg[s], sd[s], dO)[0])
     ds = oracle.gate_backward(r["s"], r["idx"], d_gate)
     s_sel = np.take_along_axis(r["s"], r["idx"], axis=1)
     dz = ds * s_sel * (1.0 - s_sel)
@@ -191,7 +200,7 @@ def cpu_baseline_backward(cfg, inp, d_out, n_tok):
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
             "sample": f"first {n_tok} tokens of the same {cfg.name} batch: routing, the forward of the "
                       f"{len(need)} touched routed experts (for the gate gradients), their and the {cfg.n_shared} "
-                      f"shared experts' FFN backward, gate / centroid / input gradients in fp64 (NumPy); "
+                      f"shared experts' FFN backward ({cfg.gemm} recipe), gate / centroid / input gradients in fp64 (NumPy); "
                       f"{dt:.1f} s wall", "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -235,24 +244,29 @@ def main_backward(args, cfg):
                 for j, c in enumerate(CALLS_TRAIN)}
     T, d, I, K, N, Ns = cfg.T, cfg.d, cfg.inter, cfg.topk, cfg.n_routed, cfg.n_shared
     rows = T * (K + Ns)
-    # dominant call: moe_ffn_backward, four GEMMs over every row (dh, da, dW_down, dW_gate_up)
-    bwd_flops = 2.0 * rows * d * I * (1 + 2 + 1 + 2)
+    # dominant call: the FFN backward, four GEMMs over every row (dh, da: Dgrad; dW_down, dW_gate_up: Wgrad).
+    # fp8: the Dgrad GEMMs run on the fp8 MFMA, the Wgrad GEMMs on the bf16 MFMA (their re-tiled E4M3 operands
+    # are exact in bf16), so the peak is the mix of the two rates over this FLOP split.
+    dgrad_flops, wgrad_flops = 2.0 * rows * d * I * 3, 2.0 * rows * d * I * 3
+    bwd_flops = dgrad_flops + wgrad_flops
     bwd_s = per_call["ffn_bwd"] / 1e3
-    roof = {"bound": "mfma", "achieved": bwd_flops / bwd_s / 1e12, "peak": MFMA_PEAK["bf16"] / 1e12,
-            "unit": "TFLOP/s", "frac": bwd_flops / bwd_s / MFMA_PEAK["bf16"], "traffic": None,
-            "kernel": "moe_ffn_backward (dh, SwiGLU backward, da, dW_down, dW_gate_up)"}
+    peak = bwd_flops / (dgrad_flops / MFMA_PEAK[cfg.gemm] + wgrad_flops / MFMA_PEAK["bf16"])
+    roof = {"bound": "mfma", "achieved": bwd_flops / bwd_s / 1e12, "peak": peak / 1e12,
+            "unit": "TFLOP/s", "frac": bwd_flops / bwd_s / peak, "traffic": None,
+            "kernel": ("moe_ffn_backward_fp8" if cfg.gemm == "fp8" else "moe_ffn_backward")
+                      + " (dh, SwiGLU backward, da, dW_down, dW_gate_up)"}
     fwd_flops = cfg.ffn_flops()
     calls = {c: {"ms": round(per_call[c], 4)} for c in CALLS_TRAIN}
     res = {
         "metric": METRIC_TRAIN, "value": T / (ms_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.gemm,
         "data": "synthetic: seeded N(0,1) tokens and output gradient, random-init N(0,0.02^2) weights",
         "config": {"workload": f"{cfg.name}: {cfg.description}, forward + backward", "T": T, "d": d,
-                   "n_routed": N, "topk": K, "n_shared": Ns, "inter": I, "gemm": "bf16"},
+                   "n_routed": N, "topk": K, "n_shared": Ns, "inter": I, "gemm": cfg.gemm},
         "roofline": roof,
         "train_step": {"TFLOP/s": (fwd_flops + bwd_flops) / (ms_step / 1e3) / 1e12,
-                       "roofline_ms": (fwd_flops + bwd_flops + cfg.router_flops()) / MFMA_PEAK["bf16"] * 1e3},
+                       "roofline_ms": ((fwd_flops + cfg.router_flops()) / MFMA_PEAK[cfg.gemm] + bwd_flops / peak) * 1e3},
         "calls": calls,
     }
     res["train_step"]["frac_of_roofline"] = res["train_step"]["roofline_ms"] / ms_step
@@ -269,8 +283,8 @@ def main():
     if args.backward:
         from moe_inputs import get_config as _gc
         cfg = _gc(args.config)
-        if cfg.gemm != "bf16" or args.mxfp4 or args.pow2_act_scales or args.batch_invariant:
-            print("bench.py: --backward runs the bf16 workloads (c2, c3) only", file=sys.stderr)
+        if cfg.gemm not in ("bf16", "fp8") or args.mxfp4 or args.pow2_act_scales or args.batch_invariant:
+            print("bench.py: --backward runs the bf16 (c2, c3) and fp8 (c4, c5) workloads", file=sys.stderr)
             sys.exit(2)
         main_backward(args, cfg)
         return

@@ -69,21 +69,40 @@ __device__ __forceinline__ float2 load_pair(const float* p) { return *reinterpre
 __device__ __forceinline__ float load_one(const uint16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float load_one(const float* p) { return *p; }
 
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// 16 lanes per (row, 128-column tile), 8 consecutive values per lane.
 template <class X>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(long long n_tiles, const X* __restrict__ x,
                                                             uint8_t* __restrict__ codes, float* __restrict__ scales) {
-  const int l = threadIdx.x & 63;
-  for (long long t = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) >> 6; t < n_tiles;
-       t += static_cast<long long>(gridDim.x) * 4) {
-    const size_t o = static_cast<size_t>(t) * 128 + 2 * l;             // row-major: tile t = row t / (C/128)
-    const float2 v = load_pair(x + o);
-    const float a = v.x, b = v.y;
-    float m = fmaxf(__builtin_fabsf(a), __builtin_fabsf(b));
+  const int l = threadIdx.x & 15;
+  for (long long t = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) >> 4; t < n_tiles;
+       t += static_cast<long long>(gridDim.x) * 16) {
+    const size_t o = static_cast<size_t>(t) * 128 + 8 * l;             // row-major: tile t = row t / (C/128)
+    float v[8];
+    load8(x + o, v);
+    float m = 0.0f;
 #pragma unroll
-    for (int s = 32; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[i]));
+#pragma unroll
+    for (int s = 8; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 16));
     const float inv = m > 0.0f ? kE4M3Max / m : 0.0f;
-    *reinterpret_cast<uint16_t*>(codes + o) =
-        static_cast<uint16_t>(f32_to_e4m3(a * inv) | (f32_to_e4m3(b * inv) << 8));
+    uint32_t c[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i >> 2] |= f32_to_e4m3(v[i] * inv) << (8 * (i & 3));
+    *reinterpret_cast<uint2*>(codes + o) = make_uint2(c[0], c[1]);
     if (l == 0) scales[t] = m > 0.0f ? m / kE4M3Max : 1.0f;
   }
 }
@@ -121,8 +140,18 @@ __global__ void row_block_prefix_kernel(int E, int n_rows, const int32_t* __rest
   pre[E] = acc;
 }
 
-// A block per (128-row block, 256 columns): thread = column. The source is bf16 rows of x (row r, DIRECT) or,
-// with GATHERED, E4M3 codes with their 1x128 fp32 scales at the row's source row (row_src / segment / direct).
+// A block per (128-row block, 1024 columns): each thread 4 adjacent columns. The source is bf16 / fp32 rows of x
+// (row r, DIRECT) or, with GATHERED, E4M3 codes with their 1x128 fp32 scales at the row's source row.
+__device__ __forceinline__ void load4(const uint16_t* p, float (&v)[4]) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+
 template <bool GATHERED, class X>
 __global__ __launch_bounds__(256) void requant_cols_kernel(int C, int E, int n_rows, const int32_t* __restrict__ off,
                                                            const int* __restrict__ pre, moe_row_mode mode,
@@ -130,8 +159,8 @@ __global__ __launch_bounds__(256) void requant_cols_kernel(int C, int E, int n_r
                                                            const X* __restrict__ x,
                                                            const uint8_t* __restrict__ xq,
                                                            const float* __restrict__ xs, uint16_t* __restrict__ out) {
-  const int ncc = cdiv(C, 256);
-  const int j = blockIdx.x / ncc, c = (blockIdx.x % ncc) * 256 + threadIdx.x;
+  const int ncc = cdiv(C, 1024);
+  const int j = blockIdx.x / ncc, c = (blockIdx.x % ncc) * 1024 + 4 * threadIdx.x;
   if (j >= pre[E]) return;
   int lo_e = 0, hi_e = E;                               // the expert e with pre[e] <= j < pre[e + 1]
   while (hi_e - lo_e > 1) {
@@ -143,18 +172,40 @@ __global__ __launch_bounds__(256) void requant_cols_kernel(int C, int E, int n_r
   const int lo = clampi(off[e], 0, n_rows), hi = clampi(off[e + 1], lo, n_rows);
   const int b0 = lo + 128 * (j - pre[e]), b1 = min(b0 + 128, hi);
   if (c >= C) return;
-  auto value = [&](int r) -> float {
-    if (!GATHERED) return load_one(x + static_cast<size_t>(r) * C + c);
+  auto values = [&](int r, float (&v)[4]) {
+    if (!GATHERED) {
+      load4(x + static_cast<size_t>(r) * C + c, v);
+      return;
+    }
     const int sr = source_row(mode, row_src, r, lo, a_rows);
-    if (sr < 0) return 0.0f;
-    return e4m3_value(xq[static_cast<size_t>(sr) * C + c]) * xs[static_cast<size_t>(sr) * (C / 128) + c / 128];
+    if (sr < 0) {
+      v[0] = v[1] = v[2] = v[3] = 0.0f;
+      return;
+    }
+    const uint32_t q = *reinterpret_cast<const uint32_t*>(xq + static_cast<size_t>(sr) * C + c);
+    const float sc = xs[static_cast<size_t>(sr) * (C / 128) + c / 128];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = e4m3_value((q >> (8 * i)) & 0xFFu) * sc;
   };
-  float amax = 0.0f;
-  for (int r = b0; r < b1; ++r) amax = fmaxf(amax, __builtin_fabsf(value(r)));
-  const int n = amax > 0.0f ? pow2_scale_exp(amax) : 0;
+  float amax[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int r = b0; r < b1; ++r) {
-    const float q = amax > 0.0f ? e4m3_value(f32_to_e4m3(__builtin_ldexpf(value(r), -n))) : 0.0f;
-    out[static_cast<size_t>(r) * C + c] = f32_to_bf16(__builtin_ldexpf(q, n));
+    float v[4];
+    values(r, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax[i] = fmaxf(amax[i], __builtin_fabsf(v[i]));
+  }
+  int n[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) n[i] = amax[i] > 0.0f ? pow2_scale_exp(amax[i]) : 0;
+  for (int r = b0; r < b1; ++r) {
+    float v[4];
+    values(r, v);
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = amax[i] > 0.0f ? __builtin_ldexpf(e4m3_value(f32_to_e4m3(__builtin_ldexpf(v[i], -n[i]))), n[i]) : 0.0f;
+    *reinterpret_cast<uint2*>(out + static_cast<size_t>(r) * C + c) = make_uint2(pack_bf16x2(o[0], o[1]),
+                                                                                 pack_bf16x2(o[2], o[3]));
   }
 }
 
@@ -172,7 +223,7 @@ hipError_t launch_transpose_rows_bf16(int n_mats, int rows, int cols, const void
 hipError_t launch_quantize_rows(long long n_rows, int cols, const void* x, bool f32_in, void* codes, float* scales,
                                 hipStream_t st) {
   const long long tiles = n_rows * (cols / 128);
-  const dim3 g(static_cast<unsigned>(grid_cap8(cdiv(tiles, 4))));
+  const dim3 g(static_cast<unsigned>(grid_cap8(cdiv(tiles, 16))));
   if (f32_in)
     hipLaunchKernelGGL(quantize_rows_kernel<float>, g, dim3(256), 0, st, tiles, static_cast<const float*>(x),
                        static_cast<uint8_t*>(codes), scales);
@@ -199,7 +250,7 @@ hipError_t launch_row_block_prefix(int E, int n_rows, const int32_t* off, int* p
 hipError_t launch_requant_cols(int C, int E, int n_rows, const int32_t* off, const int* pre, moe_row_mode mode,
                                const int32_t* row_src, int a_rows, const void* x, bool f32_in, const void* xq,
                                const float* xs, void* out, hipStream_t st) {
-  const long long blocks = (static_cast<long long>(n_rows) / 128 + E) * cdiv(C, 256);   // covers every 128-row block
+  const long long blocks = (static_cast<long long>(n_rows) / 128 + E) * cdiv(C, 1024);  // covers every 128-row block
   const dim3 g(static_cast<unsigned>(blocks));
   uint16_t* o = static_cast<uint16_t*>(out);
   if (xq != nullptr)
