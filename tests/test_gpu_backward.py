@@ -49,6 +49,8 @@ BWD_CASES = [
     ("c1", dict(gemm="bf16", act="bf16")),
     ("c1", dict(gemm="bf16", act="bf16", T=200, inter=384)),     # ragged T, 1.5 tiles of I
     ("c2", {}),
+    # the decode batch's Zipf-skewed routing (no group limit, top-6): hot experts and many empty ones
+    ("c5", dict(gemm="bf16", T=96, d=512, inter=256, n_routed=64)),
 ]
 
 
@@ -181,6 +183,7 @@ BWD8_CASES = [
     ("c1", dict(gemm="fp8", act="bf16")),
     ("c1", dict(gemm="fp8", act="bf16", T=200, inter=384)),     # ragged T, 1.5 tiles of I, 128-row blocks cut short
     ("c2", dict(gemm="fp8")),
+    ("c5", dict(T=96, d=512, inter=256, n_routed=64)),            # Zipf-skewed, empty experts
 ]
 
 
