@@ -91,6 +91,48 @@ def recorded_traffic(kernel: str, workload: str, gemm: str):
     return None
 
 
+def measure_peaks(dev):
+    """MFMA (bf16, E4M3) and device-copy rates of this GPU from the library's probes, timed with HIP events."""
+    import torch
+    from mixture_experts_layer_gate_amd import binding as B
+    seed = torch.arange(1, 65, dtype=torch.int32, device=dev)
+    out = torch.empty(B.moe_probe_blocks() * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, dt, flop in (("mfma_bf16", B.MOE_BF16, 32768), ("mfma_fp8", B.MOE_F8E4M3, 131072)):
+        B.moe_probe_mfma(dt, 100, seed, out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        iters = 4000
+        e0.record(stream)
+        B.moe_probe_mfma(dt, iters, seed, out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name + "_TFLOP/s"] = B.moe_probe_blocks() * 4 * iters * 8 * flop / (e0.elapsed_time(e1) / 1e3) / 1e12
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    B.moe_probe_copy(src, dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        B.moe_probe_copy(src, dst)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res["hbm_copy_GB/s"] = 5 * 2 * src.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del dst
+    big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)      # 4 GiB: far past the 256 MB Infinity Cache
+    acc = torch.empty(int(B.lib().moe_probe_read_blocks()) * 256, dtype=torch.int32, device=dev)
+    B.moe_probe_read(big, acc)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        B.moe_probe_read(big, acc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res["hbm_read_GB/s"] = 3 * big.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, big
+    return res
+
+
 def touched_experts(load):
     return int((load > 0).sum())
 
@@ -395,6 +437,15 @@ def main():
         "calls": calls,
     }
     res["layer"]["frac_of_roofline"] = res["layer"]["roofline_ms"] / ms_step
+    steps_ms = sorted(sum(events[i][j].elapsed_time(events[i][j + 1]) for j in range(len(CALLS)))
+                      for i in range(args.steps))
+    pct = lambda q: steps_ms[min(len(steps_ms) - 1, int(q * (len(steps_ms) - 1) + 0.5))]
+    res["step_ms_events"] = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
+    peaks = measure_peaks(dev)
+    res["peaks_measured"] = peaks
+    roof["peak_measured"] = (peaks["hbm_read_GB/s"] if roof["bound"] == "hbm"
+                             else peaks["mfma_fp8_TFLOP/s" if cfg.gemm in ("fp8", "mxfp4") else "mfma_bf16_TFLOP/s"])
+    roof["frac_of_measured"] = roof["achieved"] / roof["peak_measured"]
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, layer, args.cpu_sample)
     else:

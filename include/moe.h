@@ -413,6 +413,23 @@ moe_status moe_ffn_backward_fp8(const moe_shape* shape, int32_t n_experts, int32
                                 float* dw_gate_up, float* dw_down, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * ---- Peak probes (measurement only, not on the layer's path): the roofline
+ * figures report the published MI355X peaks beside these measured ones.
+ * moe_probe_mfma -- moe_probe_blocks() workgroups of 4 waves, each wave issuing
+ * iters x 8 independent MFMAs (MOE_BF16: 32x32x16, 32768 FLOP each;
+ * MOE_F8E4M3: 32x32x64 E4M3, 131072 FLOP each) on register operands; seed: 64
+ * int32 (operand bits); out: moe_probe_blocks() * 256 floats (written).
+ * moe_probe_copy -- dst = src, bytes a multiple of 16 (16 bytes per lane).
+ * moe_probe_read -- reads bytes (a multiple of 16) of src; out: moe_probe_read_blocks()
+ * * 256 uint32 (written).
+ */
+int32_t moe_probe_blocks(void);
+moe_status moe_probe_mfma(moe_dtype dtype, int32_t iters, const int32_t* seed, float* out, void* stream);
+moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+int32_t moe_probe_read_blocks(void);
+moe_status moe_probe_read(const void* src, size_t bytes, uint32_t* out, void* stream);
+
+/*
  * moe_tile_weights_bf16 -- copies bf16 expert weights into the tiled layout of
  * MOE_BF16_TILED, in which every 32-wide K step of a 256-row tile is one
  * contiguous 16 KB block (the grouped FFN's load pattern). n_mats matrices

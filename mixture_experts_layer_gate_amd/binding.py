@@ -66,6 +66,11 @@ _SIGS = {
     "moe_ffn_backward": [_S, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_input_grad": [_S, _P, _P, _P, _P, _P, _P],
     "moe_transpose_bf16": [_I, _I, _I, _P, _P, _P],
+    "moe_probe_blocks": [],
+    "moe_probe_mfma": [_I, _I, _P, _P, _P],
+    "moe_probe_copy": [_P, _P, ctypes.c_size_t, _P],
+    "moe_probe_read_blocks": [],
+    "moe_probe_read": [_P, ctypes.c_size_t, _P, _P],
     "moe_ffn_gate_up_cache_fp8": [_S, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_ffn_backward_fp8_workspace_bytes": [_S, _I, _I],
     "moe_ffn_backward_fp8": [_S, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -404,3 +409,25 @@ def moe_ffn_backward_fp8(shape: moe_shape, n_experts: int, n_rows: int, expert_o
                                       _ptr(gu_scale), _ptr(w_gate_up_t), _ptr(w_gate_up_t_scale), _ptr(w_down_t),
                                       _ptr(w_down_t_scale), _ptr(dy), _ptr(da), _ptr(dw_gate_up), _ptr(dw_down),
                                       _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+# ---------------------------------------------------------------- peak probes
+
+def moe_probe_blocks() -> int:
+    return int(lib().moe_probe_blocks())
+
+
+def moe_probe_mfma(dtype: int, iters: int, seed, out, stream=None):
+    _need(seed, 64, "seed"); _need(out, moe_probe_blocks() * 256, "out")
+    _check(lib().moe_probe_mfma(dtype, iters, _ptr(seed), _ptr(out), _stream(stream)))
+
+
+def moe_probe_copy(src, dst, stream=None):
+    n = src.numel() * src.element_size()
+    _need(dst, dst.numel(), "dst")
+    _check(lib().moe_probe_copy(_ptr(src), _ptr(dst), n, _stream(stream)))
+
+
+def moe_probe_read(src, out, stream=None):
+    _need(out, int(lib().moe_probe_read_blocks()) * 256, "out")
+    _check(lib().moe_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(out), _stream(stream)))

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "route.hip", "permute.hip", "combine.hip", "ffn_f32.hip", "ffn_bf16.hip",
-           "ffn_fp8.hip", "ffn_fp4.hip", "quant.hip", "balance.hip", "backward.hip", "backward_fp8.hip", "wgrad.hip"]
+           "ffn_fp8.hip", "ffn_fp4.hip", "quant.hip", "balance.hip", "backward.hip", "backward_fp8.hip", "wgrad.hip", "probe.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # no packed fp32 instructions in device code
