@@ -200,3 +200,12 @@ def test_backward_fp8_validation():
     assert L.moe_ffn_backward_fp8(*bw(ws=need - 1)) == B.MOE_E_WORKSPACE
     wide = _shape(inter=5248)                                 # 2I > 10240
     assert L.moe_ffn_backward_fp8(*bw(sh=wide, ws=1 << 40)) == B.MOE_E_UNSUPPORTED
+
+
+def test_probe_validation():
+    L = B.lib()
+    assert L.moe_probe_mfma(B.MOE_F32, 10, FAKE, FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_probe_mfma(B.MOE_BF16, 0, FAKE, FAKE, None) == B.MOE_E_INVALID
+    assert L.moe_probe_copy(FAKE, FAKE, 1 << 20, None) == B.MOE_E_INVALID          # in place
+    assert L.moe_probe_copy(FAKE, ctypes.c_void_p(0x2000), 24, None) == B.MOE_E_INVALID
+    assert L.moe_probe_read(FAKE, 24, FAKE, None) == B.MOE_E_INVALID
