@@ -58,6 +58,8 @@ ROUTE_CASES = [
     ("c2", dict(n_routed=68, n_groups=4, topk_groups=2)),   # 17-expert groups: the LDS form of the selection
     ("c3", {}),
     ("c5", {}),                                             # 384 experts, no group limit: 6 per lane
+    # the supported maxima: 1024 experts in 64 groups, top-16 of 8 groups, 4-term group scores; ragged T
+    ("c2", dict(T=300, d=256, inter=128, n_routed=1024, n_groups=64, topk_groups=8, group_topn=4, topk=16)),
 ]
 
 
@@ -738,6 +740,37 @@ def test_grouped_ffn_fp8_tile_shapes(inter, mode):
         sdiff = np.max(np.abs(hs[lo:hi].cpu().numpy() / aux["h_scale"] - 1))
         print(f"[parity] expert {e}: H codes equal {same:.4f}, max rel scale diff {sdiff:.2e}")
         assert same > 0.99 and sdiff < 1e-4
+
+
+@pytest.mark.parametrize("d,inter", [(10240, 256), (256, 10240)])
+def test_grouped_ffn_fp8_max_k(d, inter):
+    """fp8 at the largest supported K, 10240 = 80 chunks of 128: in the gate/up projection (d) and in the down
+    projection (inter), with an empty expert between two ragged ones."""
+    cfg = get_config("c2", gemm="fp8", n_routed=3, n_groups=1, topk_groups=1, T=256, topk=1, d=d, inter=inter)
+    inp = generate(cfg, DEV)
+    sh = B.moe_shape.of(cfg)
+    sizes = [77, 0, 179]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    src = np.random.default_rng(31).integers(0, cfg.T, n)
+    u32 = inp["u"].cpu().float().numpy()
+    uq, us = oracle.quantize_tiles(u32)
+    wq = [_oracle_wq(inp, e) for e in range(cfg.n_routed)]
+    dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    wgu = dev8(np.stack([tile_e4m3(w[0], True) for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
+    wdn = dev8(np.stack([tile_e4m3(w[2], False) for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
+    h = torch.empty((n, inter), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((n, inter // 128), dtype=torch.float32, device=DEV)
+    y = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    B.moe_ffn_gate_up(sh, B.MOE_F8E4M3, cfg.n_routed, n, _i32(off), B.MOE_ROWS_GATHER, _i32(src), dev8(uq), dev8(us),
+                      cfg.T, wgu, wgs, h, hs, ws)
+    B.moe_ffn_down(sh, B.MOE_F8E4M3, cfg.n_routed, n, _i32(off), h, hs, wdn, wds, y, ws)
+    torch.cuda.synchronize()
+    for e in (0, 2):
+        lo, hi = off[e], off[e + 1]
+        ref = oracle.ffn_fp8(u32[src[lo:hi]], *wq[e])
+        report(f"fp8 d={d} I={inter} expert {e} ({hi - lo} rows) y", rel_l2(y[lo:hi], ref), TOL["fp8"])
 
 
 @pytest.mark.parametrize("d", [384, 640])
