@@ -313,8 +313,8 @@ moe_status moe_combine_backward(const moe_shape* shape, moe_dtype io, const void
  * affinity (eq. (15)): per token, over its selected experts (S = sum of their
  * s), ds_k = (d_gate_k - sum_j g_j d_gate_j) / S and dz_k = ds_k s_k (1 - s_k);
  *   du_router [T, d] fp32 = sum_k dz_k e_{idx_k};
- *   d_centroids [N_r, d] fp32: row e = sum over expert e's permuted rows r (in
- *   row order) of dz(r) * u[perm_token[r]] (zero for experts without rows).
+ *   d_centroids [N_r, d] fp32: row e = sum over expert e's permuted rows r (in a
+ *   fixed order) of dz(r) * u[perm_token[r]] (zero for experts without rows).
  * scores, topk_idx, expert_offsets, perm_token and row_of are the forward's.
  * workspace: at least T*K*4 bytes.
  */

@@ -111,8 +111,9 @@ __global__ __launch_bounds__(256) void route_backward_token_kernel(int T, int d,
   }
 }
 
-// d_centroids[e][c] = sum over the rows r of expert e (in row order) of
-// dz_row[r] * u[perm_token[r]][c]; a block per (expert, 256 columns).
+// d_centroids[e][c] = sum over the rows r of expert e of dz_row[r] * u[perm_token[r]][c]; a block per (expert,
+// 256 columns). Four rows are loaded at a time into four partial sums (rows r = 4i + j go to sum j), added in the
+// order 0..3 at the end: a fixed order, so the result is deterministic.
 __global__ __launch_bounds__(256) void centroid_grad_kernel(int T, int d, int N, int n_rows, int act_bf16,
                                                             const void* __restrict__ u,
                                                             const int32_t* __restrict__ off,
@@ -122,15 +123,24 @@ __global__ __launch_bounds__(256) void centroid_grad_kernel(int T, int d, int N,
   const int e = blockIdx.x / nc, c = (blockIdx.x % nc) * 256 + threadIdx.x;
   if (e >= N || c >= d) return;
   const int lo = clampi(off[e], 0, n_rows), hi = clampi(off[e + 1], lo, n_rows);
-  float acc = 0.0f;
-  for (int r = lo; r < hi; ++r) {
+  auto term = [&](int r) -> float {
     const int t = perm_token[r];
-    if (t < 0 || t >= T) continue;
+    if (t < 0 || t >= T) return 0.0f;
     const size_t o = static_cast<size_t>(t) * d + c;
     const float uv = act_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(u)[o]) : static_cast<const float*>(u)[o];
-    acc = fmaf(dz_row[r], uv, acc);
+    return dz_row[r] * uv;
+  };
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int r = lo;
+  for (; r + 4 <= hi; r += 4) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = term(r + j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += v[j];
   }
-  dcent[static_cast<size_t>(e) * d + c] = acc;
+  for (int j = 0; r < hi; ++r, ++j) acc[j] += term(r);
+  dcent[static_cast<size_t>(e) * d + c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // Elementwise over [n_rows, I]: dGU = [dh U SiLU'(G) | dh SiLU(G)] and h = SiLU(G) U.
@@ -151,7 +161,18 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(long long n, int I
   }
 }
 
-// du[t] = d_out[t] + du_router[t] + sum_k da[row_of(t, k)] + sum_s da[T K + s T + t], fp32.
+// du[t] = d_out[t] + du_router[t] + sum_k da[row_of(t, k)] + sum_s da[T K + s T + t], fp32; a block per token,
+// 8 consecutive columns per thread (16-byte loads of the bf16 rows).
+__device__ __forceinline__ void add_bf16x8(float (&a)[8], const uint16_t* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[2 * i] += __uint_as_float(w[i] << 16);
+    a[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
 __global__ __launch_bounds__(256) void input_grad_kernel(int T, int d, int K, int Ns, const uint16_t* __restrict__ dout,
                                                          const float* __restrict__ du_router,
                                                          const uint16_t* __restrict__ da,
@@ -159,15 +180,21 @@ __global__ __launch_bounds__(256) void input_grad_kernel(int T, int d, int K, in
                                                          float* __restrict__ du) {
   const int t = blockIdx.x;
   if (t >= T) return;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+  for (int c = 8 * threadIdx.x; c < d; c += 8 * blockDim.x) {
     const size_t o = static_cast<size_t>(t) * d + c;
-    float acc = bf16_to_f32(dout[o]) + (du_router ? du_router[o] : 0.0f);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    add_bf16x8(acc, dout + o);
+    if (du_router) {
+      const float4 a = reinterpret_cast<const float4*>(du_router + o)[0], b = reinterpret_cast<const float4*>(du_router + o)[1];
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w; acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
     for (int k = 0; k < K; ++k) {
       const int r = row_of[static_cast<size_t>(t) * K + k];
-      if (r >= 0 && r < n_rows) acc += bf16_to_f32(da[static_cast<size_t>(r) * d + c]);
+      if (r >= 0 && r < n_rows) add_bf16x8(acc, da + static_cast<size_t>(r) * d + c);
     }
-    for (int s = 0; s < Ns; ++s) acc += bf16_to_f32(da[(static_cast<size_t>(T) * K + static_cast<size_t>(s) * T + t) * d + c]);
-    du[o] = acc;
+    for (int s = 0; s < Ns; ++s) add_bf16x8(acc, da + (static_cast<size_t>(T) * K + static_cast<size_t>(s) * T + t) * d + c);
+    reinterpret_cast<float4*>(du + o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4*>(du + o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
