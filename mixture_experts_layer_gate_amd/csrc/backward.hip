@@ -24,37 +24,52 @@
 
 namespace moe {
 
-// One wavefront per token; lanes stride over d in pairs of bf16. DY: uint16_t
-// (bf16 rows) or float (fp32 rows, the input of the FP8 backward's quantisers).
-__device__ __forceinline__ void store_pair(uint32_t* p, int c, float a, float b) { p[c] = pack_bf16x2(a, b); }
-__device__ __forceinline__ void store_pair(float* p, int c, float a, float b) {
-  *reinterpret_cast<float2*>(p + 2 * c) = make_float2(a, b);
+// DY: uint16_t (bf16 rows) or float (fp32 rows).
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float (&f)[8]) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                                            pack_bf16x2(f[6], f[7]));
+}
+__device__ __forceinline__ void store8(float* p, const float (&f)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
 }
 
+// One wavefront per token, 8 consecutive columns per lane and step (16-byte loads).
 template <class DY>
 __global__ __launch_bounds__(256) void combine_backward_kernel(int T, int d, int K, int Ns, const uint16_t* __restrict__ dout,
                                                                const uint16_t* __restrict__ y,
                                                                const int32_t* __restrict__ row_of,
                                                                const float* __restrict__ gate, DY* __restrict__ dy,
                                                                float* __restrict__ dgate, int n_rows) {
-  using Row = typename std::conditional<sizeof(DY) == 2, uint32_t, float>::type;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   for (int t = blockIdx.x * 4 + w; t < T; t += gridDim.x * 4) {
-    const uint32_t* o = reinterpret_cast<const uint32_t*>(dout + static_cast<size_t>(t) * d);
+    const uint16_t* o = dout + static_cast<size_t>(t) * d;
     for (int k = 0; k < K; ++k) {
       const int r = row_of[static_cast<size_t>(t) * K + k];
       const bool ok = r >= 0 && r < n_rows;
       const float g = gate[static_cast<size_t>(t) * K + k];
       float dot = 0.0f;
       if (ok) {
-        const uint32_t* yr = reinterpret_cast<const uint32_t*>(y + static_cast<size_t>(r) * d);
-        Row* dr = reinterpret_cast<Row*>(dy + static_cast<size_t>(r) * d);
-        for (int c = l; c < d / 2; c += 64) {
-          const uint32_t ov = o[c], yv = yr[c];
-          const float o0 = __uint_as_float(ov << 16), o1 = __uint_as_float(ov & 0xFFFF0000u);
-          dot = fmaf(o0, __uint_as_float(yv << 16), dot);
-          dot = fmaf(o1, __uint_as_float(yv & 0xFFFF0000u), dot);
-          store_pair(dr, c, g * o0, g * o1);
+        const uint16_t* yr = y + static_cast<size_t>(r) * d;
+        DY* dr = dy + static_cast<size_t>(r) * d;
+        for (int c = 8 * l; c < d; c += 512) {
+          float of[8], yf[8], df[8];
+          unpack8(*reinterpret_cast<const uint4*>(o + c), of);
+          unpack8(*reinterpret_cast<const uint4*>(yr + c), yf);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            dot = fmaf(of[i], yf[i], dot);
+            df[i] = g * of[i];
+          }
+          store8(dr + c, df);
         }
       }
 #pragma unroll
@@ -62,8 +77,12 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(int T, int d, int
       if (l == 0) dgate[static_cast<size_t>(t) * K + k] = ok ? dot : 0.0f;
     }
     for (int s = 0; s < Ns; ++s) {
-      Row* dr = reinterpret_cast<Row*>(dy + (static_cast<size_t>(T) * K + static_cast<size_t>(s) * T + t) * d);
-      for (int c = l; c < d / 2; c += 64) store_pair(dr, c, __uint_as_float(o[c] << 16), __uint_as_float(o[c] & 0xFFFF0000u));
+      DY* dr = dy + (static_cast<size_t>(T) * K + static_cast<size_t>(s) * T + t) * d;
+      for (int c = 8 * l; c < d; c += 512) {
+        float of[8];
+        unpack8(*reinterpret_cast<const uint4*>(o + c), of);
+        store8(dr + c, of);
+      }
     }
   }
 }
@@ -94,19 +113,35 @@ __global__ __launch_bounds__(256) void route_backward_token_kernel(int T, int d,
       if (r >= 0 && r < T * K) dz_row[r] = dz;
     }
     float* du = du_router + static_cast<size_t>(t) * d;
-    for (int c = l; c < d; c += 64) {
-      float acc = 0.0f;
-      for (int j = 0; j < K; ++j) {
-        const int ej = __shfl(e, j, 64);
-        const float dzj = __shfl(dz, j, 64);
+    int es[16];                                              // the picks, read by every lane before the column loop
+    float dzs[16];                                           // (K <= 16), so no shuffle runs under a partial mask
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      es[j] = __shfl(e, j < K ? j : 0, 64);
+      dzs[j] = __shfl(dz, j < K ? j : 0, 64);
+    }
+    for (int c = 8 * l; c < d; c += 512) {                   // 8 consecutive columns per lane
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j >= K) break;
+        const int ej = es[j];
+        const float dzj = dzs[j];
         if (ej >= 0 && ej < N) {
           const size_t off = static_cast<size_t>(ej) * d + c;
-          const float ev = act_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(cent)[off])
-                                    : static_cast<const float*>(cent)[off];
-          acc = fmaf(dzj, ev, acc);
+          float ev[8];
+          if (act_bf16) {
+            unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(cent) + off), ev);
+          } else {
+            const float4 a = reinterpret_cast<const float4*>(static_cast<const float*>(cent) + off)[0];
+            const float4 b = reinterpret_cast<const float4*>(static_cast<const float*>(cent) + off)[1];
+            ev[0] = a.x; ev[1] = a.y; ev[2] = a.z; ev[3] = a.w; ev[4] = b.x; ev[5] = b.y; ev[6] = b.z; ev[7] = b.w;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(dzj, ev[i], acc[i]);
         }
       }
-      du[c] = acc;
+      store8(du + c, acc);
     }
   }
 }
