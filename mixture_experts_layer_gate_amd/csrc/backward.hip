@@ -178,21 +178,31 @@ __global__ __launch_bounds__(256) void centroid_grad_kernel(int T, int d, int N,
   dcent[static_cast<size_t>(e) * d + c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-// Elementwise over [n_rows, I]: dGU = [dh U SiLU'(G) | dh SiLU(G)] and h = SiLU(G) U.
-__global__ __launch_bounds__(256) void swiglu_backward_kernel(long long n, int I, const uint16_t* __restrict__ dh,
+// Elementwise over [n_rows, I], 8 consecutive columns per thread (16-byte loads and stores):
+// dGU = [dh U SiLU'(G) | dh SiLU(G)] and h = SiLU(G) U.
+__global__ __launch_bounds__(256) void swiglu_backward_kernel(long long n8, int I, const uint16_t* __restrict__ dh,
                                                               const uint16_t* __restrict__ gu,
                                                               uint16_t* __restrict__ dgu, uint16_t* __restrict__ h) {
-  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+  const int I8 = I / 8;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8;
        i += static_cast<long long>(gridDim.x) * blockDim.x) {
-    const long long r = i / I;
-    const int c = static_cast<int>(i - r * I);
-    const float g = bf16_to_f32(gu[r * 2 * I + c]), up = bf16_to_f32(gu[r * 2 * I + I + c]);
-    const float dv = bf16_to_f32(dh[i]);
-    const float sg = 1.0f / (1.0f + __expf(-g));
-    const float si = g * sg;
-    dgu[r * 2 * I + c] = f32_to_bf16(dv * up * sg * (1.0f + g * (1.0f - sg)));
-    dgu[r * 2 * I + I + c] = f32_to_bf16(dv * si);
-    h[i] = f32_to_bf16(si * up);
+    const long long r = i / I8;
+    const int c = static_cast<int>(i - r * I8) * 8;
+    float g[8], up[8], dv[8], dg[8], du[8], hv[8];
+    unpack8(*reinterpret_cast<const uint4*>(gu + r * 2 * I + c), g);
+    unpack8(*reinterpret_cast<const uint4*>(gu + r * 2 * I + I + c), up);
+    unpack8(*reinterpret_cast<const uint4*>(dh + r * I + c), dv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float sg = 1.0f / (1.0f + __expf(-g[k]));
+      const float si = g[k] * sg;
+      dg[k] = dv[k] * up[k] * sg * (1.0f + g[k] * (1.0f - sg));
+      du[k] = dv[k] * si;
+      hv[k] = si * up[k];
+    }
+    store8(dgu + r * 2 * I + c, dg);
+    store8(dgu + r * 2 * I + I + c, du);
+    store8(h + r * I + c, hv);
   }
 }
 
@@ -299,9 +309,9 @@ hipError_t launch_route_backward(const Shape& s, moe_dtype act, const void* u, c
 
 hipError_t launch_swiglu_backward(long long n_rows, int I, const void* dh, const void* gu, void* dgu, void* h,
                                   hipStream_t st) {
-  const long long n = n_rows * I;
-  const long long blocks = grid_cap((n + 255) / 256);
-  hipLaunchKernelGGL(swiglu_backward_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, n, I,
+  const long long n8 = n_rows * I / 8;
+  const long long blocks = grid_cap((n8 + 255) / 256);
+  hipLaunchKernelGGL(swiglu_backward_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, n8, I,
                      static_cast<const uint16_t*>(dh), static_cast<const uint16_t*>(gu), static_cast<uint16_t*>(dgu),
                      static_cast<uint16_t*>(h));
   return hipGetLastError();
