@@ -209,3 +209,14 @@ def test_probe_validation():
     assert L.moe_probe_copy(FAKE, FAKE, 1 << 20, None) == B.MOE_E_INVALID          # in place
     assert L.moe_probe_copy(FAKE, ctypes.c_void_p(0x2000), 24, None) == B.MOE_E_INVALID
     assert L.moe_probe_read(FAKE, 24, FAKE, None) == B.MOE_E_INVALID
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """With no built library every call raises: there is no CPU fallback."""
+    from moe_inputs import get_config
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libmoe.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(ImportError, match="not built"):
+        B.lib()
+    with pytest.raises(ImportError, match="not built"):
+        B.moe_workspace_bytes(B.moe_shape.of(get_config("c1")), 2)
