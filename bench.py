@@ -56,10 +56,15 @@ def parse():
                     help="fp8: power-of-two scales on the up-projection input")
     ap.add_argument("--backward", action="store_true",
                     help="bf16 workloads: time the training step (forward + backward + bias update)")
-    ap.add_argument("--cpu-sample", type=int, default=32, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens for the CPU oracle baseline (0: skip; default 128, 8 with --backward: "
+                         "10-30 s of host work either way)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (HBM counter calibration)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.cpu_sample is None:
+        args.cpu_sample = 8 if args.backward else 128
+    return args
 
 
 FFN_SOURCES = {"bf16": ["ffn_bf16.hip", "gemm_pipe.h", "sched.h", "common.h"],
