@@ -4,19 +4,25 @@
 One step = one pass of the whole layer on one batch: moe_route, moe_permute,
 the grouped FFN over the routed and the shared experts together
 (moe_ffn_gate_up + moe_ffn_down), moe_combine and the step-end
-moe_bias_update. Inputs (seeded synthetic
-tokens and random-init weights of the workload's shape) are resident in HBM
-before the timed region. The default workload is the DeepSeek-V3-shaped layer
-(T=8192, d=7168, 256 routed experts in 8 groups, top-8 of 4 groups, 1 shared
-expert, I=2048) in bf16; ``--config c4`` runs the same shape with fp8 GEMMs.
+moe_bias_update. Inputs (seeded synthetic tokens and random-init weights of
+the workload's shape) are resident in HBM before the timed region; before
+each timed step a 1 GiB scratch buffer is written (outside the timed region)
+so that nothing of the step's inputs sits in the 256 MB Infinity Cache.
 
-Prints one JSON line with the throughput, the roofline of the dominant kernel
-(measured with HIP events on the launch stream), per-call times and the CPU
-oracle timed on a bounded token sample.
+By default the line carries the DeepSeek-V3-shaped layer (T=8192, d=7168,
+256 routed experts in 8 groups, top-8 of 4 groups, 1 shared expert, I=2048)
+in bf16 as its value, and the same shape with E4M3 expert GEMMs (1x128
+activation tiles, 128x128 weight blocks) as its "fp8" object; ``--config cN``
+runs one workload.
 
-``--backward`` (bf16 workloads) times one training step of the layer instead:
-the forward with the SwiGLU-input cache, the backward to du, the centroid and
-the expert-weight gradients (moe_combine_backward, moe_ffn_backward,
+The line holds the throughput, the roofline of the dominant kernel (the
+gate/up launch, timed with HIP events on its launch stream; algorithmic bytes
+from each step's own expert load), per-call times and HBM fractions, the
+measured MFMA / HBM peaks and the CPU oracle timed on a bounded token sample.
+
+``--backward`` times one training step of the layer instead: the forward
+with the SwiGLU-input cache, the backward to du, the centroid and the
+expert-weight gradients (moe_combine_backward, moe_ffn_backward,
 moe_route_backward, moe_input_grad) and the bias update; no optimizer.
 """
 from __future__ import annotations
@@ -47,7 +53,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default=None, choices=["c2", "c3", "c4", "c5"],
+                    help="one workload (default: the V3-shaped layer in bf16, with its fp8 form as the 'fp8' "
+                         "object of the same line)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not write the 1 GiB scratch buffer before each timed step")
     ap.add_argument("--batch-invariant", action="store_true",
                     help="router K split fixed by d, so per-token results do not depend on the batch")
     ap.add_argument("--mxfp4", action="store_true",
@@ -96,41 +106,62 @@ def recorded_traffic(kernel: str, workload: str, gemm: str):
     return None
 
 
+def _probe_lib():
+    """libmoe_probe.so: the peak probes, a measurement library of its own beside libmoe.so."""
+    import ctypes
+    path = os.path.join(ROOT, "mixture_experts_layer_gate_amd", "libmoe_probe.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run __graft_entry__.build()")
+    P = ctypes.CDLL(path)
+    P.probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    P.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    P.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    return P
+
+
 def measure_peaks(dev):
-    """MFMA (bf16, E4M3) and device-copy rates of this GPU from the library's probes, timed with HIP events."""
+    """MFMA (bf16, E4M3), device-copy and read rates of this GPU from the probe library, timed with HIP events
+    on the stream the probes are launched on."""
     import torch
-    from mixture_experts_layer_gate_amd import binding as B
-    seed = torch.arange(1, 65, dtype=torch.int32, device=dev)
-    out = torch.empty(B.moe_probe_blocks() * 256, dtype=torch.float32, device=dev)
+    P = _probe_lib()
     stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"peak probe failed with status {rc}")
+
+    seed = torch.arange(1, 65, dtype=torch.int32, device=dev)
+    nb = P.probe_mfma_blocks()
+    out = torch.empty(nb * 256, dtype=torch.float32, device=dev)
     res = {}
-    for name, dt, flop in (("mfma_bf16", B.MOE_BF16, 32768), ("mfma_fp8", B.MOE_F8E4M3, 131072)):
-        B.moe_probe_mfma(dt, 100, seed, out)
+    for name, fp8, flop in (("mfma_bf16", 0, 32768), ("mfma_fp8", 1, 131072)):
+        ok(P.probe_mfma(fp8, 100, seed.data_ptr(), out.data_ptr(), sp))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         iters = 4000
         e0.record(stream)
-        B.moe_probe_mfma(dt, iters, seed, out)
+        ok(P.probe_mfma(fp8, iters, seed.data_ptr(), out.data_ptr(), sp))
         e1.record(stream)
         torch.cuda.synchronize()
-        res[name + "_TFLOP/s"] = B.moe_probe_blocks() * 4 * iters * 8 * flop / (e0.elapsed_time(e1) / 1e3) / 1e12
+        res[name + "_TFLOP/s"] = nb * 4 * iters * 8 * flop / (e0.elapsed_time(e1) / 1e3) / 1e12
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    B.moe_probe_copy(src, dst)
+    ok(P.probe_copy(src.data_ptr(), dst.data_ptr(), src.numel(), sp))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(5):
-        B.moe_probe_copy(src, dst)
+        ok(P.probe_copy(src.data_ptr(), dst.data_ptr(), src.numel(), sp))
     e1.record(stream)
     torch.cuda.synchronize()
     res["hbm_copy_GB/s"] = 5 * 2 * src.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
     del dst
     big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)      # 4 GiB: far past the 256 MB Infinity Cache
-    acc = torch.empty(int(B.lib().moe_probe_read_blocks()) * 256, dtype=torch.int32, device=dev)
-    B.moe_probe_read(big, acc)
+    acc = torch.empty(P.probe_read_blocks() * 256, dtype=torch.int32, device=dev)
+    ok(P.probe_read(big.data_ptr(), big.numel(), acc.data_ptr(), sp))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(3):
-        B.moe_probe_read(big, acc)
+        ok(P.probe_read(big.data_ptr(), big.numel(), acc.data_ptr(), sp))
     e1.record(stream)
     torch.cuda.synchronize()
     res["hbm_read_GB/s"] = 3 * big.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
@@ -321,39 +352,27 @@ def main_backward(args, cfg):
     print(json.dumps(res))
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: the layer runs on a single MI355X with no collectives; "
-              f"--gpus {args.gpus} is not supported", file=sys.stderr)
-        sys.exit(2)
-    if args.backward:
-        from moe_inputs import get_config as _gc
-        cfg = _gc(args.config)
-        if cfg.gemm not in ("bf16", "fp8") or args.mxfp4 or args.pow2_act_scales or args.batch_invariant:
-            print("bench.py: --backward runs the bf16 (c2, c3) and fp8 (c4, c5) workloads", file=sys.stderr)
-            sys.exit(2)
-        main_backward(args, cfg)
-        return
+FLUSH_BYTES = 1 << 30     # written before every timed step: four times the 256 MB Infinity Cache
 
+
+def run_forward(args, cfg, dev, pow2_act_scales=False):
+    """Time args.steps forward steps (+ bias update) of one workload; returns the measurements.
+
+    Each timed step is bracketed by device synchronisations; before it (outside the timed region) a 1 GiB
+    scratch buffer is written so no input of the step sits in the Infinity Cache, unless --no-flush. HIP
+    events recorded on the launch stream time every call of every step. The algorithmic bytes of a step
+    follow that step's own expert load (the bias update changes which experts a batch touches).
+    """
     import numpy as np
     import torch
-    from moe_inputs import get_config, generate
+    from moe_inputs import generate
     from mixture_experts_layer_gate_amd import MoELayer
 
-    over = dict(batch_invariant=int(args.batch_invariant))
-    if args.mxfp4:
-        if get_config(args.config).gemm != "fp8":
-            print("bench.py: --mxfp4 applies to the fp8 workloads (c4, c5)", file=sys.stderr)
-            sys.exit(2)
-        over["gemm"] = "mxfp4"
-    cfg = get_config(args.config, **over)
-    dev = "cuda"
-    torch.cuda.set_device(0)
     inp = generate(cfg, dev)
-    layer = MoELayer(cfg, inp, dev, pow2_act_scales=args.pow2_act_scales)
+    layer = MoELayer(cfg, inp, dev, pow2_act_scales=pow2_act_scales)
     u = inp["u"]
     stream = torch.cuda.current_stream()
+    flush = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
 
     def step(ev=None):
         rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
@@ -374,87 +393,169 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    n_calls = len(CALLS)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)] for _ in range(args.steps)]
+    loads = torch.empty((args.steps, cfg.n_routed), dtype=torch.int32, device=dev)
+    wall = []
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(i))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         step(events[i])
+        torch.cuda.synchronize()
+        wall.append(time.perf_counter() - t0)
+        loads[i].copy_(layer.expert_load)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    per_call = {c: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
-                for j, c in enumerate(CALLS)}
+    # the same steps back to back with no flush and no synchronisation between them, for context
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_b2b = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_step = float(np.mean(wall)) * 1e3
+    call_ms = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(n_calls)]
+                        for i in range(args.steps)])
+    per_call = {c: float(call_ms[:, j].mean()) for j, c in enumerate(CALLS)}
 
-    load = layer.expert_load.cpu().numpy()
-    n_touch = touched_experts(load)
+    load = loads.cpu().numpy()
+    touched = (load > 0).sum(axis=1)                    # experts with rows, per step
     T, d, I, K, N, Ns = cfg.T, cfg.d, cfg.inter, cfg.topk, cfg.n_routed, cfg.n_shared
     wb = WEIGHT_BYTES[cfg.gemm]                 # weight bytes per element (with scales)
     ab = 2                                      # u / out bytes per element (bf16)
-    # dominant kernel: the gate/up projection of the routed and shared experts (one launch)
-    gu_bytes = (n_touch + Ns) * 2 * I * d * wb + T * d * ab
+    # dominant kernel: the gate/up projection of the routed and shared experts (one launch); its algorithmic
+    # bytes are the gate/up weights of the experts that step touched (plus the shared ones) and u, read once
+    gu_bytes = (touched + Ns) * 2 * I * d * wb + T * d * ab
     gu_flops = 2.0 * T * (K + Ns) * d * 2 * I
-    gu_s = per_call["ffn_gate_up"] / 1e3
-    gu_bound = "hbm" if gu_bytes / HBM_PEAK >= gu_flops / MFMA_PEAK[cfg.gemm] else "mfma"
+    gu_ms = call_ms[:, CALLS.index("ffn_gate_up")]
+    gu_s_total = gu_ms.sum() / 1e3
+    gu_bound = "hbm" if gu_bytes.mean() / HBM_PEAK >= gu_flops / MFMA_PEAK[cfg.gemm] else "mfma"
     if gu_bound == "hbm":
-        roof = {"bound": "hbm", "achieved": gu_bytes / gu_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": gu_bytes.sum() / gu_s_total / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": MFMA_PEAK[cfg.gemm] / 1e12,
-                "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": gu_flops * args.steps / gu_s_total / 1e12,
+                "peak": MFMA_PEAK[cfg.gemm] / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = recorded_traffic(f"ffn_gate_up_{cfg.gemm} routed+shared", cfg.name, cfg.gemm)
     roof["kernel"] = "ffn_gate_up (routed + shared experts)"
-    roof["mfma_frac"] = gu_flops / gu_s / MFMA_PEAK[cfg.gemm]
+    roof["algorithmic_bytes_per_launch"] = float(gu_bytes.mean())
+    roof["launch_ms"] = float(gu_ms.mean())
+    roof["mfma_frac"] = gu_flops * args.steps / gu_s_total / MFMA_PEAK[cfg.gemm]
 
     ffn_flops = cfg.ffn_flops()
     ffn_s = (per_call["ffn_gate_up"] + per_call["ffn_down"]) / 1e3
-    layer_bytes = (n_touch * 3 * I * d * wb + Ns * 3 * I * d * wb + 2 * T * d * ab + N * d * ab)
+    layer_bytes = float(((touched + Ns) * 3 * I * d * wb).mean() + 2 * T * d * ab + N * d * ab)
     calls = {c: {"ms": round(per_call[c], 4)} for c in CALLS}
-    calls["route"]["GB/s"] = round((T * d * ab + N * d * ab) / (per_call["route"] / 1e3) / 1e9, 1)
-    calls["combine"]["GB/s"] = round((T * d * ab * 2 + (T * K + T * Ns) * d * ab) / (per_call["combine"] / 1e3) / 1e9, 1)
-    calls["ffn_gate_up"]["TFLOP/s"] = round(gu_flops / gu_s / 1e12, 1)
-    calls["ffn_down"]["GB/s_weights"] = round((n_touch + Ns) * I * d * wb / (per_call["ffn_down"] / 1e3) / 1e9, 1)
+    route_bytes = T * d * ab + N * d * ab + T * K * 8 + N * 4           # u, centroids; idx, gates, load out
+    combine_bytes = T * d * ab * 2 + (T * K + T * Ns) * d * ab + T * K * 8   # u, out, y rows; row_of, gates
+    permute_bytes = T * K * 4 * 3 + (N + 1) * 4                        # idx in; perm_token, row_of, offsets out
+    if cfg.gemm in ("fp8", "mxfp4"):
+        permute_bytes += T * d * ab + T * d + T * d // 128 * 4          # u in; E4M3 codes and scales out
+    for c, nb in (("route", route_bytes), ("permute", permute_bytes), ("combine", combine_bytes)):
+        calls[c]["GB/s"] = round(nb / (per_call[c] / 1e3) / 1e9, 1)
+        calls[c]["hbm_frac"] = round(nb / (per_call[c] / 1e3) / HBM_PEAK, 4)
+    calls["ffn_gate_up"]["TFLOP/s"] = round(gu_flops / (per_call["ffn_gate_up"] / 1e3) / 1e12, 1)
+    calls["ffn_gate_up"]["hbm_frac"] = round(float(gu_bytes.mean()) / (per_call["ffn_gate_up"] / 1e3) / HBM_PEAK, 4)
+    dn_bytes = float(((touched + Ns) * I * d * wb).mean())
+    calls["ffn_down"]["GB/s_weights"] = round(dn_bytes / (per_call["ffn_down"] / 1e3) / 1e9, 1)
+    calls["ffn_down"]["hbm_frac_weights"] = round(dn_bytes / (per_call["ffn_down"] / 1e3) / HBM_PEAK, 4)
     calls["ffn_down"]["TFLOP/s"] = round(2.0 * T * (K + Ns) * I * d / (per_call["ffn_down"] / 1e3) / 1e12, 1)
+    steps_ms = sorted(call_ms.sum(axis=1))
+    pct = lambda q: float(steps_ms[min(len(steps_ms) - 1, int(q * (len(steps_ms) - 1) + 0.5))])
+    res = {
+        "ms_step": ms_step, "ms_b2b": ms_b2b, "roof": roof, "calls": calls,
+        "ffn": {"TFLOP/s": ffn_flops / ffn_s / 1e12, "mfma_frac": ffn_flops / ffn_s / MFMA_PEAK[cfg.gemm],
+                "hbm_frac_weights": float(((touched + Ns) * 3 * I * d * wb).mean()) / ffn_s / HBM_PEAK},
+        "layer": {"algorithmic_GB": layer_bytes / 1e9, "roofline_ms": max(layer_bytes / HBM_PEAK,
+                  (ffn_flops + cfg.router_flops()) / MFMA_PEAK[cfg.gemm]) * 1e3,
+                  "experts_touched": int(touched[-1]), "experts_touched_range": [int(touched.min()), int(touched.max())],
+                  "max_load": int(load[-1].max()), "min_load": int(load[-1].min())},
+        "step_ms_events": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
+        "inp": inp, "layer_obj": layer,
+    }
+    res["layer"]["frac_of_roofline"] = res["layer"]["roofline_ms"] / ms_step
+    return res
 
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the layer runs on a single MI355X with no collectives; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    both = args.config is None          # default: the V3-shaped layer in bf16, plus its fp8 form
+    if both:
+        args.config = "c3"
+    if args.backward:
+        from moe_inputs import get_config as _gc
+        cfg = _gc(args.config)
+        if cfg.gemm not in ("bf16", "fp8") or args.mxfp4 or args.pow2_act_scales or args.batch_invariant:
+            print("bench.py: --backward runs the bf16 (c2, c3) and fp8 (c4, c5) workloads", file=sys.stderr)
+            sys.exit(2)
+        main_backward(args, cfg)
+        return
+
+    import torch
+    from moe_inputs import get_config
+
+    over = dict(batch_invariant=int(args.batch_invariant))
+    if args.mxfp4:
+        if get_config(args.config).gemm != "fp8":
+            print("bench.py: --mxfp4 applies to the fp8 workloads (c4, c5)", file=sys.stderr)
+            sys.exit(2)
+        over["gemm"] = "mxfp4"
+    cfg = get_config(args.config, **over)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    r = run_forward(args, cfg, dev, args.pow2_act_scales)
+    T = cfg.T
     res = {
         "metric": METRIC,
-        "value": T / (ms_step / 1e3),
+        "value": T / (r["ms_step"] / 1e3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": r["ms_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.gemm,
         "data": "synthetic: seeded N(0,1) tokens, random-init N(0,0.02^2) weights of the workload's shape",
         "config": {"workload": f"{cfg.name}: {cfg.description}" + (", MXFP4 expert weights" if cfg.gemm == "mxfp4"
-                                                                     else ""), "T": T, "d": d, "n_routed": N,
-                   "groups": cfg.n_groups, "topk_groups": cfg.topk_groups, "topk": K, "n_shared": Ns, "inter": I,
-                   "gemm": cfg.gemm, "batch_invariant": bool(args.batch_invariant),
+                                                                     else ""), "T": T, "d": cfg.d,
+                   "n_routed": cfg.n_routed, "groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
+                   "topk": cfg.topk, "n_shared": cfg.n_shared, "inter": cfg.inter, "gemm": cfg.gemm,
+                   "batch_invariant": bool(args.batch_invariant),
+                   "infinity_cache_flush": not args.no_flush,
                    **({"act_scales": "pow2" if args.pow2_act_scales else "fp32"} if cfg.gemm == "fp8" else {})},
-        "roofline": roof,
-        "ffn": {"TFLOP/s": ffn_flops / ffn_s / 1e12, "mfma_frac": ffn_flops / ffn_s / MFMA_PEAK[cfg.gemm],
-                "hbm_frac_weights": (n_touch + Ns) * 3 * I * d * wb / ffn_s / HBM_PEAK},
-        "layer": {"algorithmic_GB": layer_bytes / 1e9, "roofline_ms": max(layer_bytes / HBM_PEAK,
-                  (ffn_flops + cfg.router_flops()) / MFMA_PEAK[cfg.gemm]) * 1e3,
-                  "experts_touched": n_touch, "max_load": int(load.max()), "min_load": int(load.min())},
-        "calls": calls,
+        "roofline": r["roof"],
+        "ffn": r["ffn"],
+        "layer": r["layer"],
+        "calls": r["calls"],
+        "step_ms_events": r["step_ms_events"],
+        "ms_per_step_back_to_back": r["ms_b2b"],
     }
-    res["layer"]["frac_of_roofline"] = res["layer"]["roofline_ms"] / ms_step
-    steps_ms = sorted(sum(events[i][j].elapsed_time(events[i][j + 1]) for j in range(len(CALLS)))
-                      for i in range(args.steps))
-    pct = lambda q: steps_ms[min(len(steps_ms) - 1, int(q * (len(steps_ms) - 1) + 0.5))]
-    res["step_ms_events"] = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
+    cpu = cpu_baseline(cfg, r["inp"], r["layer_obj"], args.cpu_sample) if args.cpu_sample > 0 else None
+    del r
+    torch.cuda.empty_cache()
+    if both:
+        # the fp8 half of the metric: the same V3 shape with E4M3 expert GEMMs
+        cfg8 = get_config("c4", **over)
+        r8 = run_forward(args, cfg8, dev)
+        res["fp8"] = {"workload": f"{cfg8.name}: {cfg8.description}", "value": cfg8.T / (r8["ms_step"] / 1e3),
+                      "unit": "tokens/s", "ms_per_step": r8["ms_step"], "ms_per_step_back_to_back": r8["ms_b2b"],
+                      "roofline": r8["roof"], "ffn": r8["ffn"], "layer": r8["layer"], "calls": r8["calls"],
+                      "step_ms_events": r8["step_ms_events"]}
+        del r8
+        torch.cuda.empty_cache()
     peaks = measure_peaks(dev)
     res["peaks_measured"] = peaks
-    roof["peak_measured"] = (peaks["hbm_read_GB/s"] if roof["bound"] == "hbm"
-                             else peaks["mfma_fp8_TFLOP/s" if cfg.gemm in ("fp8", "mxfp4") else "mfma_bf16_TFLOP/s"])
-    roof["frac_of_measured"] = roof["achieved"] / roof["peak_measured"]
-    if args.cpu_sample > 0:
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, layer, args.cpu_sample)
-    else:
-        res["cpu_baseline"] = None
+    for roof, gemm in [(res["roofline"], cfg.gemm)] + ([(res["fp8"]["roofline"], "fp8")] if both else []):
+        roof["peak_measured"] = (peaks["hbm_read_GB/s"] if roof["bound"] == "hbm"
+                                 else peaks["mfma_fp8_TFLOP/s" if gemm in ("fp8", "mxfp4") else "mfma_bf16_TFLOP/s"])
+        roof["frac_of_measured"] = roof["achieved"] / roof["peak_measured"]
+    res["cpu_baseline"] = cpu
     print(json.dumps(res))
 
 

@@ -125,7 +125,11 @@ moe_status moe_route(const moe_shape* shape, moe_dtype act, const void* u, const
  * row gather and the online fp8 quantisation of the activations (1x128 tiles,
  * section "Fine-Grained Quantization"; scale from the current max-abs, section
  * "Online Quantization").
- *   topk_idx       [T, K] int32 from moe_route.
+ *   topk_idx       [T, K] int32, as moe_route writes it (K distinct ids in [0, N_r) per token).
+ *                  A pair whose id lies outside [0, N_r) or repeats an earlier id of the
+ *                  same token gets no row: its row_of entry is -1 (moe_combine skips it),
+ *                  expert_offsets count only the pairs that got a row, and perm_token
+ *                  entries from expert_offsets[N_r] to T*K - 1 are -1.
  *   expert_offsets out [N_r + 1] int32: rows of expert e are [off[e], off[e+1]).
  *   perm_token     out [T*K] int32: token of each row (rows ordered by expert, then token).
  *   row_of         out [T*K] int32: row of pair (t, k) at index t*K + k.
@@ -411,23 +415,6 @@ moe_status moe_ffn_backward_fp8(const moe_shape* shape, int32_t n_experts, int32
                                 const float* gu_scale, const void* w_gate_up_t, const float* w_gate_up_t_scale,
                                 const void* w_down_t, const float* w_down_t_scale, const void* dy, void* da,
                                 float* dw_gate_up, float* dw_down, void* workspace, size_t ws_bytes, void* stream);
-
-/*
- * ---- Peak probes (measurement only, not on the layer's path): the roofline
- * figures report the published MI355X peaks beside these measured ones.
- * moe_probe_mfma -- moe_probe_blocks() workgroups of 4 waves, each wave issuing
- * iters x 8 independent MFMAs (MOE_BF16: 32x32x16, 32768 FLOP each;
- * MOE_F8E4M3: 32x32x64 E4M3, 131072 FLOP each) on register operands; seed: 64
- * int32 (operand bits); out: moe_probe_blocks() * 256 floats (written).
- * moe_probe_copy -- dst = src, bytes a multiple of 16 (16 bytes per lane).
- * moe_probe_read -- reads bytes (a multiple of 16) of src; out: moe_probe_read_blocks()
- * * 256 uint32 (written).
- */
-int32_t moe_probe_blocks(void);
-moe_status moe_probe_mfma(moe_dtype dtype, int32_t iters, const int32_t* seed, float* out, void* stream);
-moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
-int32_t moe_probe_read_blocks(void);
-moe_status moe_probe_read(const void* src, size_t bytes, uint32_t* out, void* stream);
 
 /*
  * moe_tile_weights_bf16 -- copies bf16 expert weights into the tiled layout of

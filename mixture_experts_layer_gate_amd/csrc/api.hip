@@ -672,29 +672,4 @@ moe_status moe_ffn_backward_fp8(const moe_shape* shape, int32_t n_experts, int32
 }
 
 
-int32_t moe_probe_blocks(void) { return moe::probe_mfma_blocks(); }
-int32_t moe_probe_read_blocks(void) { return moe::probe_read_blocks(); }
-
-moe_status moe_probe_read(const void* src, size_t bytes, uint32_t* out, void* stream) {
-  g_err.clear();
-  REQUIRE(src && out && bytes % 16 == 0, "probe_read: bad arguments");
-  auto st = static_cast<hipStream_t>(stream);
-  return finish(moe::launch_probe_read(src, bytes, out, st), "moe_probe_read", st);
-}
-
-moe_status moe_probe_mfma(moe_dtype dtype, int32_t iters, const int32_t* seed, float* out, void* stream) {
-  g_err.clear();
-  REQUIRE(dtype == MOE_BF16 || dtype == MOE_F8E4M3, "probe_mfma: dtype must be MOE_BF16 or MOE_F8E4M3");
-  REQUIRE(iters > 0 && seed && out, "probe_mfma: bad arguments");
-  auto st = static_cast<hipStream_t>(stream);
-  return finish(moe::launch_probe_mfma(dtype == MOE_F8E4M3, iters, seed, out, st), "moe_probe_mfma", st);
-}
-
-moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
-  g_err.clear();
-  REQUIRE(src && dst && src != dst && bytes % 16 == 0, "probe_copy: bad arguments");
-  auto st = static_cast<hipStream_t>(stream);
-  return finish(moe::launch_probe_copy(src, dst, bytes, st), "moe_probe_copy", st);
-}
-
 }  // extern "C"

@@ -100,12 +100,6 @@ hipError_t launch_swiglu_backward(long long n_rows, int I, const void* dh, const
 hipError_t launch_input_grad(const Shape& s, const void* dout, const float* du_router, const void* da,
                              const int32_t* row_of, float* du, hipStream_t st);
 hipError_t launch_transpose_tile_bf16(int n_mats, int rows, int cols, const void* w, void* out, hipStream_t st);
-// peak probes (probe.hip)
-int probe_mfma_blocks();
-int probe_read_blocks();
-hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* out, hipStream_t st);
-hipError_t launch_probe_mfma(bool fp8, int iters, const int* seed, float* out, hipStream_t st);
-hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 // FP8 backward (backward_fp8.hip)
 hipError_t launch_transpose_rows_bf16(int n_mats, int rows, int cols, const void* w, void* out, hipStream_t st);
 hipError_t launch_quantize_rows(long long n_rows, int cols, const void* x, bool f32_in, void* codes, float* scales,

@@ -102,22 +102,37 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int N, const uns
   }
 }
 
+// A pair whose expert id is out of range or repeats an earlier id of the same
+// token gets no row (row_of = -1); the masks count such a token once per
+// distinct expert, so the rows past offsets[N] (their number) hold -1.
 __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int K, int N, const int32_t* __restrict__ idx,
                                                            const unsigned long long* __restrict__ masks,
                                                            const int32_t* __restrict__ base,
+                                                           const int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm, int32_t* __restrict__ row_of) {
   const int lane = threadIdx.x & 63;
   const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int t = c * kChunk + lane;
   if (t >= T) return;
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int32_t* ti = idx + static_cast<size_t>(t) * K;
   for (int k = 0; k < K; ++k) {
-    const int e = idx[static_cast<size_t>(t) * K + k];
-    if (e < 0 || e >= N) continue;
+    const int e = ti[k];
+    bool ok = e >= 0 && e < N;
+    for (int j = 0; j < k && ok; ++j) ok = ti[j] != e;
+    if (!ok) {
+      row_of[static_cast<size_t>(t) * K + k] = -1;
+      continue;
+    }
     const size_t ce = static_cast<size_t>(c) * N + e;
     const int r = base[ce] + __popcll(masks[ce] & below);
     perm[r] = t;
     row_of[static_cast<size_t>(t) * K + k] = r;
+  }
+  const long long used = offsets[N];
+  for (int k = 0; k < K; ++k) {
+    const long long pos = static_cast<long long>(t) * K + k;
+    if (pos >= used) perm[pos] = -1;
   }
 }
 
@@ -134,8 +149,8 @@ hipError_t launch_permute_maps(const Shape& s, const int32_t* idx, int32_t* offs
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, s.T, s.N, masks, base, offsets);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(blocks), dim3(256), 0, st, s.T, s.K, s.N, idx, masks, base, perm,
-                     row_of);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(blocks), dim3(256), 0, st, s.T, s.K, s.N, idx, masks, base, offsets,
+                     perm, row_of);
   return hipGetLastError();
 }
 

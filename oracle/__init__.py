@@ -34,6 +34,6 @@ from .mxfp4 import (  # noqa: F401
 )
 from .moe import (  # noqa: F401
     affinity, balance_stats, route, permute, swiglu_ffn, quantize_tiles, quantize_blocks,
-    dequantize_tiles, dequantize_blocks, ffn_fp8, ffn_mxfp4, combine, bias_update,
+    dequantize_tiles, dequantize_blocks, ffn_fp8, ffn_quantised_acts, ffn_mxfp4, combine, bias_update,
     expert_ffn, layer_forward,
 )

@@ -266,11 +266,11 @@ def ffn_fp8(a, wgu_codes, wgu_scale, wd_codes, wd_scale, return_h=False, pow2_in
     pow2_input: the up-projection input takes power-of-two scales (the
     dispatched-activation variant); H keeps fp32 scales.
     """
-    return _ffn_quantised_acts(a, dequantize_blocks(wgu_codes, wgu_scale), dequantize_blocks(wd_codes, wd_scale),
+    return ffn_quantised_acts(a, dequantize_blocks(wgu_codes, wgu_scale), dequantize_blocks(wd_codes, wd_scale),
                                return_h, pow2_input)
 
 
-def _ffn_quantised_acts(a, wgu, wd, return_h=False, pow2_input=False):
+def ffn_quantised_acts(a, wgu, wd, return_h=False, pow2_input=False):
     """SwiGLU FFN over exact weight values wgu [2I, d], wd [d, I] (float64), with the activations of both
     GEMMs quantised online per 1x128 tile (E4M3, fp32 scales; the input optionally with power-of-two
     scales) and the products summed exactly in fp64."""
@@ -293,7 +293,7 @@ def ffn_mxfp4(a, wgu_codes, wgu_scales, wd_codes, wd_scales, return_h=False, pow
     consecutive K values ([2I, d/32] / [d, I/32]); activations quantised to E4M3 per 1x128 tile as in the
     fp8 recipe. Products of an E2M1 and an E4M3 value and their sums are exact in fp64."""
     from .mxfp4 import dequantize_mxfp4
-    return _ffn_quantised_acts(a, dequantize_mxfp4(wgu_codes, wgu_scales), dequantize_mxfp4(wd_codes, wd_scales),
+    return ffn_quantised_acts(a, dequantize_mxfp4(wgu_codes, wgu_scales), dequantize_mxfp4(wd_codes, wd_scales),
                                return_h, pow2_input)
 
 

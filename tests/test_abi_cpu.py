@@ -202,13 +202,21 @@ def test_backward_fp8_validation():
     assert L.moe_ffn_backward_fp8(*bw(sh=wide, ws=1 << 40)) == B.MOE_E_UNSUPPORTED
 
 
-def test_probe_validation():
+def test_peak_probe_library_is_separate():
+    """The benchmark's peak probes live in libmoe_probe.so, outside the product library, and reject bad
+    arguments before any launch."""
+    import os
     L = B.lib()
-    assert L.moe_probe_mfma(B.MOE_F32, 10, FAKE, FAKE, None) == B.MOE_E_INVALID
-    assert L.moe_probe_mfma(B.MOE_BF16, 0, FAKE, FAKE, None) == B.MOE_E_INVALID
-    assert L.moe_probe_copy(FAKE, FAKE, 1 << 20, None) == B.MOE_E_INVALID          # in place
-    assert L.moe_probe_copy(FAKE, ctypes.c_void_p(0x2000), 24, None) == B.MOE_E_INVALID
-    assert L.moe_probe_read(FAKE, 24, FAKE, None) == B.MOE_E_INVALID
+    for name in ("moe_probe_mfma", "moe_probe_copy", "moe_probe_read", "probe_mfma"):
+        assert not hasattr(L, name), name
+    P = ctypes.CDLL(os.path.join(os.path.dirname(B.LIB_PATH), "libmoe_probe.so"))
+    P.probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    P.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    P.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert P.probe_mfma(0, 0, FAKE, FAKE, None) == -1
+    assert P.probe_copy(FAKE, FAKE, 1 << 20, None) == -1          # in place
+    assert P.probe_copy(FAKE, ctypes.c_void_p(0x2000), 24, None) == -1
+    assert P.probe_read(FAKE, 24, FAKE, None) == -1
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

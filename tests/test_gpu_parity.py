@@ -13,6 +13,7 @@ import oracle
 from moe_inputs import get_config, generate, generate_expert
 from mixture_experts_layer_gate_amd import binding as B
 from mixture_experts_layer_gate_amd import MoELayer
+from gpu_common import i32, inputs, oracle_ffn_rows, oracle_route, oracle_wq, workspace
 from parity import TOL, np64, npi, rel_l2, report, routing_mismatches, tile_e4m3
 
 pytestmark = pytest.mark.gpu
@@ -20,32 +21,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _i32(x):
-    return torch.as_tensor(np.asarray(x), dtype=torch.int32, device=DEV).contiguous()
-
-
-_CACHE = {}
-
-
-def _inputs(name, **over):
-    key = (name, tuple(sorted(over.items())))
-    if key not in _CACHE:
-        _CACHE.clear()
-        torch.cuda.empty_cache()
-        cfg = get_config(name, **over)
-        _CACHE[key] = (cfg, generate(cfg, DEV))
-    return _CACHE[key]
-
-
-def _oracle_route(cfg, inp):
-    return oracle.route(inp["u"], inp["centroids"], inp["bias"], cfg.n_groups, cfg.topk_groups, cfg.group_topn,
-                        cfg.topk)
-
-
-def _ws(cfg):
-    sh = B.moe_shape.of(cfg)
-    gemm = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_F8E4M3}[cfg.gemm]
-    return torch.empty(B.moe_workspace_bytes(sh, gemm), dtype=torch.uint8, device=DEV)
+_i32 = i32
+_inputs = inputs
+_oracle_route = oracle_route
+_ws = workspace
 
 
 ROUTE_CASES = [
@@ -172,6 +151,46 @@ def test_permute_maps(case):
     B.moe_permute(sh, _i32(idx), None, off, perm, row_of, workspace=_ws(cfg))
     torch.cuda.synchronize()
     o_off, o_perm, o_row = oracle.permute(idx, N)
+    assert np.array_equal(npi(off), o_off)
+    assert np.array_equal(npi(perm), o_perm)
+    assert np.array_equal(npi(row_of), o_row)
+
+
+def test_permute_drops_invalid_pairs():
+    """Pairs with an expert id outside [0, N_r) or repeating an earlier id of the same token get no row
+    (row_of = -1); offsets count the remaining pairs, and perm_token past them holds -1. Expected maps from
+    the plain definition: a stable sort of the kept pairs by (expert, token)."""
+    cfg = get_config("c2", T=300)
+    T, K, N = cfg.T, cfg.topk, cfg.n_routed
+    rng = np.random.default_rng(17)
+    idx = np.sort(np.stack([rng.choice(N, K, replace=False) for _ in range(T)]), 1)
+    idx[3, 2] = N                   # out of range
+    idx[7, 0] = -5
+    idx[11, 4] = idx[11, 1]         # duplicate inside a token
+    idx[12] = idx[12, 0]            # every slot the same expert
+    idx[250:, :] = N + 3            # a run of tokens with no valid pair
+    keep = np.zeros((T, K), dtype=bool)
+    for t in range(T):
+        seen = set()
+        for k in range(K):
+            e = int(idx[t, k])
+            if 0 <= e < N and e not in seen:
+                keep[t, k] = True
+                seen.add(e)
+    pairs = sorted((int(idx[t, k]), t, k) for t in range(T) for k in range(K) if keep[t, k])
+    load = np.bincount([p[0] for p in pairs], minlength=N)
+    o_off = np.concatenate([[0], np.cumsum(load)])
+    o_perm = np.full(T * K, -1)
+    o_row = np.full(T * K, -1)
+    for r, (e, t, k) in enumerate(pairs):
+        o_perm[r] = t
+        o_row[t * K + k] = r
+    sh = B.moe_shape.of(cfg)
+    off = torch.full((N + 1,), -7, dtype=torch.int32, device=DEV)
+    perm = torch.full((T * K,), -7, dtype=torch.int32, device=DEV)
+    row_of = torch.full((T * K,), -7, dtype=torch.int32, device=DEV)
+    B.moe_permute(sh, _i32(idx), None, off, perm, row_of, workspace=_ws(cfg))
+    torch.cuda.synchronize()
     assert np.array_equal(npi(off), o_off)
     assert np.array_equal(npi(perm), o_perm)
     assert np.array_equal(npi(row_of), o_row)
@@ -324,10 +343,10 @@ def test_fp8_layer_pow2_act_scales():
     for t in toks:
         acc = u64[t].copy()
         for sh_e in range(cfg.n_shared):
-            acc = acc + oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, sh_e, shared=True), pow2_input=True)[0]
+            acc = acc + oracle.ffn_fp8(u32[[t]], *oracle_wq(cfg, inp, sh_e, shared=True), pow2_input=True)[0]
         for k in range(K):
             e = int(r["idx"][t, k])
-            acc = acc + r["gate"][t, k] * oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, e), pow2_input=True)[0]
+            acc = acc + r["gate"][t, k] * oracle.ffn_fp8(u32[[t]], *oracle_wq(cfg, inp, e), pow2_input=True)[0]
         report(f"c2 fp8 pow2 out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["fp8"])
 
 
@@ -389,11 +408,7 @@ def test_quantize_weights_bit_exact(kind):
         assert np.array_equal(scale[e].cpu().numpy(), os_)
 
 
-def _oracle_ffn_rows(cfg, inp, e, rows_tok, shared=False, wq=None):
-    u = np64(inp["u"])
-    wg = inp["s_gate_up" if shared else "w_gate_up"][e].cpu()
-    wd = inp["s_down" if shared else "w_down"][e].cpu()
-    return oracle.expert_ffn(u[rows_tok], wg, wd, cfg.gemm, wq)
+_oracle_ffn_rows = oracle_ffn_rows
 
 
 @pytest.mark.parametrize("name,mode", [("c1", "gather"), ("c1", "direct"), ("c2", "gather"), ("c2", "direct")])
@@ -594,85 +609,7 @@ def test_bias_update_bit_exact():
     assert np.array_equal(bias.cpu().numpy(), oracle.bias_update(b0, load, cfg.T, cfg.topk, 0.001))
 
 
-@pytest.mark.parametrize("name,gather", [("c1", True), ("c1", False), ("c2", True)])
-def test_layer_end_to_end(name, gather):
-    cfg, inp = _inputs(name)
-    layer = MoELayer(cfg, inp, DEV, gather_in_gemm=gather)
-    out = layer.step(inp["u"])
-    torch.cuda.synchronize()
-    res = oracle.layer_forward(cfg, inp)
-    bad = routing_mismatches(layer.topk_idx, res["route"])
-    ok = np.ones(cfg.T, dtype=bool)
-    ok[bad] = False
-    u64 = np64(inp["u"])
-    report(f"{name} out", rel_l2(np64(out)[ok], res["out"][ok]), TOL[cfg.gemm])
-    report(f"{name} out - u", rel_l2((np64(out) - u64)[ok], (res["out"] - u64)[ok]), TOL[cfg.gemm])
-    if bad.size == 0:
-        assert np.array_equal(layer.bias.cpu().numpy(), res["bias"])
-        assert np.array_equal(npi(layer.expert_offsets), res["offsets"])
-
-
-# ------------------------------------------------------------------ V3 shape, sampled
-
-def test_v3_bf16_sampled_experts_and_tokens():
-    cfg, inp = _inputs("c3")
-    T, K, N, d = cfg.T, cfg.topk, cfg.n_routed, cfg.d
-    layer = MoELayer(cfg, inp, DEV)
-    out = layer.step(inp["u"])
-    torch.cuda.synchronize()
-    r = _oracle_route(cfg, inp)
-    bad = routing_mismatches(layer.topk_idx, r)
-    o_off, o_perm, o_row = oracle.permute(r["idx"], N)
-    if bad.size == 0:
-        assert np.array_equal(npi(layer.expert_offsets), o_off)
-        assert np.array_equal(npi(layer.perm_token), o_perm)
-        assert np.array_equal(npi(layer.row_of), o_row)
-        b_ref = oracle.bias_update(inp["bias"].cpu().numpy(), r["load"], T, K, cfg.gamma)
-        assert np.array_equal(layer.bias.cpu().numpy(), b_ref)
-    load = r["load"]
-    experts = sorted({0, N - 1, int(np.argmax(load)), int(np.argmin(load)), 77})
-    y = layer.y_routed
-    goff = npi(layer.expert_offsets)
-    gperm = npi(layer.perm_token)
-    for e in experts:
-        lo, hi = goff[e], goff[e + 1]
-        if hi == lo:
-            continue
-        toks = gperm[lo:hi]
-        ref = _oracle_ffn_rows(cfg, inp, e, toks)
-        report(f"c3 expert {e} ({hi - lo} rows) y", rel_l2(y[lo:hi], ref), TOL["bf16"])
-    sample = np.random.default_rng(0).choice(T, 64, replace=False)
-    ref = _oracle_ffn_rows(cfg, inp, 0, sample, shared=True)
-    report("c3 shared y (64 tokens)", rel_l2(layer.y_shared[torch.from_numpy(sample).to(DEV)], ref), TOL["bf16"])
-    # whole-layer output on a few tokens, every FFN recomputed by the oracle
-    toks = [t for t in np.random.default_rng(1).choice(T, 6, replace=False) if t not in set(bad)][:4]
-    u64 = np64(inp["u"])
-    for t in toks:
-        acc = u64[t] + _oracle_ffn_rows(cfg, inp, 0, [t], shared=True)[0]
-        for k in range(K):
-            acc = acc + r["gate"][t, k] * _oracle_ffn_rows(cfg, inp, int(r["idx"][t, k]), [t])[0]
-        report(f"c3 out token {t}", rel_l2(np64(out[t]), acc), TOL["bf16"])
-        report(f"c3 out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["bf16"])
-
-
 # ------------------------------------------------------------------ fp8 (E4M3, 1x128 / 128x128 scales)
-
-_WQ = {}
-
-
-def _oracle_wq(inp, e, shared=False):
-    key = (id(inp), e, shared)
-    if key in _WQ:
-        return _WQ[key]
-    if len(_WQ) > 48:
-        _WQ.clear()
-    wg = inp["s_gate_up" if shared else "w_gate_up"][e].cpu().float().numpy()
-    wd = inp["s_down" if shared else "w_down"][e].cpu().float().numpy()
-    gq, gs = oracle.quantize_blocks(wg)
-    dq, ds = oracle.quantize_blocks(wd)
-    _WQ[key] = (gq, gs, dq, ds)
-    return _WQ[key]
-
 
 def _check_fp8_experts(cfg, inp, layer, experts, tag, pow2=False):
     goff = npi(layer.expert_offsets)
@@ -682,7 +619,7 @@ def _check_fp8_experts(cfg, inp, layer, experts, tag, pow2=False):
         lo, hi = goff[e], goff[e + 1]
         if hi == lo:
             continue
-        wq = _oracle_wq(inp, e)
+        wq = oracle_wq(cfg, inp, e)
         ref, aux = oracle.ffn_fp8(u32[gperm[lo:hi]], *wq, return_h=True, pow2_input=pow2)
         report(f"{tag} fp8 expert {e} ({hi - lo} rows) y", rel_l2(layer.y_routed[lo:hi], ref), TOL["fp8"])
         if hasattr(layer, "h"):
@@ -715,7 +652,7 @@ def test_grouped_ffn_fp8_tile_shapes(inter, mode):
     src = rng.integers(0, cfg.T, n)
     u32 = inp["u"].cpu().float().numpy()
     uq, us = oracle.quantize_tiles(u32)
-    wq = [_oracle_wq(inp, e) for e in range(cfg.n_routed)]
+    wq = [oracle_wq(cfg, inp, e) for e in range(cfg.n_routed)]
     dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     wgu = dev8(np.stack([tile_e4m3(w[0], True) for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
     wdn = dev8(np.stack([tile_e4m3(w[2], False) for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
@@ -755,7 +692,7 @@ def test_grouped_ffn_fp8_max_k(d, inter):
     src = np.random.default_rng(31).integers(0, cfg.T, n)
     u32 = inp["u"].cpu().float().numpy()
     uq, us = oracle.quantize_tiles(u32)
-    wq = [_oracle_wq(inp, e) for e in range(cfg.n_routed)]
+    wq = [oracle_wq(cfg, inp, e) for e in range(cfg.n_routed)]
     dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     wgu = dev8(np.stack([tile_e4m3(w[0], True) for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
     wdn = dev8(np.stack([tile_e4m3(w[2], False) for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
@@ -786,7 +723,7 @@ def test_grouped_ffn_fp8_half_column_tile(d):
     src = np.random.default_rng(6).integers(0, cfg.T, n)
     u32 = inp["u"].cpu().float().numpy()
     uq, us = oracle.quantize_tiles(u32)
-    wq = [_oracle_wq(inp, e) for e in range(cfg.n_routed)]
+    wq = [oracle_wq(cfg, inp, e) for e in range(cfg.n_routed)]
     dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     wgu = dev8(np.stack([tile_e4m3(w[0], True) for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
     wdn = dev8(np.stack([tile_e4m3(w[2], False) for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
@@ -842,10 +779,12 @@ def test_fp8_accumulation_k4096():
     assert 0.01 < err_lim < 0.03
 
 
-@pytest.mark.parametrize("name", ["c2", "c4"])
-def test_fp8_layer_sampled(name):
-    over = dict(gemm="fp8") if name == "c2" else {}
-    cfg, inp = _inputs(name, **over)
+def test_fp8_layer_two_phase_calls():
+    """The fp8 layer through the two-phase calls (moe_ffn_gate_up, moe_ffn_down) and the separate shared
+    call, on the mid shape: token quantisation bit for bit, sampled experts with their H codes, the shared
+    expert on 64 tokens and the output on 3 tokens."""
+    name = "c2"
+    cfg, inp = _inputs(name, gemm="fp8")
     T, K, N, d = cfg.T, cfg.topk, cfg.n_routed, cfg.d
     layer = MoELayer(cfg, inp, DEV)
     layer.route(inp["u"])
@@ -867,7 +806,7 @@ def test_fp8_layer_sampled(name):
     _check_fp8_experts(cfg, inp, layer, experts, name)
     u32 = inp["u"].cpu().float().numpy()
     sample = np.random.default_rng(0).choice(T, 64, replace=False)
-    sq = _oracle_wq(inp, 0, shared=True)
+    sq = oracle_wq(cfg, inp, 0, shared=True)
     ref_sh = oracle.ffn_fp8(u32[sample], *sq)
     report(f"{name} fp8 shared y (64 tokens)", rel_l2(layer.y_shared[torch.from_numpy(sample).to(DEV)], ref_sh),
            TOL["fp8"])
@@ -877,51 +816,8 @@ def test_fp8_layer_sampled(name):
     for t in toks:
         acc = u64[t].copy()
         for sh_e in range(cfg.n_shared):
-            acc = acc + oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, sh_e, shared=True))[0]
+            acc = acc + oracle.ffn_fp8(u32[[t]], *oracle_wq(cfg, inp, sh_e, shared=True))[0]
         for k in range(K):
             e = int(r["idx"][t, k])
-            acc = acc + r["gate"][t, k] * oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, e))[0]
+            acc = acc + r["gate"][t, k] * oracle.ffn_fp8(u32[[t]], *oracle_wq(cfg, inp, e))[0]
         report(f"{name} fp8 out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["fp8"])
-
-
-def test_v4_decode_fp8_ten_bias_steps():
-    """Zipf-skewed decode batch, fp8: 10 steps of route -> FFN -> combine -> bias update.
-
-    Selections and the bias trajectory are compared at every step; the layer
-    output on a sampled token and the most popular expert's rows at steps 0 and 9.
-    """
-    from moe_inputs import generate_tokens
-    cfg, inp = _inputs("c5")
-    T, K, N = cfg.T, cfg.topk, cfg.n_routed
-    layer = MoELayer(cfg, inp, DEV)
-    b_or = inp["bias"].cpu().numpy().copy()
-    flips = 0
-    for step in range(cfg.steps):
-        u = generate_tokens(cfg, DEV, step)
-        out = layer.step(u)
-        torch.cuda.synchronize()
-        r = oracle.route(u, inp["centroids"], b_or, cfg.n_groups, cfg.topk_groups, cfg.group_topn, K)
-        bad = routing_mismatches(layer.topk_idx, r)
-        flips += bad.size
-        load = r["load"]
-        print(f"[parity] c5 step {step}: experts touched {int((load > 0).sum())}, empty {int((load == 0).sum())}, "
-              f"max load {int(load.max())}, flips {bad.size}")
-        if step in (0, cfg.steps - 1):
-            u32 = u.cpu().float().numpy()
-            u64 = u.cpu().double().numpy()
-            e_top = int(np.argmax(load))
-            if bad.size == 0:
-                goff, gperm = npi(layer.expert_offsets), npi(layer.perm_token)
-                lo, hi = goff[e_top], goff[e_top + 1]
-                ref = oracle.ffn_fp8(u32[gperm[lo:hi]], *_oracle_wq(inp, e_top))
-                report(f"c5 step {step} expert {e_top} ({hi - lo} rows) y", rel_l2(layer.y_routed[lo:hi], ref),
-                       TOL["fp8"])
-            t = int([x for x in range(T) if x not in set(bad)][7])
-            acc = u64[t] + oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, 0, shared=True))[0]
-            for k in range(K):
-                acc = acc + r["gate"][t, k] * oracle.ffn_fp8(u32[[t]], *_oracle_wq(inp, int(r["idx"][t, k])))[0]
-            report(f"c5 step {step} out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["fp8"])
-        b_or = oracle.bias_update(b_or, load, T, K, cfg.gamma)
-        if flips == 0:
-            assert np.array_equal(layer.bias.cpu().numpy(), b_or), f"bias differs after step {step}"
-    print(f"[parity] c5: {flips} exempt near-tie flips over {cfg.steps} steps; final |b| max {np.abs(b_or).max():.4f}")

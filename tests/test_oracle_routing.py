@@ -25,14 +25,23 @@ def _rand_route_inputs(rng, T, d, N, bias_scale=0.01):
 
 
 def _brute_force(sb32_row, G, S, M, K, topn):
-    """Enumerate group subsets, then expert subsets, by summed scores."""
+    """Enumerate group subsets, then expert subsets, by summed scores.
+
+    A group's score is the largest sum of ``topn`` of its biased scores: every topn-subset of the group is
+    enumerated and the best one by its exact sum is kept; its value is then formed in fp32, adding the
+    subset's scores from the largest down (the reading of the selection precision). The M groups with the
+    largest summed scores are found by enumerating every M-subset of groups; the K experts by enumerating
+    every K-subset of the allowed experts.
+    """
     N = G * S
     gsc = []
     for j in range(G):
-        vals = sb32_row[j * S:(j + 1) * S]
-        best = max(np.float32(vals[a]) + np.float32(vals[b]) for a, b in itertools.combinations(range(S), 2)) \
-            if topn == 2 else max(vals)
-        gsc.append(float(best))
+        vals = [float(v) for v in sb32_row[j * S:(j + 1) * S]]
+        best = max(itertools.combinations(range(S), topn), key=lambda c: sum(vals[i] for i in c))
+        acc = np.float32(0)
+        for v in sorted((vals[i] for i in best), reverse=True):
+            acc = np.float32(acc + np.float32(v))
+        gsc.append(float(acc))
     if M < G:
         best_groups = max(itertools.combinations(range(G), M), key=lambda c: sum(gsc[j] for j in c))
     else:
@@ -42,18 +51,46 @@ def _brute_force(sb32_row, G, S, M, K, topn):
     return sorted(best), sorted(best_groups)
 
 
-@pytest.mark.parametrize("G,S,M,K", [(4, 4, 2, 2), (4, 4, 2, 3), (3, 4, 2, 4), (4, 3, 3, 5), (2, 4, 1, 3),
-                                      (4, 4, 4, 3), (1, 8, 1, 3)])
-def test_p4_brute_force_small(G, S, M, K):
-    rng = np.random.default_rng(100 + G * 31 + S * 7 + M * 3 + K)
+SMALL_SHAPES = [(4, 4, 2, 2), (4, 4, 2, 3), (3, 4, 2, 4), (4, 3, 3, 5), (2, 4, 1, 3), (4, 4, 4, 3), (1, 8, 1, 3),
+                (5, 4, 2, 4), (6, 3, 3, 4)]
+
+
+@pytest.mark.parametrize("topn", [1, 2, 3, 4])
+@pytest.mark.parametrize("G,S,M,K", SMALL_SHAPES)
+def test_p4_brute_force_small(G, S, M, K, topn):
+    """Selection and kept groups against exhaustive enumeration, for group scores of 1 to 4 terms."""
+    if topn > S:
+        pytest.skip("group_topn exceeds the group size")
+    rng = np.random.default_rng(100 + G * 31 + S * 7 + M * 3 + K + 1000 * topn)
     N = G * S
     u, e, b = _rand_route_inputs(rng, 48, 32, N)
-    r = oracle.route(u, e, b, G, M, 2, K)
+    r = oracle.route(u, e, b, G, M, topn, K)
     for t in range(u.shape[0]):
-        exp_idx, exp_groups = _brute_force(r["sb32"][t], G, S, M, K, 2)
+        if r["m_gap"][t] < 1e-6 or r["k_gap"][t] < 1e-6:
+            continue                    # a near-tie: summation order may decide it
+        exp_idx, exp_groups = _brute_force(r["sb32"][t], G, S, M, K, topn)
         assert list(r["idx"][t]) == exp_idx, (t, r["idx"][t], exp_idx)
         if M < G and G > 1:
             assert list(r["kept_groups"][t]) == exp_groups
+
+
+def test_p4_group_score_terms_matter():
+    """The number of terms in a group score changes the kept groups: one group holds the single largest
+    score, another the larger sum of its top three; topn = 1 keeps the first, topn = 3 the second."""
+    sb = np.zeros((1, 8), dtype=np.float32)
+    sb[0, :4] = [0.95, 0.10, 0.10, 0.10]       # group 0: max 0.95, top-3 sum 1.15
+    sb[0, 4:] = [0.60, 0.55, 0.50, 0.05]       # group 1: max 0.60, top-3 sum 1.65
+    z = np.log(sb / (1 - sb)).astype(np.float64)   # logits whose sigmoid gives back sb (bias 0)
+    u = z.reshape(1, 8)
+    e = np.eye(8)
+    b = np.zeros(8, dtype=np.float32)
+    r1 = oracle.route(u, e, b, 2, 1, 1, 2)
+    r3 = oracle.route(u, e, b, 2, 1, 3, 2)
+    assert list(r1["kept_groups"][0]) == [0] and list(r1["idx"][0]) == [0, 1]
+    assert list(r3["kept_groups"][0]) == [1] and list(r3["idx"][0]) == [4, 5]
+    for topn in (1, 3):
+        exp_idx, exp_groups = _brute_force(oracle.route(u, e, b, 2, 1, topn, 2)["sb32"][0], 2, 4, 1, 2, topn)
+        assert exp_groups == [0 if topn == 1 else 1]
 
 
 def test_p4_brute_force_c1_inputs():
