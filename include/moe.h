@@ -154,6 +154,26 @@ moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* top
                        void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * moe_permute_noalloc -- moe_permute without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, layouts,
+ * results and errors as moe_permute. Its scratch (the per-chunk expert masks
+ * and row bases) is a static 4 MiB array in the library, one per GPU, held
+ * until the process ends; its device address is looked up once per device
+ * on the first call made with that device current. No call allocates or
+ * frees memory. Every element of the scratch a call reads is first written by
+ * the same call, so nothing needs clearing between calls. Calls that overlap
+ * on one GPU (on different streams or threads) share the array and race:
+ * serialise them. MOE_E_UNSUPPORTED when the shape needs more scratch than
+ * moe_permute_noalloc_max_scratch() bytes (ceil(T / 64) * N_r * 12 + 256;
+ * e.g. T = 65536 with 256 experts needs 3 MiB).
+ */
+moe_status moe_permute_noalloc(const moe_shape* shape, moe_dtype act, const int32_t* topk_idx, const void* u,
+                               int32_t* expert_offsets, int32_t* perm_token, int32_t* row_of, void* a,
+                               moe_dtype a_dtype, float* a_scale, int32_t gather, void* stream);
+size_t moe_permute_noalloc_max_scratch(void);
+
+/*
  * moe_grouped_ffn -- per-expert SwiGLU FFN as one grouped GEMM pass over all experts:
  * y[r] = (SiLU(x W_g^T) * (x W_u^T)) W_d^T for every row r of every expert
  * (SwiGLU paragraph of "DeepSeek_V3_Report: Annotation", beta = 1; the three

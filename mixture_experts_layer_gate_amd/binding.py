@@ -49,6 +49,8 @@ _S = ctypes.POINTER(moe_shape)
 _SIGS = {
     "moe_route": [_S, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_permute": [_S, _I, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, ctypes.c_size_t, _P],
+    "moe_permute_noalloc": [_S, _I, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P],
+    "moe_permute_noalloc_max_scratch": [],
     "moe_grouped_ffn": [_S, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
     "moe_ffn_gate_up": [_S, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_ffn_down": [_S, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
@@ -87,7 +89,7 @@ def lib() -> ctypes.CDLL:
             for name, args in _SIGS.items():
                 f = getattr(L, name)
                 f.argtypes = args
-                f.restype = ctypes.c_size_t if name.endswith("_bytes") else ctypes.c_int
+                f.restype = ctypes.c_size_t if name.endswith(("_bytes", "_max_scratch")) else ctypes.c_int
             L.moe_workspace_bytes.restype = ctypes.c_size_t
             L.moe_last_error.restype = ctypes.c_char_p
             L.moe_version.restype = ctypes.c_char_p
@@ -164,6 +166,25 @@ def moe_permute(shape: moe_shape, topk_idx, u, expert_offsets, perm_token, row_o
     _check(lib().moe_permute(ctypes.byref(shape), act, _ptr(topk_idx), _ptr(u), _ptr(expert_offsets),
                              _ptr(perm_token), _ptr(row_of), _ptr(a), a_dtype if a_dtype is not None else act,
                              _ptr(a_scale), int(gather), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_permute_noalloc(shape: moe_shape, topk_idx, u, expert_offsets, perm_token, row_of, a=None, a_dtype=None,
+                        a_scale=None, gather=1, stream=None):
+    """moe_permute on the library's static scratch: no workspace, nothing allocated."""
+    T, d, N, K = shape.T, shape.d, shape.n_routed, shape.topk
+    _need(topk_idx, T * K, "topk_idx"); _need(expert_offsets, N + 1, "expert_offsets")
+    _need(perm_token, T * K, "perm_token"); _need(row_of, T * K, "row_of")
+    act = _dt(u) if u is not None else MOE_BF16
+    if a is not None:
+        rows = T * K if gather else T
+        _need(u, T * d, "u"); _need(a, rows * d, "a")
+        if a_dtype is None:
+            a_dtype = _dt(a)
+        if a_dtype in (MOE_F8E4M3, MOE_F8E4M3_POW2):
+            _need(a_scale, rows * (d // 128), "a_scale")
+    _check(lib().moe_permute_noalloc(ctypes.byref(shape), act, _ptr(topk_idx), _ptr(u), _ptr(expert_offsets),
+                                     _ptr(perm_token), _ptr(row_of), _ptr(a), a_dtype if a_dtype is not None else act,
+                                     _ptr(a_scale), int(gather), _stream(stream)))
 
 
 def _wscale_count(w: int, rows: int, cols: int) -> int:

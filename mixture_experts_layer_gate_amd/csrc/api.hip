@@ -81,6 +81,33 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 std::mutex g_cu_mutex;
 int g_cu[64];
 
+// Scratch of moe_permute_noalloc: one copy per GPU, held until the process
+// ends. Host code never uses the array's name as an address (on the host it is
+// a stand-in symbol): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and is kept per device.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64];
+
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_E_HIP, "permute_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_E_UNSUPPORTED, "permute_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_E_HIP, "permute_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -180,6 +207,25 @@ moe_status moe_permute(const moe_shape* shape, moe_dtype act, const int32_t* top
   }
   return finish(e, "moe_permute", st);
 }
+
+moe_status moe_permute_noalloc(const moe_shape* shape, moe_dtype act, const int32_t* topk_idx, const void* u,
+                               int32_t* expert_offsets, int32_t* perm_token, int32_t* row_of, void* a,
+                               moe_dtype a_dtype, float* a_scale, int32_t gather, void* stream) {
+  g_err.clear();
+  if (moe_status st = check_shape(shape); st != MOE_OK) return st;
+  const size_t need = moe::permute_ws_bytes(moe::to_shape(*shape));
+  if (need > kScratchBytes)
+    return fail(MOE_E_UNSUPPORTED,
+                "permute_noalloc: T=%d with %d experts needs %zu bytes of scratch, above its static %zu; "
+                "call moe_permute with a workspace",
+                shape->T, shape->n_routed, need, kScratchBytes);
+  void* ws = nullptr;
+  if (moe_status st = scratch_address(&ws); st != MOE_OK) return st;
+  return moe_permute(shape, act, topk_idx, u, expert_offsets, perm_token, row_of, a, a_dtype, a_scale, gather, ws,
+                     kScratchBytes, stream);
+}
+
+size_t moe_permute_noalloc_max_scratch(void) { return kScratchBytes; }
 
 }  // extern "C"
 
