@@ -77,7 +77,7 @@ def parse():
     return args
 
 
-FFN_SOURCES = {"bf16": ["ffn_bf16.hip", "gemm_pipe.h", "sched.h", "common.h"],
+FFN_SOURCES = {"bf16": ["ffn_bf16.hip", "gemm_w8.h", "gemm_pipe.h", "sched.h", "common.h"],
                "fp8": ["ffn_fp8.hip", "ffn_epi8.h", "gemm_pipe8.h", "gemm_pipe.h", "sched.h", "common.h"],
                "mxfp4": ["ffn_fp4.hip", "ffn_epi8.h", "gemm_pipe4.h", "gemm_pipe8.h", "gemm_pipe.h", "sched.h",
                          "common.h"]}
@@ -369,7 +369,7 @@ def run_forward(args, cfg, dev, pow2_act_scales=False):
     from mixture_experts_layer_gate_amd import MoELayer
 
     inp = generate(cfg, dev)
-    layer = MoELayer(cfg, inp, dev, pow2_act_scales=pow2_act_scales)
+    layer = MoELayer(cfg, inp, dev, pow2_act_scales=pow2_act_scales, keep_scores=False)
     u = inp["u"]
     stream = torch.cuda.current_stream()
     flush = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)

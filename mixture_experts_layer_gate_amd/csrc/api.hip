@@ -174,7 +174,9 @@ moe_status moe_route(const moe_shape* shape, moe_dtype act, const void* u, const
   const size_t need = moe::route_ws_bytes(s, act);
   if (!workspace || ws_bytes < need)
     return fail(MOE_E_WORKSPACE, "route: workspace of %zu bytes < %zu needed", ws_bytes, need);
-  if (!scores) scores = static_cast<float*>(workspace);
+  // the fp32 path computes the affinities in one kernel and selects in the next, so they go through memory:
+  // the workspace when the caller does not want them; the bf16 path writes them only when asked
+  if (!scores && act != MOE_BF16) scores = static_cast<float*>(workspace);
   auto st = static_cast<hipStream_t>(stream);
   return finish(moe::launch_route(s, act, u, centroids, bias, topk_idx, topk_gate, expert_load, scores, workspace, st),
                 "moe_route", st);

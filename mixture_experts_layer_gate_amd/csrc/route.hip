@@ -145,8 +145,8 @@ __device__ __forceinline__ void sum_slices(const float* __restrict__ part, int S
 constexpr int kSelWaves = 4;
 
 // part != nullptr: S partial logit sums per token (slice-major), added in
-// slice order, then s = Sigmoid(sum) is written to scores; otherwise scores
-// already holds the affinities.
+// slice order, then s = Sigmoid(sum) is written to scores (unless scores is
+// NULL); otherwise scores already holds the affinities.
 __global__ __launch_bounds__(64 * kSelWaves) void route_select_kernel(Shape s, const float* __restrict__ part,
                                                                       int S_part, float* __restrict__ scores,
                                                                       const float* __restrict__ bias,
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void route_select_kernel(Shape s, c
           float x[1];
           sum_slices<1>(part, S_part, static_cast<size_t>(s.T) * N, static_cast<size_t>(t) * N + e, 1, x);
           v = 1.0f / (1.0f + expf(-x[0]));
-          scores[static_cast<size_t>(t) * N + e] = v;
+          if (scores) scores[static_cast<size_t>(t) * N + e] = v;
         } else {
           v = scores[static_cast<size_t>(t) * N + e];
         }
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void route_select_reg_kernel(Shape s, const fl
         float x;
         if (part) {
           x = 1.0f / (1.0f + expf(-lg[v]));
-          scores[static_cast<size_t>(t) * N + e] = x;
+          if (scores) scores[static_cast<size_t>(t) * N + e] = x;
         } else {
           x = scores[static_cast<size_t>(t) * N + e];
         }

@@ -56,15 +56,20 @@ class MoELayer:
     input-gradient GEMMs and caches the SwiGLU inputs in forward_train, so that
     backward(d_out) returns du and leaves the centroid and expert-weight
     gradients in self.grads.
+
+    keep_scores=False skips writing the affinities s [T, N_r] in route (they
+    are only needed by balance_stats and the backward); the selection, gates
+    and loads are the same.
     """
 
     def __init__(self, cfg, weights: Dict[str, torch.Tensor], device="cuda", keep_bf16: bool = False,
                  gather_in_gemm: bool = True, pow2_act_scales: bool = False, tiled_bf16: bool = True,
-                 train: bool = False):
+                 train: bool = False, keep_scores: bool = True):
         self.cfg = cfg
         if train and cfg.gemm not in ("bf16", "fp8"):
             raise ValueError("MoELayer(train=True) needs bf16 or fp8 expert GEMMs")
         self.train = train
+        self.keep_scores = keep_scores or train
         self.shape = B.moe_shape.of(cfg)
         self.dev = torch.device(device)
         self.gemm = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_F8E4M3, "mxfp4": B.MOE_F4E2M1}[cfg.gemm]
@@ -190,7 +195,7 @@ class MoELayer:
     # ---------------------------------------------------------------- steps
     def route(self, u):
         B.moe_route(self.shape, u, self.centroids, self.bias, self.topk_idx, self.topk_gate, self.expert_load,
-                    self.scores, self.ws)
+                    self.scores if self.keep_scores else None, self.ws)
 
     def balance_stats(self, seq_len: int, alpha: float = 1e-4):
         """Eq. (17)-(20) on the last route's scores and selection: (f, P, loss) per run of seq_len tokens."""

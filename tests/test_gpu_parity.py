@@ -71,6 +71,26 @@ def test_route(name, over):
     assert max(len(set(row)) for row in (gi // S)) <= cfg.topk_groups
 
 
+@pytest.mark.parametrize("name", ["c1", "c3"])
+def test_route_without_scores(name):
+    """scores = NULL: the affinities are not written (bf16) or pass through the workspace (fp32); the
+    selection, gates and loads are bit-identical to a call that writes them."""
+    cfg, inp = _inputs(name)
+    sh = B.moe_shape.of(cfg)
+    T, K, N = cfg.T, cfg.topk, cfg.n_routed
+    outs = []
+    for with_scores in (True, False):
+        idx = torch.empty((T, K), dtype=torch.int32, device=DEV)
+        gate = torch.empty((T, K), dtype=torch.float32, device=DEV)
+        load = torch.empty((N,), dtype=torch.int32, device=DEV)
+        scores = torch.empty((T, N), dtype=torch.float32, device=DEV) if with_scores else None
+        B.moe_route(sh, inp["u"], inp["centroids"], inp["bias"], idx, gate, load, scores, _ws(cfg))
+        torch.cuda.synchronize()
+        outs.append((idx.cpu(), gate.cpu(), load.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_route_exact_ties():
     """Exact ties follow the tie rule: experts in classes of four identical ones (same centroid and bias; groups
     4..7 copy groups 0..3, so groups tie too). Within a class, a picked expert's lower-index twins are picked."""
