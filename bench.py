@@ -78,7 +78,7 @@ def parse():
 
 
 FFN_SOURCES = {"bf16": ["ffn_bf16.hip", "gemm_w8.h", "gemm_pipe.h", "sched.h", "common.h"],
-               "fp8": ["ffn_fp8.hip", "ffn_epi8.h", "gemm_pipe8.h", "gemm_pipe.h", "sched.h", "common.h"],
+               "fp8": ["ffn_fp8.hip", "ffn_epi8.h", "gemm_f8w.h", "gemm_pipe8.h", "gemm_pipe.h", "sched.h", "common.h"],
                "mxfp4": ["ffn_fp4.hip", "ffn_epi8.h", "gemm_pipe4.h", "gemm_pipe8.h", "gemm_pipe.h", "sched.h",
                          "common.h"]}
 

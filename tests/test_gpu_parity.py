@@ -699,6 +699,55 @@ def test_grouped_ffn_fp8_tile_shapes(inter, mode):
         assert same > 0.99 and sdiff < 1e-4
 
 
+@pytest.mark.parametrize("mode", ["gather", "direct"])
+def test_grouped_ffn_fp8_eight_wave_blocks(mode):
+    """The eight-wave fp8 loop (K % 1024 == 0, whole 256-column output tiles): 256-row token blocks of one to
+    eight 32-row sub-tiles, experts just over 256 rows split into two near-equal blocks, empty experts. d = 3072
+    gives the gate/up K loop three token-scale windows (an odd count, so the window slots alternate across the
+    four output-column tiles a unit streams); I = 2048 gives down two windows and d / 256 = 12 output tiles
+    (three units of four). H codes and scales are compared as well."""
+    cfg = get_config("c2", gemm="fp8", n_routed=10, n_groups=1, topk_groups=1, T=1024, topk=2, d=3072, inter=2048)
+    inp = generate(cfg, DEV)
+    sh = B.moe_shape.of(cfg)
+    sizes = [0, 1, 31, 33, 129, 255, 256, 257, 300, 520]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    assert n <= cfg.T * cfg.topk
+    src = np.random.default_rng(29).integers(0, cfg.T, n)
+    u32 = inp["u"].cpu().float().numpy()
+    uq, us = oracle.quantize_tiles(u32)
+    wq = [oracle_wq(cfg, inp, e) for e in range(cfg.n_routed)]
+    dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    wgu = dev8(np.stack([tile_e4m3(w[0], True) for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
+    wdn = dev8(np.stack([tile_e4m3(w[2], False) for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
+    h = torch.empty((n + 1, cfg.inter), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((n + 1, cfg.inter // 128), dtype=torch.float32, device=DEV)
+    h[n] = 0x5A
+    hs[n] = 3.0
+    y = torch.full((n + 1, cfg.d), 7.0, dtype=torch.bfloat16, device=DEV)
+    if mode == "gather":
+        a, a_s, a_rows, rmode, rsrc = dev8(uq), dev8(us), cfg.T, B.MOE_ROWS_GATHER, _i32(src)
+    else:
+        a, a_s, a_rows, rmode, rsrc = dev8(uq[src]), dev8(us[src]), n, B.MOE_ROWS_DIRECT, None
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    B.moe_ffn_gate_up(sh, B.MOE_F8E4M3, cfg.n_routed, n, _i32(off), rmode, rsrc, a, a_s, a_rows, wgu, wgs, h[:n],
+                      hs[:n], ws)
+    B.moe_ffn_down(sh, B.MOE_F8E4M3, cfg.n_routed, n, _i32(off), h[:n], hs[:n], wdn, wds, y[:n], ws)
+    torch.cuda.synchronize()
+    # nothing past the last row is written
+    assert torch.all(h[n] == 0x5A) and torch.all(hs[n] == 3.0) and torch.all(y[n] == 7.0)
+    for e in range(cfg.n_routed):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        ref, aux = oracle.ffn_fp8(u32[src[lo:hi]], *wq[e], return_h=True)
+        report(f"fp8 eight-wave {mode} expert {e} ({hi - lo} rows) y", rel_l2(y[lo:hi], ref), TOL["fp8"])
+        same = float(np.mean(h[lo:hi].cpu().numpy() == aux["h_codes"]))
+        sdiff = np.max(np.abs(hs[lo:hi].cpu().numpy() / aux["h_scale"] - 1))
+        print(f"[parity] expert {e}: H codes equal {same:.4f}, max rel scale diff {sdiff:.2e}")
+        assert same > 0.99 and sdiff < 1e-4
+
+
 @pytest.mark.parametrize("d,inter", [(10240, 256), (256, 10240)])
 def test_grouped_ffn_fp8_max_k(d, inter):
     """fp8 at the largest supported K, 10240 = 80 chunks of 128: in the gate/up projection (d) and in the down
