@@ -390,8 +390,11 @@ def run_forward(args, cfg, dev, pow2_act_scales=False):
 
     if args.calib_copy_mib > 0:
         calib_copy(args.calib_copy_mib, dev)
-    for _ in range(args.warmup):
+    # the load of every step run (warmup, timed, back to back), to price each launch a profiler sees
+    all_loads = torch.empty((args.warmup + 2 * args.steps, cfg.n_routed), dtype=torch.int32, device=dev)
+    for w in range(args.warmup):
         step()
+        all_loads[w].copy_(layer.expert_load)
     torch.cuda.synchronize()
     n_calls = len(CALLS)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)] for _ in range(args.steps)]
@@ -406,11 +409,13 @@ def run_forward(args, cfg, dev, pow2_act_scales=False):
         torch.cuda.synchronize()
         wall.append(time.perf_counter() - t0)
         loads[i].copy_(layer.expert_load)
+        all_loads[args.warmup + i].copy_(layer.expert_load)
     torch.cuda.synchronize()
     # the same steps back to back with no flush and no synchronisation between them, for context
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         step()
+        all_loads[args.warmup + args.steps + i].copy_(layer.expert_load)
     torch.cuda.synchronize()
     ms_b2b = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_step = float(np.mean(wall)) * 1e3
@@ -469,6 +474,7 @@ def run_forward(args, cfg, dev, pow2_act_scales=False):
         "layer": {"algorithmic_GB": layer_bytes / 1e9, "roofline_ms": max(layer_bytes / HBM_PEAK,
                   (ffn_flops + cfg.router_flops()) / MFMA_PEAK[cfg.gemm]) * 1e3,
                   "experts_touched": int(touched[-1]), "experts_touched_range": [int(touched.min()), int(touched.max())],
+                  "experts_touched_every_step": [int(x) for x in (all_loads.cpu().numpy() > 0).sum(axis=1)],
                   "max_load": int(load[-1].max()), "min_load": int(load[-1].min())},
         "step_ms_events": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
         "inp": inp, "layer_obj": layer,

@@ -97,9 +97,16 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+# MOE_SYNC_DEBUG=1: wait for the device after every call, so an asynchronous kernel error surfaces at the
+# call that caused it
+_SYNC_DEBUG = os.environ.get("MOE_SYNC_DEBUG") == "1"
+
+
 def _check(status: int):
     if status != MOE_OK:
         raise MoEError(status, lib().moe_last_error().decode())
+    if _SYNC_DEBUG:
+        torch.cuda.synchronize()
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -24,6 +24,7 @@ from typing import Dict, Optional
 import torch
 
 from . import binding as B
+from .state import load_bias_state, save_bias_state
 
 
 @dataclass
@@ -84,6 +85,7 @@ class MoELayer:
         to = lambda t: t.to(self.dev).contiguous()
         self.centroids = to(weights["centroids"])
         self.bias = weights["bias"].to(self.dev, torch.float32).clone()  # layer-owned state
+        self.step_count = 0                                               # bias updates applied so far
         self.act_dtype = self.centroids.dtype
         N, Ns = cfg.n_routed, cfg.n_shared
         self.w = {}
@@ -318,6 +320,18 @@ class MoELayer:
 
     def bias_update(self):
         B.moe_bias_update(self.shape, self.expert_load, self.cfg.gamma, self.bias)
+        self.step_count += 1
+
+    def save_state(self, path: str) -> None:
+        """Write the layer's persistent state (the expert bias and the step counter) to path; it waits for
+        the work queued on the current stream, so the bias is the one after the last queued update."""
+        save_bias_state(path, self.bias.cpu().numpy(), self.step_count)
+
+    def load_state(self, path: str) -> None:
+        """Restore the expert bias and the step counter written by save_state (bit-exact)."""
+        b, step = load_bias_state(path, self.cfg.n_routed)
+        self.bias.copy_(torch.from_numpy(b).to(self.dev))
+        self.step_count = step
 
     def forward(self, u: torch.Tensor) -> torch.Tensor:
         """Layer output for tokens u [T, d] (no bias update)."""

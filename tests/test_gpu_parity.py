@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from moe_inputs import get_config, generate, generate_expert
+from moe_inputs import get_config, generate, generate_expert, generate_tokens
 from mixture_experts_layer_gate_amd import binding as B
 from mixture_experts_layer_gate_amd import MoELayer
 from gpu_common import i32, inputs, oracle_ffn_rows, oracle_route, oracle_wq, workspace
@@ -627,6 +627,32 @@ def test_bias_update_bit_exact():
     B.moe_bias_update(sh, _i32(load), 0.001, bias)
     torch.cuda.synchronize()
     assert np.array_equal(bias.cpu().numpy(), oracle.bias_update(b0, load, cfg.T, cfg.topk, 0.001))
+
+
+def test_bias_state_resume(tmp_path):
+    """Checkpoint and resume of the balancing state: a layer saved after 3 steps of the Zipf-skewed decode
+    routing and reloaded into a fresh layer continues the bias trajectory bit for bit (same tokens per step),
+    with the step counter restored; the file holds the bias exactly as the device had it."""
+    cfg = get_config("c5", gemm="bf16", T=96, d=512, inter=256, n_routed=64)
+    inp = generate(cfg, DEV)
+    a = MoELayer(cfg, inp, DEV, keep_scores=False)
+    for step in range(3):
+        a.step(generate_tokens(cfg, DEV, step))
+    path = str(tmp_path / "bias.bin")
+    a.save_state(path)
+    saved = a.bias.cpu().numpy().copy()
+    for step in range(3, 6):
+        a.step(generate_tokens(cfg, DEV, step))
+    b = MoELayer(cfg, inp, DEV, keep_scores=False)
+    assert not np.array_equal(b.bias.cpu().numpy(), saved)
+    b.load_state(path)
+    assert b.step_count == 3 and np.array_equal(b.bias.cpu().numpy().view(np.uint32), saved.view(np.uint32))
+    for step in range(3, 6):
+        b.step(generate_tokens(cfg, DEV, step))
+    torch.cuda.synchronize()
+    assert b.step_count == a.step_count == 6
+    assert np.array_equal(b.bias.cpu().numpy().view(np.uint32), a.bias.cpu().numpy().view(np.uint32))
+    assert not np.array_equal(a.bias.cpu().numpy(), saved)
 
 
 # ------------------------------------------------------------------ fp8 (E4M3, 1x128 / 128x128 scales)
