@@ -183,6 +183,9 @@ BWD8_CASES = [
     ("c1", dict(gemm="fp8", act="bf16")),
     ("c1", dict(gemm="fp8", act="bf16", T=200, inter=384)),     # ragged T, 1.5 tiles of I, 128-row blocks cut short
     ("c2", dict(gemm="fp8")),
+    # K % 1024 == 0 and whole 256-column tiles everywhere: every fp8 GEMM of the step on the eight-wave loop
+    # (gate/up with the E4M3 cache, down, and both Dgrad GEMMs, dh with fp32 output)
+    ("c2", dict(gemm="fp8", inter=2048)),
     ("c5", dict(T=96, d=512, inter=256, n_routed=64)),            # Zipf-skewed, empty experts
 ]
 

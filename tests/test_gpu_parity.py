@@ -874,12 +874,14 @@ def test_fp8_accumulation_k4096():
     assert 0.01 < err_lim < 0.03
 
 
-def test_fp8_layer_two_phase_calls():
+@pytest.mark.parametrize("inter", [1408, 2048])
+def test_fp8_layer_two_phase_calls(inter):
     """The fp8 layer through the two-phase calls (moe_ffn_gate_up, moe_ffn_down) and the separate shared
     call, on the mid shape: token quantisation bit for bit, sampled experts with their H codes, the shared
-    expert on 64 tokens and the output on 3 tokens."""
+    expert on 64 tokens and the output on 3 tokens. inter = 1408 sends the down projection to the four-wave
+    loop (K % 1024 != 0), inter = 2048 both projections to the eight-wave one."""
     name = "c2"
-    cfg, inp = _inputs(name, gemm="fp8")
+    cfg, inp = _inputs(name, gemm="fp8", inter=inter)
     T, K, N, d = cfg.T, cfg.topk, cfg.n_routed, cfg.d
     layer = MoELayer(cfg, inp, DEV)
     layer.route(inp["u"])
