@@ -182,13 +182,11 @@ __device__ __forceinline__ int f8w_wb(int j) { return GATE_UP ? (j >= 2 ? 1 : 0)
 template <bool GATE_UP>
 constexpr int f8w_nwb() { return GATE_UP ? 2 : 1; }
 
-template <int MS, bool GATE_UP>
 struct F8WFrame {
   float fac[2][F8W::TT];   // f of the current chunk per (weight-scale index, token sub-tile)
   float r[2][F8W::TT];     // f_c / f_{c+1}, or 1
 };
 
-template <int MS>
 __device__ __forceinline__ void f8w_scale_tile(f32x16& a, float r) {
 #pragma unroll
   for (int v = 0; v < 16; ++v) a[v] *= r;
@@ -211,7 +209,7 @@ __device__ __forceinline__ void f8w_scale_loads(F8WScales& sc, const uint8_t* ld
 }
 // fac := factors of the scales in sc (r := fac_old / fac_new when `next`, else 1).
 template <int MS, bool GATE_UP>
-__device__ __forceinline__ void f8w_frame_update(F8WFrame<MS, GATE_UP>& fr, const F8WScales& sc, bool next,
+__device__ __forceinline__ void f8w_frame_update(F8WFrame& fr, const F8WScales& sc, bool next,
                                                  bool first) {
 #pragma unroll
   for (int b = 0; b < f8w_nwb<GATE_UP>(); ++b)
@@ -228,11 +226,11 @@ __device__ __forceinline__ void f8w_frame_update(F8WFrame<MS, GATE_UP>& fr, cons
 // before MFMA m.
 template <int MS, bool GATE_UP, bool FIRST>
 __device__ __forceinline__ void f8w_mma_lo(const i32x8 (&w)[F8W::TW], const i32x8 (&t)[F8W::TT],
-                                           f32x16 (&acc)[F8W::TW][F8W::TT], const F8WFrame<MS, GATE_UP>& fr) {
+                                           f32x16 (&acc)[F8W::TW][F8W::TT], const F8WFrame& fr) {
   constexpr int M = 2 * MS, D = MS > 0 ? MS : 1;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    if (FIRST) f8w_scale_tile<MS>(acc[2 + m / D][m % D], fr.r[f8w_wb<GATE_UP>(2)][m % D]);
+    if (FIRST) f8w_scale_tile(acc[2 + m / D][m % D], fr.r[f8w_wb<GATE_UP>(2)][m % D]);
     acc[m / D][m % D] = mfma_f8(w[m / D], t[m % D], acc[m / D][m % D]);
     sched_fence();
   }
@@ -246,7 +244,7 @@ __device__ __forceinline__ void f8w_mma_lo(const i32x8 (&w)[F8W::TW], const i32x
 // before the barrier).
 template <int MS, int LT, bool GATE_UP, bool SECOND, bool ISSUE>
 __device__ __forceinline__ void f8w_mma_hi(const i32x8 (&w)[F8W::TW], const i32x8 (&t)[F8W::TT],
-                                           f32x16 (&acc)[F8W::TW][F8W::TT], const F8WFrame<MS, GATE_UP>& fr,
+                                           f32x16 (&acc)[F8W::TW][F8W::TT], const F8WFrame& fr,
                                            const F8WRows& rows, uint8_t* lds, int ls, int lks) {
   constexpr int M = 2 * MS, D = MS > 0 ? MS : 1;
   constexpr int L = ISSUE ? F8W::WL + LT : 0;
@@ -260,7 +258,7 @@ __device__ __forceinline__ void f8w_mma_hi(const i32x8 (&w)[F8W::TW], const i32x
       }
     if (n < M) {
       acc[2 + n / D][n % D] = mfma_f8(w[2 + n / D], t[n % D], acc[2 + n / D][n % D]);
-      if (SECOND) f8w_scale_tile<MS>(acc[n / D][n % D], fr.r[f8w_wb<GATE_UP>(0)][n % D]);
+      if (SECOND) f8w_scale_tile(acc[n / D][n % D], fr.r[f8w_wb<GATE_UP>(0)][n % D]);
       sched_fence();
     }
   }
@@ -289,7 +287,7 @@ template <int MS, int LT, bool GATE_UP, bool SECOND, int WAIT, bool ISSUE>
 __device__ __forceinline__ void f8w_stage(const F8WRows& rows, uint8_t* lds, const F8WOffs& o, int g, int kt, int nk,
                                           int kc, int seg, int nseg, i32x8 (&w)[F8W::TW],
                                           const i32x8 (&T0)[F8W::TT], i32x8 (&T1)[F8W::TT],
-                                          f32x16 (&acc)[F8W::TW][F8W::TT], F8WFrame<MS, GATE_UP>& fr) {
+                                          f32x16 (&acc)[F8W::TW][F8W::TT], F8WFrame& fr) {
   using P = F8W;
   const int c = kt >> 1, nwin = kc / P::WIN, gw = seg * nwin + (c >> 3);
   f8w_mma_lo<MS, GATE_UP, !SECOND>(w, T0, acc, fr);
@@ -326,12 +324,12 @@ __device__ __forceinline__ void f8w_stage(const F8WRows& rows, uint8_t* lds, con
 // epilogue, then acc restarts from zero in the frame of the next block's
 // first chunk (its window landed with the stages since it was issued).
 template <int MS, bool GATE_UP, class EPI>
-__device__ __forceinline__ void f8w_finish(f32x16 (&acc)[F8W::TW][F8W::TT], F8WFrame<MS, GATE_UP>& fr, EPI& epi,
+__device__ __forceinline__ void f8w_finish(f32x16 (&acc)[F8W::TW][F8W::TT], F8WFrame& fr, EPI& epi,
                                            int seg, int nseg, int kc, const uint8_t* lds) {
 #pragma unroll
   for (int j = 0; j < F8W::TW; ++j)
 #pragma unroll
-    for (int i = 0; i < MS; ++i) f8w_scale_tile<MS>(acc[j][i], fr.fac[f8w_wb<GATE_UP>(j)][i]);
+    for (int i = 0; i < MS; ++i) f8w_scale_tile(acc[j][i], fr.fac[f8w_wb<GATE_UP>(j)][i]);
   epi(seg, acc);
 #pragma unroll
   for (int j = 0; j < F8W::TW; ++j)
@@ -369,7 +367,7 @@ __device__ __forceinline__ void f8w_stream(const F8WRows& rows, int K, int nseg,
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(3 * LPS) : "memory");
   const F8WOffs o = f8w_offsets();
   f32x16 acc[P::TW][P::TT];
-  F8WFrame<MS, GATE_UP> fr;
+  F8WFrame fr;
 #pragma unroll
   for (int j = 0; j < P::TW; ++j)
 #pragma unroll
