@@ -62,13 +62,14 @@ __device__ __forceinline__ void gate_up_tile(const W8Rows& rows, int d, int I, c
     for (int i = 0; i < 5; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-  const int ww = (threadIdx.x >> 6) & 3, h = (threadIdx.x & 63) >> 5;
+  const int ww = wave_uniform((w8_tid() >> 6) & 3);
   const int wr0 = 128 * (ww >> 1) + 32 * (ww & 1);
   const W8Offs o = w8_offsets(wr0, wr0 + 64);
   w8_mainloop<P, MS, LT>(rows, d, lds, o, acc);
+  const int tid = w8_tid(), h = (tid & 63) >> 5;
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
-    const int tr = w8_token_row(i);
+    const int tr = w8_token_row(i, tid);
     if (tr < un.rows) {
       const int c0 = un.nb * kHcols + ww * 32 + 4 * h;
       uint16_t* hrow = H + static_cast<size_t>(un.m0 + tr) * I + c0;
@@ -103,12 +104,13 @@ __device__ __forceinline__ void down_tile(const W8Rows& rows, int d, int I, cons
     for (int i = 0; i < 5; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-  const int ww = (threadIdx.x >> 6) & 3, h = (threadIdx.x & 63) >> 5;
+  const int ww = wave_uniform((w8_tid() >> 6) & 3);
   const W8Offs o = w8_offsets(64 * ww, 64 * ww + 32);
   w8_mainloop<P, MS, LT>(rows, I, lds, o, acc);
+  const int tid = w8_tid(), h = (tid & 63) >> 5;
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
-    const int tr = w8_token_row(i);
+    const int tr = w8_token_row(i, tid);
     if (tr < un.rows) {
       uint16_t* yrow = y + static_cast<size_t>(un.m0 + tr) * d;
 #pragma unroll
@@ -142,12 +144,13 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_gate_up_bf16_kernel(
     if (s_first < 0) s_first = 0;
     W8Rows rows;
     rows.trs = pipe_rsrc(a, static_cast<uint64_t>(a_rows) * d * 2);
+    const int tid = w8_tid();
 #pragma unroll
     for (int q = 0; q < FP::TLMAX; ++q) {
-      const int r = w8_load_row(w8_unit(q));
+      const int u = w8_unit(q, tid), r = w8_load_row(u, tid);
       int sr = r < un.rows ? source_row(mode, row_src, un.m0 + r, un.seg0, a_rows) : -1;
       if (sr < 0) sr = s_first;                       // rows past the block: any valid row, never stored
-      rows.ot[q] = (static_cast<uint32_t>(sr) * d + w8_load_chunk(w8_unit(q)) * 8) * 2;
+      rows.ot[q] = (static_cast<uint32_t>(sr) * d + w8_load_chunk(u, tid) * 8) * 2;
     }
     if (P::TILED) {                                   // tile nb: the gate and up rows of H columns 128 nb ..
       rows.wrs = pipe_rsrc(wgu + (static_cast<size_t>(un.e) * NB + un.nb) * FP::BW * d,
@@ -156,10 +159,10 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_gate_up_bf16_kernel(
       rows.wrs = pipe_rsrc(wgu + static_cast<size_t>(un.e) * 2 * I * d, static_cast<uint64_t>(2 * I) * d * 2);
 #pragma unroll
       for (int q = 0; q < FP::WL; ++q) {
-        const int u = q * 8 + (threadIdx.x >> 6), rw = w8_load_row(u);
+        const int u = w8_unit(q, tid), rw = w8_load_row(u, tid);
         const int j = (rw >> 5) & 3;                  // sub-tiles 0,1 of each 128: gate rows; 2,3: the matching up rows
         const int hcol = un.nb * kHcols + (rw >> 7) * 64 + (j & 1) * 32 + (rw & 31);
-        rows.ow[q] = (static_cast<uint32_t>(j >= 2 ? I + hcol : hcol) * d + w8_load_chunk(u) * 8) * 2;
+        rows.ow[q] = (static_cast<uint32_t>(j >= 2 ? I + hcol : hcol) * d + w8_load_chunk(u, tid) * 8) * 2;
       }
     }
 #define GU_CALL(MS, LT) gate_up_tile<P, MS, LT>(rows, d, I, un, lds_p, H, GU)
@@ -186,10 +189,11 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_down_bf16_kernel(int d, int I, 
     const Unit un = find_unit_balanced(t, off, E, n_rows, FP::MAXSUB, cum);
     W8Rows rows;
     rows.trs = pipe_rsrc(H, static_cast<uint64_t>(n_rows) * I * 2);
+    const int tid = w8_tid();
 #pragma unroll
     for (int q = 0; q < FP::TLMAX; ++q) {
-      const int r = w8_load_row(w8_unit(q));
-      rows.ot[q] = (static_cast<uint32_t>(un.m0 + (r < un.rows ? r : 0)) * I + w8_load_chunk(w8_unit(q)) * 8) * 2;
+      const int u = w8_unit(q, tid), r = w8_load_row(u, tid);
+      rows.ot[q] = (static_cast<uint32_t>(un.m0 + (r < un.rows ? r : 0)) * I + w8_load_chunk(u, tid) * 8) * 2;
     }
     if (P::TILED) {                                   // ceil(d / 256) tiles per expert, the last padded with zeros
       rows.wrs = pipe_rsrc(wd + (static_cast<size_t>(un.e) * NB + un.nb) * FP::BW * I,
@@ -198,9 +202,9 @@ __global__ __launch_bounds__(FP::NT, 1) void ffn_down_bf16_kernel(int d, int I, 
       rows.wrs = pipe_rsrc(wd + static_cast<size_t>(un.e) * d * I, static_cast<uint64_t>(d) * I * 2);
 #pragma unroll
       for (int q = 0; q < FP::WL; ++q) {
-        const int u = q * 8 + (threadIdx.x >> 6);
+        const int u = w8_unit(q, tid);
         rows.ow[q] =
-            (static_cast<uint32_t>(min(un.nb * FP::BW + w8_load_row(u), d - 1)) * I + w8_load_chunk(u) * 8) * 2;
+            (static_cast<uint32_t>(min(un.nb * FP::BW + w8_load_row(u, tid), d - 1)) * I + w8_load_chunk(u, tid) * 8) * 2;
       }
     }
 #define DN_CALL(MS, LT) down_tile<P, MS, LT>(rows, d, I, un, lds_p, y)

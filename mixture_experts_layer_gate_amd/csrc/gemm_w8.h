@@ -58,9 +58,20 @@ constexpr int w8_min_token_loads() {
   return LT * 8 <= W8<false>::TU ? LT : LT - 1;      // the waves with the fewest units in their last slot
 }
 
-// Tile row and logical 16-byte K chunk of this thread's load in unit u.
-__device__ __forceinline__ int w8_load_row(int u) { return u * 16 + ((threadIdx.x & 63) >> 2); }
-__device__ __forceinline__ int w8_load_chunk(int u) { return (threadIdx.x & 3) ^ ((w8_load_row(u) >> 2) & 3); }
+// threadIdx.x behind an opaque copy: lane-derived per-tile values computed from it are recomputed for
+// every tile instead of being hoisted out of a persistent kernel's tile loop (where each would hold a
+// register for the whole kernel).
+__device__ __forceinline__ int w8_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Token load unit of slot q, tile row and logical 16-byte K chunk of this thread's load in unit u
+// (tid: the thread index, from w8_tid in per-tile set-up code).
+__device__ __forceinline__ int w8_unit(int q, int tid) { return q * 8 + (tid >> 6); }
+__device__ __forceinline__ int w8_load_row(int u, int tid) { return u * 16 + ((tid & 63) >> 2); }
+__device__ __forceinline__ int w8_load_chunk(int u, int tid) { return (tid & 3) ^ ((w8_load_row(u, tid) >> 2) & 3); }
 
 struct W8Rows {
   __amdgpu_buffer_rsrc_t wrs, trs;
@@ -68,13 +79,17 @@ struct W8Rows {
   uint32_t ot[3];       // token loads: source row * K * 2 + chunk * 16
 };
 
+// Weight loads are non-temporal: a tile's weights are read once, and marking them for early eviction
+// keeps the token rows, which the block's other output tiles read again, in L2. kCachePolicyNT is the
+// cache-policy operand of a gfx950 buffer load with its nt bit (bit 1) set.
+constexpr int kCachePolicyNT = 2;
 template <class P>
 __device__ __forceinline__ void w8_issue_w(const W8Rows& r, uint8_t* st, int kb, int q) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t vo = P::TILED ? static_cast<uint32_t>(((q * 8 + w) * 64 + (threadIdx.x & 63)) * 16) : r.ow[q];
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r.wrs, (lds_void_t*)(st + (q * 8 + w) * 1024), 16, vo,
-                                           P::TILED ? kb * (P::W_BYTES / P::ROWB) : kb, 0, 0);
+                                           P::TILED ? kb * (P::W_BYTES / P::ROWB) : kb, 0, kCachePolicyNT);
 #endif
 }
 
@@ -101,7 +116,8 @@ struct W8Offs {
 };
 
 __device__ __forceinline__ W8Offs w8_offsets(int wr0, int wr1) {
-  const int l = threadIdx.x & 63, wt = threadIdx.x >> 8;
+  const int tid = w8_tid();
+  const int l = tid & 63, wt = tid >> 8;
   const int cofs = ((l >> 5) ^ (((l & 31) >> 2) & 3)) * 16;
   return {(wr0 + (l & 31)) * 64 + cofs, (wr1 + (l & 31)) * 64 + cofs,
           W8<false>::W_BYTES + (wt * 32 + (l & 31)) * 64 + cofs};
@@ -184,8 +200,6 @@ __device__ __forceinline__ void w8_mainloop(const W8Rows& rows, int K, uint8_t* 
 }
 
 // Token row (within the tile) of accumulator column l % 32 of token sub-tile i.
-__device__ __forceinline__ int w8_token_row(int i) {
-  return 32 * (2 * i + (threadIdx.x >> 8)) + (threadIdx.x & 31);
-}
+__device__ __forceinline__ int w8_token_row(int i, int tid) { return 32 * (2 * i + (tid >> 8)) + (tid & 31); }
 
 }  // namespace moe

@@ -565,10 +565,13 @@ def test_tile_weights_bf16_bit_exact(kind):
         assert np.array_equal(got[e], tile_e4m3(raw[e], kind == "gate_up"))
 
 
-@pytest.mark.parametrize("d,mode", [(2048, "gather"), (2048, "direct"), (384, "gather")])
+@pytest.mark.parametrize("d,mode", [(2048, "gather"), (2048, "direct"), (384, "gather"), (1408, "gather"),
+                                    (3328, "direct")])
 def test_grouped_ffn_bf16_tiled_equals_row_major(d, mode):
     """MOE_BF16_TILED only changes where the weight bytes are read from: its outputs equal MOE_BF16's bit for bit
-    (c2-sized experts; d = 384 pads the last down tile)."""
+    (c2-sized experts). The tiled down kernel runs up to four column tiles of a block as one stream: d = 2048 is
+    two full streams, d = 384 one stream of a full and a 128-column tile, d = 1408 a stream of four and one of two
+    ending in a 128-column tile, d = 3328 streams of 4, 4, 4 and 1 tiles. Nothing is written past the last row."""
     cfg = get_config("c2", n_routed=6, n_groups=1, topk_groups=1, T=1024, topk=2, d=d, inter=1408)
     inp = generate(cfg, DEV)
     sh = B.moe_shape.of(cfg)
@@ -585,11 +588,13 @@ def test_grouped_ffn_bf16_tiled_equals_row_major(d, mode):
     B.moe_tile_weights_bf16(inp["w_gate_up"], tg, gate_up=True)
     B.moe_tile_weights_bf16(inp["w_down"], td, gate_up=False)
     y0 = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
-    y1 = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    y1g = torch.full((n + 1, d), 7.0, dtype=torch.bfloat16, device=DEV)    # one guard row past the end
+    y1 = y1g[:n]
     B.moe_grouped_ffn(sh, B.MOE_BF16, 6, n, _i32(off), m, rs, a, None, a_rows, inp["w_gate_up"], None, inp["w_down"],
                       None, y0, _ws(cfg))
     B.moe_grouped_ffn(sh, B.MOE_BF16_TILED, 6, n, _i32(off), m, rs, a, None, a_rows, tg, None, td, None, y1, _ws(cfg))
     torch.cuda.synchronize()
+    assert torch.all(y1g[n] == 7.0)
     assert torch.equal(y0, y1)
     ref = _oracle_ffn_rows(cfg, inp, 5, src[off[5]:off[6]])
     report(f"tiled bf16 d={d} expert 5 y", rel_l2(y1[off[5]:off[6]], ref), TOL["bf16"])
