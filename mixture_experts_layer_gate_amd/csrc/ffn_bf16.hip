@@ -33,22 +33,6 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, floa
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
 }
 
-// Live token sub-tiles of this wave (token half wt takes sub-tiles wt, wt + 2, ...) and token load slots.
-__device__ __forceinline__ int w8_live(int nsub) { return (nsub + 1 - (threadIdx.x >> 8)) / 2; }
-
-// Calls f(MS, LT) as compile-time constants for a block of nsub (1..10) sub-tiles.
-#define W8_DISPATCH(nsub, CALL)                                                    \
-  do {                                                                             \
-    const int ms_ = w8_live(nsub), lt_ = ((nsub) + 3) / 4;                        \
-    if (lt_ == 1) {                                                                \
-      if (ms_ == 2) CALL(2, 1); else if (ms_ == 1) CALL(1, 1); else CALL(0, 1);   \
-    } else if (lt_ == 2) {                                                         \
-      if (ms_ == 4) CALL(4, 2); else if (ms_ == 3) CALL(3, 2); else CALL(2, 2);   \
-    } else {                                                                       \
-      if (ms_ == 5) CALL(5, 3); else CALL(4, 3);                                   \
-    }                                                                              \
-  } while (0)
-
 // One gate/up tile: wave quarter ww holds the gate rows of H columns 32 ww .. 32 ww + 31 of the tile
 // (tile rows 128 (ww >> 1) + 32 (ww & 1) ..) and the matching up rows (64 tile rows further), so the
 // SwiGLU product forms in registers.

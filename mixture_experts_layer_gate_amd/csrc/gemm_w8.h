@@ -199,6 +199,22 @@ __device__ __forceinline__ void w8_mainloop(const W8Rows& rows, int K, uint8_t* 
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Live token sub-tiles of this wave (token half wt takes sub-tiles wt, wt + 2, ...) and token load slots.
+__device__ __forceinline__ int w8_live(int nsub) { return (nsub + 1 - (threadIdx.x >> 8)) / 2; }
+
+// Calls f(MS, LT) as compile-time constants for a block of nsub (1..10) sub-tiles.
+#define W8_DISPATCH(nsub, CALL)                                                    \
+  do {                                                                             \
+    const int ms_ = w8_live(nsub), lt_ = ((nsub) + 3) / 4;                        \
+    if (lt_ == 1) {                                                                \
+      if (ms_ == 2) CALL(2, 1); else if (ms_ == 1) CALL(1, 1); else CALL(0, 1);   \
+    } else if (lt_ == 2) {                                                         \
+      if (ms_ == 4) CALL(4, 2); else if (ms_ == 3) CALL(3, 2); else CALL(2, 2);   \
+    } else {                                                                       \
+      if (ms_ == 5) CALL(5, 3); else CALL(4, 3);                                   \
+    }                                                                              \
+  } while (0)
+
 // Token row (within the tile) of accumulator column l % 32 of token sub-tile i.
 __device__ __forceinline__ int w8_token_row(int i, int tid) { return 32 * (2 * i + (tid >> 8)) + (tid & 31); }
 

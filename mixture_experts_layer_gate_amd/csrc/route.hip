@@ -10,7 +10,9 @@
 
 #include "common.h"
 #include "gemm_pipe.h"
+#include "gemm_w8.h"
 #include "launch.h"
+#include "sched.h"
 
 namespace moe {
 
@@ -69,6 +71,81 @@ __global__ __launch_bounds__(RouteTile::NT, 1) void route_logits_bf16_kernel(
   }
 }
 
+// The same product on the eight-wave loop of the expert GEMMs (gemm_w8.h),
+// for N % 4 == 0: tiles of 256 centroids x 256 tokens (eight 32-row token
+// sub-tiles of the loop's ten), K split into S slices of whole 128-wide
+// chunks. At the V3 shape that is 32 token tiles x 8 slices, one per CU, each
+// streaming 0.92 MB (the 128-token tiles above: 1.38 MB) at the loop's
+// per-CU rate. Wave quarter ww holds centroids 64 ww .. 64 ww + 63 of the
+// tile; each lane stores four consecutive partial sums of one token.
+using RouteW8 = W8<false>;
+constexpr int kRouteW8Tokens = 256;
+
+template <int MS, int LT>
+__device__ __forceinline__ void route_w8_tile(const W8Rows& rows, int K, uint8_t* lds, int T, int N, int w0, int t0,
+                                              int t_count, int t_begin, int ks, float* __restrict__ part) {
+  f32x16 acc[2][5];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+  const int ww = wave_uniform((w8_tid() >> 6) & 3);
+  const W8Offs o = w8_offsets(64 * ww, 64 * ww + 32);
+  w8_mainloop<RouteW8, MS, LT>(rows, K, lds, o, acc);
+  const int tid = w8_tid(), h = (tid & 63) >> 5;
+  // rows t0 .. t_count - 1 of this launch's token range; a store past N or t_count is dropped by the range check
+  const int rows_here = min(kRouteW8Tokens, t_count - t0);
+  const __amdgpu_buffer_rsrc_t r =
+      pipe_rsrc(part + (static_cast<size_t>(ks) * T + t_begin + t0) * N, static_cast<uint64_t>(rows_here) * N * 4);
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int tr = w8_token_row(i, tid);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = w0 + 64 * ww + 32 * j + 8 * q + 4 * h;
+        const uint32_t off = e < N ? static_cast<uint32_t>(tr * N + e) * 4 : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(acc[j][i][4 * q]), __float_as_uint(acc[j][i][4 * q + 1]),
+                  __float_as_uint(acc[j][i][4 * q + 2]), __float_as_uint(acc[j][i][4 * q + 3])},
+            r, off, 0, 0);
+      }
+  }
+}
+
+__global__ __launch_bounds__(RouteW8::NT, 1) void route_logits_w8_kernel(
+    int T, int d, int N, int n_wt, int kslice, int t_begin, int t_count, const uint16_t* __restrict__ u,
+    const uint16_t* __restrict__ cent, float* __restrict__ part, int32_t* __restrict__ load) {
+  extern __shared__ __align__(16) uint8_t lds_rw8[];
+  if (blockIdx.x == 0 && t_begin == 0)
+    for (int e = threadIdx.x; e < N; e += RouteW8::NT) load[e] = 0;   // histogram is rebuilt by the select kernel
+  const int S = cdiv(d, kslice);
+  const int ks = blockIdx.x % S, tile = blockIdx.x / S;
+  const int w0 = (tile % n_wt) * RouteW8::BW, t0 = (tile / n_wt) * kRouteW8Tokens;
+  const int k0 = ks * kslice, K = min(kslice, d - k0);
+  const int rows_t = min(kRouteW8Tokens, t_count - t0), nsub = cdiv(rows_t, 32);
+  const int tid = w8_tid();
+  W8Rows rows;
+  rows.wrs = pipe_rsrc(cent + k0, (static_cast<uint64_t>(N) * d - k0) * 2);
+  rows.trs = pipe_rsrc(u + (static_cast<size_t>(t_begin) + t0) * d + k0, (static_cast<uint64_t>(rows_t) * d - k0) * 2);
+#pragma unroll
+  for (int q = 0; q < RouteW8::WL; ++q) {
+    const int uu = w8_unit(q, tid);
+    rows.ow[q] = static_cast<uint32_t>(min(w0 + w8_load_row(uu, tid), N - 1)) * d * 2 + w8_load_chunk(uu, tid) * 16;
+  }
+#pragma unroll
+  for (int q = 0; q < RouteW8::TLMAX; ++q) {
+    const int uu = w8_unit(q, tid);
+    rows.ot[q] = static_cast<uint32_t>(min(w8_load_row(uu, tid), rows_t - 1)) * d * 2 + w8_load_chunk(uu, tid) * 16;
+  }
+#define RW8_CALL(MS, LT) route_w8_tile<MS, LT>(rows, K, lds_rw8, T, N, w0, t0, t_count, t_begin, ks, part)
+  W8_DISPATCH(nsub, RW8_CALL);
+#undef RW8_CALL
+}
+
 // fp32 operands: 16x16 output tile per block, 16-wide K slices through LDS.
 __global__ __launch_bounds__(256) void route_logits_f32_kernel(int T, int d, int N, const float* __restrict__ u,
                                                                const float* __restrict__ cent,
@@ -117,29 +194,25 @@ __device__ __forceinline__ void argmax_pair(float& v, int& id) {
 
 // Logits of this lane's V experts (e0 .. e0 + nv - 1, nv <= V) from the slice
 // partials part[p * slice + off + v], added in slice order; the loads of four
-// slices are issued together so that the chain of adds does not wait on one
-// load at a time.
+// slices are issued together (past the last slice: none) so that the chain of
+// adds does not wait on one load at a time.
 template <int V>
 __device__ __forceinline__ void sum_slices(const float* __restrict__ part, int S_part, size_t slice, size_t off,
                                            int nv, float (&x)[V]) {
 #pragma unroll
-  for (int v = 0; v < V; ++v) x[v] = v < nv ? part[off + v] : 0.0f;
-  int p = 1;
-  for (; p + 4 <= S_part; p += 4) {
+  for (int v = 0; v < V; ++v) x[v] = 0.0f;
+  for (int p = 0; p < S_part; p += 4) {
     float y[4][V];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int v = 0; v < V; ++v) y[q][v] = v < nv ? part[(p + q) * slice + off + v] : 0.0f;
+      for (int v = 0; v < V; ++v) y[q][v] = (p + q < S_part && v < nv) ? part[(p + q) * slice + off + v] : 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int v = 0; v < V; ++v) x[v] += y[q][v];
+      for (int v = 0; v < V; ++v)
+        if (p + q < S_part) x[v] = (p + q == 0) ? y[q][v] : x[v] + y[q][v];
   }
-  for (; p < S_part; ++p)
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      if (v < nv) x[v] += part[p * slice + off + v];
 }
 
 constexpr int kSelWaves = 4;
@@ -246,22 +319,30 @@ __global__ __launch_bounds__(64 * kSelWaves) void route_select_kernel(Shape s, c
   }
 }
 
-// K slices of the bf16 logits GEMM: enough tiles to give every CU one
-// (256-centroid x 128-token tiles), at most 16 slices, whole 128-wide chunks.
-// Batch-invariant mode: four slices (whole chunks) whatever T is, so each
-// logit is the same sum of the same partials in the same order for any batch;
-// four is what a V3-sized batch (64 token tiles) needs to fill the GPU.
-constexpr int kInvariantSlices = 4;
+// The bf16 logits GEMM's tiling: the eight-wave kernel when N % 4 == 0
+// (256-centroid x 256-token tiles), else the four-wave one (256 x 128), with
+// K split into slices of whole 128-wide chunks so that the tiles times the
+// slices give every CU one, at most 32 slices. Batch-invariant mode: a fixed
+// slice count whatever T is, so each logit is the same sum of the same
+// partials in the same order for any batch; it is what a V3-sized batch
+// needs to fill the GPU (eight-wave: 32 token tiles x 8; four-wave: 64 x 4).
+struct RoutePlan {
+  bool w8;
+  int bt;       // token rows per tile
+  int kslice;   // K elements per slice
+};
 
-static int route_kslice(const Shape& s) {
-  if (s.bi) return cdiv(s.d / 128, kInvariantSlices) * 128;
-  const int tiles = cdiv(s.N, RouteTile::BW) * cdiv(s.T, RouteTile::BT);
+static RoutePlan route_plan(const Shape& s) {
+  const bool w8 = s.N % 4 == 0;
+  const int bt = w8 ? kRouteW8Tokens : RouteTile::BT;
   const int chunks = s.d / 128;
-  int S = device_cu_count() / tiles;
-  S = S < 1 ? 1 : (S > 16 ? 16 : S);
+  int S = s.bi ? (w8 ? 8 : 4) : device_cu_count() / (cdiv(s.N, 256) * cdiv(s.T, bt));
+  S = S < 1 ? 1 : (S > 32 ? 32 : S);
   S = S > chunks ? chunks : S;
-  return cdiv(chunks, S) * 128;
+  return {w8, bt, cdiv(chunks, S) * 128};
 }
+
+static int route_kslice(const Shape& s) { return route_plan(s).kslice; }
 
 size_t route_ws_bytes(const Shape& s, moe_dtype act) {
   const size_t scores = (static_cast<size_t>(s.T) * s.N * sizeof(float) + 255) & ~static_cast<size_t>(255);
@@ -482,8 +563,8 @@ hipError_t launch_route(const Shape& s, moe_dtype act, const void* u, const void
   const float* part = nullptr;
   int S = 0;
   if (act == MOE_BF16) {
-    using P = RouteTile;
-    const int kslice = route_kslice(s);
+    const RoutePlan plan = route_plan(s);
+    const int kslice = plan.kslice;
     S = cdiv(s.d, kslice);
     float* p = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                         ((static_cast<size_t>(s.T) * s.N * sizeof(float) + 255) & ~static_cast<size_t>(255)));
@@ -493,18 +574,25 @@ hipError_t launch_route(const Shape& s, moe_dtype act, const void* u, const void
       // a refused request must not leave a sticky error
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(route_logits_bf16_kernel),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, RouteTile::LDS_BYTES);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(route_logits_w8_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, RouteW8::LDS_BYTES);
       (void)hipGetLastError();
     });
-    const int n_wt = cdiv(s.N, P::BW);
+    const int n_wt = cdiv(s.N, 256);
     // token ranges whose rows span less than 4 GiB (32-bit buffer offsets)
     const long long max_t = ((1LL << 32) - 1) / (2LL * s.d);
-    const int t_step = static_cast<int>(max_t < s.T ? (max_t / P::BT) * P::BT : s.T);
+    const int t_step = static_cast<int>(max_t < s.T ? (max_t / plan.bt) * plan.bt : s.T);
     for (int t_begin = 0; t_begin < s.T; t_begin += t_step) {
       const int t_count = s.T - t_begin < t_step ? s.T - t_begin : t_step;
-      const int grid = n_wt * cdiv(t_count, P::BT) * S;
-      hipLaunchKernelGGL(route_logits_bf16_kernel, dim3(grid), dim3(P::NT), P::LDS_BYTES, st, s.T, s.d, s.N, n_wt,
-                         kslice, t_begin, t_count, static_cast<const uint16_t*>(u),
-                         static_cast<const uint16_t*>(cent), p, load);
+      const int grid = n_wt * cdiv(t_count, plan.bt) * S;
+      if (plan.w8)
+        hipLaunchKernelGGL(route_logits_w8_kernel, dim3(grid), dim3(RouteW8::NT), RouteW8::LDS_BYTES, st, s.T, s.d,
+                           s.N, n_wt, kslice, t_begin, t_count, static_cast<const uint16_t*>(u),
+                           static_cast<const uint16_t*>(cent), p, load);
+      else
+        hipLaunchKernelGGL(route_logits_bf16_kernel, dim3(grid), dim3(RouteTile::NT), RouteTile::LDS_BYTES, st, s.T,
+                           s.d, s.N, n_wt, kslice, t_begin, t_count, static_cast<const uint16_t*>(u),
+                           static_cast<const uint16_t*>(cent), p, load);
     }
   } else {
     dim3 grid(cdiv(s.N, 16), cdiv(s.T, 16));
