@@ -92,7 +92,8 @@ typedef struct {
  * combine have it in both modes (no reduction is split across rows or
  * blocks); the router's logits GEMM splits its K reduction into slices, by
  * default as many as fill the GPU for this T, with batch_invariant = 1 into
- * four slices of whole 128-wide chunks (d alone fixes them). The bias update
+ * a fixed count of slices of whole 128-wide chunks that d and N_r alone set
+ * (eight, or four when N_r is not a multiple of 4). The bias update
  * and the load histogram are batch statistics by definition.
  */
 
