@@ -35,6 +35,7 @@ ROUTE_CASES = [
     ("c2", dict(T=1000, n_groups=4, topk_groups=1, topk=3, group_topn=3)),  # ragged T, 3-term group score
     ("c2", dict(n_routed=96, n_groups=8, topk_groups=3)),   # 3 experts per lane, 4-lane groups
     ("c2", dict(n_routed=68, n_groups=4, topk_groups=2)),   # 17-expert groups: the LDS form of the selection
+    ("c2", dict(n_routed=18, n_groups=3, topk_groups=2, topk=4)),   # N_r % 4 != 0: the four-wave logits kernel
     ("c3", {}),
     ("c5", {}),                                             # 384 experts, no group limit: 6 per lane
     # the supported maxima: 1024 experts in 64 groups, top-16 of 8 groups, 4-term group scores; ragged T
