@@ -114,6 +114,28 @@ def test_grouped_ffn_validation():
     assert b"workspace" in L.moe_last_error()
 
 
+def test_grouped_ffn_refuses_32_bit_offset_overflow():
+    """The expert GEMM kernels address rows through 32-bit byte offsets: shapes whose gathered activations, H or
+    one expert's weights would pass 4 GiB are refused before any launch (the router splits its token range
+    instead)."""
+    L = B.lib()
+    sh = _shape(d=7168, inter=2048)
+
+    def call(w, nr, ar, shape=sh):
+        scales = FAKE if w in (B.MOE_F8E4M3, B.MOE_F4E2M1) else None
+        return L.moe_grouped_ffn(ctypes.byref(shape), w, 4, nr, FAKE, B.MOE_ROWS_GATHER, FAKE, FAKE, scales, ar, FAKE,
+                                 scales, FAKE, scales, B.MOE_BF16, FAKE, FAKE, 1 << 40, None)
+
+    for w in (B.MOE_BF16, B.MOE_BF16_TILED):
+        assert call(w, 1000, 299_594) == B.MOE_E_UNSUPPORTED           # a_rows * d * 2 >= 2^32
+        assert b"a_rows" in L.moe_last_error()
+        assert call(w, 1 << 20, 1000) == B.MOE_E_UNSUPPORTED           # n_rows * inter * 2 >= 2^32
+        assert call(w, 1000, 299_000, _shape(d=7168, inter=150016)) == B.MOE_E_UNSUPPORTED   # 2 I d * 2 >= 2^32
+    for w in (B.MOE_F8E4M3, B.MOE_F4E2M1):
+        assert call(w, 1000, 599_187) == B.MOE_E_UNSUPPORTED           # a_rows * d >= 2^32
+        assert call(w, 1 << 21, 1000) == B.MOE_E_UNSUPPORTED           # n_rows * inter >= 2^32
+
+
 def test_permute_combine_bias_validation():
     L = B.lib()
     sh = _shape()

@@ -72,6 +72,40 @@ def test_route(name, over):
     assert max(len(set(row)) for row in (gi // S)) <= cfg.topk_groups
 
 
+def test_route_token_rows_past_4gib():
+    """u of 4 GiB (T = 2048 rows of d = 2^20 bf16): the router cuts its token range into launches whose
+    rows stay within 32-bit byte offsets (1792 + 256 tokens here). Tokens on both sides of the cut and at the end
+    against the oracle; the load histogram against the bincount of every selection. Seeded inputs made on the
+    device: u ~ N(0, 1), centroids ~ N(0, (1.7 / sqrt(d))^2) (logits of about the V3 spread), bias ~ U(-0.01, 0.01).
+    Affinities and gates to the same 1e-5 as at the V3 shape, although each fp32 sum runs over 2^20 products."""
+    T, d, N, G, M, K = 2048, 1 << 20, 16, 4, 2, 2
+    cfg = get_config("c2", T=T, d=d, n_routed=N, n_groups=G, topk_groups=M, topk=K, inter=128, n_shared=0)
+    sh = B.moe_shape.of(cfg)
+    assert T * d * 2 >= (1 << 32)                   # past the last byte a 32-bit offset reaches
+    gen = torch.Generator(device=DEV).manual_seed(20261204)
+    u = torch.randn((T, d), generator=gen, device=DEV, dtype=torch.bfloat16)
+    cent = (torch.randn((N, d), generator=gen, device=DEV) * (1.7 / d ** 0.5)).to(torch.bfloat16)
+    bias = (torch.rand((N,), generator=gen, device=DEV) * 0.02 - 0.01).float()
+    idx = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    gate = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    load = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    scores = torch.empty((T, N), dtype=torch.float32, device=DEV)
+    ws = torch.empty(B.moe_workspace_bytes(sh, B.MOE_BF16), dtype=torch.uint8, device=DEV)
+    B.moe_route(sh, u, cent, bias, idx, gate, load, scores, ws)
+    torch.cuda.synchronize()
+    gi = npi(idx)
+    assert np.array_equal(npi(load), np.bincount(gi.ravel(), minlength=N))
+    rows = np.r_[0:16, 1776:1808, 2032:2048]
+    r = oracle.route(np64(u[torch.from_numpy(rows).to(DEV)]), np64(cent), np64(bias), G, M, cfg.group_topn, K)
+    ds = np.abs(np64(scores)[rows] - r["s"]).max()
+    print(f"[parity] d = 2^20, T = {T}: max |s_gpu - s_oracle| = {ds:.2e} over {rows.size} tokens")
+    assert ds < 1e-5
+    bad = routing_mismatches(idx[torch.from_numpy(rows).to(DEV)], r)
+    ok = np.ones(rows.size, dtype=bool)
+    ok[bad] = False
+    report("d = 2^20 gates", rel_l2(np64(gate)[rows][ok], r["gate"][ok]), 1e-5)
+
+
 @pytest.mark.parametrize("name", ["c1", "c3"])
 def test_route_without_scores(name):
     """scores = NULL: the affinities are not written (bf16) or pass through the workspace (fp32); the
