@@ -581,6 +581,45 @@ def test_grouped_ffn_bf16_half_column_tile(d):
             report(f"d={d} expert {e} ({sizes[e]} rows) y", rel_l2(y[off[e]:off[e + 1]], ref), TOL["bf16"])
 
 
+def test_grouped_ffn_bf16_gather_near_4gib():
+    """The bf16 gate/up gathers token rows through 32-bit byte offsets: an a of a_rows * d * 2 bytes just under
+    4 GiB (a_rows = 299,593 at d = 7168, the most the call accepts) with rows picked at both ends of it, three
+    experts, row-major and tiled weights. y against the oracle; the tiled run equals the row-major one bit for bit.
+    Seeded inputs made on the device: a ~ N(0, 1) bf16; the experts' weights as the workload generator draws them."""
+    d, I, E = 7168, 256, 3
+    a_rows = ((1 << 32) - 1) // (2 * d)
+    cfg = get_config("c2", T=a_rows, d=d, inter=I, n_routed=E, n_groups=1, topk_groups=1, topk=1, n_shared=0)
+    sh = B.moe_shape.of(cfg)
+    gen = torch.Generator(device=DEV).manual_seed(4242)
+    a = torch.randn((a_rows, d), generator=gen, device=DEV, dtype=torch.bfloat16)
+    ws_ = [generate_expert(cfg, e, device=DEV) for e in range(E)]
+    wgu = torch.stack([w[0] for w in ws_]).contiguous()
+    wd = torch.stack([w[1] for w in ws_]).contiguous()
+    sizes = [40, 33, 23]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    rng = np.random.default_rng(11)
+    src = np.concatenate([np.arange(a_rows - 48, a_rows), np.arange(0, 16), rng.integers(0, a_rows, n - 64)])
+    rng.shuffle(src)
+    ws = torch.empty(B.moe_workspace_bytes(sh, B.MOE_BF16_TILED), dtype=torch.uint8, device=DEV)
+    y0 = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    B.moe_grouped_ffn(sh, B.MOE_BF16, E, n, _i32(off), B.MOE_ROWS_GATHER, _i32(src), a, None, a_rows, wgu, None, wd,
+                      None, y0, ws)
+    tg = torch.empty((E, B.mx_rows(2 * I), d), dtype=torch.bfloat16, device=DEV)
+    td = torch.empty((E, B.mx_rows(d), I), dtype=torch.bfloat16, device=DEV)
+    B.moe_tile_weights_bf16(wgu, tg, gate_up=True)
+    B.moe_tile_weights_bf16(wd, td, gate_up=False)
+    y1 = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    B.moe_grouped_ffn(sh, B.MOE_BF16_TILED, E, n, _i32(off), B.MOE_ROWS_GATHER, _i32(src), a, None, a_rows, tg, None,
+                      td, None, y1, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    a_rows_used = a[torch.from_numpy(src).to(DEV)].float().cpu()
+    for e in range(E):
+        ref = oracle.expert_ffn(a_rows_used[off[e]:off[e + 1]].double().numpy(), wgu[e].cpu(), wd[e].cpu(), "bf16")
+        report(f"a near 4 GiB, expert {e} ({sizes[e]} rows) y", rel_l2(y0[off[e]:off[e + 1]], ref), TOL["bf16"])
+
+
 @pytest.mark.parametrize("kind", ["gate_up", "down_padded"])
 def test_tile_weights_bf16_bit_exact(kind):
     """The tiled bf16 layout, byte for byte: the rows' bytes rearranged exactly as the E4M3 tiles (64-byte steps,
