@@ -755,6 +755,53 @@ def _check_fp8_experts(cfg, inp, layer, experts, tag, pow2=False):
             assert same > 0.99 and sdiff < 1e-4
 
 
+def test_grouped_ffn_fp8_gather_near_4gib():
+    """The fp8 gate/up gathers E4M3 token rows through 32-bit byte offsets: codes of a_rows * d bytes just under
+    4 GiB (a_rows = 599,186 at d = 7168, the most the call accepts), rows picked at both ends, three experts on the
+    eight-wave loops (d and inter multiples of 1024). Only the picked rows hold data: each is a seeded N(0, 1) row
+    quantised by the oracle's 1x128 rule; the other rows are zero codes with scale 1 and are never read. y and the
+    H codes against the oracle."""
+    d, I, E = 7168, 1024, 3
+    a_rows = ((1 << 32) - 1) // d
+    cfg = get_config("c2", gemm="fp8", d=d, inter=I, n_routed=E, n_groups=1, topk_groups=1, T=128, topk=1,
+                     n_shared=0)
+    inp = generate(cfg, DEV)
+    sh = B.moe_shape.of(cfg)
+    sizes = [40, 33, 23]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    rng = np.random.default_rng(13)
+    mid = rng.choice(np.arange(16, a_rows - 48), n - 64, replace=False)
+    src = np.concatenate([np.arange(a_rows - 48, a_rows), np.arange(0, 16), mid])
+    rng.shuffle(src)
+    u32 = rng.standard_normal((n, d)).astype(np.float32)        # row i of u32 is token row src[i]
+    uq, us = oracle.quantize_tiles(u32)
+    a = torch.zeros((a_rows, d), dtype=torch.uint8, device=DEV)
+    a_s = torch.ones((a_rows, d // 128), dtype=torch.float32, device=DEV)
+    si = torch.from_numpy(src).to(DEV)
+    a[si] = torch.from_numpy(uq).to(DEV)
+    a_s[si] = torch.from_numpy(us).to(DEV)
+    wq = [oracle_wq(cfg, inp, e) for e in range(E)]
+    dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    wgu = dev8(np.stack([tile_e4m3(w[0], True) for w in wq])); wgs = dev8(np.stack([w[1] for w in wq]))
+    wdn = dev8(np.stack([tile_e4m3(w[2], False) for w in wq])); wds = dev8(np.stack([w[3] for w in wq]))
+    h = torch.empty((n, I), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((n, I // 128), dtype=torch.float32, device=DEV)
+    y = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    B.moe_ffn_gate_up(sh, B.MOE_F8E4M3, E, n, _i32(off), B.MOE_ROWS_GATHER, _i32(src), a, a_s, a_rows, wgu, wgs, h, hs,
+                      ws)
+    B.moe_ffn_down(sh, B.MOE_F8E4M3, E, n, _i32(off), h, hs, wdn, wds, y, ws)
+    torch.cuda.synchronize()
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        ref, aux = oracle.ffn_fp8(u32[lo:hi], *wq[e], return_h=True)
+        report(f"fp8 a near 4 GiB, expert {e} ({hi - lo} rows) y", rel_l2(y[lo:hi], ref), TOL["fp8"])
+        same = float(np.mean(h[lo:hi].cpu().numpy() == aux["h_codes"]))
+        print(f"[parity] expert {e}: H codes equal {same:.4f}")
+        assert same > 0.99
+
+
 @pytest.mark.parametrize("inter,mode", [(128, "gather"), (1408, "gather"), (1408, "direct")])
 def test_grouped_ffn_fp8_tile_shapes(inter, mode):
     """fp8 grouped FFN on expert segments that reach every block shape.
