@@ -620,6 +620,76 @@ def test_grouped_ffn_bf16_gather_near_4gib():
         report(f"a near 4 GiB, expert {e} ({sizes[e]} rows) y", rel_l2(y0[off[e]:off[e + 1]], ref), TOL["bf16"])
 
 
+def _down_rows_check(tag, y, h64, wd64, off, rows, tol):
+    """y rows of the down projection against h64 @ wd64[e]^T (fp64) on the sampled rows of each expert."""
+    for e in range(len(off) - 1):
+        r = rows[(rows >= off[e]) & (rows < off[e + 1])]
+        ref = h64[np.searchsorted(rows, r)] @ wd64[e].T
+        report(f"{tag} expert {e} ({r.size} sampled rows) y", rel_l2(y[torch.from_numpy(r).to(DEV)], ref), tol)
+
+
+def test_ffn_down_h_near_4gib():
+    """The down projection reads H rows through 32-bit byte offsets: n_rows * inter * 2 bytes of bf16 H just
+    under 4 GiB (n_rows = 1,048,575 at inter = 2048, the most the call accepts; d = 1024 keeps y at 2 GiB), two
+    experts, row-major and tiled weights; sampled rows at the start, the expert boundary and the end against
+    the oracle. Seeded inputs made on the device: H ~ N(0, 1) bf16, W_d ~ N(0, 0.02^2) bf16."""
+    d, I, E = 1024, 2048, 2
+    n = ((1 << 32) - 1) // (2 * I)
+    cfg = get_config("c2", T=128, d=d, inter=I, n_routed=E, n_groups=1, topk_groups=1, topk=1, n_shared=0)
+    sh = B.moe_shape.of(cfg)
+    gen = torch.Generator(device=DEV).manual_seed(777)
+    h = torch.randn((n, I), generator=gen, device=DEV, dtype=torch.bfloat16)
+    wd = (torch.randn((E, d, I), generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    off = np.array([0, n // 2 + 5, n])
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(off[1] - 16, off[1] + 16), np.arange(n - 16, n),
+                                     np.random.default_rng(3).integers(0, n, 32)]))
+    h64 = np64(h[torch.from_numpy(rows).to(DEV)])
+    wd64 = np64(wd)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    y = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    B.moe_ffn_down(sh, B.MOE_BF16, E, n, _i32(off), h, None, wd, None, y, ws)
+    torch.cuda.synchronize()
+    _down_rows_check("bf16 H near 4 GiB", y, h64, wd64, off, rows, TOL["bf16"])
+    td = torch.empty((E, B.mx_rows(d), I), dtype=torch.bfloat16, device=DEV)
+    B.moe_tile_weights_bf16(wd, td, gate_up=False)
+    y1 = torch.empty_like(y)
+    B.moe_ffn_down(sh, B.MOE_BF16_TILED, E, n, _i32(off), h, None, td, None, y1, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y[torch.from_numpy(rows).to(DEV)], y1[torch.from_numpy(rows).to(DEV)])
+
+
+def test_ffn_down_fp8_h_near_4gib():
+    """fp8 down projection with n_rows * inter bytes of E4M3 H codes just under 4 GiB (n_rows = 2,097,151 at
+    inter = 2048, the most the call accepts; d = 1024), two experts on the eight-wave loop; sampled rows against
+    the oracle on the dequantised operands. H: seeded random finite E4M3 codes (magnitude codes 0 .. 0x7E, either
+    sign) with 1x128 scales ~ U(1e-3, 2e-3); W_d: the oracle's 128x128 quantisation of N(0, 0.02^2) weights."""
+    d, I, E = 1024, 2048, 2
+    n = ((1 << 32) - 1) // I
+    cfg = get_config("c2", T=128, d=d, inter=I, n_routed=E, n_groups=1, topk_groups=1, topk=1, n_shared=0,
+                     gemm="fp8")
+    sh = B.moe_shape.of(cfg)
+    gen = torch.Generator(device=DEV).manual_seed(778)
+    h = torch.randint(0, 0x7F, (n, I), generator=gen, device=DEV, dtype=torch.uint8)
+    h |= (torch.randint(0, 2, (n, I), generator=gen, device=DEV, dtype=torch.uint8) << 7)
+    hs = torch.rand((n, I // 128), generator=gen, device=DEV) * 1e-3 + 1e-3
+    w32 = (np.random.default_rng(5).standard_normal((E, d, I)) * 0.02).astype(np.float32)
+    wq = [oracle.quantize_blocks(w32[e]) for e in range(E)]
+    dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    wdn = dev8(np.stack([tile_e4m3(q, False) for q, _ in wq]))
+    wds = dev8(np.stack([sc for _, sc in wq]))
+    off = np.array([0, n // 2 - 7, n])
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(off[1] - 16, off[1] + 16), np.arange(n - 16, n),
+                                     np.random.default_rng(4).integers(0, n, 32)]))
+    sel = torch.from_numpy(rows).to(DEV)
+    h64 = oracle.dequantize_tiles(h[sel].cpu().numpy(), hs[sel].cpu().numpy())
+    wd64 = np.stack([oracle.dequantize_blocks(q, sc) for q, sc in wq])
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    y = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    B.moe_ffn_down(sh, B.MOE_F8E4M3, E, n, _i32(off), h, hs, wdn, wds, y, ws)
+    torch.cuda.synchronize()
+    _down_rows_check("fp8 H near 4 GiB", y, h64, wd64, off, rows, TOL["fp8"])
+
+
 @pytest.mark.parametrize("kind", ["gate_up", "down_padded"])
 def test_tile_weights_bf16_bit_exact(kind):
     """The tiled bf16 layout, byte for byte: the rows' bytes rearranged exactly as the E4M3 tiles (64-byte steps,
