@@ -133,6 +133,86 @@ def test_grouped_ffn_mxfp4_half_column_tile(d):
     _check_mx_experts(cfg, _mx_ffn_case(cfg, [0, 40, 300, 129], 6, "gather"), f"d={d}")
 
 
+def test_grouped_ffn_mxfp4_gather_near_4gib():
+    """The MXFP4 gate/up gathers E4M3 token rows through 32-bit byte offsets: codes of a_rows * d bytes just under
+    4 GiB (a_rows = 599,186 at d = 7168, the most the call accepts), rows picked at both ends, three experts. Only
+    the picked rows hold data (seeded N(0, 1) rows quantised by the oracle's 1x128 rule); the rest are zero codes
+    with scale 1 and are never read. y and the H codes against the oracle."""
+    d, I, E = 7168, 1024, 3
+    a_rows = ((1 << 32) - 1) // d
+    cfg = get_config("c2", gemm="mxfp4", d=d, inter=I, n_routed=E, n_groups=1, topk_groups=1, T=128, topk=1,
+                     n_shared=0)
+    inp = generate(cfg, DEV)
+    sh = B.moe_shape.of(cfg)
+    sizes = [40, 33, 23]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    rng = np.random.default_rng(17)
+    mid = rng.choice(np.arange(16, a_rows - 48), n - 64, replace=False)
+    src = np.concatenate([np.arange(a_rows - 48, a_rows), np.arange(0, 16), mid])
+    rng.shuffle(src)
+    u32 = rng.standard_normal((n, d)).astype(np.float32)        # row i of u32 is token row src[i]
+    uq, us = oracle.quantize_tiles(u32)
+    a = torch.zeros((a_rows, d), dtype=torch.uint8, device=DEV)
+    a_s = torch.ones((a_rows, d // 128), dtype=torch.float32, device=DEV)
+    si = torch.from_numpy(src).to(DEV)
+    a[si] = _dev(uq)
+    a_s[si] = _dev(us)
+    mg = [_oracle_mx(inp["w_gate_up"][e].cpu().float().numpy(), True) for e in range(E)]
+    md = [_oracle_mx(inp["w_down"][e].cpu().float().numpy(), False) for e in range(E)]
+    wgu, wgs = _dev(np.stack([m[0] for m in mg])), _dev(np.stack([m[1] for m in mg]))
+    wdn, wds = _dev(np.stack([m[0] for m in md])), _dev(np.stack([m[1] for m in md]))
+    h = torch.empty((n, I), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((n, I // 128), dtype=torch.float32, device=DEV)
+    y = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    B.moe_ffn_gate_up(sh, B.MOE_F4E2M1, E, n, _i32(off), B.MOE_ROWS_GATHER, _i32(src), a, a_s, a_rows, wgu, wgs, h,
+                      hs, ws)
+    B.moe_ffn_down(sh, B.MOE_F4E2M1, E, n, _i32(off), h, hs, wdn, wds, y, ws)
+    torch.cuda.synchronize()
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        ref, aux = oracle.ffn_mxfp4(u32[lo:hi], *mg[e][2], *md[e][2], return_h=True)
+        report(f"mxfp4 a near 4 GiB, expert {e} ({hi - lo} rows) y", rel_l2(y[lo:hi], ref), TOL["mxfp4"])
+        same = float(np.mean(h[lo:hi].cpu().numpy() == aux["h_codes"]))
+        print(f"[parity] mxfp4 expert {e}: H codes equal {same:.4f}")
+        assert same > 0.99
+
+
+def test_ffn_down_mxfp4_h_near_4gib():
+    """MXFP4 down projection on n_rows * inter bytes of E4M3 H codes just under 4 GiB (n_rows = 2,097,151 at
+    inter = 2048, the most the call accepts; d = 1024), two experts; sampled rows at the start, the expert boundary
+    and the end against the oracle on the dequantised operands. H: seeded random finite E4M3 codes (magnitude codes
+    0 .. 0x7E, either sign) with 1x128 scales ~ U(1e-3, 2e-3); W_d: the oracle's MXFP4 of N(0, 0.02^2) weights."""
+    d, I, E = 1024, 2048, 2
+    n = ((1 << 32) - 1) // I
+    cfg = get_config("c2", gemm="mxfp4", T=128, d=d, inter=I, n_routed=E, n_groups=1, topk_groups=1, topk=1,
+                     n_shared=0)
+    sh = B.moe_shape.of(cfg)
+    gen = torch.Generator(device=DEV).manual_seed(779)
+    h = torch.randint(0, 0x7F, (n, I), generator=gen, device=DEV, dtype=torch.uint8)
+    h |= (torch.randint(0, 2, (n, I), generator=gen, device=DEV, dtype=torch.uint8) << 7)
+    hs = torch.rand((n, I // 128), generator=gen, device=DEV) * 1e-3 + 1e-3
+    w32 = (np.random.default_rng(6).standard_normal((E, d, I)) * 0.02).astype(np.float32)
+    md = [_oracle_mx(w32[e], False) for e in range(E)]
+    wdn, wds = _dev(np.stack([m[0] for m in md])), _dev(np.stack([m[1] for m in md]))
+    off = np.array([0, n // 2 + 3, n])
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(off[1] - 16, off[1] + 16), np.arange(n - 16, n),
+                                     np.random.default_rng(7).integers(0, n, 32)]))
+    sel = torch.from_numpy(rows).to(DEV)
+    h64 = oracle.dequantize_tiles(h[sel].cpu().numpy(), hs[sel].cpu().numpy())
+    wd64 = np.stack([oracle.dequantize_mxfp4(*m[2]) for m in md])
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    y = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    B.moe_ffn_down(sh, B.MOE_F4E2M1, E, n, _i32(off), h, hs, wdn, wds, y, ws)
+    torch.cuda.synchronize()
+    for e in range(E):
+        r = rows[(rows >= off[e]) & (rows < off[e + 1])]
+        ref = h64[np.searchsorted(rows, r)] @ wd64[e].T
+        report(f"mxfp4 H near 4 GiB expert {e} ({r.size} sampled rows) y", rel_l2(y[torch.from_numpy(r).to(DEV)], ref),
+               TOL["mxfp4"])
+
+
 def test_mxfp4_through_fp8_kernels_on_lossless_conversion():
     """The pages' lossless FP4 -> FP8 conversion, on the GPU: the same MXFP4 weights converted by the oracle to
     E4M3 128x128 blocks and run through the fp8 kernels give the native MXFP4 kernels' results (both multiply
