@@ -8,7 +8,8 @@
 // codes come in the tiled layout of moe_quantize_weights (per expert, tiles of
 // 256 rows whose 64-wide K steps are contiguous 16 KB blocks in LDS order).
 // Two persistent launches over all experts, one workgroup per CU; a unit
-// streams up to four consecutive output-column tiles of one token block. Two
+// streams consecutive output-column tiles of one token block (up to two in the
+// eight-wave gate/up, four otherwise). Two
 // main loops:
 //  * eight waves, 256 weight rows x 256 token rows per tile, an expert's rows
 //    in near-equal blocks of at most eight 32-row sub-tiles (gemm_f8w.h):
@@ -168,6 +169,11 @@ __global__ __launch_bounds__(P8::NT, 1) void ffn_down_fp8_kernel(int d, int I, i
 // ---- eight-wave kernels (gemm_f8w.h) ----
 
 constexpr int kMaxExpertsW = 1024;
+// Output-column tiles per unit of the eight-wave gate/up (the down projection streams F8W::MAX_SEG): with 16
+// tiles per token block at the V3 shape, units of two balance the CUs better than units of four (gate/up
+// 3.02-3.06 -> 2.95-2.97 ms; the down projection, K = 2048, keeps four: 1.84 against 1.87 ms with two).
+constexpr int kGateUpSegW = 2;
+static_assert(kGateUpSegW <= F8W::MAX_SEG, "weight-scale table slots");
 
 template <int MS, int LT>
 __device__ __forceinline__ void gate_up8w_unit(const F8WRows& rows, int d, int I, const Unit& un, int nb0, int nseg,
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(F8W::NT, 1) void ffn_gate_up_fp8w_kernel(
   int* cum = reinterpret_cast<int*>(ldsw + F8W::LDS_BYTES);
   __shared__ int wtmp[16];
   const int kc = d / 128, NB = I / 128;
-  const int total = build_units_balanced(off, E, n_rows, F8W::MAXSUB, cdiv(NB, F8W::MAX_SEG), cum, wtmp);
+  const int total = build_units_balanced(off, E, n_rows, F8W::MAXSUB, cdiv(NB, kGateUpSegW), cum, wtmp);
   const int tid = threadIdx.x;
   F8WRows rows;
   rows.trs = pipe_rsrc(a, static_cast<uint64_t>(a_rows) * d);
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(F8W::NT, 1) void ffn_gate_up_fp8w_kernel(
   int x_off = 0;
   for (int t; (t = unit_queue_next(q, total, x_off, &tslot)) >= 0;) {
     const Unit un = find_unit_balanced<true>(t, off, E, n_rows, F8W::MAXSUB, cum);
-    const int nb0 = un.nb * F8W::MAX_SEG, nseg = min(F8W::MAX_SEG, NB - nb0);
+    const int nb0 = un.nb * kGateUpSegW, nseg = min(kGateUpSegW, NB - nb0);
     // weight scales of each tile (gate block row nb, up block row I/128 + nb) and the source row of each
     // tile row (rows past the block read any valid row and are never stored)
     const float* sexp = wgu_scale + static_cast<size_t>(un.e) * (2 * I / 128) * kc;
@@ -333,7 +339,7 @@ hipError_t launch_ffn_fp8_gate_up(const FfnArgs& p, hipStream_t st) {
   if (f8w_gate_up_fits(p)) {
     const size_t lds = F8W::LDS_BYTES + sizeof(int) * (p.n_experts + 1);
     const long long mblocks = p.n_rows / F8W::BT + p.n_experts;
-    hipLaunchKernelGGL(ffn_gate_up_fp8w_kernel, dim3(f8_grid(mblocks * cdiv(p.I / 128, F8W::MAX_SEG))),
+    hipLaunchKernelGGL(ffn_gate_up_fp8w_kernel, dim3(f8_grid(mblocks * cdiv(p.I / 128, kGateUpSegW))),
                        dim3(F8W::NT), lds, st, p.d, p.I, p.n_experts, p.n_rows, p.a_rows, p.offsets, p.mode,
                        p.row_src, static_cast<const uint8_t*>(p.a), p.a_scale, static_cast<const uint8_t*>(p.w_gu),
                        static_cast<const float*>(p.w_gu_scale), static_cast<uint8_t*>(p.h), p.h_scale,
