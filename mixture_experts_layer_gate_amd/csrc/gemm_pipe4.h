@@ -52,7 +52,7 @@ struct Pipe4 {
   static constexpr int SC_SLOTS = 3, SC_BYTES = 4 * BW;    // chunk slots of [K block][row] E8M0 scales
   static constexpr int SC_OFF = RING;
   static constexpr int MAX_CHUNKS = 64;                    // K <= 8192
-  static constexpr int MAX_SEG = 4;                        // output-column blocks streamed per unit
+  static constexpr int MAX_SEG = 2;                        // output-column blocks streamed per unit (*)
   static constexpr int SA_OFF = SC_OFF + SC_SLOTS * SC_BYTES;    // token scales [BT][kc_pad]
   static constexpr int SRC_OFF = SA_OFF + BT * MAX_CHUNKS * 4;   // source row of each tile row [BT]
   static constexpr int AMAX_OFF = SRC_OFF + BT * 4;              // epilogue exchange [2][BT]
@@ -60,6 +60,8 @@ struct Pipe4 {
   static_assert(WL * NT * 16 == W_BYTES && TL * NT * 16 == T_BYTES, "stage must split evenly over the threads");
   static_assert(64 * 16 == SC_BYTES, "one wave's 16-byte load covers a chunk's scales");
   static_assert((WL + TL) * (NS - 2) + 2 <= 63, "vmcnt range");
+  // (*) Units of two column blocks balance the CUs better than four: decode batch gate/up 1.25 -> 1.20 ms,
+  // down 0.63 -> 0.615 ms; V3 gate/up 3.02-3.05 -> 2.98 ms (one block: 1.22 / 0.66 and 2.98 / 1.77 ms).
   static_assert(BW == Pipe8::BW && BT == Pipe8::BT && TW == Pipe8::TW && TT == Pipe8::TT,
                 "same tile and wave layout as the E4M3 loop (shared epilogues)");
 };
