@@ -26,14 +26,32 @@ __device__ __forceinline__ void ld8(const void* p, moe_dtype dt, size_t off, flo
 
 constexpr int kMaxK = 16;
 
+// bf16 rows of 8 channels: all loads of a row piece are issued before the first is used.
+__device__ __forceinline__ uint4 ld_bf16x8(const void* p, size_t off) {
+  return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + off);
+}
+__device__ __forceinline__ void unpack_bf16x8(const uint4& v, float (&x)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
 // One block per token (grid-stride); each thread handles 8 consecutive channels.
+// KT > 0: bf16 rows and K = KT known at compile time, so the residual, the
+// shared rows and the K routed rows of a piece are loaded together (K + 2
+// loads in flight per lane instead of one) and then added in the same order
+// as the general form: residual, shared experts, routed k = 0 .. K - 1.
+template <int KT>
 __global__ __launch_bounds__(256) void combine_kernel(Shape s, moe_dtype io, const void* __restrict__ u,
                                                       const void* __restrict__ y, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate,
                                                       const void* __restrict__ ysh, void* __restrict__ out) {
   __shared__ int rows[kMaxK];
   __shared__ float gts[kMaxK];
-  const int d = s.d, K = s.K;
+  const int d = s.d, K = KT > 0 ? KT : s.K;
   const long long n_rows = static_cast<long long>(s.T) * K;
   for (int t = blockIdx.x; t < s.T; t += gridDim.x) {
     if (threadIdx.x < K) {
@@ -44,19 +62,43 @@ __global__ __launch_bounds__(256) void combine_kernel(Shape s, moe_dtype io, con
     __syncthreads();
     for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
       float acc[8], x[8];
-      ld8(u, io, static_cast<size_t>(t) * d + c, acc);
-      for (int sh = 0; sh < s.Ns; ++sh) {
-        ld8(ysh, io, (static_cast<size_t>(sh) * s.T + t) * d + c, x);
+      if constexpr (KT > 0) {
+        int rk[KT];
+        uint4 vy[KT];
+        const uint4 vu = ld_bf16x8(u, static_cast<size_t>(t) * d + c);
+        const uint4 vs = ld_bf16x8(ysh, static_cast<size_t>(t) * d + c);   // Ns == 1 on this path
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+          rk[k] = rows[k];
+          vy[k] = rk[k] >= 0 ? ld_bf16x8(y, static_cast<size_t>(rk[k]) * d + c) : uint4{0, 0, 0, 0};
+        }
+        unpack_bf16x8(vu, acc);
+        unpack_bf16x8(vs, x);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += x[i];
-      }
-      for (int k = 0; k < K; ++k) {
-        const int r = rows[k];
-        if (r < 0) continue;
-        const float g = gts[k];
-        ld8(y, io, static_cast<size_t>(r) * d + c, x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, x[i], acc[i]);
+        for (int k = 0; k < KT; ++k) {
+          if (rk[k] < 0) continue;
+          const float g = gts[k];
+          unpack_bf16x8(vy[k], x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, x[i], acc[i]);
+        }
+      } else {
+        ld8(u, io, static_cast<size_t>(t) * d + c, acc);
+        for (int sh = 0; sh < s.Ns; ++sh) {
+          ld8(ysh, io, (static_cast<size_t>(sh) * s.T + t) * d + c, x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += x[i];
+        }
+        for (int k = 0; k < K; ++k) {
+          const int r = rows[k];
+          if (r < 0) continue;
+          const float g = gts[k];
+          ld8(y, io, static_cast<size_t>(r) * d + c, x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, x[i], acc[i]);
+        }
       }
       const size_t o = static_cast<size_t>(t) * d + c;
       if (io == MOE_BF16) {
@@ -84,7 +126,13 @@ hipError_t launch_combine(const Shape& s, moe_dtype io, const void* u, const voi
   int blocks = s.T;
   const int cap = device_cu_count() * 32;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(threads), 0, st, s, io, u, y, row_of, gate, ysh, out);
+  const bool fast = io == MOE_BF16 && s.Ns == 1;
+  if (fast && s.K == 8)
+    hipLaunchKernelGGL(combine_kernel<8>, dim3(blocks), dim3(threads), 0, st, s, io, u, y, row_of, gate, ysh, out);
+  else if (fast && s.K == 6)
+    hipLaunchKernelGGL(combine_kernel<6>, dim3(blocks), dim3(threads), 0, st, s, io, u, y, row_of, gate, ysh, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<0>, dim3(blocks), dim3(threads), 0, st, s, io, u, y, row_of, gate, ysh, out);
   return hipGetLastError();
 }
 
