@@ -24,7 +24,7 @@
 namespace moe {
 
 using P4 = Pipe4;
-constexpr int kMaxExperts4 = 4096;
+constexpr int kMaxExperts4 = 2048;   // the schedule's per-expert table shares the LDS with the ring
 
 template <int MS, int LT>
 __device__ __forceinline__ void gate_up4_unit(const Pipe4Rows& rows, __amdgpu_buffer_rsrc_t tsrs, int d, int I,

@@ -20,8 +20,10 @@
 // Tile: BW = 256 weight rows x BT = 128 token rows, four waves in a 2 x 2 grid
 // of 128 x 64, as in gemm_pipe8.h. A stage covers 64 K values: 32-byte weight
 // rows and 64-byte token rows, streamed into LDS with buffer_load ... lds
-// through a ring of six stages (a stage holds half the weight bytes of an E4M3
-// stage; up to four are in flight while one is consumed). The weights come in
+// through a ring of seven stages (a stage holds half the weight bytes of an
+// E4M3 stage; up to five are in flight while one is consumed: a CU's load
+// throughput is its bytes in flight over the memory latency, and the decode
+// batch streams little besides the weights). The weights come in
 // the tiled layout of moe_quantize_weights_mxfp4: a tile's 8 KB of codes per
 // stage are one contiguous block that is already the stage's LDS image (rows
 // of 32 bytes, 16-byte halves XOR-swizzled), and its weight scales per chunk
@@ -29,7 +31,7 @@
 // every load instruction reads 1 KB of consecutive bytes and the stages of a
 // unit's column blocks follow each other in memory. The chunk's scales come in
 // one 16-byte-per-lane load of wave 0, issued just before the chunk's first
-// stage, into a ring of three chunk slots; wave 0 therefore counts one more
+// stage, into a ring of four chunk slots; wave 0 therefore counts one more
 // load per chunk than the other waves, and its waits allow for it.
 #pragma once
 
@@ -40,7 +42,7 @@
 namespace moe {
 
 struct Pipe4 {
-  static constexpr int BW = 256, BT = 128, BK = 64, NS = 6, NT = 256, NWAVE = NT / 64;
+  static constexpr int BW = 256, BT = 128, BK = 64, NS = 7, NT = 256, NWAVE = NT / 64;
   static constexpr int TW = 4, TT = 2;                    // 32x32 sub-tiles per wave
   static constexpr int WROWB = BK / 2, TROWB = BK;         // bytes per row per stage
   static constexpr int W_BYTES = BW * WROWB;               // E2M1 codes
@@ -49,7 +51,7 @@ struct Pipe4 {
   static constexpr int STAGE = W_BYTES + T_BYTES;
   static constexpr int WL = W_BYTES / 16 / NT, TL = T_BYTES / 16 / NT;
   static constexpr int RING = NS * STAGE;
-  static constexpr int SC_SLOTS = 3, SC_BYTES = 4 * BW;    // chunk slots of [K block][row] E8M0 scales
+  static constexpr int SC_SLOTS = 4, SC_BYTES = 4 * BW;    // chunk slots of [K block][row] E8M0 scales
   static constexpr int SC_OFF = RING;
   static constexpr int MAX_CHUNKS = 64;                    // K <= 8192
   static constexpr int MAX_SEG = 2;                        // output-column blocks streamed per unit (*)
@@ -255,7 +257,9 @@ __device__ __forceinline__ void pipe4_frame_update(float (&fac)[Pipe4::TT], floa
 // fragments; the second half of the MFMAs, with the loads of stage g+NS-1 spread
 // among them when ISSUE (into the buffer of stage g-1, which every wave has
 // finished with), and before them that stage's chunk scales when it starts a
-// chunk (g odd). A chunk's first stage also reads the next chunk's token
+// chunk (g even: the first stage of a pair; the scales of chunk c + 3 go into
+// the slot chunk c - 1 held, read for the last time before the barrier of
+// stage 2c - 1). A chunk's first stage also reads the next chunk's token
 // scales before its MFMAs and forms the frame change after them.
 template <int MS, int LT, bool SECOND, int W0, int W, bool ISSUE>
 __device__ __forceinline__ void pipe4_stage(const Pipe4Rows& rows, uint8_t* lds, int kc_pad, int kt, int g, int nk,
@@ -275,8 +279,9 @@ __device__ __forceinline__ void pipe4_stage(const Pipe4Rows& rows, uint8_t* lds,
   }
   const int ls = ISSUE ? g + P::NS - 1 : 0;
   const Pipe4Off lo = ISSUE ? pipe4_offsets(ls, nk) : Pipe4Off{0, 0, 0};
-  // stage g + NS - 1 starts a chunk when g is odd: the second stage of a pair
-  pipe4_half<MS, LT, SECOND, 1, ISSUE, ISSUE && SECOND>(fa, acc, r, rows, lds, ls, lo);
+  // stage g + NS - 1 starts a chunk when g is even: the first stage of a pair
+  static_assert(P::NS % 2 == 1, "an odd ring: the issued stage starts a chunk in the pair's first stage");
+  pipe4_half<MS, LT, SECOND, 1, ISSUE, ISSUE && !SECOND>(fa, acc, r, rows, lds, ls, lo);
   if (!SECOND) pipe4_frame_update<MS>(fac, r, sa, next);
 }
 
@@ -328,19 +333,20 @@ __device__ __forceinline__ void pipe4_pair(const Pipe4Rows& rows, uint8_t* lds, 
 }
 
 // The K loops of nseg output-column blocks of one unit as one stream of
-// total = nseg * nk stages (as pipe8_stream, with a six-stage ring); rows.wrs
+// total = nseg * nk stages (as pipe8_stream, with a seven-stage ring); rows.wrs
 // and rows.srs start at the unit's first column block. K % 128 == 0, K / 128 <= MAX_CHUNKS,
 // nseg <= MAX_SEG. Before the call the unit's source rows are in LDS and
 // visible to every wave. At the barrier of stage g every issued stage after
-// g+1 (at most three: g+2 .. g+4) may still be in flight, and for wave 0 the
-// scale loads of the chunks among them that start on an even stage; loads
-// complete in issue order, so a stage's scales, issued just before it, have
-// landed with it. The last six stages are peeled so every wait is a constant.
+// g+1 (at most four: g+2 .. g+5) may still be in flight, and for wave 0 the
+// scale loads of the chunks among them (two: the chunks start on even stages);
+// loads complete in issue order, so a stage's scales, issued just before it,
+// have landed with it. The last six stages are peeled so every wait is a
+// constant.
 template <int MS, int LT, class EPI>
 __device__ __forceinline__ void pipe4_stream(const Pipe4Rows& rows, __amdgpu_buffer_rsrc_t tsrs, int K, int nseg,
                                              uint8_t* lds, EPI& epi) {
   using P = Pipe4;
-  static_assert(P::NS == 6, "schedule written for a ring of six stages");
+  static_assert(P::NS == 7, "schedule written for a ring of seven stages");
   static_assert(LT >= 1 && LT <= P::TL && LT >= MS, "token load groups must cover the live sub-tiles");
   constexpr int L = P::WL + LT;                        // stage loads per thread (wave 0: + 1 per chunk)
   const int nk = K / P::BK, kc = K / 128, kc_pad = (kc + 3) & ~3, total = nseg * nk;   // nk even, total >= 2
@@ -351,9 +357,9 @@ __device__ __forceinline__ void pipe4_stream(const Pipe4Rows& rows, __amdgpu_buf
 #pragma unroll
     for (int q = 0; q < L; ++q) pipe4_issue_one(rows, lds + s * P::STAGE, o, q);
   }
-  // the token-scale table, stage 0 and its scales have landed; stages 1 .. min(4, total - 1) (wave 0: and the
+  // the token-scale table, stage 0 and its scales have landed; stages 1 .. min(5, total - 1) (wave 0: and the
   // scales of stages 2 and 4) may be in flight
-  if (total >= 5) pipe4_wait_barrier<4 * L + 2, 4 * L>();
+  if (total >= 6) pipe4_wait_barrier<5 * L + 2, 5 * L>();
   else if (total == 4) pipe4_wait_barrier<3 * L + 1, 3 * L>();
   else pipe4_wait_barrier<L, L>();                     // total == 2
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -378,14 +384,14 @@ __device__ __forceinline__ void pipe4_stream(const Pipe4Rows& rows, __amdgpu_buf
   Pipe4Frags<MS> f0, f1;
   pipe4_read<MS>(f0, lds, 0);
   int kt = 0, seg = 0, g = 0;
-  // steady state: each stage of the pair loads the stage five ahead; in flight at the first barrier g+2..g+4
-  // (two of them chunk starts), at the second g+3..g+5 (one)
-  for (; g + 6 < total; g += 2)
-    pipe4_pair<MS, LT, 3 * L + 2, 3 * L, true, 3 * L + 1, 3 * L, true>(rows, lds, kc_pad, kt, g, nk, seg, nseg, f0, f1,
+  // steady state: each stage of the pair loads the stage six ahead; in flight at the first barrier g+2..g+5,
+  // at the second g+3..g+6 (two chunk starts either way)
+  for (; g + 8 <= total; g += 2)
+    pipe4_pair<MS, LT, 4 * L + 2, 4 * L, true, 4 * L + 2, 4 * L, true>(rows, lds, kc_pad, kt, g, nk, seg, nseg, f0, f1,
                                                                        acc, fac, r, epi);
-  if (total - g == 6) {
-    pipe4_pair<MS, LT, 3 * L + 2, 3 * L, true, 3 * L + 1, 3 * L, false>(rows, lds, kc_pad, kt, g, nk, seg, nseg, f0, f1,
-                                                                        acc, fac, r, epi);
+  if (total - g == 6) {                               // nothing left to issue: g+2..g+5, then g+3..g+5
+    pipe4_pair<MS, LT, 4 * L + 2, 4 * L, false, 3 * L + 1, 3 * L, false>(rows, lds, kc_pad, kt, g, nk, seg, nseg, f0,
+                                                                         f1, acc, fac, r, epi);
     g += 2;
   }
   if (total - g == 4) {
