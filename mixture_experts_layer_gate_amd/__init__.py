@@ -9,4 +9,4 @@ from .binding import (  # noqa: F401
     moe_quantize_weights, moe_workspace_bytes, moe_ffn_gate_up, moe_ffn_down, MOE_F32, MOE_BF16, MOE_F8E4M3, MOE_ROWS_DIRECT,
     MOE_ROWS_GATHER, MOE_ROWS_SEGMENT,
 )
-from .layer import MoELayer  # noqa: F401
+from .layer import MoELayer, StepGraph  # noqa: F401

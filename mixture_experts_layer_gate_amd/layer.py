@@ -43,6 +43,18 @@ class LayerOutputs:
     a_scale: Optional[torch.Tensor] = None
 
 
+class StepGraph:
+    """A recorded MoELayer.step (see MoELayer.capture_step): replay() runs one step on the current stream."""
+
+    def __init__(self, layer: "MoELayer", graph: "torch.cuda.CUDAGraph"):
+        self.layer, self.graph = layer, graph
+
+    def replay(self) -> torch.Tensor:
+        self.graph.replay()
+        self.layer.step_count += 1
+        return self.layer.out
+
+
 class MoELayer:
     """One MoE layer on the current CUDA device.
 
@@ -351,6 +363,28 @@ class MoELayer:
         out = self.forward(u)
         self.bias_update()
         return out
+
+    def capture_step(self, u: torch.Tensor) -> "StepGraph":
+        """Record step(u) once into a HIP graph, for replay without per-call host launches.
+
+        Every buffer of the layer is allocated up front and no call allocates, copies to the host or
+        synchronises, so the recorded launches replay unchanged: each replay routes the tokens then in
+        u (same address, same shape) with the bias then current and updates the bias. The kernels are
+        recorded, not run; the library sets its kernels' LDS limits on first use, so at least one eager
+        step (or forward) must come before the capture.
+        """
+        if B._SYNC_DEBUG:
+            raise RuntimeError("capture_step: MOE_SYNC_DEBUG=1 synchronises inside calls, which a capture forbids")
+        u = u.contiguous()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=self.dev)          # capture needs a stream other than the default one
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                self.forward(u)
+                B.moe_bias_update(self.shape, self.expert_load, self.cfg.gamma, self.bias)
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        return StepGraph(self, graph)
 
     # ---------------------------------------------------------------- training
     def forward_train(self, u: torch.Tensor) -> torch.Tensor:
