@@ -189,7 +189,8 @@ size_t moe_permute_noalloc_max_scratch(void);
  *                or MOE_F4E2M1 (MXFP4 expert weights, "DeepSeek V3 / V4 Infra",
  *                V4 post-training FP4 QAT; a and H as with MOE_F8E4M3, the E8M0
  *                weight scales applied by the matrix instruction, fp32 accumulation).
- *   n_experts    experts in this call (routed N_r, or N_s for the shared experts).
+ *   n_experts    experts in this call (routed N_r, or N_s for the shared experts); at most 4096,
+ *                2048 with bf16 or MXFP4 weights (MOE_E_UNSUPPORTED beyond).
  *   n_rows       total rows = expert_offsets[n_experts] (T*K routed, N_s*T shared).
  *   expert_offsets [n_experts + 1] int32 device array.
  *   mode, row_src  see moe_row_mode; row_src [n_rows] int32 for MOE_ROWS_GATHER, else NULL.

@@ -242,6 +242,9 @@ moe_status check_ffn(const moe_shape* shape, moe_dtype w, int32_t n_experts, int
   SUPPORT(d % 128 == 0 && I % 128 == 0, "grouped_ffn: d (%d) and inter (%d) must be multiples of 128", d, I);
   REQUIRE(n_experts > 0 && n_rows > 0, "grouped_ffn: n_experts and n_rows must be positive");
   SUPPORT(n_experts <= 4096, "grouped_ffn: n_experts (%d) > 4096", n_experts);
+  // the bf16 and mxfp4 kernels keep their per-expert schedule table in LDS beside a larger ring
+  SUPPORT((w != MOE_BF16 && w != MOE_BF16_TILED && w != MOE_F4E2M1) || n_experts <= 2048,
+          "grouped_ffn: the bf16 and mxfp4 paths take at most 2048 experts per call (n_experts = %d)", n_experts);
   SUPPORT(static_cast<long long>(n_rows) * (d > I ? d : I) < (1LL << 40), "grouped_ffn: too many rows");
   REQUIRE(offsets != nullptr, "grouped_ffn: expert_offsets is NULL");
   REQUIRE(w == MOE_F32 || w == MOE_BF16 || w == MOE_BF16_TILED || w == MOE_F8E4M3 || w == MOE_F4E2M1,

@@ -136,6 +136,24 @@ def test_grouped_ffn_refuses_32_bit_offset_overflow():
         assert call(w, 1 << 21, 1000) == B.MOE_E_UNSUPPORTED           # n_rows * inter >= 2^32
 
 
+def test_grouped_ffn_expert_count_limits():
+    """At most 4096 experts per grouped call, 2048 on the bf16 and MXFP4 paths (their schedule table shares
+    the LDS with the ring): refused before any launch."""
+    L = B.lib()
+    sh = _shape(d=256, inter=128)
+
+    def call(w, ne):
+        scales = FAKE if w in (B.MOE_F8E4M3, B.MOE_F4E2M1) else None
+        return L.moe_grouped_ffn(ctypes.byref(sh), w, ne, 64, FAKE, B.MOE_ROWS_GATHER, FAKE, FAKE, scales, 64, FAKE,
+                                 scales, FAKE, scales, B.MOE_BF16, FAKE, FAKE, 1 << 40, None)
+
+    for w in (B.MOE_BF16, B.MOE_BF16_TILED, B.MOE_F4E2M1):
+        assert call(w, 2049) == B.MOE_E_UNSUPPORTED
+        assert b"2048" in L.moe_last_error()
+    for w in (B.MOE_F32, B.MOE_F8E4M3):
+        assert call(w, 4097) == B.MOE_E_UNSUPPORTED
+
+
 def test_permute_combine_bias_validation():
     L = B.lib()
     sh = _shape()
