@@ -125,12 +125,13 @@ def test_grouped_ffn_mxfp4_tile_shapes(inter, mode):
     _check_mx_experts(cfg, _mx_ffn_case(cfg, sizes, 23, mode), f"I={inter} {mode}")
 
 
-@pytest.mark.parametrize("d", [384, 640])
-def test_grouped_ffn_mxfp4_half_column_tile(d):
+@pytest.mark.parametrize("d,inter", [(384, 256), (640, 256), (640, 128)])
+def test_grouped_ffn_mxfp4_half_column_tile(d, inter):
     """d % 256 == 128: the last 128 output columns form a unit of their own (code rows past d read as zero,
-    scale loads clamped inside the expert's scales, no store past the row)."""
-    cfg = get_config("c2", gemm="mxfp4", n_routed=4, n_groups=1, topk_groups=1, T=512, topk=2, d=d, inter=256)
-    _check_mx_experts(cfg, _mx_ffn_case(cfg, [0, 40, 300, 129], 6, "gather"), f"d={d}")
+    scale loads clamped inside the expert's scales, no store past the row). With inter = 128 that unit's
+    down stream is two stages long, the shortest the seven-stage ring's prologue handles."""
+    cfg = get_config("c2", gemm="mxfp4", n_routed=4, n_groups=1, topk_groups=1, T=512, topk=2, d=d, inter=inter)
+    _check_mx_experts(cfg, _mx_ffn_case(cfg, [0, 40, 300, 129], 6, "gather"), f"d={d} inter={inter}")
 
 
 def test_grouped_ffn_mxfp4_gather_near_4gib():
