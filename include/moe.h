@@ -19,7 +19,7 @@
  *    call waits for its stream and reports kernel errors).
  *  - Arguments are validated on the host before anything is launched:
  *    MOE_E_INVALID for a null required pointer, a non-positive size or an
- *    inconsistent shape; MOE_E_UNSUPPORTED for shapes or dtypes this build
+ *    inconsistent shape; MOE_E_UNSUPPORTED for shapes or dtypes the library
  *    does not handle; MOE_E_WORKSPACE when ws_bytes is too small; MOE_E_HIP
  *    when a launch fails. The message of the last non-OK status of the calling
  *    thread is returned by moe_last_error(). No exception crosses the ABI.
