@@ -528,6 +528,9 @@ def main():
     if args.backward:
         from moe_inputs import get_config as _gc
         cfg = _gc(args.config)
+        if args.graph:
+            print("bench.py: --graph times forward steps; the training step runs eagerly", file=sys.stderr)
+            sys.exit(2)
         if cfg.gemm not in ("bf16", "fp8") or args.mxfp4 or args.pow2_act_scales or args.batch_invariant:
             print("bench.py: --backward runs the bf16 (c2, c3) and fp8 (c4, c5) workloads", file=sys.stderr)
             sys.exit(2)
