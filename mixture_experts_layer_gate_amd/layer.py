@@ -356,6 +356,7 @@ class MoELayer:
             self.ffn_routed(u)
             self.ffn_shared(u)
         self.combine(u)
+        self._ran = True
         return self.out
 
     def step(self, u: torch.Tensor) -> torch.Tensor:
@@ -375,6 +376,8 @@ class MoELayer:
         """
         if B._SYNC_DEBUG:
             raise RuntimeError("capture_step: MOE_SYNC_DEBUG=1 synchronises inside calls, which a capture forbids")
+        if not getattr(self, "_ran", False):
+            raise RuntimeError("capture_step: run one eager step (or forward) first")
         u = u.contiguous()
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream(device=self.dev)          # capture needs a stream other than the default one
