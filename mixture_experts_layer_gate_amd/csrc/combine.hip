@@ -39,13 +39,14 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& v, float (&x)[8]) {
   }
 }
 
-// One block per token (grid-stride); each thread handles 8 consecutive channels.
+// One block per token (grid-stride), d / 8 threads (at most 1024): each thread handles 8 consecutive
+// channels, so at d <= 8192 a token takes one pass with all of its row loads in flight.
 // KT > 0: bf16 rows and K = KT known at compile time, so the residual, the
 // shared rows and the K routed rows of a piece are loaded together (K + 2
 // loads in flight per lane instead of one) and then added in the same order
 // as the general form: residual, shared experts, routed k = 0 .. K - 1.
 template <int KT>
-__global__ __launch_bounds__(256) void combine_kernel(Shape s, moe_dtype io, const void* __restrict__ u,
+__global__ __launch_bounds__(1024) void combine_kernel(Shape s, moe_dtype io, const void* __restrict__ u,
                                                       const void* __restrict__ y, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate,
                                                       const void* __restrict__ ysh, void* __restrict__ out) {
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Shape s, moe_dtype io, con
 hipError_t launch_combine(const Shape& s, moe_dtype io, const void* u, const void* y, const int32_t* row_of,
                           const float* gate, const void* ysh, void* out, hipStream_t st) {
   int threads = s.d / 8;
-  if (threads > 256) threads = 256;
+  if (threads > 1024) threads = 1024;
   threads = ((threads + 63) / 64) * 64;
   int blocks = s.T;
   const int cap = device_cu_count() * 32;
