@@ -15,11 +15,12 @@
 // at 4 rows x 16 columns hands every lane 4 consecutive rows of one column.
 // Two such reads make one 32x32x16 operand.
 //
-// A workgroup per (expert, 256 x 128 output tile), four waves in a 2 x 2 grid
-// of 128 x 64 (4 x 2 MFMA tiles of 32 x 32), two workgroups per CU. Rows
-// advance in chunks of 32 through a ring of three 24 KB LDS stages filled by
-// direct-to-LDS buffer loads (no VGPR staging), two chunks ahead of the one
-// being multiplied. LDS rows are XOR-swizzled in 16-byte slots (slot = column
+// A workgroup per (expert, 256 x 256 output tile), eight waves in a 2 x 4 grid
+// of 128 x 64 (4 x 2 MFMA tiles of 32 x 32), one workgroup per CU: the tile
+// re-reads the X rows once per 256 output columns instead of per 128, so the
+// direct-to-LDS traffic per output falls by a third. Rows advance in chunks of
+// 32 through a ring of three 32 KB LDS stages filled by direct-to-LDS buffer
+// loads (no VGPR staging), two chunks ahead of the one being multiplied. LDS rows are XOR-swizzled in 16-byte slots (slot = column
 // chunk ^ 4 (row % 4)) so the 4 rows of one transpose read fall in 4 different
 // bank quadrants; a DMA load writes 64 consecutive slots, so each lane fetches
 // the global chunk that belongs at its slot. Rows past the expert's last,
@@ -38,9 +39,9 @@ namespace moe {
 
 namespace {
 
-constexpr int kWgBM = 256, kWgBN = 128, kWgBK = 32;
+constexpr int kWgBM = 256, kWgBN = 256, kWgBK = 32, kWgNT = 512;
 constexpr int kWgXBytes = kWgBK * kWgBM * 2;              // 16 KB
-constexpr int kWgStage = kWgXBytes + kWgBK * kWgBN * 2;   // + 8 KB
+constexpr int kWgStage = kWgXBytes + kWgBK * kWgBN * 2;   // + 16 KB
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -109,13 +110,13 @@ __device__ __forceinline__ void wg_wait_barrier() {
 // vector-memory counter only ever counts the DMA loads; otherwise Y row r is r
 // (direct) or r - lo (segment).
 template <bool GATHER>
-__global__ __launch_bounds__(256, 2) void wgrad_kernel(int M, int N, int E, int n_rows, int a_rows,
+__global__ __launch_bounds__(kWgNT, 1) void wgrad_kernel(int M, int N, int E, int n_rows, int a_rows,
                                                        const int32_t* __restrict__ off, moe_row_mode mode,
                                                        const int32_t* __restrict__ row_src,
                                                        const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
                                                        float* __restrict__ C) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int mt = cdiv(M, kWgBM), nt = N / kWgBN;
+  const int mt = cdiv(M, kWgBM), nt = cdiv(N, kWgBN);
   // XCD-aware tiles: workgroups go to the 8 XCDs round-robin, and XCD x takes the M tiles mi of expert e with
   // (mi + e) % 8 == x, each with all its N tiles, in expert order: an expert's X rows are fetched once (each M
   // tile by one XCD), its Y rows once per XCD, and all XCDs work on the same experts at a time. (Measured at
@@ -138,9 +139,10 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(int M, int N, int E, int 
   if (e >= E) return;
   const int m0 = (mfirst + 8 * (rem / nt)) * kWgBM, n0 = (rem % nt) * kWgBN;
   const int lo = clampi(off[e], 0, n_rows), hi = clampi(off[e + 1], lo, n_rows);
-  const int tid = threadIdx.x, l = tid & 63, wm = (tid >> 6) >> 1, wn = (tid >> 6) & 1;
+  const int tid = threadIdx.x, l = tid & 63, wm = (tid >> 6) >> 2, wn = (tid >> 6) & 3;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool active = m0 + wm * 128 < M;                      // M % 256 == 128: the last tile's second half is empty
+  // M or N % 256 == 128: the last tile's second half (in that dimension) is empty
+  const bool active = m0 + wm * 128 < M && n0 + wn * 64 < N;
   f32x16 acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -167,18 +169,19 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(int M, int N, int E, int 
   };
 
   if (nch > 0) {
-    // DMA load q of this wave fills LDS slots (q * 4 + w) * 64 + lane of the X (or Y) part of a stage
-    uint32_t vx[4], vy[2];
+    // DMA load q of this wave fills LDS slots (q * 8 + w) * 64 + lane of the X (or Y) part of a stage: two
+    // 512-byte rows, the lanes of each at the 16-byte slots of their row
+    uint32_t vx[2], vy[2];
     int yrow[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 2 * (q * 4 + w) + (l >> 5), c = (l & 31) ^ (4 * (row & 3));
+    for (int q = 0; q < 2; ++q) {
+      const int row = 2 * (q * 8 + w) + (l >> 5), c = (l & 31) ^ (4 * (row & 3));
       vx[q] = static_cast<uint32_t>(row * M * 2 + c * 16);
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      yrow[q] = 4 * (q * 4 + w) + (l >> 4);
-      const int c = (l & 15) ^ (4 * (yrow[q] & 3));
+      yrow[q] = 2 * (q * 8 + w) + (l >> 5);
+      const int c = (l & 31) ^ (4 * (yrow[q] & 3));
       vy[q] = static_cast<uint32_t>(GATHER ? c * 16 : yrow[q] * N * 2 + c * 16);
     }
     auto issue = [&](int ch) {
@@ -187,21 +190,19 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(int M, int N, int E, int 
       const __amdgpu_buffer_rsrc_t rx =
           pipe_rsrc(X + static_cast<size_t>(r0) * M + m0, range_bytes((static_cast<long long>(hi - r0) * M - m0) * 2));
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(st + (q * 4 + w) * 1024), 16, vx[q], 0, 0, 0);
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(st + (q * 8 + w) * 1024), 16, vx[q], 0, 0, 0);
       if (GATHER) {
         const __amdgpu_buffer_rsrc_t ry =
             pipe_rsrc(Y + n0, range_bytes((static_cast<long long>(a_rows) * N - n0) * 2));
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const int base = r0 + 4 * (q * 4 + w);                 // wave-uniform: scalar loads, clamped to the rows
+          const int base = r0 + 2 * (q * 8 + w);                 // wave-uniform: scalar loads, clamped to the rows
           const int s0 = row_src[min(base, hi - 1)], s1 = row_src[min(base + 1, hi - 1)];
-          const int s2 = row_src[min(base + 2, hi - 1)], s3 = row_src[min(base + 3, hi - 1)];
-          const int sel = l >> 4;
-          const int sr = sel == 0 ? s0 : (sel == 1 ? s1 : (sel == 2 ? s2 : s3));
+          const int sr = (l >> 5) ? s1 : s0;
           const bool ok = r0 + yrow[q] < hi && sr >= 0 && sr < a_rows;
           const uint32_t vo = ok ? static_cast<uint32_t>(sr) * static_cast<uint32_t>(N * 2) + vy[q] : kWgOut;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void_t*)(st + kWgXBytes + (q * 4 + w) * 1024), 16, vo, 0,
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void_t*)(st + kWgXBytes + (q * 8 + w) * 1024), 16, vo, 0,
                                                    0, 0);
         }
       } else {
@@ -212,17 +213,17 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(int M, int N, int E, int 
                                                             : 0u);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void_t*)(st + kWgXBytes + (q * 4 + w) * 1024), 16, vy[q],
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void_t*)(st + kWgXBytes + (q * 8 + w) * 1024), 16, vy[q],
                                                    0, 0, 0);
       }
     };
     // prologue: chunks 0 and 1 in flight
     issue(0);
     if (nch > 1) issue(1);
-    // iteration ch: wait for chunk ch (only chunk ch + 1's six loads may still be in flight), issue the DMA of
+    // iteration ch: wait for chunk ch (only chunk ch + 1's four loads may still be in flight), issue the DMA of
     // chunk ch + 2 into the stage chunk ch - 1 used, multiply chunk ch
     for (int ch = 0; ch < nch; ++ch) {
-      if (ch + 1 < nch) wg_wait_barrier<6>();
+      if (ch + 1 < nch) wg_wait_barrier<4>();
       else wg_wait_barrier<0>();
       if (ch + 2 < nch) issue(ch + 2);
       if (active) {
@@ -261,13 +262,13 @@ hipError_t launch_wgrad(int M, int N, int E, int n_rows, int a_rows, const int32
       (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kWgNS * kWgStage);
     (void)hipGetLastError();
   });
-  const long long blocks = 8LL * ((E + 7) / 8) * cdiv(M, kWgBM) * (N / kWgBN);   // whole groups of 8 experts
+  const long long blocks = 8LL * ((E + 7) / 8) * cdiv(M, kWgBM) * cdiv(N, kWgBN);   // whole groups of 8 experts
   const size_t lds = static_cast<size_t>(kWgNS) * kWgStage;
   if (mode == MOE_ROWS_GATHER)
-    hipLaunchKernelGGL(wgrad_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, M, N, E, n_rows,
+    hipLaunchKernelGGL(wgrad_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kWgNT), lds, st, M, N, E, n_rows,
                        a_rows, off, mode, row_src, static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Y), C);
   else
-    hipLaunchKernelGGL(wgrad_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, M, N, E, n_rows,
+    hipLaunchKernelGGL(wgrad_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kWgNT), lds, st, M, N, E, n_rows,
                        a_rows, off, mode, row_src, static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Y), C);
   return hipGetLastError();
 }
