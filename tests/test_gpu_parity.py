@@ -405,14 +405,16 @@ def test_fp8_layer_pow2_act_scales():
         report(f"c2 fp8 pow2 out-u token {t}", rel_l2(np64(out[t]) - u64[t], acc - u64[t]), TOL["fp8"])
 
 
-@pytest.mark.parametrize("gemm", ["bf16", "fp8"])
+@pytest.mark.parametrize("gemm", ["bf16", "fp8", "mxfp4"])
 def test_batch_invariance(gemm):
     """batch_invariant = 1: 100 tokens of a 4096-token batch, placed among other tokens in a 160-token batch,
-    and one of them alone, get bit-identical affinities, selections, gates and layer outputs. The default
-    mode's differing affinities are printed for contrast (its router K split follows T)."""
+    and one of them alone, get bit-identical affinities, selections, gates and layer outputs. At d = 4096
+    (32 chunks of 128) the default mode's router K split follows T (16 slices for the 4096-token batch, 32
+    for the small ones), so there the affinities of the same tokens differ between the batches: checked, so
+    that the mode is shown to matter."""
     from dataclasses import replace
     from moe_inputs import generate_tokens
-    cfg, inp = _inputs("c2", gemm=gemm, batch_invariant=1)
+    cfg, inp = _inputs("c2", gemm=gemm, batch_invariant=1, d=4096)
     T = cfg.T
     sel = np.random.default_rng(5).choice(T, 100, replace=False)
     other = generate_tokens(cfg, DEV, step=3)[:60]
@@ -439,6 +441,7 @@ def test_batch_invariance(gemm):
     n_diff = int((full0["scores"][torch.from_numpy(sel)] != part0["scores"][torch.from_numpy(rows_b)]).sum())
     print(f"[parity] {gemm} batch-invariant mode: 0 differing results; default mode: {n_diff} of "
           f"{100 * cfg.n_routed} affinities differ between the two batches")
+    assert n_diff > 0, "the default mode's K split should follow T at this shape"
 
 
 @pytest.mark.parametrize("kind", ["gate_up", "down", "down_padded"])
