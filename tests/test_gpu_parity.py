@@ -40,6 +40,8 @@ ROUTE_CASES = [
     ("c5", {}),                                             # 384 experts, no group limit: 6 per lane
     # the supported maxima: 1024 experts in 64 groups, top-16 of 8 groups, 4-term group scores; ragged T
     ("c2", dict(T=300, d=256, inter=128, n_routed=1024, n_groups=64, topk_groups=8, group_topn=4, topk=16)),
+    # a 4096-token batch with 512 experts in 64 groups, top-16 of 8 groups, 4-term group scores (8 per lane)
+    ("c2", dict(d=256, inter=128, n_routed=512, n_groups=64, topk_groups=8, group_topn=4, topk=16)),
 ]
 
 
