@@ -43,6 +43,8 @@ __global__ __launch_bounds__(256) void perm_mask_kernel(int T, int K, int N, con
     for (int e = lane; e < N; e += kWave) masks[static_cast<size_t>(c) * N + e] = m[e];
 }
 
+constexpr int kScanRegs = 32;
+
 // One block of 1024 threads. Thread (p, e) = (tid / N, tid % N) counts expert
 // e's pairs over the p-th of P = 1024 / N runs of chunks (N <= 1024), so the
 // chunk loop is P times shorter than with one thread per expert; the run
@@ -59,9 +61,21 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int N, const uns
   const bool act = p < P;
   const int c0 = act ? static_cast<int>(static_cast<long long>(p) * nch / P) : 0;
   const int c1 = act ? static_cast<int>(static_cast<long long>(p + 1) * nch / P) : 0;
+  // runs of at most kScanRegs chunks (T <= 8192 with 256 experts): the run's masks are loaded together and
+  // their counts kept in registers for the base pass; longer runs stream them twice
+  const int n_run = c1 - c0;
+  const bool in_regs = n_run <= kScanRegs;
+  int pc[kScanRegs];
   int cnt = 0;
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kScanRegs; ++i) pc[i] = i < n_run ? __popcll(masks[static_cast<size_t>(c0 + i) * N + e]) : 0;
+#pragma unroll
+    for (int i = 0; i < kScanRegs; ++i) cnt += pc[i];
+  } else {
 #pragma unroll 8
-  for (int c = c0; c < c1; ++c) cnt += __popcll(masks[static_cast<size_t>(c) * N + e]);
+    for (int c = c0; c < c1; ++c) cnt += __popcll(masks[static_cast<size_t>(c) * N + e]);
+  }
   if (act) run_cnt[tid] = cnt;
   __syncthreads();
   // expert totals (threads e < N), then the exclusive scan over experts
@@ -94,13 +108,24 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int N, const uns
   __syncthreads();
   if (act) {
     int run = run_cnt[tid];
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < kScanRegs; ++i)
+        if (i < n_run) {
+          base[static_cast<size_t>(c0 + i) * N + e] = run;
+          run += pc[i];
+        }
+    } else {
 #pragma unroll 8
-    for (int c = c0; c < c1; ++c) {
-      base[static_cast<size_t>(c) * N + e] = run;
-      run += __popcll(masks[static_cast<size_t>(c) * N + e]);
+      for (int c = c0; c < c1; ++c) {
+        base[static_cast<size_t>(c) * N + e] = run;
+        run += __popcll(masks[static_cast<size_t>(c) * N + e]);
+      }
     }
   }
 }
+
+constexpr int kScatterK = 16;   // the largest top-K the library accepts
 
 // A pair whose expert id is out of range or repeats an earlier id of the same
 // token gets no row (row_of = -1); the masks count such a token once per
@@ -116,18 +141,50 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int K, int N, 
   if (t >= T) return;
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int32_t* ti = idx + static_cast<size_t>(t) * K;
-  for (int k = 0; k < K; ++k) {
-    const int e = ti[k];
-    bool ok = e >= 0 && e < N;
-    for (int j = 0; j < k && ok; ++j) ok = ti[j] != e;
-    if (!ok) {
-      row_of[static_cast<size_t>(t) * K + k] = -1;
-      continue;
+  if (K <= kScatterK) {
+    // the token's ids, then the base and mask of every kept pair, each batch of loads issued together
+    int ev[kScatterK];
+#pragma unroll
+    for (int k = 0; k < kScatterK; ++k) ev[k] = k < K ? ti[k] : -1;
+    bool ok[kScatterK];
+#pragma unroll
+    for (int k = 0; k < kScatterK; ++k) {
+      ok[k] = k < K && ev[k] >= 0 && ev[k] < N;
+#pragma unroll
+      for (int j = 0; j < k; ++j) ok[k] = ok[k] && ev[j] != ev[k];
     }
-    const size_t ce = static_cast<size_t>(c) * N + e;
-    const int r = base[ce] + __popcll(masks[ce] & below);
-    perm[r] = t;
-    row_of[static_cast<size_t>(t) * K + k] = r;
+    int bv[kScatterK];
+    unsigned long long mv[kScatterK];
+#pragma unroll
+    for (int k = 0; k < kScatterK; ++k) {
+      const size_t ce = static_cast<size_t>(c) * N + (ok[k] ? ev[k] : 0);
+      bv[k] = ok[k] ? base[ce] : 0;
+      mv[k] = ok[k] ? masks[ce] : 0ull;
+    }
+#pragma unroll
+    for (int k = 0; k < kScatterK; ++k) {
+      if (k >= K) break;
+      int r = -1;
+      if (ok[k]) {
+        r = bv[k] + __popcll(mv[k] & below);
+        perm[r] = t;
+      }
+      row_of[static_cast<size_t>(t) * K + k] = r;
+    }
+  } else {
+    for (int k = 0; k < K; ++k) {
+      const int e = ti[k];
+      bool ok = e >= 0 && e < N;
+      for (int j = 0; j < k && ok; ++j) ok = ti[j] != e;
+      if (!ok) {
+        row_of[static_cast<size_t>(t) * K + k] = -1;
+        continue;
+      }
+      const size_t ce = static_cast<size_t>(c) * N + e;
+      const int r = base[ce] + __popcll(masks[ce] & below);
+      perm[r] = t;
+      row_of[static_cast<size_t>(t) * K + k] = r;
+    }
   }
   const long long used = offsets[N];
   for (int k = 0; k < K; ++k) {
