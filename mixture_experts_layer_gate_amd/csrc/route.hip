@@ -552,7 +552,7 @@ static hipError_t launch_select_reg(const Shape& s, const float* part, int S, fl
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long n = static_cast<long long>(s.T) * s.K;
-  long long hb = (n + 16383) / 16384;
+  long long hb = (n + 1023) / 1024;               // about 1024 pairs per block: one pass of the block
   hb = hb < 1 ? 1 : (hb > 64 ? 64 : hb);
   hipLaunchKernelGGL(route_hist_kernel, dim3(static_cast<unsigned>(hb)), dim3(1024), 0, st, n, s.N, idx, load);
   return hipGetLastError();
